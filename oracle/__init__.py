@@ -1,0 +1,317 @@
+"""CPU oracle for block-scaled quantization and block-scaled GEMM.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, the smoke check in
+``__graft_entry__.py`` and the CPU-baseline leg of ``bench.py`` may import
+this package.  The product library never loads it and shares no code with it.
+
+The arithmetic lives in ``mx_oracle.c`` (plain C, FP64 / exact FP32, encoders
+that search the decoded alphabet).  This module compiles it with gcc and
+wraps it with ctypes over numpy arrays.  Every function states which page
+passage it follows in the C source.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mx_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+MXFP8, MXFP4, NVFP4 = 1, 2, 3
+RNE, SR = 0, 1
+IN_BF16, IN_F32 = 0, 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile mx_oracle.c into liboracle.so next to it (gcc, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _P(t):
+    return ctypes.POINTER(t)
+
+
+def lib():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    L = ctypes.CDLL(_LIB)
+    c_u8p, c_f32p, c_f64p = _P(ctypes.c_uint8), _P(ctypes.c_float), _P(ctypes.c_double)
+    i64, u64, u32 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    sig = {
+        "mxo_init": (ci, []),
+        "mxo_e2m1_decode": (ctypes.c_double, [u32]),
+        "mxo_e4m3_decode": (ctypes.c_double, [u32]),
+        "mxo_e8m0_decode": (ctypes.c_double, [u32]),
+        "mxo_e2m1_encode_rne": (u32, [ctypes.c_double]),
+        "mxo_e4m3_encode_rne": (u32, [ctypes.c_double]),
+        "mxo_e2m1_encode_sr": (u32, [ctypes.c_double, u32]),
+        "mxo_e4m3_encode_sr": (u32, [ctypes.c_double, u32]),
+        "mxo_philox4x32_10": (None, [_P(ctypes.c_uint32), _P(ctypes.c_uint32), _P(ctypes.c_uint32)]),
+        "mxo_rand16": (u32, [u64, u64, u64]),
+        "mxo_rht_signs": (u32, [u64]),
+        "mxo_rht16": (None, [vp, ci, c_f32p, i64, i64, u32, ci]),
+        "mxo_quantize_mx": (ci, [vp, ci, i64, i64, i64, ci, ci, u64, u64, ci, u32, c_u8p, c_u8p]),
+        "mxo_tensor_amax": (ctypes.c_float, [vp, ci, i64, i64, i64, ci, u32]),
+        "mxo_quantize_nvfp4": (ci, [vp, ci, i64, i64, i64, ci, u64, u64, ci, u32, c_f32p,
+                                    c_u8p, c_u8p, c_f32p]),
+        "mxo_dequantize": (None, [ci, c_u8p, c_u8p, c_f32p, i64, i64, c_f32p]),
+        "mxo_dequantize_f64": (None, [ci, c_u8p, c_u8p, i64, i64, c_f64p]),
+        "mxo_requant_transpose": (ci, [ci, vp, c_u8p, c_f32p, i64, i64, ci, u64, u64, c_u8p, c_u8p]),
+        "mxo_gemm_f64": (None, [c_f64p, c_f64p, i64, i64, i64, ctypes.c_double, c_f64p, c_f64p]),
+        "mxo_gemm_f64_sampled": (None, [c_f64p, c_f64p, i64, _P(i64), _P(i64), i64,
+                                        ctypes.c_double, c_f64p, c_f64p]),
+        "mxo_codes_bytes": (i64, [ci, i64, i64]),
+        "mxo_scales_bytes": (i64, [ci, i64, i64]),
+        "mxo_tensor_bytes": (i64, [ci, i64, i64]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    L.mxo_init()
+    _lib = L
+    return L
+
+
+def _ptr(a: np.ndarray, t):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(_P(t))
+
+
+def _vptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _in(x: np.ndarray):
+    """Input matrix as (array, dtype code).  bf16 data is passed as uint16 bits."""
+    if x.dtype == np.uint16:
+        return np.ascontiguousarray(x), IN_BF16
+    if x.dtype == np.float32:
+        return np.ascontiguousarray(x), IN_F32
+    raise TypeError("oracle inputs are bf16 bits (uint16) or float32")
+
+
+# --- scalar codecs ---------------------------------------------------------
+def e2m1_decode(code: int) -> float:
+    return lib().mxo_e2m1_decode(code)
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().mxo_e4m3_decode(code)
+
+
+def e8m0_decode(code: int) -> float:
+    return lib().mxo_e8m0_decode(code)
+
+
+def e2m1_encode_rne(y: float) -> int:
+    return lib().mxo_e2m1_encode_rne(y)
+
+
+def e4m3_encode_rne(y: float) -> int:
+    return lib().mxo_e4m3_encode_rne(y)
+
+
+def e2m1_encode_sr(y: float, r16: int) -> int:
+    return lib().mxo_e2m1_encode_sr(y, r16)
+
+
+def e4m3_encode_sr(y: float, r16: int) -> int:
+    return lib().mxo_e4m3_encode_sr(y, r16)
+
+
+def philox4x32_10(ctr, key):
+    c = (ctypes.c_uint32 * 4)(*[int(v) & 0xFFFFFFFF for v in ctr])
+    k = (ctypes.c_uint32 * 2)(*[int(v) & 0xFFFFFFFF for v in key])
+    o = (ctypes.c_uint32 * 4)()
+    lib().mxo_philox4x32_10(c, k, o)
+    return [o[i] for i in range(4)]
+
+
+def rand16(seed: int, counter: int, n: int) -> int:
+    return lib().mxo_rand16(seed, counter, n)
+
+
+def rht_signs(seed: int) -> int:
+    return lib().mxo_rht_signs(seed)
+
+
+# --- tensor operations -----------------------------------------------------
+def rht16(x: np.ndarray, sign_mask: int, inverse: bool = False) -> np.ndarray:
+    x, dt = _in(x)
+    rows, cols = x.shape
+    assert cols % 16 == 0
+    y = np.empty((rows, cols), np.float32)
+    lib().mxo_rht16(_vptr(x), dt, _ptr(y, ctypes.c_float), rows, cols, sign_mask, int(inverse))
+    return y
+
+
+def codes_bytes(fmt, rows, cols):
+    return lib().mxo_codes_bytes(fmt, rows, cols)
+
+
+def scales_bytes(fmt, rows, cols):
+    return lib().mxo_scales_bytes(fmt, rows, cols)
+
+
+def tensor_bytes(fmt, rows, cols):
+    return lib().mxo_tensor_bytes(fmt, rows, cols)
+
+
+def tensor_amax(x: np.ndarray, rht: bool = False, sign_mask: int = 0) -> float:
+    x, dt = _in(x)
+    rows, cols = x.shape
+    return float(lib().mxo_tensor_amax(_vptr(x), dt, cols, rows, cols, int(rht), sign_mask))
+
+
+def quantize(x: np.ndarray, fmt: int, rnd: int = RNE, seed: int = 0, counter: int = 0,
+             rht: bool = False, sign_mask: int = 0, amax: float | None = None):
+    """Quantize a [rows, cols] matrix along cols.
+
+    Returns (codes, scales, tensor_scale): codes uint8 [rows, cols] (MXFP8) or
+    [rows, cols/2] (FP4, element 2j in the low nibble); scales uint8
+    [rows, cols/32] (E8M0) or [rows, cols/16] (E4M3); tensor_scale a float
+    (NVFP4) or None.
+    """
+    x, dt = _in(x)
+    rows, cols = x.shape
+    cb = codes_bytes(fmt, rows, cols) // max(rows, 1)
+    codes = np.zeros((rows, cb), np.uint8)
+    if fmt == NVFP4:
+        scales = np.zeros((rows, cols // 16), np.uint8)
+        ts = np.zeros(1, np.float32)
+        am = None if amax is None else np.array([amax], np.float32)
+        rc = lib().mxo_quantize_nvfp4(_vptr(x), dt, cols, rows, cols, rnd, seed, counter, int(rht),
+                                      sign_mask, None if am is None else _ptr(am, ctypes.c_float),
+                                      _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8),
+                                      _ptr(ts, ctypes.c_float))
+        if rc:
+            raise ValueError("oracle rejected the shape")
+        return codes, scales, float(ts[0])
+    scales = np.zeros((rows, cols // 32), np.uint8)
+    rc = lib().mxo_quantize_mx(_vptr(x), dt, cols, rows, cols, fmt, rnd, seed, counter, int(rht),
+                               sign_mask, _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8))
+    if rc:
+        raise ValueError("oracle rejected the shape")
+    return codes, scales, None
+
+
+def dequantize(fmt: int, codes: np.ndarray, scales: np.ndarray, tensor_scale, rows: int,
+               cols: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    ts = np.array([tensor_scale if tensor_scale is not None else 1.0], np.float32)
+    y = np.empty((rows, cols), np.float32)
+    lib().mxo_dequantize(fmt, _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8),
+                         _ptr(ts, ctypes.c_float), rows, cols, _ptr(y, ctypes.c_float))
+    return y
+
+
+def dequantize_f64(fmt: int, codes: np.ndarray, scales: np.ndarray, rows: int,
+                   cols: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    y = np.empty((rows, cols), np.float64)
+    lib().mxo_dequantize_f64(fmt, _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8),
+                             rows, cols, _ptr(y, ctypes.c_double))
+    return y
+
+
+def requant_transpose(rows: int, cols: int, rnd: int = SR, seed: int = 0, counter: int = 0,
+                      nvfp4=None, bf16: np.ndarray | None = None):
+    """Source [rows, cols] (an NVFP4 (codes, scales, S) triple, or bf16 bits)
+    -> MXFP8 codes [cols, rows] and E8M0 scales [cols, rows/32]."""
+    codes = np.zeros((cols, rows), np.uint8)
+    scales = np.zeros((cols, rows // 32), np.uint8)
+    if nvfp4 is not None:
+        c, s, ts = nvfp4
+        c = np.ascontiguousarray(c, np.uint8)
+        s = np.ascontiguousarray(s, np.uint8)
+        tsa = np.array([ts], np.float32)
+        rc = lib().mxo_requant_transpose(NVFP4, _vptr(c), _ptr(s, ctypes.c_uint8),
+                                         _ptr(tsa, ctypes.c_float), rows, cols, rnd, seed, counter,
+                                         _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8))
+    else:
+        b = np.ascontiguousarray(bf16, np.uint16)
+        rc = lib().mxo_requant_transpose(0, _vptr(b), None, None, rows, cols, rnd, seed, counter,
+                                         _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8))
+    if rc:
+        raise ValueError("oracle rejected the shape")
+    return codes, scales
+
+
+def gemm(A: np.ndarray, B: np.ndarray, post_scale: float = 1.0):
+    """FP64 C = A @ B.T over decoded operands, and tol = 1e-5 * sum|a*b|."""
+    A = np.ascontiguousarray(A, np.float64)
+    B = np.ascontiguousarray(B, np.float64)
+    M, K = A.shape
+    N = B.shape[0]
+    C = np.empty((M, N), np.float64)
+    T = np.empty((M, N), np.float64)
+    lib().mxo_gemm_f64(_ptr(A, ctypes.c_double), _ptr(B, ctypes.c_double), M, N, K,
+                       float(post_scale), _ptr(C, ctypes.c_double), _ptr(T, ctypes.c_double))
+    return C, T
+
+
+def gemm_sampled(A: np.ndarray, B: np.ndarray, ri: np.ndarray, cj: np.ndarray,
+                 post_scale: float = 1.0):
+    A = np.ascontiguousarray(A, np.float64)
+    B = np.ascontiguousarray(B, np.float64)
+    ri = np.ascontiguousarray(ri, np.int64)
+    cj = np.ascontiguousarray(cj, np.int64)
+    n = ri.size
+    C = np.empty(n, np.float64)
+    T = np.empty(n, np.float64)
+    lib().mxo_gemm_f64_sampled(_ptr(A, ctypes.c_double), _ptr(B, ctypes.c_double), A.shape[1],
+                               _ptr(ri, ctypes.c_int64), _ptr(cj, ctypes.c_int64), n,
+                               float(post_scale), _ptr(C, ctypes.c_double), _ptr(T, ctypes.c_double))
+    return C, T
+
+
+def bf16_interval(C: np.ndarray, tol: np.ndarray):
+    """BF16-output acceptance interval [bf16_rne(C - tol), bf16_rne(C + tol)]
+    as float64 arrays (the rounding here is the plain definition: nearest
+    bf16, ties to even, computed through float32 which is exact for the
+    bounds' own rounding because it is done on the FP64 value directly)."""
+    lo = _round_bf16_f64(C - tol)
+    hi = _round_bf16_f64(C + tol)
+    return lo, hi
+
+
+def _round_bf16_f64(v: np.ndarray) -> np.ndarray:
+    """Round FP64 values to the nearest bf16 (ties to even), returned as FP64.
+
+    Done in exact integer arithmetic on the FP64 significand so no double
+    rounding through FP32 occurs."""
+    v = np.asarray(v, np.float64)
+    m, e = np.frexp(v)  # v = m * 2^e, |m| in [0.5, 1)
+    # bf16 keeps 8 significant bits: scale to an integer significand of 8 bits
+    # for normal values; clamp the exponent at the bf16 normal minimum (2^-126)
+    # so subnormals keep fewer bits.
+    e_min = -125  # smallest e (frexp convention) of a normal bf16
+    bits = 8 - np.maximum(e_min - e, 0)
+    bits = np.maximum(bits, 0)
+    scaled = np.ldexp(m, bits)  # exact
+    r = np.rint(scaled)  # round half to even (numpy rint)
+    out = np.ldexp(r, e - bits)
+    # overflow to inf beyond the bf16 max
+    big = np.abs(out) > 3.3895313892515355e38
+    out = np.where(big, np.sign(out) * np.inf, out)
+    return out

@@ -1,0 +1,651 @@
+/*
+ * mx_oracle.c -- plain, slow CPU oracle for block-scaled (microscaling)
+ * quantization and block-scaled GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It shares no source, header, table or helper with the
+ * HIP library; every number format is decoded from its bit-level definition
+ * and every encoder works by searching the decoded alphabet for the nearest
+ * value, never by bit tricks.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [MXF]  "Microscaling (MX) and block-scaled 4-bit formats"
+ *          sections "The problem", "Microscaling", "The idea", "NVFP4",
+ *          "Hardware and kernels", glossary ("scale factor",
+ *          "stochastic rounding").
+ *   [FP4]  "08 - FP4, MXFP4, NVFP4: The Blackwell Frontier"
+ *          sections "Why 4-bit floats at all?" (E2M1 bit layout and code
+ *          points), "The two Blackwell formats: MXFP4 vs NVFP4" (format
+ *          table), "The OCP Microscaling (MX) spec".
+ *   [INK]  "Thinking Machines ... Inkling 2 Small: end-to-end 4-bit training"
+ *          section "A precision choice for each stage" (stochastic rounding,
+ *          dequantize -> transpose -> stochastic requantize to MXFP8).
+ *   [MIL]  "LMSYS and humans& ... MXFP8 and NVFP4 RL recipes in Miles"
+ *          section "Recipe 1: End-to-end MXFP8" (32 E4M3 values share one
+ *          E8M0 scale, one-dimensional block).
+ *   [PHX]  Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
+ *          1, 2, 3", SC'11 -- the Philox-4x32 bijection and key schedule.
+ *
+ * Where the pages leave a step open, the plainest reading is taken; each such
+ * reading is marked READING below.
+ *
+ * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fno-fast-math -shared
+ * (FP32 expressions must be evaluated exactly as written, one IEEE rounding
+ * per operation, no fused multiply-add.)
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define MXO_MXFP8 1
+#define MXO_MXFP4 2
+#define MXO_NVFP4 3
+#define MXO_RNE 0
+#define MXO_SR 1
+
+/* ------------------------------------------------------------------------ */
+/* Element and scale decoders, written from the bit-level definitions.       */
+/* ------------------------------------------------------------------------ */
+
+/* E2M1: bits S E E M (bit 3 = sign), exponent bias 1, exponent 0 is
+ * subnormal (value = M * 0.5).  [FP4] "Why 4-bit floats at all?" gives the
+ * layout and the resulting code points {0, .5, 1, 1.5, 2, 3, 4, 6}; [MXF]
+ * "The problem" gives the same non-negative alphabet. */
+double mxo_e2m1_decode(uint32_t code) {
+  code &= 0xF;
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double mag = (e == 0) ? m * 0.5 : ldexp(1.0 + m / 2.0, e - 1);
+  return s ? -mag : mag;
+}
+
+/* E4M3 (READING: the OCP "FN" flavour -- bias 7, no infinities, the all-ones
+ * exponent-and-mantissa pattern is NaN, largest finite 448).  The pages name
+ * E4M3 as the MXFP8 element ([MIL] "Recipe 1") and as the NVFP4 block scale
+ * ([MXF] "NVFP4"; [FP4] format table) without giving its bits. */
+double mxo_e4m3_decode(uint32_t code) {
+  code &= 0xFF;
+  int s = (code >> 7) & 1, e = (code >> 3) & 0xF, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  double mag = (e == 0) ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -mag : mag;
+}
+
+/* E8M0: an unsigned power of two made of exponent bits only, 2^-127..2^127,
+ * with one code reserved for NaN ([FP4] "The OCP Microscaling (MX) spec";
+ * [MXF] "Microscaling"). */
+double mxo_e8m0_decode(uint32_t code) {
+  code &= 0xFF;
+  if (code == 0xFF) return NAN;
+  return ldexp(1.0, (int)code - 127);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Alphabets: the non-negative finite values of an element format, sorted,  */
+/* with their codes.  Built by decoding every code.                          */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int n;
+  double v[128];
+  uint32_t code[128];
+  uint32_t sign_bit;
+} mxo_alphabet;
+
+static mxo_alphabet g_e2m1, g_e4m3;
+static int g_ready = 0;
+
+static void build_alphabet(mxo_alphabet* a, double (*dec)(uint32_t), int ncodes,
+                           uint32_t sign_bit) {
+  a->n = 0;
+  a->sign_bit = sign_bit;
+  for (int c = 0; c < ncodes; ++c) {
+    if (c & sign_bit) continue; /* non-negative half only */
+    double v = dec((uint32_t)c);
+    if (isnan(v)) continue;
+    a->v[a->n] = v;
+    a->code[a->n] = (uint32_t)c;
+    a->n++;
+  }
+  /* insertion sort by value (codes are already monotone, but do not rely on it) */
+  for (int i = 1; i < a->n; ++i) {
+    double v = a->v[i];
+    uint32_t c = a->code[i];
+    int j = i - 1;
+    while (j >= 0 && a->v[j] > v) {
+      a->v[j + 1] = a->v[j];
+      a->code[j + 1] = a->code[j];
+      --j;
+    }
+    a->v[j + 1] = v;
+    a->code[j + 1] = c;
+  }
+}
+
+static void ensure_tables(void) {
+  if (g_ready) return;
+  build_alphabet(&g_e2m1, mxo_e2m1_decode, 16, 0x8);
+  build_alphabet(&g_e4m3, mxo_e4m3_decode, 256, 0x80);
+  g_ready = 1;
+}
+
+int mxo_init(void) {
+  ensure_tables();
+  return g_e2m1.n * 1000 + g_e4m3.n;
+}
+
+/* Index i with v[i] <= a < v[i+1]; a must be in [0, vmax). */
+static int bracket(const mxo_alphabet* al, double a) {
+  int lo = 0, hi = al->n - 1; /* invariant v[lo] <= a < v[hi] */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (al->v[mid] <= a) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+/* Round-to-nearest, ties to the even code (READING of "round-to-nearest",
+ * [MXF] "Open points"), saturating to the largest finite value (READING:
+ * elements beyond the range saturate), sign preserved, so -0 exists.
+ * y must not be NaN. */
+static uint32_t encode_rne(const mxo_alphabet* al, double y) {
+  uint32_t sign = signbit(y) ? al->sign_bit : 0;
+  double a = fabs(y);
+  double vmax = al->v[al->n - 1];
+  if (a >= vmax) return sign | al->code[al->n - 1];
+  int i = bracket(al, a);
+  double lo = al->v[i], hi = al->v[i + 1];
+  double mid = 0.5 * (lo + hi); /* exact: both are short dyadic numbers */
+  uint32_t c;
+  if (a < mid) c = al->code[i];
+  else if (a > mid) c = al->code[i + 1];
+  else c = (al->code[i] & 1) ? al->code[i + 1] : al->code[i];
+  return sign | c;
+}
+
+/* Stochastic rounding: round up or down at random, with the probability of
+ * going up proportional to the distance from the lower neighbour, so the
+ * expected value is preserved ([MXF] glossary "stochastic rounding"; [INK]
+ * "A precision choice for each stage").
+ * READING: 16 random bits r per element; with lo <= a < hi the neighbours and
+ * t = (a - lo) * 2^16 / (hi - lo), round up exactly when r < floor(t).
+ * P(up) = floor(t)/65536.  Saturate at the largest finite value. */
+static uint32_t encode_sr(const mxo_alphabet* al, double y, uint32_t r16) {
+  uint32_t sign = signbit(y) ? al->sign_bit : 0;
+  double a = fabs(y);
+  double vmax = al->v[al->n - 1];
+  if (a >= vmax) return sign | al->code[al->n - 1];
+  int i = bracket(al, a);
+  double lo = al->v[i], hi = al->v[i + 1];
+  if (a == lo) return sign | al->code[i];
+  double t = (a - lo) * 65536.0 / (hi - lo); /* exact: hi-lo is a power of two */
+  double ft = floor(t);
+  return sign | ((double)(r16 & 0xFFFF) < ft ? al->code[i + 1] : al->code[i]);
+}
+
+uint32_t mxo_e2m1_encode_rne(double y) { ensure_tables(); return encode_rne(&g_e2m1, y); }
+uint32_t mxo_e4m3_encode_rne(double y) { ensure_tables(); return encode_rne(&g_e4m3, y); }
+uint32_t mxo_e2m1_encode_sr(double y, uint32_t r) { ensure_tables(); return encode_sr(&g_e2m1, y, r); }
+uint32_t mxo_e4m3_encode_sr(double y, uint32_t r) { ensure_tables(); return encode_sr(&g_e4m3, y, r); }
+
+/* ------------------------------------------------------------------------ */
+/* Counter-based random numbers: Philox-4x32 with 10 rounds, from [PHX].     */
+/* ------------------------------------------------------------------------ */
+static void mul32(uint32_t a, uint32_t b, uint32_t* hi, uint32_t* lo) {
+  uint64_t p = (uint64_t)a * (uint64_t)b;
+  *hi = (uint32_t)(p >> 32);
+  *lo = (uint32_t)p;
+}
+
+/* One application of the Philox S-box followed by the word permutation of
+ * the 4-word variant: the two multiplied words pass their low halves
+ * through, their high halves are xored into the other two words together
+ * with the round key.  Multipliers and Weyl key increments as published. */
+void mxo_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+  uint32_t k0 = key_in[0], k1 = key_in[1];
+  for (int round = 0; round < 10; ++round) {
+    uint32_t hi0, lo0, hi1, lo1;
+    mul32(M0, c0, &hi0, &lo0);
+    mul32(M1, c2, &hi1, &lo1);
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n1 = lo1;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    uint32_t n3 = lo0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    k0 += W0;
+    k1 += W1;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* READING (stream layout): key = (seed low word, seed high word); the random
+ * value of output element n comes from call number counter + floor(n/8),
+ * whose 128-bit counter is (low word, high word, 0, 0); the call's four
+ * words give eight 16-bit values, element n taking half (n & 1) of word
+ * (n & 7) >> 1, low half first. */
+uint32_t mxo_rand16(uint64_t seed, uint64_t counter, uint64_t n) {
+  uint64_t c = counter + (n >> 3);
+  uint32_t ctr[4] = {(uint32_t)c, (uint32_t)(c >> 32), 0u, 0u};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t w[4];
+  mxo_philox4x32_10(ctr, key, w);
+  uint32_t word = w[(n & 7) >> 1];
+  return (word >> (16 * (n & 1))) & 0xFFFFu;
+}
+
+/* READING: the 16 random signs of the Hadamard transform are the low 16 bits
+ * of word 0 of the Philox call with counter (0, 0, 0, 1), a counter that no
+ * element draw uses (element draws keep the top word 0). */
+uint32_t mxo_rht_signs(uint64_t seed) {
+  uint32_t ctr[4] = {0u, 0u, 0u, 1u};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t w[4];
+  mxo_philox4x32_10(ctr, key, w);
+  return w[0] & 0xFFFFu;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Random Hadamard transform over groups of 16 along a row.                 */
+/* READING: y = (1/4) * H16 * D * x, with H16 the Sylvester Hadamard matrix  */
+/* in natural order (entry (i,j) = (-1)^popcount(i&j)) and D the diagonal of */
+/* signs (bit j of the mask set = negate element j), the same signs for all  */
+/* groups.  Evaluated in FP32 as four butterfly stages with strides 1, 2, 4, */
+/* 8, then the 1/4 factor; the inverse runs the same stages on y, scales by  */
+/* 1/4, then reapplies the signs.  [MXF] "NVFP4" (random Hadamard transforms */
+/* to bound block outliers); [INK] "Why communication became the next        */
+/* bottleneck" (a random Hadamard rotation spreads outliers).                */
+/* ------------------------------------------------------------------------ */
+static void hadamard_stages(float v[16]) {
+  for (int h = 1; h < 16; h <<= 1) {
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+}
+
+static void rht16_group(const float* x, float* y, uint32_t mask, int inverse) {
+  float v[16];
+  if (!inverse) {
+    for (int j = 0; j < 16; ++j) v[j] = ((mask >> j) & 1) ? -x[j] : x[j];
+    hadamard_stages(v);
+    for (int j = 0; j < 16; ++j) y[j] = 0.25f * v[j];
+  } else {
+    for (int j = 0; j < 16; ++j) v[j] = x[j];
+    hadamard_stages(v);
+    for (int j = 0; j < 16; ++j) {
+      float u = 0.25f * v[j];
+      y[j] = ((mask >> j) & 1) ? -u : u;
+    }
+  }
+}
+
+/* Input element types accepted by the oracle. */
+#define MXO_IN_BF16 0
+#define MXO_IN_F32 1
+
+static float load_elem(const void* x, int dt, int64_t idx) {
+  if (dt == MXO_IN_F32) return ((const float*)x)[idx];
+  uint32_t bits = (uint32_t)((const uint16_t*)x)[idx] << 16; /* bf16 widens exactly */
+  float f;
+  memcpy(&f, &bits, 4);
+  return f;
+}
+
+/* Widen (and optionally Hadamard-rotate) one row into FP32. */
+static void load_row(const void* x, int dt, int64_t ld, int64_t r, int64_t cols,
+                     int rht, uint32_t mask, float* out) {
+  for (int64_t c = 0; c < cols; ++c) out[c] = load_elem(x, dt, r * ld + c);
+  if (rht) {
+    for (int64_t g = 0; g < cols; g += 16) {
+      float tmp[16];
+      rht16_group(out + g, tmp, mask, 0);
+      memcpy(out + g, tmp, sizeof tmp);
+    }
+  }
+}
+
+void mxo_rht16(const void* x, int xdt, float* y, int64_t rows, int64_t cols, uint32_t mask,
+               int inverse) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    float in[16];
+    for (int64_t g = 0; g < cols; g += 16) {
+      for (int j = 0; j < 16; ++j) in[j] = load_elem(x, xdt, r * cols + g + j);
+      rht16_group(in, y + r * cols + g, mask, inverse);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* MX quantization: 32 consecutive elements along a row share one E8M0      */
+/* scale ([MXF] "Microscaling", "The idea"; [MIL] "Recipe 1"; [FP4] format   */
+/* table).  A block decodes as v_i = X * P_i (X the shared scale, P_i the    */
+/* element), so elements are encoded from x_i / X ([MXF] glossary "scale    */
+/* factor": divided by before being squeezed, multiplied back after).        */
+/* READING (shared exponent): X = 2^e with e = floor(log2(max|x|)) - emax,   */
+/* emax the exponent of the element's largest power of two (E4M3: 8, E2M1:   */
+/* 2), clamped to [-127, 127]; scaled values above the element maximum       */
+/* saturate.  An all-zero block gets e = -127.  A block holding NaN or Inf   */
+/* gets the NaN scale code 0xFF and element codes 0.                         */
+/* ------------------------------------------------------------------------ */
+static void mx_encode_block(const float* v, int n, int fmt, int rnd, uint64_t seed,
+                            uint64_t counter, uint64_t n0, uint8_t* codes_row,
+                            int64_t col0, uint8_t* scale_out) {
+  const mxo_alphabet* al = (fmt == MXO_MXFP8) ? &g_e4m3 : &g_e2m1;
+  int emax = (fmt == MXO_MXFP8) ? 8 : 2;
+  double amax = 0.0;
+  int bad = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!isfinite(v[i])) bad = 1;
+    double a = fabs((double)v[i]);
+    if (a > amax) amax = a;
+  }
+  uint32_t codes[32];
+  if (bad) {
+    *scale_out = 0xFF;
+    for (int i = 0; i < n; ++i) codes[i] = 0;
+  } else {
+    int e;
+    if (amax == 0.0) {
+      e = -127;
+    } else {
+      int E;
+      frexp(amax, &E); /* amax = m * 2^E, m in [0.5, 1) -> floor(log2 amax) = E - 1 */
+      e = E - 1 - emax;
+      if (e < -127) e = -127;
+      if (e > 127) e = 127;
+    }
+    *scale_out = (uint8_t)(e + 127);
+    for (int i = 0; i < n; ++i) {
+      double y = ldexp((double)v[i], -e); /* exact */
+      codes[i] = (rnd == MXO_SR) ? encode_sr(al, y, mxo_rand16(seed, counter, n0 + i))
+                                 : encode_rne(al, y);
+    }
+  }
+  for (int i = 0; i < n; ++i) {
+    int64_t c = col0 + i;
+    if (fmt == MXO_MXFP8) {
+      codes_row[c] = (uint8_t)codes[i];
+    } else { /* READING: element 2j in the low nibble, 2j+1 in the high nibble */
+      uint8_t* b = &codes_row[c >> 1];
+      if (c & 1) *b = (uint8_t)((*b & 0x0F) | (codes[i] << 4));
+      else *b = (uint8_t)((*b & 0xF0) | codes[i]);
+    }
+  }
+}
+
+static int64_t code_row_bytes(int fmt, int64_t cols) {
+  return fmt == MXO_MXFP8 ? cols : cols / 2;
+}
+
+int mxo_quantize_mx(const void* x, int xdt, int64_t ld, int64_t rows, int64_t cols, int fmt,
+                    int rnd, uint64_t seed, uint64_t counter, int rht, uint32_t mask,
+                    uint8_t* codes, uint8_t* scales) {
+  ensure_tables();
+  if ((fmt != MXO_MXFP8 && fmt != MXO_MXFP4) || cols % 32 || (rht && cols % 16)) return -1;
+#pragma omp parallel
+  {
+    float* row = (float*)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+      load_row(x, xdt, ld, r, cols, rht, mask, row);
+      uint8_t* crow = codes + r * code_row_bytes(fmt, cols);
+      for (int64_t b = 0; b < cols / 32; ++b)
+        mx_encode_block(row + b * 32, 32, fmt, rnd, seed, counter, (uint64_t)(r * cols + b * 32),
+                        crow, b * 32, &scales[r * (cols / 32) + b]);
+    }
+    free(row);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* NVFP4: 16 E2M1 elements share one E4M3 scale, plus one FP32 scale per     */
+/* tensor that keeps the block scales in range ([MXF] "NVFP4"; [FP4] format  */
+/* table and the paragraph under it: "two-level microscaling").              */
+/* READING (all FP32, one rounding per operation, in this order):            */
+/*   T = max|x| over the tensor (or the caller's amax)                      */
+/*   T == 0: S = 1, every block scale code 0, element codes +-0.            */
+/*   S  = T / 2688            (2688 = 6 * 448: largest E2M1 x largest E4M3)  */
+/*   per 16-block: q = a_b / (6*S);  sb = E4M3 RNE of q (saturating)         */
+/*   sb decodes to 0: element codes +-0                                      */
+/*   else r = 1 / (dec(sb) * S);  y_i = x_i * r;  E2M1 (RNE or SR) of y_i.   */
+/* Stored: codes, block-scale codes, and S (a decode multiplier: x is        */
+/* recovered as e2m1 * e4m3 * S).                                            */
+/* ------------------------------------------------------------------------ */
+float mxo_tensor_amax(const void* x, int xdt, int64_t ld, int64_t rows, int64_t cols, int rht,
+                      uint32_t mask) {
+  float best = 0.0f;
+#pragma omp parallel
+  {
+    float local = 0.0f;
+    float* row = (float*)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+      load_row(x, xdt, ld, r, cols, rht, mask, row);
+      for (int64_t c = 0; c < cols; ++c) {
+        float a = fabsf(row[c]);
+        if (a > local) local = a;
+      }
+    }
+#pragma omp critical
+    if (local > best) best = local;
+    free(row);
+  }
+  return best;
+}
+
+int mxo_quantize_nvfp4(const void* x, int xdt, int64_t ld, int64_t rows, int64_t cols, int rnd,
+                       uint64_t seed, uint64_t counter, int rht, uint32_t mask,
+                       const float* amax_in, uint8_t* codes, uint8_t* scales,
+                       float* tensor_scale) {
+  ensure_tables();
+  if (cols % 16) return -1;
+  float T = amax_in ? *amax_in : mxo_tensor_amax(x, xdt, ld, rows, cols, rht, mask);
+  float S = (T == 0.0f) ? 1.0f : T / 2688.0f;
+  *tensor_scale = S;
+#pragma omp parallel
+  {
+    float* row = (float*)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+      load_row(x, xdt, ld, r, cols, rht, mask, row);
+      uint8_t* crow = codes + r * (cols / 2);
+      for (int64_t b = 0; b < cols / 16; ++b) {
+        const float* v = row + b * 16;
+        uint32_t sb = 0;
+        float rcp = 0.0f;
+        if (T != 0.0f) {
+          float ab = 0.0f;
+          for (int i = 0; i < 16; ++i) {
+            float a = fabsf(v[i]);
+            if (a > ab) ab = a;
+          }
+          float d = 6.0f * S;
+          float q = ab / d;
+          sb = encode_rne(&g_e4m3, (double)q);
+          float dsb = (float)mxo_e4m3_decode(sb);
+          if (dsb != 0.0f) {
+            float p = dsb * S;
+            rcp = 1.0f / p;
+          }
+        }
+        scales[r * (cols / 16) + b] = (uint8_t)sb;
+        for (int i = 0; i < 16; ++i) {
+          uint32_t code;
+          if (rcp == 0.0f) {
+            code = signbit(v[i]) ? 0x8u : 0x0u;
+          } else {
+            float y = v[i] * rcp;
+            uint64_t n = (uint64_t)(r * cols + b * 16 + i);
+            code = (rnd == MXO_SR) ? encode_sr(&g_e2m1, (double)y, mxo_rand16(seed, counter, n))
+                                   : encode_rne(&g_e2m1, (double)y);
+          }
+          int64_t c = b * 16 + i;
+          uint8_t* byte = &crow[c >> 1];
+          if (c & 1) *byte = (uint8_t)((*byte & 0x0F) | (code << 4));
+          else *byte = (uint8_t)((*byte & 0xF0) | code);
+        }
+      }
+    }
+    free(row);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decoding: multiply each element back by its scale(s).                     */
+/* MX: x = P * 2^(c-127).  NVFP4: x = fp32(e2m1 * e4m3 * S); the first       */
+/* product is exact, so there is one FP32 rounding.                          */
+/* ------------------------------------------------------------------------ */
+static double elem_value(int fmt, const uint8_t* codes_row, int64_t c) {
+  if (fmt == MXO_MXFP8) return mxo_e4m3_decode(codes_row[c]);
+  uint8_t b = codes_row[c >> 1];
+  return mxo_e2m1_decode((c & 1) ? (b >> 4) : (b & 0xF));
+}
+
+void mxo_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales,
+                    const float* tensor_scale, int64_t rows, int64_t cols, float* y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint8_t* crow = codes + r * code_row_bytes(fmt == MXO_NVFP4 ? MXO_MXFP4 : fmt, cols);
+    for (int64_t c = 0; c < cols; ++c) {
+      if (fmt == MXO_NVFP4) {
+        double p = elem_value(MXO_MXFP4, crow, c) *
+                   mxo_e4m3_decode(scales[r * (cols / 16) + c / 16]);
+        y[r * cols + c] = (float)p * *tensor_scale;
+      } else {
+        double p = elem_value(fmt, crow, c) * mxo_e8m0_decode(scales[r * (cols / 32) + c / 32]);
+        y[r * cols + c] = (float)p; /* exact unless it leaves the FP32 range */
+      }
+    }
+  }
+}
+
+/* FP64 values used by the GEMM oracle: the exact product of element and
+ * block scale(s), without the NVFP4 tensor scale (applied after the sum). */
+void mxo_dequantize_f64(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                        int64_t cols, double* y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint8_t* crow = codes + r * code_row_bytes(fmt == MXO_NVFP4 ? MXO_MXFP4 : fmt, cols);
+    for (int64_t c = 0; c < cols; ++c) {
+      if (fmt == MXO_NVFP4)
+        y[r * cols + c] =
+            elem_value(MXO_MXFP4, crow, c) * mxo_e4m3_decode(scales[r * (cols / 16) + c / 16]);
+      else
+        y[r * cols + c] =
+            elem_value(fmt, crow, c) * mxo_e8m0_decode(scales[r * (cols / 32) + c / 32]);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward-pass requantization ([INK] "A precision choice for each stage": */
+/* saved values are dequantized, transposed at higher precision, then        */
+/* stochastically re-quantized to MXFP8).                                    */
+/* READING: "higher precision" is FP32; the output is the transpose          */
+/* [cols, rows] in MXFP8 E4M3 with 32-blocks along its rows (the source's    */
+/* row axis); the random draw of an element is indexed by its position in    */
+/* the transposed output.  The source is an NVFP4 tensor or a BF16 matrix.   */
+/* ------------------------------------------------------------------------ */
+int mxo_requant_transpose(int src_fmt, const void* src_codes_or_bf16, const uint8_t* src_scales,
+                          const float* src_tensor_scale, int64_t rows, int64_t cols, int rnd,
+                          uint64_t seed, uint64_t counter, uint8_t* codes, uint8_t* scales) {
+  ensure_tables();
+  if (rows % 32) return -1;
+  float* xt = (float*)malloc(sizeof(float) * (size_t)(rows * cols > 0 ? rows * cols : 1));
+  if (!xt) return -2;
+  /* dequantize to FP32 and transpose */
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t c = 0; c < cols; ++c) {
+      float v;
+      if (src_fmt == MXO_NVFP4) {
+        const uint8_t* crow = (const uint8_t*)src_codes_or_bf16 + r * (cols / 2);
+        double p = elem_value(MXO_MXFP4, crow, c) *
+                   mxo_e4m3_decode(src_scales[r * (cols / 16) + c / 16]);
+        v = (float)p * *src_tensor_scale;
+      } else {
+        v = load_elem(src_codes_or_bf16, MXO_IN_BF16, r * cols + c);
+      }
+      xt[c * rows + r] = v;
+    }
+  }
+  /* MXFP8 along the new rows */
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < cols; ++r) {
+    for (int64_t b = 0; b < rows / 32; ++b)
+      mx_encode_block(xt + r * rows + b * 32, 32, MXO_MXFP8, rnd, seed, counter,
+                      (uint64_t)(r * rows + b * 32), codes + r * rows, b * 32,
+                      &scales[r * (rows / 32) + b]);
+  }
+  free(xt);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block-scaled GEMM: C[i,j] = sum_k A[i,k] * B[j,k] over the decoded        */
+/* operands, in FP64; the NVFP4 tensor scales multiply the sum at the end.   */
+/* Also returns tol[i,j] = 1e-5 * sum_k |A[i,k] * B[j,k]| (same factor).     */
+/* ([MXF] "Hardware and kernels": the block scales are applied inside the    */
+/* matrix multiply.)  Operands are given as FP64 arrays from                 */
+/* mxo_dequantize_f64; A is [M, K] and B is [N, K], both K-contiguous.       */
+/* ------------------------------------------------------------------------ */
+void mxo_gemm_f64(const double* A, const double* B, int64_t M, int64_t N, int64_t K,
+                  double post_scale, double* C, double* tol) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t j = 0; j < N; ++j) {
+      double s = 0.0, sa = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        double p = A[i * K + k] * B[j * K + k];
+        s += p;
+        sa += fabs(p);
+      }
+      C[i * N + j] = s * post_scale;
+      if (tol) tol[i * N + j] = 1e-5 * sa * fabs(post_scale);
+    }
+  }
+}
+
+/* Sampled entries of the same product (for large shapes): entry t is
+ * (rows[t], cols[t]). */
+void mxo_gemm_f64_sampled(const double* A, const double* B, int64_t K, const int64_t* ri,
+                          const int64_t* cj, int64_t count, double post_scale, double* C,
+                          double* tol) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < count; ++t) {
+    const double* a = A + ri[t] * K;
+    const double* b = B + cj[t] * K;
+    double s = 0.0, sa = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      double p = a[k] * b[k];
+      s += p;
+      sa += fabs(p);
+    }
+    C[t] = s * post_scale;
+    tol[t] = 1e-5 * sa * fabs(post_scale);
+  }
+}
+
+/* Byte counts of the stored forms ([MXF] "Microscaling": one 8-bit scale per
+ * 32 elements, MXFP4 averaging 4.25 bits; [FP4] format table: NVFP4 4 + 8/16
+ * bits plus one FP32 per tensor). */
+int64_t mxo_codes_bytes(int fmt, int64_t rows, int64_t cols) {
+  return fmt == MXO_MXFP8 ? rows * cols : rows * cols / 2;
+}
+int64_t mxo_scales_bytes(int fmt, int64_t rows, int64_t cols) {
+  return fmt == MXO_NVFP4 ? rows * cols / 16 : rows * cols / 32;
+}
+int64_t mxo_tensor_bytes(int fmt, int64_t rows, int64_t cols) {
+  return mxo_codes_bytes(fmt, rows, cols) + mxo_scales_bytes(fmt, rows, cols) +
+         (fmt == MXO_NVFP4 ? 4 : 0);
+}
