@@ -1,0 +1,212 @@
+/*
+ * mx.h -- C ABI of the block-scaled (microscaling) quantization and GEMM
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes follows these web pages (cited by title and
+ * section):
+ *   "Microscaling (MX) and block-scaled 4-bit formats"           [MXF]
+ *   "08 - FP4, MXFP4, NVFP4: The Blackwell Frontier"              [FP4]
+ *   "Thinking Machines ... Inkling 2 Small: end-to-end 4-bit training"  [INK]
+ *   "LMSYS and humans& ... MXFP8 and NVFP4 RL recipes in Miles"   [MIL]
+ *
+ * Formats (mx_format):
+ *   MX_MXFP8_E4M3  32 consecutive E4M3 elements share one E8M0 power-of-two
+ *                  scale; one-dimensional blocks along a row ([MIL] "Recipe 1:
+ *                  End-to-end MXFP8"; [MXF] "The idea").
+ *   MX_MXFP4_E2M1  32 E2M1 elements + one E8M0 scale, 4.25 bits per element
+ *                  ([MXF] "Microscaling"; [FP4] format table).
+ *   MX_NVFP4       16 E2M1 elements + one E4M3 scale, plus one FP32 scale per
+ *                  tensor ([MXF] "NVFP4"; [FP4] format table).
+ *
+ * Conventions shared by every call:
+ *   - Pointers are device pointers (HIP), except the mx_tensor descriptor
+ *     itself and the arguments documented as host values.
+ *   - Ownership: the caller allocates and frees every buffer.  The library
+ *     never allocates, frees or synchronizes.
+ *   - Execution: every call enqueues work on `stream` (NULL = the default
+ *     stream) and returns before the work has run.  Buffers must stay alive
+ *     until the stream reaches the work.  Calls are thread-safe; the library
+ *     keeps no global state.
+ *   - Errors: arguments are checked on the host before anything is enqueued
+ *     (no HIP call happens on a failed check).  A failed check returns
+ *     MX_ERR_NULL / MX_ERR_SHAPE / MX_ERR_ALIGN / MX_ERR_FORMAT /
+ *     MX_ERR_UNSUPPORTED; a failed launch returns MX_ERR_HIP.  Nothing aborts.
+ *   - Alignment: device pointers to inputs and to code/scale arrays must be
+ *     16-byte aligned and leading dimensions must keep every row 16-byte
+ *     aligned; GEMM outputs only need element alignment.
+ */
+#ifndef MX_H_
+#define MX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t* mx_stream;
+
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_NULL = 1,        /* a required pointer is NULL */
+  MX_ERR_SHAPE = 2,       /* sizes inconsistent or not a multiple of the block */
+  MX_ERR_ALIGN = 3,       /* pointer or leading dimension misaligned */
+  MX_ERR_FORMAT = 4,      /* unknown format, dtype or rounding mode */
+  MX_ERR_UNSUPPORTED = 5, /* valid values in a combination the library does not offer */
+  MX_ERR_HIP = 6          /* the HIP runtime rejected a launch */
+} mx_status;
+
+typedef enum { MX_MXFP8_E4M3 = 1, MX_MXFP4_E2M1 = 2, MX_NVFP4 = 3 } mx_format;
+
+/* Rounding of elements: round-to-nearest, ties to the even code, or
+ * stochastic rounding ([MXF] "Open points"; glossary "stochastic rounding";
+ * [INK] "A precision choice for each stage").  Out-of-range elements
+ * saturate to the largest finite value under both modes. */
+typedef enum { MX_RNE = 0, MX_SR = 1 } mx_round;
+
+typedef enum { MX_BF16 = 0, MX_F32 = 1 } mx_dtype;
+
+/* Counter-based random stream for stochastic rounding (host struct, passed by
+ * value).  Output element n (row-major linear index in the *output* tensor)
+ * uses 16 bits of Philox-4x32-10 (Salmon et al., SC'11) with key = seed and
+ * counter = (counter + n/8) in the low two words, so results are a pure
+ * function of (input, seed, counter).  A caller that wants disjoint streams
+ * advances `counter` by ceil(numel / 8) per call. */
+typedef struct {
+  uint64_t seed;
+  uint64_t counter;
+} mx_rng;
+
+/* One quantized matrix, logical shape [rows, cols], blocks along cols.
+ * (host struct; the pointers inside are device pointers)
+ *   codes   MXFP8: uint8 [rows, cols], one E4M3 code per element.
+ *           FP4 formats: uint8 [rows, cols/2], element 2j in the low nibble
+ *           and element 2j+1 in the high nibble of byte j.
+ *   scales  uint8 [rows, cols/32] E8M0 codes (MX formats) or
+ *           uint8 [rows, cols/16] E4M3 codes (NVFP4), row-major.
+ *   tensor_scale  NVFP4 only: FP32 S, the per-tensor decode multiplier
+ *           (x ~ e2m1 * e4m3 * S); NULL for MX formats.  For the stacked
+ *           weights of mx_gemm_grouped it points to one S per group.
+ * Rows are dense: the row pitch is cols (or cols/2) bytes. */
+typedef struct {
+  int32_t fmt; /* mx_format */
+  int32_t reserved;
+  int64_t rows;
+  int64_t cols;
+  void* codes;
+  uint8_t* scales;
+  float* tensor_scale;
+} mx_tensor;
+
+#define MX_FLAG_RHT16 1u      /* apply the 16-point random Hadamard transform first */
+#define MX_FLAG_AMAX_GIVEN 2u /* NVFP4: *amax already holds max|x| (after RHT if set) */
+
+/* Bytes of the code and scale arrays of a [rows, cols] tensor ([MXF]
+ * "Microscaling": 8 bits per 32 elements; [FP4] format table).  Returns 0 for
+ * an invalid format.  Host function, no device work. */
+size_t mx_codes_bytes(int32_t fmt, int64_t rows, int64_t cols);
+size_t mx_scales_bytes(int32_t fmt, int64_t rows, int64_t cols);
+
+/* 16 random signs of the Hadamard transform for a seed: bit j set = negate
+ * element j of every 16-group.  Taken from Philox-4x32-10 with key = seed and
+ * counter (0, 0, 0, 1), a counter no element draw uses.  Host function. */
+uint16_t mx_rht_signs(uint64_t seed);
+
+/* Quantize x [rows, cols] (row pitch ld_x elements, dtype xdt) along cols
+ * into `out` (fmt, rows, cols and pointers filled in by the caller).
+ *
+ * MX formats ([MXF] "Microscaling", "The idea"): per 32-block, the shared
+ * scale is X = 2^e with e = floor(log2 max|x|) - emax (emax = 8 for E4M3, 2
+ * for E2M1), clamped to [-127, 127]; an all-zero block gets e = -127; a block
+ * holding NaN or Inf gets the NaN scale code 0xFF and element codes 0.
+ * Elements are x / X rounded (rnd) and saturated.
+ *
+ * NVFP4 ([MXF] "NVFP4"; [FP4] format table): T = max|x| over the tensor,
+ * S = T / 2688 (S = 1 when T = 0); per 16-block sb = E4M3 round-to-nearest of
+ * max|x| / (6 S); elements x * (1 / (dec(sb) * S)) rounded to E2M1 (rnd);
+ * blocks whose sb decodes to 0 store +-0.  All steps are FP32, one rounding
+ * each, in that order.  `amax` (device, one float) is required: with
+ * MX_FLAG_AMAX_GIVEN it is read, otherwise T is computed into it first (two
+ * passes over x).  Inputs must be finite.
+ *
+ * MX_FLAG_RHT16 ([MXF] "NVFP4": random Hadamard transforms bound block
+ * outliers): each 16-group of a row is first mapped to
+ * y = (1/4) H16 D x in FP32 (see mx_hadamard16) and y is quantized.
+ *
+ * Requirements: cols % 32 == 0 (MX) or % 16 == 0 (NVFP4); out->rows == rows.
+ * SR stream: see mx_rng. */
+mx_status mx_quantize(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ld_x,
+                      const mx_tensor* out, int32_t rnd, mx_rng rng, uint32_t flags,
+                      uint16_t rht_sign_mask, float* amax, mx_stream stream);
+
+/* Per-tensor amax of x (after the Hadamard transform when MX_FLAG_RHT16 is
+ * set) into *amax (device float, overwritten).  The first pass of NVFP4
+ * quantization ([MXF] "NVFP4": second-level per-tensor scale). */
+mx_status mx_amax(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ld_x,
+                  uint32_t flags, uint16_t rht_sign_mask, float* amax, mx_stream stream);
+
+/* Decode `in` into y [rows, cols] (row pitch ld_y, dtype ydt): MX elements
+ * times 2^(c-127); NVFP4 as fp32(e2m1 * e4m3 * S) ([MXF] glossary "scale
+ * factor": multiplied back after).  With MX_FLAG_RHT16 the inverse Hadamard
+ * transform (same signs) is applied to the FP32 values before output.  BF16
+ * output rounds to nearest even. */
+mx_status mx_dequantize(const mx_tensor* in, void* y, int32_t ydt, int64_t ld_y, uint32_t flags,
+                        uint16_t rht_sign_mask, mx_stream stream);
+
+/* Backward-pass requantization ([INK] "A precision choice for each stage":
+ * dequantize saved values, transpose at higher precision, stochastically
+ * re-quantize to MXFP8).  Source [rows, cols]: either an NVFP4 tensor `src`
+ * (x = fp32(e2m1 * e4m3 * S)) or a BF16 matrix x_bf16 with row pitch ld_x
+ * (exactly one of the two is non-NULL).  Output `out`: MXFP8 E4M3 of the
+ * transpose, logical [cols, rows], 32-blocks along its rows (the source row
+ * axis).  The SR index of an element is its position in the output.
+ * Requirements: rows % 32 == 0, cols % 16 == 0, out->fmt == MX_MXFP8_E4M3. */
+mx_status mx_requant_transpose(const mx_tensor* src, const void* x_bf16, int64_t ld_x,
+                               int64_t rows, int64_t cols, const mx_tensor* out, int32_t rnd,
+                               mx_rng rng, mx_stream stream);
+
+/* Standalone 16-point random Hadamard transform along rows of x [rows, cols]
+ * (dense rows): y = (1/4) H16 D x per 16-group, H16 the Sylvester Hadamard
+ * matrix in natural order, D = diag of the signs in sign_mask, evaluated in
+ * FP32 as butterfly stages of stride 1, 2, 4, 8.  inverse != 0 applies the
+ * stages, the 1/4 factor, then the signs (x = D H16 y / 4).  ([MXF] "NVFP4";
+ * [INK] "Why communication became the next bottleneck".)  cols % 16 == 0;
+ * x and y may not overlap unless x == y with xdt == ydt. */
+mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_t rows,
+                        int64_t cols, uint16_t sign_mask, int32_t inverse, mx_stream stream);
+
+/* Block-scaled GEMM C = A * B^T ([MXF] "Hardware and kernels": the block
+ * scales are applied inside the matrix multiply).  A is [M, K], B is [N, K]
+ * (both quantized along K), C is [M, N] row-major with row pitch ldc in
+ * dtype cdt (FP32, or BF16 rounded to nearest even).  MX operands use the
+ * scaled FP8/FP4 matrix instructions; NVFP4 operands apply their E4M3 block
+ * scales explicitly and multiply the FP32 result by S_A * S_B.
+ * Requirements: A->fmt == B->fmt; A->cols == B->cols == K; K % 32 == 0. */
+mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,
+                  mx_stream stream);
+
+/* Grouped NVFP4 GEMM for a mixture-of-experts forward pass ([MXF] "NVFP4";
+ * [INK] "A precision choice for each stage": NVFP4 forward in the expert
+ * layers).  B stacks num_groups expert matrices [N, K] as one NVFP4 tensor of
+ * rows = num_groups * N whose tensor_scale points to num_groups floats.
+ * group_offsets (device, int64 [num_groups + 1], non-decreasing, first 0, last
+ * = number of routed rows R) assigns output rows [off[e], off[e+1]) to expert
+ * e.  A row source: if row_index is non-NULL (device int32 [R]), routed row r
+ * reads A row row_index[r] (A is [tokens, K]); otherwise A has R rows.
+ * C is [R, N] (pitch ldc).  C[r, :] = A[src(r)] * B_e^T * S_A * S_B[e].
+ * Requirements: A and B NVFP4, K % 32 == 0, num_groups >= 1, `routed_rows`
+ * (host) = R, B->rows % num_groups == 0. */
+mx_status mx_gemm_grouped(const mx_tensor* A, const int32_t* row_index, int64_t routed_rows,
+                          const mx_tensor* B, int32_t num_groups, const int64_t* group_offsets,
+                          void* C, int32_t cdt, int64_t ldc, mx_stream stream);
+
+/* Human-readable name of a status code (static string). */
+const char* mx_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX_H_ */

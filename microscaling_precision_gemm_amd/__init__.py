@@ -1,0 +1,225 @@
+"""Python binding of libmx (block-scaled quantization and GEMM for MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/mx.h``.  PyTorch provides
+device memory and streams.  The functions keep the C names; tensors are
+torch CUDA (HIP) tensors, results are written into caller-provided or newly
+allocated torch buffers.  There is no CPU fallback: if ``libmx.so`` is not
+built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmx.so")
+
+MX_MXFP8_E4M3, MX_MXFP4_E2M1, MX_NVFP4 = 1, 2, 3
+MX_RNE, MX_SR = 0, 1
+MX_BF16, MX_F32 = 0, 1
+MX_FLAG_RHT16, MX_FLAG_AMAX_GIVEN = 1, 2
+
+FORMATS = {"mxfp8": MX_MXFP8_E4M3, "mxfp4": MX_MXFP4_E2M1, "nvfp4": MX_NVFP4}
+
+# every function declared in include/mx.h
+EXPORTED = [
+    "mx_codes_bytes", "mx_scales_bytes", "mx_rht_signs", "mx_quantize", "mx_amax",
+    "mx_dequantize", "mx_requant_transpose", "mx_hadamard16", "mx_gemm", "mx_gemm_grouped",
+    "mx_status_string",
+]
+
+
+class MXError(RuntimeError):
+    pass
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("reserved", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p)]
+
+
+class _Rng(ctypes.Structure):
+    _fields_ = [("seed", ctypes.c_uint64), ("counter", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def load():
+    """Load libmx.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MXError(f"{LIB_PATH} is not built; run microscaling_precision_gemm_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u32, u64, u16 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                   ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint16)
+    TP = ctypes.POINTER(_Tensor)
+    sig = {
+        "mx_codes_bytes": (ctypes.c_size_t, [i32, i64, i64]),
+        "mx_scales_bytes": (ctypes.c_size_t, [i32, i64, i64]),
+        "mx_rht_signs": (u16, [u64]),
+        "mx_quantize": (i32, [vp, i32, i64, i64, i64, TP, i32, _Rng, u32, u16, vp, vp]),
+        "mx_amax": (i32, [vp, i32, i64, i64, i64, u32, u16, vp, vp]),
+        "mx_dequantize": (i32, [TP, vp, i32, i64, u32, u16, vp]),
+        "mx_requant_transpose": (i32, [TP, vp, i64, i64, i64, TP, i32, _Rng, vp]),
+        "mx_hadamard16": (i32, [vp, i32, vp, i32, i64, i64, u16, i32, vp]),
+        "mx_gemm": (i32, [TP, TP, vp, i32, i64, vp]),
+        "mx_gemm_grouped": (i32, [TP, vp, i64, TP, i32, vp, vp, i32, i64, vp]),
+        "mx_status_string": (ctypes.c_char_p, [i32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise MXError(f"libmx: {load().mx_status_string(status).decode()} (status {status})")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return MX_BF16
+    if t.dtype == torch.float32:
+        return MX_F32
+    raise MXError(f"unsupported dtype {t.dtype}")
+
+
+class MXTensor:
+    """A quantized [rows, cols] matrix: codes, block scales and (NVFP4) the
+    per-tensor scale, as torch uint8 / float32 device tensors."""
+
+    def __init__(self, fmt: int, rows: int, cols: int, codes, scales, tensor_scale=None):
+        self.fmt, self.rows, self.cols = int(fmt), int(rows), int(cols)
+        self.codes, self.scales, self.tensor_scale = codes, scales, tensor_scale
+
+    def desc(self) -> _Tensor:
+        return _Tensor(self.fmt, 0, self.rows, self.cols, _ptr(self.codes), _ptr(self.scales),
+                       _ptr(self.tensor_scale))
+
+    def view_rows(self, r0: int, r1: int, tensor_scale=None) -> "MXTensor":
+        """Rows [r0, r1) as a tensor sharing storage."""
+        return MXTensor(self.fmt, r1 - r0, self.cols, self.codes[r0:r1], self.scales[r0:r1],
+                        tensor_scale if tensor_scale is not None else self.tensor_scale)
+
+
+def empty(fmt: int, rows: int, cols: int, device="cuda", n_tensor_scales: int = 1) -> MXTensor:
+    """Allocate the buffers of a quantized [rows, cols] tensor."""
+    torch = _torch()
+    L = load()
+    cb = L.mx_codes_bytes(fmt, rows, cols)
+    sb = L.mx_scales_bytes(fmt, rows, cols)
+    codes = torch.empty((rows, cb // max(rows, 1)), dtype=torch.uint8, device=device)
+    scales = torch.empty((rows, sb // max(rows, 1)), dtype=torch.uint8, device=device)
+    ts = torch.empty(n_tensor_scales, dtype=torch.float32, device=device) if fmt == MX_NVFP4 else None
+    return MXTensor(fmt, rows, cols, codes, scales, ts)
+
+
+def mx_codes_bytes(fmt: int, rows: int, cols: int) -> int:
+    return int(load().mx_codes_bytes(fmt, rows, cols))
+
+
+def mx_scales_bytes(fmt: int, rows: int, cols: int) -> int:
+    return int(load().mx_scales_bytes(fmt, rows, cols))
+
+
+def mx_rht_signs(seed: int) -> int:
+    return int(load().mx_rht_signs(seed))
+
+
+def mx_quantize(x, out: MXTensor, rnd: int = MX_RNE, seed: int = 0, counter: int = 0,
+                flags: int = 0, sign_mask: int = 0, amax=None, stream=None) -> MXTensor:
+    """Quantize x [rows, cols] (bf16 or fp32, row pitch x.stride(0)) into `out`.
+    NVFP4 needs `amax` (a 1-element fp32 device tensor): read when
+    MX_FLAG_AMAX_GIVEN is set, else computed into it."""
+    L = load()
+    d = out.desc()
+    _check(L.mx_quantize(_ptr(x), _dt(x), x.shape[0], x.shape[1], x.stride(0), ctypes.byref(d),
+                         rnd, _Rng(seed, counter), flags, sign_mask, _ptr(amax), _stream(stream)))
+    return out
+
+
+def mx_amax(x, amax, flags: int = 0, sign_mask: int = 0, stream=None):
+    L = load()
+    _check(L.mx_amax(_ptr(x), _dt(x), x.shape[0], x.shape[1], x.stride(0), flags, sign_mask,
+                     _ptr(amax), _stream(stream)))
+    return amax
+
+
+def mx_dequantize(t: MXTensor, y, flags: int = 0, sign_mask: int = 0, stream=None):
+    L = load()
+    d = t.desc()
+    _check(L.mx_dequantize(ctypes.byref(d), _ptr(y), _dt(y), y.stride(0), flags, sign_mask,
+                           _stream(stream)))
+    return y
+
+
+def mx_requant_transpose(out: MXTensor, src: MXTensor | None = None, x_bf16=None,
+                         rnd: int = MX_SR, seed: int = 0, counter: int = 0, stream=None):
+    """Source [rows, cols] (NVFP4 `src` or bf16 `x_bf16`) -> MXFP8 `out` of
+    shape [cols, rows]."""
+    L = load()
+    sdesc = None
+    if src is not None:
+        rows, cols = src.rows, src.cols
+        sdesc = src.desc()
+        sd = ctypes.byref(sdesc)
+        xp, ld = None, 0
+    else:
+        rows, cols = x_bf16.shape
+        sd = None
+        xp, ld = _ptr(x_bf16), x_bf16.stride(0)
+    od = out.desc()
+    _check(L.mx_requant_transpose(sd, xp, ld, rows, cols, ctypes.byref(od), rnd,
+                                  _Rng(seed, counter), _stream(stream)))
+    return out
+
+
+def mx_hadamard16(x, y, sign_mask: int, inverse: bool = False, stream=None):
+    L = load()
+    _check(L.mx_hadamard16(_ptr(x), _dt(x), _ptr(y), _dt(y), x.shape[0], x.shape[1], sign_mask,
+                           int(inverse), _stream(stream)))
+    return y
+
+
+def mx_gemm(A: MXTensor, B: MXTensor, C, stream=None):
+    """C [M, N] (fp32 or bf16, row pitch C.stride(0)) = A [M, K] * B [N, K]^T."""
+    L = load()
+    da, db = A.desc(), B.desc()
+    _check(L.mx_gemm(ctypes.byref(da), ctypes.byref(db), _ptr(C), _dt(C), C.stride(0),
+                     _stream(stream)))
+    return C
+
+
+def mx_gemm_grouped(A: MXTensor, row_index, routed_rows: int, B: MXTensor, num_groups: int,
+                    group_offsets, C, stream=None):
+    L = load()
+    da, db = A.desc(), B.desc()
+    _check(L.mx_gemm_grouped(ctypes.byref(da), _ptr(row_index), routed_rows, ctypes.byref(db),
+                             num_groups, _ptr(group_offsets), _ptr(C), _dt(C), C.stride(0),
+                             _stream(stream)))
+    return C

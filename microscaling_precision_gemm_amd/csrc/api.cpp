@@ -1,0 +1,244 @@
+// api.cpp -- the C ABI declared in include/mx.h: argument checks (no HIP call
+// before they pass), dispatch to the kernel launchers, status mapping.
+#include "../../include/mx.h"
+
+#include <hip/hip_runtime.h>
+
+#include "device/codec.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_fmt(int32_t f) { return f == MX_MXFP8_E4M3 || f == MX_MXFP4_E2M1 || f == MX_NVFP4; }
+bool valid_dt(int32_t d) { return d == MX_BF16 || d == MX_F32; }
+int64_t dt_bytes(int32_t d) { return d == MX_BF16 ? 2 : 4; }
+int64_t block_of(int32_t f) { return f == MX_NVFP4 ? 16 : 32; }
+
+mx_status hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+
+// Checks the descriptor of a quantized tensor of logical shape [rows, cols].
+mx_status check_tensor(const mx_tensor* t, int64_t rows, int64_t cols) {
+  if (!t) return MX_ERR_NULL;
+  if (!valid_fmt(t->fmt)) return MX_ERR_FORMAT;
+  if (t->rows != rows || t->cols != cols || rows < 0 || cols < 0) return MX_ERR_SHAPE;
+  if (cols % block_of(t->fmt)) return MX_ERR_SHAPE;
+  if (rows * cols > 0) {
+    if (!t->codes || !t->scales) return MX_ERR_NULL;
+    if (!aligned16(t->codes) || !aligned16(t->scales)) return MX_ERR_ALIGN;
+  }
+  if (t->fmt == MX_NVFP4) {
+    if (!t->tensor_scale) return MX_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(t->tensor_scale) & 3u) return MX_ERR_ALIGN;
+  }
+  return MX_OK;
+}
+
+// Output matrices written element by element only need element alignment.
+mx_status check_output(const void* p, int32_t dt, int64_t rows, int64_t cols, int64_t ld) {
+  if (!valid_dt(dt)) return MX_ERR_FORMAT;
+  if (rows < 0 || cols < 0 || ld < cols) return MX_ERR_SHAPE;
+  if (rows * cols == 0) return MX_OK;
+  if (!p) return MX_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(p) % dt_bytes(dt)) return MX_ERR_ALIGN;
+  return MX_OK;
+}
+
+mx_status check_matrix(const void* p, int32_t dt, int64_t rows, int64_t cols, int64_t ld) {
+  if (!valid_dt(dt)) return MX_ERR_FORMAT;
+  if (rows < 0 || cols < 0 || ld < cols) return MX_ERR_SHAPE;
+  if (rows * cols == 0) return MX_OK;
+  if (!p) return MX_ERR_NULL;
+  if (!aligned16(p) || (ld * dt_bytes(dt)) % 16) return MX_ERR_ALIGN;
+  return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mx_codes_bytes(int32_t fmt, int64_t rows, int64_t cols) {
+  if (!valid_fmt(fmt) || rows < 0 || cols < 0) return 0;
+  return (size_t)(fmt == MX_MXFP8_E4M3 ? rows * cols : rows * cols / 2);
+}
+
+size_t mx_scales_bytes(int32_t fmt, int64_t rows, int64_t cols) {
+  if (!valid_fmt(fmt) || rows < 0 || cols < 0) return 0;
+  return (size_t)(rows * (cols / block_of(fmt)));
+}
+
+uint16_t mx_rht_signs(uint64_t seed) {
+  mxk::u32x4 w = mxk::philox4x32_10(0u, 0u, 0u, 1u, (uint32_t)seed, (uint32_t)(seed >> 32));
+  return (uint16_t)(w.x & 0xFFFFu);
+}
+
+const char* mx_status_string(int32_t s) {
+  switch (s) {
+    case MX_OK: return "ok";
+    case MX_ERR_NULL: return "required pointer is NULL";
+    case MX_ERR_SHAPE: return "inconsistent or unsupported shape";
+    case MX_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case MX_ERR_FORMAT: return "unknown format, dtype or rounding mode";
+    case MX_ERR_UNSUPPORTED: return "unsupported combination";
+    case MX_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+mx_status mx_quantize(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ld_x,
+                      const mx_tensor* out, int32_t rnd, mx_rng rng, uint32_t flags,
+                      uint16_t rht_sign_mask, float* amax, mx_stream stream) {
+  if (!out) return MX_ERR_NULL;
+  if (rnd != MX_RNE && rnd != MX_SR) return MX_ERR_FORMAT;
+  if (flags & ~(MX_FLAG_RHT16 | MX_FLAG_AMAX_GIVEN)) return MX_ERR_UNSUPPORTED;
+  mx_status st = check_matrix(x, xdt, rows, cols, ld_x);
+  if (st != MX_OK) return st;
+  st = check_tensor(out, rows, cols);
+  if (st != MX_OK) return st;
+  if (out->fmt == MX_NVFP4) {
+    if (!amax) return MX_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(amax) & 3u) return MX_ERR_ALIGN;
+  } else if (flags & MX_FLAG_AMAX_GIVEN) {
+    return MX_ERR_UNSUPPORTED;
+  }
+  if (rows * cols == 0 && out->fmt != MX_NVFP4) return MX_OK;
+  mxk::QuantArgs a;
+  a.x = x;
+  a.xdt = xdt;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld_x = ld_x;
+  a.fmt = out->fmt;
+  a.codes = static_cast<uint8_t*>(out->codes);
+  a.scales = out->scales;
+  a.tensor_scale = out->tensor_scale;
+  a.amax = amax;
+  a.sr = rnd == MX_SR;
+  a.seed = rng.seed;
+  a.counter = rng.counter;
+  a.rht = (flags & MX_FLAG_RHT16) != 0;
+  a.sign_mask = rht_sign_mask;
+  a.amax_given = (flags & MX_FLAG_AMAX_GIVEN) != 0;
+  return hip_status(mxk::launch_quantize(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_amax(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ld_x,
+                  uint32_t flags, uint16_t rht_sign_mask, float* amax, mx_stream stream) {
+  if (flags & ~MX_FLAG_RHT16) return MX_ERR_UNSUPPORTED;
+  mx_status st = check_matrix(x, xdt, rows, cols, ld_x);
+  if (st != MX_OK) return st;
+  if (!amax) return MX_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(amax) & 3u) return MX_ERR_ALIGN;
+  if (cols % 16) return MX_ERR_SHAPE;
+  return hip_status(mxk::launch_amax(x, xdt, rows, cols, ld_x, (flags & MX_FLAG_RHT16) != 0,
+                                     rht_sign_mask, amax, reinterpret_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_dequantize(const mx_tensor* in, void* y, int32_t ydt, int64_t ld_y, uint32_t flags,
+                        uint16_t rht_sign_mask, mx_stream stream) {
+  if (!in) return MX_ERR_NULL;
+  if (flags & ~MX_FLAG_RHT16) return MX_ERR_UNSUPPORTED;
+  mx_status st = check_tensor(in, in->rows, in->cols);
+  if (st != MX_OK) return st;
+  st = check_matrix(y, ydt, in->rows, in->cols, ld_y);
+  if (st != MX_OK) return st;
+  if (in->rows * in->cols == 0) return MX_OK;
+  return hip_status(mxk::launch_dequantize(in->fmt, static_cast<const uint8_t*>(in->codes),
+                                           in->scales, in->tensor_scale, in->rows, in->cols, y,
+                                           ydt, ld_y, (flags & MX_FLAG_RHT16) != 0, rht_sign_mask,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_requant_transpose(const mx_tensor* src, const void* x_bf16, int64_t ld_x,
+                               int64_t rows, int64_t cols, const mx_tensor* out, int32_t rnd,
+                               mx_rng rng, mx_stream stream) {
+  if (!out) return MX_ERR_NULL;
+  if ((src == nullptr) == (x_bf16 == nullptr)) return MX_ERR_NULL;
+  if (rnd != MX_RNE && rnd != MX_SR) return MX_ERR_FORMAT;
+  if (rows < 0 || cols < 0) return MX_ERR_SHAPE;
+  if (rows % 32 || cols % 16) return MX_ERR_SHAPE;
+  if (src) {
+    mx_status st = check_tensor(src, rows, cols);
+    if (st != MX_OK) return st;
+    if (src->fmt != MX_NVFP4) return MX_ERR_UNSUPPORTED;
+  } else {
+    mx_status st = check_matrix(x_bf16, MX_BF16, rows, cols, ld_x);
+    if (st != MX_OK) return st;
+  }
+  mx_status st = check_tensor(out, cols, rows);
+  if (st != MX_OK) return st;
+  if (out->fmt != MX_MXFP8_E4M3) return MX_ERR_UNSUPPORTED;
+  if (rows * cols == 0) return MX_OK;
+  return hip_status(mxk::launch_requant_transpose(
+      src ? static_cast<const uint8_t*>(src->codes) : nullptr, src ? src->scales : nullptr,
+      src ? src->tensor_scale : nullptr, static_cast<const uint16_t*>(x_bf16), ld_x, rows, cols,
+      static_cast<uint8_t*>(out->codes), out->scales, rnd == MX_SR, rng.seed, rng.counter,
+      reinterpret_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_t rows,
+                        int64_t cols, uint16_t sign_mask, int32_t inverse, mx_stream stream) {
+  mx_status st = check_matrix(x, xdt, rows, cols, cols);
+  if (st != MX_OK) return st;
+  st = check_matrix(y, ydt, rows, cols, cols);
+  if (st != MX_OK) return st;
+  if (cols % 16) return MX_ERR_SHAPE;
+  if (rows * cols == 0) return MX_OK;
+  if (x == y && xdt != ydt) return MX_ERR_UNSUPPORTED;
+  return hip_status(mxk::launch_hadamard16(x, xdt, y, ydt, rows, cols, sign_mask, inverse != 0,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,
+                  mx_stream stream) {
+  if (!A || !B) return MX_ERR_NULL;
+  mx_status st = check_tensor(A, A->rows, A->cols);
+  if (st != MX_OK) return st;
+  st = check_tensor(B, B->rows, B->cols);
+  if (st != MX_OK) return st;
+  if (A->fmt != B->fmt) return MX_ERR_UNSUPPORTED;
+  if (A->cols != B->cols || A->cols % 32) return MX_ERR_SHAPE;
+  const int64_t M = A->rows, N = B->rows, K = A->cols;
+  st = check_output(C, cdt, M, N, ldc);
+  if (st != MX_OK) return st;
+  if (M * N == 0) return MX_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (A->fmt == MX_NVFP4) {
+    // one group covering all rows; offsets are not needed on the device for
+    // a single group, so the plain GEMM is the grouped kernel with R = M.
+    return hip_status(mxk::launch_gemm_nvfp4(
+        static_cast<const uint8_t*>(A->codes), A->scales, A->tensor_scale, nullptr, M,
+        static_cast<const uint8_t*>(B->codes), B->scales, B->tensor_scale, 1, nullptr, N, K, C,
+        cdt, ldc, s));
+  }
+  return hip_status(mxk::launch_gemm_mx(A->fmt, static_cast<const uint8_t*>(A->codes), A->scales,
+                                        static_cast<const uint8_t*>(B->codes), B->scales, M, N, K,
+                                        C, cdt, ldc, s));
+}
+
+mx_status mx_gemm_grouped(const mx_tensor* A, const int32_t* row_index, int64_t routed_rows,
+                          const mx_tensor* B, int32_t num_groups, const int64_t* group_offsets,
+                          void* C, int32_t cdt, int64_t ldc, mx_stream stream) {
+  if (!A || !B) return MX_ERR_NULL;
+  if (num_groups < 1) return MX_ERR_SHAPE;
+  mx_status st = check_tensor(A, A->rows, A->cols);
+  if (st != MX_OK) return st;
+  st = check_tensor(B, B->rows, B->cols);
+  if (st != MX_OK) return st;
+  if (A->fmt != MX_NVFP4 || B->fmt != MX_NVFP4) return MX_ERR_UNSUPPORTED;
+  if (A->cols != B->cols || A->cols % 32) return MX_ERR_SHAPE;
+  if (B->rows % num_groups) return MX_ERR_SHAPE;
+  if (routed_rows < 0) return MX_ERR_SHAPE;
+  if (!row_index && routed_rows != A->rows) return MX_ERR_SHAPE;
+  if (!group_offsets) return MX_ERR_NULL;
+  const int64_t N = B->rows / num_groups, K = A->cols;
+  st = check_output(C, cdt, routed_rows, N, ldc);
+  if (st != MX_OK) return st;
+  if (routed_rows * N == 0) return MX_OK;
+  return hip_status(mxk::launch_gemm_nvfp4(
+      static_cast<const uint8_t*>(A->codes), A->scales, A->tensor_scale, row_index, routed_rows,
+      static_cast<const uint8_t*>(B->codes), B->scales, B->tensor_scale, num_groups,
+      group_offsets, N, K, C, cdt, ldc, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+// codec.h -- element/scale encoders and decoders and the counter-based RNG
+// used by the gfx950 kernels.  Everything here is __host__ __device__ and free
+// of GPU builtins so the same source can be checked exhaustively on the host.
+//
+// Formats ("Microscaling (MX) and block-scaled 4-bit formats", sections "The
+// problem", "Microscaling", "NVFP4"; "08 - FP4, MXFP4, NVFP4: The Blackwell
+// Frontier", "Why 4-bit floats at all?" and the MXFP4/NVFP4 table):
+//   E2M1 (S E E M): 0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives;
+//   E4M3 (OCP "FN" reading: bias 7, no Inf, 0x7F/0xFF NaN, max 448);
+//   E8M0: 2^(c-127), 0xFF NaN.
+//
+// Encoders work on the FP32 bit pattern of |y|: the kept mantissa bits are the
+// top bits of the FP32 mantissa (normal range) or an integer multiple of the
+// subnormal step (subnormal range).
+//   RNE: round to nearest, ties to the even code; saturate at the largest
+//        finite value.
+//   SR:  with lo <= |y| < hi the neighbours and r a 16-bit random value,
+//        round up exactly when r < floor((|y| - lo) * 2^16 / (hi - lo)); the
+//        probability of rounding up is proportional to the distance from lo
+//        (glossary "stochastic rounding"; "Thinking Machines ... Inkling 2
+//        Small", "A precision choice for each stage").  In the normal range
+//        that floor is the discarded mantissa bits shifted right.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxk {
+
+__host__ __device__ inline uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__host__ __device__ inline float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// ---- E4M3 ---------------------------------------------------------------
+// magnitude code of a (a >= 0, not NaN)
+__host__ __device__ inline uint32_t e4m3_rne_mag(float a) {
+  if (a >= 448.0f) return 0x7Eu;
+  if (a < 0.015625f) return (uint32_t)rintf(a * 512.0f);  // multiples of 2^-9; 8 = 2^-6
+  uint32_t b = f2u(a);
+  b += 0x7FFFFu + ((b >> 20) & 1u);
+  return (b >> 20) - (120u << 3);
+}
+
+__host__ __device__ inline uint32_t e4m3_sr_mag(float a, uint32_t r16) {
+  if (a >= 448.0f) return 0x7Eu;
+  if (a < 0.015625f) {
+    float s = a * 512.0f;  // exact
+    float m = floorf(s);
+    uint32_t t = (uint32_t)((s - m) * 65536.0f);  // exact, floor of a positive value
+    return (uint32_t)m + (r16 < t ? 1u : 0u);
+  }
+  uint32_t b = f2u(a);
+  uint32_t t = (b & 0xFFFFFu) >> 4;
+  return (b >> 20) - (120u << 3) + (r16 < t ? 1u : 0u);
+}
+
+// exact FP32 value of an E4M3 magnitude code (c in 0..0x7E)
+__host__ __device__ inline float e4m3_mag_value(uint32_t c) {
+  if (c < 8u) return (float)c * 0.001953125f;  // m * 2^-9
+  return u2f((((c >> 3) + 120u) << 23) | ((c & 7u) << 20));
+}
+
+// ---- E2M1 ---------------------------------------------------------------
+__host__ __device__ inline uint32_t e2m1_rne_mag(float a) {
+  if (a >= 6.0f) return 7u;
+  if (a < 1.0f) return (uint32_t)rintf(a * 2.0f);  // 0, 0.5, 1.0 -> codes 0, 1, 2
+  uint32_t b = f2u(a);
+  b += 0x1FFFFFu + ((b >> 22) & 1u);
+  uint32_t c = (b >> 22) - 252u;
+  return c > 7u ? 7u : c;
+}
+
+__host__ __device__ inline uint32_t e2m1_sr_mag(float a, uint32_t r16) {
+  if (a >= 6.0f) return 7u;
+  if (a < 1.0f) {
+    float s = a * 2.0f;
+    float m = floorf(s);
+    uint32_t t = (uint32_t)((s - m) * 65536.0f);
+    return (uint32_t)m + (r16 < t ? 1u : 0u);
+  }
+  uint32_t b = f2u(a);
+  uint32_t t = (b & 0x3FFFFFu) >> 6;
+  return (b >> 22) - 252u + (r16 < t ? 1u : 0u);
+}
+
+__host__ __device__ inline float e2m1_value(uint32_t c) {
+  // magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 encoded as (exponent, mantissa)
+  uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  float mag = e == 0 ? 0.5f * (float)m : u2f(((e + 126u) << 23) | (m << 22));
+  return (c & 8u) ? -mag : mag;
+}
+
+// Sign-carrying encoders for a signed FP32 y.
+__host__ __device__ inline uint32_t e4m3_encode(float y, bool sr, uint32_t r16) {
+  uint32_t s = (f2u(y) >> 24) & 0x80u;
+  float a = __builtin_fabsf(y);
+  return s | (sr ? e4m3_sr_mag(a, r16) : e4m3_rne_mag(a));
+}
+__host__ __device__ inline uint32_t e2m1_encode(float y, bool sr, uint32_t r16) {
+  uint32_t s = (f2u(y) >> 28) & 0x8u;
+  float a = __builtin_fabsf(y);
+  return s | (sr ? e2m1_sr_mag(a, r16) : e2m1_rne_mag(a));
+}
+
+// ---- E8M0 shared scale of an MX block ------------------------------------
+// From the FP32 bits of the block's max |x| (sign cleared): the exponent of
+// the largest power of two <= amax, minus the element's emax, clamped so the
+// code stays in [0, 254]; 0xFF when the block holds NaN or Inf.
+__host__ __device__ inline uint32_t e8m0_from_amax_bits(uint32_t amax_bits, uint32_t emax) {
+  if (amax_bits >= 0x7F800000u) return 0xFFu;
+  uint32_t e = amax_bits >> 23;  // biased exponent; 0 for zero and subnormals
+  return e > emax ? e - emax : 0u;
+}
+// 1 / 2^(code-127) as an exact FP32 (code in 0..254-emax)
+__host__ __device__ inline float e8m0_inverse(uint32_t code) { return u2f((254u - code) << 23); }
+
+// ---- bf16 ---------------------------------------------------------------
+__host__ __device__ inline float bf16_to_f32(uint16_t h) { return u2f((uint32_t)h << 16); }
+// round to nearest even (inputs here are finite)
+__host__ __device__ inline uint16_t f32_to_bf16(float f) {
+  uint32_t b = f2u(f);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+// ---- Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) ------------------
+struct u32x4 {
+  uint32_t x, y, z, w;
+};
+__host__ __device__ inline u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return {c0, c1, c2, c3};
+}
+
+// Eight 16-bit random values for output elements 8q .. 8q+7 of a stream.
+__host__ __device__ inline void rand16x8(uint64_t seed, uint64_t counter, uint64_t q,
+                                         uint32_t out[8]) {
+  uint64_t c = counter + q;
+  u32x4 w = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), 0u, 0u, (uint32_t)seed,
+                          (uint32_t)(seed >> 32));
+  out[0] = w.x & 0xFFFFu; out[1] = w.x >> 16;
+  out[2] = w.y & 0xFFFFu; out[3] = w.y >> 16;
+  out[4] = w.z & 0xFFFFu; out[5] = w.z >> 16;
+  out[6] = w.w & 0xFFFFu; out[7] = w.w >> 16;
+}
+
+// ---- 16-point Hadamard butterflies on 8 in-lane values ---------------------
+// Strides 1, 2, 4 inside a half-group of 8 (the stride-8 stage pairs two
+// lanes and is done by the caller).
+__host__ __device__ inline void hadamard8_stages(float v[8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & h) continue;
+      float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+}
+
+}  // namespace mxk

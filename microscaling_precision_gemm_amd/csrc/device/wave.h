@@ -1,0 +1,34 @@
+// wave.h -- cross-lane helpers for 64-wide CDNA wavefronts (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxk {
+
+// DPP quad permutations: lane i of each quad reads lane perm[i].
+// [1,0,3,2] -> 0xB1 (exchange with lane ^ 1); [2,3,0,1] -> 0x4E (lane ^ 2).
+__device__ inline uint32_t dpp_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ inline uint32_t dpp_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+}
+__device__ inline float dpp_xor1f(float v) { return __builtin_bit_cast(float, dpp_xor1(__builtin_bit_cast(uint32_t, v))); }
+
+__device__ inline uint32_t lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// value of `v` held by lane `src` (any lane of the wave)
+__device__ inline uint32_t lane_read(uint32_t v, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src << 2), (int)v);
+}
+
+// max over the 64 lanes
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = lane_read(v, lane_id() ^ (uint32_t)off);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+}  // namespace mxk

@@ -1,0 +1,51 @@
+// launch.h -- internal launchers between the C ABI (api.cpp) and the kernels.
+// Arguments are already validated when these run.  Each returns the HIP error
+// of its launch(es).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxk {
+
+enum Fmt { FMT_MXFP8 = 1, FMT_MXFP4 = 2, FMT_NVFP4 = 3 };
+enum DType { DT_BF16 = 0, DT_F32 = 1 };
+
+struct QuantArgs {
+  const void* x;
+  int xdt;
+  int64_t rows, cols, ld_x;
+  int fmt;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* tensor_scale;  // NVFP4
+  float* amax;          // NVFP4
+  bool sr;
+  uint64_t seed, counter;
+  bool rht;
+  uint32_t sign_mask;
+  bool amax_given;
+};
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+hipError_t launch_amax(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ld_x, bool rht,
+                       uint32_t sign_mask, float* amax, hipStream_t s);
+hipError_t launch_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales,
+                             const float* tensor_scale, int64_t rows, int64_t cols, void* y,
+                             int ydt, int64_t ld_y, bool rht, uint32_t sign_mask, hipStream_t s);
+hipError_t launch_hadamard16(const void* x, int xdt, void* y, int ydt, int64_t rows, int64_t cols,
+                             uint32_t sign_mask, bool inverse, hipStream_t s);
+hipError_t launch_requant_transpose(const uint8_t* src_codes, const uint8_t* src_scales,
+                                    const float* src_tensor_scale, const uint16_t* x_bf16,
+                                    int64_t ld_x, int64_t rows, int64_t cols, uint8_t* codes,
+                                    uint8_t* scales, bool sr, uint64_t seed, uint64_t counter,
+                                    hipStream_t s);
+hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                          const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
+                          int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s);
+hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                             const int32_t* row_index, int64_t routed_rows,
+                             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
+                             int32_t groups, const int64_t* offsets, int64_t N, int64_t K,
+                             void* C, int cdt, int64_t ldc, hipStream_t s);
+
+}  // namespace mxk

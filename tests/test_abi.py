@@ -1,0 +1,128 @@
+"""The C-ABI library loads without a GPU, exports every function that
+include/mx.h declares, and rejects bad arguments on the host (no device work
+happens for a rejected call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import microscaling_precision_gemm_amd as mx
+    if not os.path.exists(mx.LIB_PATH):
+        from microscaling_precision_gemm_amd.build import build
+        build()
+    mx.load()
+    return mx
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "mx.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_header_declares_the_binding_list(mx):
+    assert header_functions() == sorted(mx.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(mx):
+    L = mx.load()
+    for name in header_functions():
+        assert hasattr(L, name), name
+
+
+def test_host_helpers(mx, orc):
+    for fmt, rows, cols in ((1, 3, 64), (2, 5, 96), (3, 7, 48)):
+        assert mx.mx_codes_bytes(fmt, rows, cols) == orc.codes_bytes(fmt, rows, cols)
+        assert mx.mx_scales_bytes(fmt, rows, cols) == orc.scales_bytes(fmt, rows, cols)
+    assert mx.mx_codes_bytes(9, 4, 32) == 0
+    for seed in (0, 1, 2**40 + 5):
+        assert mx.mx_rht_signs(seed) == orc.rht_signs(seed)
+    assert mx.load().mx_status_string(2) == b"inconsistent or unsupported shape"
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: every call below fails its checks
+
+
+def _t(mx, fmt, rows, cols, codes=FAKE, scales=FAKE, ts=FAKE):
+    return mx._Tensor(fmt, 0, rows, cols, codes, scales, ts)
+
+
+def test_quantize_argument_checks(mx):
+    L = mx.load()
+    rng = mx._Rng(0, 0)
+    t = _t(mx, 1, 4, 64)
+    q = lambda *a: L.mx_quantize(*a)
+    assert q(FAKE, 0, 4, 64, 64, None, 0, rng, 0, 0, None, None) == 1            # out NULL
+    assert q(None, 0, 4, 64, 64, ctypes.byref(t), 0, rng, 0, 0, None, None) == 1  # x NULL
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(t), 7, rng, 0, 0, None, None) == 4  # rounding
+    assert q(FAKE, 5, 4, 64, 64, ctypes.byref(t), 0, rng, 0, 0, None, None) == 4  # dtype
+    assert q(FAKE, 0, 4, 64, 32, ctypes.byref(t), 0, rng, 0, 0, None, None) == 2  # ld < cols
+    assert q(FAKE + 4, 0, 4, 64, 64, ctypes.byref(t), 0, rng, 0, 0, None, None) == 3  # align
+    assert q(FAKE, 0, 4, 64, 68, ctypes.byref(t), 0, rng, 0, 0, None, None) == 3  # row pitch
+    bad = _t(mx, 1, 4, 48)
+    assert q(FAKE, 0, 4, 48, 48, ctypes.byref(bad), 0, rng, 0, 0, None, None) == 2  # 48 % 32
+    wrong = _t(mx, 1, 5, 64)
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(wrong), 0, rng, 0, 0, None, None) == 2  # rows
+    fmt = _t(mx, 9, 4, 64)
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(fmt), 0, rng, 0, 0, None, None) == 4
+    nv = _t(mx, 3, 4, 64)
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(nv), 0, rng, 0, 0, None, None) == 1  # amax NULL
+    nots = _t(mx, 3, 4, 64, ts=None)
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(nots), 0, rng, 0, 0, FAKE, None) == 1
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(t), 0, rng, 8, 0, None, None) == 5  # flags
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(t), 0, rng, 2, 0, None, None) == 5  # amax on MX
+    nocodes = _t(mx, 1, 4, 64, codes=None)
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(nocodes), 0, rng, 0, 0, None, None) == 1
+
+
+def test_other_entry_point_checks(mx):
+    L = mx.load()
+    rng = mx._Rng(0, 0)
+    a8 = _t(mx, 1, 64, 64)
+    a4 = _t(mx, 2, 64, 64)
+    nv = _t(mx, 3, 64, 64)
+    # gemm: mixed formats, K mismatch, K % 32, C pitch
+    assert L.mx_gemm(ctypes.byref(a8), ctypes.byref(a4), FAKE, 1, 64, None) == 5
+    b = _t(mx, 1, 64, 96)
+    assert L.mx_gemm(ctypes.byref(a8), ctypes.byref(b), FAKE, 1, 64, None) == 2
+    assert L.mx_gemm(ctypes.byref(a8), ctypes.byref(a8), FAKE, 1, 63, None) == 2
+    assert L.mx_gemm(ctypes.byref(a8), ctypes.byref(a8), None, 1, 64, None) == 1
+    n16 = _t(mx, 3, 8, 48)
+    assert L.mx_gemm(ctypes.byref(n16), ctypes.byref(n16), FAKE, 1, 8, None) == 2
+    # grouped: non-NVFP4, groups < 1, rows not divisible, missing offsets
+    assert L.mx_gemm_grouped(ctypes.byref(a8), None, 64, ctypes.byref(a8), 1, FAKE, FAKE, 0, 64, None) == 5
+    assert L.mx_gemm_grouped(ctypes.byref(nv), None, 64, ctypes.byref(nv), 0, FAKE, FAKE, 0, 64, None) == 2
+    assert L.mx_gemm_grouped(ctypes.byref(nv), None, 64, ctypes.byref(nv), 3, FAKE, FAKE, 0, 64, None) == 2
+    assert L.mx_gemm_grouped(ctypes.byref(nv), None, 64, ctypes.byref(nv), 2, None, FAKE, 0, 32, None) == 1
+    assert L.mx_gemm_grouped(ctypes.byref(nv), None, 60, ctypes.byref(nv), 2, FAKE, FAKE, 0, 32, None) == 2
+    # requant: both or neither source, wrong out format, rows % 32
+    out = _t(mx, 1, 64, 64)
+    assert L.mx_requant_transpose(ctypes.byref(nv), FAKE, 64, 64, 64, ctypes.byref(out), 1, rng, None) == 1
+    assert L.mx_requant_transpose(None, None, 64, 64, 64, ctypes.byref(out), 1, rng, None) == 1
+    out4 = _t(mx, 2, 64, 64)
+    assert L.mx_requant_transpose(ctypes.byref(nv), None, 0, 64, 64, ctypes.byref(out4), 1, rng, None) == 5
+    assert L.mx_requant_transpose(None, FAKE, 64, 48, 64, ctypes.byref(out), 1, rng, None) == 2
+    src8 = _t(mx, 1, 64, 64)
+    assert L.mx_requant_transpose(ctypes.byref(src8), None, 0, 64, 64, ctypes.byref(out), 1, rng, None) == 5
+    # hadamard: cols % 16, in-place with dtype change
+    assert L.mx_hadamard16(FAKE, 0, FAKE, 0, 4, 24, 0, 0, None) == 2
+    assert L.mx_hadamard16(FAKE, 0, FAKE, 1, 4, 32, 0, 0, None) == 5
+    # amax / dequantize
+    assert L.mx_amax(FAKE, 0, 4, 64, 64, 0, 0, None, None) == 1
+    assert L.mx_amax(FAKE, 0, 4, 64, 64, 4, 0, FAKE, None) == 5
+    assert L.mx_dequantize(ctypes.byref(a8), FAKE, 0, 32, 0, 0, None) == 2
+    assert L.mx_dequantize(None, FAKE, 0, 64, 0, 0, None) == 1
+
+
+def test_binding_fails_loudly_without_library(mx, monkeypatch):
+    monkeypatch.setattr(mx, "_lib", None)
+    monkeypatch.setattr(mx, "LIB_PATH", "/nonexistent/libmx.so")
+    with pytest.raises(mx.MXError):
+        mx.load()

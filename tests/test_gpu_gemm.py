@@ -1,0 +1,126 @@
+"""GPU parity of the block-scaled GEMMs against the FP64 oracle on the
+decoded operands: |C - C_oracle| <= 1e-5 * sum_k |a_k b_k| for FP32 output,
+and C within [bf16(C_oracle - tol), bf16(C_oracle + tol)] for BF16 output."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import microscaling_precision_gemm_amd as mx
+    from tests.gpu_util import check_gemm, dev, upload
+
+
+def _operands(fmt, M, N, K, seed, outliers=True):
+    a = W.normal_bf16(M, K, 1.0, seed, 50, outlier_entries=0.002 if outliers else 0.0, outlier_mult=50)
+    b = W.normal_bf16(N, K, 0.5, seed, 51)
+    qa = oracle.quantize(a, fmt, 0)
+    qb = oracle.quantize(b, fmt, 0)
+    return qa, qb
+
+
+def _oracle_gemm(fmt, qa, qb, M, N, K):
+    Ad = oracle.dequantize_f64(fmt, qa[0], qa[1], M, K)
+    Bd = oracle.dequantize_f64(fmt, qb[0], qb[1], N, K)
+    post = 1.0
+    if fmt == 3:
+        post = float(np.float64(qa[2]) * np.float64(qb[2]))
+    return oracle.gemm(Ad, Bd, post)
+
+
+GEMM_SHAPES = [(32, 32, 32), (64, 96, 64), (130, 70, 96), (256, 256, 256), (257, 129, 544),
+               (1, 300, 1024)]
+
+
+@pytest.mark.parametrize("shape", GEMM_SHAPES)
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("cdt", ["f32", "bf16"])
+def test_gemm_within_tolerance(shape, fmt, cdt):
+    M, N, K = shape
+    qa, qb = _operands(fmt, M, N, K, M + N + K)
+    A = upload(fmt, *qa)
+    B = upload(fmt, *qb)
+    C = torch.full((M, N + 3), float("nan"), dtype=torch.float32 if cdt == "f32" else torch.bfloat16,
+                   device=dev())[:, :N]
+    mx.mx_gemm(A, B, C)
+    torch.cuda.synchronize()
+    Chat, tol = _oracle_gemm(fmt, qa, qb, M, N, K)
+    check_gemm(C.float().cpu().numpy(), Chat, tol, cdt == "bf16", f"fmt {fmt} {shape} {cdt}")
+
+
+@pytest.mark.parametrize("gather", [False, True])
+def test_grouped_nvfp4(gather):
+    tokens, K, N, E, topk = 96, 256, 80, 5, 2
+    X = W.normal_bf16(tokens, K, 1.0, 3, 52)
+    row_index, offsets = W.uniform_topk_routing(tokens, E, topk, 3, 53)
+    R = row_index.size
+    Wb = [W.normal_bf16(N, K, 0.02, 3, 60 + e) for e in range(E)]
+    qw = [oracle.quantize(w, 3, 0) for w in Wb]
+    if gather:
+        qx = oracle.quantize(X, 3, 0)
+        A = upload(3, *qx)
+        ri = torch.from_numpy(row_index).to(dev())
+    else:
+        Xr = X[row_index]
+        qx = oracle.quantize(np.ascontiguousarray(Xr), 3, 0)
+        A = upload(3, *qx)
+        ri = None
+    B = upload(3, np.concatenate([q[0] for q in qw]), np.concatenate([q[1] for q in qw]),
+               np.array([q[2] for q in qw], np.float32))
+    off = torch.from_numpy(offsets).to(dev())
+    C = torch.empty(R, N, dtype=torch.bfloat16, device=dev())
+    mx.mx_gemm_grouped(A, ri, R, B, E, off, C)
+    torch.cuda.synchronize()
+    Cg = C.float().cpu().numpy()
+    Ad = oracle.dequantize_f64(3, qx[0], qx[1], qx[0].shape[0], K)
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi == lo:
+            continue
+        rows = row_index[lo:hi] if gather else np.arange(lo, hi)
+        Bd = oracle.dequantize_f64(3, qw[e][0], qw[e][1], N, K)
+        Chat, tol = oracle.gemm(Ad[rows], Bd, float(np.float64(qx[2]) * np.float64(qw[e][2])))
+        check_gemm(Cg[lo:hi], Chat, tol, True, f"expert {e}")
+
+
+def test_grouped_nvfp4_empty_and_uneven_groups():
+    K, N = 64, 32
+    offsets = np.array([0, 0, 3, 3, 200, 201], np.int64)  # empty groups and a ragged one
+    E = offsets.size - 1
+    R = int(offsets[-1])
+    X = W.normal_bf16(R, K, 1.0, 4, 54)
+    qx = oracle.quantize(X, 3, 0)
+    qw = [oracle.quantize(W.normal_bf16(N, K, 1.0, 4, 70 + e), 3, 0) for e in range(E)]
+    A = upload(3, *qx)
+    B = upload(3, np.concatenate([q[0] for q in qw]), np.concatenate([q[1] for q in qw]),
+               np.array([q[2] for q in qw], np.float32))
+    C = torch.empty(R, N, dtype=torch.float32, device=dev())
+    mx.mx_gemm_grouped(A, None, R, B, E, torch.from_numpy(offsets).to(dev()), C)
+    torch.cuda.synchronize()
+    Cg = C.cpu().numpy()
+    Ad = oracle.dequantize_f64(3, qx[0], qx[1], R, K)
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            Bd = oracle.dequantize_f64(3, qw[e][0], qw[e][1], N, K)
+            Chat, tol = oracle.gemm(Ad[lo:hi], Bd, float(np.float64(qx[2]) * np.float64(qw[e][2])))
+            check_gemm(Cg[lo:hi], Chat, tol, False, f"expert {e}")
+
+
+def test_gemm_identity_closed_form():
+    """A = identity in MXFP4 (1.0 coded with scale 2^0 after the 2^2 shift):
+    C equals the decoded B transposed exactly."""
+    K = 128
+    eye = np.eye(K, dtype=np.float32)
+    qa = oracle.quantize(eye, 2, 0)
+    b = W.normal_bf16(64, K, 1.0, 5, 55)
+    qb = oracle.quantize(b, 2, 0)
+    C = torch.empty(K, 64, dtype=torch.float32, device=dev())
+    mx.mx_gemm(upload(2, *qa), upload(2, *qb), C)
+    torch.cuda.synchronize()
+    Bd = oracle.dequantize_f64(2, qb[0], qb[1], 64, K)
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), Bd.T)
