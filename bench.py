@@ -1,0 +1,320 @@
+"""Benchmark of the block-scaled quantize + GEMM hot path on one MI355X.
+
+One step = quantize A (activations 4096x4096 BF16, N(0,1), 1% of K-columns
+x50) and B (weights 4096x4096 BF16, N(0, 0.02^2)) to MXFP4 E2M1 with E8M0
+scales per 32 (round-to-nearest-even), then the block-scaled GEMM
+C = A * B^T (4096^3, FP32 accumulation, BF16 out).  Inputs are resident in
+HBM before the timed region and rotate over 16 copies (1 GiB of BF16) so the
+256 MB last-level cache does not hold them between steps.
+
+Prints one JSON line: metric / value (TFLOP/s of the whole step: 2*M*N*K per
+step time), the roofline of the dominant kernel (the GEMM) measured with HIP
+events on the stream the kernels run on, the quantizer's HBM throughput, a
+CPU baseline (the oracle on a bounded sample, rank 0), and secondary
+measurements of the other workloads (MXFP8 GEMM, NVFP4 grouped MoE GEMM,
+backward requant + wgrad, RHT + NVFP4 stochastic rounding) unless
+--no-detail is given.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X dense peaks (AMD public figures) and HBM bandwidth
+PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-detail", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="output rows of the GEMM sample the oracle is timed on")
+    return ap.parse_args()
+
+
+class Timer:
+    """Per-launch HIP-event timing on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+
+
+def time_fn(torch, fn, iters, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(iters):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ts]))
+
+
+def upload_bf16(torch, bits: np.ndarray):
+    return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def headline(torch, mx, W, args):
+    M = N = K = 4096
+    A_bits, B_bits = W.cfg2(0, 4096)
+    A0 = upload_bf16(torch, A_bits)
+    B0 = upload_bf16(torch, B_bits)
+    nrot = 16
+    As = [A0] + [A0.clone() for _ in range(nrot - 1)]
+    Bs = [B0] + [B0.clone() for _ in range(nrot - 1)]
+    qa = mx.empty(mx.MX_MXFP4_E2M1, M, K)
+    qb = mx.empty(mx.MX_MXFP4_E2M1, N, K)
+    C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tq, tg = Timer(torch), Timer(torch)
+
+    def step(i, timed):
+        a, b = As[i % nrot], Bs[i % nrot]
+        s = tq.start() if timed else None
+        mx.mx_quantize(a, qa, mx.MX_RNE)
+        if timed:
+            tq.stop(s)
+            s = tq.start()
+        mx.mx_quantize(b, qb, mx.MX_RNE)
+        if timed:
+            tq.stop(s)
+            s = tg.start()
+        mx.mx_gemm(qa, qb, C)
+        if timed:
+            tg.stop(s)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    flops = 2.0 * M * N * K
+    gemm_ms = tg.mean_ms()
+    quant_ms = tq.mean_ms()
+    # algorithmic bytes of one MXFP4 quantize of a 4096x4096 BF16 operand:
+    # read 2 B/elem, write 0.5 B codes + 1/32 B scales
+    qbytes = M * K * (2 + 0.5 + 1 / 32)
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    out = {
+        "ms_per_step": ms_step,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "gemm_ms": gemm_ms,
+        "gemm_tflops": gemm_tflops,
+        "quant_ms": quant_ms,
+        "quant_gbs": qbytes / (quant_ms * 1e-3) / 1e9,
+        "qbytes": qbytes,
+        "flops": flops,
+        "A_bits": A_bits,
+        "B_bits": B_bits,
+    }
+    return out
+
+
+def cpu_baseline(W, oracle, A_bits, B_bits, rows: int):
+    """The oracle, untuned, on a bounded sample of the same step: quantize
+    `rows` rows of A and all of B, then `rows` output rows of the FP64 GEMM.
+    Throughput is reported in the step's unit (TFLOP/s of 2*M*N*K-equivalent
+    work), scaled by the sampled fraction of the output."""
+    oracle.lib()
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    qa = oracle.quantize(np.ascontiguousarray(A_bits[:rows]), oracle.MXFP4)
+    qb = oracle.quantize(B_bits, oracle.MXFP4)
+    Ad = oracle.dequantize_f64(oracle.MXFP4, qa[0], qa[1], rows, A_bits.shape[1])
+    Bd = oracle.dequantize_f64(oracle.MXFP4, qb[0], qb[1], B_bits.shape[0], B_bits.shape[1])
+    oracle.gemm(Ad, Bd)
+    dt = time.perf_counter() - t0
+    M, K = A_bits.shape
+    N = B_bits.shape[0]
+    # the sample does rows/M of the GEMM and (rows + N)/(M + N) of the quantization;
+    # charge it the GEMM fraction of the step's flops
+    sample_flops = 2.0 * rows * N * K
+    return {"value": sample_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": dt,
+            "sample": f"MXFP4 quantize of {rows} rows of A and all 4096 rows of B, then "
+                      f"{rows} of the 4096 output rows of the FP64 GEMM (K=4096); "
+                      f"throughput = 2*{rows}*{N}*{K} / time"}
+
+
+def detail(torch, mx, W, args):
+    """Secondary workloads (each timed in isolation, median over iterations)."""
+    res = {}
+    it, wu = 20, 5
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+
+    def randn(r, c, std=1.0):
+        return (torch.randn(r, c, generator=g, device="cuda", dtype=torch.float32) * std).to(torch.bfloat16)
+
+    # MXFP8 4096^3 GEMM: exact (BF16-staged) and the native FP8 instruction
+    M = N = K = 4096
+    a, b = randn(M, K), randn(N, K, 0.02)
+    qa, qb = mx.empty(1, M, K), mx.empty(1, N, K)
+    mx.mx_quantize(a, qa)
+    mx.mx_quantize(b, qb)
+    C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ms = time_fn(torch, lambda: mx.mx_gemm(qa, qb, C), it, wu)
+    res["mxfp8_gemm_4096_exact"] = {"ms": ms, "tflops": 2 * M * N * K / ms / 1e9,
+                                    "frac_fp8_peak": 2 * M * N * K / ms / 1e9 / PEAK_TFLOPS["fp8"],
+                                    "frac_bf16_peak": 2 * M * N * K / ms / 1e9 / PEAK_TFLOPS["bf16"]}
+    ms = time_fn(torch, lambda: mx.mx_gemm_ex(qa, qb, C, mx.MX_GEMM_FP8_NATIVE), it, wu)
+    res["mxfp8_gemm_4096_native_fp8"] = {"ms": ms, "tflops": 2 * M * N * K / ms / 1e9,
+                                         "frac_fp8_peak": 2 * M * N * K / ms / 1e9 / PEAK_TFLOPS["fp8"]}
+    mx.mx_quantize(a, qa)
+    ms = time_fn(torch, lambda: mx.mx_quantize(a, qa), it, wu)
+    by = M * K * (2 + 1 + 1 / 32)
+    res["mxfp8_quantize_4096x4096"] = {"ms": ms, "gbs": by / ms / 1e6, "frac_hbm": by / ms / 1e6 / PEAK_HBM_GBS}
+    del a, b, qa, qb, C
+
+    # NVFP4 MoE forward: 4096 tokens x 7168, top-8 of 32 experts, W_e 2048x7168
+    tokens, hid, E, topk, inter = 4096, 7168, 32, 8, 2048
+    X = randn(tokens, hid)
+    row_index, offsets = W.uniform_topk_routing(tokens, E, topk, 0, 6)
+    R = int(offsets[-1])
+    Wt = randn(E * inter, hid, 0.02)
+    qw = mx.empty(3, E * inter, hid, n_tensor_scales=E)
+    amax = torch.zeros(E, dtype=torch.float32, device="cuda")
+    for e in range(E):
+        mx.mx_quantize(Wt[e * inter:(e + 1) * inter], qw.view_rows(e * inter, (e + 1) * inter, qw.tensor_scale[e:e + 1]),
+                       amax=amax[e:e + 1])
+    del Wt
+    qx = mx.empty(3, tokens, hid)
+    xa = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ri = torch.from_numpy(row_index).cuda()
+    off = torch.from_numpy(offsets).cuda()
+    Cg = torch.empty(R, inter, dtype=torch.bfloat16, device="cuda")
+    ms_q = time_fn(torch, lambda: mx.mx_quantize(X, qx, amax=xa), it, wu)
+    ms_g = time_fn(torch, lambda: mx.mx_gemm_grouped(qx, ri, R, qw, E, off, Cg), it, wu)
+    fl = 2.0 * R * inter * hid
+    by = tokens * hid * (2 * 2 + 0.5 + 1 / 16)
+    res["nvfp4_moe_fwd"] = {"quant_ms": ms_q, "quant_gbs_2pass": by / ms_q / 1e6,
+                            "gemm_ms": ms_g, "gemm_tflops": fl / ms_g / 1e9,
+                            "frac_fp4_peak": fl / ms_g / 1e9 / PEAK_TFLOPS["fp4"],
+                            "frac_fp8_peak": fl / ms_g / 1e9 / PEAK_TFLOPS["fp8"],
+                            "frac_bf16_peak": fl / ms_g / 1e9 / PEAK_TFLOPS["bf16"]}
+    del X, qw, qx, Cg
+
+    # backward: NVFP4 X [16384, 4096] -> MXFP8 X^T (SR); dY [16384, 14336] -> MXFP8 dY^T (SR);
+    # wgrad GEMM M=4096 N=14336 K=16384 -> FP32
+    T_, H, O = 16384, 4096, 14336
+    Xb = randn(T_, H)
+    qx = mx.empty(3, T_, H)
+    mx.mx_quantize(Xb, qx, amax=torch.zeros(1, device="cuda"))
+    xt = mx.empty(1, H, T_)
+    ms_r = time_fn(torch, lambda: mx.mx_requant_transpose(xt, src=qx, rnd=mx.MX_SR, seed=0, counter=0), it, wu)
+    by_r = T_ * H * (0.5 + 1 / 16 + 1 + 1 / 32)
+    del Xb
+    dY = randn(T_, O)
+    dyt = mx.empty(1, O, T_)
+    ms_d = time_fn(torch, lambda: mx.mx_requant_transpose(dyt, x_bf16=dY, rnd=mx.MX_SR, seed=0, counter=T_ * H // 8), it, wu)
+    by_d = T_ * O * (2 + 1 + 1 / 32)
+    del dY
+    Cw = torch.empty(H, O, dtype=torch.float32, device="cuda")
+    ms_w = time_fn(torch, lambda: mx.mx_gemm(xt, dyt, Cw), 5, 2)
+    ms_wn = time_fn(torch, lambda: mx.mx_gemm_ex(xt, dyt, Cw, mx.MX_GEMM_FP8_NATIVE), 5, 2)
+    fl = 2.0 * H * O * T_
+    res["backward_requant_wgrad"] = {
+        "requant_nvfp4_ms": ms_r, "requant_gbs": by_r / ms_r / 1e6, "requant_frac_hbm": by_r / ms_r / 1e6 / PEAK_HBM_GBS,
+        "dy_quant_t_ms": ms_d, "dy_gbs": by_d / ms_d / 1e6, "dy_frac_hbm": by_d / ms_d / 1e6 / PEAK_HBM_GBS,
+        "wgrad_exact_ms": ms_w, "wgrad_exact_tflops": fl / ms_w / 1e9,
+        "wgrad_native_fp8_ms": ms_wn, "wgrad_native_fp8_tflops": fl / ms_wn / 1e9}
+    del qx, xt, dyt, Cw
+
+    # RHT16 + NVFP4 SR of an 8192x7168 Student-t(3) gradient (two passes)
+    G = torch.distributions.StudentT(3.0).sample((8192, 7168)).to(device="cuda", dtype=torch.bfloat16)
+    qg = mx.empty(3, 8192, 7168)
+    ga = torch.zeros(1, device="cuda")
+    mask = mx.mx_rht_signs(0)
+    ms_h = time_fn(torch, lambda: mx.mx_quantize(G, qg, mx.MX_SR, 0, 0, mx.MX_FLAG_RHT16, mask, ga), it, wu)
+    by2 = 8192 * 7168 * (2 * 2 + 0.5 + 1 / 16)
+    res["rht_nvfp4_sr_8192x7168"] = {"ms": ms_h, "gbs_2pass": by2 / ms_h / 1e6,
+                                     "frac_hbm": by2 / ms_h / 1e6 / PEAK_HBM_GBS}
+    del G, qg
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the path is measured on one MI355X "
+              "(see DESIGN.md for how it would shard); --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    import microscaling_precision_gemm_amd as mx
+    import workloads as W
+    mx.load()
+    torch.cuda.synchronize()
+    h = headline(torch, mx, W, args)
+    roof = {"bound": "mfma", "achieved": h["gemm_tflops"], "peak": PEAK_TFLOPS["fp4"],
+            "unit": "TFLOP/s", "frac": h["gemm_tflops"] / PEAK_TFLOPS["fp4"], "traffic": None,
+            "kernel": "k_gemm_mx<MXFP4, BF16 out, 256x256>", "gemm_ms": h["gemm_ms"]}
+    line = {
+        "metric": "block-scaled GEMM TFLOPS (MXFP4/NVFP4/MXFP8 4096^3) + quantize HBM GB/s",
+        "value": h["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 (e2m1 codes, e8m0 scales) -> fp32 accumulate -> bf16",
+        "data": "synthetic",
+        "config": {"workload": "MXFP4 E2M1 quantize (RNE, E8M0/32) of A 4096x4096 BF16 N(0,1) "
+                               "with 1% of K-columns x50 and B 4096x4096 BF16 N(0,0.02^2), then "
+                               "block-scaled GEMM M=N=K=4096, FP32 accumulate, BF16 out",
+                   "M": 4096, "N": 4096, "K": 4096, "input_rotation": 16},
+        "roofline": roof,
+        "quantize": {"ms_per_operand": h["quant_ms"], "achieved_gbs": h["quant_gbs"],
+                     "peak_gbs": PEAK_HBM_GBS, "frac": h["quant_gbs"] / PEAK_HBM_GBS,
+                     "bytes_per_operand": h["qbytes"]},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        line["cpu_baseline"] = cpu_baseline(W, oracle, h["A_bits"], h["B_bits"], args.cpu_rows)
+    if not args.no_detail:
+        line["detail"] = detail(torch, mx, W, args)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

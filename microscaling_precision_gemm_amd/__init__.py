@@ -19,13 +19,15 @@ MX_MXFP8_E4M3, MX_MXFP4_E2M1, MX_NVFP4 = 1, 2, 3
 MX_RNE, MX_SR = 0, 1
 MX_BF16, MX_F32 = 0, 1
 MX_FLAG_RHT16, MX_FLAG_AMAX_GIVEN = 1, 2
+MX_GEMM_FP8_NATIVE = 1
 
 FORMATS = {"mxfp8": MX_MXFP8_E4M3, "mxfp4": MX_MXFP4_E2M1, "nvfp4": MX_NVFP4}
 
 # every function declared in include/mx.h
 EXPORTED = [
     "mx_codes_bytes", "mx_scales_bytes", "mx_rht_signs", "mx_quantize", "mx_amax",
-    "mx_dequantize", "mx_requant_transpose", "mx_hadamard16", "mx_gemm", "mx_gemm_grouped",
+    "mx_dequantize", "mx_requant_transpose", "mx_hadamard16", "mx_gemm", "mx_gemm_ex",
+    "mx_gemm_grouped",
     "mx_status_string",
 ]
 
@@ -68,6 +70,7 @@ def load():
         "mx_requant_transpose": (i32, [TP, vp, i64, i64, i64, TP, i32, _Rng, vp]),
         "mx_hadamard16": (i32, [vp, i32, vp, i32, i64, i64, u16, i32, vp]),
         "mx_gemm": (i32, [TP, TP, vp, i32, i64, vp]),
+        "mx_gemm_ex": (i32, [TP, TP, vp, i32, i64, u32, vp]),
         "mx_gemm_grouped": (i32, [TP, vp, i64, TP, i32, vp, vp, i32, i64, vp]),
         "mx_status_string": (ctypes.c_char_p, [i32]),
     }
@@ -212,6 +215,16 @@ def mx_gemm(A: MXTensor, B: MXTensor, C, stream=None):
     da, db = A.desc(), B.desc()
     _check(L.mx_gemm(ctypes.byref(da), ctypes.byref(db), _ptr(C), _dt(C), C.stride(0),
                      _stream(stream)))
+    return C
+
+
+def mx_gemm_ex(A: MXTensor, B: MXTensor, C, flags: int = 0, stream=None):
+    """mx_gemm with options (MX_GEMM_FP8_NATIVE: MXFP8 on the FP8 matrix
+    instruction, see include/mx.h for its accuracy)."""
+    L = load()
+    da, db = A.desc(), B.desc()
+    _check(L.mx_gemm_ex(ctypes.byref(da), ctypes.byref(db), _ptr(C), _dt(C), C.stride(0), flags,
+                        _stream(stream)))
     return C
 
 

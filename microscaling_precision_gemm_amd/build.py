@@ -20,7 +20,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "quantize.hip"),
     os.path.join(CSRC, "kernels", "requant.hip"),
     os.path.join(CSRC, "kernels", "gemm_mx.hip"),
-    os.path.join(CSRC, "kernels", "gemm_nvfp4.hip"),
+    os.path.join(CSRC, "kernels", "gemm_staged.hip"),
 ]
 
 # -ffp-contract=off: the quantizers' FP32 scale arithmetic must round once per

@@ -189,31 +189,45 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
-mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,
-                  mx_stream stream) {
+mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,
+                     uint32_t flags, mx_stream stream) {
   if (!A || !B) return MX_ERR_NULL;
+  if (flags & ~MX_GEMM_FP8_NATIVE) return MX_ERR_UNSUPPORTED;
   mx_status st = check_tensor(A, A->rows, A->cols);
   if (st != MX_OK) return st;
   st = check_tensor(B, B->rows, B->cols);
   if (st != MX_OK) return st;
   if (A->fmt != B->fmt) return MX_ERR_UNSUPPORTED;
+  if ((flags & MX_GEMM_FP8_NATIVE) && A->fmt != MX_MXFP8_E4M3) return MX_ERR_UNSUPPORTED;
   if (A->cols != B->cols || A->cols % 32) return MX_ERR_SHAPE;
   const int64_t M = A->rows, N = B->rows, K = A->cols;
   st = check_output(C, cdt, M, N, ldc);
   if (st != MX_OK) return st;
   if (M * N == 0) return MX_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (A->fmt == MX_NVFP4) {
-    // one group covering all rows; offsets are not needed on the device for
-    // a single group, so the plain GEMM is the grouped kernel with R = M.
-    return hip_status(mxk::launch_gemm_nvfp4(
-        static_cast<const uint8_t*>(A->codes), A->scales, A->tensor_scale, nullptr, M,
-        static_cast<const uint8_t*>(B->codes), B->scales, B->tensor_scale, 1, nullptr, N, K, C,
-        cdt, ldc, s));
+  const uint8_t* ac = static_cast<const uint8_t*>(A->codes);
+  const uint8_t* bc = static_cast<const uint8_t*>(B->codes);
+  switch (A->fmt) {
+    case MX_NVFP4:
+      // one group covering all rows (no offsets array needed)
+      return hip_status(mxk::launch_gemm_nvfp4(ac, A->scales, A->tensor_scale, nullptr, M, bc,
+                                               B->scales, B->tensor_scale, 1, nullptr, N, K, C,
+                                               cdt, ldc, s));
+    case MX_MXFP8_E4M3:
+      if (flags & MX_GEMM_FP8_NATIVE)
+        return hip_status(mxk::launch_gemm_mx(A->fmt, ac, A->scales, bc, B->scales, M, N, K, C,
+                                              cdt, ldc, s));
+      return hip_status(mxk::launch_gemm_mxfp8_exact(ac, A->scales, bc, B->scales, M, N, K, C,
+                                                     cdt, ldc, s));
+    default:
+      return hip_status(mxk::launch_gemm_mx(A->fmt, ac, A->scales, bc, B->scales, M, N, K, C, cdt,
+                                            ldc, s));
   }
-  return hip_status(mxk::launch_gemm_mx(A->fmt, static_cast<const uint8_t*>(A->codes), A->scales,
-                                        static_cast<const uint8_t*>(B->codes), B->scales, M, N, K,
-                                        C, cdt, ldc, s));
+}
+
+mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,
+                  mx_stream stream) {
+  return mx_gemm_ex(A, B, C, cdt, ldc, 0u, stream);
 }
 
 mx_status mx_gemm_grouped(const mx_tensor* A, const int32_t* row_index, int64_t routed_rows,

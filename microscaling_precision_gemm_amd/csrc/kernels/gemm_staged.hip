@@ -1,0 +1,321 @@
+// gemm_staged.hip -- block-scaled GEMMs whose block scales are applied
+// explicitly while the operands are staged into LDS as exact BF16 values, then
+// contracted on v_mfma_f32_32x32x16_bf16 (exact products, FP32 accumulation).
+//
+//  * NVFP4 ("Microscaling (MX) and block-scaled 4-bit formats", section
+//    "NVFP4"): E2M1 elements, an E4M3 scale per 16 and an FP32 scale per
+//    tensor.  The E4M3 block scale has no counterpart in the matrix
+//    instructions (their block scale is an E8M0 power of two per 32), so each
+//    element is multiplied by it here; e2m1 * e4m3 has at most 2 + 4
+//    significant bits and is exact in BF16.  The per-tensor scales multiply
+//    the FP32 accumulator in the epilogue.  Plain and grouped (mixture-of-
+//    experts forward: "Thinking Machines ... Inkling 2 Small", section "A
+//    precision choice for each stage") variants, with an optional row gather
+//    of A.
+//  * MXFP8, exact: E4M3 * 2^(c-127) is exact in BF16 for scale codes c in
+//    [3, 246].  (gfx950's FP8 matrix instruction truncates products inside
+//    8-element groups, see gemm_mx.hip, so the exact MXFP8 product is formed
+//    on the BF16 instruction.)
+//
+// Conversion: gfx950's v_cvt_scalef32_pk_* instructions scale by the
+// exponent of their FP32 scale operand only (measured), which is exactly the
+// E8M0 scale of MXFP8.  NVFP4 elements are converted with scale 1 and
+// multiplied by the E4M3 scale in FP32 (exact), then truncated to BF16
+// (exact).
+//
+// Workgroup: 256 threads (2x2 waves), BM x BN tile, K step 64 elements,
+// double-buffered BF16 tiles in LDS with a 144-byte row pitch (8 consecutive
+// rows hit distinct banks for the 16-byte fragment reads).  Grouped launch:
+// the workgroup index enumerates (n tile, group, m tile); the grid is sized
+// with an upper bound of ceil(R/BM) + groups m tiles and surplus workgroups
+// exit.
+#include "../device/codec.h"
+#include "../launch.h"
+
+namespace mxk {
+
+namespace {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+constexpr int kBK = 64;                // K elements per step
+constexpr int kPitch = kBK * 2 + 16;   // LDS bytes per row
+
+// staged unit: 32 consecutive K elements of one row
+template <int SRC>
+struct Unit {
+  static constexpr int kCodeWords = SRC == FMT_NVFP4 ? 4 : 8;  // dwords of codes
+  uint32_t w[kCodeWords];
+  uint32_t s;  // NVFP4: two E4M3 bytes; MXFP8: one E8M0 byte
+};
+
+template <int SRC>
+__device__ inline void convert_store(const Unit<SRC>& u, uint8_t* dst) {
+  uint32_t out[16];
+  if constexpr (SRC == FMT_NVFP4) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const float sbv = e4m3_mag_value((u.s >> (8 * blk)) & 0xFFu);
+#pragma unroll
+      for (int wd = 0; wd < 2; ++wd) {
+        const uint32_t word = u.w[blk * 2 + wd];
+        const v2f f[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3)};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float lo = f[b][0] * sbv, hi = f[b][1] * sbv;  // exact products
+          out[blk * 8 + wd * 4 + b] = (f2u(lo) >> 16) | (f2u(hi) & 0xFFFF0000u);
+        }
+      }
+    }
+  } else {
+    const uint32_t c = u.s & 0xFFu;
+    if (c >= 1u && c != 0xFFu) {
+      const float X = u2f(c << 23);  // 2^(c-127), a normal FP32
+#pragma unroll
+      for (int wd = 0; wd < 8; ++wd) {
+        out[2 * wd] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.w[wd], X, false));
+        out[2 * wd + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.w[wd], X, true));
+      }
+    } else {
+      // scale code 0 (2^-127 is an FP32 subnormal, which the converter does
+      // not take as a scale) or 0xFF (NaN): convert at scale 1, multiply in FP32
+      const float X = c == 0u ? u2f(0x00400000u) : __builtin_nanf("");
+#pragma unroll
+      for (int wd = 0; wd < 8; ++wd) {
+        const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.w[wd], 1.0f, false);
+        const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.w[wd], 1.0f, true);
+        out[2 * wd] = (f2u(lo[0] * X) >> 16) | (f2u(lo[1] * X) & 0xFFFF0000u);
+        out[2 * wd + 1] = (f2u(hi[0] * X) >> 16) | (f2u(hi[1] * X) & 0xFFFF0000u);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+}
+
+template <int SRC, int CDT, int BM, int BN, bool GATHER>
+__global__ __launch_bounds__(256) void k_gemm_staged(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const float* __restrict__ a_ts,
+    const int32_t* __restrict__ row_index, int64_t R, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ SB, const float* __restrict__ b_ts, int32_t groups,
+    const int64_t* __restrict__ offsets, int64_t N, int64_t K, void* __restrict__ C, int64_t ldc,
+    uint32_t tiles_n, uint32_t tiles_m_bound) {
+  constexpr int kRows = BM + BN;
+  constexpr int kUnits = kRows * 2 / 256;  // 32-element units per thread per step
+  constexpr int FM = BM / 2 / 32, FN = BN / 2 / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kRows * kPitch];
+
+  // workgroup -> (n tile, m tile over all groups); consecutive ids share the
+  // m tile (A rows) and walk n, and ids on one XCD (id mod 8) are adjacent
+  uint32_t id = blockIdx.x;
+  const uint32_t total = tiles_n * tiles_m_bound;
+  if ((total & 7u) == 0) id = (id & 7u) * (total >> 3) + (id >> 3);
+  const int64_t tile = id / tiles_n;
+  const int64_t n0 = (int64_t)(id % tiles_n) * BN;
+
+  int64_t g = -1, g_lo = 0, g_hi = 0;
+  if (offsets == nullptr) {
+    if (tile * BM < R) {
+      g = 0;
+      g_lo = tile * BM;
+      g_hi = R;
+    }
+  } else {
+    int64_t acc = 0;
+    for (int32_t e = 0; e < groups; ++e) {
+      const int64_t lo = offsets[e], hi = offsets[e + 1];
+      const int64_t nt = (hi - lo + BM - 1) / BM;
+      if (tile < acc + nt) {
+        g = e;
+        g_lo = lo + (tile - acc) * BM;
+        g_hi = hi;
+        break;
+      }
+      acc += nt;
+    }
+  }
+  if (g < 0) return;  // surplus workgroup (uniform across the block)
+
+  const uint32_t t = threadIdx.x;
+  const uint32_t lane = t & 63u, wid = t >> 6;
+  const uint32_t wm = wid >> 1, wn = wid & 1u;
+  const int64_t m0 = g_lo;
+  const int64_t rowbytes = SRC == FMT_NVFP4 ? K / 2 : K;
+  const int64_t sblocks = SRC == FMT_NVFP4 ? K / 16 : K / 32;
+  const int64_t steps = (K + kBK - 1) / kBK;
+  const uint8_t* Bg = B + g * N * rowbytes;
+  const uint8_t* SBg = SB + g * N * sblocks;
+
+  // per-unit sources (fixed over the K loop): unit u = t + 256 j covers row
+  // u / 2, K half u % 2 of each step
+  const uint8_t* csrc[kUnits];
+  const uint8_t* ssrc[kUnits];
+  uint32_t dst_off[kUnits];
+#pragma unroll
+  for (int j = 0; j < kUnits; ++j) {
+    const uint32_t u = t + 256u * j;
+    const uint32_t r = u >> 1, h = u & 1u;
+    dst_off[j] = r * kPitch + h * 64;
+    csrc[j] = nullptr;
+    ssrc[j] = nullptr;
+    if (r < (uint32_t)BM) {
+      const int64_t rr = m0 + r;
+      if (rr < g_hi) {
+        const int64_t src_row = GATHER ? (int64_t)row_index[rr] : rr;
+        csrc[j] = A + src_row * rowbytes + h * (SRC == FMT_NVFP4 ? 16 : 32);
+        ssrc[j] = SA + src_row * sblocks + h * (SRC == FMT_NVFP4 ? 2 : 1);
+      }
+    } else {
+      const int64_t rr = n0 + (r - BM);
+      if (rr < N) {
+        csrc[j] = Bg + rr * rowbytes + h * (SRC == FMT_NVFP4 ? 16 : 32);
+        ssrc[j] = SBg + rr * sblocks + h * (SRC == FMT_NVFP4 ? 2 : 1);
+      }
+    }
+  }
+
+  Unit<SRC> reg[kUnits];
+  auto load_step = [&](int64_t step) {
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+      const uint32_t h = (t + 256u * j) & 1u;
+      const int64_t k0 = step * kBK + h * 32;  // first K element of the unit
+      const bool ok = csrc[j] != nullptr && k0 < K;  // K % 32 == 0: a unit is all in or out
+      if constexpr (SRC == FMT_NVFP4) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        uint32_t s = 0;
+        if (ok) {
+          v = *reinterpret_cast<const uint4*>(csrc[j] + step * (kBK / 2));
+          s = *reinterpret_cast<const uint16_t*>(ssrc[j] + step * (kBK / 16));
+        }
+        reg[j].w[0] = v.x; reg[j].w[1] = v.y; reg[j].w[2] = v.z; reg[j].w[3] = v.w;
+        reg[j].s = s;
+      } else {
+        uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+        uint32_t s = 127u;
+        if (ok) {
+          const uint4* p = reinterpret_cast<const uint4*>(csrc[j] + step * kBK);
+          v0 = p[0];
+          v1 = p[1];
+          s = ssrc[j][step * (kBK / 32)];
+        }
+        reg[j].w[0] = v0.x; reg[j].w[1] = v0.y; reg[j].w[2] = v0.z; reg[j].w[3] = v0.w;
+        reg[j].w[4] = v1.x; reg[j].w[5] = v1.y; reg[j].w[6] = v1.z; reg[j].w[7] = v1.w;
+        reg[j].s = s;
+      }
+    }
+  };
+  auto store_step = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) convert_store<SRC>(reg[j], &lds[buf][dst_off[j]]);
+  };
+
+  v16f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  load_step(0);
+  store_step(0);
+  __syncthreads();
+  const uint32_t lr = lane & 31u, lg = lane >> 5;
+  for (int64_t st = 0; st < steps; ++st) {
+    const int buf = (int)(st & 1);
+    if (st + 1 < steps) load_step(st + 1);
+    const uint8_t* L = lds[buf];
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const uint32_t off = (kk * 16 + lg * 8) * 2;
+      v8bf af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(L + (wm * (BM / 2) + i * 32 + lr) * kPitch + off));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(L + (BM + wn * (BN / 2) + j * 32 + lr) * kPitch + off));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (st + 1 < steps) store_step(buf ^ 1);
+    __syncthreads();
+  }
+
+  float sab = 1.0f;
+  if constexpr (SRC == FMT_NVFP4) sab = *a_ts * b_ts[g];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = n0 + wn * (BN / 2) + j * 32 + lr;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + wm * (BM / 2) + i * 32 + 8 * (v / 4) + 4 * lg + (v % 4);
+        if (row < g_hi && col < N) {
+          const float val = SRC == FMT_NVFP4 ? acc[i][j][v] * sab : acc[i][j][v];
+          if constexpr (CDT == DT_F32) static_cast<float*>(C)[row * ldc + col] = val;
+          else static_cast<uint16_t*>(C)[row * ldc + col] = f32_to_bf16(val);
+        }
+      }
+    }
+}
+
+template <int SRC, int CDT, int BM, int BN, bool GATHER>
+hipError_t run(const uint8_t* a, const uint8_t* sa, const float* ats, const int32_t* ri, int64_t R,
+               const uint8_t* b, const uint8_t* sb, const float* bts, int32_t groups,
+               const int64_t* off, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
+  const uint32_t tn = (uint32_t)((N + BN - 1) / BN);
+  const uint32_t tmb = (uint32_t)((R + BM - 1) / BM + (off ? groups : 0));
+  hipLaunchKernelGGL((k_gemm_staged<SRC, CDT, BM, BN, GATHER>), dim3(tn * tmb), dim3(256), 0, s,
+                     a, sa, ats, ri, R, b, sb, bts, groups, off, N, K, C, ldc, tn, tmb);
+  return hipGetLastError();
+}
+
+template <int SRC, int CDT, bool GATHER>
+hipError_t run_sized(const uint8_t* a, const uint8_t* sa, const float* ats, const int32_t* ri,
+                     int64_t R, const uint8_t* b, const uint8_t* sb, const float* bts,
+                     int32_t groups, const int64_t* off, int64_t N, int64_t K, void* C,
+                     int64_t ldc, hipStream_t s) {
+  if (R * N >= (int64_t)256 * 256 * 192)
+    return run<SRC, CDT, 256, 256, GATHER>(a, sa, ats, ri, R, b, sb, bts, groups, off, N, K, C, ldc, s);
+  return run<SRC, CDT, 128, 128, GATHER>(a, sa, ats, ri, R, b, sb, bts, groups, off, N, K, C, ldc, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                             const int32_t* row_index, int64_t routed_rows,
+                             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
+                             int32_t groups, const int64_t* offsets, int64_t N, int64_t K,
+                             void* C, int cdt, int64_t ldc, hipStream_t s) {
+  if (routed_rows == 0 || N == 0) return hipSuccess;
+#define MXK_NV(D, G) \
+  run_sized<FMT_NVFP4, D, G>(a_codes, a_scales, a_ts, row_index, routed_rows, b_codes, b_scales, b_ts, groups, offsets, N, K, C, ldc, s)
+  if (row_index) return cdt == DT_F32 ? MXK_NV(DT_F32, true) : MXK_NV(DT_BF16, true);
+  return cdt == DT_F32 ? MXK_NV(DT_F32, false) : MXK_NV(DT_BF16, false);
+#undef MXK_NV
+}
+
+hipError_t launch_gemm_mxfp8_exact(const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                   int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
+                                   hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (cdt == DT_F32)
+    return run_sized<FMT_MXFP8, DT_F32, false>(a_codes, a_scales, nullptr, nullptr, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
+  return run_sized<FMT_MXFP8, DT_BF16, false>(a_codes, a_scales, nullptr, nullptr, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
+}
+
+}  // namespace mxk

@@ -42,6 +42,10 @@ hipError_t launch_requant_transpose(const uint8_t* src_codes, const uint8_t* src
 hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
                           int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s);
+hipError_t launch_gemm_mxfp8_exact(const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                   int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
+                                   hipStream_t s);
 hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                              const int32_t* row_index, int64_t routed_rows,
                              const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
