@@ -12,23 +12,36 @@
 //        in nibble k (low nibble first) -- the packed bytes verbatim.
 //   FP8: lane l holds 32 bytes: bytes 0..15 are elements 16*(l/32) .. +15 of
 //        K-block 0 and bytes 16..31 the same positions of K-block 1.
+// The FP4 form of this instruction runs at twice the FP8 rate; the 16x16x128
+// FP4 form only at the FP8 rate (measured), so 32x32x64 is used.
 //
 // MXFP4 is exact on this instruction (FP32 accumulation of exact products).
-// The FP8 variant is offered as the hardware-native MXFP8 path: gfx950 sums
-// the FP8 products of each 8-element group in a narrow aligned window (about
-// 14 bits below the group's largest product) before FP32 accumulation, so it
-// does not meet a 1e-5 relative bound in general.  The exact MXFP8 GEMM is the
+// The FP8 variant is the hardware-native MXFP8 path: gfx950 sums the FP8
+// products of each 8-element group in a narrow aligned window (about 14 bits
+// below the group's largest product) before FP32 accumulation, so it does not
+// meet a 1e-5 relative bound in general; the exact MXFP8 GEMM is the
 // BF16-staged kernel in gemm_staged.hip.
 //
-// Kernel structure: 256 threads (4 waves in 2x2), a BM x BN C tile per
-// workgroup, (BM/2) x (BN/2) per wave as 32x32 instruction tiles.  Each K
-// step moves 64 code bytes per row (FP4: 128 elements, two instructions;
-// FP8: 64 elements, one instruction) plus the row's scale bytes for that step
-// into a double-buffered LDS tile whose row pitch (80 bytes) keeps the
-// 16-byte fragment reads of 8 consecutive rows on distinct banks.  The scale
-// dword sits in the row's padding.  Workgroup -> tile mapping keeps the
-// tiles of one XCD (workgroups are dealt round-robin over the 8 XCDs)
-// adjacent in M and N for L2 reuse.
+// Pipelined kernel (K a multiple of the step): 256 threads (4 waves, 2x2), a
+// 256x256 C tile per workgroup, 128x128 per wave (4x4 instruction tiles, 256
+// accumulator registers), one workgroup per CU.  Each K step moves one
+// 128-byte segment per row (FP4: 256 elements, four instruction slices; FP8:
+// 128 elements, two) plus the row's scale bytes of the step, straight from
+// global memory into LDS with global_load_lds (no register staging), two
+// stage buffers deep.  Full 128-byte segments stream markedly faster than
+// half lines (measured).  The 16-byte chunks of a row are XOR-swizzled by
+// (row & 7), so fragment reads of 8 consecutive rows hit distinct bank
+// groups.  Slice fragments are double-buffered in registers; a wave waits for
+// the next stage and joins the one barrier of the step just before the last
+// slice's matrix instructions, so the refill of the stage just consumed and
+// the first reads of the next stage overlap that slice.  The epilogue
+// stages each wave's accumulator tile through LDS and writes C rows with
+// 16-byte stores.  Workgroup -> tile mapping keeps the tiles of one XCD
+// (workgroups are dealt round-robin over the 8 XCDs) adjacent in M and N for
+// L2 reuse.
+//
+// A simple kernel (register-staged, 128x128 tiles, any K % 32 == 0) covers
+// shapes the pipelined one does not take.
 #include "../device/codec.h"
 #include "../launch.h"
 
@@ -38,9 +51,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-
-constexpr int kPitch = 80;     // LDS bytes per row: 64 code bytes, 4 scale bytes, pad
-constexpr int kRowBytes = 64;  // code bytes per row per K step
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));  // plain vector: stays in registers
 
 template <int FMT>
 struct StepCfg {
@@ -58,8 +69,7 @@ __device__ inline void tile_of(uint32_t id, uint32_t tm, uint32_t tn, uint32_t* 
     const uint32_t per = total >> 3;
     lin = (id & 7u) * per + (id >> 3);
   }
-  // grouped order: groups of G tile-rows, column-major inside a group
-  const uint32_t G = 4;
+  const uint32_t G = 4;  // groups of G tile-rows, column-major inside a group
   const uint32_t group = lin / (G * tn);
   const uint32_t first_m = group * G;
   const uint32_t gsize = (tm - first_m) < G ? (tm - first_m) : G;
@@ -68,20 +78,354 @@ __device__ inline void tile_of(uint32_t id, uint32_t tm, uint32_t tn, uint32_t* 
   *n = in / gsize;
 }
 
-template <int FMT, int CDT, int BM, int BN>
-__global__ __launch_bounds__(256) void k_gemm_mx(const uint8_t* __restrict__ A,
-                                                 const uint8_t* __restrict__ SA,
-                                                 const uint8_t* __restrict__ B,
-                                                 const uint8_t* __restrict__ SB, int64_t M,
-                                                 int64_t N, int64_t K, void* __restrict__ C,
-                                                 int64_t ldc, uint32_t tiles_m, uint32_t tiles_n) {
-  using SC = StepCfg<FMT>;
-  constexpr int kRows = BM + BN;
-  constexpr int kPieces = kRows * (kRowBytes / 16) / 256;  // 16-byte code pieces per thread
-  constexpr int kScaleLoads = (kRows + 255) / 256;         // scale dwords per thread
-  constexpr int FM = BM / 2 / 32, FN = BN / 2 / 32;        // instruction tiles per wave
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kRows * kPitch];
+template <int CDT>
+__device__ inline void store_c(void* C, int64_t ldc, int64_t row, int64_t col, float v) {
+  if constexpr (CDT == DT_F32) static_cast<float*>(C)[row * ldc + col] = v;
+  else static_cast<uint16_t*>(C)[row * ldc + col] = f32_to_bf16(v);
+}
 
+// ---------------------------------------------------------------------------
+// pipelined kernel
+// ---------------------------------------------------------------------------
+constexpr int kTile = 256;                  // BM = BN
+constexpr int kRowsAll = 2 * kTile;         // A rows then B rows in a stage
+constexpr int kSeg = 128;                   // code bytes per row per K step
+constexpr int kCodeBytes = kRowsAll * kSeg; // 64 KB
+constexpr int kScaleBytes = kRowsAll * 8;   // two scale dwords per row (FP8 uses one)
+constexpr int kStageBytes = kCodeBytes + kScaleBytes;
+constexpr int kStages = 2;
+
+// Workgroup barrier for the DMA pipeline: this wave's LDS reads are complete
+// (lgkmcnt 0) and the compiler may not move memory accesses across it, but
+// DMAs still in flight are not waited for (a memory fence would drain them).
+__device__ inline void dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt limiting only the vector-memory counter (gfx9 encoding: vmcnt in
+// bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// K slices (64-element instructions) per step and scale dwords per row
+template <int FMT>
+struct PipeCfg {
+  static constexpr int kSlices = FMT == FMT_MXFP8 ? 2 : 4;
+  static constexpr int kKElems = FMT == FMT_MXFP8 ? 128 : 256;
+  static constexpr int kScaleDw = FMT == FMT_MXFP8 ? 1 : 2;
+};
+
+// Copy assignment of one thread: wave-uniform operand bases (waves 0-1 copy
+// A rows, waves 2-3 B rows) and 32-bit per-lane byte offsets.  Code
+// instruction i of wave w fills LDS rows 8*(16w+i) .. +7 (8 lanes per
+// 128-byte row); scale instruction j fills scale dword (j & 1) of rows
+// 64*(4*(w%2) + j/2) + lane ... for the wave's operand.
+struct PipeCtx {
+  const uint8_t* cbase;
+  const uint8_t* sbase;
+  uint32_t coff[16];
+  uint32_t soff[4];
+  uint32_t wid;
+};
+
+template <int FMT>
+__device__ inline void issue_stage(const PipeCtx& x, uint32_t step, uint8_t* __restrict__ stage) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(x.cbase + (x.coff[i] + step * (uint32_t)kSeg)),
+                                     (lds_ptr_t)(stage + (8u * (16u * x.wid + i)) * kSeg), 16, 0, 0);
+  // scales: per operand 256 rows x kScaleDw dwords; waves (2 per operand)
+  // take 128 rows each, one instruction per 64 rows and dword
+  constexpr int kDw = PipeCfg<FMT>::kScaleDw;
+  const uint32_t op = x.wid >> 1, half = x.wid & 1u;
+#pragma unroll
+  for (int j = 0; j < 2 * kDw; ++j) {
+    const uint32_t dw = j % kDw, blk = j / kDw;  // dword index, 64-row block within the wave's 128
+    const uint32_t row = op * kTile + half * 128u + blk * 64u;
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(x.sbase + (x.soff[j] + step * 4u * kDw + 4u * dw)),
+                                     (lds_ptr_t)(stage + kCodeBytes + dw * (kRowsAll * 4) + row * 4u), 4, 0, 0);
+  }
+}
+template <int FMT>
+constexpr int dma_per_stage() { return 16 + 2 * PipeCfg<FMT>::kScaleDw; }
+
+// Fragments of one K slice for one wave (16 bytes per operand tile; FP8 keeps
+// the lane's second 16 bytes in the *hi arrays).
+template <int FMT>
+struct Slice {
+  u4 a[4], b[4];
+  u4 ahi[FMT == FMT_MXFP8 ? 4 : 1], bhi[FMT == FMT_MXFP8 ? 4 : 1];
+};
+
+// LDS byte offset of logical 16-byte chunk c of stage row r (chunks of a row
+// are XOR-swizzled by the row's low 3 bits: 8 consecutive rows reading the
+// same logical chunk hit 8 different bank groups).
+__device__ inline uint32_t chunk_off(uint32_t r, uint32_t c) { return r * kSeg + 16u * (c ^ (r & 7u)); }
+
+template <int FMT>
+__device__ inline void load_slice(const uint8_t* __restrict__ L, uint32_t q, uint32_t wm, uint32_t wn,
+                                  uint32_t lr, uint32_t lg, Slice<FMT>& f) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t r = t < 4 ? wm * 128 + t * 32 + lr : kTile + wn * 128 + (t - 4) * 32 + lr;
+    if constexpr (FMT == FMT_MXFP8) {
+      const u4 x0 = *reinterpret_cast<const u4*>(L + chunk_off(r, 4 * q + lg));
+      const u4 x1 = *reinterpret_cast<const u4*>(L + chunk_off(r, 4 * q + 2 + lg));
+      if (t < 4) { f.a[t] = x0; f.ahi[t] = x1; }
+      else { f.b[t - 4] = x0; f.bhi[t - 4] = x1; }
+    } else {
+      const u4 x0 = *reinterpret_cast<const u4*>(L + chunk_off(r, 2 * q + lg));
+      if (t < 4) f.a[t] = x0;
+      else f.b[t - 4] = x0;
+    }
+  }
+}
+
+// raw scale dwords of the wave's rows for one stage
+struct Scales {
+  uint32_t a[2][4], b[2][4];
+};
+template <int FMT>
+__device__ inline void load_scales(const uint8_t* __restrict__ L, uint32_t wm, uint32_t wn,
+                                   uint32_t lr, Scales& s) {
+  const uint8_t* LS = L + kCodeBytes;
+#pragma unroll
+  for (int d = 0; d < PipeCfg<FMT>::kScaleDw; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s.a[d][i] = *reinterpret_cast<const uint32_t*>(LS + d * (kRowsAll * 4) + (wm * 128 + i * 32 + lr) * 4);
+      s.b[d][i] = *reinterpret_cast<const uint32_t*>(LS + d * (kRowsAll * 4) + (kTile + wn * 128 + i * 32 + lr) * 4);
+    }
+}
+
+__device__ inline v8i widen(u4 lo, u4 hi) {
+  return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+__device__ inline v8i widen4(u4 lo) {
+  return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+}
+
+// 16 MFMAs of K slice q.  The lane's scale byte for slice q is byte
+// (2q + lg) of the step's scale bytes: dword (2q + lg) / 4, selected by
+// shifting lg bytes down and opsel = 2 * (q % 2) (FP4), or opsel = 2q (FP8).
+template <int FMT, int Q>
+__device__ inline void mfma_slice(const Slice<FMT>& f, const Scales& sc, uint32_t lg,
+                                  v16f (&acc)[4][4]) {
+  constexpr int D = FMT == FMT_MXFP8 ? 0 : Q / 2;
+  constexpr int OPSEL = FMT == FMT_MXFP8 ? 2 * Q : 2 * (Q % 2);
+  uint32_t sa[4], sb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sa[i] = sc.a[D][i] >> (8 * lg);
+    sb[i] = sc.b[D][i] >> (8 * lg);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (FMT == FMT_MXFP8)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f.a[i], f.ahi[i]), widen(f.b[j], f.bhi[j]), acc[i][j], 0, 0, OPSEL, (int)sa[i], OPSEL, (int)sb[j]);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen4(f.a[i]), widen4(f.b[j]), acc[i][j], 4, 4, OPSEL, (int)sa[i], OPSEL, (int)sb[j]);
+    }
+}
+
+// Epilogue through LDS: each wave writes its 128x128 accumulator tile into
+// LDS in 64-row halves and stores it back row-contiguous, 16 bytes per lane.
+template <int CDT>
+__device__ inline void store_tile(uint8_t* __restrict__ smem, const v16f (&acc)[4][4], void* C,
+                                  int64_t ldc, int64_t M, int64_t N, int64_t r0, int64_t c0,
+                                  bool vec, uint32_t wid, uint32_t lane) {
+  constexpr int EB = CDT == DT_F32 ? 4 : 2;   // bytes per element
+  constexpr int PITCH = 128 * EB + 16;        // LDS row pitch (bank spread)
+  uint8_t* W = smem + wid * (64 * PITCH);
+  const uint32_t lr = lane & 31u, lg = lane >> 5;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {           // row halves 0..63, 64..127 of the wave tile
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) {      // instruction-tile rows inside the half
+      const int i = 2 * h + i2;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t row = i2 * 32 + 8 * (v / 4) + 4 * lg + (v % 4);
+          const uint32_t col = j * 32 + lr;
+          if constexpr (CDT == DT_F32) *reinterpret_cast<float*>(W + row * PITCH + col * 4) = acc[i][j][v];
+          else *reinterpret_cast<uint16_t*>(W + row * PITCH + col * 2) = f32_to_bf16(acc[i][j][v]);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // own LDS writes done
+    asm volatile("" ::: "memory");
+    // 64 rows x (128 * EB) bytes; each lane moves 16 bytes per step
+    constexpr int LPR = 128 * EB / 16;  // lanes per row
+    constexpr int RPI = 64 / LPR;       // rows per instruction
+#pragma unroll
+    for (int k = 0; k < 64 / RPI; ++k) {
+      const uint32_t row = k * RPI + lane / LPR;
+      const uint32_t cb = (lane % LPR) * 16;
+      const u4 val = *reinterpret_cast<const u4*>(W + row * PITCH + cb);
+      const int64_t grow = r0 + h * 64 + row;
+      const int64_t gcol = c0 + cb / EB;
+      if (grow < M) {
+        if (vec && gcol + 16 / EB <= N) {
+          *reinterpret_cast<u4*>(static_cast<uint8_t*>(C) + (grow * ldc + gcol) * EB) = val;
+        } else {
+          for (int e = 0; e < 16 / EB; ++e)
+            if (gcol + e < N) {
+              if constexpr (CDT == DT_F32) static_cast<uint32_t*>(C)[grow * ldc + gcol + e] = val[e];
+              else static_cast<uint16_t*>(C)[grow * ldc + gcol + e] = (uint16_t)(val[e / 2] >> (16 * (e & 1)));
+            }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // reads done before reuse
+    asm volatile("" ::: "memory");
+  }
+}
+
+// One workgroup per CU (256 accumulator registers per lane).
+template <int FMT, int CDT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx_pipe(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, void* __restrict__ C,
+    int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t vec) {
+  using PC = PipeCfg<FMT>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint32_t tmi, tni;
+  tile_of(blockIdx.x, tiles_m, tiles_n, &tmi, &tni);
+  const int64_t m0 = (int64_t)tmi * kTile, n0 = (int64_t)tni * kTile;
+  const uint32_t t = threadIdx.x;
+  const uint32_t lane = t & 63u, wid = t >> 6;
+  const uint32_t wm = wid >> 1, wn = wid & 1u;
+  const int64_t rowbytes = FMT == FMT_MXFP8 ? K : K / 2;
+  const int64_t kblocks = K / 32;
+  const uint32_t steps = (uint32_t)(K / PC::kKElems);
+
+  // Code instruction i of wave w: LDS row r = 8*(16w+i) + lane/8, physical
+  // chunk p = lane%8 holding logical chunk p ^ (r & 7).  Rows past M / N read
+  // the last valid row (their results are not stored).
+  PipeCtx x;
+  x.wid = wid;
+  const bool waveA = wid < 2;
+  x.cbase = waveA ? A : B;
+  x.sbase = waveA ? SA : SB;
+  const int64_t lim = waveA ? M : N;
+  const int64_t row0 = waveA ? m0 : n0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t r = 8u * (16u * wid + i) + (lane >> 3);
+    const uint32_t c = (lane & 7u) ^ (r & 7u);
+    int64_t grow = row0 + (r & (kTile - 1));
+    grow = grow < lim ? grow : lim - 1;
+    x.coff[i] = (uint32_t)(grow * rowbytes) + 16u * c;
+  }
+#pragma unroll
+  for (int j = 0; j < 2 * PC::kScaleDw; ++j) {
+    const uint32_t blk = j / PC::kScaleDw;
+    int64_t grow = row0 + (wid & 1u) * 128u + blk * 64u + lane;
+    grow = grow < lim ? grow : lim - 1;
+    x.soff[j] = (uint32_t)(grow * kblocks);
+  }
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // Two LDS stages.  Within stage st the K slices run with their fragments
+  // double-buffered in registers; before the last slice of stage st the wave
+  // waits for stage st+1's DMAs and joins the barrier (all waves then hold
+  // every fragment of stage st, so its buffer is refilled with stage st+2)
+  // and starts reading stage st+1's first slice.
+  const uint32_t lr = lane & 31u, lg = lane >> 5;
+  constexpr int DPS = dma_per_stage<FMT>();
+  issue_stage<FMT>(x, 0, smem);
+  if (steps > 1) {
+    issue_stage<FMT>(x, 1, smem + kStageBytes);
+    wait_vmcnt<DPS>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  dma_barrier();
+  Slice<FMT> S0, S1;
+  Scales sc, scn;
+  load_scales<FMT>(smem, wm, wn, lr, sc);
+  load_slice<FMT>(smem, 0, wm, wn, lr, lg, S0);
+  for (uint32_t st = 0; st < steps; ++st) {
+    uint8_t* cur = smem + (st & 1u) * kStageBytes;
+    uint8_t* nxt = smem + ((st + 1u) & 1u) * kStageBytes;
+    if constexpr (PC::kSlices == 4) {
+      load_slice<FMT>(cur, 1, wm, wn, lr, lg, S1);
+      mfma_slice<FMT, 0>(S0, sc, lg, acc);
+      load_slice<FMT>(cur, 2, wm, wn, lr, lg, S0);
+      mfma_slice<FMT, 1>(S1, sc, lg, acc);
+      load_slice<FMT>(cur, 3, wm, wn, lr, lg, S1);
+      mfma_slice<FMT, 2>(S0, sc, lg, acc);
+    } else {
+      load_slice<FMT>(cur, 1, wm, wn, lr, lg, S1);
+      mfma_slice<FMT, 0>(S0, sc, lg, acc);
+    }
+    // stage st fully in registers: switch buffers
+    if (st + 1 < steps) {
+      wait_vmcnt<0>();  // stage st+1 (the only stage in flight)
+      dma_barrier();
+      if (st + 2 < steps) issue_stage<FMT>(x, st + 2, cur);
+      load_scales<FMT>(nxt, wm, wn, lr, scn);
+      load_slice<FMT>(nxt, 0, wm, wn, lr, lg, S0);
+    }
+    mfma_slice<FMT, PC::kSlices - 1>(S1, sc, lg, acc);
+    sc = scn;
+  }
+
+  // epilogue: LDS is free once every wave is past its last fragment read
+  dma_barrier();
+  store_tile<CDT>(smem, acc, C, ldc, M, N, m0 + wm * 128, n0 + wn * 128, vec != 0, wid, lane);
+}
+
+template <int FMT, int CDT>
+hipError_t launch_pipe(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
+                       int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
+  const uint32_t tm = (uint32_t)((M + kTile - 1) / kTile), tn = (uint32_t)((N + kTile - 1) / kTile);
+  const size_t smem = (size_t)kStages * kStageBytes;
+  auto kern = k_gemm_mx_pipe<FMT, CDT>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  // 16-byte row stores need a 16-byte aligned C and row pitch
+  const int64_t eb = CDT == DT_F32 ? 4 : 2;
+  const uint32_t vec = ((reinterpret_cast<uintptr_t>(C) & 15u) == 0 && (ldc * eb) % 16 == 0) ? 1u : 0u;
+  hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(256), smem, s, a, sa, b, sb, M, N, K, C, ldc, tm, tn, vec);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// simple kernel: register-staged double buffer, 128x128 tiles, any K % 32
+// ---------------------------------------------------------------------------
+constexpr int kPitchS = 80;  // LDS bytes per row: 64 code bytes, 4 scale bytes, pad
+
+template <int FMT, int CDT>
+__global__ __launch_bounds__(256) void k_gemm_mx_simple(const uint8_t* __restrict__ A,
+                                                        const uint8_t* __restrict__ SA,
+                                                        const uint8_t* __restrict__ B,
+                                                        const uint8_t* __restrict__ SB, int64_t M,
+                                                        int64_t N, int64_t K, void* __restrict__ C,
+                                                        int64_t ldc, uint32_t tiles_m,
+                                                        uint32_t tiles_n) {
+  using SC = StepCfg<FMT>;
+  constexpr int BM = 128, BN = 128, kRows = BM + BN;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kRows * kPitchS];
   uint32_t tmi, tni;
   tile_of(blockIdx.x, tiles_m, tiles_n, &tmi, &tni);
   const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
@@ -92,129 +436,83 @@ __global__ __launch_bounds__(256) void k_gemm_mx(const uint8_t* __restrict__ A,
   const int64_t kblocks = K / 32;
   const int64_t steps = (K + SC::kKElems - 1) / SC::kKElems;
 
-  // global source rows of this thread's pieces (fixed over the K loop)
-  const uint8_t* src[kPieces];
-  uint32_t piece_off[kPieces];
+  uint4 reg[4];
+  uint32_t sreg = 0;
+  auto load_step = [&](int64_t step) {
+    const int64_t kb = step * 64;
 #pragma unroll
-  for (int j = 0; j < kPieces; ++j) {
-    const uint32_t p = t + 256u * j;
-    const uint32_t r = p >> 2;
-    piece_off[j] = r * kPitch + (p & 3u) * 16;
-    const bool isA = r < (uint32_t)BM;
-    const int64_t grow = isA ? m0 + r : n0 + (r - BM);
-    const int64_t lim = isA ? M : N;
-    src[j] = (grow < lim) ? (isA ? A : B) + grow * rowbytes + (p & 3u) * 16 : nullptr;
-  }
-  const uint8_t* ssrc[kScaleLoads];
-#pragma unroll
-  for (int j = 0; j < kScaleLoads; ++j) {
-    const uint32_t r = t + 256u * j;
-    ssrc[j] = nullptr;
-    if (r < (uint32_t)kRows) {
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t p = t + 256u * j;
+      const uint32_t r = p >> 2;
       const bool isA = r < (uint32_t)BM;
       const int64_t grow = isA ? m0 + r : n0 + (r - BM);
-      const int64_t lim = isA ? M : N;
-      if (grow < lim) ssrc[j] = (isA ? SA : SB) + grow * kblocks;
-    }
-  }
-
-  uint4 reg[kPieces];
-  uint32_t sreg[kScaleLoads];
-  auto load_step = [&](int64_t step) {
-    const int64_t kb = step * kRowBytes;
-#pragma unroll
-    for (int j = 0; j < kPieces; ++j) {
-      const int64_t off = kb + (int64_t)((t + 256u * j) & 3u) * 16;
-      reg[j] = (src[j] != nullptr && off < rowbytes)
-                   ? *reinterpret_cast<const uint4*>(src[j] + kb)
+      const int64_t off = kb + (p & 3u) * 16;
+      reg[j] = (grow < (isA ? M : N) && off < rowbytes)
+                   ? *reinterpret_cast<const uint4*>((isA ? A : B) + grow * rowbytes + off)
                    : make_uint4(0, 0, 0, 0);
     }
+    const bool isA = t < (uint32_t)BM;
+    const int64_t grow = isA ? m0 + t : n0 + (t - BM);
     const int64_t b0 = step * SC::kBlocks;
-#pragma unroll
-    for (int j = 0; j < kScaleLoads; ++j) {
-      uint32_t w = 0;
-      if (ssrc[j] != nullptr) {
-        if (b0 + SC::kBlocks <= kblocks) {
-          if constexpr (SC::kBlocks == 4) w = *reinterpret_cast<const uint32_t*>(ssrc[j] + b0);
-          else w = *reinterpret_cast<const uint16_t*>(ssrc[j] + b0);
-        } else {
-          for (int i = 0; i < SC::kBlocks; ++i)
-            if (b0 + i < kblocks) w |= (uint32_t)ssrc[j][b0 + i] << (8 * i);
-        }
-      }
-      sreg[j] = w;
-    }
+    uint32_t w = 0;
+    if (grow < (isA ? M : N))
+      for (int i = 0; i < SC::kBlocks; ++i)
+        if (b0 + i < kblocks) w |= (uint32_t)(isA ? SA : SB)[grow * kblocks + b0 + i] << (8 * i);
+    sreg = w;
   };
   auto store_step = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < kPieces; ++j)
-      *reinterpret_cast<uint4*>(&lds[buf][piece_off[j]]) = reg[j];
-#pragma unroll
-    for (int j = 0; j < kScaleLoads; ++j) {
-      const uint32_t r = t + 256u * j;
-      if (r < (uint32_t)kRows) *reinterpret_cast<uint32_t*>(&lds[buf][r * kPitch + kRowBytes]) = sreg[j];
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t p = t + 256u * j;
+      *reinterpret_cast<uint4*>(&lds[buf][(p >> 2) * kPitchS + (p & 3u) * 16]) = reg[j];
     }
+    *reinterpret_cast<uint32_t*>(&lds[buf][t * kPitchS + 64]) = sreg;
   };
 
-  v16f acc[FM][FN];
+  v16f acc[2][2];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  // alignment of the per-row scale words: K % 128 == 0 (FP4) / K % 64 == 0
-  // (FP8) keeps every step's scale bytes inside the row; otherwise the byte
-  // loop above handles the tail.
   load_step(0);
   store_step(0);
   __syncthreads();
-
   const uint32_t lr = lane & 31u, lg = lane >> 5;
   for (int64_t st = 0; st < steps; ++st) {
     const int buf = (int)(st & 1);
     if (st + 1 < steps) load_step(st + 1);
     const uint8_t* L = lds[buf];
-    // scale words of this lane's rows, shifted so byte 0 is this lane's block
-    uint32_t sa[FM], sb[FN];
+    uint32_t sa[2], sb[2];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      sa[i] = *reinterpret_cast<const uint32_t*>(L + (wm * (BM / 2) + i * 32 + lr) * kPitch + kRowBytes) >> (8 * lg);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      sb[j] = *reinterpret_cast<const uint32_t*>(L + (BM + wn * (BN / 2) + j * 32 + lr) * kPitch + kRowBytes) >> (8 * lg);
+    for (int i = 0; i < 2; ++i) {
+      sa[i] = *reinterpret_cast<const uint32_t*>(L + (wm * 64 + i * 32 + lr) * kPitchS + 64) >> (8 * lg);
+      sb[i] = *reinterpret_cast<const uint32_t*>(L + (BM + wn * 64 + i * 32 + lr) * kPitchS + 64) >> (8 * lg);
+    }
 #pragma unroll
     for (int ins = 0; ins < SC::kInstr; ++ins) {
-      v8i af[FM], bf[FN];
+      v8i af[2], bf[2];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint8_t* row = L + (wm * (BM / 2) + i * 32 + lr) * kPitch;
+      for (int i = 0; i < 2; ++i) {
+        const uint8_t* ra = L + (wm * 64 + i * 32 + lr) * kPitchS;
+        const uint8_t* rb = L + (BM + wn * 64 + i * 32 + lr) * kPitchS;
         if constexpr (FMT == FMT_MXFP8) {
-          const uint4 a0 = *reinterpret_cast<const uint4*>(row + 16 * lg);
-          const uint4 a1 = *reinterpret_cast<const uint4*>(row + 32 + 16 * lg);
+          const uint4 a0 = *reinterpret_cast<const uint4*>(ra + 16 * lg), a1 = *reinterpret_cast<const uint4*>(ra + 32 + 16 * lg);
+          const uint4 b0 = *reinterpret_cast<const uint4*>(rb + 16 * lg), b1 = *reinterpret_cast<const uint4*>(rb + 32 + 16 * lg);
           af[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+          bf[i] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
         } else {
-          const uint4 a0 = *reinterpret_cast<const uint4*>(row + ins * 32 + 16 * lg);
+          const uint4 a0 = *reinterpret_cast<const uint4*>(ra + ins * 32 + 16 * lg);
+          const uint4 b0 = *reinterpret_cast<const uint4*>(rb + ins * 32 + 16 * lg);
           af[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
+          bf[i] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
         }
       }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint8_t* row = L + (BM + wn * (BN / 2) + j * 32 + lr) * kPitch;
-        if constexpr (FMT == FMT_MXFP8) {
-          const uint4 b0 = *reinterpret_cast<const uint4*>(row + 16 * lg);
-          const uint4 b1 = *reinterpret_cast<const uint4*>(row + 32 + 16 * lg);
-          bf[j] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-        } else {
-          const uint4 b0 = *reinterpret_cast<const uint4*>(row + ins * 32 + 16 * lg);
-          bf[j] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
-        }
-      }
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
+        for (int j = 0; j < 2; ++j) {
           if constexpr (FMT == FMT_MXFP8)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, (int)sa[i], 0, (int)sb[j]);
           else if (ins == 0)
@@ -226,43 +524,31 @@ __global__ __launch_bounds__(256) void k_gemm_mx(const uint8_t* __restrict__ A,
     if (st + 1 < steps) store_step(buf ^ 1);
     __syncthreads();
   }
-
-  // epilogue: lane holds C[row][col], col = lane % 32,
-  // row = 8*(v/4) + 4*(lane/32) + v%4 inside each 32x32 instruction tile
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t col = n0 + wn * (BN / 2) + j * 32 + lr;
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + wn * 64 + j * 32 + lr;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm * (BM / 2) + i * 32 + 8 * (v / 4) + 4 * lg + (v % 4);
-        if (row < M && col < N) {
-          if constexpr (CDT == DT_F32)
-            static_cast<float*>(C)[row * ldc + col] = acc[i][j][v];
-          else
-            static_cast<uint16_t*>(C)[row * ldc + col] = f32_to_bf16(acc[i][j][v]);
-        }
+        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v / 4) + 4 * lg + (v % 4);
+        if (row < M && col < N) store_c<CDT>(C, ldc, row, col, acc[i][j][v]);
       }
     }
 }
 
-template <int FMT, int CDT, int BM, int BN>
+template <int FMT, int CDT>
 hipError_t run(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, int64_t M,
                int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
-  const uint32_t tm = (uint32_t)((M + BM - 1) / BM), tn = (uint32_t)((N + BN - 1) / BN);
-  hipLaunchKernelGGL((k_gemm_mx<FMT, CDT, BM, BN>), dim3(tm * tn), dim3(256), 0, s, a, sa, b, sb,
+  const int64_t rb = FMT == FMT_MXFP8 ? K : K / 2;
+  const bool fits32 = (M > N ? M : N) * rb < ((int64_t)1 << 32) - 4096;
+  const bool pipe = fits32 && K > 0 && (K % PipeCfg<FMT>::kKElems == 0) &&
+                    M * N >= (int64_t)kTile * kTile * 128;
+  if (pipe) return launch_pipe<FMT, CDT>(a, sa, b, sb, M, N, K, C, ldc, s);
+  const uint32_t tm = (uint32_t)((M + 127) / 128), tn = (uint32_t)((N + 127) / 128);
+  hipLaunchKernelGGL((k_gemm_mx_simple<FMT, CDT>), dim3(tm * tn), dim3(256), 0, s, a, sa, b, sb,
                      M, N, K, C, ldc, tm, tn);
   return hipGetLastError();
-}
-
-template <int FMT, int CDT>
-hipError_t run_sized(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
-                     int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
-  // large problems: 256x256 tiles (one tile per CU at 4096^2); small ones
-  // keep more workgroups in flight with 128x128
-  if (M * N >= (int64_t)256 * 256 * 192) return run<FMT, CDT, 256, 256>(a, sa, b, sb, M, N, K, C, ldc, s);
-  return run<FMT, CDT, 128, 128>(a, sa, b, sb, M, N, K, C, ldc, s);
 }
 
 }  // namespace
@@ -271,12 +557,11 @@ hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scal
                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
                           int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (fmt == FMT_MXFP8) {
-    return cdt == DT_F32 ? run_sized<FMT_MXFP8, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s)
-                         : run_sized<FMT_MXFP8, DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
-  }
-  return cdt == DT_F32 ? run_sized<FMT_MXFP4, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s)
-                       : run_sized<FMT_MXFP4, DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
+  if (fmt == FMT_MXFP8)
+    return cdt == DT_F32 ? run<FMT_MXFP8, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s)
+                         : run<FMT_MXFP8, DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
+  return cdt == DT_F32 ? run<FMT_MXFP4, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s)
+                       : run<FMT_MXFP4, DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
 }
 
 }  // namespace mxk

@@ -138,3 +138,25 @@ def test_mxfp8_native_fp8_path_within_hardware_bound(shape):
     torch.cuda.synchronize()
     Chat, tol = _oracle_gemm(1, qa, qb, M, N, K)
     check_gemm(C.cpu().numpy(), Chat, tol * 100.0, False, f"native fp8 {shape}")
+
+
+@pytest.mark.parametrize("fmt,flags,cdt", [(2, 0, "bf16"), (2, 0, "f32"), (1, 1, "bf16"), (1, 1, "f32")])
+def test_pipelined_ragged_tiles_and_unaligned_ldc(fmt, flags, cdt):
+    """Shapes large enough for the 256x256 pipelined kernel, with M and N not
+    multiples of the tile and a C row pitch that is not 16-byte aligned (the
+    epilogue then falls back to element stores).  MXFP8 here runs the native
+    FP8 path (flags=1), whose bound is 100x the exact one."""
+    M, N, K = 2900, 3000, 512
+    qa, qb = _operands(fmt, M, N, K, 17)
+    dt = torch.float32 if cdt == "f32" else torch.bfloat16
+    C = torch.full((M, N + 3), float("nan"), dtype=dt, device=dev())[:, :N]
+    mx.mx_gemm_ex(upload(fmt, *qa), upload(fmt, *qb), C, flags)
+    torch.cuda.synchronize()
+    Chat, tol = _oracle_gemm(fmt, qa, qb, M, N, K)
+    check_gemm(C.float().cpu().numpy(), Chat, tol * (100.0 if flags else 1.0), cdt == "bf16",
+               f"pipelined fmt {fmt} {cdt}")
+    C2 = torch.full((M, N), float("nan"), dtype=dt, device=dev())
+    mx.mx_gemm_ex(upload(fmt, *qa), upload(fmt, *qb), C2, flags)
+    torch.cuda.synchronize()
+    check_gemm(C2.float().cpu().numpy(), Chat, tol * (100.0 if flags else 1.0), cdt == "bf16",
+               f"pipelined aligned fmt {fmt} {cdt}")
