@@ -5,7 +5,9 @@ x50) and B (weights 4096x4096 BF16, N(0, 0.02^2)) to MXFP4 E2M1 with E8M0
 scales per 32 (round-to-nearest-even), then the block-scaled GEMM
 C = A * B^T (4096^3, FP32 accumulation, BF16 out).  Inputs are resident in
 HBM before the timed region and rotate over 16 copies (1 GiB of BF16) so the
-256 MB last-level cache does not hold them between steps.
+256 MB last-level cache does not hold them between steps.  The step's three
+calls are launched eagerly (--graph replays them from a HIP graph captured
+once per input slot instead).
 
 Prints one JSON line: metric / value (TFLOP/s of the whole step: 2*M*N*K per
 step time), the roofline of the dominant kernel (the GEMM) measured with HIP
@@ -39,10 +41,40 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-detail", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a HIP graph captured through the C ABI "
+                         "instead of launching its calls eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="output rows of the GEMM sample the oracle is timed on")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device copy (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+# HBM traffic of the GEMM kernel from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes, stored with the hash of the kernel source they were taken on: a
+# changed kernel reports null until the counters are taken again.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mxfp4_4096_traffic.txt")
+GEMM_SOURCE = os.path.join(ROOT, "microscaling_precision_gemm_amd", "csrc", "kernels", "gemm_mx.hip")
+
+
+def gemm_traffic():
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith("#"):
+                k, v = ln.split(":", 1)
+                kv[k.strip()] = v.strip()
+    with open(GEMM_SOURCE, "rb") as f:
+        h = hashlib.sha256(f.read()).hexdigest()
+    if kv.get("kernel_source_sha256") != h or "hbm_bytes_per_launch" not in kv:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
 
 
 class Timer:
@@ -87,6 +119,11 @@ def upload_bf16(torch, bits: np.ndarray):
 
 
 def headline(torch, mx, W, args):
+    """Timed region: `steps` steps of eager launches (quantize A, quantize B,
+    GEMM), or with --graph replays of one HIP graph per input slot captured
+    through the C ABI.  Then the kernel-timing region: the same calls
+    launched eagerly, each bracketed by HIP events on the stream they run on
+    (events between the launches of the timed region would stall it)."""
     M = N = K = 4096
     A_bits, B_bits = W.cfg2(0, 4096)
     A0 = upload_bf16(torch, A_bits)
@@ -97,32 +134,55 @@ def headline(torch, mx, W, args):
     qa = mx.empty(mx.MX_MXFP4_E2M1, M, K)
     qb = mx.empty(mx.MX_MXFP4_E2M1, N, K)
     C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    tq, tg = Timer(torch), Timer(torch)
 
-    def step(i, timed):
-        a, b = As[i % nrot], Bs[i % nrot]
-        s = tq.start() if timed else None
-        mx.mx_quantize(a, qa, mx.MX_RNE)
-        if timed:
-            tq.stop(s)
-            s = tq.start()
-        mx.mx_quantize(b, qb, mx.MX_RNE)
-        if timed:
-            tq.stop(s)
-            s = tg.start()
+    def launch(i):
+        mx.mx_quantize(As[i], qa, mx.MX_RNE)
+        mx.mx_quantize(Bs[i], qb, mx.MX_RNE)
         mx.mx_gemm(qa, qb, C)
-        if timed:
-            tg.stop(s)
+
+    for i in range(nrot):
+        launch(i)
+    torch.cuda.synchronize()
+    graphs = None
+    if args.graph:
+        graphs = []
+        for i in range(nrot):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                launch(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def step(i):
+        if graphs is not None:
+            graphs[i % nrot].replay()
+        else:
+            launch(i % nrot)
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, True)
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+
+    # kernel timing: every launch between its own pair of events
+    tq, tg = Timer(torch), Timer(torch)
+    for i in range(args.steps):
+        a, b = As[i % nrot], Bs[i % nrot]
+        s = tq.start()
+        mx.mx_quantize(a, qa, mx.MX_RNE)
+        tq.stop(s)
+        s = tq.start()
+        mx.mx_quantize(b, qb, mx.MX_RNE)
+        tq.stop(s)
+        s = tg.start()
+        mx.mx_gemm(qa, qb, C)
+        tg.stop(s)
+    torch.cuda.synchronize()
     flops = 2.0 * M * N * K
     gemm_ms = tg.mean_ms()
     quant_ms = tq.mean_ms()
@@ -141,34 +201,39 @@ def headline(torch, mx, W, args):
         "flops": flops,
         "A_bits": A_bits,
         "B_bits": B_bits,
+        "launch": "eager" if graphs is None else "hip graph per step",
     }
     return out
 
 
-def cpu_baseline(W, oracle, A_bits, B_bits, rows: int):
+def cpu_baseline(W, oracle, A_bits, B_bits, rows: int, min_seconds: float = 10.0):
     """The oracle, untuned, on a bounded sample of the same step: quantize
-    `rows` rows of A and all of B, then `rows` output rows of the FP64 GEMM.
-    Throughput is reported in the step's unit (TFLOP/s of 2*M*N*K-equivalent
-    work), scaled by the sampled fraction of the output."""
+    `rows` rows of A and all of B, then `rows` output rows of the FP64 GEMM,
+    repeated until at least `min_seconds` have passed.  Throughput is reported
+    in the step's unit (TFLOP/s of 2*M*N*K-equivalent work) over the sampled
+    fraction of the output."""
     oracle.lib()
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    t0 = time.perf_counter()
-    qa = oracle.quantize(np.ascontiguousarray(A_bits[:rows]), oracle.MXFP4)
-    qb = oracle.quantize(B_bits, oracle.MXFP4)
-    Ad = oracle.dequantize_f64(oracle.MXFP4, qa[0], qa[1], rows, A_bits.shape[1])
-    Bd = oracle.dequantize_f64(oracle.MXFP4, qb[0], qb[1], B_bits.shape[0], B_bits.shape[1])
-    oracle.gemm(Ad, Bd)
-    dt = time.perf_counter() - t0
     M, K = A_bits.shape
     N = B_bits.shape[0]
-    # the sample does rows/M of the GEMM and (rows + N)/(M + N) of the quantization;
-    # charge it the GEMM fraction of the step's flops
-    sample_flops = 2.0 * rows * N * K
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        qa = oracle.quantize(np.ascontiguousarray(A_bits[:rows]), oracle.MXFP4)
+        qb = oracle.quantize(B_bits, oracle.MXFP4)
+        Ad = oracle.dequantize_f64(oracle.MXFP4, qa[0], qa[1], rows, K)
+        Bd = oracle.dequantize_f64(oracle.MXFP4, qb[0], qb[1], N, K)
+        oracle.gemm(Ad, Bd)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    sample_flops = 2.0 * rows * N * K * reps
     return {"value": sample_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "seconds": dt,
-            "sample": f"MXFP4 quantize of {rows} rows of A and all 4096 rows of B, then "
-                      f"{rows} of the 4096 output rows of the FP64 GEMM (K=4096); "
-                      f"throughput = 2*{rows}*{N}*{K} / time"}
+            "sample": f"{reps} repetitions of: MXFP4 quantize of {rows} rows of A and all {N} rows "
+                      f"of B, then {rows} of the {M} output rows of the FP64 GEMM (K={K}); "
+                      f"throughput = {reps}*2*{rows}*{N}*{K} / time"}
 
 
 def detail(torch, mx, W, args):
@@ -282,9 +347,16 @@ def main():
     import workloads as W
     mx.load()
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     h = headline(torch, mx, W, args)
     roof = {"bound": "mfma", "achieved": h["gemm_tflops"], "peak": PEAK_TFLOPS["fp4"],
-            "unit": "TFLOP/s", "frac": h["gemm_tflops"] / PEAK_TFLOPS["fp4"], "traffic": None,
+            "unit": "TFLOP/s", "frac": h["gemm_tflops"] / PEAK_TFLOPS["fp4"], "traffic": gemm_traffic(),
+            "traffic_unit": "bytes per launch", "algorithmic_bytes": 2 * 4096 * 4096 * (0.5 + 1 / 32) + 4096 * 4096 * 2,
             "kernel": "k_gemm_mx<MXFP4, BF16 out, 256x256>", "gemm_ms": h["gemm_ms"]}
     line = {
         "metric": "block-scaled GEMM TFLOPS (MXFP4/NVFP4/MXFP8 4096^3) + quantize HBM GB/s",
@@ -297,12 +369,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4 (e2m1 codes, e8m0 scales) -> fp32 accumulate -> bf16",
+        "dtype": "mxfp4",
         "data": "synthetic",
         "config": {"workload": "MXFP4 E2M1 quantize (RNE, E8M0/32) of A 4096x4096 BF16 N(0,1) "
                                "with 1% of K-columns x50 and B 4096x4096 BF16 N(0,0.02^2), then "
                                "block-scaled GEMM M=N=K=4096, FP32 accumulate, BF16 out",
-                   "M": 4096, "N": 4096, "K": 4096, "input_rotation": 16},
+                   "M": 4096, "N": 4096, "K": 4096, "input_rotation": 16, "launch": h["launch"]},
         "roofline": roof,
         "quantize": {"ms_per_operand": h["quant_ms"], "achieved_gbs": h["quant_gbs"],
                      "peak_gbs": PEAK_HBM_GBS, "frac": h["quant_gbs"] / PEAK_HBM_GBS,

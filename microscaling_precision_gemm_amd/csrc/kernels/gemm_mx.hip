@@ -42,6 +42,8 @@
 //
 // A simple kernel (register-staged, 128x128 tiles, any K % 32 == 0) covers
 // shapes the pipelined one does not take.
+#include <atomic>
+
 #include "../device/codec.h"
 #include "../launch.h"
 
@@ -401,8 +403,19 @@ hipError_t launch_pipe(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
   const uint32_t tm = (uint32_t)((M + kTile - 1) / kTile), tn = (uint32_t)((N + kTile - 1) / kTile);
   const size_t smem = (size_t)kStages * kStageBytes;
   auto kern = k_gemm_mx_pipe<FMT, CDT>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  // The dynamic LDS limit is raised once per device (bit d of a mask), so
+  // that later launches -- including those recorded into a HIP graph --
+  // make no call beyond the launch itself.
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_done.fetch_or(bit, std::memory_order_acq_rel);
+  }
   // 16-byte row stores need a 16-byte aligned C and row pitch
   const int64_t eb = CDT == DT_F32 ? 4 : 2;
   const uint32_t vec = ((reinterpret_cast<uintptr_t>(C) & 15u) == 0 && (ldc * eb) % 16 == 0) ? 1u : 0u;
