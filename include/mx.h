@@ -25,8 +25,9 @@
  *     never allocates, frees or synchronizes.
  *   - Execution: every call enqueues work on `stream` (NULL = the default
  *     stream) and returns before the work has run.  Buffers must stay alive
- *     until the stream reaches the work.  Calls are thread-safe; the library
- *     keeps no global state.
+ *     until the stream reaches the work.  Calls are thread-safe; the only
+ *     state the library keeps is a per-device flag recording that a kernel's
+ *     dynamic LDS limit has been raised (set on first use, idempotent).
  *   - Errors: arguments are checked on the host before anything is enqueued
  *     (no HIP call happens on a failed check).  A failed check returns
  *     MX_ERR_NULL / MX_ERR_SHAPE / MX_ERR_ALIGN / MX_ERR_FORMAT /
