@@ -3,11 +3,18 @@
 //
 // All kernels here are HBM-bound streaming kernels.  Work unit: a "chunk" of
 // 8 consecutive elements of a row, held by one lane (one 128-bit BF16 load).
-// A 64-lane wave covers 64 consecutive chunks, so an MX block of 32 elements
-// is one lane quad and an NVFP4 block of 16 (or a Hadamard group of 16) is one
-// lane pair; block maxima and the stride-8 butterfly use DPP quad permutes.
+// A 64-lane wave covers a slab of 64 consecutive chunks, so an MX block of 32
+// elements is one lane quad and an NVFP4 block of 16 (or a Hadamard group of
+// 16) is one lane pair; block maxima and the stride-8 butterfly use DPP quad
+// permutes.  Each wave owns kU consecutive slabs and issues all their loads
+// before any arithmetic, so every lane keeps kU 128-bit loads in flight.
 // Codes are stored with one 64-bit (MXFP8) or 32-bit (FP4) store per lane and
 // the scale bytes of 4 blocks are gathered into one 32-bit store.
+//
+// Chunk q of a [rows, cols] matrix is chunk q % (cols/8) of row q / (cols/8);
+// blocks never straddle rows (cols is a multiple of the block), so block,
+// scale and random-number indices are all linear in q and only the input
+// address needs the row (a division, skipped when rows are dense).
 //
 // Method sources: "Microscaling (MX) and block-scaled 4-bit formats"
 // (sections "Microscaling", "The idea", "NVFP4", glossary "scale factor",
@@ -23,61 +30,70 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Walks chunk indices q = q0 + lane with a wave-uniform q0, tracking
-// (row, chunk-in-row) incrementally so the loop needs no integer division.
-struct ChunkWalk {
-  int64_t q0, row, c8;  // position of lane 0 of this wave
-  int64_t step, step_rows, step_rem, cpr;
-  __device__ void init(int64_t start, int64_t stride, int64_t cpr_) {
-    cpr = cpr_;
-    q0 = start;
-    row = start / cpr;
-    c8 = start - row * cpr;
-    step = stride;
-    step_rows = stride / cpr;
-    step_rem = stride - step_rows * cpr;
-  }
-  __device__ void advance() {
-    q0 += step;
-    row += step_rows;
-    c8 += step_rem;
-    if (c8 >= cpr) {
-      c8 -= cpr;
-      row += 1;
-    }
-  }
-  // (row, chunk-in-row) of this lane's chunk
-  __device__ void lane_pos(uint32_t lane, int64_t* r, int64_t* c) const {
-    int64_t cc = c8 + lane, rr = row;
-    while (cc >= cpr) {  // at most 64 / cpr + 1 steps; cpr >= 2
-      cc -= cpr;
-      rr += 1;
-    }
-    *r = rr;
-    *c = cc;
-  }
+constexpr int kU = 4;  // slabs (64 chunks each) per wave
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// Element offset of chunk q in a [rows, cols] matrix with row pitch ld
+// (cpr = cols / 8 chunks per row).
+__device__ inline int64_t chunk_offset(int64_t q, int64_t cpr, int64_t ld, bool dense) {
+  if (dense) return 8 * q;
+  int64_t row;
+  if (q < ((int64_t)1 << 32) && cpr < ((int64_t)1 << 32))
+    row = (int64_t)((uint32_t)q / (uint32_t)cpr);
+  else
+    row = q / cpr;
+  return row * ld + 8 * (q - row * cpr);
+}
+
+// The raw bits of one chunk: 16 bytes (BF16) or 32 bytes (FP32).
+template <int XDT>
+struct Raw {
+  u4 w[XDT == DT_BF16 ? 1 : 2];
 };
 
 template <int XDT>
-__device__ inline void load8(const void* base, int64_t off, bool valid, float v[8]) {
-  if (!valid) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-    return;
-  }
+__device__ inline void load_raw(const void* base, int64_t off, Raw<XDT>& r) {
   if constexpr (XDT == DT_BF16) {
-    uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
-    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    r.w[0] = *reinterpret_cast<const u4*>(static_cast<const uint16_t*>(base) + off);
+  } else {
+    const u4* p = reinterpret_cast<const u4*>(static_cast<const float*>(base) + off);
+    r.w[0] = p[0];
+    r.w[1] = p[1];
+  }
+}
+
+// Issue the loads of the kU slabs starting at chunk q0 (this lane's chunk of
+// the first slab).  Chunks past the end (q >= Q, Q >= 1) load chunk Q - 1
+// instead, so every load is unconditional; their values are never stored.
+template <int XDT>
+__device__ inline void load_slabs(const void* x, int64_t q0, int64_t Q, int64_t cpr, int64_t ld,
+                                  bool dense, Raw<XDT> (&raw)[kU]) {
+  int64_t off[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    int64_t q = q0 + 64 * u;
+    q = q < Q ? q : Q - 1;
+    off[u] = chunk_offset(q, cpr, ld, dense);
+  }
+#pragma unroll
+  for (int u = 0; u < kU; ++u) load_raw<XDT>(x, off[u], raw[u]);
+}
+
+template <int XDT>
+__device__ inline void widen(const Raw<XDT>& r, float v[8]) {
+  if constexpr (XDT == DT_BF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = u2f(w[i] << 16);
-      v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
+      v[2 * i] = u2f(r.w[0][i] << 16);
+      v[2 * i + 1] = u2f(r.w[0][i] & 0xFFFF0000u);
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-    float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = u2f(r.w[0][i]);
+      v[4 + i] = u2f(r.w[1][i]);
+    }
   }
 }
 
@@ -140,6 +156,36 @@ __device__ inline uint32_t max_abs_bits(const float v[8]) {
   return m;
 }
 
+// Round-to-nearest-even encoders on gfx950's conversion instructions (scale
+// operand 1.0, i.e. no scaling).  Over every finite FP32 input they give the
+// same codes as the bit-arithmetic encoders of codec.h (checked exhaustively
+// on the device): E2M1 saturates to +-6 by itself; E4M3 is clamped to +-448
+// first because the instruction sends values past the largest finite
+// midpoint to NaN.  Element 2j goes to the low nibble (byte) of pair j.
+__device__ inline uint32_t pack_e2m1_rne(const float y[8]) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+  return w;
+}
+
+typedef short v2s __attribute__((ext_vector_type(2)));
+
+__device__ inline void pack_e4m3_rne(const float y[8], uint32_t w[2]) {
+  float c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = fmaxf(fminf(y[i], 448.0f), -448.0f);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    v2s p = {0, 0};
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, c[4 * h], c[4 * h + 1], 1.0f, false);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, c[4 * h + 2], c[4 * h + 3], 1.0f, true);
+    w[h] = __builtin_bit_cast(uint32_t, p);
+  }
+}
+
 // Gather the scale byte of `group` consecutive lane groups (group = 4 lanes
 // per MX block, 2 per NVFP4 block) into lane 4*group*k and store 4 bytes at a
 // time; `blocks_left` is the number of valid blocks from this lane's block on.
@@ -158,137 +204,198 @@ __device__ inline void store_scales(uint8_t* scales, int64_t block, uint32_t sc,
 }
 
 // ---- MX (E8M0 per 32) quantizer -------------------------------------------
+// Encoded chunk: 8 codes packed (FP8: two words, FP4: one) and the block's
+// scale byte.
+template <int FMT>
+struct Enc {
+  uint32_t w[FMT == FMT_MXFP8 ? 2 : 1];
+  uint32_t sc;
+};
+
+template <int FMT, bool SR>
+__device__ inline void encode_mx(const QuantArgs& a, int64_t q, const float v[8], Enc<FMT>& e) {
+  constexpr uint32_t emax = FMT == FMT_MXFP8 ? 8u : 2u;
+  uint32_t m = max_abs_bits(v);
+  uint32_t o = dpp_xor1(m);
+  m = o > m ? o : m;
+  o = dpp_xor2(m);
+  m = o > m ? o : m;
+  const uint32_t sc = e8m0_from_amax_bits(m, emax);
+  const float inv = e8m0_inverse(sc);
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = v[i] * inv;  // exact scaling by a power of two
+  if constexpr (!SR) {
+    if constexpr (FMT == FMT_MXFP8) {
+      pack_e4m3_rne(y, e.w);
+    } else {
+      e.w[0] = pack_e2m1_rne(y);
+    }
+  } else {
+    uint32_t r[8];
+    rand16x8(a.seed, a.counter, (uint64_t)q, r);
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      c[i] = FMT == FMT_MXFP8 ? e4m3_encode(y[i], true, r[i]) : e2m1_encode(y[i], true, r[i]);
+    if constexpr (FMT == FMT_MXFP8) {
+      e.w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      e.w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    } else {
+      uint32_t p = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p |= c[i] << (4 * i);
+      e.w[0] = p;
+    }
+  }
+  if (sc == 0xFFu) {  // NaN / Inf in the block
+#pragma unroll
+    for (int i = 0; i < (FMT == FMT_MXFP8 ? 2 : 1); ++i) e.w[i] = 0u;
+  }
+  e.sc = sc;
+}
+
+template <int FMT>
+__device__ inline void store_enc(const QuantArgs& a, int64_t q, int64_t Q, uint32_t lane,
+                                 uint32_t lanes_per_block, const Enc<FMT>& e) {
+  if (q < Q) {
+    if constexpr (FMT == FMT_MXFP8) {
+      *reinterpret_cast<uint2*>(a.codes + q * 8) = make_uint2(e.w[0], e.w[1]);
+    } else {
+      *reinterpret_cast<uint32_t*>(a.codes + q * 4) = e.w[0];
+    }
+  }
+  const uint32_t sh = lanes_per_block == 4 ? 2 : 1;
+  store_scales(a.scales, q >> sh, e.sc, lane, lanes_per_block, (Q - q) >> sh);
+}
+
+// Each wave: load kU slabs, encode them all, then store them all (so the
+// waits for the loads are not held up by stores).
 template <int XDT, int FMT, bool SR, bool RHT>
 __global__ __launch_bounds__(kThreads) void k_quant_mx(QuantArgs a, int64_t Q) {
   const uint32_t lane = threadIdx.x & 63u;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t cpr = a.cols >> 3;
-  constexpr uint32_t emax = FMT == FMT_MXFP8 ? 8u : 2u;
-  ChunkWalk w;
-  w.init(wave * 64, nwaves * 64, cpr);
-  for (; w.q0 < Q; w.advance()) {
-    const int64_t q = w.q0 + lane;
-    const bool valid = q < Q;
-    int64_t row, c8;
-    w.lane_pos(lane, &row, &c8);
+  const bool dense = a.ld_x == a.cols;
+  const int64_t q0 = wave * (64 * kU) + lane;
+  Raw<XDT> raw[kU];
+  load_slabs<XDT>(a.x, q0, Q, cpr, a.ld_x, dense, raw);
+  Enc<FMT> enc[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int64_t q = q0 + 64 * u;
     float v[8];
-    load8<XDT>(a.x, row * a.ld_x + 8 * c8, valid, v);
-    if constexpr (RHT) rht_forward(v, a.sign_mask, (uint32_t)(c8 & 1));
-    uint32_t m = max_abs_bits(v);
-    uint32_t o = dpp_xor1(m);
-    m = o > m ? o : m;
-    o = dpp_xor2(m);
-    m = o > m ? o : m;
-    const uint32_t sc = e8m0_from_amax_bits(m, emax);
-    const float inv = e8m0_inverse(sc);
-    uint32_t r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if constexpr (SR) rand16x8(a.seed, a.counter, (uint64_t)q, r);
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float y = v[i] * inv;  // exact scaling by a power of two
-      c[i] = FMT == FMT_MXFP8 ? e4m3_encode(y, SR, r[i]) : e2m1_encode(y, SR, r[i]);
-      if (sc == 0xFFu) c[i] = 0u;
-    }
-    if (valid) {
-      if constexpr (FMT == FMT_MXFP8) {
-        uint2 p;
-        p.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-        p.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-        *reinterpret_cast<uint2*>(a.codes + q * 8) = p;
-      } else {
-        uint32_t p = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p |= c[i] << (4 * i);
-        *reinterpret_cast<uint32_t*>(a.codes + q * 4) = p;
-      }
-    }
-    store_scales(a.scales, q >> 2, sc, lane, 4u, (Q - q) >> 2);
+    widen<XDT>(raw[u], v);
+    if constexpr (RHT) rht_forward(v, a.sign_mask, (uint32_t)(q & 1));
+    encode_mx<FMT, SR>(a, q, v, enc[u]);
   }
+#pragma unroll
+  for (int u = 0; u < kU; ++u) store_enc<FMT>(a, q0 + 64 * u, Q, lane, 4u, enc[u]);
 }
 
 // ---- NVFP4 (E4M3 per 16 + FP32 per tensor) quantizer ----------------------
+template <bool SR>
+__device__ inline void encode_nv(const QuantArgs& a, float S, float d, int64_t q, const float v[8],
+                                 Enc<FMT_NVFP4>& e) {
+#pragma clang fp contract(off)
+  uint32_t m = max_abs_bits(v);
+  uint32_t o = dpp_xor1(m);
+  m = o > m ? o : m;
+  const float qb = u2f(m) / d;
+  const uint32_t sb = e4m3_rne_mag(qb);
+  const float dsb = e4m3_mag_value(sb);
+  float rcp = 0.0f;
+  if (dsb != 0.0f) {
+    const float p = dsb * S;
+    rcp = 1.0f / p;
+  }
+  // rcp = 0 (a zero block scale) gives y = +-0 and so the codes +-0
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = v[i] * rcp;
+  if constexpr (!SR) {
+    e.w[0] = pack_e2m1_rne(y);
+  } else {
+    uint32_t r[8];
+    rand16x8(a.seed, a.counter, (uint64_t)q, r);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed |= e2m1_encode(y[i], true, r[i]) << (4 * i);
+    e.w[0] = packed;
+  }
+  e.sc = sb;
+}
+
 template <int XDT, bool SR, bool RHT>
 __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(QuantArgs a, int64_t Q) {
 #pragma clang fp contract(off)
   const uint32_t lane = threadIdx.x & 63u;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t cpr = a.cols >> 3;
+  const bool dense = a.ld_x == a.cols;
+  const int64_t q0 = wave * (64 * kU) + lane;
+  Raw<XDT> raw[kU];
+  load_slabs<XDT>(a.x, q0, Q, cpr, a.ld_x, dense, raw);
   const float T = *a.amax;
   const float S = (T == 0.0f) ? 1.0f : T / 2688.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) *a.tensor_scale = S;
   const float d = 6.0f * S;
-  ChunkWalk w;
-  w.init(wave * 64, nwaves * 64, cpr);
-  for (; w.q0 < Q; w.advance()) {
-    const int64_t q = w.q0 + lane;
-    const bool valid = q < Q;
-    int64_t row, c8;
-    w.lane_pos(lane, &row, &c8);
-    float v[8];
-    load8<XDT>(a.x, row * a.ld_x + 8 * c8, valid, v);
-    if constexpr (RHT) rht_forward(v, a.sign_mask, (uint32_t)(c8 & 1));
-    uint32_t m = max_abs_bits(v);
-    uint32_t o = dpp_xor1(m);
-    m = o > m ? o : m;
-    const float qb = u2f(m) / d;
-    const uint32_t sb = e4m3_rne_mag(qb);
-    const float dsb = e4m3_mag_value(sb);
-    float rcp = 0.0f;
-    if (dsb != 0.0f) {
-      const float p = dsb * S;
-      rcp = 1.0f / p;
-    }
-    uint32_t r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if constexpr (SR) rand16x8(a.seed, a.counter, (uint64_t)q, r);
-    uint32_t packed = 0;
+  Enc<FMT_NVFP4> enc[kU];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t c;
-      if (rcp == 0.0f) {
-        c = (f2u(v[i]) >> 28) & 0x8u;
-      } else {
-        const float y = v[i] * rcp;
-        c = e2m1_encode(y, SR, r[i]);
-      }
-      packed |= c << (4 * i);
-    }
-    if (valid) *reinterpret_cast<uint32_t*>(a.codes + q * 4) = packed;
-    store_scales(a.scales, q >> 1, sb, lane, 2u, (Q - q) >> 1);
+  for (int u = 0; u < kU; ++u) {
+    const int64_t q = q0 + 64 * u;
+    float v[8];
+    widen<XDT>(raw[u], v);
+    if constexpr (RHT) rht_forward(v, a.sign_mask, (uint32_t)(q & 1));
+    encode_nv<SR>(a, S, d, q, v, enc[u]);
   }
+#pragma unroll
+  for (int u = 0; u < kU; ++u) store_enc<FMT_NVFP4>(a, q0 + 64 * u, Q, lane, 2u, enc[u]);
+}
+
+// Empty tensor: only the tensor scale is published.
+__global__ void k_nv_scale_only(const float* amax, float* tensor_scale) {
+#pragma clang fp contract(off)
+  const float T = *amax;
+  *tensor_scale = (T == 0.0f) ? 1.0f : T / 2688.0f;
 }
 
 // ---- per-tensor amax ------------------------------------------------------
 __global__ void k_zero_f32(float* p) { *p = 0.0f; }
 
+// Grid-stride over groups of kU slabs with 1024-lane workgroups and a grid
+// of at most one workgroup per CU: every workgroup ends with one atomic max
+// on the same word, and those serialize, so the count is kept at 256.
+constexpr int kAmaxThreads = 1024;
+
 template <int XDT, bool RHT>
-__global__ __launch_bounds__(kThreads) void k_amax(const void* x, int64_t cols, int64_t ld_x,
-                                                   int64_t Q, uint32_t sign_mask, float* amax) {
+__global__ __launch_bounds__(kAmaxThreads) void k_amax(const void* x, int64_t cols, int64_t ld_x,
+                                                       int64_t Q, uint32_t sign_mask, float* amax) {
   const uint32_t lane = threadIdx.x & 63u;
-  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
-  ChunkWalk w;
-  w.init(wave * 64, nwaves * 64, cols >> 3);
+  const int64_t wave = ((int64_t)blockIdx.x * kAmaxThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kAmaxThreads) >> 6;
+  const int64_t cpr = cols >> 3;
+  const bool dense = ld_x == cols;
   uint32_t m = 0;
-  for (; w.q0 < Q; w.advance()) {
-    const int64_t q = w.q0 + lane;
-    int64_t row, c8;
-    w.lane_pos(lane, &row, &c8);
-    float v[8];
-    load8<XDT>(x, row * ld_x + 8 * c8, q < Q, v);
-    if constexpr (RHT) rht_forward(v, sign_mask, (uint32_t)(c8 & 1));
-    uint32_t b = max_abs_bits(v);
-    m = b > m ? b : m;
+  for (int64_t q0 = wave * (64 * kU) + lane; q0 - lane < Q; q0 += nwaves * (64 * kU)) {
+    Raw<XDT> raw[kU];
+    load_slabs<XDT>(x, q0, Q, cpr, ld_x, dense, raw);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float v[8];
+      widen<XDT>(raw[u], v);
+      if constexpr (RHT) rht_forward(v, sign_mask, (uint32_t)((q0 + 64 * u) & 1));
+      const uint32_t b = max_abs_bits(v);
+      m = b > m ? b : m;  // chunks past the end repeat chunk Q - 1
+    }
   }
   m = wave_max_u32(m);
-  __shared__ uint32_t red[kThreads / 64];
+  __shared__ uint32_t red[kAmaxThreads / 64];
   if (lane == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t t = red[0];
-    for (int i = 1; i < kThreads / 64; ++i) t = red[i] > t ? red[i] : t;
+    for (int i = 1; i < kAmaxThreads / 64; ++i) t = red[i] > t ? red[i] : t;
     // non-negative floats order like their bit patterns
     atomicMax(reinterpret_cast<unsigned int*>(amax), t);
   }
@@ -302,15 +409,14 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* codes, cons
                                                       uint32_t sign_mask) {
   const uint32_t lane = threadIdx.x & 63u;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const float S = FMT == FMT_NVFP4 ? *tensor_scale : 1.0f;
-  ChunkWalk w;
-  w.init(wave * 64, nwaves * 64, cols >> 3);
-  for (; w.q0 < Q; w.advance()) {
-    const int64_t q = w.q0 + lane;
+  const int64_t cpr = cols >> 3;
+  const bool dense = ld_y == cols;
+  const int64_t q0 = wave * (64 * kU) + lane;
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int64_t q = q0 + 64 * u;
     const bool valid = q < Q;
-    int64_t row, c8;
-    w.lane_pos(lane, &row, &c8);
     float v[8];
     if (valid) {
       uint32_t cw[8];
@@ -351,8 +457,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* codes, cons
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
-    if constexpr (RHT) rht_inverse(v, sign_mask, (uint32_t)(c8 & 1));
-    if (valid) store8<YDT>(y, row * ld_y + 8 * c8, v);
+    if constexpr (RHT) rht_inverse(v, sign_mask, (uint32_t)(q & 1));
+    if (valid) store8<YDT>(y, chunk_offset(q, cpr, ld_y, dense), v);
   }
 }
 
@@ -362,24 +468,32 @@ __global__ __launch_bounds__(kThreads) void k_hadamard(const void* x, void* y, i
                                                        int64_t Q, uint32_t sign_mask) {
   const uint32_t lane = threadIdx.x & 63u;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
-  for (int64_t q0 = wave * 64; q0 < Q; q0 += nwaves * 64) {
-    const int64_t q = q0 + lane;
-    const bool valid = q < Q;
+  const int64_t q0 = wave * (64 * kU) + lane;
+  Raw<XDT> raw[kU];
+  load_slabs<XDT>(x, q0, Q, cols >> 3, cols, true, raw);
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int64_t q = q0 + 64 * u;
     float v[8];
-    load8<XDT>(x, q * 8, valid, v);
+    widen<XDT>(raw[u], v);
     if constexpr (INV) rht_inverse(v, sign_mask, (uint32_t)(q & 1));
     else rht_forward(v, sign_mask, (uint32_t)(q & 1));
-    if (valid) store8<YDT>(y, q * 8, v);
+    if (q < Q) store8<YDT>(y, q * 8, v);
   }
 }
 
+// one wave per kU slabs, 4 waves per workgroup
 int grid_for(int64_t Q) {
-  int64_t waves = (Q + 63) / 64;
-  int64_t blocks = (waves + 3) / 4;
-  const int64_t cap = 256 * 16;
-  if (blocks > cap) blocks = cap;
+  const int64_t waves = (Q + 64 * kU - 1) / (64 * kU);
+  const int64_t blocks = (waves + 3) / 4;
   return (int)(blocks < 1 ? 1 : blocks);
+}
+
+// grid of the grid-stride amax: at most 256 workgroups of 1024 lanes
+int grid_for_amax(int64_t Q) {
+  const int64_t waves = (Q + 64 * kU - 1) / (64 * kU);
+  const int64_t b = (waves + kAmaxThreads / 64 - 1) / (kAmaxThreads / 64);
+  return (int)(b > 256 ? 256 : (b < 1 ? 1 : b));
 }
 
 template <int XDT, int FMT, bool SR, bool RHT>
@@ -410,13 +524,13 @@ hipError_t launch_amax(const void* x, int xdt, int64_t rows, int64_t cols, int64
   hipLaunchKernelGGL(k_zero_f32, dim3(1), dim3(1), 0, s, amax);
   const int64_t Q = rows * (cols / 8);
   if (Q == 0) return hipGetLastError();
-  const int g = grid_for(Q);
+  const int g = grid_for_amax(Q);
   if (xdt == DT_BF16) {
-    if (rht) hipLaunchKernelGGL((k_amax<DT_BF16, true>), dim3(g), dim3(kThreads), 0, s, x, cols, ld_x, Q, sign_mask, amax);
-    else hipLaunchKernelGGL((k_amax<DT_BF16, false>), dim3(g), dim3(kThreads), 0, s, x, cols, ld_x, Q, sign_mask, amax);
+    if (rht) hipLaunchKernelGGL((k_amax<DT_BF16, true>), dim3(g), dim3(kAmaxThreads), 0, s, x, cols, ld_x, Q, sign_mask, amax);
+    else hipLaunchKernelGGL((k_amax<DT_BF16, false>), dim3(g), dim3(kAmaxThreads), 0, s, x, cols, ld_x, Q, sign_mask, amax);
   } else {
-    if (rht) hipLaunchKernelGGL((k_amax<DT_F32, true>), dim3(g), dim3(kThreads), 0, s, x, cols, ld_x, Q, sign_mask, amax);
-    else hipLaunchKernelGGL((k_amax<DT_F32, false>), dim3(g), dim3(kThreads), 0, s, x, cols, ld_x, Q, sign_mask, amax);
+    if (rht) hipLaunchKernelGGL((k_amax<DT_F32, true>), dim3(g), dim3(kAmaxThreads), 0, s, x, cols, ld_x, Q, sign_mask, amax);
+    else hipLaunchKernelGGL((k_amax<DT_F32, false>), dim3(g), dim3(kAmaxThreads), 0, s, x, cols, ld_x, Q, sign_mask, amax);
   }
   return hipGetLastError();
 }
@@ -430,7 +544,7 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
     }
     if (Q == 0) {
       // still publish S for an empty tensor
-      hipLaunchKernelGGL((k_quant_nvfp4<DT_BF16, false, false>), dim3(1), dim3(kThreads), 0, s, a, (int64_t)0);
+      hipLaunchKernelGGL(k_nv_scale_only, dim3(1), dim3(1), 0, s, a.amax, a.tensor_scale);
       return hipGetLastError();
     }
     return a.xdt == DT_BF16 ? quant_nv_d<DT_BF16>(a, Q, s) : quant_nv_d<DT_F32>(a, Q, s);
