@@ -90,10 +90,33 @@ typedef struct {
  *   tensor_scale  NVFP4 only: FP32 S, the per-tensor decode multiplier
  *           (x ~ e2m1 * e4m3 * S); NULL for MX formats.  For the stacked
  *           weights of mx_gemm_grouped it points to one S per group.
- * Rows are dense: the row pitch is cols (or cols/2) bytes. */
+ * Rows are dense: the row pitch is cols (or cols/2) bytes.
+ *
+ * layout (mx_layout) selects how the code and scale bytes are ordered:
+ *   MX_LAYOUT_ROWS   the row-major arrays above (every format, every call).
+ *   MX_LAYOUT_TILED  matrix-instruction tiles (MX formats only; rows % 32 ==
+ *           0 and cols % 1024 == 0).  Same byte counts as MX_LAYOUT_ROWS.
+ *     codes: the [rows, row_bytes] code matrix is cut into tiles of 32 rows x
+ *           128 bytes (256 FP4 or 128 FP8 elements); tile (T, t) (rows 32T..,
+ *           code bytes 128t..) is 4096 contiguous bytes at byte offset
+ *           (T * row_bytes / 128 + t) * 4096, and within it the 16-byte chunk
+ *           c (bytes 16c .. 16c+15 of the tile row) of tile row r is at
+ *           (c / 2) * 1024 + ((c % 2) * 32 + r) * 16.
+ *     scales: tiles of 32 rows x 32 blocks (1024 elements); tile (T, g) is
+ *           1024 contiguous bytes at (T * cols / 1024 + g) * 1024, and the
+ *           scale of block b (0..31 within the tile) of tile row r is byte
+ *           ((b % 2) * 32 + r) * 16 + b / 2.
+ *     (One 1024-byte run of a code tile is exactly the operand fragment a
+ *     wavefront loads for a 32 x 64-element matrix instruction, and lane
+ *     (b % 2) * 32 + r finds all the scales it applies in one 16-byte word.)
+ *   Accepted by mx_quantize (output), mx_dequantize (input) and mx_gemm /
+ *   mx_gemm_ex (both operands tiled; MXFP8 then needs MX_GEMM_FP8_NATIVE);
+ *   other calls return MX_ERR_UNSUPPORTED for a tiled tensor. */
+typedef enum { MX_LAYOUT_ROWS = 0, MX_LAYOUT_TILED = 1 } mx_layout;
+
 typedef struct {
-  int32_t fmt; /* mx_format */
-  int32_t reserved;
+  int32_t fmt;    /* mx_format */
+  int32_t layout; /* mx_layout */
   int64_t rows;
   int64_t cols;
   void* codes;

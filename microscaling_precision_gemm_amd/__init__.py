@@ -20,6 +20,7 @@ MX_RNE, MX_SR = 0, 1
 MX_BF16, MX_F32 = 0, 1
 MX_FLAG_RHT16, MX_FLAG_AMAX_GIVEN = 1, 2
 MX_GEMM_FP8_NATIVE = 1
+MX_LAYOUT_ROWS, MX_LAYOUT_TILED = 0, 1
 
 FORMATS = {"mxfp8": MX_MXFP8_E4M3, "mxfp4": MX_MXFP4_E2M1, "nvfp4": MX_NVFP4}
 
@@ -37,7 +38,7 @@ class MXError(RuntimeError):
 
 
 class _Tensor(ctypes.Structure):
-    _fields_ = [("fmt", ctypes.c_int32), ("reserved", ctypes.c_int32), ("rows", ctypes.c_int64),
+    _fields_ = [("fmt", ctypes.c_int32), ("layout", ctypes.c_int32), ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("tensor_scale", ctypes.c_void_p)]
 
@@ -114,24 +115,32 @@ def _dt(t) -> int:
 
 class MXTensor:
     """A quantized [rows, cols] matrix: codes, block scales and (NVFP4) the
-    per-tensor scale, as torch uint8 / float32 device tensors."""
+    per-tensor scale, as torch uint8 / float32 device tensors; `layout` is
+    MX_LAYOUT_ROWS or MX_LAYOUT_TILED (byte order specified in mx.h)."""
 
-    def __init__(self, fmt: int, rows: int, cols: int, codes, scales, tensor_scale=None):
+    def __init__(self, fmt: int, rows: int, cols: int, codes, scales, tensor_scale=None,
+                 layout: int = MX_LAYOUT_ROWS):
         self.fmt, self.rows, self.cols = int(fmt), int(rows), int(cols)
         self.codes, self.scales, self.tensor_scale = codes, scales, tensor_scale
+        self.layout = int(layout)
 
     def desc(self) -> _Tensor:
-        return _Tensor(self.fmt, 0, self.rows, self.cols, _ptr(self.codes), _ptr(self.scales),
-                       _ptr(self.tensor_scale))
+        return _Tensor(self.fmt, self.layout, self.rows, self.cols, _ptr(self.codes),
+                       _ptr(self.scales), _ptr(self.tensor_scale))
 
     def view_rows(self, r0: int, r1: int, tensor_scale=None) -> "MXTensor":
-        """Rows [r0, r1) as a tensor sharing storage."""
+        """Rows [r0, r1) as a tensor sharing storage (row layout only)."""
+        if self.layout != MX_LAYOUT_ROWS:
+            raise MXError("view_rows needs the row layout")
         return MXTensor(self.fmt, r1 - r0, self.cols, self.codes[r0:r1], self.scales[r0:r1],
                         tensor_scale if tensor_scale is not None else self.tensor_scale)
 
 
-def empty(fmt: int, rows: int, cols: int, device="cuda", n_tensor_scales: int = 1) -> MXTensor:
-    """Allocate the buffers of a quantized [rows, cols] tensor."""
+def empty(fmt: int, rows: int, cols: int, device="cuda", n_tensor_scales: int = 1,
+          layout: int = MX_LAYOUT_ROWS) -> MXTensor:
+    """Allocate the buffers of a quantized [rows, cols] tensor.  (Tiled
+    tensors have the same byte counts; their [rows, bytes/rows] shape is
+    only a container.)"""
     torch = _torch()
     L = load()
     cb = L.mx_codes_bytes(fmt, rows, cols)
@@ -139,7 +148,7 @@ def empty(fmt: int, rows: int, cols: int, device="cuda", n_tensor_scales: int = 
     codes = torch.empty((rows, cb // max(rows, 1)), dtype=torch.uint8, device=device)
     scales = torch.empty((rows, sb // max(rows, 1)), dtype=torch.uint8, device=device)
     ts = torch.empty(n_tensor_scales, dtype=torch.float32, device=device) if fmt == MX_NVFP4 else None
-    return MXTensor(fmt, rows, cols, codes, scales, ts)
+    return MXTensor(fmt, rows, cols, codes, scales, ts, layout)
 
 
 def mx_codes_bytes(fmt: int, rows: int, cols: int) -> int:

@@ -18,11 +18,17 @@ int64_t block_of(int32_t f) { return f == MX_NVFP4 ? 16 : 32; }
 mx_status hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 
 // Checks the descriptor of a quantized tensor of logical shape [rows, cols].
+// The tiled layout is MX-only with rows % 32 == 0 and cols % 1024 == 0.
 mx_status check_tensor(const mx_tensor* t, int64_t rows, int64_t cols) {
   if (!t) return MX_ERR_NULL;
   if (!valid_fmt(t->fmt)) return MX_ERR_FORMAT;
+  if (t->layout != MX_LAYOUT_ROWS && t->layout != MX_LAYOUT_TILED) return MX_ERR_FORMAT;
   if (t->rows != rows || t->cols != cols || rows < 0 || cols < 0) return MX_ERR_SHAPE;
   if (cols % block_of(t->fmt)) return MX_ERR_SHAPE;
+  if (t->layout == MX_LAYOUT_TILED) {
+    if (t->fmt == MX_NVFP4) return MX_ERR_UNSUPPORTED;
+    if (rows % 32 || cols % 1024) return MX_ERR_SHAPE;
+  }
   if (rows * cols > 0) {
     if (!t->codes || !t->scales) return MX_ERR_NULL;
     if (!aligned16(t->codes) || !aligned16(t->scales)) return MX_ERR_ALIGN;
@@ -119,6 +125,7 @@ mx_status mx_quantize(const void* x, int32_t xdt, int64_t rows, int64_t cols, in
   a.rht = (flags & MX_FLAG_RHT16) != 0;
   a.sign_mask = rht_sign_mask;
   a.amax_given = (flags & MX_FLAG_AMAX_GIVEN) != 0;
+  a.tiled = out->layout == MX_LAYOUT_TILED;
   return hip_status(mxk::launch_quantize(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -146,6 +153,7 @@ mx_status mx_dequantize(const mx_tensor* in, void* y, int32_t ydt, int64_t ld_y,
   return hip_status(mxk::launch_dequantize(in->fmt, static_cast<const uint8_t*>(in->codes),
                                            in->scales, in->tensor_scale, in->rows, in->cols, y,
                                            ydt, ld_y, (flags & MX_FLAG_RHT16) != 0, rht_sign_mask,
+                                           in->layout == MX_LAYOUT_TILED,
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -160,14 +168,14 @@ mx_status mx_requant_transpose(const mx_tensor* src, const void* x_bf16, int64_t
   if (src) {
     mx_status st = check_tensor(src, rows, cols);
     if (st != MX_OK) return st;
-    if (src->fmt != MX_NVFP4) return MX_ERR_UNSUPPORTED;
+    if (src->fmt != MX_NVFP4 || src->layout != MX_LAYOUT_ROWS) return MX_ERR_UNSUPPORTED;
   } else {
     mx_status st = check_matrix(x_bf16, MX_BF16, rows, cols, ld_x);
     if (st != MX_OK) return st;
   }
   mx_status st = check_tensor(out, cols, rows);
   if (st != MX_OK) return st;
-  if (out->fmt != MX_MXFP8_E4M3) return MX_ERR_UNSUPPORTED;
+  if (out->fmt != MX_MXFP8_E4M3 || out->layout != MX_LAYOUT_ROWS) return MX_ERR_UNSUPPORTED;
   if (rows * cols == 0) return MX_OK;
   return hip_status(mxk::launch_requant_transpose(
       src ? static_cast<const uint8_t*>(src->codes) : nullptr, src ? src->scales : nullptr,
@@ -200,6 +208,10 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
   if (A->fmt != B->fmt) return MX_ERR_UNSUPPORTED;
   if ((flags & MX_GEMM_FP8_NATIVE) && A->fmt != MX_MXFP8_E4M3) return MX_ERR_UNSUPPORTED;
   if (A->cols != B->cols || A->cols % 32) return MX_ERR_SHAPE;
+  const bool tiled = A->layout == MX_LAYOUT_TILED;
+  if ((B->layout == MX_LAYOUT_TILED) != tiled) return MX_ERR_UNSUPPORTED;
+  // tiled MXFP8 only has the native-FP8 kernel
+  if (tiled && A->fmt == MX_MXFP8_E4M3 && !(flags & MX_GEMM_FP8_NATIVE)) return MX_ERR_UNSUPPORTED;
   const int64_t M = A->rows, N = B->rows, K = A->cols;
   st = check_output(C, cdt, M, N, ldc);
   if (st != MX_OK) return st;
@@ -207,6 +219,9 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const uint8_t* ac = static_cast<const uint8_t*>(A->codes);
   const uint8_t* bc = static_cast<const uint8_t*>(B->codes);
+  if (tiled)
+    return hip_status(mxk::launch_gemm_mx_tiled(A->fmt, ac, A->scales, bc, B->scales, M, N, K, C,
+                                                cdt, ldc, s));
   switch (A->fmt) {
     case MX_NVFP4:
       // one group covering all rows (no offsets array needed)

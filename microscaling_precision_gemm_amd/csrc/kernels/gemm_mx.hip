@@ -30,8 +30,8 @@
 // global memory into LDS with global_load_lds (no register staging), two
 // stage buffers deep.  Full 128-byte segments stream markedly faster than
 // half lines (measured).  The 16-byte chunks of a row are XOR-swizzled by
-// (row & 7), so fragment reads of 8 consecutive rows hit distinct bank
-// groups.  Slice fragments are double-buffered in registers; a wave waits for
+// ((row >> 1) & 7), so fragment reads of 16 consecutive rows hit distinct
+// bank groups.  Slice fragments are double-buffered in registers; a wave waits for
 // the next stage and joins the one barrier of the step just before the last
 // slice's matrix instructions, so the refill of the stage just consumed and
 // the first reads of the next stage overlap that slice.  The epilogue
@@ -45,15 +45,13 @@
 #include <atomic>
 
 #include "../device/codec.h"
+#include "../device/gemm_common.h"
 #include "../launch.h"
 
 namespace mxk {
 
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));  // plain vector: stays in registers
 
 template <int FMT>
 struct StepCfg {
@@ -62,23 +60,6 @@ struct StepCfg {
   static constexpr int kBlocks = kKElems / 32;                 // scale bytes per row per step
 };
 
-// Map a linear workgroup id to a (tile_m, tile_n) so that the ids that land
-// on one XCD (id mod 8) form compact groups of tiles.
-__device__ inline void tile_of(uint32_t id, uint32_t tm, uint32_t tn, uint32_t* m, uint32_t* n) {
-  const uint32_t total = tm * tn;
-  uint32_t lin = id;
-  if ((total & 7u) == 0) {
-    const uint32_t per = total >> 3;
-    lin = (id & 7u) * per + (id >> 3);
-  }
-  const uint32_t G = 4;  // groups of G tile-rows, column-major inside a group
-  const uint32_t group = lin / (G * tn);
-  const uint32_t first_m = group * G;
-  const uint32_t gsize = (tm - first_m) < G ? (tm - first_m) : G;
-  const uint32_t in = lin - group * G * tn;
-  *m = first_m + in % gsize;
-  *n = in / gsize;
-}
 
 template <int CDT>
 __device__ inline void store_c(void* C, int64_t ldc, int64_t row, int64_t col, float v) {
@@ -93,9 +74,16 @@ constexpr int kTile = 256;                  // BM = BN
 constexpr int kRowsAll = 2 * kTile;         // A rows then B rows in a stage
 constexpr int kSeg = 128;                   // code bytes per row per K step
 constexpr int kCodeBytes = kRowsAll * kSeg; // 64 KB
-constexpr int kScaleBytes = kRowsAll * 8;   // two scale dwords per row (FP8 uses one)
-constexpr int kStageBytes = kCodeBytes + kScaleBytes;
+constexpr int kStageBytes = kCodeBytes;
 constexpr int kStages = 2;
+// Scales are staged per period of steps: 16 bytes of every row (two FP4
+// steps or four FP8 steps), in three rotating 8 KB buffers after the code
+// stages, loaded two periods ahead.
+constexpr int kScaleRow = 16;
+constexpr int kScaleBuf = kRowsAll * kScaleRow;
+constexpr int kScaleBufs = 3;
+constexpr int kScaleBase = kStages * kStageBytes;
+constexpr int kSmemBytes = kScaleBase + kScaleBufs * kScaleBuf;  // 152 KB
 
 // Workgroup barrier for the DMA pipeline: this wave's LDS reads are complete
 // (lgkmcnt 0) and the compiler may not move memory accesses across it, but
@@ -105,6 +93,25 @@ __device__ inline void dma_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// Scheduling barrier: no instruction moves across it.
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// sched_group_barrier masks
+constexpr int kSgMfma = 0x008, kSgVmem = 0x010, kSgDsRead = 0x100;
+
+// Order a region as N rounds of (1 MFMA, V vector-memory ops, D LDS reads),
+// then the remaining MFMAs of the region's 16.
+template <int N, int V, int D>
+__device__ inline void interleave() {
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(kSgVmem, V, 0);
+    if constexpr (D > 0) __builtin_amdgcn_sched_group_barrier(kSgDsRead, D, 0);
+  }
+  if constexpr (N < 16) __builtin_amdgcn_sched_group_barrier(kSgMfma, 16 - N, 0);
 }
 
 // s_waitcnt limiting only the vector-memory counter (gfx9 encoding: vmcnt in
@@ -123,20 +130,23 @@ template <int FMT>
 struct PipeCfg {
   static constexpr int kSlices = FMT == FMT_MXFP8 ? 2 : 4;
   static constexpr int kKElems = FMT == FMT_MXFP8 ? 128 : 256;
-  static constexpr int kScaleDw = FMT == FMT_MXFP8 ? 1 : 2;
+  static constexpr int kScaleDw = FMT == FMT_MXFP8 ? 1 : 2;      // scale dwords per row and step
+  static constexpr int kPeriod = kScaleRow / (4 * kScaleDw);       // steps per scale period
 };
 
 // Copy assignment of one thread: wave-uniform operand bases (waves 0-1 copy
 // A rows, waves 2-3 B rows) and 32-bit per-lane byte offsets.  Code
 // instruction i of wave w fills LDS rows 8*(16w+i) .. +7 (8 lanes per
-// 128-byte row); scale instruction j fills scale dword (j & 1) of rows
-// 64*(4*(w%2) + j/2) + lane ... for the wave's operand.
+// 128-byte row).  Scale instruction of wave w fills 16 bytes of rows
+// 64w + lane of operand A (even steps) or B (odd steps).
 struct PipeCtx {
   const uint8_t* cbase;
-  const uint8_t* sbase;
+  const uint8_t* sA;
+  const uint8_t* sB;
   uint32_t coff[16];
-  uint32_t soff[4];
+  uint32_t soffA, soffB;
   uint32_t wid;
+  uint32_t nper;  // scale periods in K
 };
 
 template <int FMT>
@@ -145,20 +155,21 @@ __device__ inline void issue_stage(const PipeCtx& x, uint32_t step, uint8_t* __r
   for (int i = 0; i < 16; ++i)
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)(x.cbase + (x.coff[i] + step * (uint32_t)kSeg)),
                                      (lds_ptr_t)(stage + (8u * (16u * x.wid + i)) * kSeg), 16, 0, 0);
-  // scales: per operand 256 rows x kScaleDw dwords; waves (2 per operand)
-  // take 128 rows each, one instruction per 64 rows and dword
-  constexpr int kDw = PipeCfg<FMT>::kScaleDw;
-  const uint32_t op = x.wid >> 1, half = x.wid & 1u;
-#pragma unroll
-  for (int j = 0; j < 2 * kDw; ++j) {
-    const uint32_t dw = j % kDw, blk = j / kDw;  // dword index, 64-row block within the wave's 128
-    const uint32_t row = op * kTile + half * 128u + blk * 64u;
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(x.sbase + (x.soff[j] + step * 4u * kDw + 4u * dw)),
-                                     (lds_ptr_t)(stage + kCodeBytes + dw * (kRowsAll * 4) + row * 4u), 4, 0, 0);
-  }
 }
-template <int FMT>
-constexpr int dma_per_stage() { return 16 + 2 * PipeCfg<FMT>::kScaleDw; }
+
+// One scale DMA: period `per` (clamped to the last one; a clamped copy lands
+// in a buffer nobody reads) of operand `op`'s rows 64w .. 64w+63 into scale
+// buffer `buf`.
+__device__ inline void issue_scales(const PipeCtx& x, uint8_t* __restrict__ smem, uint32_t per,
+                                    uint32_t buf, uint32_t op) {
+  per = per < x.nper ? per : x.nper - 1;
+  const uint8_t* base = op ? x.sB : x.sA;
+  const uint32_t off = (op ? x.soffB : x.soffA) + per * (uint32_t)kScaleRow;
+  __builtin_amdgcn_global_load_lds((gbl_ptr_t)(base + off),
+                                   (lds_ptr_t)(smem + kScaleBase + buf * kScaleBuf + op * (kTile * kScaleRow) +
+                                               x.wid * (64 * kScaleRow)),
+                                   16, 0, 0);
+}
 
 // Fragments of one K slice for one wave (16 bytes per operand tile; FP8 keeps
 // the lane's second 16 bytes in the *hi arrays).
@@ -168,10 +179,12 @@ struct Slice {
   u4 ahi[FMT == FMT_MXFP8 ? 4 : 1], bhi[FMT == FMT_MXFP8 ? 4 : 1];
 };
 
-// LDS byte offset of logical 16-byte chunk c of stage row r (chunks of a row
-// are XOR-swizzled by the row's low 3 bits: 8 consecutive rows reading the
-// same logical chunk hit 8 different bank groups).
-__device__ inline uint32_t chunk_off(uint32_t r, uint32_t c) { return r * kSeg + 16u * (c ^ (r & 7u)); }
+// LDS byte offset of logical 16-byte chunk c of stage row r.  The LDS banks
+// span 256 bytes (two rows) and a 16-byte read is served 16 lanes at a time,
+// so the chunks of a row are XOR-swizzled by (row >> 1) & 7: 16 consecutive
+// rows reading the same logical chunk land on 16 distinct 16-byte slots.
+__device__ inline uint32_t swz(uint32_t r) { return (r >> 1) & 7u; }
+__device__ inline uint32_t chunk_off(uint32_t r, uint32_t c) { return r * kSeg + 16u * (c ^ swz(r)); }
 
 template <int FMT>
 __device__ inline void load_slice(const uint8_t* __restrict__ L, uint32_t q, uint32_t wm, uint32_t wn,
@@ -196,17 +209,27 @@ __device__ inline void load_slice(const uint8_t* __restrict__ L, uint32_t q, uin
 struct Scales {
   uint32_t a[2][4], b[2][4];
 };
+// Scale dwords of step `step` for the wave's rows (FP4: two per row, one
+// 64-bit read; FP8: one).
 template <int FMT>
-__device__ inline void load_scales(const uint8_t* __restrict__ L, uint32_t wm, uint32_t wn,
-                                   uint32_t lr, Scales& s) {
-  const uint8_t* LS = L + kCodeBytes;
+__device__ inline void load_scales(const uint8_t* __restrict__ smem, uint32_t step, uint32_t wm,
+                                   uint32_t wn, uint32_t lr, Scales& s) {
+  constexpr uint32_t P = PipeCfg<FMT>::kPeriod;
+  const uint8_t* LS = smem + kScaleBase + ((step / P) % kScaleBufs) * kScaleBuf +
+                      (step % P) * (4 * PipeCfg<FMT>::kScaleDw);
 #pragma unroll
-  for (int d = 0; d < PipeCfg<FMT>::kScaleDw; ++d)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s.a[d][i] = *reinterpret_cast<const uint32_t*>(LS + d * (kRowsAll * 4) + (wm * 128 + i * 32 + lr) * 4);
-      s.b[d][i] = *reinterpret_cast<const uint32_t*>(LS + d * (kRowsAll * 4) + (kTile + wn * 128 + i * 32 + lr) * 4);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ra = wm * 128 + i * 32 + lr, rb = kTile + wn * 128 + i * 32 + lr;
+    if constexpr (FMT == FMT_MXFP8) {
+      s.a[0][i] = *reinterpret_cast<const uint32_t*>(LS + ra * kScaleRow);
+      s.b[0][i] = *reinterpret_cast<const uint32_t*>(LS + rb * kScaleRow);
+    } else {
+      const uint2 va = *reinterpret_cast<const uint2*>(LS + ra * kScaleRow);
+      const uint2 vb = *reinterpret_cast<const uint2*>(LS + rb * kScaleRow);
+      s.a[0][i] = va.x; s.a[1][i] = va.y;
+      s.b[0][i] = vb.x; s.b[1][i] = vb.y;
     }
+  }
 }
 
 __device__ inline v8i widen(u4 lo, u4 hi) {
@@ -216,82 +239,129 @@ __device__ inline v8i widen4(u4 lo) {
   return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
 }
 
-// 16 MFMAs of K slice q.  The lane's scale byte for slice q is byte
-// (2q + lg) of the step's scale bytes: dword (2q + lg) / 4, selected by
-// shifting lg bytes down and opsel = 2 * (q % 2) (FP4), or opsel = 2q (FP8).
+// Scale dwords shifted so that byte 0 / byte 2 (selected by opsel) are
+// this lane's K-blocks: lane group lg (lanes 32..63) takes the odd blocks.
+__device__ inline void shift_scales(const Scales& in, uint32_t lg, Scales& out) {
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out.a[d][i] = in.a[d][i] >> (8 * lg);
+      out.b[d][i] = in.b[d][i] >> (8 * lg);
+    }
+}
+
+// 16 MFMAs of K slice q with pre-shifted scales.  The lane's scale byte for
+// slice q is byte (2q + lg) of the step's scale bytes: dword (2q + lg) / 4,
+// after the shift by lg bytes selected by opsel = 2 * (q % 2) (FP4), or
+// opsel = 2q (FP8, one dword per step).
 template <int FMT, int Q>
-__device__ inline void mfma_slice(const Slice<FMT>& f, const Scales& sc, uint32_t lg,
-                                  v16f (&acc)[4][4]) {
+__device__ inline void mfma_slice(const Slice<FMT>& f, const Scales& sh, v16f (&acc)[4][4]) {
   constexpr int D = FMT == FMT_MXFP8 ? 0 : Q / 2;
   constexpr int OPSEL = FMT == FMT_MXFP8 ? 2 * Q : 2 * (Q % 2);
-  uint32_t sa[4], sb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sa[i] = sc.a[D][i] >> (8 * lg);
-    sb[i] = sc.b[D][i] >> (8 * lg);
-  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (FMT == FMT_MXFP8)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f.a[i], f.ahi[i]), widen(f.b[j], f.bhi[j]), acc[i][j], 0, 0, OPSEL, (int)sa[i], OPSEL, (int)sb[j]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f.a[i], f.ahi[i]), widen(f.b[j], f.bhi[j]), acc[i][j], 0, 0, OPSEL, (int)sh.a[D][i], OPSEL, (int)sh.b[D][j]);
       else
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen4(f.a[i]), widen4(f.b[j]), acc[i][j], 4, 4, OPSEL, (int)sa[i], OPSEL, (int)sb[j]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen4(f.a[i]), widen4(f.b[j]), acc[i][j], 4, 4, OPSEL, (int)sh.a[D][i], OPSEL, (int)sh.b[D][j]);
     }
 }
 
-// Epilogue through LDS: each wave writes its 128x128 accumulator tile into
-// LDS in 64-row halves and stores it back row-contiguous, 16 bytes per lane.
-template <int CDT>
-__device__ inline void store_tile(uint8_t* __restrict__ smem, const v16f (&acc)[4][4], void* C,
-                                  int64_t ldc, int64_t M, int64_t N, int64_t r0, int64_t c0,
-                                  bool vec, uint32_t wid, uint32_t lane) {
-  constexpr int EB = CDT == DT_F32 ? 4 : 2;   // bytes per element
-  constexpr int PITCH = 128 * EB + 16;        // LDS row pitch (bank spread)
-  uint8_t* W = smem + wid * (64 * PITCH);
-  const uint32_t lr = lane & 31u, lg = lane >> 5;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {           // row halves 0..63, 64..127 of the wave tile
-#pragma unroll
-    for (int i2 = 0; i2 < 2; ++i2) {      // instruction-tile rows inside the half
-      const int i = 2 * h + i2;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const uint32_t row = i2 * 32 + 8 * (v / 4) + 4 * lg + (v % 4);
-          const uint32_t col = j * 32 + lr;
-          if constexpr (CDT == DT_F32) *reinterpret_cast<float*>(W + row * PITCH + col * 4) = acc[i][j][v];
-          else *reinterpret_cast<uint16_t*>(W + row * PITCH + col * 2) = f32_to_bf16(acc[i][j][v]);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // own LDS writes done
-    asm volatile("" ::: "memory");
-    // 64 rows x (128 * EB) bytes; each lane moves 16 bytes per step
-    constexpr int LPR = 128 * EB / 16;  // lanes per row
-    constexpr int RPI = 64 / LPR;       // rows per instruction
-#pragma unroll
-    for (int k = 0; k < 64 / RPI; ++k) {
-      const uint32_t row = k * RPI + lane / LPR;
-      const uint32_t cb = (lane % LPR) * 16;
-      const u4 val = *reinterpret_cast<const u4*>(W + row * PITCH + cb);
-      const int64_t grow = r0 + h * 64 + row;
-      const int64_t gcol = c0 + cb / EB;
-      if (grow < M) {
-        if (vec && gcol + 16 / EB <= N) {
-          *reinterpret_cast<u4*>(static_cast<uint8_t*>(C) + (grow * ldc + gcol) * EB) = val;
-        } else {
-          for (int e = 0; e < 16 / EB; ++e)
-            if (gcol + e < N) {
-              if constexpr (CDT == DT_F32) static_cast<uint32_t*>(C)[grow * ldc + gcol + e] = val[e];
-              else static_cast<uint16_t*>(C)[grow * ldc + gcol + e] = (uint16_t)(val[e / 2] >> (16 * (e & 1)));
-            }
-        }
+// Register state of the pipeline: slice fragments (double-buffered), the
+// scale dwords of the current and the next stage, and the current ones
+// shifted for this lane.
+template <int FMT>
+struct PipeState {
+  Slice<FMT> s[PipeCfg<FMT>::kSlices];  // one buffer per slice of a step
+  Scales sc, scn, sh;
+};
+
+// One K step.  SWITCH: a next stage exists; DMA: refill the buffer of the
+// stage being consumed with stage st + 2.
+//
+// FP4 (four slices, one fragment buffer each):
+//   W0: MFMAs of slice 0 | LDS reads of slices 1 and 2
+//   W1: MFMAs of slice 1 | LDS reads of slice 3
+//   wait for this wave's DMAs of stage st+1; barrier (every wave holds all
+//   of stage st in registers and stage st+1 has landed)
+//   W2: MFMAs of slice 2 | DMAs of stage st+2 into the buffer just released
+//   W3: MFMAs of slice 3 | LDS reads of stage st+1's scales and slice 0
+// FP8 (two slices):
+//   W0: MFMAs of slice 0 | LDS reads of slice 1
+//   wait; barrier
+//   W1: MFMAs of slice 1 | DMAs of stage st+2, reads of st+1's scales and
+//       slice 0
+// Spreading the DMAs over matrix work keeps their issue from stalling it.
+template <int FMT, bool SWITCH, bool DMA>
+__device__ inline void pipe_step(const PipeCtx& x, uint8_t* __restrict__ smem, uint32_t st,
+                                 uint32_t wm, uint32_t wn, uint32_t lr, uint32_t lg,
+                                 PipeState<FMT>& ps, v16f (&acc)[4][4]) {
+  uint8_t* cur = smem + (st & 1u) * kStageBytes;
+  uint8_t* nxt = smem + ((st + 1u) & 1u) * kStageBytes;
+  // the scale reads precede slice 0's reads: waiting for them leaves those
+  // in flight
+  shift_scales(ps.sc, lg, ps.sh);
+  sched_fence();
+  if constexpr (FMT == FMT_MXFP4) {
+    load_slice<FMT>(cur, 1, wm, wn, lr, lg, ps.s[1]);
+    load_slice<FMT>(cur, 2, wm, wn, lr, lg, ps.s[2]);
+    mfma_slice<FMT, 0>(ps.s[0], ps.sh, acc);
+    interleave<8, 0, 2>();
+    sched_fence();
+    load_slice<FMT>(cur, 3, wm, wn, lr, lg, ps.s[3]);
+    mfma_slice<FMT, 1>(ps.s[1], ps.sh, acc);
+    interleave<8, 0, 1>();
+    sched_fence();
+    if constexpr (SWITCH) {
+      wait_vmcnt<0>();
+      dma_barrier();
+      sched_fence();
+      if constexpr (DMA) {
+        issue_stage<FMT>(x, st + 2, cur);
+        const uint32_t q = st / PipeCfg<FMT>::kPeriod + 2;
+        issue_scales(x, smem, q, q % kScaleBufs, st & 1u);
       }
+      mfma_slice<FMT, 2>(ps.s[2], ps.sh, acc);
+      interleave<16, 1, 0>();
+      sched_fence();
+      load_scales<FMT>(smem, st + 1, wm, wn, lr, ps.scn);
+      load_slice<FMT>(nxt, 0, wm, wn, lr, lg, ps.s[0]);
+      mfma_slice<FMT, 3>(ps.s[3], ps.sh, acc);
+      interleave<8, 0, 3>();
+      sched_fence();
+      ps.sc = ps.scn;
+    } else {
+      mfma_slice<FMT, 2>(ps.s[2], ps.sh, acc);
+      mfma_slice<FMT, 3>(ps.s[3], ps.sh, acc);
+      sched_fence();
     }
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // reads done before reuse
-    asm volatile("" ::: "memory");
+  } else {
+    load_slice<FMT>(cur, 1, wm, wn, lr, lg, ps.s[1]);
+    mfma_slice<FMT, 0>(ps.s[0], ps.sh, acc);
+    interleave<8, 0, 2>();
+    sched_fence();
+    if constexpr (SWITCH) {
+      wait_vmcnt<0>();
+      dma_barrier();
+      sched_fence();
+      if constexpr (DMA) {
+        issue_stage<FMT>(x, st + 2, cur);
+        const uint32_t q = st / PipeCfg<FMT>::kPeriod + 2;
+        issue_scales(x, smem, q, q % kScaleBufs, st & 1u);
+      }
+      load_scales<FMT>(smem, st + 1, wm, wn, lr, ps.scn);
+      load_slice<FMT>(nxt, 0, wm, wn, lr, lg, ps.s[0]);
+      mfma_slice<FMT, 1>(ps.s[1], ps.sh, acc);
+      interleave<12, 2, 2>();
+      sched_fence();
+      ps.sc = ps.scn;
+    } else {
+      mfma_slice<FMT, 1>(ps.s[1], ps.sh, acc);
+      sched_fence();
+    }
   }
 }
 
@@ -314,29 +384,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t steps = (uint32_t)(K / PC::kKElems);
 
   // Code instruction i of wave w: LDS row r = 8*(16w+i) + lane/8, physical
-  // chunk p = lane%8 holding logical chunk p ^ (r & 7).  Rows past M / N read
+  // chunk p = lane%8 holding logical chunk p ^ swz(r).  Rows past M / N read
   // the last valid row (their results are not stored).
   PipeCtx x;
-  x.wid = wid;
+  x.wid = __builtin_amdgcn_readfirstlane(wid);  // wave-uniform: LDS bases in scalar registers
+  x.nper = steps / PC::kPeriod;
   const bool waveA = wid < 2;
   x.cbase = waveA ? A : B;
-  x.sbase = waveA ? SA : SB;
   const int64_t lim = waveA ? M : N;
   const int64_t row0 = waveA ? m0 : n0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const uint32_t r = 8u * (16u * wid + i) + (lane >> 3);
-    const uint32_t c = (lane & 7u) ^ (r & 7u);
+    const uint32_t c = (lane & 7u) ^ swz(r);
     int64_t grow = row0 + (r & (kTile - 1));
     grow = grow < lim ? grow : lim - 1;
     x.coff[i] = (uint32_t)(grow * rowbytes) + 16u * c;
   }
-#pragma unroll
-  for (int j = 0; j < 2 * PC::kScaleDw; ++j) {
-    const uint32_t blk = j / PC::kScaleDw;
-    int64_t grow = row0 + (wid & 1u) * 128u + blk * 64u + lane;
-    grow = grow < lim ? grow : lim - 1;
-    x.soff[j] = (uint32_t)(grow * kblocks);
+  x.sA = SA;
+  x.sB = SB;
+  {
+    int64_t ga = m0 + 64 * wid + lane, gb = n0 + 64 * wid + lane;
+    ga = ga < M ? ga : M - 1;
+    gb = gb < N ? gb : N - 1;
+    x.soffA = (uint32_t)(ga * kblocks);
+    x.soffB = (uint32_t)(gb * kblocks);
   }
 
   v16f acc[4][4];
@@ -351,46 +423,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // double-buffered in registers; before the last slice of stage st the wave
   // waits for stage st+1's DMAs and joins the barrier (all waves then hold
   // every fragment of stage st, so its buffer is refilled with stage st+2)
-  // and starts reading stage st+1's first slice.
+  // and starts reading stage st+1's first slice.  The loop body has no
+  // branch (the last two steps are peeled), so the matrix instructions stay
+  // where they are written.
   const uint32_t lr = lane & 31u, lg = lane >> 5;
-  constexpr int DPS = dma_per_stage<FMT>();
   issue_stage<FMT>(x, 0, smem);
+  issue_scales(x, smem, 0, 0, 0);
+  issue_scales(x, smem, 0, 0, 1);
+  issue_scales(x, smem, 1, 1, 0);
+  issue_scales(x, smem, 1, 1, 1);
   if (steps > 1) {
     issue_stage<FMT>(x, 1, smem + kStageBytes);
-    wait_vmcnt<DPS>();
+    wait_vmcnt<16>();  // stage 0 and the first two scale periods
   } else {
     wait_vmcnt<0>();
   }
   dma_barrier();
-  Slice<FMT> S0, S1;
-  Scales sc, scn;
-  load_scales<FMT>(smem, wm, wn, lr, sc);
-  load_slice<FMT>(smem, 0, wm, wn, lr, lg, S0);
-  for (uint32_t st = 0; st < steps; ++st) {
-    uint8_t* cur = smem + (st & 1u) * kStageBytes;
-    uint8_t* nxt = smem + ((st + 1u) & 1u) * kStageBytes;
-    if constexpr (PC::kSlices == 4) {
-      load_slice<FMT>(cur, 1, wm, wn, lr, lg, S1);
-      mfma_slice<FMT, 0>(S0, sc, lg, acc);
-      load_slice<FMT>(cur, 2, wm, wn, lr, lg, S0);
-      mfma_slice<FMT, 1>(S1, sc, lg, acc);
-      load_slice<FMT>(cur, 3, wm, wn, lr, lg, S1);
-      mfma_slice<FMT, 2>(S0, sc, lg, acc);
-    } else {
-      load_slice<FMT>(cur, 1, wm, wn, lr, lg, S1);
-      mfma_slice<FMT, 0>(S0, sc, lg, acc);
-    }
-    // stage st fully in registers: switch buffers
-    if (st + 1 < steps) {
-      wait_vmcnt<0>();  // stage st+1 (the only stage in flight)
-      dma_barrier();
-      if (st + 2 < steps) issue_stage<FMT>(x, st + 2, cur);
-      load_scales<FMT>(nxt, wm, wn, lr, scn);
-      load_slice<FMT>(nxt, 0, wm, wn, lr, lg, S0);
-    }
-    mfma_slice<FMT, PC::kSlices - 1>(S1, sc, lg, acc);
-    sc = scn;
+  PipeState<FMT> ps;
+  load_scales<FMT>(smem, 0, wm, wn, lr, ps.sc);
+  load_slice<FMT>(smem, 0, wm, wn, lr, lg, ps.s[0]);
+  uint32_t st = 0;
+  for (; st + 2 < steps; ++st) pipe_step<FMT, true, true>(x, smem, st, wm, wn, lr, lg, ps, acc);
+  if (st + 1 < steps) {
+    pipe_step<FMT, true, false>(x, smem, st, wm, wn, lr, lg, ps, acc);
+    ++st;
   }
+  pipe_step<FMT, false, false>(x, smem, st, wm, wn, lr, lg, ps, acc);
 
   // epilogue: LDS is free once every wave is past its last fragment read
   dma_barrier();
@@ -401,7 +459,7 @@ template <int FMT, int CDT>
 hipError_t launch_pipe(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                        int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
   const uint32_t tm = (uint32_t)((M + kTile - 1) / kTile), tn = (uint32_t)((N + kTile - 1) / kTile);
-  const size_t smem = (size_t)kStages * kStageBytes;
+  const size_t smem = (size_t)kSmemBytes;
   auto kern = k_gemm_mx_pipe<FMT, CDT>;
   // The dynamic LDS limit is raised once per device (bit d of a mask), so
   // that later launches -- including those recorded into a HIP graph --
@@ -555,7 +613,8 @@ hipError_t run(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint
                int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
   const int64_t rb = FMT == FMT_MXFP8 ? K : K / 2;
   const bool fits32 = (M > N ? M : N) * rb < ((int64_t)1 << 32) - 4096;
-  const bool pipe = fits32 && K > 0 && (K % PipeCfg<FMT>::kKElems == 0) &&
+  // K a multiple of 512: whole steps and whole 16-byte scale periods per row
+  const bool pipe = fits32 && K > 0 && (K % 512 == 0) &&
                     M * N >= (int64_t)kTile * kTile * 128;
   if (pipe) return launch_pipe<FMT, CDT>(a, sa, b, sb, M, N, K, C, ldc, s);
   const uint32_t tm = (uint32_t)((M + 127) / 128), tn = (uint32_t)((N + 127) / 128);

@@ -1,0 +1,230 @@
+// gemm_tiled.hip -- block-scaled GEMM C = A * B^T for MX operands stored in
+// the matrix-instruction tile layout (mx_layout MX_LAYOUT_TILED, specified in
+// include/mx.h), on gfx950's scaled matrix instruction
+// v_mfma_scale_f32_32x32x64_f8f6f4 ("Microscaling (MX) and block-scaled 4-bit
+// formats", section "Hardware and kernels": the block scales are applied
+// inside the matrix instruction).
+//
+// In the tile layout, the operand fragment of one 32-row x 64-element
+// matrix instruction is 1024 contiguous bytes (FP4; FP8 two such runs), with
+// lane l's 16 bytes at offset 16 l, and the scales a lane applies over 1024
+// elements of K are one 16-byte word.  So every wave loads its fragments
+// straight from global memory into registers with fully coalesced 16-byte
+// loads, and the main loop uses no LDS at all.  (Measured on gfx950: LDS
+// writes -- ds_write or global-to-LDS DMA -- issued while matrix
+// instructions run slow those instructions down by about half, while global
+// loads into registers overlap them completely.)
+//
+// Workgroup: 4 waves (2 x 2) over a 256x256 C tile, each wave 128x128 (4x4
+// instruction tiles, 256 accumulator registers), one wave per SIMD.  Per K
+// step (128 code bytes per row: 256 FP4 or 128 FP8 elements) a wave loads 8
+// row tiles (4 of A, 4 of B) x 4 KB.  Fragments are kept one step ahead:
+// after the matrix instructions of slice q of step s, the registers of slice
+// q receive the loads of step s+1.  Scales are loaded one 1024-element group
+// ahead.  The epilogue stages each wave's tile through LDS for row-contiguous
+// 16-byte stores.
+#include <atomic>
+
+#include "../device/codec.h"
+#include "../device/gemm_common.h"
+#include "../launch.h"
+
+namespace mxk {
+
+namespace {
+
+// global-address-space pointers (plain pointers rebuilt from integers would
+// compile to flat accesses, which also count against the LDS counter)
+typedef const __attribute__((address_space(1))) uint8_t* gptr;
+typedef const __attribute__((address_space(1))) u4* gptr4;
+
+template <int FMT>
+struct TCfg {
+  static constexpr int kSlices = FMT == FMT_MXFP8 ? 2 : 4;        // instructions per step along K
+  static constexpr int kParts = FMT == FMT_MXFP8 ? 2 : 1;         // 1 KB loads per tile and slice
+  static constexpr int kStepsPerGroup = FMT == FMT_MXFP8 ? 8 : 4; // steps per 1024-element group
+};
+
+// Fragments of one slice: 8 row tiles (A 0..3, B 4..7) x parts.
+template <int FMT>
+struct TSlice {
+  u4 f[8][TCfg<FMT>::kParts];
+};
+
+template <int FMT>
+__device__ inline void load_slice_t(const gptr (&base)[8], uint32_t step, uint32_t q,
+                                    uint32_t lane16, TSlice<FMT>& s) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int p = 0; p < TCfg<FMT>::kParts; ++p)
+      s.f[t][p] = *reinterpret_cast<gptr4>(
+          base[t] + (uint32_t)(step * 4096u + (q * TCfg<FMT>::kParts + p) * 1024u + lane16));
+}
+
+__device__ inline v8i widen4(u4 lo) {
+  return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+}
+__device__ inline v8i widen(u4 lo, u4 hi) {
+  return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// 16 instructions of slice Q of step S (within the scale group).  The
+// lane's scale byte: FP4 byte Q of dword S; FP8 byte 2 (S % 2) + Q of dword
+// S / 2 (opsel selects the byte).
+template <int FMT, int S, int Q>
+__device__ inline void mfma_slice_t(const TSlice<FMT>& f, const u4 (&sc)[8], v16f (&acc)[4][4]) {
+  constexpr int D = FMT == FMT_MXFP8 ? S / 2 : S;
+  constexpr int OPSEL = FMT == FMT_MXFP8 ? 2 * (S % 2) + Q : Q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (FMT == FMT_MXFP8)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            widen(f.f[i][0], f.f[i][1]), widen(f.f[4 + j][0], f.f[4 + j][1]), acc[i][j], 0, 0, OPSEL,
+            (int)sc[i][D], OPSEL, (int)sc[4 + j][D]);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            widen4(f.f[i][0]), widen4(f.f[4 + j][0]), acc[i][j], 4, 4, OPSEL, (int)sc[i][D], OPSEL,
+            (int)sc[4 + j][D]);
+    }
+}
+
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// A wave-uniform 64-bit value moved to scalar registers.  readfirstlane
+// returns a signed int: each half goes through uint32_t so that the low half
+// is not sign-extended into the high one.
+__device__ inline uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Steps S .. kStepsPerGroup-1 of group g: after slice q's instructions, slice
+// q of the next step (clamped to the last step, a harmless reload) is loaded
+// into the same registers.
+template <int FMT, int S, int Q>
+__device__ inline void run_group(const gptr (&base)[8], uint32_t g, uint32_t steps,
+                                 uint32_t lane16, TSlice<FMT> (&fr)[TCfg<FMT>::kSlices],
+                                 const u4 (&sc)[8], v16f (&acc)[4][4]) {
+  constexpr int SPG = TCfg<FMT>::kStepsPerGroup, KS = TCfg<FMT>::kSlices;
+  if constexpr (S < SPG) {
+    if constexpr (Q < KS) {
+      const uint32_t st = g * SPG + S;
+      const uint32_t nst = st + 1 < steps ? st + 1 : st;
+      mfma_slice_t<FMT, S, Q>(fr[Q], sc, acc);
+      load_slice_t<FMT>(base, nst, Q, lane16, fr[Q]);
+      sched_fence();
+      run_group<FMT, S, Q + 1>(base, g, steps, lane16, fr, sc, acc);
+    } else {
+      run_group<FMT, S + 1, 0>(base, g, steps, lane16, fr, sc, acc);
+    }
+  }
+}
+
+template <int FMT, int CDT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx_tiled(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, void* __restrict__ C,
+    int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t vec) {
+  using TC = TCfg<FMT>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint32_t tmi, tni;
+  tile_of(blockIdx.x, tiles_m, tiles_n, &tmi, &tni);
+  const int64_t m0 = (int64_t)tmi * 256, n0 = (int64_t)tni * 256;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t wm = wid >> 1, wn = wid & 1u;
+  const uint32_t steps = (uint32_t)((FMT == FMT_MXFP8 ? K : K / 2) / 128);  // code tiles per row tile
+  const uint32_t groups = (uint32_t)(K / 1024);
+  const uint32_t lane16 = lane * 16u;
+
+  // Row tiles of this wave (tiles past M / N repeat the last one; their
+  // results are not stored).  Bases are wave-uniform.
+  gptr cb[8];
+  gptr sb[8];
+  const int64_t last_a = M / 32 - 1, last_b = N / 32 - 1;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    int64_t rt = t < 4 ? m0 / 32 + wm * 4 + t : n0 / 32 + wn * 4 + (t - 4);
+    const int64_t last = t < 4 ? last_a : last_b;
+    rt = rt < last ? rt : last;
+    // wave-uniform: keep the bases in scalar registers
+    const uint64_t c = reinterpret_cast<uint64_t>((t < 4 ? A : B) + rt * (int64_t)steps * 4096);
+    const uint64_t d = reinterpret_cast<uint64_t>((t < 4 ? SA : SB) + rt * (int64_t)groups * 1024);
+    cb[t] = (gptr)uniform_u64(c);
+    sb[t] = (gptr)uniform_u64(d);
+  }
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  u4 sc[8], scn[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) sc[t] = *reinterpret_cast<gptr4>(sb[t] + (uint32_t)lane16);
+  TSlice<FMT> fr[TC::kSlices];
+#pragma unroll
+  for (int q = 0; q < TC::kSlices; ++q) load_slice_t<FMT>(cb, 0, q, lane16, fr[q]);
+
+  for (uint32_t g = 0; g < groups; ++g) {
+    // next group's scales (the last group reloads its own)
+    const uint32_t ng = g + 1 < groups ? g + 1 : g;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) scn[t] = *reinterpret_cast<gptr4>(sb[t] + (uint32_t)(ng * 1024u + lane16));
+    sched_fence();
+    run_group<FMT, 0, 0>(cb, g, steps, lane16, fr, sc, acc);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) sc[t] = scn[t];
+  }
+
+  // the clamped reloads of the last step are still in flight: let them land
+  __builtin_amdgcn_s_waitcnt((0 & 15) | (0 << 14) | (7 << 4) | (15 << 8));  // vmcnt(0)
+  store_tile<CDT>(smem, acc, C, ldc, M, N, m0 + wm * 128, n0 + wn * 128, vec != 0, wid, lane);
+}
+
+template <int FMT, int CDT>
+hipError_t launch_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
+                    int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
+  const uint32_t tm = (uint32_t)((M + 255) / 256), tn = (uint32_t)((N + 255) / 256);
+  constexpr int kEpiBytes = 4 * 64 * (128 * (CDT == DT_F32 ? 4 : 2) + 16);  // store_tile staging
+  auto kern = k_gemm_mx_tiled<FMT, CDT>;
+  // raised once per device, so later launches (also inside HIP graphs) make
+  // no call beyond the launch itself
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kEpiBytes);
+    if (e != hipSuccess) return e;
+    attr_done.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  const int64_t eb = CDT == DT_F32 ? 4 : 2;
+  const uint32_t vec = ((reinterpret_cast<uintptr_t>(C) & 15u) == 0 && (ldc * eb) % 16 == 0) ? 1u : 0u;
+  hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(256), kEpiBytes, s, a, sa, b, sb, M, N, K, C, ldc, tm, tn, vec);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mx_tiled(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                                const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
+                                hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (fmt == FMT_MXFP8)
+    return cdt == DT_F32 ? launch_t<FMT_MXFP8, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s)
+                         : launch_t<FMT_MXFP8, DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
+  return cdt == DT_F32 ? launch_t<FMT_MXFP4, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s)
+                       : launch_t<FMT_MXFP4, DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
+}
+
+}  // namespace mxk

@@ -21,6 +21,7 @@
 // "stochastic rounding"); "08 - FP4, MXFP4, NVFP4: The Blackwell Frontier"
 // (MXFP4/NVFP4 table and the paragraph on two-level scaling).
 #include "../device/codec.h"
+#include "../device/tiles.h"
 #include "../device/wave.h"
 #include "../launch.h"
 
@@ -255,9 +256,49 @@ __device__ inline void encode_mx(const QuantArgs& a, int64_t q, const float v[8]
   e.sc = sc;
 }
 
+// Tiled layout (MX only; cols % 1024 == 0, so a 64-chunk slab lies in one
+// row): the lane's 8 codes go to their tile chunk, and the lane holding the
+// first of 4 consecutive blocks stores the pairs (b, b+2) and (b+1, b+3),
+// which sit in the two lane-group slots of its tile row, as 16-bit words.
+template <int FMT>
+__device__ inline void store_enc_tiled(const QuantArgs& a, int64_t q, uint32_t lane,
+                                       const Enc<FMT>& e) {
+  const int64_t cpr = a.cols >> 3;
+  const uint64_t qv = (uint64_t)(q - lane);  // the slab's first chunk: wave-uniform
+  // (readfirstlane returns a signed int: each half goes through uint32_t)
+  const uint32_t qlo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)qv);
+  const uint32_t qhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(qv >> 32));
+  const int64_t qs = (int64_t)(((uint64_t)qhi << 32) | qlo);
+  const int64_t row = (qs >> 32) == 0 && (cpr >> 32) == 0 ? (int64_t)((uint32_t)qs / (uint32_t)cpr)
+                                                          : qs / cpr;
+  const int64_t c8 = qs - row * cpr + lane;
+  constexpr int64_t kBytesPerChunk = FMT == FMT_MXFP8 ? 8 : 4;
+  const int64_t off = tiled_code_off(row, c8 * kBytesPerChunk, cpr * kBytesPerChunk);
+  if constexpr (FMT == FMT_MXFP8) {
+    *reinterpret_cast<uint2*>(a.codes + off) = make_uint2(e.w[0], e.w[1]);
+  } else {
+    *reinterpret_cast<uint32_t*>(a.codes + off) = e.w[0];
+  }
+  const uint32_t s1 = lane_read(e.sc, lane + 4);
+  const uint32_t s2 = lane_read(e.sc, lane + 8);
+  const uint32_t s3 = lane_read(e.sc, lane + 12);
+  if ((lane & 15u) == 0) {
+    const int64_t blk = c8 >> 2;
+    const int64_t so = tiled_scale_off(row, blk, a.cols);  // block blk (even) of the lg = 0 slot
+    *reinterpret_cast<uint16_t*>(a.scales + so) = (uint16_t)(e.sc | (s2 << 8));
+    *reinterpret_cast<uint16_t*>(a.scales + so + 32 * 16) = (uint16_t)(s1 | (s3 << 8));
+  }
+}
+
 template <int FMT>
 __device__ inline void store_enc(const QuantArgs& a, int64_t q, int64_t Q, uint32_t lane,
                                  uint32_t lanes_per_block, const Enc<FMT>& e) {
+  if constexpr (FMT != FMT_NVFP4) {
+    if (a.tiled) {  // Q is a multiple of the slab: every lane is valid
+      store_enc_tiled<FMT>(a, q, lane, e);
+      return;
+    }
+  }
   if (q < Q) {
     if constexpr (FMT == FMT_MXFP8) {
       *reinterpret_cast<uint2*>(a.codes + q * 8) = make_uint2(e.w[0], e.w[1]);
@@ -406,7 +447,7 @@ template <int FMT, int YDT, bool RHT>
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* codes, const uint8_t* scales,
                                                       const float* tensor_scale, int64_t cols,
                                                       void* y, int64_t ld_y, int64_t Q,
-                                                      uint32_t sign_mask) {
+                                                      uint32_t sign_mask, bool tiled) {
   const uint32_t lane = threadIdx.x & 63u;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const float S = FMT == FMT_NVFP4 ? *tensor_scale : 1.0f;
@@ -420,15 +461,24 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* codes, cons
     float v[8];
     if (valid) {
       uint32_t cw[8];
+      // tiled layout (MX only): code and scale offsets of this chunk
+      int64_t coff = q * (FMT == FMT_MXFP8 ? 8 : 4), soff = q >> 2;
+      if constexpr (FMT != FMT_NVFP4) {
+        if (tiled) {
+          const int64_t row = q / cpr, c8 = q - row * cpr;
+          coff = tiled_code_off(row, c8 * (FMT == FMT_MXFP8 ? 8 : 4), cpr * (FMT == FMT_MXFP8 ? 8 : 4));
+          soff = tiled_scale_off(row, c8 >> 2, cols);
+        }
+      }
       if constexpr (FMT == FMT_MXFP8) {
-        uint2 p = *reinterpret_cast<const uint2*>(codes + q * 8);
+        uint2 p = *reinterpret_cast<const uint2*>(codes + coff);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           cw[i] = (p.x >> (8 * i)) & 0xFFu;
           cw[4 + i] = (p.y >> (8 * i)) & 0xFFu;
         }
       } else {
-        uint32_t p = *reinterpret_cast<const uint32_t*>(codes + q * 4);
+        uint32_t p = *reinterpret_cast<const uint32_t*>(codes + coff);
 #pragma unroll
         for (int i = 0; i < 8; ++i) cw[i] = (p >> (4 * i)) & 0xFu;
       }
@@ -437,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* codes, cons
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = (e2m1_value(cw[i]) * sbv) * S;  // first product exact
       } else {
-        const uint32_t sc = scales[q >> 2];
+        const uint32_t sc = scales[soff];
         // 2^(sc-127) as FP32 (sc = 0 is the subnormal 2^-127); 0xFF is NaN
         const float X = sc == 0xFFu ? __builtin_nanf("") : (sc == 0u ? u2f(0x00400000u) : u2f(sc << 23));
 #pragma unroll
@@ -557,13 +607,14 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
 
 hipError_t launch_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales,
                              const float* tensor_scale, int64_t rows, int64_t cols, void* y,
-                             int ydt, int64_t ld_y, bool rht, uint32_t sign_mask, hipStream_t s) {
+                             int ydt, int64_t ld_y, bool rht, uint32_t sign_mask, bool tiled,
+                             hipStream_t s) {
   const int64_t Q = rows * (cols / 8);
   if (Q == 0) return hipSuccess;
   const int g = grid_for(Q);
 #define MXK_DQ(F, Y, R)                                                                       \
   hipLaunchKernelGGL((k_dequant<F, Y, R>), dim3(g), dim3(kThreads), 0, s, codes, scales,       \
-                     tensor_scale, cols, y, ld_y, Q, sign_mask)
+                     tensor_scale, cols, y, ld_y, Q, sign_mask, tiled)
 #define MXK_DQ_Y(F, R)                 \
   if (ydt == DT_BF16) MXK_DQ(F, DT_BF16, R); \
   else MXK_DQ(F, DT_F32, R);

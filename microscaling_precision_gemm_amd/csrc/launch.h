@@ -24,6 +24,7 @@ struct QuantArgs {
   bool rht;
   uint32_t sign_mask;
   bool amax_given;
+  bool tiled;  // codes and scales in the matrix-instruction tile layout
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
@@ -31,7 +32,8 @@ hipError_t launch_amax(const void* x, int xdt, int64_t rows, int64_t cols, int64
                        uint32_t sign_mask, float* amax, hipStream_t s);
 hipError_t launch_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales,
                              const float* tensor_scale, int64_t rows, int64_t cols, void* y,
-                             int ydt, int64_t ld_y, bool rht, uint32_t sign_mask, hipStream_t s);
+                             int ydt, int64_t ld_y, bool rht, uint32_t sign_mask, bool tiled,
+                             hipStream_t s);
 hipError_t launch_hadamard16(const void* x, int xdt, void* y, int ydt, int64_t rows, int64_t cols,
                              uint32_t sign_mask, bool inverse, hipStream_t s);
 hipError_t launch_requant_transpose(const uint8_t* src_codes, const uint8_t* src_scales,
@@ -42,6 +44,11 @@ hipError_t launch_requant_transpose(const uint8_t* src_codes, const uint8_t* src
 hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
                           int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s);
+// A and B in the tiled layout (M, N multiples of 32, K of 1024)
+hipError_t launch_gemm_mx_tiled(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                                const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
+                                hipStream_t s);
 hipError_t launch_gemm_mxfp8_exact(const uint8_t* a_codes, const uint8_t* a_scales,
                                    const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                    int64_t N, int64_t K, void* C, int cdt, int64_t ldc,

@@ -126,3 +126,26 @@ def test_binding_fails_loudly_without_library(mx, monkeypatch):
     monkeypatch.setattr(mx, "LIB_PATH", "/nonexistent/libmx.so")
     with pytest.raises(mx.MXError):
         mx.load()
+
+
+def _tl(mx, fmt, rows, cols, layout, ts=FAKE):
+    return mx._Tensor(fmt, layout, rows, cols, FAKE, FAKE, ts)
+
+
+def test_layout_argument_checks(mx):
+    L = mx.load()
+    rng = mx._Rng(0, 0)
+    q = lambda out, rows, cols: L.mx_quantize(FAKE, 0, rows, cols, cols, ctypes.byref(out), 0, rng, 0, 0, None, None)
+    assert q(_tl(mx, 2, 32, 1024, 7), 32, 1024) == 4              # unknown layout
+    assert q(_tl(mx, 2, 32, 512, 1), 32, 512) == 2                # tiled needs cols % 1024
+    assert q(_tl(mx, 2, 48, 1024, 1), 48, 1024) == 2              # tiled needs rows % 32
+    assert L.mx_quantize(FAKE, 0, 32, 1024, 1024, ctypes.byref(_tl(mx, 3, 32, 1024, 1)), 0, rng, 0, 0,
+                         FAKE, None) == 5                          # NVFP4 has no tiled layout
+    g = lambda a, b, flags=0: L.mx_gemm_ex(ctypes.byref(a), ctypes.byref(b), FAKE, 0, 64, flags, None)
+    assert g(_tl(mx, 2, 64, 1024, 1), _tl(mx, 2, 64, 1024, 0)) == 5  # mixed layouts
+    assert g(_tl(mx, 1, 64, 1024, 1), _tl(mx, 1, 64, 1024, 1)) == 5  # tiled MXFP8 needs native
+    src = _tl(mx, 3, 64, 1024, 1)
+    assert L.mx_requant_transpose(ctypes.byref(src), None, 0, 64, 1024, ctypes.byref(_tl(mx, 1, 1024, 64, 0)),
+                                  1, rng, None) == 5
+    assert L.mx_requant_transpose(None, FAKE, 1024, 1024, 1024, ctypes.byref(_tl(mx, 1, 1024, 1024, 1)),
+                                  1, rng, None) == 5               # tiled requant output
