@@ -5,8 +5,9 @@ x50) and B (weights 4096x4096 BF16, N(0, 0.02^2)) to MXFP4 E2M1 with E8M0
 scales per 32 (round-to-nearest-even), then the block-scaled GEMM
 C = A * B^T (4096^3, FP32 accumulation, BF16 out).  Inputs are resident in
 HBM before the timed region and rotate over 16 copies (1 GiB of BF16) so the
-256 MB last-level cache does not hold them between steps.  The step's three
-calls are launched eagerly (--graph replays them from a HIP graph captured
+256 MB last-level cache does not hold them between steps.  The quantizer
+writes the matrix-instruction tile layout, which the GEMM reads with
+register-direct loads.  The step's three calls are launched eagerly (--graph replays them from a HIP graph captured
 once per input slot instead).
 
 Prints one JSON line: metric / value (TFLOP/s of the whole step: 2*M*N*K per
@@ -57,7 +58,7 @@ def parse():
 # passes, stored with the hash of the kernel source they were taken on: a
 # changed kernel reports null until the counters are taken again.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mxfp4_4096_traffic.txt")
-GEMM_SOURCE = os.path.join(ROOT, "microscaling_precision_gemm_amd", "csrc", "kernels", "gemm_mx.hip")
+GEMM_SOURCE = os.path.join(ROOT, "microscaling_precision_gemm_amd", "csrc", "kernels", "gemm_tiled.hip")
 
 
 def gemm_traffic():
@@ -131,8 +132,10 @@ def headline(torch, mx, W, args):
     nrot = 16
     As = [A0] + [A0.clone() for _ in range(nrot - 1)]
     Bs = [B0] + [B0.clone() for _ in range(nrot - 1)]
-    qa = mx.empty(mx.MX_MXFP4_E2M1, M, K)
-    qb = mx.empty(mx.MX_MXFP4_E2M1, N, K)
+    # operands quantized straight into the matrix-instruction tile layout,
+    # which the register-direct GEMM kernel reads
+    qa = mx.empty(mx.MX_MXFP4_E2M1, M, K, layout=mx.MX_LAYOUT_TILED)
+    qb = mx.empty(mx.MX_MXFP4_E2M1, N, K, layout=mx.MX_LAYOUT_TILED)
     C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
 
     def launch(i):
@@ -260,11 +263,24 @@ def detail(torch, mx, W, args):
     ms = time_fn(torch, lambda: mx.mx_gemm_ex(qa, qb, C, mx.MX_GEMM_FP8_NATIVE), it, wu)
     res["mxfp8_gemm_4096_native_fp8"] = {"ms": ms, "tflops": 2 * M * N * K / ms / 1e9,
                                          "frac_fp8_peak": 2 * M * N * K / ms / 1e9 / PEAK_TFLOPS["fp8"]}
+    qat, qbt = mx.empty(1, M, K, layout=mx.MX_LAYOUT_TILED), mx.empty(1, N, K, layout=mx.MX_LAYOUT_TILED)
+    mx.mx_quantize(a, qat)
+    mx.mx_quantize(b, qbt)
+    ms = time_fn(torch, lambda: mx.mx_gemm_ex(qat, qbt, C, mx.MX_GEMM_FP8_NATIVE), it, wu)
+    res["mxfp8_gemm_4096_native_fp8_tiled"] = {"ms": ms, "tflops": 2 * M * N * K / ms / 1e9,
+                                               "frac_fp8_peak": 2 * M * N * K / ms / 1e9 / PEAK_TFLOPS["fp8"]}
     mx.mx_quantize(a, qa)
     ms = time_fn(torch, lambda: mx.mx_quantize(a, qa), it, wu)
     by = M * K * (2 + 1 + 1 / 32)
     res["mxfp8_quantize_4096x4096"] = {"ms": ms, "gbs": by / ms / 1e6, "frac_hbm": by / ms / 1e6 / PEAK_HBM_GBS}
-    del a, b, qa, qb, C
+    # MXFP4 4096^3 on row-major operands (LDS-pipelined kernel), for comparison
+    q4a, q4b = mx.empty(2, M, K), mx.empty(2, N, K)
+    mx.mx_quantize(a, q4a)
+    mx.mx_quantize(b, q4b)
+    ms = time_fn(torch, lambda: mx.mx_gemm(q4a, q4b, C), it, wu)
+    res["mxfp4_gemm_4096_rows_layout"] = {"ms": ms, "tflops": 2 * M * N * K / ms / 1e9,
+                                          "frac_fp4_peak": 2 * M * N * K / ms / 1e9 / PEAK_TFLOPS["fp4"]}
+    del a, b, qa, qb, qat, qbt, q4a, q4b, C
 
     # NVFP4 MoE forward: 4096 tokens x 7168, top-8 of 32 experts, W_e 2048x7168
     tokens, hid, E, topk, inter = 4096, 7168, 32, 8, 2048
@@ -357,7 +373,8 @@ def main():
     roof = {"bound": "mfma", "achieved": h["gemm_tflops"], "peak": PEAK_TFLOPS["fp4"],
             "unit": "TFLOP/s", "frac": h["gemm_tflops"] / PEAK_TFLOPS["fp4"], "traffic": gemm_traffic(),
             "traffic_unit": "bytes per launch", "algorithmic_bytes": 2 * 4096 * 4096 * (0.5 + 1 / 32) + 4096 * 4096 * 2,
-            "kernel": "k_gemm_mx<MXFP4, BF16 out, 256x256>", "gemm_ms": h["gemm_ms"]}
+            "kernel": "k_gemm_mx_tiled<MXFP4, BF16 out> (256x256 per workgroup, tile layout)",
+            "gemm_ms": h["gemm_ms"]}
     line = {
         "metric": "block-scaled GEMM TFLOPS (MXFP4/NVFP4/MXFP8 4096^3) + quantize HBM GB/s",
         "value": h["value"],
@@ -374,7 +391,8 @@ def main():
         "config": {"workload": "MXFP4 E2M1 quantize (RNE, E8M0/32) of A 4096x4096 BF16 N(0,1) "
                                "with 1% of K-columns x50 and B 4096x4096 BF16 N(0,0.02^2), then "
                                "block-scaled GEMM M=N=K=4096, FP32 accumulate, BF16 out",
-                   "M": 4096, "N": 4096, "K": 4096, "input_rotation": 16, "launch": h["launch"]},
+                   "M": 4096, "N": 4096, "K": 4096, "input_rotation": 16, "launch": h["launch"],
+                   "layout": "mx tile layout"},
         "roofline": roof,
         "quantize": {"ms_per_operand": h["quant_ms"], "achieved_gbs": h["quant_gbs"],
                      "peak_gbs": PEAK_HBM_GBS, "frac": h["quant_gbs"] / PEAK_HBM_GBS,

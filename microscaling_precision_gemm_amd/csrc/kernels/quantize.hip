@@ -256,49 +256,9 @@ __device__ inline void encode_mx(const QuantArgs& a, int64_t q, const float v[8]
   e.sc = sc;
 }
 
-// Tiled layout (MX only; cols % 1024 == 0, so a 64-chunk slab lies in one
-// row): the lane's 8 codes go to their tile chunk, and the lane holding the
-// first of 4 consecutive blocks stores the pairs (b, b+2) and (b+1, b+3),
-// which sit in the two lane-group slots of its tile row, as 16-bit words.
-template <int FMT>
-__device__ inline void store_enc_tiled(const QuantArgs& a, int64_t q, uint32_t lane,
-                                       const Enc<FMT>& e) {
-  const int64_t cpr = a.cols >> 3;
-  const uint64_t qv = (uint64_t)(q - lane);  // the slab's first chunk: wave-uniform
-  // (readfirstlane returns a signed int: each half goes through uint32_t)
-  const uint32_t qlo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)qv);
-  const uint32_t qhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(qv >> 32));
-  const int64_t qs = (int64_t)(((uint64_t)qhi << 32) | qlo);
-  const int64_t row = (qs >> 32) == 0 && (cpr >> 32) == 0 ? (int64_t)((uint32_t)qs / (uint32_t)cpr)
-                                                          : qs / cpr;
-  const int64_t c8 = qs - row * cpr + lane;
-  constexpr int64_t kBytesPerChunk = FMT == FMT_MXFP8 ? 8 : 4;
-  const int64_t off = tiled_code_off(row, c8 * kBytesPerChunk, cpr * kBytesPerChunk);
-  if constexpr (FMT == FMT_MXFP8) {
-    *reinterpret_cast<uint2*>(a.codes + off) = make_uint2(e.w[0], e.w[1]);
-  } else {
-    *reinterpret_cast<uint32_t*>(a.codes + off) = e.w[0];
-  }
-  const uint32_t s1 = lane_read(e.sc, lane + 4);
-  const uint32_t s2 = lane_read(e.sc, lane + 8);
-  const uint32_t s3 = lane_read(e.sc, lane + 12);
-  if ((lane & 15u) == 0) {
-    const int64_t blk = c8 >> 2;
-    const int64_t so = tiled_scale_off(row, blk, a.cols);  // block blk (even) of the lg = 0 slot
-    *reinterpret_cast<uint16_t*>(a.scales + so) = (uint16_t)(e.sc | (s2 << 8));
-    *reinterpret_cast<uint16_t*>(a.scales + so + 32 * 16) = (uint16_t)(s1 | (s3 << 8));
-  }
-}
-
 template <int FMT>
 __device__ inline void store_enc(const QuantArgs& a, int64_t q, int64_t Q, uint32_t lane,
                                  uint32_t lanes_per_block, const Enc<FMT>& e) {
-  if constexpr (FMT != FMT_NVFP4) {
-    if (a.tiled) {  // Q is a multiple of the slab: every lane is valid
-      store_enc_tiled<FMT>(a, q, lane, e);
-      return;
-    }
-  }
   if (q < Q) {
     if constexpr (FMT == FMT_MXFP8) {
       *reinterpret_cast<uint2*>(a.codes + q * 8) = make_uint2(e.w[0], e.w[1]);
@@ -332,6 +292,143 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx(QuantArgs a, int64_t Q) {
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) store_enc<FMT>(a, q0 + 64 * u, Q, lane, 4u, enc[u]);
+}
+
+// ---- MX quantizer writing the matrix-instruction tile layout --------------
+// One wave per code tile (32 rows x 128 code bytes: 256 FP4 / 128 FP8
+// elements per row).  Lane l = 32 lg + r owns row r of the tile and its
+// blocks b = 2j + lg (j = 0 .. 3 FP4, 0 .. 1 FP8): block maxima and the
+// Hadamard transform stay inside the lane, every code store is one 16-byte
+// chunk (a wave writes whole 1 KB runs of its tile) and the lane's scale
+// bytes are consecutive in the scale tile.  Same element arithmetic as
+// k_quant_mx; the random stream index of an element is its row-major
+// position, as in the row layout.
+template <int XDT>
+__device__ inline void load_block(const void* x, int64_t off, float v[32]) {
+  Raw<XDT> r[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) load_raw<XDT>(x, off + 8 * c, r[c]);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) widen<XDT>(r[c], v + 8 * c);
+}
+
+// y = (1/4) H16 D x on the two 16-groups of a block, in the lane (butterfly
+// strides 1, 2, 4, 8 in that order, as in rht_forward).
+__device__ inline void rht_block(float v[32], uint32_t mask) {
+#pragma unroll
+  for (int h16 = 0; h16 < 2; ++h16) {
+    float* g = v + 16 * h16;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((mask >> i) & 1u) g[i] = -g[i];
+    hadamard8_stages(g);
+    hadamard8_stages(g + 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = g[i], q = g[i + 8];
+      g[i] = p + q;
+      g[i + 8] = p - q;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) g[i] = 0.25f * g[i];
+  }
+}
+
+template <int XDT, int FMT, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads) void k_quant_mx_tiled(QuantArgs a, int64_t ntiles) {
+  constexpr int BPL = FMT == FMT_MXFP8 ? 2 : 4;    // blocks per lane
+  constexpr int EPT = FMT == FMT_MXFP8 ? 128 : 256; // elements per tile row
+  constexpr uint32_t emax = FMT == FMT_MXFP8 ? 8u : 2u;
+  const uint32_t lane = threadIdx.x & 63u;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  if (wave >= ntiles) return;  // whole waves
+  const int64_t tpr = a.cols / EPT;  // code tiles per row tile
+  const int64_t T = wave / tpr, t = wave - T * tpr;
+  const uint32_t r = lane & 31u, lg = lane >> 5;
+  const int64_t row = 32 * T + r;
+  const int64_t col0 = t * EPT;
+  float v[BPL][32];
+#pragma unroll
+  for (int j = 0; j < BPL; ++j) load_block<XDT>(a.x, row * a.ld_x + col0 + 32 * (2 * j + lg), v[j]);
+  uint8_t* ctile = a.codes + (T * tpr + t) * 4096;
+  uint32_t scw = 0;  // the lane's scale bytes, block j in byte j
+#pragma unroll
+  for (int j = 0; j < BPL; ++j) {
+    const int64_t col = col0 + 32 * (2 * j + lg);
+    if constexpr (RHT) rht_block(v[j], a.sign_mask);
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t bits = f2u(v[j][i]) & 0x7FFFFFFFu;
+      m = bits > m ? bits : m;
+    }
+    const uint32_t sc = e8m0_from_amax_bits(m, emax);
+    const float inv = e8m0_inverse(sc);
+    u4 out[FMT == FMT_MXFP8 ? 2 : 1];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {  // 8 elements at a time
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = v[j][8 * c + i] * inv;  // exact
+      uint32_t w[2];
+      if constexpr (!SR) {
+        if constexpr (FMT == FMT_MXFP8) pack_e4m3_rne(y, w);
+        else w[0] = pack_e2m1_rne(y);
+      } else {
+        uint32_t rr[8];
+        rand16x8(a.seed, a.counter, (uint64_t)((row * a.cols + col) / 8 + c), rr);
+        uint32_t cc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          cc[i] = FMT == FMT_MXFP8 ? e4m3_encode(y[i], true, rr[i]) : e2m1_encode(y[i], true, rr[i]);
+        if constexpr (FMT == FMT_MXFP8) {
+          w[0] = cc[0] | (cc[1] << 8) | (cc[2] << 16) | (cc[3] << 24);
+          w[1] = cc[4] | (cc[5] << 8) | (cc[6] << 16) | (cc[7] << 24);
+        } else {
+          uint32_t p = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) p |= cc[i] << (4 * i);
+          w[0] = p;
+        }
+      }
+      if (sc == 0xFFu) w[0] = w[1] = 0u;  // NaN / Inf in the block
+      if constexpr (FMT == FMT_MXFP8) {
+        out[c >> 1][2 * (c & 1)] = w[0];
+        out[c >> 1][2 * (c & 1) + 1] = w[1];
+      } else {
+        out[0][c] = w[0];
+      }
+    }
+    // block b = 2j + lg: FP4 one chunk (run j, slot lane); FP8 chunks 2b and
+    // 2b + 1 (run b, slots r and 32 + r)
+    if constexpr (FMT == FMT_MXFP8) {
+      const uint32_t b = 2 * j + lg;
+      *reinterpret_cast<u4*>(ctile + b * 1024 + r * 16) = out[0];
+      *reinterpret_cast<u4*>(ctile + b * 1024 + (32 + r) * 16) = out[1];
+    } else {
+      *reinterpret_cast<u4*>(ctile + j * 1024 + lane * 16) = out[0];
+    }
+    scw |= sc << (8 * j);
+  }
+  // scale tile of the 1024-element group; the lane's BPL bytes are
+  // consecutive at byte (group position of the tile) * BPL
+  const int64_t gsz = 1024 / EPT;  // code tiles per scale group
+  uint8_t* stile = a.scales + (T * (a.cols / 1024) + t / gsz) * 1024 + lane * 16 + (t % gsz) * BPL;
+  if constexpr (BPL == 4) *reinterpret_cast<uint32_t*>(stile) = scw;
+  else *reinterpret_cast<uint16_t*>(stile) = (uint16_t)scw;
+}
+
+template <int XDT, int FMT, bool SR, bool RHT>
+hipError_t quant_mx_tiled_t(const QuantArgs& a, hipStream_t s) {
+  const int64_t ntiles = (a.rows / 32) * (a.cols / (FMT == FMT_MXFP8 ? 128 : 256));
+  const int64_t blocks = (ntiles + 3) / 4;
+  hipLaunchKernelGGL((k_quant_mx_tiled<XDT, FMT, SR, RHT>), dim3((uint32_t)blocks), dim3(kThreads), 0, s, a, ntiles);
+  return hipGetLastError();
+}
+template <int XDT, int FMT>
+hipError_t quant_mx_tiled_d(const QuantArgs& a, hipStream_t s) {
+  if (a.sr) return a.rht ? quant_mx_tiled_t<XDT, FMT, true, true>(a, s) : quant_mx_tiled_t<XDT, FMT, true, false>(a, s);
+  return a.rht ? quant_mx_tiled_t<XDT, FMT, false, true>(a, s) : quant_mx_tiled_t<XDT, FMT, false, false>(a, s);
 }
 
 // ---- NVFP4 (E4M3 per 16 + FP32 per tensor) quantizer ----------------------
@@ -600,6 +697,11 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
     return a.xdt == DT_BF16 ? quant_nv_d<DT_BF16>(a, Q, s) : quant_nv_d<DT_F32>(a, Q, s);
   }
   if (Q == 0) return hipSuccess;
+  if (a.tiled) {
+    if (a.fmt == FMT_MXFP8)
+      return a.xdt == DT_BF16 ? quant_mx_tiled_d<DT_BF16, FMT_MXFP8>(a, s) : quant_mx_tiled_d<DT_F32, FMT_MXFP8>(a, s);
+    return a.xdt == DT_BF16 ? quant_mx_tiled_d<DT_BF16, FMT_MXFP4>(a, s) : quant_mx_tiled_d<DT_F32, FMT_MXFP4>(a, s);
+  }
   if (a.fmt == FMT_MXFP8)
     return a.xdt == DT_BF16 ? quant_mx_d<DT_BF16, FMT_MXFP8>(a, Q, s) : quant_mx_d<DT_F32, FMT_MXFP8>(a, Q, s);
   return a.xdt == DT_BF16 ? quant_mx_d<DT_BF16, FMT_MXFP4>(a, Q, s) : quant_mx_d<DT_F32, FMT_MXFP4>(a, Q, s);
