@@ -295,134 +295,88 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx(QuantArgs a, int64_t Q) {
 }
 
 // ---- MX quantizer writing the matrix-instruction tile layout --------------
-// One wave per code tile (32 rows x 128 code bytes: 256 FP4 / 128 FP8
-// elements per row).  Lane l = 32 lg + r owns row r of the tile and its
-// blocks b = 2j + lg (j = 0 .. 3 FP4, 0 .. 1 FP8): block maxima and the
-// Hadamard transform stay inside the lane, every code store is one 16-byte
-// chunk (a wave writes whole 1 KB runs of its tile) and the lane's scale
-// bytes are consecutive in the scale tile.  Same element arithmetic as
-// k_quant_mx; the random stream index of an element is its row-major
-// position, as in the row layout.
-template <int XDT>
-__device__ inline void load_block(const void* x, int64_t off, float v[32]) {
-  Raw<XDT> r[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) load_raw<XDT>(x, off + 8 * c, r[c]);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) widen<XDT>(r[c], v + 8 * c);
-}
-
-// y = (1/4) H16 D x on the two 16-groups of a block, in the lane (butterfly
-// strides 1, 2, 4, 8 in that order, as in rht_forward).
-__device__ inline void rht_block(float v[32], uint32_t mask) {
-#pragma unroll
-  for (int h16 = 0; h16 < 2; ++h16) {
-    float* g = v + 16 * h16;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if ((mask >> i) & 1u) g[i] = -g[i];
-    hadamard8_stages(g);
-    hadamard8_stages(g + 8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = g[i], q = g[i + 8];
-      g[i] = p + q;
-      g[i + 8] = p - q;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) g[i] = 0.25f * g[i];
-  }
-}
+// One wave per 8 rows x 64 NT columns (NT = 4 load instructions, a quarter
+// of a 1024-column scale group).  Load instruction t of the wave covers
+// columns 64 t .. 64 t + 63 of its 8 rows (t counted from the start of the
+// scale group): lane 8 i + k holds chunk k (8 elements) of row i, so an MX
+// block is a lane quad and a Hadamard group a lane pair, exactly as in the
+// row layout, and the element arithmetic is encode_mx's (random stream
+// indexed by the chunk's row-major position).  Each load instruction reads
+// 8 rows x 128 contiguous bytes, and the codes of one instruction fill whole
+// 128-byte runs of the code tile (two for FP4, four for FP8).  The first
+// lane of a quad sees blocks of one parity of its row, which are
+// consecutive bytes of its row's 16-byte word of the scale tile: the NT = 4
+// bytes go out in one 32-bit store.
+// Load instructions per wave: 4 (a quarter of a scale group) measured faster
+// than 8 or 16 for both roundings -- more waves in flight, which SR's
+// branchy encoders need most.
+constexpr int kTiledNT = 4;
 
 template <int XDT, int FMT, bool SR, bool RHT>
-__global__ __launch_bounds__(kThreads) void k_quant_mx_tiled(QuantArgs a, int64_t ntiles) {
-  constexpr int BPL = FMT == FMT_MXFP8 ? 2 : 4;    // blocks per lane
-  constexpr int EPT = FMT == FMT_MXFP8 ? 128 : 256; // elements per tile row
-  constexpr uint32_t emax = FMT == FMT_MXFP8 ? 8u : 2u;
+__global__ __launch_bounds__(kThreads) void k_quant_mx_tiled(QuantArgs a, int64_t nwaves) {
+  constexpr int NT = kTiledNT;
+  constexpr int kParts = 16 / NT;  // waves per scale group and row octet
   const uint32_t lane = threadIdx.x & 63u;
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  if (wave >= ntiles) return;  // whole waves
-  const int64_t tpr = a.cols / EPT;  // code tiles per row tile
-  const int64_t T = wave / tpr, t = wave - T * tpr;
-  const uint32_t r = lane & 31u, lg = lane >> 5;
-  const int64_t row = 32 * T + r;
-  const int64_t col0 = t * EPT;
-  float v[BPL][32];
+  if (wave >= nwaves) return;  // whole waves
+  const int64_t gpr = a.cols >> 10;  // scale groups per row
+  const int64_t wpr = gpr * kParts;  // waves per row octet
+  const int64_t R8 = wave / wpr, rem = wave - R8 * wpr;
+  const int64_t G = rem / kParts;
+  const int t0 = (int)(rem - G * kParts) * NT;  // first instruction index in the group
+  const uint32_t i = lane >> 3, k = lane & 7u;
+  const int64_t row = 8 * R8 + i;
+  const int64_t col0 = G * 1024 + 64 * t0 + 8 * k;  // the lane's element in the wave's instruction 0
+  Raw<XDT> raw[NT];
+  {
+    const int64_t xoff = row * a.ld_x + col0;
 #pragma unroll
-  for (int j = 0; j < BPL; ++j) load_block<XDT>(a.x, row * a.ld_x + col0 + 32 * (2 * j + lg), v[j]);
-  uint8_t* ctile = a.codes + (T * tpr + t) * 4096;
-  uint32_t scw = 0;  // the lane's scale bytes, block j in byte j
-#pragma unroll
-  for (int j = 0; j < BPL; ++j) {
-    const int64_t col = col0 + 32 * (2 * j + lg);
-    if constexpr (RHT) rht_block(v[j], a.sign_mask);
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t bits = f2u(v[j][i]) & 0x7FFFFFFFu;
-      m = bits > m ? bits : m;
-    }
-    const uint32_t sc = e8m0_from_amax_bits(m, emax);
-    const float inv = e8m0_inverse(sc);
-    u4 out[FMT == FMT_MXFP8 ? 2 : 1];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {  // 8 elements at a time
-      float y[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = v[j][8 * c + i] * inv;  // exact
-      uint32_t w[2];
-      if constexpr (!SR) {
-        if constexpr (FMT == FMT_MXFP8) pack_e4m3_rne(y, w);
-        else w[0] = pack_e2m1_rne(y);
-      } else {
-        uint32_t rr[8];
-        rand16x8(a.seed, a.counter, (uint64_t)((row * a.cols + col) / 8 + c), rr);
-        uint32_t cc[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          cc[i] = FMT == FMT_MXFP8 ? e4m3_encode(y[i], true, rr[i]) : e2m1_encode(y[i], true, rr[i]);
-        if constexpr (FMT == FMT_MXFP8) {
-          w[0] = cc[0] | (cc[1] << 8) | (cc[2] << 16) | (cc[3] << 24);
-          w[1] = cc[4] | (cc[5] << 8) | (cc[6] << 16) | (cc[7] << 24);
-        } else {
-          uint32_t p = 0;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) p |= cc[i] << (4 * i);
-          w[0] = p;
-        }
-      }
-      if (sc == 0xFFu) w[0] = w[1] = 0u;  // NaN / Inf in the block
-      if constexpr (FMT == FMT_MXFP8) {
-        out[c >> 1][2 * (c & 1)] = w[0];
-        out[c >> 1][2 * (c & 1) + 1] = w[1];
-      } else {
-        out[0][c] = w[0];
-      }
-    }
-    // block b = 2j + lg: FP4 one chunk (run j, slot lane); FP8 chunks 2b and
-    // 2b + 1 (run b, slots r and 32 + r)
-    if constexpr (FMT == FMT_MXFP8) {
-      const uint32_t b = 2 * j + lg;
-      *reinterpret_cast<u4*>(ctile + b * 1024 + r * 16) = out[0];
-      *reinterpret_cast<u4*>(ctile + b * 1024 + (32 + r) * 16) = out[1];
-    } else {
-      *reinterpret_cast<u4*>(ctile + j * 1024 + lane * 16) = out[0];
-    }
-    scw |= sc << (8 * j);
+    for (int t = 0; t < NT; ++t) load_raw<XDT>(a.x, xoff + 64 * t, raw[t]);
   }
-  // scale tile of the 1024-element group; the lane's BPL bytes are
-  // consecutive at byte (group position of the tile) * BPL
-  const int64_t gsz = 1024 / EPT;  // code tiles per scale group
-  uint8_t* stile = a.scales + (T * (a.cols / 1024) + t / gsz) * 1024 + lane * 16 + (t % gsz) * BPL;
-  if constexpr (BPL == 4) *reinterpret_cast<uint32_t*>(stile) = scw;
-  else *reinterpret_cast<uint16_t*>(stile) = (uint16_t)scw;
+  const int64_t q0 = (row * a.cols + col0) >> 3;
+  Enc<FMT> enc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float v[8];
+    widen<XDT>(raw[t], v);
+    if constexpr (RHT) rht_forward(v, a.sign_mask, k & 1u);
+    encode_mx<FMT, SR>(a, q0 + 8 * t, v, enc[t]);
+  }
+  // Codes: instruction index T = t0 + t in the group.  FP4: code byte
+  // 512 G + 32 T + 4 k of the row, i.e. code tile 4 G + T/4, chunk
+  // 2 (T%4) + k/4, byte 4 (k%4).  FP8: code byte 1024 G + 64 T + 8 k, i.e.
+  // code tile 8 G + T/2, chunk 4 (T%2) + k/2, byte 8 (k%2).
+  const uint32_t r = (uint32_t)row & 31u;
+  const int64_t row_bytes = FMT == FMT_MXFP8 ? a.cols : a.cols >> 1;
+  uint8_t* cbase = a.codes + ((row >> 5) * (row_bytes >> 7) + G * (FMT == FMT_MXFP8 ? 8 : 4)) * 4096;
+  if constexpr (FMT == FMT_MXFP8) {
+    cbase += (k >> 2) * 1024u + (((k >> 1) & 1u) * 32u + r) * 16u + 8u * (k & 1u) + (t0 >> 1) * 4096;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)  // t0 is even
+      *reinterpret_cast<uint2*>(cbase + (t >> 1) * 4096 + (t & 1) * 2048) = make_uint2(enc[t].w[0], enc[t].w[1]);
+  } else {
+    cbase += ((k >> 2) * 32u + r) * 16u + 4u * (k & 3u) + (t0 >> 2) * 4096;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)  // t0 is a multiple of 4
+      *reinterpret_cast<uint32_t*>(cbase + (t >> 2) * 4096 + (t & 3) * 1024) = enc[t].w[0];
+  }
+  // Scales: block 32 G + 2 T + k/4 of the row is byte T of the word at
+  // ((k/4) * 32 + r) * 16 in scale tile G of the row tile.
+  if ((k & 3u) == 0) {
+    uint32_t w[NT / 4];
+#pragma unroll
+    for (int d = 0; d < NT / 4; ++d)
+      w[d] = enc[4 * d].sc | (enc[4 * d + 1].sc << 8) | (enc[4 * d + 2].sc << 16) | (enc[4 * d + 3].sc << 24);
+    static_assert(NT == 4, "one 32-bit scale store per quad");
+    *reinterpret_cast<uint32_t*>(a.scales + ((row >> 5) * gpr + G) * 1024 + ((k >> 2) * 32u + r) * 16u + t0) = w[0];
+  }
 }
 
 template <int XDT, int FMT, bool SR, bool RHT>
 hipError_t quant_mx_tiled_t(const QuantArgs& a, hipStream_t s) {
-  const int64_t ntiles = (a.rows / 32) * (a.cols / (FMT == FMT_MXFP8 ? 128 : 256));
-  const int64_t blocks = (ntiles + 3) / 4;
-  hipLaunchKernelGGL((k_quant_mx_tiled<XDT, FMT, SR, RHT>), dim3((uint32_t)blocks), dim3(kThreads), 0, s, a, ntiles);
+  const int64_t nwaves = (a.rows / 8) * (a.cols / (64 * kTiledNT));
+  const int64_t blocks = (nwaves + 3) / 4;
+  hipLaunchKernelGGL((k_quant_mx_tiled<XDT, FMT, SR, RHT>), dim3((uint32_t)blocks), dim3(kThreads), 0, s, a, nwaves);
   return hipGetLastError();
 }
 template <int XDT, int FMT>
