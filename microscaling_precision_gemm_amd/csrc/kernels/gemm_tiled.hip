@@ -10,10 +10,11 @@
 // lane l's 16 bytes at offset 16 l, and the scales a lane applies over 1024
 // elements of K are one 16-byte word.  So every wave loads its fragments
 // straight from global memory into registers with fully coalesced 16-byte
-// loads, and the main loop uses no LDS at all.  (Measured on gfx950: LDS
-// writes -- ds_write or global-to-LDS DMA -- issued while matrix
-// instructions run slow those instructions down by about half, while global
-// loads into registers overlap them completely.)
+// loads, and the main loop uses no LDS at all.  (Measured on gfx950 with
+// realistic operands: a variant that shares fragments between the waves
+// through a global-to-LDS DMA ring moves fewer bytes per CU, but runs the
+// matrix instructions at a lower, power-limited clock and ends up slower
+// over the whole quantize + GEMM step.)
 //
 // Workgroup: 4 waves (2 x 2) over a 256x256 C tile, each wave 128x128 (4x4
 // instruction tiles, 256 accumulator registers), one wave per SIMD.  Per K
