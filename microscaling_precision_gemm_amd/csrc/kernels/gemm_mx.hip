@@ -482,6 +482,292 @@ hipError_t launch_pipe(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
 }
 
 // ---------------------------------------------------------------------------
+// exact MXFP8: the same DMA pipeline feeding the BF16 instruction
+// ---------------------------------------------------------------------------
+// gfx950's FP8 instruction is not exact (see above), so the exact MXFP8 GEMM
+// contracts on v_mfma_f32_32x32x16_bf16: E4M3 * 2^(c-127) is exact in BF16
+// for scale codes c in [3, 246].  The FP8 stages land in LDS exactly as for
+// the native kernel.  For each 32-element K-block b of a step, lane
+// (r = l mod 32, g = l / 32) reads its row's 16-byte chunk 2b + g (the FP8
+// fragment read, conflict-free under the swizzle), converts it with the
+// block's scale (v_cvt_scalef32_pk_bf16_fp8 scales by the exponent of its
+// FP32 operand, i.e. by the E8M0 value) and feeds two BF16 instructions:
+// chunk bytes 0..7, then 8..15.  A and B use the same assignment of K
+// positions to (instruction, lane group, element), so each instruction sums
+// exactly the products of its 16 positions and every block's 32 products are
+// summed.  Conversion costs two VALU instructions per matrix instruction and
+// runs between them; reads and conversions run one half-block ahead.
+//
+// Scale codes 0 (2^-127, an FP32 subnormal the converter does not take as a
+// scale) and 255 (NaN) are not converted correctly here: the launcher follows
+// this kernel with the staged kernel in fix-up mode, which recomputes
+// exactly every output tile whose operand rows hold such a code.
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// 8 BF16 values (element 2k in the low half of word k) from the 8 FP8 codes
+// in w0, w1, scaled by E8M0 code c (1 .. 254).
+__device__ inline u4 conv8(uint32_t w0, uint32_t w1, uint32_t c) {
+  const float X = u2f(c << 23);
+  u4 o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, X, false));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, X, true));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, X, false));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, X, true));
+  return o;
+}
+
+// Register state: raw chunks of two blocks, the converted halves, and the
+// scale dwords (byte b: block b of the step) of the current and next step.
+struct XState {
+  u4 raw[2][8];  // [block parity][A 0..3, B 4..7]
+  u4 lo[8], hi[8];
+  uint32_t sc[8], scn[8];
+};
+
+__device__ inline void read_raw(const uint8_t* __restrict__ L, uint32_t b, uint32_t wm, uint32_t wn,
+                                uint32_t lr, uint32_t lg, u4 (&raw)[8]) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t r = t < 4 ? wm * 128 + t * 32 + lr : kTile + wn * 128 + (t - 4) * 32 + lr;
+    raw[t] = *reinterpret_cast<const u4*>(L + chunk_off(r, 2 * b + lg));
+  }
+}
+
+// half H (0: chunk bytes 0..7, 1: 8..15) of block b (scale byte b)
+template <int H>
+__device__ inline void conv_half(const u4 (&raw)[8], const uint32_t (&sc)[8], uint32_t b, u4 (&out)[8]) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) out[t] = conv8(raw[t][2 * H], raw[t][2 * H + 1], (sc[t] >> (8 * b)) & 0xFFu);
+}
+
+__device__ inline void mfma_bf16_16(const u4 (&f)[8], v16f (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, f[i]),
+                                                          __builtin_bit_cast(v8bf, f[4 + j]), acc[i][j], 0, 0, 0);
+}
+
+constexpr int kSgValu = 0x002;
+
+// Order a region as 16 matrix instructions with V VALU, D LDS-read and M
+// vector-memory instructions spread between them.
+template <int V, int D, int M, int I = 0>
+__device__ inline void spread_x() {
+  if constexpr (I < 16) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    constexpr int v = ((I + 1) * V + 15) / 16 - (I * V + 15) / 16;
+    constexpr int d = ((I + 1) * D + 15) / 16 - (I * D + 15) / 16;
+    constexpr int m = ((I + 1) * M + 15) / 16 - (I * M + 15) / 16;
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(kSgValu, v, 0);
+    if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(kSgDsRead, d, 0);
+    if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(kSgVmem, m, 0);
+    spread_x<V, D, M, I + 1>();
+  }
+}
+
+__device__ inline void load_scales_x(const uint8_t* __restrict__ smem, uint32_t step, uint32_t wm, uint32_t wn,
+                                     uint32_t lr, uint32_t (&s)[8]) {
+  Scales t;
+  load_scales<FMT_MXFP8>(smem, step, wm, wn, lr, t);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s[i] = t.a[0][i];
+    s[4 + i] = t.b[0][i];
+  }
+}
+
+// One K step (4 blocks, 8 half-block windows of 16 instructions):
+//   H0 b0 lo | convert b0 hi              H1 b0 hi | convert b1 lo, read b2
+//   H2 b1 lo | convert b1 hi              H3 b1 hi | convert b2 lo, read b3
+//   wait for this wave's DMAs of stage st+1; barrier
+//   H4 b2 lo | convert b2 hi, DMAs        H5 b2 hi | convert b3 lo, read b0',
+//                                                     scales of st+1
+//   H6 b3 lo | convert b3 hi              H7 b3 hi | convert b0' lo, read b1'
+// (primes: stage st+1).  SWITCH: a next stage exists; DMA: refill the buffer
+// just consumed with stage st+2.
+template <bool SWITCH, bool DMA>
+__device__ inline void exact_step(const PipeCtx& x, uint8_t* __restrict__ smem, uint32_t st, uint32_t wm,
+                                  uint32_t wn, uint32_t lr, uint32_t lg, XState& xs, v16f (&acc)[4][4]) {
+  uint8_t* cur = smem + (st & 1u) * kStageBytes;
+  uint8_t* nxt = smem + ((st + 1u) & 1u) * kStageBytes;
+  constexpr int CV = 40;  // VALU per conversion window (32 conversions + scale bytes)
+  // H0
+  conv_half<1>(xs.raw[0], xs.sc, 0, xs.hi);
+  mfma_bf16_16(xs.lo, acc);
+  spread_x<CV, 0, 0>();
+  sched_fence();
+  // H1
+  conv_half<0>(xs.raw[1], xs.sc, 1, xs.lo);
+  read_raw(cur, 2, wm, wn, lr, lg, xs.raw[0]);
+  mfma_bf16_16(xs.hi, acc);
+  spread_x<CV, 8, 0>();
+  sched_fence();
+  // H2
+  conv_half<1>(xs.raw[1], xs.sc, 1, xs.hi);
+  mfma_bf16_16(xs.lo, acc);
+  spread_x<CV, 0, 0>();
+  sched_fence();
+  // H3
+  conv_half<0>(xs.raw[0], xs.sc, 2, xs.lo);
+  read_raw(cur, 3, wm, wn, lr, lg, xs.raw[1]);
+  mfma_bf16_16(xs.hi, acc);
+  spread_x<CV, 8, 0>();
+  sched_fence();
+  if constexpr (SWITCH) {
+    wait_vmcnt<0>();
+    dma_barrier();
+    sched_fence();
+  }
+  // H4
+  if constexpr (DMA) {
+    issue_stage<FMT_MXFP8>(x, st + 2, cur);
+    const uint32_t q = st / PipeCfg<FMT_MXFP8>::kPeriod + 2;
+    issue_scales(x, smem, q, q % kScaleBufs, st & 1u);
+  }
+  conv_half<1>(xs.raw[0], xs.sc, 2, xs.hi);
+  mfma_bf16_16(xs.lo, acc);
+  spread_x<CV, 0, DMA ? 17 : 0>();
+  sched_fence();
+  // H5
+  conv_half<0>(xs.raw[1], xs.sc, 3, xs.lo);
+  if constexpr (SWITCH) {
+    read_raw(nxt, 0, wm, wn, lr, lg, xs.raw[0]);
+    load_scales_x(smem, st + 1, wm, wn, lr, xs.scn);
+  }
+  mfma_bf16_16(xs.hi, acc);
+  spread_x<CV, SWITCH ? 12 : 0, 0>();
+  sched_fence();
+  // H6
+  conv_half<1>(xs.raw[1], xs.sc, 3, xs.hi);
+  mfma_bf16_16(xs.lo, acc);
+  spread_x<CV, 0, 0>();
+  sched_fence();
+  // H7
+  if constexpr (SWITCH) {
+    conv_half<0>(xs.raw[0], xs.scn, 0, xs.lo);
+    read_raw(nxt, 1, wm, wn, lr, lg, xs.raw[1]);
+  }
+  mfma_bf16_16(xs.hi, acc);
+  spread_x<SWITCH ? CV : 0, SWITCH ? 8 : 0, 0>();
+  sched_fence();
+  if constexpr (SWITCH) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) xs.sc[t] = xs.scn[t];
+  }
+}
+
+template <int CDT>
+__device__ inline void exact_body(const PipeCtx& x, uint8_t* __restrict__ smem, uint32_t steps, uint32_t wm,
+                                  uint32_t wn, uint32_t lr, uint32_t lg, uint32_t wid, uint32_t lane,
+                                  void* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t m0,
+                                  int64_t n0, uint32_t vec) {
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  XState xs;
+  load_scales_x(smem, 0, wm, wn, lr, xs.sc);
+  read_raw(smem, 0, wm, wn, lr, lg, xs.raw[0]);
+  read_raw(smem, 1, wm, wn, lr, lg, xs.raw[1]);
+  conv_half<0>(xs.raw[0], xs.sc, 0, xs.lo);
+  sched_fence();
+  uint32_t st = 0;
+  for (; st + 2 < steps; ++st) exact_step<true, true>(x, smem, st, wm, wn, lr, lg, xs, acc);
+  if (st + 1 < steps) {
+    exact_step<true, false>(x, smem, st, wm, wn, lr, lg, xs, acc);
+    ++st;
+  }
+  exact_step<false, false>(x, smem, st, wm, wn, lr, lg, xs, acc);
+  dma_barrier();
+  store_tile<CDT>(smem, acc, C, ldc, M, N, m0 + wm * 128, n0 + wn * 128, vec != 0, wid, lane);
+}
+
+template <int CDT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx8_exact(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, void* __restrict__ C,
+    int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t vec) {
+  using PC = PipeCfg<FMT_MXFP8>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint32_t tmi, tni;
+  tile_of(blockIdx.x, tiles_m, tiles_n, &tmi, &tni);
+  const int64_t m0 = (int64_t)tmi * kTile, n0 = (int64_t)tni * kTile;
+  const uint32_t t = threadIdx.x;
+  const uint32_t lane = t & 63u, wid = t >> 6;
+  const uint32_t wm = wid >> 1, wn = wid & 1u;
+  const int64_t rowbytes = K;
+  const int64_t kblocks = K / 32;
+  const uint32_t steps = (uint32_t)(K / PC::kKElems);
+
+  PipeCtx x;
+  x.wid = __builtin_amdgcn_readfirstlane(wid);
+  x.nper = steps / PC::kPeriod;
+  const bool waveA = wid < 2;
+  x.cbase = waveA ? A : B;
+  const int64_t lim = waveA ? M : N;
+  const int64_t row0 = waveA ? m0 : n0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t r = 8u * (16u * wid + i) + (lane >> 3);
+    const uint32_t c = (lane & 7u) ^ swz(r);
+    int64_t grow = row0 + (r & (kTile - 1));
+    grow = grow < lim ? grow : lim - 1;
+    x.coff[i] = (uint32_t)(grow * rowbytes) + 16u * c;
+  }
+  x.sA = SA;
+  x.sB = SB;
+  {
+    int64_t ga = m0 + 64 * wid + lane, gb = n0 + 64 * wid + lane;
+    ga = ga < M ? ga : M - 1;
+    gb = gb < N ? gb : N - 1;
+    x.soffA = (uint32_t)(ga * kblocks);
+    x.soffB = (uint32_t)(gb * kblocks);
+  }
+  issue_stage<FMT_MXFP8>(x, 0, smem);
+  issue_scales(x, smem, 0, 0, 0);
+  issue_scales(x, smem, 0, 0, 1);
+  issue_scales(x, smem, 1, 1, 0);
+  issue_scales(x, smem, 1, 1, 1);
+  if (steps > 1) issue_stage<FMT_MXFP8>(x, 1, smem + kStageBytes);
+  if (steps > 1) {
+    wait_vmcnt<16>();  // stage 0 and the first two scale periods
+  } else {
+    wait_vmcnt<0>();
+  }
+  dma_barrier();
+  exact_body<CDT>(x, smem, steps, wm, wn, lane & 31u, lane >> 5, wid, lane, C, ldc, M, N, m0, n0, vec);
+}
+
+template <int CDT>
+hipError_t launch_exact(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
+                        int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
+  const uint32_t tm = (uint32_t)((M + kTile - 1) / kTile), tn = (uint32_t)((N + kTile - 1) / kTile);
+  const size_t smem = (size_t)kSmemBytes;
+  auto kern = k_gemm_mx8_exact<CDT>;
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_done.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  const int64_t eb = CDT == DT_F32 ? 4 : 2;
+  const uint32_t vec = ((reinterpret_cast<uintptr_t>(C) & 15u) == 0 && (ldc * eb) % 16 == 0) ? 1u : 0u;
+  hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(256), smem, s, a, sa, b, sb, M, N, K, C, ldc, tm, tn, vec);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // simple kernel: register-staged double buffer, 128x128 tiles, any K % 32
 // ---------------------------------------------------------------------------
 constexpr int kPitchS = 80;  // LDS bytes per row: 64 code bytes, 4 scale bytes, pad
@@ -624,6 +910,19 @@ hipError_t run(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint
 }
 
 }  // namespace
+
+bool gemm_mxfp8_exact_pipe_fits(int64_t M, int64_t N, int64_t K) {
+  const bool fits32 = (M > N ? M : N) * K < ((int64_t)1 << 32) - 4096;
+  return fits32 && K > 0 && (K % 512 == 0) && M * N >= (int64_t)kTile * kTile * 128;
+}
+
+hipError_t launch_gemm_mxfp8_exact_pipe(const uint8_t* a_codes, const uint8_t* a_scales,
+                                        const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                        int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
+                                        hipStream_t s) {
+  return cdt == DT_F32 ? launch_exact<DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s)
+                       : launch_exact<DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
+}
 
 hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,

@@ -40,6 +40,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 64;                // K elements per step
 constexpr int kPitch = kBK * 2 + 16;   // LDS bytes per row
@@ -100,7 +101,18 @@ __device__ inline void convert_store(const Unit<SRC>& u, uint8_t* dst) {
     *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
 }
 
-template <int SRC, int CDT, int BM, int BN, bool GATHER>
+// nonzero when some byte of w is 0x00 or 0xFF
+__device__ inline uint32_t special_bytes(uint32_t w) {
+  const uint32_t z = (w - 0x01010101u) & ~w & 0x80808080u;
+  const uint32_t nw = ~w;
+  return z | ((nw - 0x01010101u) & ~nw & 0x80808080u);
+}
+
+// FIXUP (MXFP8, K % 512 == 0): the workgroup first scans the scale rows of
+// its tile and computes the tile only if one holds a code 0 or 255 -- the
+// codes the pipelined exact MXFP8 kernel does not convert; the output of
+// that kernel for such tiles is overwritten.
+template <int SRC, int CDT, int BM, int BN, bool GATHER, bool FIXUP = false>
 __global__ __launch_bounds__(256) void k_gemm_staged(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const float* __restrict__ a_ts,
     const int32_t* __restrict__ row_index, int64_t R, const uint8_t* __restrict__ B,
@@ -144,6 +156,25 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
   if (g < 0) return;  // surplus workgroup (uniform across the block)
 
   const uint32_t t = threadIdx.x;
+  if constexpr (FIXUP) {
+    static_assert(SRC == FMT_MXFP8 && BM == 256 && BN == 256, "fix-up pass of the exact MXFP8 GEMM");
+    __shared__ uint32_t found[4];
+    const int64_t kb = K / 32;  // scale bytes per row, a multiple of 16
+    uint32_t sp = 0;
+    const int64_t ra = g_lo + t, rb = n0 + t;
+    const u4* pa = ra < g_hi ? reinterpret_cast<const u4*>(SA + ra * kb) : nullptr;
+    const u4* pb = rb < N ? reinterpret_cast<const u4*>(SB + rb * kb) : nullptr;
+    for (int64_t q = 0; q < kb / 16; ++q) {
+      const u4 va = pa ? pa[q] : u4{1u, 1u, 1u, 1u};
+      const u4 vb = pb ? pb[q] : u4{1u, 1u, 1u, 1u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sp |= special_bytes(va[e]) | special_bytes(vb[e]);
+    }
+    const bool wave_found = __builtin_amdgcn_ballot_w64(sp != 0u) != 0;
+    if ((t & 63u) == 0) found[t >> 6] = wave_found ? 1u : 0u;
+    __syncthreads();
+    if ((found[0] | found[1] | found[2] | found[3]) == 0u) return;  // uniform
+  }
   const uint32_t lane = t & 63u, wid = t >> 6;
   const uint32_t wm = wid >> 1, wn = wid & 1u;
   const int64_t m0 = g_lo;
@@ -272,13 +303,13 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
     }
 }
 
-template <int SRC, int CDT, int BM, int BN, bool GATHER>
+template <int SRC, int CDT, int BM, int BN, bool GATHER, bool FIXUP = false>
 hipError_t run(const uint8_t* a, const uint8_t* sa, const float* ats, const int32_t* ri, int64_t R,
                const uint8_t* b, const uint8_t* sb, const float* bts, int32_t groups,
                const int64_t* off, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
   const uint32_t tn = (uint32_t)((N + BN - 1) / BN);
   const uint32_t tmb = (uint32_t)((R + BM - 1) / BM + (off ? groups : 0));
-  hipLaunchKernelGGL((k_gemm_staged<SRC, CDT, BM, BN, GATHER>), dim3(tn * tmb), dim3(256), 0, s,
+  hipLaunchKernelGGL((k_gemm_staged<SRC, CDT, BM, BN, GATHER, FIXUP>), dim3(tn * tmb), dim3(256), 0, s,
                      a, sa, ats, ri, R, b, sb, bts, groups, off, N, K, C, ldc, tn, tmb);
   return hipGetLastError();
 }
@@ -313,6 +344,16 @@ hipError_t launch_gemm_mxfp8_exact(const uint8_t* a_codes, const uint8_t* a_scal
                                    int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
                                    hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
+  // large shapes: raw FP8 stages through LDS, converted after the fragment
+  // reads (gemm_mx.hip)
+  if (gemm_mxfp8_exact_pipe_fits(M, N, K)) {
+    const hipError_t e = launch_gemm_mxfp8_exact_pipe(a_codes, a_scales, b_codes, b_scales, M, N, K, C, cdt, ldc, s);
+    if (e != hipSuccess) return e;
+    // tiles whose operands hold scale codes 0 or 255, recomputed here
+    if (cdt == DT_F32)
+      return run<FMT_MXFP8, DT_F32, 256, 256, false, true>(a_codes, a_scales, nullptr, nullptr, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
+    return run<FMT_MXFP8, DT_BF16, 256, 256, false, true>(a_codes, a_scales, nullptr, nullptr, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
+  }
   if (cdt == DT_F32)
     return run_sized<FMT_MXFP8, DT_F32, false>(a_codes, a_scales, nullptr, nullptr, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
   return run_sized<FMT_MXFP8, DT_BF16, false>(a_codes, a_scales, nullptr, nullptr, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);

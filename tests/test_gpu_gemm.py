@@ -140,12 +140,14 @@ def test_mxfp8_native_fp8_path_within_hardware_bound(shape):
     check_gemm(C.cpu().numpy(), Chat, tol * 100.0, False, f"native fp8 {shape}")
 
 
-@pytest.mark.parametrize("fmt,flags,cdt", [(2, 0, "bf16"), (2, 0, "f32"), (1, 1, "bf16"), (1, 1, "f32")])
+@pytest.mark.parametrize("fmt,flags,cdt", [(2, 0, "bf16"), (2, 0, "f32"), (1, 1, "bf16"), (1, 1, "f32"),
+                                            (1, 0, "bf16"), (1, 0, "f32")])
 def test_pipelined_ragged_tiles_and_unaligned_ldc(fmt, flags, cdt):
-    """Shapes large enough for the 256x256 pipelined kernel, with M and N not
+    """Shapes large enough for the 256x256 pipelined kernels, with M and N not
     multiples of the tile and a C row pitch that is not 16-byte aligned (the
-    epilogue then falls back to element stores).  MXFP8 here runs the native
-    FP8 path (flags=1), whose bound is 100x the exact one."""
+    epilogue then falls back to element stores).  MXFP8 runs the exact path
+    (flags=0: FP8 stages converted to BF16 for the BF16 instruction) and the
+    native FP8 path (flags=1), whose bound is 100x the exact one."""
     M, N, K = 2900, 3000, 512
     qa, qb = _operands(fmt, M, N, K, 17)
     dt = torch.float32 if cdt == "f32" else torch.bfloat16
@@ -160,3 +162,34 @@ def test_pipelined_ragged_tiles_and_unaligned_ldc(fmt, flags, cdt):
     torch.cuda.synchronize()
     check_gemm(C2.float().cpu().numpy(), Chat, tol * (100.0 if flags else 1.0), cdt == "bf16",
                f"pipelined aligned fmt {fmt} {cdt}")
+
+
+@pytest.mark.parametrize("cdt", ["bf16", "f32"])
+def test_exact_mxfp8_special_scale_codes(cdt):
+    """At a size that takes the pipelined exact MXFP8 kernel, E8M0 scale codes
+    0 (2^-127, on nonzero codes) and 255 (NaN) in a few blocks of A and B:
+    the tiles holding them are recomputed by the fix-up pass, so NaN reaches
+    exactly the rows and columns the oracle gives, and everything else stays
+    within the bound."""
+    M, N, K = 2048, 4096, 512
+    qa, qb = _operands(1, M, N, K, 29)
+    sa, sb = qa[1].copy(), qb[1].copy()
+    sa[5, 3] = 0
+    sa[700, 10] = 255
+    sb[1234, 7] = 0
+    sb[3000, 2] = 255
+    qa = (qa[0], sa)
+    qb = (qb[0], sb)
+    dt = torch.float32 if cdt == "f32" else torch.bfloat16
+    C = torch.full((M, N), 7.0, dtype=dt, device=dev())
+    mx.mx_gemm(upload(1, *qa), upload(1, *qb), C)
+    torch.cuda.synchronize()
+    Chat, tol = _oracle_gemm(1, qa, qb, M, N, K)
+    got = C.float().cpu().numpy()
+    nan_want = np.isnan(Chat)
+    assert nan_want[700].all() and nan_want[:, 3000].all() and nan_want.sum() == N + M - 1
+    assert np.isnan(got[nan_want]).all(), "NaN scale blocks must give NaN outputs"
+    keep = ~nan_want
+    assert not np.isnan(got[keep]).any()
+    check_gemm(np.where(keep, got, 0.0), np.where(keep, Chat, 0.0), np.where(keep, tol, 1.0),
+               cdt == "bf16", f"exact mxfp8 special scales {cdt}")
