@@ -225,7 +225,7 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
   switch (A->fmt) {
     case MX_NVFP4:
       // one group covering all rows (no offsets array needed)
-      return hip_status(mxk::launch_gemm_nvfp4(ac, A->scales, A->tensor_scale, nullptr, M, bc,
+      return hip_status(mxk::launch_gemm_nvfp4(ac, A->scales, A->tensor_scale, nullptr, M, M, bc,
                                                B->scales, B->tensor_scale, 1, nullptr, N, K, C,
                                                cdt, ldc, s));
     case MX_MXFP8_E4M3:
@@ -265,7 +265,7 @@ mx_status mx_gemm_grouped(const mx_tensor* A, const int32_t* row_index, int64_t 
   if (st != MX_OK) return st;
   if (routed_rows * N == 0) return MX_OK;
   return hip_status(mxk::launch_gemm_nvfp4(
-      static_cast<const uint8_t*>(A->codes), A->scales, A->tensor_scale, row_index, routed_rows,
+      static_cast<const uint8_t*>(A->codes), A->scales, A->tensor_scale, row_index, A->rows, routed_rows,
       static_cast<const uint8_t*>(B->codes), B->scales, B->tensor_scale, num_groups,
       group_offsets, N, K, C, cdt, ldc, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -115,7 +115,7 @@ __device__ inline uint32_t special_bytes(uint32_t w) {
 template <int SRC, int CDT, int BM, int BN, bool GATHER, bool FIXUP = false>
 __global__ __launch_bounds__(256) void k_gemm_staged(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const float* __restrict__ a_ts,
-    const int32_t* __restrict__ row_index, int64_t R, const uint8_t* __restrict__ B,
+    const int32_t* __restrict__ row_index, int64_t a_rows, int64_t R, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, const float* __restrict__ b_ts, int32_t groups,
     const int64_t* __restrict__ offsets, int64_t N, int64_t K, void* __restrict__ C, int64_t ldc,
     uint32_t tiles_n, uint32_t tiles_m_bound) {
@@ -199,7 +199,11 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
     if (r < (uint32_t)BM) {
       const int64_t rr = m0 + r;
       if (rr < g_hi) {
-        const int64_t src_row = GATHER ? (int64_t)row_index[rr] : rr;
+        int64_t src_row = rr;
+        if constexpr (GATHER) {  // entries outside [0, a_rows) clamped
+          src_row = row_index[rr];
+          src_row = src_row < 0 ? 0 : (src_row < a_rows ? src_row : a_rows - 1);
+        }
         csrc[j] = A + src_row * rowbytes + h * (SRC == FMT_NVFP4 ? 16 : 32);
         ssrc[j] = SA + src_row * sblocks + h * (SRC == FMT_NVFP4 ? 2 : 1);
       }
@@ -304,36 +308,41 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
 }
 
 template <int SRC, int CDT, int BM, int BN, bool GATHER, bool FIXUP = false>
-hipError_t run(const uint8_t* a, const uint8_t* sa, const float* ats, const int32_t* ri, int64_t R,
+hipError_t run(const uint8_t* a, const uint8_t* sa, const float* ats, const int32_t* ri, int64_t a_rows, int64_t R,
                const uint8_t* b, const uint8_t* sb, const float* bts, int32_t groups,
                const int64_t* off, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
   const uint32_t tn = (uint32_t)((N + BN - 1) / BN);
   const uint32_t tmb = (uint32_t)((R + BM - 1) / BM + (off ? groups : 0));
   hipLaunchKernelGGL((k_gemm_staged<SRC, CDT, BM, BN, GATHER, FIXUP>), dim3(tn * tmb), dim3(256), 0, s,
-                     a, sa, ats, ri, R, b, sb, bts, groups, off, N, K, C, ldc, tn, tmb);
+                     a, sa, ats, ri, a_rows, R, b, sb, bts, groups, off, N, K, C, ldc, tn, tmb);
   return hipGetLastError();
 }
 
 template <int SRC, int CDT, bool GATHER>
 hipError_t run_sized(const uint8_t* a, const uint8_t* sa, const float* ats, const int32_t* ri,
-                     int64_t R, const uint8_t* b, const uint8_t* sb, const float* bts,
+                     int64_t a_rows, int64_t R, const uint8_t* b, const uint8_t* sb, const float* bts,
                      int32_t groups, const int64_t* off, int64_t N, int64_t K, void* C,
                      int64_t ldc, hipStream_t s) {
   if (R * N >= (int64_t)256 * 256 * 192)
-    return run<SRC, CDT, 256, 256, GATHER>(a, sa, ats, ri, R, b, sb, bts, groups, off, N, K, C, ldc, s);
-  return run<SRC, CDT, 128, 128, GATHER>(a, sa, ats, ri, R, b, sb, bts, groups, off, N, K, C, ldc, s);
+    return run<SRC, CDT, 256, 256, GATHER>(a, sa, ats, ri, a_rows, R, b, sb, bts, groups, off, N, K, C, ldc, s);
+  return run<SRC, CDT, 128, 128, GATHER>(a, sa, ats, ri, a_rows, R, b, sb, bts, groups, off, N, K, C, ldc, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
-                             const int32_t* row_index, int64_t routed_rows,
+                             const int32_t* row_index, int64_t a_rows, int64_t routed_rows,
                              const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
                              int32_t groups, const int64_t* offsets, int64_t N, int64_t K,
                              void* C, int cdt, int64_t ldc, hipStream_t s) {
   if (routed_rows == 0 || N == 0) return hipSuccess;
+  // large shapes: FP4 stages through LDS, converted after the fragment
+  // reads (gemm_nvpipe.hip)
+  if (gemm_nvfp4_pipe_fits(a_rows, routed_rows, N, K))
+    return launch_gemm_nvfp4_pipe(a_codes, a_scales, a_ts, row_index, a_rows, routed_rows, b_codes, b_scales,
+                                  b_ts, groups, offsets, N, K, C, cdt, ldc, s);
 #define MXK_NV(D, G) \
-  run_sized<FMT_NVFP4, D, G>(a_codes, a_scales, a_ts, row_index, routed_rows, b_codes, b_scales, b_ts, groups, offsets, N, K, C, ldc, s)
+  run_sized<FMT_NVFP4, D, G>(a_codes, a_scales, a_ts, row_index, a_rows, routed_rows, b_codes, b_scales, b_ts, groups, offsets, N, K, C, ldc, s)
   if (row_index) return cdt == DT_F32 ? MXK_NV(DT_F32, true) : MXK_NV(DT_BF16, true);
   return cdt == DT_F32 ? MXK_NV(DT_F32, false) : MXK_NV(DT_BF16, false);
 #undef MXK_NV
@@ -351,12 +360,12 @@ hipError_t launch_gemm_mxfp8_exact(const uint8_t* a_codes, const uint8_t* a_scal
     if (e != hipSuccess) return e;
     // tiles whose operands hold scale codes 0 or 255, recomputed here
     if (cdt == DT_F32)
-      return run<FMT_MXFP8, DT_F32, 256, 256, false, true>(a_codes, a_scales, nullptr, nullptr, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
-    return run<FMT_MXFP8, DT_BF16, 256, 256, false, true>(a_codes, a_scales, nullptr, nullptr, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
+      return run<FMT_MXFP8, DT_F32, 256, 256, false, true>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
+    return run<FMT_MXFP8, DT_BF16, 256, 256, false, true>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
   }
   if (cdt == DT_F32)
-    return run_sized<FMT_MXFP8, DT_F32, false>(a_codes, a_scales, nullptr, nullptr, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
-  return run_sized<FMT_MXFP8, DT_BF16, false>(a_codes, a_scales, nullptr, nullptr, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
+    return run_sized<FMT_MXFP8, DT_F32, false>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
+  return run_sized<FMT_MXFP8, DT_BF16, false>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
 }
 
 }  // namespace mxk

@@ -59,10 +59,19 @@ hipError_t launch_gemm_mxfp8_exact(const uint8_t* a_codes, const uint8_t* a_scal
                                    const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                    int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
                                    hipStream_t s);
+// a_rows: rows of the A source (row_index entries are clamped to it)
 hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
-                             const int32_t* row_index, int64_t routed_rows,
+                             const int32_t* row_index, int64_t a_rows, int64_t routed_rows,
                              const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
                              int32_t groups, const int64_t* offsets, int64_t N, int64_t K,
                              void* C, int cdt, int64_t ldc, hipStream_t s);
+
+// NVFP4 on the DMA pipeline (FP16 instruction); shapes it takes
+bool gemm_nvfp4_pipe_fits(int64_t a_rows, int64_t R, int64_t N, int64_t K);
+hipError_t launch_gemm_nvfp4_pipe(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                                  const int32_t* row_index, int64_t a_rows, int64_t routed_rows,
+                                  const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts,
+                                  int32_t groups, const int64_t* offsets, int64_t N, int64_t K, void* C,
+                                  int cdt, int64_t ldc, hipStream_t s);
 
 }  // namespace mxk

@@ -141,13 +141,14 @@ def test_mxfp8_native_fp8_path_within_hardware_bound(shape):
 
 
 @pytest.mark.parametrize("fmt,flags,cdt", [(2, 0, "bf16"), (2, 0, "f32"), (1, 1, "bf16"), (1, 1, "f32"),
-                                            (1, 0, "bf16"), (1, 0, "f32")])
+                                            (1, 0, "bf16"), (1, 0, "f32"), (3, 0, "bf16"), (3, 0, "f32")])
 def test_pipelined_ragged_tiles_and_unaligned_ldc(fmt, flags, cdt):
     """Shapes large enough for the 256x256 pipelined kernels, with M and N not
     multiples of the tile and a C row pitch that is not 16-byte aligned (the
     epilogue then falls back to element stores).  MXFP8 runs the exact path
     (flags=0: FP8 stages converted to BF16 for the BF16 instruction) and the
-    native FP8 path (flags=1), whose bound is 100x the exact one."""
+    native FP8 path (flags=1), whose bound is 100x the exact one; NVFP4 its
+    FP4 stages converted to FP16 with the E4M3 block scales applied."""
     M, N, K = 2900, 3000, 512
     qa, qb = _operands(fmt, M, N, K, 17)
     dt = torch.float32 if cdt == "f32" else torch.bfloat16
@@ -193,3 +194,43 @@ def test_exact_mxfp8_special_scale_codes(cdt):
     assert not np.isnan(got[keep]).any()
     check_gemm(np.where(keep, got, 0.0), np.where(keep, Chat, 0.0), np.where(keep, tol, 1.0),
                cdt == "bf16", f"exact mxfp8 special scales {cdt}")
+
+
+@pytest.mark.parametrize("gather", [False, True])
+@pytest.mark.parametrize("cdt", ["bf16", "f32"])
+def test_grouped_nvfp4_pipelined(gather, cdt):
+    """Grouped NVFP4 at a size that takes the pipelined kernel (R x N >= 2^22,
+    K a multiple of 256; K = 768 runs the loop once and both peeled steps),
+    with an empty group and groups that do not fill their last row tile."""
+    K, N = 768, 2048
+    offsets = np.array([0, 700, 700, 1930, 2048], np.int64)
+    E = offsets.size - 1
+    R = int(offsets[-1])
+    tokens = 1500
+    X = W.normal_bf16(tokens, K, 1.0, 6, 56)
+    rng = np.random.default_rng(6)
+    row_index = rng.integers(0, tokens, R).astype(np.int32)
+    qw = [oracle.quantize(W.normal_bf16(N, K, 0.05, 6, 80 + e), 3, 0) for e in range(E)]
+    if gather:
+        qx = oracle.quantize(X, 3, 0)
+        ri = torch.from_numpy(row_index).to(dev())
+    else:
+        qx = oracle.quantize(np.ascontiguousarray(X[row_index]), 3, 0)
+        ri = None
+    A = upload(3, *qx)
+    B = upload(3, np.concatenate([q[0] for q in qw]), np.concatenate([q[1] for q in qw]),
+               np.array([q[2] for q in qw], np.float32))
+    dt = torch.float32 if cdt == "f32" else torch.bfloat16
+    C = torch.full((R, N), float("nan"), dtype=dt, device=dev())
+    mx.mx_gemm_grouped(A, ri, R, B, E, torch.from_numpy(offsets).to(dev()), C)
+    torch.cuda.synchronize()
+    Cg = C.float().cpu().numpy()
+    Ad = oracle.dequantize_f64(3, qx[0], qx[1], qx[0].shape[0], K)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        rows = row_index[lo:hi] if gather else np.arange(lo, hi)
+        Bd = oracle.dequantize_f64(3, qw[e][0], qw[e][1], N, K)
+        Chat, tol = oracle.gemm(Ad[rows], Bd, float(np.float64(qx[2]) * np.float64(qw[e][2])))
+        check_gemm(Cg[lo:hi], Chat, tol, cdt == "bf16", f"pipelined expert {e} gather={gather}")
