@@ -232,7 +232,8 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
  * group_offsets (device, int64 [num_groups + 1], non-decreasing, first 0, last
  * = number of routed rows R) assigns output rows [off[e], off[e+1]) to expert
  * e.  A row source: if row_index is non-NULL (device int32 [R]), routed row r
- * reads A row row_index[r] (A is [tokens, K]); otherwise A has R rows.
+ * reads A row row_index[r] (A is [tokens, K]; entries outside [0, tokens) are
+ * clamped into it); otherwise A has R rows.
  * C is [R, N] (pitch ldc).  C[r, :] = A[src(r)] * B_e^T * S_A * S_B[e].
  * Requirements: A and B NVFP4, K % 32 == 0, num_groups >= 1, `routed_rows`
  * (host) = R, B->rows % num_groups == 0. */

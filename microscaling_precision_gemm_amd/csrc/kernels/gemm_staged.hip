@@ -164,11 +164,19 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
     const int64_t ra = g_lo + t, rb = n0 + t;
     const u4* pa = ra < g_hi ? reinterpret_cast<const u4*>(SA + ra * kb) : nullptr;
     const u4* pb = rb < N ? reinterpret_cast<const u4*>(SB + rb * kb) : nullptr;
-    for (int64_t q = 0; q < kb / 16; ++q) {
-      const u4 va = pa ? pa[q] : u4{1u, 1u, 1u, 1u};
-      const u4 vb = pb ? pb[q] : u4{1u, 1u, 1u, 1u};
+    const int64_t n16 = kb / 16;
+    for (int64_t q0 = 0; q0 < n16; q0 += 8) {  // 16 loads in flight per lane
+      u4 v[16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sp |= special_bytes(va[e]) | special_bytes(vb[e]);
+      for (int u = 0; u < 8; ++u) {
+        const int64_t q = q0 + u < n16 ? q0 + u : n16 - 1;
+        v[u] = pa ? pa[q] : u4{1u, 1u, 1u, 1u};
+        v[8 + u] = pb ? pb[q] : u4{1u, 1u, 1u, 1u};
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sp |= special_bytes(v[u][e]);
     }
     const bool wave_found = __builtin_amdgcn_ballot_w64(sp != 0u) != 0;
     if ((t & 63u) == 0) found[t >> 6] = wave_found ? 1u : 0u;
