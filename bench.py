@@ -249,7 +249,7 @@ def detail(torch, mx, W, args):
     def randn(r, c, std=1.0):
         return (torch.randn(r, c, generator=g, device="cuda", dtype=torch.float32) * std).to(torch.bfloat16)
 
-    # MXFP8 4096^3 GEMM: exact (BF16-staged) and the native FP8 instruction
+    # MXFP8 4096^3 GEMM: exact (FP8 converted to BF16) and the native FP8 instruction
     M = N = K = 4096
     a, b = randn(M, K), randn(N, K, 0.02)
     qa, qb = mx.empty(1, M, K), mx.empty(1, N, K)

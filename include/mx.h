@@ -207,10 +207,12 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
  * dtype cdt (FP32, or BF16 rounded to nearest even).  The result is the
  * FP32-accumulated sum of the exact products of the decoded operands:
  *   MXFP4  scaled FP4 matrix instructions (E8M0 scales inside the instruction);
- *   MXFP8  E4M3 * 2^(c-127) staged as exact BF16 (exact for scale codes c in
- *          [3, 246]), BF16 matrix instructions;
- *   NVFP4  e2m1 * e4m3 staged as exact BF16, BF16 matrix instructions, the
- *          FP32 result multiplied by S_A * S_B.
+ *   MXFP8  E4M3 * 2^(c-127) converted to exact BF16 (exact for scale codes c
+ *          in [3, 246]; codes 0 and 255 give 2^-127 and NaN), BF16 matrix
+ *          instructions;
+ *   NVFP4  e2m1 * e4m3 converted to exact FP16, FP16 matrix instructions
+ *          (BF16 for shapes too small for the pipelined kernel), the FP32
+ *          result multiplied by S_A * S_B.
  * Requirements: A->fmt == B->fmt; A->cols == B->cols == K; K % 32 == 0. */
 mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,
                   mx_stream stream);
