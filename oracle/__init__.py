@@ -23,6 +23,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 MXFP8, MXFP4, NVFP4 = 1, 2, 3
 RNE, SR = 0, 1
+# quantizer variants (bits)
+V_CEIL, V_FOUR6, V_2D = 1, 2, 4
 IN_BF16, IN_F32 = 0, 1
 
 _lib = None
@@ -66,9 +68,9 @@ def lib():
         "mxo_rand16": (u32, [u64, u64, u64]),
         "mxo_rht_signs": (u32, [u64]),
         "mxo_rht16": (None, [vp, ci, c_f32p, i64, i64, u32, ci]),
-        "mxo_quantize_mx": (ci, [vp, ci, i64, i64, i64, ci, ci, u64, u64, ci, u32, c_u8p, c_u8p]),
+        "mxo_quantize_mx": (ci, [vp, ci, i64, i64, i64, ci, ci, u64, u64, ci, u32, ci, c_u8p, c_u8p]),
         "mxo_tensor_amax": (ctypes.c_float, [vp, ci, i64, i64, i64, ci, u32]),
-        "mxo_quantize_nvfp4": (ci, [vp, ci, i64, i64, i64, ci, u64, u64, ci, u32, c_f32p,
+        "mxo_quantize_nvfp4": (ci, [vp, ci, i64, i64, i64, ci, u64, u64, ci, u32, ci, c_f32p,
                                     c_u8p, c_u8p, c_f32p]),
         "mxo_dequantize": (None, [ci, c_u8p, c_u8p, c_f32p, i64, i64, c_f32p]),
         "mxo_dequantize_f64": (None, [ci, c_u8p, c_u8p, i64, i64, c_f64p]),
@@ -182,8 +184,14 @@ def tensor_amax(x: np.ndarray, rht: bool = False, sign_mask: int = 0) -> float:
 
 
 def quantize(x: np.ndarray, fmt: int, rnd: int = RNE, seed: int = 0, counter: int = 0,
-             rht: bool = False, sign_mask: int = 0, amax: float | None = None):
+             rht: bool = False, sign_mask: int = 0, amax: float | None = None,
+             variant: int = 0):
     """Quantize a [rows, cols] matrix along cols.
+
+    ``variant`` is a set of V_* bits: V_CEIL (MX formats: the smallest shared
+    scale that saturates no element), V_FOUR6 (NVFP4, round-to-nearest: each
+    block's maximum mapped to 4 or 6, whichever decodes with less error),
+    V_2D (NVFP4: one block scale per 16 x 16 tile).
 
     Returns (codes, scales, tensor_scale): codes uint8 [rows, cols] (MXFP8) or
     [rows, cols/2] (FP4, element 2j in the low nibble); scales uint8
@@ -199,7 +207,8 @@ def quantize(x: np.ndarray, fmt: int, rnd: int = RNE, seed: int = 0, counter: in
         ts = np.zeros(1, np.float32)
         am = None if amax is None else np.array([amax], np.float32)
         rc = lib().mxo_quantize_nvfp4(_vptr(x), dt, cols, rows, cols, rnd, seed, counter, int(rht),
-                                      sign_mask, None if am is None else _ptr(am, ctypes.c_float),
+                                      sign_mask, variant,
+                                      None if am is None else _ptr(am, ctypes.c_float),
                                       _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8),
                                       _ptr(ts, ctypes.c_float))
         if rc:
@@ -207,7 +216,8 @@ def quantize(x: np.ndarray, fmt: int, rnd: int = RNE, seed: int = 0, counter: in
         return codes, scales, float(ts[0])
     scales = np.zeros((rows, cols // 32), np.uint8)
     rc = lib().mxo_quantize_mx(_vptr(x), dt, cols, rows, cols, fmt, rnd, seed, counter, int(rht),
-                               sign_mask, _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8))
+                               sign_mask, variant, _ptr(codes, ctypes.c_uint8),
+                               _ptr(scales, ctypes.c_uint8))
     if rc:
         raise ValueError("oracle rejected the shape")
     return codes, scales, None

@@ -45,6 +45,11 @@
 #define MXO_RNE 0
 #define MXO_SR 1
 
+/* Quantizer variants (bits of the `variant` argument). */
+#define MXO_V_CEIL 1   /* MX: smallest shared scale that saturates no element */
+#define MXO_V_FOUR6 2  /* NVFP4: per block, map the block max to 4 or to 6 */
+#define MXO_V_2D 4     /* NVFP4: one block scale per 16 x 16 tile */
+
 /* ------------------------------------------------------------------------ */
 /* Element and scale decoders, written from the bit-level definitions.       */
 /* ------------------------------------------------------------------------ */
@@ -334,9 +339,14 @@ void mxo_rht16(const void* x, int xdt, float* y, int64_t rows, int64_t cols, uin
 /* 2), clamped to [-127, 127]; scaled values above the element maximum       */
 /* saturate.  An all-zero block gets e = -127.  A block holding NaN or Inf   */
 /* gets the NaN scale code 0xFF and element codes 0.                         */
+/* Variant MXO_V_CEIL ([FP4] "The two Blackwell formats: MXFP4 vs NVFP4": a  */
+/* power-of-two scale either wastes range or saturates the block maximum).   */
+/* READING: the "no saturation" choice -- e is the smallest integer in       */
+/* [-127, 127] with max|x| <= g_max * 2^e (g_max the largest element value), */
+/* 127 when there is none; found by trying every e in increasing order.      */
 /* ------------------------------------------------------------------------ */
-static void mx_encode_block(const float* v, int n, int fmt, int rnd, uint64_t seed,
-                            uint64_t counter, uint64_t n0, uint8_t* codes_row,
+static void mx_encode_block(const float* v, int n, int fmt, int rnd, int ceil_rule,
+                            uint64_t seed, uint64_t counter, uint64_t n0, uint8_t* codes_row,
                             int64_t col0, uint8_t* scale_out) {
   const mxo_alphabet* al = (fmt == MXO_MXFP8) ? &g_e4m3 : &g_e2m1;
   int emax = (fmt == MXO_MXFP8) ? 8 : 2;
@@ -353,7 +363,11 @@ static void mx_encode_block(const float* v, int n, int fmt, int rnd, uint64_t se
     for (int i = 0; i < n; ++i) codes[i] = 0;
   } else {
     int e;
-    if (amax == 0.0) {
+    if (ceil_rule) {
+      double gmax = al->v[al->n - 1];
+      e = -127;
+      while (e < 127 && amax > ldexp(gmax, e)) ++e;
+    } else if (amax == 0.0) {
       e = -127;
     } else {
       int E;
@@ -387,9 +401,11 @@ static int64_t code_row_bytes(int fmt, int64_t cols) {
 
 int mxo_quantize_mx(const void* x, int xdt, int64_t ld, int64_t rows, int64_t cols, int fmt,
                     int rnd, uint64_t seed, uint64_t counter, int rht, uint32_t mask,
-                    uint8_t* codes, uint8_t* scales) {
+                    int variant, uint8_t* codes, uint8_t* scales) {
   ensure_tables();
   if ((fmt != MXO_MXFP8 && fmt != MXO_MXFP4) || cols % 32 || (rht && cols % 16)) return -1;
+  if (variant & ~MXO_V_CEIL) return -1;
+  const int ceil_rule = (variant & MXO_V_CEIL) != 0;
 #pragma omp parallel
   {
     float* row = (float*)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
@@ -398,8 +414,8 @@ int mxo_quantize_mx(const void* x, int xdt, int64_t ld, int64_t rows, int64_t co
       load_row(x, xdt, ld, r, cols, rht, mask, row);
       uint8_t* crow = codes + r * code_row_bytes(fmt, cols);
       for (int64_t b = 0; b < cols / 32; ++b)
-        mx_encode_block(row + b * 32, 32, fmt, rnd, seed, counter, (uint64_t)(r * cols + b * 32),
-                        crow, b * 32, &scales[r * (cols / 32) + b]);
+        mx_encode_block(row + b * 32, 32, fmt, rnd, ceil_rule, seed, counter,
+                        (uint64_t)(r * cols + b * 32), crow, b * 32, &scales[r * (cols / 32) + b]);
     }
     free(row);
   }
@@ -442,60 +458,129 @@ float mxo_tensor_amax(const void* x, int xdt, int64_t ld, int64_t rows, int64_t 
   return best;
 }
 
+/* One 16-element block whose block scale is chosen for the block maximum ab
+ * mapped to k (k = 6: the format's rule above).  Writes the 16 codes and
+ * returns the block-scale code. */
+static uint32_t nv_encode_block(const float* v, float ab, float T, float S, float k, int rnd,
+                                uint64_t seed, uint64_t counter, uint64_t n0, uint32_t codes[16]) {
+  uint32_t sb = 0;
+  float rcp = 0.0f;
+  if (T != 0.0f) {
+    float d = k * S;
+    float q = ab / d;
+    sb = encode_rne(&g_e4m3, (double)q);
+    float dsb = (float)mxo_e4m3_decode(sb);
+    if (dsb != 0.0f) {
+      float p = dsb * S;
+      rcp = 1.0f / p;
+    }
+  }
+  for (int i = 0; i < 16; ++i) {
+    if (rcp == 0.0f) {
+      codes[i] = signbit(v[i]) ? 0x8u : 0x0u;
+    } else {
+      float y = v[i] * rcp;
+      codes[i] = (rnd == MXO_SR) ? encode_sr(&g_e2m1, (double)y, mxo_rand16(seed, counter, n0 + i))
+                                 : encode_rne(&g_e2m1, (double)y);
+    }
+  }
+  return sb;
+}
+
+/* Squared error of a block against its decoded values (for MXO_V_FOUR6).
+ * READING (the pages say only that the choice aims at lower quantization
+ * error): the error is the sum of squared differences between x and its
+ * decoded value fp32(e2m1 * e4m3 * S), evaluated in FP32 in a fixed order --
+ * d = x - xhat rounded once, each half of 8 elements accumulated with fused
+ * multiply-adds acc = fma(d, d, acc) from element 0 up, then the two halves
+ * added -- so that the choice is a reproducible function of the input. */
+static float nv_block_sq_error(const float* v, const uint32_t codes[16], uint32_t sb, float S) {
+  double dsb = mxo_e4m3_decode(sb);
+  float half[2] = {0.0f, 0.0f};
+  for (int h = 0; h < 2; ++h) {
+    for (int i = 0; i < 8; ++i) {
+      int j = 8 * h + i;
+      double p = mxo_e2m1_decode(codes[j]) * dsb; /* exact */
+      float xh = (float)p * S;
+      float d = v[j] - xh;
+      half[h] = fmaf(d, d, half[h]);
+    }
+  }
+  return half[0] + half[1];
+}
+
+/* NVFP4 quantization with the variants:
+ *   MXO_V_FOUR6 ([INK] "A precision choice for each stage": for activations
+ *     a Four Over Six technique chooses between block scales to lower the
+ *     quantization error).
+ *     READING: every block is encoded twice, with its maximum mapped to 6
+ *     (the rule above) and to 4 (q = a_b / (4 S)); the encoding with the
+ *     smaller error (nv_block_sq_error) is kept, the 6-encoding on a tie.
+ *     S is the format's T / 2688 in both, so a 4-candidate whose scale
+ *     saturates at 448 simply loses.  Round-to-nearest only.
+ *   MXO_V_2D ([MXF] "NVFP4": two-dimensional weight quantisation so forward
+ *     and backward passes see consistent values).  READING: one block scale
+ *     per tile of 16 rows x 16 columns (the last band of rows may be shorter),
+ *     from the maximum over the whole tile, stored in each of the tile's rows
+ *     so the tensor keeps the ordinary layout; elements are encoded as above.
+ *     The quantized values of the transpose are then the transpose of the
+ *     quantized values.
+ * The two variants are not combined. */
 int mxo_quantize_nvfp4(const void* x, int xdt, int64_t ld, int64_t rows, int64_t cols, int rnd,
-                       uint64_t seed, uint64_t counter, int rht, uint32_t mask,
+                       uint64_t seed, uint64_t counter, int rht, uint32_t mask, int variant,
                        const float* amax_in, uint8_t* codes, uint8_t* scales,
                        float* tensor_scale) {
   ensure_tables();
   if (cols % 16) return -1;
+  if (variant & ~(MXO_V_FOUR6 | MXO_V_2D)) return -1;
+  if ((variant & MXO_V_FOUR6) && ((variant & MXO_V_2D) || rnd == MXO_SR)) return -1;
+  const int four6 = (variant & MXO_V_FOUR6) != 0;
+  const int64_t band = (variant & MXO_V_2D) ? 16 : 1;
   float T = amax_in ? *amax_in : mxo_tensor_amax(x, xdt, ld, rows, cols, rht, mask);
   float S = (T == 0.0f) ? 1.0f : T / 2688.0f;
   *tensor_scale = S;
+  const int64_t nbands = (rows + band - 1) / band;
 #pragma omp parallel
   {
-    float* row = (float*)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+    float* buf = (float*)malloc(sizeof(float) * (size_t)(band * (cols > 0 ? cols : 1)));
 #pragma omp for schedule(static)
-    for (int64_t r = 0; r < rows; ++r) {
-      load_row(x, xdt, ld, r, cols, rht, mask, row);
-      uint8_t* crow = codes + r * (cols / 2);
+    for (int64_t t = 0; t < nbands; ++t) {
+      const int64_t r0 = t * band;
+      const int64_t nr = (rows - r0 < band) ? rows - r0 : band;
+      for (int64_t i = 0; i < nr; ++i) load_row(x, xdt, ld, r0 + i, cols, rht, mask, buf + i * cols);
       for (int64_t b = 0; b < cols / 16; ++b) {
-        const float* v = row + b * 16;
-        uint32_t sb = 0;
-        float rcp = 0.0f;
-        if (T != 0.0f) {
-          float ab = 0.0f;
-          for (int i = 0; i < 16; ++i) {
-            float a = fabsf(v[i]);
+        float ab = 0.0f;
+        for (int64_t i = 0; i < nr; ++i)
+          for (int j = 0; j < 16; ++j) {
+            float a = fabsf(buf[i * cols + b * 16 + j]);
             if (a > ab) ab = a;
           }
-          float d = 6.0f * S;
-          float q = ab / d;
-          sb = encode_rne(&g_e4m3, (double)q);
-          float dsb = (float)mxo_e4m3_decode(sb);
-          if (dsb != 0.0f) {
-            float p = dsb * S;
-            rcp = 1.0f / p;
+        for (int64_t i = 0; i < nr; ++i) {
+          const int64_t r = r0 + i;
+          const float* v = buf + i * cols + b * 16;
+          const uint64_t n0 = (uint64_t)(r * cols + b * 16);
+          uint32_t c6[16], c4[16];
+          uint32_t sb = nv_encode_block(v, ab, T, S, 6.0f, rnd, seed, counter, n0, c6);
+          const uint32_t* cw = c6;
+          if (four6 && T != 0.0f) {
+            uint32_t sb4 = nv_encode_block(v, ab, T, S, 4.0f, rnd, seed, counter, n0, c4);
+            if (nv_block_sq_error(v, c4, sb4, S) < nv_block_sq_error(v, c6, sb, S)) {
+              sb = sb4;
+              cw = c4;
+            }
           }
-        }
-        scales[r * (cols / 16) + b] = (uint8_t)sb;
-        for (int i = 0; i < 16; ++i) {
-          uint32_t code;
-          if (rcp == 0.0f) {
-            code = signbit(v[i]) ? 0x8u : 0x0u;
-          } else {
-            float y = v[i] * rcp;
-            uint64_t n = (uint64_t)(r * cols + b * 16 + i);
-            code = (rnd == MXO_SR) ? encode_sr(&g_e2m1, (double)y, mxo_rand16(seed, counter, n))
-                                   : encode_rne(&g_e2m1, (double)y);
+          scales[r * (cols / 16) + b] = (uint8_t)sb;
+          uint8_t* crow = codes + r * (cols / 2);
+          for (int j = 0; j < 16; ++j) {
+            int64_t c = b * 16 + j;
+            uint8_t* byte = &crow[c >> 1];
+            if (c & 1) *byte = (uint8_t)((*byte & 0x0F) | (cw[j] << 4));
+            else *byte = (uint8_t)((*byte & 0xF0) | cw[j]);
           }
-          int64_t c = b * 16 + i;
-          uint8_t* byte = &crow[c >> 1];
-          if (c & 1) *byte = (uint8_t)((*byte & 0x0F) | (code << 4));
-          else *byte = (uint8_t)((*byte & 0xF0) | code);
         }
       }
     }
-    free(row);
+    free(buf);
   }
   return 0;
 }
@@ -583,7 +668,7 @@ int mxo_requant_transpose(int src_fmt, const void* src_codes_or_bf16, const uint
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < cols; ++r) {
     for (int64_t b = 0; b < rows / 32; ++b)
-      mx_encode_block(xt + r * rows + b * 32, 32, MXO_MXFP8, rnd, seed, counter,
+      mx_encode_block(xt + r * rows + b * 32, 32, MXO_MXFP8, rnd, 0, seed, counter,
                       (uint64_t)(r * rows + b * 32), codes + r * rows, b * 32,
                       &scales[r * (rows / 32) + b]);
   }
