@@ -280,6 +280,14 @@ def detail(torch, mx, W, args):
     ms = time_fn(torch, lambda: mx.mx_gemm(q4a, q4b, C), it, wu)
     res["mxfp4_gemm_4096_rows_layout"] = {"ms": ms, "tflops": 2 * M * N * K / ms / 1e9,
                                           "frac_fp4_peak": 2 * M * N * K / ms / 1e9 / PEAK_TFLOPS["fp4"]}
+    # MXFP4 tile-layout quantize of the activation operand, floor and ceil scale rules
+    q4t = mx.empty(2, M, K, layout=mx.MX_LAYOUT_TILED)
+    by4 = M * K * (2 + 0.5 + 1 / 32)
+    for name, fl_ in (("floor", 0), ("ceil", mx.MX_FLAG_SCALE_CEIL)):
+        ms = time_fn(torch, lambda: mx.mx_quantize(a, q4t, flags=fl_), it, wu)
+        res[f"mxfp4_quantize_tiled_4096x4096_{name}"] = {"ms": ms, "gbs": by4 / ms / 1e6,
+                                                         "frac_hbm": by4 / ms / 1e6 / PEAK_HBM_GBS}
+    del q4t
     del a, b, qa, qb, qat, qbt, q4a, q4b, C
 
     # NVFP4 MoE forward: 4096 tokens x 7168, top-8 of 32 experts, W_e 2048x7168
@@ -293,17 +301,32 @@ def detail(torch, mx, W, args):
     for e in range(E):
         mx.mx_quantize(Wt[e * inter:(e + 1) * inter], qw.view_rows(e * inter, (e + 1) * inter, qw.tensor_scale[e:e + 1]),
                        amax=amax[e:e + 1])
-    del Wt
+    # the same expert weights with 2-D 16x16 blocks (each expert: amax pass + encode pass)
+    qw2 = mx.empty(3, E * inter, hid, n_tensor_scales=E)
+
+    def quant_experts_2d():
+        for e in range(E):
+            mx.mx_quantize(Wt[e * inter:(e + 1) * inter],
+                           qw2.view_rows(e * inter, (e + 1) * inter, qw2.tensor_scale[e:e + 1]),
+                           flags=mx.MX_FLAG_BLOCK_2D, amax=amax[e:e + 1])
+    ms_w2 = time_fn(torch, quant_experts_2d, 5, 2)
+    byw = E * inter * hid * (2 * 2 + 0.5 + 1 / 16)
+    res["nvfp4_2d_weights_32x2048x7168"] = {"ms_all_experts": ms_w2, "gbs_2pass": byw / ms_w2 / 1e6,
+                                            "frac_hbm": byw / ms_w2 / 1e6 / PEAK_HBM_GBS}
+    del Wt, qw2
     qx = mx.empty(3, tokens, hid)
     xa = torch.zeros(1, dtype=torch.float32, device="cuda")
     ri = torch.from_numpy(row_index).cuda()
     off = torch.from_numpy(offsets).cuda()
     Cg = torch.empty(R, inter, dtype=torch.bfloat16, device="cuda")
     ms_q = time_fn(torch, lambda: mx.mx_quantize(X, qx, amax=xa), it, wu)
+    ms_q46 = time_fn(torch, lambda: mx.mx_quantize(X, qx, flags=mx.MX_FLAG_FOUR_OVER_SIX, amax=xa), it, wu)
     ms_g = time_fn(torch, lambda: mx.mx_gemm_grouped(qx, ri, R, qw, E, off, Cg), it, wu)
     fl = 2.0 * R * inter * hid
     by = tokens * hid * (2 * 2 + 0.5 + 1 / 16)
     res["nvfp4_moe_fwd"] = {"quant_ms": ms_q, "quant_gbs_2pass": by / ms_q / 1e6,
+                            "quant_four_over_six_ms": ms_q46,
+                            "quant_four_over_six_gbs_2pass": by / ms_q46 / 1e6,
                             "gemm_ms": ms_g, "gemm_tflops": fl / ms_g / 1e9,
                             "frac_fp4_peak": fl / ms_g / 1e9 / PEAK_TFLOPS["fp4"],
                             "frac_fp8_peak": fl / ms_g / 1e9 / PEAK_TFLOPS["fp8"],

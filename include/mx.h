@@ -126,6 +126,9 @@ typedef struct {
 
 #define MX_FLAG_RHT16 1u      /* apply the 16-point random Hadamard transform first */
 #define MX_FLAG_AMAX_GIVEN 2u /* NVFP4: *amax already holds max|x| (after RHT if set) */
+#define MX_FLAG_SCALE_CEIL 4u    /* MX: the smallest scale that saturates no element */
+#define MX_FLAG_FOUR_OVER_SIX 8u /* NVFP4, RNE: per block, map the max to 4 or 6 */
+#define MX_FLAG_BLOCK_2D 16u     /* NVFP4: one block scale per 16 x 16 tile */
 
 /* Bytes of the code and scale arrays of a [rows, cols] tensor ([MXF]
  * "Microscaling": 8 bits per 32 elements; [FP4] format table).  Returns 0 for
@@ -158,6 +161,27 @@ uint16_t mx_rht_signs(uint64_t seed);
  * MX_FLAG_RHT16 ([MXF] "NVFP4": random Hadamard transforms bound block
  * outliers): each 16-group of a row is first mapped to
  * y = (1/4) H16 D x in FP32 (see mx_hadamard16) and y is quantized.
+ *
+ * Variants (the stored format is unchanged, so every consumer reads them):
+ *   MX_FLAG_SCALE_CEIL (MX formats; [FP4] "The two Blackwell formats: MXFP4
+ *     vs NVFP4": a power-of-two scale either wastes range or saturates the
+ *     block maximum): e is the smallest integer in [-127, 127] with
+ *     max|x| <= g_max * 2^e (g_max = 448 for E4M3, 6 for E2M1), so no
+ *     element saturates.
+ *   MX_FLAG_FOUR_OVER_SIX (NVFP4 with MX_RNE; [INK] "A precision choice for
+ *     each stage": a choice between block scales that lowers the
+ *     quantization error): each block is encoded with sb from
+ *     max|x| / (6 S) and from max|x| / (4 S); the encoding whose decoded
+ *     values have the smaller squared error is kept, the first on a tie.  The
+ *     error is an FP32 sum: d = x - fp32(e2m1 * e4m3 * S), each half of 8
+ *     elements accumulated as acc = fma(d, d, acc) from its first element,
+ *     then the two halves added.
+ *   MX_FLAG_BLOCK_2D (NVFP4; [MXF] "NVFP4": two-dimensional weight
+ *     quantisation): one block scale per tile of 16 rows x 16 columns (the
+ *     last band of rows may be shorter), from the tile's max|x|, stored in
+ *     each of its rows; the quantized values of x^T are then the transpose of
+ *     those of x.  Not combined with MX_FLAG_FOUR_OVER_SIX.
+ * Other combinations return MX_ERR_UNSUPPORTED.
  *
  * Requirements: cols % 32 == 0 (MX) or % 16 == 0 (NVFP4); out->rows == rows.
  * SR stream: see mx_rng. */

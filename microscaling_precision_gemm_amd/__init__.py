@@ -19,6 +19,7 @@ MX_MXFP8_E4M3, MX_MXFP4_E2M1, MX_NVFP4 = 1, 2, 3
 MX_RNE, MX_SR = 0, 1
 MX_BF16, MX_F32 = 0, 1
 MX_FLAG_RHT16, MX_FLAG_AMAX_GIVEN = 1, 2
+MX_FLAG_SCALE_CEIL, MX_FLAG_FOUR_OVER_SIX, MX_FLAG_BLOCK_2D = 4, 8, 16
 MX_GEMM_FP8_NATIVE = 1
 MX_LAYOUT_ROWS, MX_LAYOUT_TILED = 0, 1
 

@@ -96,11 +96,18 @@ mx_status mx_quantize(const void* x, int32_t xdt, int64_t rows, int64_t cols, in
                       uint16_t rht_sign_mask, float* amax, mx_stream stream) {
   if (!out) return MX_ERR_NULL;
   if (rnd != MX_RNE && rnd != MX_SR) return MX_ERR_FORMAT;
-  if (flags & ~(MX_FLAG_RHT16 | MX_FLAG_AMAX_GIVEN)) return MX_ERR_UNSUPPORTED;
+  if (flags & ~(MX_FLAG_RHT16 | MX_FLAG_AMAX_GIVEN | MX_FLAG_SCALE_CEIL | MX_FLAG_FOUR_OVER_SIX |
+                MX_FLAG_BLOCK_2D))
+    return MX_ERR_UNSUPPORTED;
   mx_status st = check_matrix(x, xdt, rows, cols, ld_x);
   if (st != MX_OK) return st;
   st = check_tensor(out, rows, cols);
   if (st != MX_OK) return st;
+  const bool nv = out->fmt == MX_NVFP4;
+  if ((flags & MX_FLAG_SCALE_CEIL) && nv) return MX_ERR_UNSUPPORTED;
+  if ((flags & (MX_FLAG_FOUR_OVER_SIX | MX_FLAG_BLOCK_2D)) && !nv) return MX_ERR_UNSUPPORTED;
+  if ((flags & MX_FLAG_FOUR_OVER_SIX) && (rnd != MX_RNE || (flags & MX_FLAG_BLOCK_2D)))
+    return MX_ERR_UNSUPPORTED;
   if (out->fmt == MX_NVFP4) {
     if (!amax) return MX_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(amax) & 3u) return MX_ERR_ALIGN;
@@ -126,6 +133,9 @@ mx_status mx_quantize(const void* x, int32_t xdt, int64_t rows, int64_t cols, in
   a.sign_mask = rht_sign_mask;
   a.amax_given = (flags & MX_FLAG_AMAX_GIVEN) != 0;
   a.tiled = out->layout == MX_LAYOUT_TILED;
+  a.ceil = (flags & MX_FLAG_SCALE_CEIL) != 0;
+  a.four6 = (flags & MX_FLAG_FOUR_OVER_SIX) != 0;
+  a.block2d = (flags & MX_FLAG_BLOCK_2D) != 0;
   return hip_status(mxk::launch_quantize(a, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -109,6 +109,18 @@ __host__ __device__ inline uint32_t e8m0_from_amax_bits(uint32_t amax_bits, uint
   uint32_t e = amax_bits >> 23;  // biased exponent; 0 for zero and subnormals
   return e > emax ? e - emax : 0u;
 }
+// The same block under the ceil (no-saturation) rule: the smallest scale with
+// amax <= gmax * X.  That is the floor code, plus one when amax's significand
+// exceeds gmax's (gmax_mant: the element maximum's FP32 mantissa field, E4M3
+// 448 = 1.75 * 2^8 -> 0x600000, E2M1 6 = 1.5 * 2^2 -> 0x400000).  Below
+// 2^emax * 2^-127 the floor code is clamped to 0 and nothing saturates.
+__host__ __device__ inline uint32_t e8m0_ceil_from_amax_bits(uint32_t amax_bits, uint32_t emax,
+                                                             uint32_t gmax_mant) {
+  if (amax_bits >= 0x7F800000u) return 0xFFu;
+  uint32_t e = amax_bits >> 23;
+  if (e < emax) return 0u;
+  return e - emax + ((amax_bits & 0x7FFFFFu) > gmax_mant ? 1u : 0u);
+}
 // 1 / 2^(code-127) as an exact FP32 (code in 0..254-emax)
 __host__ __device__ inline float e8m0_inverse(uint32_t code) { return u2f((254u - code) << 23); }
 

@@ -192,7 +192,8 @@ __device__ inline void encode_mx(const QuantArgs& a, int64_t q, const float v[8]
   m = o > m ? o : m;
   o = dpp_xor2(m);
   m = o > m ? o : m;
-  const uint32_t sc = e8m0_from_amax_bits(m, emax);
+  constexpr uint32_t gmax_mant = FMT == FMT_MXFP8 ? 0x600000u : 0x400000u;
+  const uint32_t sc = a.ceil ? e8m0_ceil_from_amax_bits(m, emax, gmax_mant) : e8m0_from_amax_bits(m, emax);
   const float inv = e8m0_inverse(sc);
   float y[8];
 #pragma unroll
@@ -389,7 +390,59 @@ __device__ inline void encode_nv(const QuantArgs& a, float S, float d, int64_t q
   e.sc = sb;
 }
 
-template <int XDT, bool SR, bool RHT>
+// Four Over Six ("Thinking Machines ... Inkling 2 Small", section "A
+// precision choice for each stage": a choice between block scales that
+// lowers the quantization error).  The block is encoded with its maximum
+// mapped to 6 (d6 = 6 S, the format's rule) and to 4 (d4 = 4 S); the one
+// whose decoded values fp32(e2m1 * e4m3 * S) have the smaller squared error
+// is kept, 6 on a tie.  The error is an FP32 sum in a fixed order: each lane
+// of the pair accumulates its 8 elements with fused multiply-adds from
+// element 0, then the pair's two partial sums are added, so the choice is a
+// reproducible function of the input.  Round-to-nearest only.
+__device__ inline float nv_sq_err(const float v[8], uint32_t w, float dsb, float S) {
+#pragma clang fp contract(off)
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float xh = (e2m1_value((w >> (4 * i)) & 0xFu) * dsb) * S;  // first product exact
+    const float d = v[i] - xh;
+    acc = __builtin_fmaf(d, d, acc);
+  }
+  return acc;
+}
+
+__device__ inline void encode_nv46(float S, float d6, float d4, const float v[8],
+                                   Enc<FMT_NVFP4>& e) {
+#pragma clang fp contract(off)
+  uint32_t m = max_abs_bits(v);
+  uint32_t o = dpp_xor1(m);
+  m = o > m ? o : m;
+  const float ab = u2f(m);
+  uint32_t sb[2], w[2];
+  float err[2];
+  const float d[2] = {d6, d4};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    sb[k] = e4m3_rne_mag(ab / d[k]);
+    const float dsb = e4m3_mag_value(sb[k]);
+    float rcp = 0.0f;
+    if (dsb != 0.0f) {
+      const float p = dsb * S;
+      rcp = 1.0f / p;
+    }
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = v[i] * rcp;
+    w[k] = pack_e2m1_rne(y);
+    const float part = nv_sq_err(v, w[k], dsb, S);
+    err[k] = part + dpp_xor1f(part);  // addition commutes: both lanes get the same sum
+  }
+  const bool four = err[1] < err[0];
+  e.w[0] = four ? w[1] : w[0];
+  e.sc = four ? sb[1] : sb[0];
+}
+
+template <int XDT, bool SR, bool RHT, bool F46>
 __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(QuantArgs a, int64_t Q) {
 #pragma clang fp contract(off)
   const uint32_t lane = threadIdx.x & 63u;
@@ -410,7 +463,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(QuantArgs a, int64_t Q
     float v[8];
     widen<XDT>(raw[u], v);
     if constexpr (RHT) rht_forward(v, a.sign_mask, (uint32_t)(q & 1));
-    encode_nv<SR>(a, S, d, q, v, enc[u]);
+    if constexpr (F46) encode_nv46(S, d, 4.0f * S, v, enc[u]);
+    else encode_nv<SR>(a, S, d, q, v, enc[u]);
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) store_enc<FMT_NVFP4>(a, q0 + 64 * u, Q, lane, 2u, enc[u]);
@@ -421,6 +475,109 @@ __global__ void k_nv_scale_only(const float* amax, float* tensor_scale) {
 #pragma clang fp contract(off)
   const float T = *amax;
   *tensor_scale = (T == 0.0f) ? 1.0f : T / 2688.0f;
+}
+
+// ---- NVFP4 with 2-D blocks --------------------------------------------------
+// "Microscaling (MX) and block-scaled 4-bit formats", section "NVFP4":
+// two-dimensional weight quantisation, so that the forward and the backward
+// (transposed) use see the same values.  One E4M3 block scale per tile of
+// 16 rows x 16 columns, from the tile's max |x| (the last band of rows may be
+// shorter), stored in each of the tile's rows so the tensor keeps the
+// ordinary row layout; elements are encoded as in the 1-D quantizer.
+// One wave per band of 16 rows x 128 columns: lane 8 i + k holds chunk k
+// (8 elements) of rows i and i + 8 of each 64-column half, so each load
+// instruction reads 8 rows x 128 contiguous bytes (BF16).  A tile is the 16
+// lanes with the same k >> 1 over both row halves: the in-lane max over the
+// halves, then lane exchanges at distance 1, 8, 16 and 32.
+constexpr int k2dCols = 128;
+
+template <int XDT, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads) void k_quant_nvfp4_2d(QuantArgs a, int64_t nwaves,
+                                                             int64_t groups_per_band) {
+#pragma clang fp contract(off)
+  const uint32_t lane = threadIdx.x & 63u;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  if (wave >= nwaves) return;
+  const int64_t band = wave / groups_per_band;
+  const int64_t G = wave - band * groups_per_band;
+  const uint32_t i = lane >> 3, k = lane & 7u;
+  const int64_t rows = a.rows, cols = a.cols;
+  // load u: row half h = u & 1, column half c = u >> 1
+  int64_t row[4], col[4];
+  bool ok[4];
+  Raw<XDT> raw[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    row[u] = band * 16 + 8 * (u & 1) + i;
+    col[u] = G * k2dCols + 64 * (u >> 1) + 8 * k;
+    ok[u] = row[u] < rows && col[u] < cols;
+    const int64_t r = row[u] < rows ? row[u] : rows - 1;
+    const int64_t c = col[u] < cols ? col[u] : cols - 8;
+    load_raw<XDT>(a.x, r * a.ld_x + c, raw[u]);
+  }
+  const float T = *a.amax;
+  const float S = (T == 0.0f) ? 1.0f : T / 2688.0f;
+  if (wave == 0 && lane == 0) *a.tensor_scale = S;
+  const float d = 6.0f * S;
+  float v[4][8];
+  uint32_t m[2] = {0u, 0u};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    widen<XDT>(raw[u], v[u]);
+    if constexpr (RHT) rht_forward(v[u], a.sign_mask, k & 1u);
+    const uint32_t b = ok[u] ? max_abs_bits(v[u]) : 0u;
+    m[u >> 1] = b > m[u >> 1] ? b : m[u >> 1];
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    uint32_t t = m[c];
+    uint32_t o = dpp_xor1(t);
+    t = o > t ? o : t;
+    o = lane_read(t, lane ^ 8u);
+    t = o > t ? o : t;
+    o = lane_read(t, lane ^ 16u);
+    t = o > t ? o : t;
+    o = lane_read(t, lane ^ 32u);
+    m[c] = o > t ? o : t;
+  }
+  const int64_t spr = cols >> 4;  // scale bytes per row
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t sb = e4m3_rne_mag(u2f(m[u >> 1]) / d);
+    const float dsb = e4m3_mag_value(sb);
+    float rcp = 0.0f;
+    if (dsb != 0.0f) {
+      const float p = dsb * S;
+      rcp = 1.0f / p;
+    }
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = v[u][j] * rcp;
+    uint32_t w;
+    if constexpr (!SR) {
+      w = pack_e2m1_rne(y);
+    } else {
+      uint32_t r[8];
+      rand16x8(a.seed, a.counter, (uint64_t)((row[u] * cols + col[u]) >> 3), r);
+      w = 0u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w |= e2m1_encode(y[j], true, r[j]) << (4 * j);
+    }
+    if (ok[u]) *reinterpret_cast<uint32_t*>(a.codes + row[u] * (cols >> 1) + (col[u] >> 1)) = w;
+    // Scale bytes: lane 8 i + 2 p holds block p of its row's 64-column half.
+    // With a multiple of 4 blocks per row the half's 4 blocks are all valid
+    // and 4-byte aligned (one 32-bit store); otherwise one byte per block.
+    const uint32_t s1 = lane_read(sb, lane + 2u), s2 = lane_read(sb, lane + 4u),
+                   s3 = lane_read(sb, lane + 6u);
+    if (ok[u]) {
+      uint8_t* sp = a.scales + row[u] * spr + (col[u] >> 4);
+      if ((spr & 3) == 0) {
+        if (k == 0u) *reinterpret_cast<uint32_t*>(sp) = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
+      } else if ((k & 1u) == 0u) {
+        *sp = (uint8_t)sb;
+      }
+    }
+  }
 }
 
 // ---- per-tensor amax ------------------------------------------------------
@@ -448,8 +605,10 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const void* x, int64_t co
       float v[8];
       widen<XDT>(raw[u], v);
       if constexpr (RHT) rht_forward(v, sign_mask, (uint32_t)((q0 + 64 * u) & 1));
-      const uint32_t b = max_abs_bits(v);
-      m = b > m ? b : m;  // chunks past the end repeat chunk Q - 1
+      // Chunks past the end reload chunk Q - 1 and are left out: after the
+      // Hadamard transform a pair of them is not a group of the input.
+      const uint32_t b = q0 + 64 * u < Q ? max_abs_bits(v) : 0u;
+      m = b > m ? b : m;
     }
   }
   m = wave_max_u32(m);
@@ -575,7 +734,18 @@ hipError_t quant_mx_t(const QuantArgs& a, int64_t Q, hipStream_t s) {
 }
 template <int XDT, bool SR, bool RHT>
 hipError_t quant_nv_t(const QuantArgs& a, int64_t Q, hipStream_t s) {
-  hipLaunchKernelGGL((k_quant_nvfp4<XDT, SR, RHT>), dim3(grid_for(Q)), dim3(kThreads), 0, s, a, Q);
+  if (a.block2d) {
+    const int64_t gpb = (a.cols + k2dCols - 1) / k2dCols;
+    const int64_t nwaves = (a.rows + 15) / 16 * gpb;
+    const int64_t blocks = (nwaves + kThreads / 64 - 1) / (kThreads / 64);
+    hipLaunchKernelGGL((k_quant_nvfp4_2d<XDT, SR, RHT>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                       a, nwaves, gpb);
+  } else if (a.four6) {
+    if constexpr (SR) return hipErrorInvalidValue;  // rejected before launch
+    hipLaunchKernelGGL((k_quant_nvfp4<XDT, false, RHT, true>), dim3(grid_for(Q)), dim3(kThreads), 0, s, a, Q);
+  } else {
+    hipLaunchKernelGGL((k_quant_nvfp4<XDT, SR, RHT, false>), dim3(grid_for(Q)), dim3(kThreads), 0, s, a, Q);
+  }
   return hipGetLastError();
 }
 template <int XDT, int FMT>

@@ -25,6 +25,9 @@ struct QuantArgs {
   uint32_t sign_mask;
   bool amax_given;
   bool tiled;  // codes and scales in the matrix-instruction tile layout
+  bool ceil;     // MX: ceil (no-saturation) scale rule
+  bool four6;    // NVFP4: Four Over Six block-scale choice (round-to-nearest)
+  bool block2d;  // NVFP4: one block scale per 16 x 16 tile
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);

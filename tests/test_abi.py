@@ -76,7 +76,13 @@ def test_quantize_argument_checks(mx):
     assert q(FAKE, 0, 4, 64, 64, ctypes.byref(nv), 0, rng, 0, 0, None, None) == 1  # amax NULL
     nots = _t(mx, 3, 4, 64, ts=None)
     assert q(FAKE, 0, 4, 64, 64, ctypes.byref(nots), 0, rng, 0, 0, FAKE, None) == 1
-    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(t), 0, rng, 8, 0, None, None) == 5  # flags
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(t), 0, rng, 64, 0, None, None) == 5  # flags
+    # variants: ceil is MX-only; Four Over Six is NVFP4 + RNE, not with 2-D; 2-D is NVFP4-only
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(nv), 0, rng, 4, 0, FAKE, None) == 5
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(t), 0, rng, 8, 0, None, None) == 5
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(t), 0, rng, 16, 0, None, None) == 5
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(nv), 1, rng, 8, 0, FAKE, None) == 5
+    assert q(FAKE, 0, 4, 64, 64, ctypes.byref(nv), 0, rng, 8 | 16, 0, FAKE, None) == 5
     assert q(FAKE, 0, 4, 64, 64, ctypes.byref(t), 0, rng, 2, 0, None, None) == 5  # amax on MX
     nocodes = _t(mx, 1, 4, 64, codes=None)
     assert q(FAKE, 0, 4, 64, 64, ctypes.byref(nocodes), 0, rng, 0, 0, None, None) == 1

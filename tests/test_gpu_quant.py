@@ -64,6 +64,19 @@ def test_nvfp4_quantize_bit_exact(shape, rnd, rht, dt):
     assert np.array_equal(c, wc), f"codes differ at {np.argwhere(c != wc)[:5]}"
 
 
+@pytest.mark.parametrize("shape", [(1, 16), (1, 48), (3, 16), (5, 80)])
+def test_amax_with_hadamard_on_tensors_shorter_than_a_wave(shape):
+    """Fewer chunks than lanes: lanes past the end must not add transformed
+    duplicates of the last chunk to the maximum."""
+    rows, cols = shape
+    bits = W.normal_bf16(rows, cols, 1.0, rows + cols, 42)
+    mask = oracle.rht_signs(rows * cols)
+    amax = torch.zeros(1, dtype=torch.float32, device=dev())
+    mx.mx_amax(to_gpu_bf16(bits), amax, mx.MX_FLAG_RHT16, mask)
+    torch.cuda.synchronize()
+    assert float(amax.cpu()[0]) == oracle.tensor_amax(bits, True, mask)
+
+
 def test_nvfp4_amax_given_and_zero_tensor():
     bits = W.normal_bf16(64, 128, 1.0, 3, 41)
     x = to_gpu_bf16(bits)

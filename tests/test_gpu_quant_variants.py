@@ -1,0 +1,203 @@
+"""GPU parity of the quantizer variants against the CPU oracle, bit for bit:
+the ceil (no-saturation) E8M0 rule in both MX layouts, the Four Over Six NVFP4
+block-scale choice and 2-D (16 x 16) NVFP4 blocks, on shapes with ragged
+tails, both input dtypes, strided inputs, SR and the Hadamard transform where
+the variant allows them, and at the sizes the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import microscaling_precision_gemm_amd as mx
+    from tests.gpu_util import dev, host, to_gpu_bf16, to_gpu_f32
+    from tests.tiles import untile_codes, untile_scales
+
+
+def _inputs(rows, cols, dt, seed, pad=0, spread=False):
+    """N(0, 1.5^2) with 1% outliers x60.  With `spread`, rows are scaled by
+    powers of two over 2^-40 .. 2^40 and some 32-blocks get a maximum planted
+    on the ceil rule's boundaries: exactly g_max * 2^k (g_max = 6 or 448), or
+    the next value above it in the input dtype."""
+    bits = W.normal_bf16(rows, cols, 1.5, seed, 50, outlier_entries=0.01, outlier_mult=60.0)
+    x = W.bf16_bits_to_f32(bits).astype(np.float64)
+    if spread:
+        g = W.rng(seed, 51)
+        x *= np.exp2(np.round(g.uniform(-40, 40, (rows, 1))))
+        for t in range(min(rows * (cols // 32), 64)):
+            r, b = t % rows, (t // rows) % (cols // 32)
+            v = (6.0 if t % 4 < 2 else 448.0) * 2.0 ** int(g.integers(-30, 30))
+            if t % 2:
+                v *= (1 + 2.0**-7) if dt == "bf16" else (1 + 2.0**-23)
+            blk = x[r, 32 * b:32 * b + 32]
+            blk *= 0.5 * v / max(np.abs(blk).max(), 1e-300)  # the rest of the block below v
+            blk[int(g.integers(0, 32))] = v if t % 3 else -v
+    if dt == "bf16":
+        b = W.f64_to_bf16_bits(x)
+        return b, to_gpu_bf16(b, pad)
+    f = x.astype(np.float32)
+    if not spread:
+        f = (f * np.float32(1.0 + 2.0**-12)).astype(np.float32)  # full FP32 mantissas
+    return f, to_gpu_f32(f, pad)
+
+
+def _quant(x, fmt, rnd=0, seed=0, counter=0, flags=0, mask=0, amax_value=None, layout=0):
+    rows, cols = x.shape
+    out = mx.empty(fmt, rows, cols, device=dev(), layout=layout)
+    amax = torch.zeros(1, dtype=torch.float32, device=dev())
+    if amax_value is not None:
+        amax.fill_(amax_value)
+        flags |= mx.MX_FLAG_AMAX_GIVEN
+    mx.mx_quantize(x, out, rnd, seed, counter, flags, mask, amax if fmt == mx.MX_NVFP4 else None)
+    torch.cuda.synchronize()
+    return out, amax
+
+
+def _same(got, want, what):
+    assert np.array_equal(got, want), f"{what} differ at {np.argwhere(got != want)[:5]}"
+
+
+# --- ceil rule ----------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(1, 32), (7, 96), (33, 256), (130, 544)])
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("rnd", [0, 1])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_ceil_rule_rows_bit_exact(shape, fmt, rnd, dt):
+    rows, cols = shape
+    seed = rows * 13 + cols + fmt + 5 * rnd
+    x_np, x = _inputs(rows, cols, dt, seed, pad=16 if rows % 2 else 0, spread=True)
+    out, _ = _quant(x, fmt, rnd, seed, 11, mx.MX_FLAG_SCALE_CEIL)
+    c, s, _ = host(out)
+    wc, ws, _ = oracle.quantize(x_np, fmt, rnd, seed, 11, variant=oracle.V_CEIL)
+    _same(s, ws, "scales")
+    _same(c, wc, "codes")
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("rnd,rht", [(0, False), (1, False), (0, True)])
+def test_ceil_rule_tiled_bit_exact(fmt, rnd, rht):
+    R, C = 64, 2048
+    x_np, x = _inputs(R, C, "bf16", 7 + fmt, spread=True)
+    mask = oracle.rht_signs(3) if rht else 0
+    flags = mx.MX_FLAG_SCALE_CEIL | (mx.MX_FLAG_RHT16 if rht else 0)
+    out, _ = _quant(x, fmt, rnd, 2, 9, flags, mask, layout=mx.MX_LAYOUT_TILED)
+    c, s, _ = host(out)
+    rb = C if fmt == 1 else C // 2
+    wc, ws, _ = oracle.quantize(x_np, fmt, rnd, 2, 9, rht=rht, sign_mask=mask, variant=oracle.V_CEIL)
+    _same(untile_scales(s, R, C // 32), ws, "scales")
+    _same(untile_codes(c, R, rb), wc, "codes")
+
+
+# --- Four Over Six -----------------------------------------------------------
+@pytest.mark.parametrize("shape", [(1, 16), (7, 96), (33, 256), (130, 544), (257, 1040)])
+@pytest.mark.parametrize("rht", [False, True])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_four_over_six_bit_exact(shape, rht, dt):
+    rows, cols = shape
+    seed = rows * 7 + cols + int(rht)
+    x_np, x = _inputs(rows, cols, dt, seed, pad=8 if rows % 2 else 0)
+    mask = oracle.rht_signs(seed)
+    flags = mx.MX_FLAG_FOUR_OVER_SIX | (mx.MX_FLAG_RHT16 if rht else 0)
+    out, amax = _quant(x, 3, 0, 0, 0, flags, mask)
+    c, s, ts = host(out)
+    wc, ws, wts = oracle.quantize(x_np, 3, 0, rht=rht, sign_mask=mask, variant=oracle.V_FOUR6)
+    assert float(ts[0]) == wts
+    _same(s, ws, "scales")
+    _same(c, wc, "codes")
+
+
+def test_four_over_six_worked_blocks_and_given_amax():
+    """The hand-worked blocks (S = 1 through a given amax of 2688) and an
+    all-zero tensor."""
+    x = np.zeros((2, 64), np.float32)
+    x[:, 0:16] = 48.0
+    x[:, 0] = 64.0
+    x[:, 16:32] = 16.0
+    x[:, 16] = 96.0
+    x[:, 32] = 12.0
+    x[:, 33] = 6.0
+    x[1] *= -0.5
+    out, _ = _quant(to_gpu_f32(x), 3, flags=mx.MX_FLAG_FOUR_OVER_SIX, amax_value=2688.0)
+    c, s, ts = host(out)
+    wc, ws, wts = oracle.quantize(x, 3, amax=2688.0, variant=oracle.V_FOUR6)
+    assert float(ts[0]) == wts == 1.0
+    _same(s, ws, "scales")
+    _same(c, wc, "codes")
+    assert s[0, 0] == 0x58 and s[0, 1] == 0x58 and s[0, 2] == 0x40
+    z = torch.zeros(16, 64, dtype=torch.bfloat16, device=dev())
+    out, _ = _quant(z, 3, flags=mx.MX_FLAG_FOUR_OVER_SIX)
+    c, s, ts = host(out)
+    assert float(ts[0]) == 1.0 and not c.any() and not s.any()
+
+
+# --- 2-D blocks ----------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(1, 16), (16, 128), (53, 208), (64, 256), (130, 1040), (257, 2048)])
+@pytest.mark.parametrize("rnd", [0, 1])
+@pytest.mark.parametrize("rht", [False, True])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_2d_blocks_bit_exact(shape, rnd, rht, dt):
+    rows, cols = shape
+    seed = rows * 3 + cols + 2 * rnd + int(rht)
+    x_np, x = _inputs(rows, cols, dt, seed, pad=16 if rows % 2 else 0)
+    mask = oracle.rht_signs(seed + 2)
+    flags = mx.MX_FLAG_BLOCK_2D | (mx.MX_FLAG_RHT16 if rht else 0)
+    out, amax = _quant(x, 3, rnd, seed, 4, flags, mask)
+    c, s, ts = host(out)
+    wc, ws, wts = oracle.quantize(x_np, 3, rnd, seed, 4, rht=rht, sign_mask=mask,
+                                  variant=oracle.V_2D)
+    assert float(ts[0]) == wts
+    _same(s, ws, "scales")
+    _same(c, wc, "codes")
+
+
+def test_2d_blocks_transpose_consistency_on_gpu():
+    """Quantizing W and W^T with 2-D blocks gives transposed decoded values."""
+    bits = W.normal_bf16(256, 384, 0.02, 6, 52, outlier_entries=0.002, outlier_mult=30.0)
+    w = to_gpu_bf16(bits)
+    wt = w.t().contiguous()
+    q, _ = _quant(w, 3, flags=mx.MX_FLAG_BLOCK_2D)
+    qt, _ = _quant(wt, 3, flags=mx.MX_FLAG_BLOCK_2D)
+    y = torch.empty(256, 384, dtype=torch.float32, device=dev())
+    yt = torch.empty(384, 256, dtype=torch.float32, device=dev())
+    mx.mx_dequantize(q, y)
+    mx.mx_dequantize(qt, yt)
+    torch.cuda.synchronize()
+    assert torch.equal(y.t().contiguous().view(torch.int32), yt.view(torch.int32))
+
+
+# --- benchmark sizes -------------------------------------------------------------
+def test_four_over_six_moe_activations_full_size():
+    """The MoE activation tensor (4096 tokens x 7168, N(0,1)) with Four Over Six."""
+    bits = W.normal_bf16(4096, 7168, 1.0, 0, 60)
+    out, _ = _quant(to_gpu_bf16(bits), 3, flags=mx.MX_FLAG_FOUR_OVER_SIX)
+    c, s, ts = host(out)
+    wc, ws, wts = oracle.quantize(bits, 3, variant=oracle.V_FOUR6)
+    assert float(ts[0]) == wts
+    _same(s, ws, "scales")
+    _same(c, wc, "codes")
+
+
+def test_2d_blocks_expert_weights_full_size():
+    """One expert's weight matrix (2048 x 7168, N(0, 0.02^2)) with 2-D blocks."""
+    bits = W.normal_bf16(2048, 7168, 0.02, 0, 61)
+    out, _ = _quant(to_gpu_bf16(bits), 3, flags=mx.MX_FLAG_BLOCK_2D)
+    c, s, ts = host(out)
+    wc, ws, wts = oracle.quantize(bits, 3, variant=oracle.V_2D)
+    assert float(ts[0]) == wts
+    _same(s, ws, "scales")
+    _same(c, wc, "codes")
+
+
+def test_ceil_rule_mxfp4_tiled_full_size():
+    """The GEMM benchmark's activation operand (4096 x 4096, tile layout) under
+    the ceil rule."""
+    bits = W.normal_bf16(4096, 4096, 1.0, 0, 62, outlier_entries=0.001, outlier_mult=50.0)
+    out, _ = _quant(to_gpu_bf16(bits), 2, flags=mx.MX_FLAG_SCALE_CEIL, layout=mx.MX_LAYOUT_TILED)
+    c, s, _ = host(out)
+    wc, ws, _ = oracle.quantize(bits, 2, variant=oracle.V_CEIL)
+    _same(untile_scales(s, 4096, 128), ws, "scales")
+    _same(untile_codes(c, 4096, 2048), wc, "codes")
