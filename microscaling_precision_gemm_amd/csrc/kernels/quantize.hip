@@ -333,7 +333,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx_tiled(QuantArgs a, int64_
       *reinterpret_cast<uint32_t*>(cbase + (t >> 2) * 4096 + (t & 3) * 1024) = enc[t].w[0];
   }
   // Scales: block 32 G + 2 T + k/4 of the row is byte T of the word at
-  // ((k/4) * 32 + r) * 16 in scale tile G of the row tile.
+  // ((k/4) * 32 + r) * 16 in scale tile G of the row tile.  (Restaging the
+  // 4 waves' parts through LDS into whole 16-byte words measured slower: the
+  // workgroup barrier costs more than the 4-byte stores.)
   if ((k & 3u) == 0) {
     uint32_t w[NT / 4];
 #pragma unroll
@@ -399,12 +401,20 @@ __device__ inline void encode_nv(const QuantArgs& a, float S, float d, int64_t q
 // of the pair accumulates its 8 elements with fused multiply-adds from
 // element 0, then the pair's two partial sums are added, so the choice is a
 // reproducible function of the input.  Round-to-nearest only.
+// The 8 codes are decoded by the hardware conversion (scale 1: exact), two
+// per instruction, byte b giving elements 2b (low nibble) and 2b + 1.
 __device__ inline float nv_sq_err(const float v[8], uint32_t w, float dsb, float S) {
 #pragma clang fp contract(off)
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  v2f q[4];
+  q[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  q[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  q[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  q[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float xh = (e2m1_value((w >> (4 * i)) & 0xFu) * dsb) * S;  // first product exact
+    const float xh = (q[i >> 1][i & 1] * dsb) * S;  // first product exact
     const float d = v[i] - xh;
     acc = __builtin_fmaf(d, d, acc);
   }
@@ -484,12 +494,15 @@ __global__ void k_nv_scale_only(const float* amax, float* tensor_scale) {
 // 16 rows x 16 columns, from the tile's max |x| (the last band of rows may be
 // shorter), stored in each of the tile's rows so the tensor keeps the
 // ordinary row layout; elements are encoded as in the 1-D quantizer.
-// One wave per band of 16 rows x 128 columns: lane 8 i + k holds chunk k
-// (8 elements) of rows i and i + 8 of each 64-column half, so each load
-// instruction reads 8 rows x 128 contiguous bytes (BF16).  A tile is the 16
-// lanes with the same k >> 1 over both row halves: the in-lane max over the
+// One wave per band of 16 rows x 64 k2dGroups columns: lane 8 i + k holds
+// chunk k (8 elements) of rows i and i + 8 of each 64-column group, so each
+// load instruction reads 8 rows x 128 contiguous bytes (BF16) and a wave
+// writes 32 k2dGroups contiguous code bytes per row.  A tile is the 16 lanes
+// with the same k >> 1 over both row halves: the in-lane max over the
 // halves, then lane exchanges at distance 1, 8, 16 and 32.
-constexpr int k2dCols = 128;
+constexpr int k2dGroups = 4;  // measured: 2 groups (64-byte code runs) ran at the same speed
+constexpr int k2dCols = 64 * k2dGroups;
+constexpr int k2dLoads = 2 * k2dGroups;
 
 template <int XDT, bool SR, bool RHT>
 __global__ __launch_bounds__(kThreads) void k_quant_nvfp4_2d(QuantArgs a, int64_t nwaves,
@@ -502,12 +515,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4_2d(QuantArgs a, int64_
   const int64_t G = wave - band * groups_per_band;
   const uint32_t i = lane >> 3, k = lane & 7u;
   const int64_t rows = a.rows, cols = a.cols;
-  // load u: row half h = u & 1, column half c = u >> 1
-  int64_t row[4], col[4];
-  bool ok[4];
-  Raw<XDT> raw[4];
+  // load u: row half h = u & 1, column group c = u >> 1
+  int64_t row[k2dLoads], col[k2dLoads];
+  bool ok[k2dLoads];
+  Raw<XDT> raw[k2dLoads];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < k2dLoads; ++u) {
     row[u] = band * 16 + 8 * (u & 1) + i;
     col[u] = G * k2dCols + 64 * (u >> 1) + 8 * k;
     ok[u] = row[u] < rows && col[u] < cols;
@@ -519,17 +532,19 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4_2d(QuantArgs a, int64_
   const float S = (T == 0.0f) ? 1.0f : T / 2688.0f;
   if (wave == 0 && lane == 0) *a.tensor_scale = S;
   const float d = 6.0f * S;
-  float v[4][8];
-  uint32_t m[2] = {0u, 0u};
+  float v[k2dLoads][8];
+  uint32_t m[k2dGroups];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int c = 0; c < k2dGroups; ++c) m[c] = 0u;
+#pragma unroll
+  for (int u = 0; u < k2dLoads; ++u) {
     widen<XDT>(raw[u], v[u]);
     if constexpr (RHT) rht_forward(v[u], a.sign_mask, k & 1u);
     const uint32_t b = ok[u] ? max_abs_bits(v[u]) : 0u;
     m[u >> 1] = b > m[u >> 1] ? b : m[u >> 1];
   }
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < k2dGroups; ++c) {
     uint32_t t = m[c];
     uint32_t o = dpp_xor1(t);
     t = o > t ? o : t;
@@ -541,8 +556,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4_2d(QuantArgs a, int64_
     m[c] = o > t ? o : t;
   }
   const int64_t spr = cols >> 4;  // scale bytes per row
+  // Full groups (cols a multiple of 64 k2dGroups): every chunk of the wave
+  // is in range column-wise and the wave's code bytes of a row are one
+  // 32 k2dGroups-byte run, its scale bytes one 4 k2dGroups-byte run.
+  const bool full = (cols % k2dCols) == 0;
+  uint32_t w[k2dLoads], sw[k2dLoads];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < k2dLoads; ++u) {
     const uint32_t sb = e4m3_rne_mag(u2f(m[u >> 1]) / d);
     const float dsb = e4m3_mag_value(sb);
     float rcp = 0.0f;
@@ -553,29 +573,50 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4_2d(QuantArgs a, int64_
     float y[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = v[u][j] * rcp;
-    uint32_t w;
     if constexpr (!SR) {
-      w = pack_e2m1_rne(y);
+      w[u] = pack_e2m1_rne(y);
     } else {
       uint32_t r[8];
       rand16x8(a.seed, a.counter, (uint64_t)((row[u] * cols + col[u]) >> 3), r);
-      w = 0u;
+      w[u] = 0u;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) w |= e2m1_encode(y[j], true, r[j]) << (4 * j);
+      for (int j = 0; j < 8; ++j) w[u] |= e2m1_encode(y[j], true, r[j]) << (4 * j);
     }
-    if (ok[u]) *reinterpret_cast<uint32_t*>(a.codes + row[u] * (cols >> 1) + (col[u] >> 1)) = w;
-    // Scale bytes: lane 8 i + 2 p holds block p of its row's 64-column half.
-    // With a multiple of 4 blocks per row the half's 4 blocks are all valid
-    // and 4-byte aligned (one 32-bit store); otherwise one byte per block.
+    // lane 8 i + 2 p holds block p of its row's 64-column group: gather the
+    // group's 4 scale bytes into lane 8 i
     const uint32_t s1 = lane_read(sb, lane + 2u), s2 = lane_read(sb, lane + 4u),
                    s3 = lane_read(sb, lane + 6u);
-    if (ok[u]) {
+    sw[u] = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
+    if (!full && ok[u]) {
+      *reinterpret_cast<uint32_t*>(a.codes + row[u] * (cols >> 1) + (col[u] >> 1)) = w[u];
       uint8_t* sp = a.scales + row[u] * spr + (col[u] >> 4);
       if ((spr & 3) == 0) {
-        if (k == 0u) *reinterpret_cast<uint32_t*>(sp) = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
+        if (k == 0u) *reinterpret_cast<uint32_t*>(sp) = sw[u];
       } else if ((k & 1u) == 0u) {
         *sp = (uint8_t)sb;
       }
+    }
+  }
+  if (!full) return;
+  // Full groups: the codes are restaged through LDS so that every store
+  // instruction writes 8 rows x 128 contiguous bytes, and lane 8 i stores its
+  // row's scale run with one 16-byte store.  Each wave uses its own 2 KB of
+  // LDS; LDS operations of one wave complete in order.
+  static_assert(k2dGroups == 4, "the restaging assumes 128 code bytes per row");
+  __shared__ uint32_t stage[kThreads / 64][16][32];
+  uint32_t (*st)[32] = stage[threadIdx.x >> 6];
+#pragma unroll
+  for (int u = 0; u < k2dLoads; ++u) st[8 * (u & 1) + i][8 * (u >> 1) + k] = w[u];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t r = band * 16 + 8 * h + i;
+    const uint4 q = *reinterpret_cast<const uint4*>(&st[8 * h + i][4 * k]);
+    if (r < rows) {
+      *reinterpret_cast<uint4*>(a.codes + r * (cols >> 1) + G * (k2dCols / 2) + 16 * k) = q;
+      if (k == 0u)
+        *reinterpret_cast<uint4*>(a.scales + r * spr + G * (k2dCols / 16)) =
+            make_uint4(sw[h], sw[2 + h], sw[4 + h], sw[6 + h]);
     }
   }
 }
