@@ -280,6 +280,24 @@ def detail(torch, mx, W, args):
     ms = time_fn(torch, lambda: mx.mx_gemm(q4a, q4b, C), it, wu)
     res["mxfp4_gemm_4096_rows_layout"] = {"ms": ms, "tflops": 2 * M * N * K / ms / 1e9,
                                           "frac_fp4_peak": 2 * M * N * K / ms / 1e9 / PEAK_TFLOPS["fp4"]}
+    # fused quantize-and-GEMM: the 4096^3 MXFP4 product written as MXFP4 (tile layout) by the
+    # GEMM's epilogue, against the product written in BF16 and quantized by a second kernel
+    q4at, q4bt = mx.empty(2, M, K, layout=mx.MX_LAYOUT_TILED), mx.empty(2, N, K, layout=mx.MX_LAYOUT_TILED)
+    mx.mx_quantize(a, q4at)
+    mx.mx_quantize(b, q4bt)
+    q4c = mx.empty(2, M, N, layout=mx.MX_LAYOUT_TILED)
+    ms_fr = time_fn(torch, lambda: mx.mx_gemm_quantize(q4at, q4bt, q4c), it, wu)
+    ms_fs = time_fn(torch, lambda: mx.mx_gemm_quantize(q4at, q4bt, q4c, mx.MX_SR, 1, 0), it, wu)
+
+    def two_step(rnd):
+        mx.mx_gemm(q4at, q4bt, C)
+        mx.mx_quantize(C, q4c, rnd, 1, 0)
+    ms_tr = time_fn(torch, lambda: two_step(mx.MX_RNE), it, wu)
+    ms_ts = time_fn(torch, lambda: two_step(mx.MX_SR), it, wu)
+    res["mxfp4_gemm_quantize_4096_fused"] = {
+        "fused_rne_ms": ms_fr, "fused_rne_tflops": 2 * M * N * K / ms_fr / 1e9, "two_step_rne_ms": ms_tr,
+        "fused_sr_ms": ms_fs, "two_step_sr_ms": ms_ts}
+    del q4at, q4bt, q4c
     # MXFP4 tile-layout quantize of the activation operand, floor and ceil scale rules
     q4t = mx.empty(2, M, K, layout=mx.MX_LAYOUT_TILED)
     by4 = M * K * (2 + 0.5 + 1 / 32)

@@ -251,6 +251,25 @@ mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, 
 mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,
                      uint32_t flags, mx_stream stream);
 
+/* Block-scaled GEMM whose product leaves the kernel already quantized
+ * ([MXF] "Open points": fused quantize-and-GEMM kernels, since computing block
+ * scales is memory traffic of its own).  C = A * B^T [M, N] as mx_gemm_ex
+ * computes it in FP32 (tile-layout operands: MXFP4, or MXFP8 with
+ * MX_GEMM_FP8_NATIVE and that flag's bound), then quantized along its rows
+ * exactly as mx_quantize quantizes an FP32 matrix: 32-column blocks, E8M0
+ * floor rule (or MX_FLAG_SCALE_CEIL), rounding rnd, SR draws indexed by the
+ * element's row-major position in C.  The FP32 product is never stored: since
+ * it is fixed only to within the GEMM's bound, codes and scales are too (a
+ * value near a rounding or scale boundary may land on either side).
+ * `out` is MXFP8 or MXFP4 with rows = M and cols = N, in the row layout or
+ * the tile layout (then M % 32 == 0 and N % 1024 == 0), so it can be the A
+ * operand of the next product.  flags: MX_GEMM_FP8_NATIVE,
+ * MX_FLAG_SCALE_CEIL; anything else returns MX_ERR_UNSUPPORTED, as do
+ * row-layout operands and an NVFP4 output (its tensor scale needs the whole
+ * product first). */
+mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, const mx_tensor* out,
+                           int32_t rnd, mx_rng rng, uint32_t flags, mx_stream stream);
+
 /* Grouped NVFP4 GEMM for a mixture-of-experts forward pass ([MXF] "NVFP4";
  * [INK] "A precision choice for each stage": NVFP4 forward in the expert
  * layers).  B stacks num_groups expert matrices [N, K] as one NVFP4 tensor of

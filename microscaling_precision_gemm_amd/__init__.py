@@ -29,7 +29,7 @@ FORMATS = {"mxfp8": MX_MXFP8_E4M3, "mxfp4": MX_MXFP4_E2M1, "nvfp4": MX_NVFP4}
 EXPORTED = [
     "mx_codes_bytes", "mx_scales_bytes", "mx_rht_signs", "mx_quantize", "mx_amax",
     "mx_dequantize", "mx_requant_transpose", "mx_hadamard16", "mx_gemm", "mx_gemm_ex",
-    "mx_gemm_grouped",
+    "mx_gemm_grouped", "mx_gemm_quantize",
     "mx_status_string",
 ]
 
@@ -74,6 +74,7 @@ def load():
         "mx_gemm": (i32, [TP, TP, vp, i32, i64, vp]),
         "mx_gemm_ex": (i32, [TP, TP, vp, i32, i64, u32, vp]),
         "mx_gemm_grouped": (i32, [TP, vp, i64, TP, i32, vp, vp, i32, i64, vp]),
+        "mx_gemm_quantize": (i32, [TP, TP, TP, i32, _Rng, u32, vp]),
         "mx_status_string": (ctypes.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -236,6 +237,18 @@ def mx_gemm_ex(A: MXTensor, B: MXTensor, C, flags: int = 0, stream=None):
     _check(L.mx_gemm_ex(ctypes.byref(da), ctypes.byref(db), _ptr(C), _dt(C), C.stride(0), flags,
                         _stream(stream)))
     return C
+
+
+def mx_gemm_quantize(A: MXTensor, B: MXTensor, out: MXTensor, rnd: int = MX_RNE, seed: int = 0,
+                     counter: int = 0, flags: int = 0, stream=None) -> MXTensor:
+    """C = A * B^T (tile-layout MX operands) written quantized into `out`
+    (MXFP8 or MXFP4, [M, N], row or tile layout) by the GEMM's epilogue.
+    flags: MX_GEMM_FP8_NATIVE (MXFP8 operands), MX_FLAG_SCALE_CEIL."""
+    L = load()
+    da, db, do = A.desc(), B.desc(), out.desc()
+    _check(L.mx_gemm_quantize(ctypes.byref(da), ctypes.byref(db), ctypes.byref(do), rnd,
+                              _Rng(seed, counter), flags, _stream(stream)))
+    return out
 
 
 def mx_gemm_grouped(A: MXTensor, row_index, routed_rows: int, B: MXTensor, num_groups: int,

@@ -250,6 +250,32 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
   }
 }
 
+mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, const mx_tensor* out,
+                           int32_t rnd, mx_rng rng, uint32_t flags, mx_stream stream) {
+  if (!A || !B || !out) return MX_ERR_NULL;
+  if (rnd != MX_RNE && rnd != MX_SR) return MX_ERR_FORMAT;
+  if (flags & ~(MX_GEMM_FP8_NATIVE | MX_FLAG_SCALE_CEIL)) return MX_ERR_UNSUPPORTED;
+  mx_status st = check_tensor(A, A->rows, A->cols);
+  if (st != MX_OK) return st;
+  st = check_tensor(B, B->rows, B->cols);
+  if (st != MX_OK) return st;
+  if (A->fmt != B->fmt || A->layout != MX_LAYOUT_TILED || B->layout != MX_LAYOUT_TILED)
+    return MX_ERR_UNSUPPORTED;
+  if (A->fmt == MX_MXFP8_E4M3 ? !(flags & MX_GEMM_FP8_NATIVE) : (flags & MX_GEMM_FP8_NATIVE) != 0)
+    return MX_ERR_UNSUPPORTED;
+  if (A->cols != B->cols) return MX_ERR_SHAPE;
+  const int64_t M = A->rows, N = B->rows, K = A->cols;
+  st = check_tensor(out, M, N);
+  if (st != MX_OK) return st;
+  if (out->fmt == MX_NVFP4) return MX_ERR_UNSUPPORTED;
+  if (M * N == 0) return MX_OK;
+  return hip_status(mxk::launch_gemm_mx_tiled_quant(
+      A->fmt, static_cast<const uint8_t*>(A->codes), A->scales,
+      static_cast<const uint8_t*>(B->codes), B->scales, M, N, K, out->fmt,
+      out->layout == MX_LAYOUT_TILED, static_cast<uint8_t*>(out->codes), out->scales, rnd == MX_SR,
+      rng.seed, rng.counter, (flags & MX_FLAG_SCALE_CEIL) != 0, reinterpret_cast<hipStream_t>(stream)));
+}
+
 mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,
                   mx_stream stream) {
   return mx_gemm_ex(A, B, C, cdt, ldc, 0u, stream);

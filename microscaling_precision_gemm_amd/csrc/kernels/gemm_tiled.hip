@@ -28,6 +28,8 @@
 
 #include "../device/codec.h"
 #include "../device/gemm_common.h"
+#include "../device/mxenc.h"
+#include "../device/wave.h"
 #include "../launch.h"
 
 namespace mxk {
@@ -125,19 +127,14 @@ __device__ inline void run_group(const gptr (&base)[8], uint32_t g, uint32_t ste
   }
 }
 
-template <int FMT, int CDT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx_tiled(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, void* __restrict__ C,
-    int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t vec) {
+// The main loop: the accumulators of this wave's 128x128 part of the C tile
+// at (m0, n0).
+template <int FMT>
+__device__ inline void tiled_mainloop(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
+                                      const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB,
+                                      int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
+                                      uint32_t wm, uint32_t wn, uint32_t lane, v16f (&acc)[4][4]) {
   using TC = TCfg<FMT>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint32_t tmi, tni;
-  tile_of(blockIdx.x, tiles_m, tiles_n, &tmi, &tni);
-  const int64_t m0 = (int64_t)tmi * 256, n0 = (int64_t)tni * 256;
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t wm = wid >> 1, wn = wid & 1u;
   const uint32_t steps = (uint32_t)((FMT == FMT_MXFP8 ? K : K / 2) / 128);  // code tiles per row tile
   const uint32_t groups = (uint32_t)(K / 1024);
   const uint32_t lane16 = lane * 16u;
@@ -159,7 +156,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     sb[t] = (gptr)uniform_u64(d);
   }
 
-  v16f acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -187,7 +183,181 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // the clamped reloads of the last step are still in flight: let them land
   __builtin_amdgcn_s_waitcnt((0 & 15) | (0 << 14) | (7 << 4) | (15 << 8));  // vmcnt(0)
+}
+
+template <int FMT, int CDT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx_tiled(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, void* __restrict__ C,
+    int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t vec) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint32_t tmi, tni;
+  tile_of(blockIdx.x, tiles_m, tiles_n, &tmi, &tni);
+  const int64_t m0 = (int64_t)tmi * 256, n0 = (int64_t)tni * 256;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t wm = wid >> 1, wn = wid & 1u;
+  v16f acc[4][4];
+  tiled_mainloop<FMT>(A, SA, B, SB, M, N, K, m0, n0, wm, wn, lane, acc);
   store_tile<CDT>(smem, acc, C, ldc, M, N, m0 + wm * 128, n0 + wn * 128, vec != 0, wid, lane);
+}
+
+// ---- GEMM with its output quantized (fused quantize-and-GEMM) --------------
+// "Microscaling (MX) and block-scaled 4-bit formats", section "Open points":
+// fused quantize-and-GEMM kernels, because computing block scales is memory
+// traffic of its own.  The output C = A * B^T is not written in 16 or 32 bits:
+// each wave stages its FP32 accumulators through LDS (as the FP32 epilogue
+// does), reads 8 consecutive columns of a row per lane -- a lane quad is one
+// 32-column block -- and runs the quantizer's block encoder on them, so the
+// result is what the MX quantizer makes of the FP32 product matrix, and the
+// codes and scales go straight to their layout (row-major, or the
+// matrix-instruction tile layout, ready to be the next product's operand).
+// The random stream of SR is indexed by the element's row-major position in
+// C, as for a quantizer call on C.
+template <int OFMT, bool SR, bool OTILED>
+__device__ inline void store_tile_quant(uint8_t* __restrict__ smem, const v16f (&acc)[4][4],
+                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                        int64_t M, int64_t N, int64_t r0, int64_t c0, uint32_t wid,
+                                        uint32_t lane, const MxEnc& enc) {
+  constexpr int PITCH = 128 * 4 + 16;  // FP32 rows, as the FP32 epilogue
+  uint8_t* W = smem + wid * (64 * PITCH);
+  const uint32_t lr = lane & 31u, lg = lane >> 5;
+  const uint32_t ch = lane & 15u;  // 8-column chunk of the wave tile's row
+  const int64_t row_bytes = OFMT == FMT_MXFP8 ? N : N >> 1;
+  const int64_t spr = N >> 5;  // scale bytes per row
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) {
+      const int i = 2 * h + i2;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t row = i2 * 32 + 8 * (v / 4) + 4 * lg + (v % 4);
+          *reinterpret_cast<float*>(W + row * PITCH + (j * 32 + lr) * 4) = acc[i][j][v];
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // own LDS writes done
+    asm volatile("" ::: "memory");
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t row = 4 * k + (lane >> 4);
+      const u4 lo = *reinterpret_cast<const u4*>(W + row * PITCH + ch * 32);
+      const u4 hi = *reinterpret_cast<const u4*>(W + row * PITCH + ch * 32 + 16);
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = u2f(lo[e]);
+        v[4 + e] = u2f(hi[e]);
+      }
+      const int64_t grow = r0 + h * 64 + row;
+      const int64_t gcol = c0 + 8 * ch;
+      Enc<OFMT> e;
+      encode_mx<OFMT, SR>(enc, (grow * N + gcol) >> 3, v, e);
+      // the scale bytes of the row's 4 blocks, gathered in its first lane
+      const uint32_t s1 = lane_read(e.sc, lane + 4u), s2 = lane_read(e.sc, lane + 8u),
+                     s3 = lane_read(e.sc, lane + 12u);
+      if (grow < M && gcol < N) {  // N % 32 == 0: a block is all in or all out
+        if constexpr (!OTILED) {
+          if constexpr (OFMT == FMT_MXFP8)
+            *reinterpret_cast<uint2*>(codes + grow * row_bytes + gcol) = make_uint2(e.w[0], e.w[1]);
+          else
+            *reinterpret_cast<uint32_t*>(codes + grow * row_bytes + (gcol >> 1)) = e.w[0];
+          // one 32-bit store of the row's 4 blocks when they are all in range
+          // and 4-byte aligned, else one byte per block
+          const bool wide = (spr & 3) == 0 && c0 + 128 <= N;
+          if (wide ? ch == 0 : (ch & 3u) == 0) {
+            uint8_t* sp = scales + grow * spr + (gcol >> 5);
+            if (wide) *reinterpret_cast<uint32_t*>(sp) = e.sc | (s1 << 8) | (s2 << 16) | (s3 << 24);
+            else *sp = (uint8_t)e.sc;
+          }
+        } else {
+          // tile layout (M % 32 == 0, N % 1024 == 0): code byte b of the row
+          // is byte b % 16 of chunk (b % 128) / 16 of code tile b / 128
+          const int64_t T = grow >> 5;
+          const uint32_t r = (uint32_t)grow & 31u;
+          const int64_t b = OFMT == FMT_MXFP8 ? gcol : gcol >> 1;
+          const uint32_t c = (uint32_t)(b & 127) >> 4;
+          uint8_t* cp = codes + (T * (row_bytes >> 7) + (b >> 7)) * 4096 + (c >> 1) * 1024u +
+                        ((c & 1u) * 32u + r) * 16u + (uint32_t)(b & 15);
+          if constexpr (OFMT == FMT_MXFP8)
+            *reinterpret_cast<uint2*>(cp) = make_uint2(e.w[0], e.w[1]);
+          else
+            *reinterpret_cast<uint32_t*>(cp) = e.w[0];
+          // block bi of the row: byte bi / 2 % 16 of the word ((bi % 2) * 32 + r)
+          // in scale tile bi / 32
+          if ((ch & 3u) == 0) {
+            const int64_t bi = gcol >> 5;
+            const uint32_t bb = (uint32_t)(bi & 31);
+            scales[(T * (N >> 10) + (bi >> 5)) * 1024 + ((bb & 1u) * 32u + r) * 16u + (bb >> 1)] =
+                (uint8_t)e.sc;
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // reads done before reuse
+    asm volatile("" ::: "memory");
+  }
+}
+
+template <int FMT, int OFMT, bool SR, bool OTILED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx_tiled_q(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, MxEnc enc, uint32_t tiles_m, uint32_t tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint32_t tmi, tni;
+  tile_of(blockIdx.x, tiles_m, tiles_n, &tmi, &tni);
+  const int64_t m0 = (int64_t)tmi * 256, n0 = (int64_t)tni * 256;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t wm = wid >> 1, wn = wid & 1u;
+  v16f acc[4][4];
+  tiled_mainloop<FMT>(A, SA, B, SB, M, N, K, m0, n0, wm, wn, lane, acc);
+  store_tile_quant<OFMT, SR, OTILED>(smem, acc, codes, scales, M, N, m0 + wm * 128, n0 + wn * 128, wid,
+                                     lane, enc);
+}
+
+// Raise a kernel's dynamic LDS limit once per device, so later launches (also
+// inside HIP graphs) make no call beyond the launch itself.
+inline hipError_t ensure_smem(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    done.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  return hipSuccess;
+}
+
+template <int FMT, int OFMT, bool SR, bool OTILED>
+hipError_t launch_q(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, int64_t M,
+                    int64_t N, int64_t K, uint8_t* codes, uint8_t* scales, const MxEnc& enc,
+                    hipStream_t s) {
+  const uint32_t tm = (uint32_t)((M + 255) / 256), tn = (uint32_t)((N + 255) / 256);
+  constexpr int kEpiBytes = 4 * 64 * (128 * 4 + 16);
+  auto kern = k_gemm_mx_tiled_q<FMT, OFMT, SR, OTILED>;
+  static std::atomic<uint64_t> attr_done{0};
+  const hipError_t e = ensure_smem((const void*)kern, kEpiBytes, attr_done);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(256), kEpiBytes, s, a, sa, b, sb, M, N, K, codes, scales, enc,
+                     tm, tn);
+  return hipGetLastError();
+}
+
+template <int FMT, int OFMT>
+hipError_t launch_q_d(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, int64_t M,
+                      int64_t N, int64_t K, uint8_t* codes, uint8_t* scales, const MxEnc& enc, bool sr,
+                      bool otiled, hipStream_t s) {
+  if (sr)
+    return otiled ? launch_q<FMT, OFMT, true, true>(a, sa, b, sb, M, N, K, codes, scales, enc, s)
+                  : launch_q<FMT, OFMT, true, false>(a, sa, b, sb, M, N, K, codes, scales, enc, s);
+  return otiled ? launch_q<FMT, OFMT, false, true>(a, sa, b, sb, M, N, K, codes, scales, enc, s)
+                : launch_q<FMT, OFMT, false, false>(a, sa, b, sb, M, N, K, codes, scales, enc, s);
 }
 
 template <int FMT, int CDT>
@@ -215,6 +385,22 @@ hipError_t launch_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const
 }
 
 }  // namespace
+
+hipError_t launch_gemm_mx_tiled_quant(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                                      const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                      int64_t N, int64_t K, int ofmt, bool otiled, uint8_t* codes,
+                                      uint8_t* scales, bool sr, uint64_t seed, uint64_t counter,
+                                      bool ceil, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const MxEnc enc{ceil, seed, counter};
+  if (fmt == FMT_MXFP8)
+    return ofmt == FMT_MXFP8
+               ? launch_q_d<FMT_MXFP8, FMT_MXFP8>(a_codes, a_scales, b_codes, b_scales, M, N, K, codes, scales, enc, sr, otiled, s)
+               : launch_q_d<FMT_MXFP8, FMT_MXFP4>(a_codes, a_scales, b_codes, b_scales, M, N, K, codes, scales, enc, sr, otiled, s);
+  return ofmt == FMT_MXFP8
+             ? launch_q_d<FMT_MXFP4, FMT_MXFP8>(a_codes, a_scales, b_codes, b_scales, M, N, K, codes, scales, enc, sr, otiled, s)
+             : launch_q_d<FMT_MXFP4, FMT_MXFP4>(a_codes, a_scales, b_codes, b_scales, M, N, K, codes, scales, enc, sr, otiled, s);
+}
 
 hipError_t launch_gemm_mx_tiled(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                                 const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,

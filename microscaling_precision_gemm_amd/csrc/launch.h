@@ -48,6 +48,13 @@ hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scal
                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
                           int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s);
 // A and B in the tiled layout (M, N multiples of 32, K of 1024)
+// C = A * B^T of tile-layout MX operands, written quantized along its rows
+// (MX format ofmt, row or tile layout) by the GEMM's epilogue.
+hipError_t launch_gemm_mx_tiled_quant(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                                      const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                      int64_t N, int64_t K, int ofmt, bool otiled, uint8_t* codes,
+                                      uint8_t* scales, bool sr, uint64_t seed, uint64_t counter,
+                                      bool ceil, hipStream_t s);
 hipError_t launch_gemm_mx_tiled(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                                 const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                 int64_t N, int64_t K, void* C, int cdt, int64_t ldc,

@@ -78,6 +78,7 @@ def lib():
         "mxo_gemm_f64": (None, [c_f64p, c_f64p, i64, i64, i64, ctypes.c_double, c_f64p, c_f64p]),
         "mxo_gemm_f64_sampled": (None, [c_f64p, c_f64p, i64, _P(i64), _P(i64), i64,
                                         ctypes.c_double, c_f64p, c_f64p]),
+        "mxo_encode_elems": (None, [ci, ci, c_f64p, _P(u64), i64, u64, u64, c_u8p]),
         "mxo_codes_bytes": (i64, [ci, i64, i64]),
         "mxo_scales_bytes": (i64, [ci, i64, i64]),
         "mxo_tensor_bytes": (i64, [ci, i64, i64]),
@@ -149,6 +150,18 @@ def philox4x32_10(ctr, key):
 
 def rand16(seed: int, counter: int, n: int) -> int:
     return lib().mxo_rand16(seed, counter, n)
+
+
+def encode_elems(fmt: int, y: np.ndarray, rnd: int = RNE, n=None, seed: int = 0,
+                 counter: int = 0) -> np.ndarray:
+    """Element codes (E4M3 for MXFP8, E2M1 for MXFP4) of the float64 values y,
+    by RNE or by SR with the random value of element index n[t]."""
+    y = np.ascontiguousarray(y, np.float64).ravel()
+    idx = np.zeros(y.size, np.uint64) if n is None else np.ascontiguousarray(n, np.uint64).ravel()
+    out = np.zeros(y.size, np.uint8)
+    lib().mxo_encode_elems(fmt, rnd, _ptr(y, ctypes.c_double), _ptr(idx, ctypes.c_uint64), y.size,
+                           seed, counter, _ptr(out, ctypes.c_uint8))
+    return out
 
 
 def rht_signs(seed: int) -> int:

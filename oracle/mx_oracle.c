@@ -242,6 +242,20 @@ uint32_t mxo_rand16(uint64_t seed, uint64_t counter, uint64_t n) {
   return (word >> (16 * (n & 1))) & 0xFFFFu;
 }
 
+/* Element codes of many values at once: y[t] encoded to E4M3 (elem = 1) or
+ * E2M1 (elem = 2) by round-to-nearest, or by SR with the random value of
+ * element index n[t] of the stream (seed, counter).  A loop over the encoders
+ * and the stream above, for checks that need many encodings. */
+void mxo_encode_elems(int elem, int rnd, const double* y, const uint64_t* n, int64_t count,
+                      uint64_t seed, uint64_t counter, uint8_t* codes) {
+  ensure_tables();
+  const mxo_alphabet* al = elem == MXO_MXFP8 ? &g_e4m3 : &g_e2m1;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < count; ++t)
+    codes[t] = (uint8_t)(rnd == MXO_SR ? encode_sr(al, y[t], mxo_rand16(seed, counter, n[t]))
+                                       : encode_rne(al, y[t]));
+}
+
 /* READING: the 16 random signs of the Hadamard transform are the low 16 bits
  * of word 0 of the Philox call with counter (0, 0, 0, 1), a counter that no
  * element draw uses (element draws keep the top word 0). */

@@ -229,3 +229,21 @@ def test_2d_equal_rows_reduce_to_1d(orc):
     a = orc.quantize(w, orc.NVFP4, variant=orc.V_2D)
     b = orc.quantize(w, orc.NVFP4)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+# --- vectorised element encoder (used by the fused quantize-GEMM checks) -------
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_encode_elems_equals_the_scalar_encoders(orc, fmt, rnd):
+    g = np.random.default_rng(fmt + 2 * rnd)
+    y = g.standard_normal(300) * (100.0 if fmt == 1 else 3.0)
+    y[:4] = [0.0, -0.0, 1e9, -1e9]
+    n = g.integers(0, 1 << 40, 300).astype(np.uint64)
+    got = orc.encode_elems(fmt, y, rnd, n, seed=7, counter=11)
+    if rnd == 0:
+        enc = orc.e4m3_encode_rne if fmt == 1 else orc.e2m1_encode_rne
+        want = [enc(float(v)) for v in y]
+    else:
+        enc = orc.e4m3_encode_sr if fmt == 1 else orc.e2m1_encode_sr
+        want = [enc(float(v), orc.rand16(7, 11, int(k))) for v, k in zip(y, n)]
+    assert list(got) == want
