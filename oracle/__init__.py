@@ -22,6 +22,9 @@ _SRC = os.path.join(_HERE, "mx_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 MXFP8, MXFP4, NVFP4 = 1, 2, 3
+# the other MX element types: INT8 (two's complement, 6 fraction bits; also the
+# block-scaled "S2F6" combine format), FP8 E5M2, FP6 E3M2 and E2M3
+MXINT8, MXFP8_E5M2, MXFP6_E3M2, MXFP6_E2M3 = 4, 5, 6, 7
 RNE, SR = 0, 1
 # quantizer variants (bits)
 V_CEIL, V_FOUR6, V_2D = 1, 2, 4
@@ -60,6 +63,13 @@ def lib():
         "mxo_e2m1_decode": (ctypes.c_double, [u32]),
         "mxo_e4m3_decode": (ctypes.c_double, [u32]),
         "mxo_e8m0_decode": (ctypes.c_double, [u32]),
+        "mxo_e5m2_decode": (ctypes.c_double, [u32]),
+        "mxo_e3m2_decode": (ctypes.c_double, [u32]),
+        "mxo_e2m3_decode": (ctypes.c_double, [u32]),
+        "mxo_int8_decode": (ctypes.c_double, [u32]),
+        "mxo_elem_decode": (ctypes.c_double, [ci, u32]),
+        "mxo_elem_encode_rne": (u32, [ci, ctypes.c_double]),
+        "mxo_elem_encode_sr": (u32, [ci, ctypes.c_double, u32]),
         "mxo_e2m1_encode_rne": (u32, [ctypes.c_double]),
         "mxo_e4m3_encode_rne": (u32, [ctypes.c_double]),
         "mxo_e2m1_encode_sr": (u32, [ctypes.c_double, u32]),
@@ -140,6 +150,19 @@ def e4m3_encode_sr(y: float, r16: int) -> int:
     return lib().mxo_e4m3_encode_sr(y, r16)
 
 
+def elem_decode(fmt: int, code: int) -> float:
+    """Value of one element code of MX format fmt (any MX format above)."""
+    return lib().mxo_elem_decode(fmt, code)
+
+
+def elem_encode_rne(fmt: int, y: float) -> int:
+    return lib().mxo_elem_encode_rne(fmt, y)
+
+
+def elem_encode_sr(fmt: int, y: float, r16: int) -> int:
+    return lib().mxo_elem_encode_sr(fmt, y, r16)
+
+
 def philox4x32_10(ctr, key):
     c = (ctypes.c_uint32 * 4)(*[int(v) & 0xFFFFFFFF for v in ctr])
     k = (ctypes.c_uint32 * 2)(*[int(v) & 0xFFFFFFFF for v in key])
@@ -154,7 +177,7 @@ def rand16(seed: int, counter: int, n: int) -> int:
 
 def encode_elems(fmt: int, y: np.ndarray, rnd: int = RNE, n=None, seed: int = 0,
                  counter: int = 0) -> np.ndarray:
-    """Element codes (E4M3 for MXFP8, E2M1 for MXFP4) of the float64 values y,
+    """Element codes (the element type of MX format fmt) of the float64 values y,
     by RNE or by SR with the random value of element index n[t]."""
     y = np.ascontiguousarray(y, np.float64).ravel()
     idx = np.zeros(y.size, np.uint64) if n is None else np.ascontiguousarray(n, np.uint64).ravel()

@@ -42,6 +42,10 @@
 #define MXO_MXFP8 1
 #define MXO_MXFP4 2
 #define MXO_NVFP4 3
+#define MXO_MXINT8 4      /* 8-bit two's complement, 6 fraction bits (S2F6) */
+#define MXO_MXFP8_E5M2 5
+#define MXO_MXFP6_E3M2 6
+#define MXO_MXFP6_E2M3 7
 #define MXO_RNE 0
 #define MXO_SR 1
 
@@ -86,28 +90,55 @@ double mxo_e8m0_decode(uint32_t code) {
   return ldexp(1.0, (int)code - 127);
 }
 
+/* The other MX element types ([MXF] "The idea" and [FP4] "The OCP
+ * Microscaling (MX) spec" name FP8 E5M2, FP6 E3M2 and E2M3, and INT8 as MX
+ * elements, without their bits).  READING: the OCP definitions --
+ *   E5M2: bias 15, IEEE-style, exponent 31 holds Inf (mantissa 0) and NaN;
+ *         largest finite 57344.
+ *   E3M2: bias 3, no Inf or NaN, largest 28.   E2M3: bias 1, largest 7.5.
+ *   INT8: two's complement with an implied scale 2^-6, so -2 .. 127/64.
+ * The last is also this reading of the block-scaled "S2F6" 8-bit fixed-point
+ * format ([INK] "Why communication became the next bottleneck": 8.25 bits per
+ * value, i.e. 8-bit elements with one 8-bit scale per 32). */
+static double minifloat(uint32_t code, int ebits, int mbits, int bias, int ieee_top) {
+  int s = (code >> (ebits + mbits)) & 1;
+  int e = (code >> mbits) & ((1 << ebits) - 1);
+  int m = code & ((1 << mbits) - 1);
+  double mag;
+  if (ieee_top && e == (1 << ebits) - 1) mag = m ? NAN : INFINITY;
+  else if (e == 0) mag = ldexp((double)m, 1 - bias - mbits);
+  else mag = ldexp(1.0 + ldexp((double)m, -mbits), e - bias);
+  return s ? -mag : mag;
+}
+double mxo_e5m2_decode(uint32_t code) { return minifloat(code & 0xFF, 5, 2, 15, 1); }
+double mxo_e3m2_decode(uint32_t code) { return minifloat(code & 0x3F, 3, 2, 3, 0); }
+double mxo_e2m3_decode(uint32_t code) { return minifloat(code & 0x3F, 2, 3, 1, 0); }
+double mxo_int8_decode(uint32_t code) { return (double)(int8_t)(uint8_t)code / 64.0; }
+
 /* ------------------------------------------------------------------------ */
 /* Alphabets: the non-negative finite values of an element format, sorted,  */
 /* with their codes.  Built by decoding every code.                          */
 /* ------------------------------------------------------------------------ */
 typedef struct {
   int n;
-  double v[128];
-  uint32_t code[128];
-  uint32_t sign_bit;
+  double v[256];
+  uint32_t code[256];
+  uint32_t sign_bit; /* sign-magnitude formats: the sign bit; 0 for two's complement */
+  int twos;          /* two's complement: v holds every value, negative ones included */
 } mxo_alphabet;
 
-static mxo_alphabet g_e2m1, g_e4m3;
+static mxo_alphabet g_e2m1, g_e4m3, g_e5m2, g_e3m2, g_e2m3, g_int8;
 static int g_ready = 0;
 
 static void build_alphabet(mxo_alphabet* a, double (*dec)(uint32_t), int ncodes,
-                           uint32_t sign_bit) {
+                           uint32_t sign_bit, int twos) {
   a->n = 0;
   a->sign_bit = sign_bit;
+  a->twos = twos;
   for (int c = 0; c < ncodes; ++c) {
-    if (c & sign_bit) continue; /* non-negative half only */
+    if (!twos && (c & sign_bit)) continue; /* non-negative half only */
     double v = dec((uint32_t)c);
-    if (isnan(v)) continue;
+    if (isnan(v) || isinf(v)) continue;
     a->v[a->n] = v;
     a->code[a->n] = (uint32_t)c;
     a->n++;
@@ -129,8 +160,12 @@ static void build_alphabet(mxo_alphabet* a, double (*dec)(uint32_t), int ncodes,
 
 static void ensure_tables(void) {
   if (g_ready) return;
-  build_alphabet(&g_e2m1, mxo_e2m1_decode, 16, 0x8);
-  build_alphabet(&g_e4m3, mxo_e4m3_decode, 256, 0x80);
+  build_alphabet(&g_e2m1, mxo_e2m1_decode, 16, 0x8, 0);
+  build_alphabet(&g_e4m3, mxo_e4m3_decode, 256, 0x80, 0);
+  build_alphabet(&g_e5m2, mxo_e5m2_decode, 256, 0x80, 0);
+  build_alphabet(&g_e3m2, mxo_e3m2_decode, 64, 0x20, 0);
+  build_alphabet(&g_e2m3, mxo_e2m3_decode, 64, 0x20, 0);
+  build_alphabet(&g_int8, mxo_int8_decode, 256, 0, 1);
   g_ready = 1;
 }
 
@@ -155,6 +190,15 @@ static int bracket(const mxo_alphabet* al, double a) {
  * elements beyond the range saturate), sign preserved, so -0 exists.
  * y must not be NaN. */
 static uint32_t encode_rne(const mxo_alphabet* al, double y) {
+  if (al->twos) { /* signed list: saturate at both ends, nearest, ties to the even code */
+    if (y <= al->v[0]) return al->code[0];
+    if (y >= al->v[al->n - 1]) return al->code[al->n - 1];
+    int i = bracket(al, y);
+    double lo = al->v[i], hi = al->v[i + 1], mid = 0.5 * (lo + hi);
+    if (y < mid) return al->code[i];
+    if (y > mid) return al->code[i + 1];
+    return (al->code[i] & 1) ? al->code[i + 1] : al->code[i];
+  }
   uint32_t sign = signbit(y) ? al->sign_bit : 0;
   double a = fabs(y);
   double vmax = al->v[al->n - 1];
@@ -177,6 +221,15 @@ static uint32_t encode_rne(const mxo_alphabet* al, double y) {
  * t = (a - lo) * 2^16 / (hi - lo), round up exactly when r < floor(t).
  * P(up) = floor(t)/65536.  Saturate at the largest finite value. */
 static uint32_t encode_sr(const mxo_alphabet* al, double y, uint32_t r16) {
+  if (al->twos) { /* READING: on the signed value -- up means toward +inf */
+    if (y <= al->v[0]) return al->code[0];
+    if (y >= al->v[al->n - 1]) return al->code[al->n - 1];
+    int i = bracket(al, y);
+    double lo = al->v[i], hi = al->v[i + 1];
+    if (y == lo) return al->code[i];
+    double ft = floor((y - lo) * 65536.0 / (hi - lo));
+    return (double)(r16 & 0xFFFF) < ft ? al->code[i + 1] : al->code[i];
+  }
   uint32_t sign = signbit(y) ? al->sign_bit : 0;
   double a = fabs(y);
   double vmax = al->v[al->n - 1];
@@ -193,6 +246,49 @@ uint32_t mxo_e2m1_encode_rne(double y) { ensure_tables(); return encode_rne(&g_e
 uint32_t mxo_e4m3_encode_rne(double y) { ensure_tables(); return encode_rne(&g_e4m3, y); }
 uint32_t mxo_e2m1_encode_sr(double y, uint32_t r) { ensure_tables(); return encode_sr(&g_e2m1, y, r); }
 uint32_t mxo_e4m3_encode_sr(double y, uint32_t r) { ensure_tables(); return encode_sr(&g_e4m3, y, r); }
+
+/* Element format of an MX format: alphabet, emax (the exponent of the
+ * element's largest power of two) and bits per element. */
+typedef struct {
+  const mxo_alphabet* al;
+  int emax, bits;
+} mxo_elem;
+
+static int elem_of(int fmt, mxo_elem* e) {
+  ensure_tables();
+  switch (fmt) {
+    case MXO_MXFP8: *e = (mxo_elem){&g_e4m3, 8, 8}; return 0;
+    case MXO_MXFP4: *e = (mxo_elem){&g_e2m1, 2, 4}; return 0;
+    case MXO_MXINT8: *e = (mxo_elem){&g_int8, 0, 8}; return 0;
+    case MXO_MXFP8_E5M2: *e = (mxo_elem){&g_e5m2, 15, 8}; return 0;
+    case MXO_MXFP6_E3M2: *e = (mxo_elem){&g_e3m2, 4, 6}; return 0;
+    case MXO_MXFP6_E2M3: *e = (mxo_elem){&g_e2m3, 2, 6}; return 0;
+    default: return -1;
+  }
+}
+
+/* Element codes of one MX format (fmt as above): RNE, and SR with r16. */
+uint32_t mxo_elem_encode_rne(int fmt, double y) {
+  mxo_elem e;
+  if (elem_of(fmt, &e)) return 0xFFFFFFFFu;
+  return encode_rne(e.al, y);
+}
+uint32_t mxo_elem_encode_sr(int fmt, double y, uint32_t r) {
+  mxo_elem e;
+  if (elem_of(fmt, &e)) return 0xFFFFFFFFu;
+  return encode_sr(e.al, y, r);
+}
+double mxo_elem_decode(int fmt, uint32_t code) {
+  switch (fmt) {
+    case MXO_MXFP8: return mxo_e4m3_decode(code);
+    case MXO_MXFP4: return mxo_e2m1_decode(code);
+    case MXO_MXINT8: return mxo_int8_decode(code);
+    case MXO_MXFP8_E5M2: return mxo_e5m2_decode(code);
+    case MXO_MXFP6_E3M2: return mxo_e3m2_decode(code);
+    case MXO_MXFP6_E2M3: return mxo_e2m3_decode(code);
+    default: return NAN;
+  }
+}
 
 /* ------------------------------------------------------------------------ */
 /* Counter-based random numbers: Philox-4x32 with 10 rounds, from [PHX].     */
@@ -242,14 +338,15 @@ uint32_t mxo_rand16(uint64_t seed, uint64_t counter, uint64_t n) {
   return (word >> (16 * (n & 1))) & 0xFFFFu;
 }
 
-/* Element codes of many values at once: y[t] encoded to E4M3 (elem = 1) or
- * E2M1 (elem = 2) by round-to-nearest, or by SR with the random value of
+/* Element codes of many values at once: y[t] encoded to the element type of
+ * MX format `elem` (E4M3 for 1, E2M1 for 2, ...) by round-to-nearest, or by SR with the random value of
  * element index n[t] of the stream (seed, counter).  A loop over the encoders
  * and the stream above, for checks that need many encodings. */
 void mxo_encode_elems(int elem, int rnd, const double* y, const uint64_t* n, int64_t count,
                       uint64_t seed, uint64_t counter, uint8_t* codes) {
-  ensure_tables();
-  const mxo_alphabet* al = elem == MXO_MXFP8 ? &g_e4m3 : &g_e2m1;
+  mxo_elem el;
+  if (elem_of(elem, &el)) return;
+  const mxo_alphabet* al = el.al;
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < count; ++t)
     codes[t] = (uint8_t)(rnd == MXO_SR ? encode_sr(al, y[t], mxo_rand16(seed, counter, n[t]))
@@ -342,6 +439,37 @@ void mxo_rht16(const void* x, int xdt, float* y, int64_t rows, int64_t cols, uin
   }
 }
 
+/* Code storage of a row: 8-bit elements one per byte; FP4 element 2j in the
+ * low nibble of byte j (READING); FP6 (READING: the pages give no packing)
+ * element c at bits 6c .. 6c+5 of the row's little-endian bit string, so 4
+ * elements fill 3 bytes. */
+static void put_code(int bits, uint8_t* row, int64_t c, uint32_t code) {
+  if (bits == 8) {
+    row[c] = (uint8_t)code;
+  } else if (bits == 4) {
+    uint8_t* b = &row[c >> 1];
+    if (c & 1) *b = (uint8_t)((*b & 0x0F) | (code << 4));
+    else *b = (uint8_t)((*b & 0xF0) | code);
+  } else {
+    for (int k = 0; k < bits; ++k) {
+      int64_t bit = c * bits + k;
+      uint8_t m = (uint8_t)(1u << (bit & 7));
+      if ((code >> k) & 1) row[bit >> 3] |= m;
+      else row[bit >> 3] &= (uint8_t)~m;
+    }
+  }
+}
+static uint32_t get_code(int bits, const uint8_t* row, int64_t c) {
+  if (bits == 8) return row[c];
+  if (bits == 4) return (c & 1) ? (row[c >> 1] >> 4) : (row[c >> 1] & 0xF);
+  uint32_t code = 0;
+  for (int k = 0; k < bits; ++k) {
+    int64_t bit = c * bits + k;
+    code |= (uint32_t)((row[bit >> 3] >> (bit & 7)) & 1) << k;
+  }
+  return code;
+}
+
 /* ------------------------------------------------------------------------ */
 /* MX quantization: 32 consecutive elements along a row share one E8M0      */
 /* scale ([MXF] "Microscaling", "The idea"; [MIL] "Recipe 1"; [FP4] format   */
@@ -362,8 +490,10 @@ void mxo_rht16(const void* x, int xdt, float* y, int64_t rows, int64_t cols, uin
 static void mx_encode_block(const float* v, int n, int fmt, int rnd, int ceil_rule,
                             uint64_t seed, uint64_t counter, uint64_t n0, uint8_t* codes_row,
                             int64_t col0, uint8_t* scale_out) {
-  const mxo_alphabet* al = (fmt == MXO_MXFP8) ? &g_e4m3 : &g_e2m1;
-  int emax = (fmt == MXO_MXFP8) ? 8 : 2;
+  mxo_elem el;
+  elem_of(fmt, &el);
+  const mxo_alphabet* al = el.al;
+  const int emax = el.emax;
   double amax = 0.0;
   int bad = 0;
   for (int i = 0; i < n; ++i) {
@@ -397,27 +527,22 @@ static void mx_encode_block(const float* v, int n, int fmt, int rnd, int ceil_ru
                                  : encode_rne(al, y);
     }
   }
-  for (int i = 0; i < n; ++i) {
-    int64_t c = col0 + i;
-    if (fmt == MXO_MXFP8) {
-      codes_row[c] = (uint8_t)codes[i];
-    } else { /* READING: element 2j in the low nibble, 2j+1 in the high nibble */
-      uint8_t* b = &codes_row[c >> 1];
-      if (c & 1) *b = (uint8_t)((*b & 0x0F) | (codes[i] << 4));
-      else *b = (uint8_t)((*b & 0xF0) | codes[i]);
-    }
-  }
+  for (int i = 0; i < n; ++i) put_code(el.bits, codes_row, col0 + i, codes[i]);
 }
 
 static int64_t code_row_bytes(int fmt, int64_t cols) {
-  return fmt == MXO_MXFP8 ? cols : cols / 2;
+  mxo_elem el;
+  if (fmt == MXO_NVFP4) return cols / 2;
+  if (elem_of(fmt, &el)) return 0;
+  return cols * el.bits / 8;
 }
 
 int mxo_quantize_mx(const void* x, int xdt, int64_t ld, int64_t rows, int64_t cols, int fmt,
                     int rnd, uint64_t seed, uint64_t counter, int rht, uint32_t mask,
                     int variant, uint8_t* codes, uint8_t* scales) {
   ensure_tables();
-  if ((fmt != MXO_MXFP8 && fmt != MXO_MXFP4) || cols % 32 || (rht && cols % 16)) return -1;
+  mxo_elem el;
+  if (elem_of(fmt, &el) || cols % 32 || (rht && cols % 16)) return -1;
   if (variant & ~MXO_V_CEIL) return -1;
   const int ceil_rule = (variant & MXO_V_CEIL) != 0;
 #pragma omp parallel
@@ -605,9 +730,9 @@ int mxo_quantize_nvfp4(const void* x, int xdt, int64_t ld, int64_t rows, int64_t
 /* product is exact, so there is one FP32 rounding.                          */
 /* ------------------------------------------------------------------------ */
 static double elem_value(int fmt, const uint8_t* codes_row, int64_t c) {
-  if (fmt == MXO_MXFP8) return mxo_e4m3_decode(codes_row[c]);
-  uint8_t b = codes_row[c >> 1];
-  return mxo_e2m1_decode((c & 1) ? (b >> 4) : (b & 0xF));
+  mxo_elem el;
+  elem_of(fmt, &el);
+  return mxo_elem_decode(fmt, get_code(el.bits, codes_row, c));
 }
 
 void mxo_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales,
@@ -739,7 +864,7 @@ void mxo_gemm_f64_sampled(const double* A, const double* B, int64_t K, const int
  * 32 elements, MXFP4 averaging 4.25 bits; [FP4] format table: NVFP4 4 + 8/16
  * bits plus one FP32 per tensor). */
 int64_t mxo_codes_bytes(int fmt, int64_t rows, int64_t cols) {
-  return fmt == MXO_MXFP8 ? rows * cols : rows * cols / 2;
+  return rows * code_row_bytes(fmt, cols);
 }
 int64_t mxo_scales_bytes(int fmt, int64_t rows, int64_t cols) {
   return fmt == MXO_NVFP4 ? rows * cols / 16 : rows * cols / 32;
