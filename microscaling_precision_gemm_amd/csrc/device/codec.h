@@ -100,6 +100,94 @@ __host__ __device__ inline uint32_t e2m1_encode(float y, bool sr, uint32_t r16) 
   return s | (sr ? e2m1_sr_mag(a, r16) : e2m1_rne_mag(a));
 }
 
+// ---- the other MX element types -------------------------------------------
+// "Microscaling (MX) and block-scaled 4-bit formats", section "The idea", and
+// "08 - FP4, MXFP4, NVFP4: The Blackwell Frontier", section "The OCP
+// Microscaling (MX) spec", name FP8 E5M2, FP6 E3M2 / E2M3 and INT8 as MX
+// elements; their bits follow the OCP definitions: sign-magnitude minifloats
+// with EB exponent bits, MB mantissa bits and bias BIAS (E5M2 keeps its top
+// exponent for Inf/NaN, the FP6 types use every code), and INT8 two's
+// complement with an implied scale 2^-6 (also the block-scaled "S2F6" combine
+// format of "Thinking Machines ... Inkling 2 Small", section "Why
+// communication became the next bottleneck").  Encoders saturate at the
+// largest finite value; RNE and SR exactly as for E4M3 / E2M1 above.
+template <int EB, int MB, int BIAS, uint32_t MAXC>
+struct Minifloat {
+  static constexpr int kShift = 23 - MB;
+  static constexpr uint32_t kSign = 1u << (EB + MB);
+  // exact FP32 value of a finite magnitude code
+  static __host__ __device__ float value(uint32_t c) {
+    const uint32_t e = c >> MB, m = c & ((1u << MB) - 1u);
+    if (e == 0) return (float)m * u2f((uint32_t)(128 - BIAS - MB) << 23);  // m * 2^(1-BIAS-MB)
+    return u2f(((e + 127u - (uint32_t)BIAS) << 23) | (m << kShift));
+  }
+  static __host__ __device__ float maxv() { return value(MAXC); }
+  static __host__ __device__ float min_normal() { return u2f((uint32_t)(128 - BIAS) << 23); }
+  static __host__ __device__ float inv_step() { return u2f((uint32_t)(126 + BIAS + MB) << 23); }
+  static __host__ __device__ uint32_t rne_mag(float a) {
+    if (a >= maxv()) return MAXC;
+    if (a < min_normal()) return (uint32_t)rintf(a * inv_step());
+    uint32_t b = f2u(a);
+    b += (1u << (kShift - 1)) - 1u + ((b >> kShift) & 1u);
+    const uint32_t c = (b >> kShift) - ((127u - (uint32_t)BIAS) << MB);
+    return c > MAXC ? MAXC : c;
+  }
+  static __host__ __device__ uint32_t sr_mag(float a, uint32_t r16) {
+    if (a >= maxv()) return MAXC;
+    if (a < min_normal()) {
+      const float sc = a * inv_step();  // exact
+      const float m = floorf(sc);
+      const uint32_t t = (uint32_t)((sc - m) * 65536.0f);
+      return (uint32_t)m + (r16 < t ? 1u : 0u);
+    }
+    const uint32_t b = f2u(a);
+    const uint32_t t = (b & ((1u << kShift) - 1u)) >> (kShift - 16);
+    return (b >> kShift) - ((127u - (uint32_t)BIAS) << MB) + (r16 < t ? 1u : 0u);
+  }
+  static __host__ __device__ uint32_t encode(float y, bool sr, uint32_t r16) {
+    const uint32_t s = (f2u(y) >> 31) ? kSign : 0u;
+    const float a = __builtin_fabsf(y);
+    return s | (sr ? sr_mag(a, r16) : rne_mag(a));
+  }
+};
+typedef Minifloat<5, 2, 15, 0x7Bu> E5M2;  // largest finite 57344
+typedef Minifloat<3, 2, 3, 0x1Fu> E3M2;   // largest 28
+typedef Minifloat<2, 3, 1, 0x1Fu> E2M3;   // largest 7.5
+
+// signed value of an E5M2 code (Inf and NaN in the top exponent)
+__host__ __device__ inline float e5m2_value(uint32_t c) {
+  const uint32_t mag = c & 0x7Fu;
+  float v = mag >= 0x7Du ? __builtin_nanf("") : (mag == 0x7Cu ? __builtin_inff() : E5M2::value(mag));
+  return (c & 0x80u) ? -v : v;
+}
+template <class F>
+__host__ __device__ inline float fp6_value(uint32_t c) {
+  const float v = F::value(c & 0x1Fu);
+  return (c & 0x20u) ? -v : v;
+}
+
+// INT8 with 6 fraction bits: y * 64 rounded (RNE, or SR on the signed value:
+// up toward +inf), saturated to [-128, 127]; the code is the two's
+// complement byte.
+// The SR threshold floor((s - floor(s)) * 2^16) is formed as
+// floor(s * 2^16) - floor(s) * 2^16: for a small negative s, s - floor(s) =
+// 1 - |s| would round in FP32, while both terms here are integers below 2^24
+// once s is clamped to [-129, 128] (which keeps the saturation).
+__host__ __device__ inline uint32_t int8_encode(float y, bool sr, uint32_t r16) {
+  const float s = fminf(fmaxf(y * 64.0f, -129.0f), 128.0f);  // y * 64 is exact
+  float v;
+  if (!sr) {
+    v = rintf(s);
+  } else {
+    const float m = floorf(s);
+    const uint32_t t = (uint32_t)(floorf(s * 65536.0f) - m * 65536.0f);
+    v = m + (r16 < t ? 1.0f : 0.0f);
+  }
+  v = fminf(fmaxf(v, -128.0f), 127.0f);
+  return (uint32_t)(uint8_t)(int8_t)(int)v;
+}
+__host__ __device__ inline float int8_value(uint32_t c) { return (float)(int8_t)(uint8_t)c * 0.015625f; }
+
 // ---- E8M0 shared scale of an MX block ------------------------------------
 // From the FP32 bits of the block's max |x| (sign cleared): the exponent of
 // the largest power of two <= amax, minus the element's emax, clamped so the

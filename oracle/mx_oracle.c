@@ -227,7 +227,11 @@ static uint32_t encode_sr(const mxo_alphabet* al, double y, uint32_t r16) {
     int i = bracket(al, y);
     double lo = al->v[i], hi = al->v[i + 1];
     if (y == lo) return al->code[i];
-    double ft = floor((y - lo) * 65536.0 / (hi - lo));
+    /* t = floor((y - lo) * 2^16 / (hi - lo)), formed as floor(y * S) - lo * S
+     * with S = 2^16 / (hi - lo) a power of two: y - lo itself is not exact
+     * for a tiny negative y (lo = -1/64), both terms here are. */
+    double S = 65536.0 / (hi - lo);
+    double ft = floor(y * S) - lo * S;
     return (double)(r16 & 0xFFFF) < ft ? al->code[i + 1] : al->code[i];
   }
   uint32_t sign = signbit(y) ? al->sign_bit : 0;
