@@ -17,6 +17,19 @@
  *                  ([MXF] "Microscaling"; [FP4] format table).
  *   MX_NVFP4       16 E2M1 elements + one E4M3 scale, plus one FP32 scale per
  *                  tensor ([MXF] "NVFP4"; [FP4] format table).
+ *   The other MX element types ([MXF] "The idea"; [FP4] "The OCP
+ *   Microscaling (MX) spec"), 32 elements + one E8M0 scale, bits as the OCP
+ *   definitions give them:
+ *   MX_MXINT8      8-bit two's complement with 6 fraction bits (-2 .. 127/64);
+ *                  with MX_FLAG_RHT16 this is also the block-scaled "S2F6"
+ *                  combine codec ([INK] "Why communication became the next
+ *                  bottleneck": 8.25 bits per value).
+ *   MX_MXFP8_E5M2  E5M2 (bias 15, largest finite 57344; the encoder saturates).
+ *   MX_MXFP6_E3M2, MX_MXFP6_E2M3  FP6 (largest 28 / 7.5), packed 4 elements in
+ *                  3 bytes: element c of a row at bits 6c .. 6c+5 of the row's
+ *                  little-endian bit string.
+ *   They are taken by mx_quantize, mx_amax and mx_dequantize (row layout);
+ *   products of them are not offered (MX_ERR_UNSUPPORTED).
  *
  * Conventions shared by every call:
  *   - Pointers are device pointers (HIP), except the mx_tensor descriptor
@@ -59,7 +72,15 @@ typedef enum {
   MX_ERR_HIP = 6          /* the HIP runtime rejected a launch */
 } mx_status;
 
-typedef enum { MX_MXFP8_E4M3 = 1, MX_MXFP4_E2M1 = 2, MX_NVFP4 = 3 } mx_format;
+typedef enum {
+  MX_MXFP8_E4M3 = 1,
+  MX_MXFP4_E2M1 = 2,
+  MX_NVFP4 = 3,
+  MX_MXINT8 = 4,
+  MX_MXFP8_E5M2 = 5,
+  MX_MXFP6_E3M2 = 6,
+  MX_MXFP6_E2M3 = 7
+} mx_format;
 
 /* Rounding of elements: round-to-nearest, ties to the even code, or
  * stochastic rounding ([MXF] "Open points"; glossary "stochastic rounding";
@@ -82,15 +103,17 @@ typedef struct {
 
 /* One quantized matrix, logical shape [rows, cols], blocks along cols.
  * (host struct; the pointers inside are device pointers)
- *   codes   MXFP8: uint8 [rows, cols], one E4M3 code per element.
+ *   codes   8-bit elements (MXFP8 E4M3 / E5M2, MXINT8): uint8 [rows, cols],
+ *           one code per element.
  *           FP4 formats: uint8 [rows, cols/2], element 2j in the low nibble
  *           and element 2j+1 in the high nibble of byte j.
+ *           FP6 formats: uint8 [rows, 3 cols / 4], see MX_MXFP6_*.
  *   scales  uint8 [rows, cols/32] E8M0 codes (MX formats) or
  *           uint8 [rows, cols/16] E4M3 codes (NVFP4), row-major.
  *   tensor_scale  NVFP4 only: FP32 S, the per-tensor decode multiplier
  *           (x ~ e2m1 * e4m3 * S); NULL for MX formats.  For the stacked
  *           weights of mx_gemm_grouped it points to one S per group.
- * Rows are dense: the row pitch is cols (or cols/2) bytes.
+ * Rows are dense: the row pitch is the row's code bytes.
  *
  * layout (mx_layout) selects how the code and scale bytes are ordered:
  *   MX_LAYOUT_ROWS   the row-major arrays above (every format, every call).

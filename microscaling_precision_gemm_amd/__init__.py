@@ -16,6 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmx.so")
 
 MX_MXFP8_E4M3, MX_MXFP4_E2M1, MX_NVFP4 = 1, 2, 3
+MX_MXINT8, MX_MXFP8_E5M2, MX_MXFP6_E3M2, MX_MXFP6_E2M3 = 4, 5, 6, 7
 MX_RNE, MX_SR = 0, 1
 MX_BF16, MX_F32 = 0, 1
 MX_FLAG_RHT16, MX_FLAG_AMAX_GIVEN = 1, 2
@@ -23,7 +24,9 @@ MX_FLAG_SCALE_CEIL, MX_FLAG_FOUR_OVER_SIX, MX_FLAG_BLOCK_2D = 4, 8, 16
 MX_GEMM_FP8_NATIVE = 1
 MX_LAYOUT_ROWS, MX_LAYOUT_TILED = 0, 1
 
-FORMATS = {"mxfp8": MX_MXFP8_E4M3, "mxfp4": MX_MXFP4_E2M1, "nvfp4": MX_NVFP4}
+FORMATS = {"mxfp8": MX_MXFP8_E4M3, "mxfp4": MX_MXFP4_E2M1, "nvfp4": MX_NVFP4, "mxint8": MX_MXINT8,
+           "s2f6": MX_MXINT8, "mxfp8_e5m2": MX_MXFP8_E5M2, "mxfp6_e3m2": MX_MXFP6_E3M2,
+           "mxfp6_e2m3": MX_MXFP6_E2M3}
 
 # every function declared in include/mx.h
 EXPORTED = [

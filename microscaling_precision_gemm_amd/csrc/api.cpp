@@ -10,7 +10,19 @@
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool valid_fmt(int32_t f) { return f == MX_MXFP8_E4M3 || f == MX_MXFP4_E2M1 || f == MX_NVFP4; }
+bool valid_fmt(int32_t f) { return f >= MX_MXFP8_E4M3 && f <= MX_MXFP6_E2M3; }
+// the formats every kernel takes; the other MX element types are quantized,
+// decoded and (E5M2) multiplied natively, see include/mx.h
+bool core_fmt(int32_t f) { return f == MX_MXFP8_E4M3 || f == MX_MXFP4_E2M1 || f == MX_NVFP4; }
+int64_t code_bits(int32_t f) {
+  switch (f) {
+    case MX_MXFP4_E2M1:
+    case MX_NVFP4: return 4;
+    case MX_MXFP6_E3M2:
+    case MX_MXFP6_E2M3: return 6;
+    default: return 8;
+  }
+}
 bool valid_dt(int32_t d) { return d == MX_BF16 || d == MX_F32; }
 int64_t dt_bytes(int32_t d) { return d == MX_BF16 ? 2 : 4; }
 int64_t block_of(int32_t f) { return f == MX_NVFP4 ? 16 : 32; }
@@ -26,7 +38,7 @@ mx_status check_tensor(const mx_tensor* t, int64_t rows, int64_t cols) {
   if (t->rows != rows || t->cols != cols || rows < 0 || cols < 0) return MX_ERR_SHAPE;
   if (cols % block_of(t->fmt)) return MX_ERR_SHAPE;
   if (t->layout == MX_LAYOUT_TILED) {
-    if (t->fmt == MX_NVFP4) return MX_ERR_UNSUPPORTED;
+    if (t->fmt != MX_MXFP8_E4M3 && t->fmt != MX_MXFP4_E2M1) return MX_ERR_UNSUPPORTED;
     if (rows % 32 || cols % 1024) return MX_ERR_SHAPE;
   }
   if (rows * cols > 0) {
@@ -65,7 +77,7 @@ extern "C" {
 
 size_t mx_codes_bytes(int32_t fmt, int64_t rows, int64_t cols) {
   if (!valid_fmt(fmt) || rows < 0 || cols < 0) return 0;
-  return (size_t)(fmt == MX_MXFP8_E4M3 ? rows * cols : rows * cols / 2);
+  return (size_t)(rows * (cols * code_bits(fmt) / 8));
 }
 
 size_t mx_scales_bytes(int32_t fmt, int64_t rows, int64_t cols) {
@@ -215,7 +227,7 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
   if (st != MX_OK) return st;
   st = check_tensor(B, B->rows, B->cols);
   if (st != MX_OK) return st;
-  if (A->fmt != B->fmt) return MX_ERR_UNSUPPORTED;
+  if (A->fmt != B->fmt || !core_fmt(A->fmt)) return MX_ERR_UNSUPPORTED;
   if ((flags & MX_GEMM_FP8_NATIVE) && A->fmt != MX_MXFP8_E4M3) return MX_ERR_UNSUPPORTED;
   if (A->cols != B->cols || A->cols % 32) return MX_ERR_SHAPE;
   const bool tiled = A->layout == MX_LAYOUT_TILED;
@@ -267,7 +279,7 @@ mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, const mx_tens
   const int64_t M = A->rows, N = B->rows, K = A->cols;
   st = check_tensor(out, M, N);
   if (st != MX_OK) return st;
-  if (out->fmt == MX_NVFP4) return MX_ERR_UNSUPPORTED;
+  if (out->fmt != MX_MXFP8_E4M3 && out->fmt != MX_MXFP4_E2M1) return MX_ERR_UNSUPPORTED;
   if (M * N == 0) return MX_OK;
   return hip_status(mxk::launch_gemm_mx_tiled_quant(
       A->fmt, static_cast<const uint8_t*>(A->codes), A->scales,

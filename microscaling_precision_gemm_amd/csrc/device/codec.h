@@ -207,10 +207,16 @@ __host__ __device__ inline uint32_t e8m0_ceil_from_amax_bits(uint32_t amax_bits,
   if (amax_bits >= 0x7F800000u) return 0xFFu;
   uint32_t e = amax_bits >> 23;
   if (e < emax) return 0u;
-  return e - emax + ((amax_bits & 0x7FFFFFu) > gmax_mant ? 1u : 0u);
+  const uint32_t c = e - emax + ((amax_bits & 0x7FFFFFu) > gmax_mant ? 1u : 0u);
+  return c > 254u ? 254u : c;  // e clamped to 127 (INT8, emax 0, near the FP32 maximum)
 }
-// 1 / 2^(code-127) as an exact FP32 (code in 0..254-emax)
+// 1 / 2^(code-127) as an exact FP32 (code in 0..253)
 __host__ __device__ inline float e8m0_inverse(uint32_t code) { return u2f((254u - code) << 23); }
+// v / 2^(code-127) exactly, code in 0..254 (254 would need the FP32
+// subnormal 2^-127: two exact steps instead)
+__host__ __device__ inline float e8m0_unscale(float v, uint32_t code) {
+  return code <= 253u ? v * e8m0_inverse(code) : (v * 0x1p-64f) * 0x1p-63f;
+}
 
 // ---- bf16 ---------------------------------------------------------------
 __host__ __device__ inline float bf16_to_f32(uint16_t h) { return u2f((uint32_t)h << 16); }

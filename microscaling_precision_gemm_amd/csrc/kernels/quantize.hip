@@ -176,8 +176,13 @@ template <int FMT>
 __device__ inline void store_enc(const QuantArgs& a, int64_t q, int64_t Q, uint32_t lane,
                                  uint32_t lanes_per_block, const Enc<FMT>& e) {
   if (q < Q) {
-    if constexpr (FMT == FMT_MXFP8) {
+    if constexpr (MxFmt<FMT>::bits == 8) {
       *reinterpret_cast<uint2*>(a.codes + q * 8) = make_uint2(e.w[0], e.w[1]);
+    } else if constexpr (MxFmt<FMT>::bits == 6) {  // 6 bytes at 6 q: 2-byte aligned
+      uint16_t* p = reinterpret_cast<uint16_t*>(a.codes + q * 6);
+      p[0] = (uint16_t)e.w[0];
+      p[1] = (uint16_t)(e.w[0] >> 16);
+      p[2] = (uint16_t)e.w[1];
     } else {
       *reinterpret_cast<uint32_t*>(a.codes + q * 4) = e.w[0];
     }
@@ -628,21 +633,27 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* codes, cons
     if (valid) {
       uint32_t cw[8];
       // tiled layout (MX only): code and scale offsets of this chunk
-      int64_t coff = q * (FMT == FMT_MXFP8 ? 8 : 4), soff = q >> 2;
-      if constexpr (FMT != FMT_NVFP4) {
+      constexpr int kBits = FMT == FMT_NVFP4 ? 4 : (int)MxFmt<FMT>::bits;
+      int64_t coff = q * kBits, soff = q >> 2;
+      if constexpr (FMT == FMT_MXFP8 || FMT == FMT_MXFP4) {
         if (tiled) {
           const int64_t row = q / cpr, c8 = q - row * cpr;
           coff = tiled_code_off(row, c8 * (FMT == FMT_MXFP8 ? 8 : 4), cpr * (FMT == FMT_MXFP8 ? 8 : 4));
           soff = tiled_scale_off(row, c8 >> 2, cols);
         }
       }
-      if constexpr (FMT == FMT_MXFP8) {
+      if constexpr (kBits == 8) {
         uint2 p = *reinterpret_cast<const uint2*>(codes + coff);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           cw[i] = (p.x >> (8 * i)) & 0xFFu;
           cw[4 + i] = (p.y >> (8 * i)) & 0xFFu;
         }
+      } else if constexpr (kBits == 6) {  // element i at bits 6 i of the chunk's 6 bytes
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(codes + coff);
+        const uint64_t b = (uint64_t)p[0] | ((uint64_t)p[1] << 16) | ((uint64_t)p[2] << 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cw[i] = (uint32_t)(b >> (6 * i)) & 0x3Fu;
       } else {
         uint32_t p = *reinterpret_cast<const uint32_t*>(codes + coff);
 #pragma unroll
@@ -663,8 +674,16 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* codes, cons
             const uint32_t mag = cw[i] & 0x7Fu;
             e = mag == 0x7Fu ? __builtin_nanf("") : e4m3_mag_value(mag);
             if (cw[i] & 0x80u) e = -e;
-          } else {
+          } else if constexpr (FMT == FMT_MXFP4) {
             e = e2m1_value(cw[i]);
+          } else if constexpr (FMT == FMT_MXINT8) {
+            e = int8_value(cw[i]);
+          } else if constexpr (FMT == FMT_MXFP8_E5M2) {
+            e = e5m2_value(cw[i]);
+          } else if constexpr (FMT == FMT_MXFP6_E3M2) {
+            e = fp6_value<E3M2>(cw[i]);
+          } else {
+            e = fp6_value<E2M3>(cw[i]);
           }
           v[i] = e * X;
         }
@@ -782,9 +801,17 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
       return a.xdt == DT_BF16 ? quant_mx_tiled_d<DT_BF16, FMT_MXFP8>(a, s) : quant_mx_tiled_d<DT_F32, FMT_MXFP8>(a, s);
     return a.xdt == DT_BF16 ? quant_mx_tiled_d<DT_BF16, FMT_MXFP4>(a, s) : quant_mx_tiled_d<DT_F32, FMT_MXFP4>(a, s);
   }
-  if (a.fmt == FMT_MXFP8)
-    return a.xdt == DT_BF16 ? quant_mx_d<DT_BF16, FMT_MXFP8>(a, Q, s) : quant_mx_d<DT_F32, FMT_MXFP8>(a, Q, s);
-  return a.xdt == DT_BF16 ? quant_mx_d<DT_BF16, FMT_MXFP4>(a, Q, s) : quant_mx_d<DT_F32, FMT_MXFP4>(a, Q, s);
+#define MXK_QD(F) \
+  return a.xdt == DT_BF16 ? quant_mx_d<DT_BF16, F>(a, Q, s) : quant_mx_d<DT_F32, F>(a, Q, s)
+  switch (a.fmt) {
+    case FMT_MXFP8: MXK_QD(FMT_MXFP8);
+    case FMT_MXFP4: MXK_QD(FMT_MXFP4);
+    case FMT_MXINT8: MXK_QD(FMT_MXINT8);
+    case FMT_MXFP8_E5M2: MXK_QD(FMT_MXFP8_E5M2);
+    case FMT_MXFP6_E3M2: MXK_QD(FMT_MXFP6_E3M2);
+    default: MXK_QD(FMT_MXFP6_E2M3);
+  }
+#undef MXK_QD
 }
 
 hipError_t launch_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales,
@@ -805,6 +832,10 @@ hipError_t launch_dequantize(int fmt, const uint8_t* codes, const uint8_t* scale
   else { MXK_DQ_Y(F, false) }
   if (fmt == FMT_MXFP8) { MXK_DQ_R(FMT_MXFP8) }
   else if (fmt == FMT_MXFP4) { MXK_DQ_R(FMT_MXFP4) }
+  else if (fmt == FMT_MXINT8) { MXK_DQ_R(FMT_MXINT8) }
+  else if (fmt == FMT_MXFP8_E5M2) { MXK_DQ_R(FMT_MXFP8_E5M2) }
+  else if (fmt == FMT_MXFP6_E3M2) { MXK_DQ_R(FMT_MXFP6_E3M2) }
+  else if (fmt == FMT_MXFP6_E2M3) { MXK_DQ_R(FMT_MXFP6_E2M3) }
   else { MXK_DQ_R(FMT_NVFP4) }
 #undef MXK_DQ_R
 #undef MXK_DQ_Y

@@ -7,7 +7,18 @@
 
 namespace mxk {
 
-enum Fmt { FMT_MXFP8 = 1, FMT_MXFP4 = 2, FMT_NVFP4 = 3 };
+// MX formats: FP8 E4M3, FP4 E2M1, NVFP4, then the other MX element types
+// (INT8 with 6 fraction bits, FP8 E5M2, FP6 E3M2 and E2M3), all with E8M0
+// scales per 32 except NVFP4.
+enum Fmt {
+  FMT_MXFP8 = 1,
+  FMT_MXFP4 = 2,
+  FMT_NVFP4 = 3,
+  FMT_MXINT8 = 4,
+  FMT_MXFP8_E5M2 = 5,
+  FMT_MXFP6_E3M2 = 6,
+  FMT_MXFP6_E2M3 = 7
+};
 enum DType { DT_BF16 = 0, DT_F32 = 1 };
 
 struct QuantArgs {

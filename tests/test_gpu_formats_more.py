@@ -1,0 +1,174 @@
+"""GPU parity of the other MX element types (INT8 / S2F6, FP8 E5M2, FP6 E3M2
+and E2M3) against the CPU oracle: bit-exact codes and scales from the
+quantizer (both input dtypes, RNE and SR, the Hadamard transform, the ceil
+rule, strided inputs, ragged tails), bit-exact decoding, and the S2F6 combine
+codec (Hadamard transform + block-scaled INT8, then decode + inverse
+transform) at the mixture-of-experts combine size."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import microscaling_precision_gemm_amd as mx
+    from tests.gpu_util import dev, host, to_gpu_bf16, to_gpu_f32, upload
+
+FMTS = [4, 5, 6, 7]
+SHAPES = [(1, 32), (7, 96), (33, 256), (130, 544)]
+
+
+def _inputs(rows, cols, dt, seed, pad=0, spread=False):
+    bits = W.normal_bf16(rows, cols, 1.5, seed, 80, outlier_entries=0.01, outlier_mult=60.0)
+    x = W.bf16_bits_to_f32(bits).astype(np.float64)
+    if spread:
+        x *= np.exp2(np.round(W.rng(seed, 81).uniform(-30, 30, (rows, 1))))
+    if dt == "bf16":
+        b = W.f64_to_bf16_bits(x)
+        return b, to_gpu_bf16(b, pad)
+    f = (x.astype(np.float32) * np.float32(1.0 + 2.0**-12)).astype(np.float32)
+    return f, to_gpu_f32(f, pad)
+
+
+def _quant(x, fmt, rnd=0, seed=0, counter=0, flags=0, mask=0):
+    rows, cols = x.shape
+    out = mx.empty(fmt, rows, cols, device=dev())
+    mx.mx_quantize(x, out, rnd, seed, counter, flags, mask)
+    torch.cuda.synchronize()
+    return out
+
+
+def _same(got, want, what):
+    assert np.array_equal(got, want), f"{what} differ at {np.argwhere(got != want)[:5]}"
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rnd", [0, 1])
+@pytest.mark.parametrize("rht", [False, True])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_quantize_bit_exact(shape, fmt, rnd, rht, dt):
+    rows, cols = shape
+    seed = rows * 11 + cols + 3 * fmt + rnd
+    x_np, x = _inputs(rows, cols, dt, seed, pad=16 if rows % 2 else 0, spread=not rht)
+    mask = oracle.rht_signs(seed)
+    out = _quant(x, fmt, rnd, seed, 7 * seed, mx.MX_FLAG_RHT16 if rht else 0, mask)
+    c, s, _ = host(out)
+    wc, ws, _ = oracle.quantize(x_np, fmt, rnd, seed, 7 * seed, rht=rht, sign_mask=mask)
+    _same(s, ws, "scales")
+    _same(c, wc, "codes")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_quantize_ceil_rule_bit_exact(fmt, rnd):
+    x_np, x = _inputs(64, 512, "f32", 5 + fmt, spread=True)
+    out = _quant(x, fmt, rnd, 3, 1, mx.MX_FLAG_SCALE_CEIL)
+    c, s, _ = host(out)
+    wc, ws, _ = oracle.quantize(x_np, fmt, rnd, 3, 1, variant=oracle.V_CEIL)
+    _same(s, ws, "scales")
+    _same(c, wc, "codes")
+
+
+@pytest.mark.parametrize("ceil", [False, True])
+def test_int8_block_maxima_near_the_fp32_limit(ceil):
+    """INT8's emax is 0, so maxima of 2^127 and above need scale code 254 (and
+    the ceil rule clamps there); zero and NaN blocks as for the other formats."""
+    x = np.zeros((4, 64), np.float32)
+    x[0, :32] = np.linspace(-3e38, 3.3e38, 32, dtype=np.float32)
+    x[0, 32:] = np.float32(1.7e38)
+    x[1, :32] = np.float32(2.0**127)
+    x[1, 5] = np.float32(-(2.0**127) * 1.5)
+    x[2, 32:] = np.float32(1e-38)
+    x[3, :32] = np.float32(np.nan)
+    flags = mx.MX_FLAG_SCALE_CEIL if ceil else 0
+    out = _quant(to_gpu_f32(x), 4, flags=flags)
+    c, s, _ = host(out)
+    wc, ws, _ = oracle.quantize(x, 4, variant=oracle.V_CEIL if ceil else 0)
+    _same(s, ws, "scales")
+    _same(c, wc, "codes")
+    assert s[0, 0] == 254 and s[3, 0] == 0xFF
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rht", [False, True])
+@pytest.mark.parametrize("ydt", ["f32", "bf16"])
+def test_dequantize_bit_exact(fmt, rht, ydt):
+    rows, cols = 96, 640
+    x = W.normal_bf16(rows, cols, 2.0, fmt, 82, outlier_entries=0.01, outlier_mult=30.0)
+    mask = oracle.rht_signs(fmt + 10)
+    c, s, _ = oracle.quantize(x, fmt, rht=rht, sign_mask=mask)
+    want = oracle.dequantize(fmt, c, s, None, rows, cols)
+    if rht:
+        want = oracle.rht16(want, mask, inverse=True)
+    t = upload(fmt, c, s)
+    t.cols = cols  # upload infers cols from the 8-bit or 4-bit code width
+    y = torch.empty(rows, cols, dtype=torch.float32 if ydt == "f32" else torch.bfloat16, device=dev())
+    mx.mx_dequantize(t, y, mx.MX_FLAG_RHT16 if rht else 0, mask)
+    torch.cuda.synchronize()
+    if ydt == "f32":
+        _same(y.cpu().numpy().view(np.uint32), want.view(np.uint32), "decoded values")
+    else:
+        wb = W.f64_to_bf16_bits(want.astype(np.float64))
+        _same(y.view(torch.int16).cpu().numpy().view(np.uint16), wb, "decoded bf16 values")
+
+
+def test_s2f6_codec_round_trip_exact_on_representable_values():
+    """Transformed values that are multiples of 2^-6 below 2, with every block
+    maximum at least 1: encode (Hadamard + INT8) and decode (INT8 + inverse)
+    return x bit for bit on the GPU too."""
+    g = np.random.default_rng(13)
+    mask = oracle.rht_signs(21)
+    k = g.integers(-127, 128, (64, 1024))
+    k[:, ::32] = -127  # block max 127/64 < 2: scale 2^0
+    y = (k / 64.0).astype(np.float32)
+    x = oracle.rht16(y, mask, inverse=True)
+    out = _quant(to_gpu_f32(x), 4, flags=mx.MX_FLAG_RHT16, mask=mask)
+    back = torch.empty(64, 1024, dtype=torch.float32, device=dev())
+    mx.mx_dequantize(out, back, mx.MX_FLAG_RHT16, mask)
+    torch.cuda.synchronize()
+    _same(back.cpu().numpy().view(np.uint32), x.view(np.uint32), "round trip")
+
+
+def test_s2f6_codec_moe_combine_size_sampled_rows():
+    """The combine tensor of the MoE workload (32768 routed rows x 7168, BF16
+    N(0,1)): Hadamard + INT8 encode on the GPU, checked against the oracle on
+    bands of rows (rows are independent), and the decoded round trip's error
+    against its bound: at most one step 2^(e-6) per transformed element (half
+    a step when rounded, a full one when saturated at 127/64), carried over
+    unchanged by the orthonormal inverse transform."""
+    rows, cols = 32768, 7168
+    bits = W.normal_bf16(rows, cols, 1.0, 0, 83)
+    x = to_gpu_bf16(bits)
+    mask = mx.mx_rht_signs(0)
+    out = _quant(x, 4, flags=mx.MX_FLAG_RHT16, mask=mask)
+    back = torch.empty(rows, cols, dtype=torch.float32, device=dev())
+    mx.mx_dequantize(out, back, mx.MX_FLAG_RHT16, mask)
+    torch.cuda.synchronize()
+    c, s = out.codes.cpu().numpy(), out.scales.cpu().numpy()
+    for r0 in (0, 12345, rows - 96):
+        wc, ws, _ = oracle.quantize(bits[r0:r0 + 96], 4, rht=True, sign_mask=mask)
+        _same(s[r0:r0 + 96], ws, f"scales rows {r0}..")
+        _same(c[r0:r0 + 96], wc, f"codes rows {r0}..")
+    xr = W.bf16_bits_to_f32(bits[:2048]).astype(np.float64)
+    err = back[:2048].cpu().numpy().astype(np.float64) - xr
+    # per 16-group: the transform is orthonormal, so the group's error norm is
+    # the transformed error norm, each element of which is at most one step
+    step = np.repeat(2.0 ** (s[:2048].astype(np.float64) - 127 - 6), 32, axis=1)
+    gerr = np.sqrt((err ** 2).reshape(2048, -1, 16).sum(axis=2))
+    gbound = np.sqrt((step ** 2).reshape(2048, -1, 16).sum(axis=2)) * (1 + 1e-5) + 1e-6
+    assert np.all(gerr <= gbound)
+    assert float(np.sqrt(np.mean(err ** 2))) < 0.015  # about step / sqrt(12) = 0.009 here
+
+
+def test_other_formats_are_rejected_where_not_offered():
+    a = mx.empty(5, 64, 1024, device=dev())
+    C = torch.empty(64, 64, dtype=torch.float32, device=dev())
+    with pytest.raises(mx.MXError):
+        mx.mx_gemm(a, a, C)
+    tiled_fp6 = mx.empty(6, 64, 1024, device=dev(), layout=mx.MX_LAYOUT_TILED)
+    with pytest.raises(mx.MXError):
+        mx.mx_quantize(torch.zeros(64, 1024, dtype=torch.bfloat16, device=dev()), tiled_fp6)
