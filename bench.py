@@ -377,6 +377,32 @@ def detail(torch, mx, W, args):
         "wgrad_native_fp8_ms": ms_wn, "wgrad_native_fp8_tflops": fl / ms_wn / 1e9}
     del qx, xt, dyt, Cw
 
+    # S2F6 combine codec on the MoE combine tensor (32768 routed rows x 7168, BF16): encode
+    # = Hadamard transform + block-scaled INT8 (RNE), decode = INT8 + inverse transform to BF16
+    Rc, Hc = 32768, 7168
+    Xc = randn(Rc, Hc)
+    qc = mx.empty(mx.MX_MXINT8, Rc, Hc)
+    Yc = torch.empty(Rc, Hc, dtype=torch.bfloat16, device="cuda")
+    mask_c = mx.mx_rht_signs(0)
+    ms_e = time_fn(torch, lambda: mx.mx_quantize(Xc, qc, flags=mx.MX_FLAG_RHT16, sign_mask=mask_c), it, wu)
+    ms_d = time_fn(torch, lambda: mx.mx_dequantize(qc, Yc, mx.MX_FLAG_RHT16, mask_c), it, wu)
+    by_e = Rc * Hc * (2 + 1 + 1 / 32)
+    res["s2f6_combine_codec_32768x7168"] = {
+        "encode_ms": ms_e, "encode_gbs": by_e / ms_e / 1e6, "encode_frac_hbm": by_e / ms_e / 1e6 / PEAK_HBM_GBS,
+        "decode_ms": ms_d, "decode_gbs": by_e / ms_d / 1e6, "decode_frac_hbm": by_e / ms_d / 1e6 / PEAK_HBM_GBS,
+        "bits_per_value": 8.25}
+    # the other element types: quantize 8192x7168 BF16 (RNE)
+    Xq = Xc[:8192]
+    for name, f in (("mxint8", mx.MX_MXINT8), ("mxfp8_e5m2", mx.MX_MXFP8_E5M2),
+                    ("mxfp6_e3m2", mx.MX_MXFP6_E3M2), ("mxfp6_e2m3", mx.MX_MXFP6_E2M3)):
+        qf = mx.empty(f, 8192, Hc)
+        ms_f = time_fn(torch, lambda: mx.mx_quantize(Xq, qf), it, wu)
+        byf = 8192 * Hc * (2 + (0.75 if "fp6" in name else 1) + 1 / 32)
+        res[f"{name}_quantize_8192x7168"] = {"ms": ms_f, "gbs": byf / ms_f / 1e6,
+                                             "frac_hbm": byf / ms_f / 1e6 / PEAK_HBM_GBS}
+        del qf
+    del Xc, qc, Yc, Xq
+
     # RHT16 + NVFP4 SR of an 8192x7168 Student-t(3) gradient (two passes)
     G = torch.distributions.StudentT(3.0).sample((8192, 7168)).to(device="cuda", dtype=torch.bfloat16)
     qg = mx.empty(3, 8192, 7168)
