@@ -402,6 +402,21 @@ def detail(torch, mx, W, args):
                                              "frac_hbm": byf / ms_f / 1e6 / PEAK_HBM_GBS}
         del qf
     del Xc, qc, Yc, Xq
+    # products of the other MX formats and mixed pairs (4096^3, BF16 out)
+    M2 = 4096
+    Xa, Xb = randn(M2, M2), randn(M2, M2, 0.02)
+    Cm = torch.empty(M2, M2, dtype=torch.bfloat16, device="cuda")
+    for name, fa_, fb_ in (("mxint8_x_mxint8", mx.MX_MXINT8, mx.MX_MXINT8),
+                           ("e5m2_x_e4m3", mx.MX_MXFP8_E5M2, mx.MX_MXFP8_E4M3),
+                           ("fp6_e2m3_x_fp4", mx.MX_MXFP6_E2M3, mx.MX_MXFP4_E2M1)):
+        qa_, qb_ = mx.empty(fa_, M2, M2), mx.empty(fb_, M2, M2)
+        mx.mx_quantize(Xa, qa_)
+        mx.mx_quantize(Xb, qb_)
+        ms_m = time_fn(torch, lambda: mx.mx_gemm(qa_, qb_, Cm), it, wu)
+        res[f"gemm_4096_{name}"] = {"ms": ms_m, "tflops": 2 * M2**3 / ms_m / 1e9,
+                                    "frac_bf16_peak": 2 * M2**3 / ms_m / 1e9 / PEAK_TFLOPS["bf16"]}
+        del qa_, qb_
+    del Xa, Xb, Cm
 
     # RHT16 + NVFP4 SR of an 8192x7168 Student-t(3) gradient (two passes)
     G = torch.distributions.StudentT(3.0).sample((8192, 7168)).to(device="cuda", dtype=torch.bfloat16)

@@ -28,8 +28,10 @@
  *   MX_MXFP6_E3M2, MX_MXFP6_E2M3  FP6 (largest 28 / 7.5), packed 4 elements in
  *                  3 bytes: element c of a row at bits 6c .. 6c+5 of the row's
  *                  little-endian bit string.
- *   They are taken by mx_quantize, mx_amax and mx_dequantize (row layout);
- *   products of them are not offered (MX_ERR_UNSUPPORTED).
+ *   They are taken by mx_quantize, mx_amax and mx_dequantize, and as GEMM
+ *   operands by mx_gemm / mx_gemm_ex (row layout, no flags), also mixed with
+ *   MXFP8 E4M3 or MXFP4 (any pair of MX formats: A->fmt may differ from
+ *   B->fmt).
  *
  * Conventions shared by every call:
  *   - Pointers are device pointers (HIP), except the mx_tensor descriptor
@@ -260,7 +262,11 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
  *   NVFP4  e2m1 * e4m3 converted to exact FP16, FP16 matrix instructions
  *          (BF16 for shapes too small for the pipelined kernel), the FP32
  *          result multiplied by S_A * S_B.
- * Requirements: A->fmt == B->fmt; A->cols == B->cols == K; K % 32 == 0. */
+ *   Other MX pairs (mixed formats, INT8, E5M2, FP6): every element times its
+ *          scale decoded to exact BF16 (exact while the scaled values are
+ *          normal BF16 values), BF16 matrix instructions.
+ * Requirements: A->fmt == B->fmt, or both MX formats (E8M0 scales) in the
+ * row layout; A->cols == B->cols == K; K % 32 == 0. */
 mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,
                   mx_stream stream);
 

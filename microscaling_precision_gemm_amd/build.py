@@ -23,6 +23,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "gemm_staged.hip"),
     os.path.join(CSRC, "kernels", "gemm_tiled.hip"),
     os.path.join(CSRC, "kernels", "gemm_nvpipe.hip"),
+    os.path.join(CSRC, "kernels", "gemm_any.hip"),
 ]
 
 # -ffp-contract=off: the quantizers' FP32 scale arithmetic must round once per

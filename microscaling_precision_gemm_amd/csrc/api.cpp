@@ -227,7 +227,20 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
   if (st != MX_OK) return st;
   st = check_tensor(B, B->rows, B->cols);
   if (st != MX_OK) return st;
-  if (A->fmt != B->fmt || !core_fmt(A->fmt)) return MX_ERR_UNSUPPORTED;
+  if (A->fmt != B->fmt || !core_fmt(A->fmt)) {
+    // mixed formats or the other MX element types: every MX (E8M0) pair, row
+    // layout, exact BF16 staging
+    if (A->fmt == MX_NVFP4 || B->fmt == MX_NVFP4 || flags) return MX_ERR_UNSUPPORTED;
+    if (A->layout != MX_LAYOUT_ROWS || B->layout != MX_LAYOUT_ROWS) return MX_ERR_UNSUPPORTED;
+    if (A->cols != B->cols || A->cols % 32) return MX_ERR_SHAPE;
+    st = check_output(C, cdt, A->rows, B->rows, ldc);
+    if (st != MX_OK) return st;
+    if (A->rows * B->rows == 0) return MX_OK;
+    return hip_status(mxk::launch_gemm_mx_any(A->fmt, static_cast<const uint8_t*>(A->codes), A->scales,
+                                              B->fmt, static_cast<const uint8_t*>(B->codes), B->scales,
+                                              A->rows, B->rows, A->cols, C, cdt, ldc,
+                                              reinterpret_cast<hipStream_t>(stream)));
+  }
   if ((flags & MX_GEMM_FP8_NATIVE) && A->fmt != MX_MXFP8_E4M3) return MX_ERR_UNSUPPORTED;
   if (A->cols != B->cols || A->cols % 32) return MX_ERR_SHAPE;
   const bool tiled = A->layout == MX_LAYOUT_TILED;

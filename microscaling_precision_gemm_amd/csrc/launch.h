@@ -59,6 +59,11 @@ hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scal
                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
                           int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s);
 // A and B in the tiled layout (M, N multiples of 32, K of 1024)
+// C = A * B^T for any pair of MX formats (E8M0 scales; row layout), exact
+// BF16 staging (gemm_any.hip).
+hipError_t launch_gemm_mx_any(int fa, const uint8_t* a_codes, const uint8_t* a_scales, int fb,
+                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
+                              int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s);
 // C = A * B^T of tile-layout MX operands, written quantized along its rows
 // (MX format ofmt, row or tile layout) by the GEMM's epilogue.
 hipError_t launch_gemm_mx_tiled_quant(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,

@@ -88,14 +88,30 @@ def test_quantize_argument_checks(mx):
     assert q(FAKE, 0, 4, 64, 64, ctypes.byref(nocodes), 0, rng, 0, 0, None, None) == 1
 
 
+def test_gemm_format_pair_checks(mx):
+    """Mixed formats and the other MX element types: row layout, no flags, no
+    NVFP4 in the pair."""
+    L = mx.load()
+    g = lambda A, B, flags=0: L.mx_gemm_ex(ctypes.byref(A), ctypes.byref(B), FAKE, 1, 64, flags, None)
+    int8 = _t(mx, 4, 64, 256)
+    fp6 = _t(mx, 6, 64, 256)
+    nv = _t(mx, 3, 64, 256)
+    assert g(int8, nv) == 5
+    assert g(int8, fp6, 1) == 5
+    tiled = mx._Tensor(4, 1, 64, 1024, FAKE, FAKE, None)
+    assert g(tiled, tiled) == 5
+    short = _t(mx, 6, 64, 224)
+    assert g(int8, short) == 2
+
+
 def test_other_entry_point_checks(mx):
     L = mx.load()
     rng = mx._Rng(0, 0)
     a8 = _t(mx, 1, 64, 64)
     a4 = _t(mx, 2, 64, 64)
     nv = _t(mx, 3, 64, 64)
-    # gemm: mixed formats, K mismatch, K % 32, C pitch
-    assert L.mx_gemm(ctypes.byref(a8), ctypes.byref(a4), FAKE, 1, 64, None) == 5
+    # gemm: a mixed pair with NVFP4, K mismatch, K % 32, C pitch
+    assert L.mx_gemm(ctypes.byref(a8), ctypes.byref(nv), FAKE, 1, 64, None) == 5
     b = _t(mx, 1, 64, 96)
     assert L.mx_gemm(ctypes.byref(a8), ctypes.byref(b), FAKE, 1, 64, None) == 2
     assert L.mx_gemm(ctypes.byref(a8), ctypes.byref(a8), FAKE, 1, 63, None) == 2

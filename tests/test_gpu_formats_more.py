@@ -165,10 +165,65 @@ def test_s2f6_codec_moe_combine_size_sampled_rows():
 
 
 def test_other_formats_are_rejected_where_not_offered():
+    """A pair with NVFP4, flags on a generic pair, and the tile layout."""
     a = mx.empty(5, 64, 1024, device=dev())
+    nv = mx.empty(3, 64, 1024, device=dev())
     C = torch.empty(64, 64, dtype=torch.float32, device=dev())
     with pytest.raises(mx.MXError):
-        mx.mx_gemm(a, a, C)
+        mx.mx_gemm(a, nv, C)
+    with pytest.raises(mx.MXError):
+        mx.mx_gemm_ex(a, a, C, mx.MX_GEMM_FP8_NATIVE)
     tiled_fp6 = mx.empty(6, 64, 1024, device=dev(), layout=mx.MX_LAYOUT_TILED)
     with pytest.raises(mx.MXError):
         mx.mx_quantize(torch.zeros(64, 1024, dtype=torch.bfloat16, device=dev()), tiled_fp6)
+
+
+# --- products of any pair of MX formats ---------------------------------------
+ALL_MX = [1, 2, 4, 5, 6, 7]
+
+
+def _operand(fmt, rows, K, seed, tid, std):
+    x = W.normal_bf16(rows, K, std, seed, tid, outlier_entries=0.005, outlier_mult=20.0)
+    c, s, _ = oracle.quantize(x, fmt)
+    return c, s
+
+
+@pytest.mark.parametrize("fa", ALL_MX)
+@pytest.mark.parametrize("fb", ALL_MX)
+def test_gemm_any_pair_of_mx_formats(fa, fb):
+    """C = A * B^T with A and B in any MX formats (mixed included): exact
+    products of the decoded operands, FP32 accumulation, within
+    1e-5 * sum|a*b| of the oracle's FP64 product."""
+    M, N, K = 200, 136, 320
+    ca, sa = _operand(fa, M, K, fa * 10 + fb, 90, 1.0)
+    cb, sb = _operand(fb, N, K, fa * 10 + fb, 91, 0.05)
+    A = upload(fa, ca, sa)
+    A.cols = K
+    B = upload(fb, cb, sb)
+    B.cols = K
+    C = torch.empty(M, N, dtype=torch.float32, device=dev())
+    if fa == fb and fa in (1, 2):
+        pytest.skip("same-format MXFP8 / MXFP4 products have their own kernels and tests")
+    mx.mx_gemm(A, B, C)
+    torch.cuda.synchronize()
+    Cw, tol = oracle.gemm(oracle.dequantize_f64(fa, ca, sa, M, K), oracle.dequantize_f64(fb, cb, sb, N, K))
+    from tests.gpu_util import check_gemm
+    check_gemm(C.cpu().numpy(), Cw, tol, False, f"fa={fa} fb={fb}")
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 32), (257, 129, 96), (512, 640, 2048)])
+@pytest.mark.parametrize("cdt", ["f32", "bf16"])
+def test_gemm_any_ragged_shapes_and_bf16_output(shape, cdt):
+    M, N, K = shape
+    ca, sa = _operand(4, M, K, 5, 92, 1.0)       # MXINT8 activations
+    cb, sb = _operand(6, N, K, 5, 93, 0.05)      # MXFP6 E3M2 weights
+    A = upload(4, ca, sa)
+    A.cols = K
+    B = upload(6, cb, sb)
+    B.cols = K
+    C = torch.empty(M, N, dtype=torch.float32 if cdt == "f32" else torch.bfloat16, device=dev())
+    mx.mx_gemm(A, B, C)
+    torch.cuda.synchronize()
+    Cw, tol = oracle.gemm(oracle.dequantize_f64(4, ca, sa, M, K), oracle.dequantize_f64(6, cb, sb, N, K))
+    from tests.gpu_util import check_gemm
+    check_gemm(C.float().cpu().numpy(), Cw, tol, cdt == "bf16", f"{shape} {cdt}")
