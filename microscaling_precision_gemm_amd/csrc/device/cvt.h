@@ -36,4 +36,55 @@ __device__ inline void pack_e4m3_rne(const float y[8], uint32_t w[2]) {
   }
 }
 
+// ---- stochastic rounding on the conversion instructions ---------------------
+// The SR rule used throughout: with lo <= |y| < hi the neighbours, round up
+// exactly when r16 < floor((|y| - lo) * 2^16 / (hi - lo)).  gfx950's scaled
+// SR conversions take a 32-bit seed and round |y| up exactly when the seed's
+// top 16 bits are at least 2^16 - floor((|y| - lo) * 2^16 / (hi - lo)),
+// ignoring the lower seed bits and the lower fraction bits (measured on the
+// device), so the seed (~r16 & 0xFFFF) << 16 takes the rule's decision.
+// Inputs are clamped to the largest finite value first (the rule saturates;
+// the instruction would round past it).  Checked on the device against the
+// software encoders of codec.h for E4M3, E5M2 and E2M1 over every FP32 input
+// up to +Inf and its negative.  The FP4 pair instruction draws its first
+// element from seed bits 16..31 but its second from bits 15..30, so FP4 is
+// converted one element per instruction.
+typedef float v2f_cvt __attribute__((ext_vector_type(2)));
+
+__device__ inline uint32_t sr_seed(uint32_t r16) { return (~r16 & 0xFFFFu) << 16; }
+
+#define MXK_SR8(BUILTIN, MAXV)                                                                   \
+  _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                               \
+    const float* c = y + 4 * h;                                                                 \
+    const uint32_t* rr = r + 4 * h;                                                             \
+    int a = 0;                                                                                  \
+    a = BUILTIN(a, fmaxf(fminf(c[0], MAXV), -MAXV), sr_seed(rr[0]), 1.0f, 0);                   \
+    a = BUILTIN(a, fmaxf(fminf(c[1], MAXV), -MAXV), sr_seed(rr[1]), 1.0f, 1);                   \
+    a = BUILTIN(a, fmaxf(fminf(c[2], MAXV), -MAXV), sr_seed(rr[2]), 1.0f, 2);                   \
+    a = BUILTIN(a, fmaxf(fminf(c[3], MAXV), -MAXV), sr_seed(rr[3]), 1.0f, 3);                   \
+    w[h] = (uint32_t)a;                                                                         \
+  }
+
+// 8 E4M3 codes by SR (r: the 8 random 16-bit values), 4 per word
+__device__ inline void pack_e4m3_sr(const float y[8], const uint32_t r[8], uint32_t w[2]) {
+  MXK_SR8(__builtin_amdgcn_cvt_scalef32_sr_fp8_f32, 448.0f)
+}
+// 8 E5M2 codes by SR
+__device__ inline void pack_e5m2_sr(const float y[8], const uint32_t r[8], uint32_t w[2]) {
+  MXK_SR8(__builtin_amdgcn_cvt_scalef32_sr_bf8_f32, 57344.0f)
+}
+#undef MXK_SR8
+
+// 8 E2M1 codes by SR, element i in nibble i
+__device__ inline uint32_t pack_e2m1_sr(const float y[8], const uint32_t r[8]) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float c = fmaxf(fminf(y[i], 6.0f), -6.0f);
+    const uint32_t t = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, v2f_cvt{c, c}, sr_seed(r[i]), 1.0f, 0);
+    w |= (t & 0xFu) << (4 * i);
+  }
+  return w;
+}
+
 }  // namespace mxk

@@ -95,8 +95,15 @@ __device__ inline void encode_mx(const MxEnc& a, int64_t q, const float v[8], En
     uint32_t r[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     if constexpr (SR) rand16x8(a.seed, a.counter, (uint64_t)q, r);
     uint32_t c[8];
+    if constexpr (FMT == FMT_MXFP8_E5M2 && SR) {  // SR on the conversion instruction
+      uint32_t w8[2];
+      pack_e5m2_sr(y, r, w8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = mx_elem_encode<FMT>(y[i], SR, r[i]);
+      for (int i = 0; i < 8; ++i) c[i] = (w8[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = mx_elem_encode<FMT>(y[i], SR, r[i]);
+    }
     if constexpr (MxFmt<FMT>::bits == 8) {
       e.w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
       e.w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
@@ -110,22 +117,11 @@ __device__ inline void encode_mx(const MxEnc& a, int64_t q, const float v[8], En
     } else {
       e.w[0] = pack_e2m1_rne(y);
     }
-  } else {
+  } else {  // SR on the conversion instructions (cvt.h)
     uint32_t r[8];
     rand16x8(a.seed, a.counter, (uint64_t)q, r);
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      c[i] = FMT == FMT_MXFP8 ? e4m3_encode(y[i], true, r[i]) : e2m1_encode(y[i], true, r[i]);
-    if constexpr (FMT == FMT_MXFP8) {
-      e.w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-      e.w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-    } else {
-      uint32_t p = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p |= c[i] << (4 * i);
-      e.w[0] = p;
-    }
+    if constexpr (FMT == FMT_MXFP8) pack_e4m3_sr(y, r, e.w);
+    else e.w[0] = pack_e2m1_sr(y, r);
   }
   if (sc == 0xFFu) {  // NaN / Inf in the block
 #pragma unroll

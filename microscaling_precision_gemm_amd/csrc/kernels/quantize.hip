@@ -333,10 +333,7 @@ __device__ inline void encode_nv(const QuantArgs& a, float S, float d, int64_t q
   } else {
     uint32_t r[8];
     rand16x8(a.seed, a.counter, (uint64_t)q, r);
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= e2m1_encode(y[i], true, r[i]) << (4 * i);
-    e.w[0] = packed;
+    e.w[0] = pack_e2m1_sr(y, r);  // SR on the conversion instruction
   }
   e.sc = sb;
 }
@@ -527,9 +524,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4_2d(QuantArgs a, int64_
     } else {
       uint32_t r[8];
       rand16x8(a.seed, a.counter, (uint64_t)((row[u] * cols + col[u]) >> 3), r);
-      w[u] = 0u;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) w[u] |= e2m1_encode(y[j], true, r[j]) << (4 * j);
+      w[u] = pack_e2m1_sr(y, r);  // SR on the conversion instruction
     }
     // lane 8 i + 2 p holds block p of its row's 64-column group: gather the
     // group's 4 scale bytes into lane 8 i

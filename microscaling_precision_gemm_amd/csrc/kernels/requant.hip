@@ -190,11 +190,7 @@ __global__ __launch_bounds__(256) void k_requant_t(const uint8_t* __restrict__ s
     if constexpr (SR) {
       uint32_t rnd[8];
       rand16x8(seed, counter, (uint64_t)(n >> 3), rnd);
-      uint32_t cc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) cc[i] = e4m3_encode(y[i], true, rnd[i]);
-      p[0] = cc[0] | (cc[1] << 8) | (cc[2] << 16) | (cc[3] << 24);
-      p[1] = cc[4] | (cc[5] << 8) | (cc[6] << 16) | (cc[7] << 24);
+      pack_e4m3_sr(y, rnd, p);  // SR on the conversion instruction
     } else {
       pack_e4m3_rne(y, p);
     }
