@@ -214,6 +214,29 @@ mx_status mx_quantize(const void* x, int32_t xdt, int64_t rows, int64_t cols, in
                       const mx_tensor* out, int32_t rnd, mx_rng rng, uint32_t flags,
                       uint16_t rht_sign_mask, float* amax, mx_stream stream);
 
+/* Several quantizations in one call: jobs[i] holds the arguments of one
+ * mx_quantize call, and the result is that of calling mx_quantize on jobs[0],
+ * jobs[1], ... in order on `stream`.  Consecutive jobs that write MXFP8 or
+ * MXFP4 in the tile layout with the same format, input dtype, rounding and
+ * MX_FLAG_RHT16 setting are quantized by one kernel launch (up to 4 per
+ * launch), which saves the launch gaps and the ramp of small tensors; other
+ * jobs are launched one by one.  Every job is checked before anything is
+ * enqueued; the first failing job's status is returned.  No job's input may
+ * be written by an earlier job of the same call.  `jobs` is a host array;
+ * `out` points to a host descriptor. */
+typedef struct {
+  const void* x;
+  int32_t xdt;
+  int64_t rows, cols, ld_x;
+  const mx_tensor* out;
+  int32_t rnd;
+  mx_rng rng;
+  uint32_t flags;
+  uint16_t rht_sign_mask;
+  float* amax;
+} mx_quantize_job;
+mx_status mx_quantize_batch(const mx_quantize_job* jobs, int32_t count, mx_stream stream);
+
 /* Per-tensor amax of x (after the Hadamard transform when MX_FLAG_RHT16 is
  * set) into *amax (device float, overwritten).  The first pass of NVFP4
  * quantization ([MXF] "NVFP4": second-level per-tensor scale). */

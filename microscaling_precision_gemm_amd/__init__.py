@@ -32,7 +32,7 @@ FORMATS = {"mxfp8": MX_MXFP8_E4M3, "mxfp4": MX_MXFP4_E2M1, "nvfp4": MX_NVFP4, "m
 EXPORTED = [
     "mx_codes_bytes", "mx_scales_bytes", "mx_rht_signs", "mx_quantize", "mx_amax",
     "mx_dequantize", "mx_requant_transpose", "mx_hadamard16", "mx_gemm", "mx_gemm_ex",
-    "mx_gemm_grouped", "mx_gemm_quantize",
+    "mx_gemm_grouped", "mx_gemm_quantize", "mx_quantize_batch",
     "mx_status_string",
 ]
 
@@ -49,6 +49,13 @@ class _Tensor(ctypes.Structure):
 
 class _Rng(ctypes.Structure):
     _fields_ = [("seed", ctypes.c_uint64), ("counter", ctypes.c_uint64)]
+
+
+class _Job(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("xdt", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("ld_x", ctypes.c_int64), ("out", ctypes.POINTER(_Tensor)),
+                ("rnd", ctypes.c_int32), ("rng", _Rng), ("flags", ctypes.c_uint32),
+                ("rht_sign_mask", ctypes.c_uint16), ("amax", ctypes.c_void_p)]
 
 
 _lib = None
@@ -78,6 +85,7 @@ def load():
         "mx_gemm_ex": (i32, [TP, TP, vp, i32, i64, u32, vp]),
         "mx_gemm_grouped": (i32, [TP, vp, i64, TP, i32, vp, vp, i32, i64, vp]),
         "mx_gemm_quantize": (i32, [TP, TP, TP, i32, _Rng, u32, vp]),
+        "mx_quantize_batch": (i32, [ctypes.POINTER(_Job), i32, vp]),
         "mx_status_string": (ctypes.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -178,6 +186,35 @@ def mx_quantize(x, out: MXTensor, rnd: int = MX_RNE, seed: int = 0, counter: int
     _check(L.mx_quantize(_ptr(x), _dt(x), x.shape[0], x.shape[1], x.stride(0), ctypes.byref(d),
                          rnd, _Rng(seed, counter), flags, sign_mask, _ptr(amax), _stream(stream)))
     return out
+
+
+class QuantizeBatch:
+    """A prepared mx_quantize_batch call: the job array is built once (the
+    tensors must stay alive), and each run() is one call of the C function."""
+
+    def __init__(self, jobs):
+        self._descs = [j["out"].desc() for j in jobs]
+        self._keep = [j["x"] for j in jobs] + [j["out"] for j in jobs]
+        self._arr = (_Job * max(len(jobs), 1))()
+        for i, j in enumerate(jobs):
+            x = j["x"]
+            self._arr[i] = _Job(_ptr(x), _dt(x), x.shape[0], x.shape[1], x.stride(0),
+                                ctypes.pointer(self._descs[i]), j.get("rnd", MX_RNE),
+                                _Rng(j.get("seed", 0), j.get("counter", 0)), j.get("flags", 0),
+                                j.get("sign_mask", 0), _ptr(j.get("amax")))
+        self._n = len(jobs)
+        self._fn = load().mx_quantize_batch
+
+    def run(self, stream=None):
+        _check(self._fn(self._arr, self._n, _stream(stream)))
+
+
+def mx_quantize_batch(jobs, stream=None):
+    """Several mx_quantize calls in one: each job is a dict with the keys of
+    mx_quantize (x, out, and optionally rnd, seed, counter, flags, sign_mask,
+    amax).  Compatible tile-layout jobs share kernel launches."""
+    QuantizeBatch(jobs).run(stream)
+    return [j["out"] for j in jobs]
 
 
 def mx_amax(x, amax, flags: int = 0, sign_mask: int = 0, stream=None):

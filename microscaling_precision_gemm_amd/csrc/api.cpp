@@ -103,9 +103,12 @@ const char* mx_status_string(int32_t s) {
   }
 }
 
-mx_status mx_quantize(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ld_x,
-                      const mx_tensor* out, int32_t rnd, mx_rng rng, uint32_t flags,
-                      uint16_t rht_sign_mask, float* amax, mx_stream stream) {
+namespace {
+// Checks the arguments of one quantization and fills its kernel arguments.
+mx_status make_quant_args(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ld_x,
+                          const mx_tensor* out, int32_t rnd, mx_rng rng, uint32_t flags,
+                          uint16_t rht_sign_mask, float* amax, mxk::QuantArgs* a, bool* empty) {
+  *empty = false;
   if (!out) return MX_ERR_NULL;
   if (rnd != MX_RNE && rnd != MX_SR) return MX_ERR_FORMAT;
   if (flags & ~(MX_FLAG_RHT16 | MX_FLAG_AMAX_GIVEN | MX_FLAG_SCALE_CEIL | MX_FLAG_FOUR_OVER_SIX |
@@ -126,29 +129,75 @@ mx_status mx_quantize(const void* x, int32_t xdt, int64_t rows, int64_t cols, in
   } else if (flags & MX_FLAG_AMAX_GIVEN) {
     return MX_ERR_UNSUPPORTED;
   }
-  if (rows * cols == 0 && out->fmt != MX_NVFP4) return MX_OK;
+  if (rows * cols == 0 && out->fmt != MX_NVFP4) {
+    *empty = true;
+    return MX_OK;
+  }
+  a->x = x;
+  a->xdt = xdt;
+  a->rows = rows;
+  a->cols = cols;
+  a->ld_x = ld_x;
+  a->fmt = out->fmt;
+  a->codes = static_cast<uint8_t*>(out->codes);
+  a->scales = out->scales;
+  a->tensor_scale = out->tensor_scale;
+  a->amax = amax;
+  a->sr = rnd == MX_SR;
+  a->seed = rng.seed;
+  a->counter = rng.counter;
+  a->rht = (flags & MX_FLAG_RHT16) != 0;
+  a->sign_mask = rht_sign_mask;
+  a->amax_given = (flags & MX_FLAG_AMAX_GIVEN) != 0;
+  a->tiled = out->layout == MX_LAYOUT_TILED;
+  a->ceil = (flags & MX_FLAG_SCALE_CEIL) != 0;
+  a->four6 = (flags & MX_FLAG_FOUR_OVER_SIX) != 0;
+  a->block2d = (flags & MX_FLAG_BLOCK_2D) != 0;
+  return MX_OK;
+}
+}  // namespace
+
+mx_status mx_quantize(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ld_x,
+                      const mx_tensor* out, int32_t rnd, mx_rng rng, uint32_t flags,
+                      uint16_t rht_sign_mask, float* amax, mx_stream stream) {
   mxk::QuantArgs a;
-  a.x = x;
-  a.xdt = xdt;
-  a.rows = rows;
-  a.cols = cols;
-  a.ld_x = ld_x;
-  a.fmt = out->fmt;
-  a.codes = static_cast<uint8_t*>(out->codes);
-  a.scales = out->scales;
-  a.tensor_scale = out->tensor_scale;
-  a.amax = amax;
-  a.sr = rnd == MX_SR;
-  a.seed = rng.seed;
-  a.counter = rng.counter;
-  a.rht = (flags & MX_FLAG_RHT16) != 0;
-  a.sign_mask = rht_sign_mask;
-  a.amax_given = (flags & MX_FLAG_AMAX_GIVEN) != 0;
-  a.tiled = out->layout == MX_LAYOUT_TILED;
-  a.ceil = (flags & MX_FLAG_SCALE_CEIL) != 0;
-  a.four6 = (flags & MX_FLAG_FOUR_OVER_SIX) != 0;
-  a.block2d = (flags & MX_FLAG_BLOCK_2D) != 0;
+  bool empty = false;
+  const mx_status st = make_quant_args(x, xdt, rows, cols, ld_x, out, rnd, rng, flags, rht_sign_mask, amax,
+                                       &a, &empty);
+  if (st != MX_OK || empty) return st;
   return hip_status(mxk::launch_quantize(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_quantize_batch(const mx_quantize_job* jobs, int32_t count, mx_stream stream) {
+  if (count < 0) return MX_ERR_SHAPE;
+  if (count == 0) return MX_OK;
+  if (!jobs) return MX_ERR_NULL;
+  // every job is checked before anything is enqueued
+  for (int32_t i = 0; i < count; ++i) {
+    const mx_quantize_job& j = jobs[i];
+    mxk::QuantArgs a;
+    bool empty = false;
+    const mx_status st = make_quant_args(j.x, j.xdt, j.rows, j.cols, j.ld_x, j.out, j.rnd, j.rng, j.flags,
+                                         j.rht_sign_mask, j.amax, &a, &empty);
+    if (st != MX_OK) return st;
+  }
+  constexpr int kChunk = 64;  // then built and launched kChunk at a time
+  mxk::QuantArgs args[kChunk];
+  for (int32_t i0 = 0; i0 < count; i0 += kChunk) {
+    int n = 0;
+    const int32_t i1 = count - i0 < kChunk ? count : i0 + kChunk;
+    for (int32_t i = i0; i < i1; ++i) {
+      const mx_quantize_job& j = jobs[i];
+      bool empty = false;
+      const mx_status st = make_quant_args(j.x, j.xdt, j.rows, j.cols, j.ld_x, j.out, j.rnd, j.rng, j.flags,
+                                           j.rht_sign_mask, j.amax, &args[n], &empty);
+      if (st != MX_OK) return st;
+      if (!empty) ++n;
+    }
+    const mx_status st = hip_status(mxk::launch_quantize_batch(args, n, reinterpret_cast<hipStream_t>(stream)));
+    if (st != MX_OK) return st;
+  }
+  return MX_OK;
 }
 
 mx_status mx_amax(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ld_x,

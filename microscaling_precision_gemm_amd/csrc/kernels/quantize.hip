@@ -233,13 +233,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx(QuantArgs a, int64_t Q) {
 // branchy encoders need most.
 constexpr int kTiledNT = 4;
 
+// One wave of the tile-layout quantizer (wave index within its tensor).
 template <int XDT, int FMT, bool SR, bool RHT>
-__global__ __launch_bounds__(kThreads) void k_quant_mx_tiled(QuantArgs a, int64_t nwaves) {
+__device__ __attribute__((always_inline)) inline void quant_tiled_wave(const QuantArgs& a, int64_t wave) {
   constexpr int NT = kTiledNT;
   constexpr int kParts = 16 / NT;  // waves per scale group and row octet
   const uint32_t lane = threadIdx.x & 63u;
-  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  if (wave >= nwaves) return;  // whole waves
   const int64_t gpr = a.cols >> 10;  // scale groups per row
   const int64_t wpr = gpr * kParts;  // waves per row octet
   const int64_t R8 = wave / wpr, rem = wave - R8 * wpr;
@@ -296,12 +295,48 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx_tiled(QuantArgs a, int64_
 }
 
 template <int XDT, int FMT, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads) void k_quant_mx_tiled(QuantArgs a, int64_t nwaves) {
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  if (wave >= nwaves) return;  // whole waves
+  quant_tiled_wave<XDT, FMT, SR, RHT>(a, wave);
+}
+
+// Several tensors in one launch (same format, input dtype, rounding and
+// transform): the waves of job j are [first[j], first[j+1]).  Every job has
+// a multiple of 4 waves, so a workgroup never spans two jobs.
+// The job is chosen from the workgroup's first wave, so the choice is
+// uniform and its arguments come in through scalar loads.
+template <int XDT, int FMT, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads) void k_quant_mx_tiled_batch(QuantBatch b) {
+  const int64_t wave0 = (int64_t)blockIdx.x * (kThreads / 64);
+  int j = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxBatch; ++k) j += (k < b.n && wave0 >= b.first[k]) ? 1 : 0;
+  const int64_t wave = wave0 + (threadIdx.x >> 6);
+  if (wave >= b.first[b.n]) return;
+  quant_tiled_wave<XDT, FMT, SR, RHT>(b.job[j], wave - b.first[j]);
+}
+
+template <int XDT, int FMT, bool SR, bool RHT>
 hipError_t quant_mx_tiled_t(const QuantArgs& a, hipStream_t s) {
   const int64_t nwaves = (a.rows / 8) * (a.cols / (64 * kTiledNT));
   const int64_t blocks = (nwaves + 3) / 4;
   hipLaunchKernelGGL((k_quant_mx_tiled<XDT, FMT, SR, RHT>), dim3((uint32_t)blocks), dim3(kThreads), 0, s, a, nwaves);
   return hipGetLastError();
 }
+template <int XDT, int FMT, bool SR, bool RHT>
+hipError_t quant_mx_tiled_batch_t(const QuantBatch& b, hipStream_t s) {
+  const int64_t blocks = (b.first[b.n] + 3) / 4;
+  hipLaunchKernelGGL((k_quant_mx_tiled_batch<XDT, FMT, SR, RHT>), dim3((uint32_t)blocks), dim3(kThreads), 0, s, b);
+  return hipGetLastError();
+}
+template <int XDT, int FMT>
+hipError_t quant_mx_tiled_batch_d(const QuantBatch& b, hipStream_t s) {
+  const QuantArgs& a = b.job[0];
+  if (a.sr) return a.rht ? quant_mx_tiled_batch_t<XDT, FMT, true, true>(b, s) : quant_mx_tiled_batch_t<XDT, FMT, true, false>(b, s);
+  return a.rht ? quant_mx_tiled_batch_t<XDT, FMT, false, true>(b, s) : quant_mx_tiled_batch_t<XDT, FMT, false, false>(b, s);
+}
+
 template <int XDT, int FMT>
 hipError_t quant_mx_tiled_d(const QuantArgs& a, hipStream_t s) {
   if (a.sr) return a.rht ? quant_mx_tiled_t<XDT, FMT, true, true>(a, s) : quant_mx_tiled_t<XDT, FMT, true, false>(a, s);
@@ -807,6 +842,44 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
     default: MXK_QD(FMT_MXFP6_E2M3);
   }
 #undef MXK_QD
+}
+
+namespace {
+// jobs that can share one tile-layout launch
+bool batchable(const QuantArgs& a) {
+  return a.tiled && (a.fmt == FMT_MXFP8 || a.fmt == FMT_MXFP4) && a.rows * a.cols > 0;
+}
+bool same_kernel(const QuantArgs& a, const QuantArgs& b) {
+  return a.fmt == b.fmt && a.xdt == b.xdt && a.sr == b.sr && a.rht == b.rht;
+}
+}  // namespace
+
+hipError_t launch_quantize_batch(const QuantArgs* a, int n, hipStream_t s) {
+  int i = 0;
+  while (i < n) {
+    int m = 1;
+    if (batchable(a[i]))
+      while (m < kMaxBatch && i + m < n && batchable(a[i + m]) && same_kernel(a[i], a[i + m])) ++m;
+    hipError_t e;
+    if (m == 1) {
+      e = launch_quantize(a[i], s);
+    } else {
+      QuantBatch b{};
+      b.n = m;
+      b.first[0] = 0;
+      for (int k = 0; k < m; ++k) {
+        b.job[k] = a[i + k];
+        b.first[k + 1] = b.first[k] + (a[i + k].rows / 8) * (a[i + k].cols / (64 * kTiledNT));
+      }
+      if (a[i].fmt == FMT_MXFP8)
+        e = a[i].xdt == DT_BF16 ? quant_mx_tiled_batch_d<DT_BF16, FMT_MXFP8>(b, s) : quant_mx_tiled_batch_d<DT_F32, FMT_MXFP8>(b, s);
+      else
+        e = a[i].xdt == DT_BF16 ? quant_mx_tiled_batch_d<DT_BF16, FMT_MXFP4>(b, s) : quant_mx_tiled_batch_d<DT_F32, FMT_MXFP4>(b, s);
+    }
+    if (e != hipSuccess) return e;
+    i += m;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales,

@@ -42,6 +42,19 @@ struct QuantArgs {
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+
+// Up to kMaxBatch tile-layout MX quantizations in one launch.
+constexpr int kMaxBatch = 4;
+struct QuantBatch {
+  QuantArgs job[kMaxBatch];
+  int64_t first[kMaxBatch + 1];  // first wave of each job; first[n] = total
+  int n;
+};
+// Quantize n tensors: one launch per group of up to kMaxBatch consecutive
+// jobs that are tile-layout MX with the same format, input dtype, rounding
+// and transform; any other job is launched on its own.  Same results as n
+// launch_quantize calls in order.
+hipError_t launch_quantize_batch(const QuantArgs* a, int n, hipStream_t s);
 hipError_t launch_amax(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ld_x, bool rht,
                        uint32_t sign_mask, float* amax, hipStream_t s);
 hipError_t launch_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales,

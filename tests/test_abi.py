@@ -88,6 +88,24 @@ def test_quantize_argument_checks(mx):
     assert q(FAKE, 0, 4, 64, 64, ctypes.byref(nocodes), 0, rng, 0, 0, None, None) == 1
 
 
+def test_quantize_batch_checks(mx):
+    """Every job is checked before anything is enqueued: a bad job after a
+    good one returns the bad job's status (without a GPU an enqueued launch
+    would have returned MX_ERR_HIP instead)."""
+    L = mx.load()
+    assert L.mx_quantize_batch(None, 0, None) == 0
+    assert L.mx_quantize_batch(None, 2, None) == 1
+    assert L.mx_quantize_batch(None, -1, None) == 2
+    good = mx._Tensor(2, 1, 32, 1024, FAKE, FAKE, None)
+    bad = _t(mx, 1, 4, 48)
+    jobs = (mx._Job * 2)()
+    jobs[0] = mx._Job(FAKE, 0, 32, 1024, 1024, ctypes.pointer(good), 0, mx._Rng(0, 0), 0, 0, None)
+    jobs[1] = mx._Job(FAKE, 0, 4, 48, 48, ctypes.pointer(bad), 0, mx._Rng(0, 0), 0, 0, None)
+    assert L.mx_quantize_batch(jobs, 2, None) == 2
+    jobs[1] = mx._Job(FAKE, 0, 32, 1024, 1024, ctypes.pointer(good), 0, mx._Rng(0, 0), 64, 0, None)
+    assert L.mx_quantize_batch(jobs, 2, None) == 5
+
+
 def test_gemm_format_pair_checks(mx):
     """Mixed formats and the other MX element types: row layout, no flags, no
     NVFP4 in the pair."""

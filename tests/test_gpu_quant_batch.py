@@ -1,0 +1,87 @@
+"""mx_quantize_batch against individual mx_quantize calls, bit for bit:
+tile-layout jobs that share launches (more than one launch's worth, mixed
+shapes, per-job random streams), and lists mixing in jobs that are launched on
+their own (row layout, NVFP4, other input dtypes)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import microscaling_precision_gemm_amd as mx
+    from tests.gpu_util import dev, host, to_gpu_bf16, to_gpu_f32
+
+
+def _x(rows, cols, seed, f32=False):
+    bits = W.normal_bf16(rows, cols, 1.0, seed, 100, outlier_entries=0.002, outlier_mult=40.0)
+    if f32:
+        return to_gpu_f32(W.bf16_bits_to_f32(bits))
+    return to_gpu_bf16(bits)
+
+
+def _job(x, fmt, layout, rnd=0, seed=0, counter=0, flags=0, mask=0, amax=None):
+    out = mx.empty(fmt, x.shape[0], x.shape[1], device=dev(), layout=layout)
+    return dict(x=x, out=out, rnd=rnd, seed=seed, counter=counter, flags=flags, sign_mask=mask, amax=amax)
+
+
+def _single(j):
+    out = mx.empty(j["out"].fmt, j["x"].shape[0], j["x"].shape[1], device=dev(), layout=j["out"].layout)
+    amax = None
+    if j["amax"] is not None:
+        amax = torch.zeros(1, dtype=torch.float32, device=dev())
+    mx.mx_quantize(j["x"], out, j["rnd"], j["seed"], j["counter"], j["flags"], j["sign_mask"], amax)
+    return out
+
+
+def _check(jobs):
+    mx.mx_quantize_batch(jobs)
+    singles = [_single(j) for j in jobs]
+    torch.cuda.synchronize()
+    for k, (j, s) in enumerate(zip(jobs, singles)):
+        c, sc, ts = host(j["out"])
+        c2, sc2, ts2 = host(s)
+        assert np.array_equal(sc, sc2), f"job {k}: scales"
+        assert np.array_equal(c, c2), f"job {k}: codes"
+        if ts is not None:
+            assert np.array_equal(ts, ts2), f"job {k}: tensor scale"
+
+
+def test_two_tiled_mxfp4_operands():
+    T = mx.MX_LAYOUT_TILED
+    _check([_job(_x(4096, 4096, 1), 2, T), _job(_x(4096, 4096, 2), 2, T)])
+
+
+@pytest.mark.parametrize("rnd,rht", [(0, False), (1, False), (1, True)])
+def test_more_jobs_than_one_launch_mixed_shapes(rnd, rht):
+    T = mx.MX_LAYOUT_TILED
+    flags = mx.MX_FLAG_RHT16 if rht else 0
+    shapes = [(32, 1024), (96, 2048), (256, 3072), (64, 1024), (128, 2048), (32, 4096)]
+    jobs = [_job(_x(r, c, 10 + i), 1, T, rnd, 7 + i, 1000 * i, flags, mx.mx_rht_signs(i) if rht else 0)
+            for i, (r, c) in enumerate(shapes)]
+    _check(jobs)
+
+
+def test_lists_with_jobs_launched_on_their_own():
+    T, Rw = mx.MX_LAYOUT_TILED, mx.MX_LAYOUT_ROWS
+    amax = torch.zeros(1, dtype=torch.float32, device=dev())
+    jobs = [
+        _job(_x(64, 1024, 20), 2, T),
+        _job(_x(64, 1024, 21), 2, T, flags=mx.MX_FLAG_SCALE_CEIL),
+        _job(_x(48, 512, 22), 1, Rw, rnd=1, seed=3),
+        _job(_x(64, 1024, 23), 2, T),
+        _job(_x(64, 512, 24), 3, Rw, amax=amax),
+        _job(_x(64, 1024, 25, f32=True), 2, T),
+        _job(_x(64, 1024, 26), 1, T),
+        _job(_x(96, 2048, 27), 1, T),
+    ]
+    _check(jobs)
+
+
+def test_empty_jobs_and_empty_list():
+    mx.mx_quantize_batch([])
+    T = mx.MX_LAYOUT_TILED
+    z = torch.empty(0, 1024, dtype=torch.bfloat16, device=dev())
+    _check([_job(z, 2, mx.MX_LAYOUT_ROWS), _job(_x(32, 1024, 30), 2, T)])
