@@ -415,7 +415,15 @@ def detail(torch, mx, W, args):
         res[f"gemm_4096_{name}"] = {"ms": ms_m, "tflops": 2 * M2**3 / ms_m / 1e9,
                                     "frac_bf16_peak": 2 * M2**3 / ms_m / 1e9 / PEAK_TFLOPS["bf16"]}
         del qa_, qb_
-    del Xa, Xb, Cm
+    # E5M2 x E4M3 in the tile layout on the scaled FP8 instruction (MX_GEMM_FP8_NATIVE)
+    qa_ = mx.empty(mx.MX_MXFP8_E5M2, M2, M2, layout=mx.MX_LAYOUT_TILED)
+    qb_ = mx.empty(mx.MX_MXFP8_E4M3, M2, M2, layout=mx.MX_LAYOUT_TILED)
+    mx.mx_quantize(Xa, qa_)
+    mx.mx_quantize(Xb, qb_)
+    ms_m = time_fn(torch, lambda: mx.mx_gemm_ex(qa_, qb_, Cm, mx.MX_GEMM_FP8_NATIVE), it, wu)
+    res["gemm_4096_e5m2_x_e4m3_native_fp8_tiled"] = {"ms": ms_m, "tflops": 2 * M2**3 / ms_m / 1e9,
+                                                     "frac_fp8_peak": 2 * M2**3 / ms_m / 1e9 / PEAK_TFLOPS["fp8"]}
+    del qa_, qb_, Xa, Xb, Cm
 
     # RHT16 + NVFP4 SR of an 8192x7168 Student-t(3) gradient (two passes)
     G = torch.distributions.StudentT(3.0).sample((8192, 7168)).to(device="cuda", dtype=torch.bfloat16)

@@ -31,7 +31,9 @@
  *   They are taken by mx_quantize, mx_amax and mx_dequantize, and as GEMM
  *   operands by mx_gemm / mx_gemm_ex (row layout, no flags), also mixed with
  *   MXFP8 E4M3 or MXFP4 (any pair of MX formats: A->fmt may differ from
- *   B->fmt).
+ *   B->fmt).  MX_MXFP8_E5M2 also has the tile layout; a tiled pair of E4M3 /
+ *   E5M2 operands with at least one E5M2 runs on the scaled FP8 instruction
+ *   with MX_GEMM_FP8_NATIVE (that flag's bound).
  *
  * Conventions shared by every call:
  *   - Pointers are device pointers (HIP), except the mx_tensor descriptor
@@ -119,8 +121,9 @@ typedef struct {
  *
  * layout (mx_layout) selects how the code and scale bytes are ordered:
  *   MX_LAYOUT_ROWS   the row-major arrays above (every format, every call).
- *   MX_LAYOUT_TILED  matrix-instruction tiles (MX formats only; rows % 32 ==
- *           0 and cols % 1024 == 0).  Same byte counts as MX_LAYOUT_ROWS.
+ *   MX_LAYOUT_TILED  matrix-instruction tiles (MXFP8 E4M3 / E5M2 and MXFP4;
+ *           rows % 32 == 0 and cols % 1024 == 0).  Same byte counts as
+ *           MX_LAYOUT_ROWS.
  *     codes: the [rows, row_bytes] code matrix is cut into tiles of 32 rows x
  *           128 bytes (256 FP4 or 128 FP8 elements); tile (T, t) (rows 32T..,
  *           code bytes 128t..) is 4096 contiguous bytes at byte offset

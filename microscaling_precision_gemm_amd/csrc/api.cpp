@@ -38,7 +38,8 @@ mx_status check_tensor(const mx_tensor* t, int64_t rows, int64_t cols) {
   if (t->rows != rows || t->cols != cols || rows < 0 || cols < 0) return MX_ERR_SHAPE;
   if (cols % block_of(t->fmt)) return MX_ERR_SHAPE;
   if (t->layout == MX_LAYOUT_TILED) {
-    if (t->fmt != MX_MXFP8_E4M3 && t->fmt != MX_MXFP4_E2M1) return MX_ERR_UNSUPPORTED;
+    if (t->fmt != MX_MXFP8_E4M3 && t->fmt != MX_MXFP4_E2M1 && t->fmt != MX_MXFP8_E5M2)
+      return MX_ERR_UNSUPPORTED;
     if (rows % 32 || cols % 1024) return MX_ERR_SHAPE;
   }
   if (rows * cols > 0) {
@@ -276,6 +277,21 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
   if (st != MX_OK) return st;
   st = check_tensor(B, B->rows, B->cols);
   if (st != MX_OK) return st;
+  const bool fp8a = A->fmt == MX_MXFP8_E4M3 || A->fmt == MX_MXFP8_E5M2;
+  const bool fp8b = B->fmt == MX_MXFP8_E4M3 || B->fmt == MX_MXFP8_E5M2;
+  if (A->layout == MX_LAYOUT_TILED && B->layout == MX_LAYOUT_TILED && fp8a && fp8b &&
+      (A->fmt == MX_MXFP8_E5M2 || B->fmt == MX_MXFP8_E5M2)) {
+    // FP8 pairs with E5M2 in the tile layout: the scaled FP8 instruction
+    if (!(flags & MX_GEMM_FP8_NATIVE)) return MX_ERR_UNSUPPORTED;
+    if (A->cols != B->cols) return MX_ERR_SHAPE;
+    st = check_output(C, cdt, A->rows, B->rows, ldc);
+    if (st != MX_OK) return st;
+    if (A->rows * B->rows == 0) return MX_OK;
+    return hip_status(mxk::launch_gemm_mx_tiled(A->fmt, static_cast<const uint8_t*>(A->codes), A->scales,
+                                                static_cast<const uint8_t*>(B->codes), B->scales, A->rows,
+                                                B->rows, A->cols, C, cdt, ldc,
+                                                reinterpret_cast<hipStream_t>(stream), B->fmt));
+  }
   if (A->fmt != B->fmt || !core_fmt(A->fmt)) {
     // mixed formats or the other MX element types: every MX (E8M0) pair, row
     // layout, exact BF16 staging
@@ -305,7 +321,7 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
   const uint8_t* bc = static_cast<const uint8_t*>(B->codes);
   if (tiled)
     return hip_status(mxk::launch_gemm_mx_tiled(A->fmt, ac, A->scales, bc, B->scales, M, N, K, C,
-                                                cdt, ldc, s));
+                                                cdt, ldc, s, B->fmt));
   switch (A->fmt) {
     case MX_NVFP4:
       // one group covering all rows (no offsets array needed)

@@ -72,10 +72,15 @@ __device__ inline v8i widen(u4 lo, u4 hi) {
   return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
+// Matrix-instruction element types (cbsz / blgp): FP8 E4M3 0, FP8 E5M2 1,
+// FP4 E2M1 4.  A and B may differ within a width class (8-bit or FP4).
+template <int FMT>
+constexpr int kDefaultType = FMT == FMT_MXFP8 ? 0 : 4;
+
 // 16 instructions of slice Q of step S (within the scale group).  The
 // lane's scale byte: FP4 byte Q of dword S; FP8 byte 2 (S % 2) + Q of dword
 // S / 2 (opsel selects the byte).
-template <int FMT, int S, int Q>
+template <int FMT, int S, int Q, int TA, int TB>
 __device__ inline void mfma_slice_t(const TSlice<FMT>& f, const u4 (&sc)[8], v16f (&acc)[4][4]) {
   constexpr int D = FMT == FMT_MXFP8 ? S / 2 : S;
   constexpr int OPSEL = FMT == FMT_MXFP8 ? 2 * (S % 2) + Q : Q;
@@ -85,11 +90,11 @@ __device__ inline void mfma_slice_t(const TSlice<FMT>& f, const u4 (&sc)[8], v16
     for (int j = 0; j < 4; ++j) {
       if constexpr (FMT == FMT_MXFP8)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            widen(f.f[i][0], f.f[i][1]), widen(f.f[4 + j][0], f.f[4 + j][1]), acc[i][j], 0, 0, OPSEL,
+            widen(f.f[i][0], f.f[i][1]), widen(f.f[4 + j][0], f.f[4 + j][1]), acc[i][j], TA, TB, OPSEL,
             (int)sc[i][D], OPSEL, (int)sc[4 + j][D]);
       else
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            widen4(f.f[i][0]), widen4(f.f[4 + j][0]), acc[i][j], 4, 4, OPSEL, (int)sc[i][D], OPSEL,
+            widen4(f.f[i][0]), widen4(f.f[4 + j][0]), acc[i][j], TA, TB, OPSEL, (int)sc[i][D], OPSEL,
             (int)sc[4 + j][D]);
     }
 }
@@ -108,7 +113,7 @@ __device__ inline uint64_t uniform_u64(uint64_t v) {
 // Steps S .. kStepsPerGroup-1 of group g: after slice q's instructions, slice
 // q of the next step (clamped to the last step, a harmless reload) is loaded
 // into the same registers.
-template <int FMT, int S, int Q>
+template <int FMT, int S, int Q, int TA, int TB>
 __device__ inline void run_group(const gptr (&base)[8], uint32_t g, uint32_t steps,
                                  uint32_t lane16, TSlice<FMT> (&fr)[TCfg<FMT>::kSlices],
                                  const u4 (&sc)[8], v16f (&acc)[4][4]) {
@@ -117,19 +122,19 @@ __device__ inline void run_group(const gptr (&base)[8], uint32_t g, uint32_t ste
     if constexpr (Q < KS) {
       const uint32_t st = g * SPG + S;
       const uint32_t nst = st + 1 < steps ? st + 1 : st;
-      mfma_slice_t<FMT, S, Q>(fr[Q], sc, acc);
+      mfma_slice_t<FMT, S, Q, TA, TB>(fr[Q], sc, acc);
       load_slice_t<FMT>(base, nst, Q, lane16, fr[Q]);
       sched_fence();
-      run_group<FMT, S, Q + 1>(base, g, steps, lane16, fr, sc, acc);
+      run_group<FMT, S, Q + 1, TA, TB>(base, g, steps, lane16, fr, sc, acc);
     } else {
-      run_group<FMT, S + 1, 0>(base, g, steps, lane16, fr, sc, acc);
+      run_group<FMT, S + 1, 0, TA, TB>(base, g, steps, lane16, fr, sc, acc);
     }
   }
 }
 
 // The main loop: the accumulators of this wave's 128x128 part of the C tile
 // at (m0, n0).
-template <int FMT>
+template <int FMT, int TA = kDefaultType<FMT>, int TB = kDefaultType<FMT>>
 __device__ inline void tiled_mainloop(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
                                       const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB,
                                       int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
@@ -176,7 +181,7 @@ __device__ inline void tiled_mainloop(const uint8_t* __restrict__ A, const uint8
 #pragma unroll
     for (int t = 0; t < 8; ++t) scn[t] = *reinterpret_cast<gptr4>(sb[t] + (uint32_t)(ng * 1024u + lane16));
     sched_fence();
-    run_group<FMT, 0, 0>(cb, g, steps, lane16, fr, sc, acc);
+    run_group<FMT, 0, 0, TA, TB>(cb, g, steps, lane16, fr, sc, acc);
 #pragma unroll
     for (int t = 0; t < 8; ++t) sc[t] = scn[t];
   }
@@ -185,7 +190,7 @@ __device__ inline void tiled_mainloop(const uint8_t* __restrict__ A, const uint8
   __builtin_amdgcn_s_waitcnt((0 & 15) | (0 << 14) | (7 << 4) | (15 << 8));  // vmcnt(0)
 }
 
-template <int FMT, int CDT>
+template <int FMT, int CDT, int TA = kDefaultType<FMT>, int TB = kDefaultType<FMT>>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx_tiled(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, void* __restrict__ C,
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t wm = wid >> 1, wn = wid & 1u;
   v16f acc[4][4];
-  tiled_mainloop<FMT>(A, SA, B, SB, M, N, K, m0, n0, wm, wn, lane, acc);
+  tiled_mainloop<FMT, TA, TB>(A, SA, B, SB, M, N, K, m0, n0, wm, wn, lane, acc);
   store_tile<CDT>(smem, acc, C, ldc, M, N, m0 + wm * 128, n0 + wn * 128, vec != 0, wid, lane);
 }
 
@@ -360,12 +365,12 @@ hipError_t launch_q_d(const uint8_t* a, const uint8_t* sa, const uint8_t* b, con
                 : launch_q<FMT, OFMT, false, false>(a, sa, b, sb, M, N, K, codes, scales, enc, s);
 }
 
-template <int FMT, int CDT>
+template <int FMT, int CDT, int TA = kDefaultType<FMT>, int TB = kDefaultType<FMT>>
 hipError_t launch_t(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                     int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
   const uint32_t tm = (uint32_t)((M + 255) / 256), tn = (uint32_t)((N + 255) / 256);
   constexpr int kEpiBytes = 4 * 64 * (128 * (CDT == DT_F32 ? 4 : 2) + 16);  // store_tile staging
-  auto kern = k_gemm_mx_tiled<FMT, CDT>;
+  auto kern = k_gemm_mx_tiled<FMT, CDT, TA, TB>;
   // raised once per device, so later launches (also inside HIP graphs) make
   // no call beyond the launch itself
   static std::atomic<uint64_t> attr_done{0};
@@ -405,8 +410,18 @@ hipError_t launch_gemm_mx_tiled_quant(int fmt, const uint8_t* a_codes, const uin
 hipError_t launch_gemm_mx_tiled(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                                 const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                 int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
-                                hipStream_t s) {
+                                hipStream_t s, int fmt_b) {
   if (M == 0 || N == 0) return hipSuccess;
+  // FP8 pairs with E5M2 on either side
+  if (fmt == FMT_MXFP8_E5M2 || fmt_b == FMT_MXFP8_E5M2) {
+#define MXK_T8(TA, TB) \
+  (cdt == DT_F32 ? launch_t<FMT_MXFP8, DT_F32, TA, TB>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s) \
+                 : launch_t<FMT_MXFP8, DT_BF16, TA, TB>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s))
+    if (fmt == FMT_MXFP8_E5M2 && fmt_b == FMT_MXFP8_E5M2) return MXK_T8(1, 1);
+    if (fmt == FMT_MXFP8_E5M2) return MXK_T8(1, 0);
+    return MXK_T8(0, 1);
+#undef MXK_T8
+  }
   if (fmt == FMT_MXFP8)
     return cdt == DT_F32 ? launch_t<FMT_MXFP8, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s)
                          : launch_t<FMT_MXFP8, DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);

@@ -267,9 +267,10 @@ __device__ __attribute__((always_inline)) inline void quant_tiled_wave(const Qua
   // 2 (T%4) + k/4, byte 4 (k%4).  FP8: code byte 1024 G + 64 T + 8 k, i.e.
   // code tile 8 G + T/2, chunk 4 (T%2) + k/2, byte 8 (k%2).
   const uint32_t r = (uint32_t)row & 31u;
-  const int64_t row_bytes = FMT == FMT_MXFP8 ? a.cols : a.cols >> 1;
-  uint8_t* cbase = a.codes + ((row >> 5) * (row_bytes >> 7) + G * (FMT == FMT_MXFP8 ? 8 : 4)) * 4096;
-  if constexpr (FMT == FMT_MXFP8) {
+  constexpr bool k8 = MxFmt<FMT>::bits == 8;  // E4M3 or E5M2 (else E2M1)
+  const int64_t row_bytes = k8 ? a.cols : a.cols >> 1;
+  uint8_t* cbase = a.codes + ((row >> 5) * (row_bytes >> 7) + G * (k8 ? 8 : 4)) * 4096;
+  if constexpr (k8) {
     cbase += (k >> 2) * 1024u + (((k >> 1) & 1u) * 32u + r) * 16u + 8u * (k & 1u) + (t0 >> 1) * 4096;
 #pragma unroll
     for (int t = 0; t < NT; ++t)  // t0 is even
@@ -665,10 +666,10 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* codes, cons
       // tiled layout (MX only): code and scale offsets of this chunk
       constexpr int kBits = FMT == FMT_NVFP4 ? 4 : (int)MxFmt<FMT>::bits;
       int64_t coff = q * kBits, soff = q >> 2;
-      if constexpr (FMT == FMT_MXFP8 || FMT == FMT_MXFP4) {
+      if constexpr (FMT == FMT_MXFP8 || FMT == FMT_MXFP4 || FMT == FMT_MXFP8_E5M2) {
         if (tiled) {
           const int64_t row = q / cpr, c8 = q - row * cpr;
-          coff = tiled_code_off(row, c8 * (FMT == FMT_MXFP8 ? 8 : 4), cpr * (FMT == FMT_MXFP8 ? 8 : 4));
+          coff = tiled_code_off(row, c8 * kBits, cpr * kBits);
           soff = tiled_scale_off(row, c8 >> 2, cols);
         }
       }
@@ -829,6 +830,9 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   if (a.tiled) {
     if (a.fmt == FMT_MXFP8)
       return a.xdt == DT_BF16 ? quant_mx_tiled_d<DT_BF16, FMT_MXFP8>(a, s) : quant_mx_tiled_d<DT_F32, FMT_MXFP8>(a, s);
+    if (a.fmt == FMT_MXFP8_E5M2)
+      return a.xdt == DT_BF16 ? quant_mx_tiled_d<DT_BF16, FMT_MXFP8_E5M2>(a, s)
+                              : quant_mx_tiled_d<DT_F32, FMT_MXFP8_E5M2>(a, s);
     return a.xdt == DT_BF16 ? quant_mx_tiled_d<DT_BF16, FMT_MXFP4>(a, s) : quant_mx_tiled_d<DT_F32, FMT_MXFP4>(a, s);
   }
 #define MXK_QD(F) \
@@ -847,7 +851,8 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
 namespace {
 // jobs that can share one tile-layout launch
 bool batchable(const QuantArgs& a) {
-  return a.tiled && (a.fmt == FMT_MXFP8 || a.fmt == FMT_MXFP4) && a.rows * a.cols > 0;
+  return a.tiled && (a.fmt == FMT_MXFP8 || a.fmt == FMT_MXFP4 || a.fmt == FMT_MXFP8_E5M2) &&
+         a.rows * a.cols > 0;
 }
 bool same_kernel(const QuantArgs& a, const QuantArgs& b) {
   return a.fmt == b.fmt && a.xdt == b.xdt && a.sr == b.sr && a.rht == b.rht;
@@ -873,6 +878,9 @@ hipError_t launch_quantize_batch(const QuantArgs* a, int n, hipStream_t s) {
       }
       if (a[i].fmt == FMT_MXFP8)
         e = a[i].xdt == DT_BF16 ? quant_mx_tiled_batch_d<DT_BF16, FMT_MXFP8>(b, s) : quant_mx_tiled_batch_d<DT_F32, FMT_MXFP8>(b, s);
+      else if (a[i].fmt == FMT_MXFP8_E5M2)
+        e = a[i].xdt == DT_BF16 ? quant_mx_tiled_batch_d<DT_BF16, FMT_MXFP8_E5M2>(b, s)
+                                : quant_mx_tiled_batch_d<DT_F32, FMT_MXFP8_E5M2>(b, s);
       else
         e = a[i].xdt == DT_BF16 ? quant_mx_tiled_batch_d<DT_BF16, FMT_MXFP4>(b, s) : quant_mx_tiled_batch_d<DT_F32, FMT_MXFP4>(b, s);
     }

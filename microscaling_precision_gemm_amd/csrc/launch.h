@@ -87,7 +87,7 @@ hipError_t launch_gemm_mx_tiled_quant(int fmt, const uint8_t* a_codes, const uin
 hipError_t launch_gemm_mx_tiled(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                                 const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                 int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
-                                hipStream_t s);
+                                hipStream_t s, int fmt_b);
 // exact MXFP8 on the DMA pipeline (BF16 instruction); shapes it takes
 bool gemm_mxfp8_exact_pipe_fits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_mxfp8_exact_pipe(const uint8_t* a_codes, const uint8_t* a_scales,

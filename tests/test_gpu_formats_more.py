@@ -227,3 +227,62 @@ def test_gemm_any_ragged_shapes_and_bf16_output(shape, cdt):
     Cw, tol = oracle.gemm(oracle.dequantize_f64(4, ca, sa, M, K), oracle.dequantize_f64(6, cb, sb, N, K))
     from tests.gpu_util import check_gemm
     check_gemm(C.float().cpu().numpy(), Cw, tol, cdt == "bf16", f"{shape} {cdt}")
+
+
+# --- E5M2 in the tile layout and on the scaled FP8 instruction -------------------
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_e5m2_tiled_quantize_and_decode(rnd):
+    from tests.tiles import untile_codes, untile_scales
+    R, C = 64, 2048
+    x = W.normal_bf16(R, C, 1.0, 4, 95, outlier_entries=0.002, outlier_mult=60)
+    xt = to_gpu_bf16(x)
+    out = mx.empty(5, R, C, device=dev(), layout=mx.MX_LAYOUT_TILED)
+    mx.mx_quantize(xt, out, rnd, 3, 17)
+    rows = mx.empty(5, R, C, device=dev())
+    mx.mx_quantize(xt, rows, rnd, 3, 17)
+    yt = torch.empty(R, C, dtype=torch.float32, device=dev())
+    yr = torch.empty(R, C, dtype=torch.float32, device=dev())
+    mx.mx_dequantize(out, yt)
+    mx.mx_dequantize(rows, yr)
+    torch.cuda.synchronize()
+    c, s, _ = host(out)
+    wc, ws, _ = oracle.quantize(x, 5, rnd, 3, 17)
+    _same(untile_scales(s, R, C // 32), ws, "scales")
+    _same(untile_codes(c, R, C), wc, "codes")
+    assert torch.equal(yt.view(torch.int32), yr.view(torch.int32))
+
+
+@pytest.mark.parametrize("fa,fb", [(5, 5), (5, 1), (1, 5)])
+@pytest.mark.parametrize("cdt", ["f32", "bf16"])
+def test_e5m2_pairs_on_the_fp8_instruction(fa, fb, cdt):
+    """Tiled E4M3 / E5M2 pairs with MX_GEMM_FP8_NATIVE: within that flag's
+    bound (1e-3 * sum|a*b|) of the oracle's exact product."""
+    from tests.gpu_util import check_gemm
+    from tests.tiles import tile_codes, tile_scales
+    M, N, K = 288, 320, 2048
+    ca, sa = _operand(fa, M, K, fa + 2 * fb, 96, 1.0)
+    cb, sb = _operand(fb, N, K, fa + 2 * fb, 97, 0.05)
+    A = mx.MXTensor(fa, M, K, torch.from_numpy(tile_codes(ca)).to(dev()), torch.from_numpy(tile_scales(sa)).to(dev()),
+                    None, mx.MX_LAYOUT_TILED)
+    B = mx.MXTensor(fb, N, K, torch.from_numpy(tile_codes(cb)).to(dev()), torch.from_numpy(tile_scales(sb)).to(dev()),
+                    None, mx.MX_LAYOUT_TILED)
+    C = torch.empty(M, N, dtype=torch.float32 if cdt == "f32" else torch.bfloat16, device=dev())
+    with pytest.raises(mx.MXError):
+        mx.mx_gemm(A, B, C)  # the FP8 instruction only on request
+    mx.mx_gemm_ex(A, B, C, mx.MX_GEMM_FP8_NATIVE)
+    torch.cuda.synchronize()
+    Cw, tol = oracle.gemm(oracle.dequantize_f64(fa, ca, sa, M, K), oracle.dequantize_f64(fb, cb, sb, N, K))
+    check_gemm(C.float().cpu().numpy(), Cw, tol * 100, cdt == "bf16", f"fa={fa} fb={fb} {cdt}")
+
+
+def test_e5m2_tiled_jobs_in_a_batch():
+    T = mx.MX_LAYOUT_TILED
+    xs = [to_gpu_bf16(W.normal_bf16(64, 1024, 1.0, 40 + i, 98)) for i in range(3)]
+    outs = [mx.empty(5, 64, 1024, device=dev(), layout=T) for _ in xs]
+    mx.mx_quantize_batch([dict(x=x, out=o, rnd=1, seed=9, counter=100 * i) for i, (x, o) in enumerate(zip(xs, outs))])
+    singles = [mx.empty(5, 64, 1024, device=dev(), layout=T) for _ in xs]
+    for i, (x, o) in enumerate(zip(xs, singles)):
+        mx.mx_quantize(x, o, 1, 9, 100 * i)
+    torch.cuda.synchronize()
+    for o, s1 in zip(outs, singles):
+        assert torch.equal(o.codes, s1.codes) and torch.equal(o.scales, s1.scales)
