@@ -32,7 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # MI355X dense peaks (AMD public figures) and HBM bandwidth
-PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
+PEAK_TFLOPS = {"fp4": 10100.0, "fp6": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
 PEAK_HBM_GBS = 8000.0
 
 
@@ -405,15 +405,24 @@ def detail(torch, mx, W, args):
     M2 = 4096
     Xa, Xb = randn(M2, M2), randn(M2, M2, 0.02)
     Cm = torch.empty(M2, M2, dtype=torch.bfloat16, device="cuda")
-    for name, fa_, fb_ in (("mxint8_x_mxint8", mx.MX_MXINT8, mx.MX_MXINT8),
-                           ("e5m2_x_e4m3", mx.MX_MXFP8_E5M2, mx.MX_MXFP8_E4M3),
-                           ("fp6_e2m3_x_fp4", mx.MX_MXFP6_E2M3, mx.MX_MXFP4_E2M1)):
+    # (FP6 pairs other than E3M2 x E3M2 run on the scaled FP6/FP4 instruction,
+    # k_gemm_mx_f6; the rest decode to BF16 in k_gemm_mx_any)
+    for name, fa_, fb_, native in (("mxint8_x_mxint8", mx.MX_MXINT8, mx.MX_MXINT8, False),
+                                   ("e5m2_x_e4m3", mx.MX_MXFP8_E5M2, mx.MX_MXFP8_E4M3, False),
+                                   ("fp6_e3m2_x_fp6_e3m2", mx.MX_MXFP6_E3M2, mx.MX_MXFP6_E3M2, False),
+                                   ("fp6_e2m3_x_fp6_e2m3", mx.MX_MXFP6_E2M3, mx.MX_MXFP6_E2M3, True),
+                                   ("fp6_e2m3_x_fp4", mx.MX_MXFP6_E2M3, mx.MX_MXFP4_E2M1, True),
+                                   ("fp6_e3m2_x_fp4", mx.MX_MXFP6_E3M2, mx.MX_MXFP4_E2M1, True)):
         qa_, qb_ = mx.empty(fa_, M2, M2), mx.empty(fb_, M2, M2)
         mx.mx_quantize(Xa, qa_)
         mx.mx_quantize(Xb, qb_)
         ms_m = time_fn(torch, lambda: mx.mx_gemm(qa_, qb_, Cm), it, wu)
-        res[f"gemm_4096_{name}"] = {"ms": ms_m, "tflops": 2 * M2**3 / ms_m / 1e9,
-                                    "frac_bf16_peak": 2 * M2**3 / ms_m / 1e9 / PEAK_TFLOPS["bf16"]}
+        tf = 2 * M2**3 / ms_m / 1e9
+        res[f"gemm_4096_{name}"] = {"ms": ms_m, "tflops": tf,
+                                    "kernel": "k_gemm_mx_f6 (scaled FP6/FP4 instruction)" if native
+                                    else "k_gemm_mx_any (exact BF16 decode)",
+                                    "frac_peak": tf / PEAK_TFLOPS["fp6" if native else "bf16"],
+                                    "peak": "fp6" if native else "bf16"}
         del qa_, qb_
     # E5M2 x E4M3 in the tile layout on the scaled FP8 instruction (MX_GEMM_FP8_NATIVE)
     qa_ = mx.empty(mx.MX_MXFP8_E5M2, M2, M2, layout=mx.MX_LAYOUT_TILED)

@@ -288,9 +288,20 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
  *   NVFP4  e2m1 * e4m3 converted to exact FP16, FP16 matrix instructions
  *          (BF16 for shapes too small for the pipelined kernel), the FP32
  *          result multiplied by S_A * S_B.
- *   Other MX pairs (mixed formats, INT8, E5M2, FP6): every element times its
- *          scale decoded to exact BF16 (exact while the scaled values are
- *          normal BF16 values), BF16 matrix instructions.
+ *   FP6 pairs (E2M3 or E3M2 against E2M3, E3M2 or MXFP4, not E3M2 x E3M2),
+ *          K % 128 == 0: scaled FP6/FP4 matrix instructions, which form the
+ *          exact sum of each instruction's 64 products (measured on gfx950;
+ *          E3M2 x E3M2 is summed in a narrower window and takes the BF16
+ *          path below).
+ *   Other MX pairs (mixed formats, INT8, E5M2, E3M2 x E3M2, FP6 with other
+ *          K): every element times its scale decoded to exact BF16 (exact
+ *          while the scaled values are normal BF16 values), BF16 matrix
+ *          instructions.
+ * The scaled matrix instructions (MXFP4, FP6 pairs, MX_GEMM_FP8_NATIVE) flush
+ * partial sums and results that fall into FP32's subnormal range (measured),
+ * so those paths meet their bound while every pair of blocks has scale codes
+ * with c_A + c_B >= 135 (MXFP4 and FP6 pairs; native E4M3 146, E5M2 160):
+ * then every nonzero partial sum is at least 2^-126.
  * Requirements: A->fmt == B->fmt, or both MX formats (E8M0 scales) in the
  * row layout; A->cols == B->cols == K; K % 32 == 0. */
 mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,

@@ -77,6 +77,12 @@ hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scal
 hipError_t launch_gemm_mx_any(int fa, const uint8_t* a_codes, const uint8_t* a_scales, int fb,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
                               int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s);
+// MX pairs with an FP6 operand (E2M3/E3M2 against E2M3/E3M2/E2M1, not E3M2 x
+// E3M2) on the scaled FP6/FP4 instruction (gemm_f6.hip); shapes it takes.
+bool gemm_mx_f6_fits(int fa, int fb, int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_mx_f6(int fa, const uint8_t* a_codes, const uint8_t* a_scales, int fb,
+                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
+                             int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s);
 // C = A * B^T of tile-layout MX operands, written quantized along its rows
 // (MX format ofmt, row or tile layout) by the GEMM's epilogue.
 hipError_t launch_gemm_mx_tiled_quant(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,

@@ -286,3 +286,119 @@ def test_e5m2_tiled_jobs_in_a_batch():
     torch.cuda.synchronize()
     for o, s1 in zip(outs, singles):
         assert torch.equal(o.codes, s1.codes) and torch.equal(o.scales, s1.scales)
+
+
+# --- FP6 pairs on the scaled FP6/FP4 matrix instruction ----------------------------
+F6_PAIRS = [(7, 7), (7, 6), (6, 7), (7, 2), (2, 7), (6, 2), (2, 6), (6, 6)]
+
+
+def _operand_blocks(fmt, rows, K, seed, tid, std):
+    """Rows and K-blocks scaled by independent powers of two (2^-12 .. 2^12), so
+    that the scale codes of a row's blocks differ and a block scale applied to
+    the wrong block or lane group shows."""
+    x = W.bf16_bits_to_f32(W.normal_bf16(rows, K, std, seed, tid)).astype(np.float64)
+    g = W.rng(seed, tid + 1)
+    x *= np.exp2(g.integers(-12, 13, (rows, 1)))
+    x *= np.repeat(np.exp2(g.integers(-12, 13, (1, K // 32))), 32, axis=1)
+    c, s, _ = oracle.quantize(W.f64_to_bf16_bits(x), fmt)
+    return c, s
+
+
+@pytest.mark.parametrize("fa,fb", F6_PAIRS)
+@pytest.mark.parametrize("shape", [(200, 136, 384), (300, 520, 1024), (33, 257, 128)])
+def test_gemm_fp6_pairs_on_the_scaled_instruction(fa, fb, shape):
+    """K % 128 == 0: the FP6 pairs run on the scaled FP6/FP4 instruction (E3M2 x
+    E3M2 on the BF16 kernel), within 1e-5 * sum|a*b| of the oracle's FP64
+    product; ragged M and N, several workgroup tiles, one K step."""
+    M, N, K = shape
+    seed = fa * 10 + fb + K
+    ca, sa = _operand_blocks(fa, M, K, seed, 94, 1.0)
+    cb, sb = _operand_blocks(fb, N, K, seed, 96, 0.05)
+    A = upload(fa, ca, sa)
+    A.cols = K
+    B = upload(fb, cb, sb)
+    B.cols = K
+    C = torch.empty(M, N, dtype=torch.float32, device=dev())
+    mx.mx_gemm(A, B, C)
+    torch.cuda.synchronize()
+    Cw, tol = oracle.gemm(oracle.dequantize_f64(fa, ca, sa, M, K), oracle.dequantize_f64(fb, cb, sb, N, K))
+    from tests.gpu_util import check_gemm
+    check_gemm(C.cpu().numpy(), Cw, tol, False, f"fa={fa} fb={fb} {shape}")
+
+
+@pytest.mark.parametrize("fa,fb", [(7, 2), (6, 7)])
+def test_gemm_fp6_bf16_output_and_strided_c(fa, fb):
+    """BF16 output into a C with a row pitch wider than N (element stores)."""
+    M, N, K, ldc = 160, 200, 512, 264
+    ca, sa = _operand_blocks(fa, M, K, 3, 98, 1.0)
+    cb, sb = _operand_blocks(fb, N, K, 3, 100, 0.05)
+    A = upload(fa, ca, sa)
+    A.cols = K
+    B = upload(fb, cb, sb)
+    B.cols = K
+    Cbuf = torch.full((M, ldc), 7.0, dtype=torch.bfloat16, device=dev())
+    mx.mx_gemm(A, B, Cbuf[:, :N])
+    torch.cuda.synchronize()
+    Cw, tol = oracle.gemm(oracle.dequantize_f64(fa, ca, sa, M, K), oracle.dequantize_f64(fb, cb, sb, N, K))
+    from tests.gpu_util import check_gemm
+    got = Cbuf.float().cpu().numpy()
+    check_gemm(got[:, :N], Cw, tol, True, f"fa={fa} fb={fb} bf16")
+    assert np.all(got[:, N:] == 7.0)
+
+
+def test_gemm_fp6_full_size_sampled():
+    """4096^3 MXFP6 E2M3 x MXFP4 (the launch the benchmark times), checked on
+    sampled rows and columns against the oracle's exact product."""
+    M = N = K = 4096
+    ca, sa = _operand(7, M, K, 1, 102, 1.0)
+    cb, sb = _operand(2, N, K, 1, 104, 0.05)
+    A = upload(7, ca, sa)
+    A.cols = K
+    B = upload(2, cb, sb)
+    B.cols = K
+    C = torch.empty(M, N, dtype=torch.bfloat16, device=dev())
+    mx.mx_gemm(A, B, C)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(5)
+    ri = g.integers(0, M, 3000)
+    cj = g.integers(0, N, 3000)
+    Cw, tol = oracle.gemm_sampled(oracle.dequantize_f64(7, ca, sa, M, K), oracle.dequantize_f64(2, cb, sb, N, K),
+                                  ri, cj)
+    from tests.gpu_util import check_gemm
+    got = C.float().cpu().numpy()[ri, cj]
+    check_gemm(got, Cw, tol, True, "4096^3 e2m3 x e2m1")
+
+
+@pytest.mark.parametrize("fa,fb,csum", [(7, 7, 135), (6, 7, 135), (7, 2, 135), (2, 6, 135), (2, 2, 130)])
+def test_scaled_instruction_at_the_low_scale_limit(fa, fb, csum):
+    """The scaled matrix instructions flush FP32-subnormal partial sums; the
+    bound holds while c_A + c_B reaches the documented limit, where the
+    smallest nonzero product is exactly 2^-126 or above (random codes, every
+    block of A at scale code c_A and of B at c_B)."""
+    M, N, K = 96, 160, 512
+    g = np.random.default_rng(csum + fa + fb)
+    def codes(fmt, rows):
+        bits = 8 if fmt in (1, 4, 5) else 6 if fmt in (6, 7) else 4
+        c, _, _ = oracle.quantize(np.zeros((rows, K), np.uint16), fmt)
+        raw = g.integers(0, 1 << bits, (rows, K))
+        packed = np.zeros_like(c)
+        for k in range(K):  # element k at bits bits*k of the row
+            bit = bits * k
+            packed[:, bit // 8] |= ((raw[:, k] << (bit % 8)) & 0xFF).astype(np.uint8)
+            if bit % 8 + bits > 8:
+                packed[:, bit // 8 + 1] |= (raw[:, k] >> (8 - bit % 8)).astype(np.uint8)
+        return packed
+    ca, cb = codes(fa, M), codes(fb, N)
+    sa = np.full((M, K // 32), csum // 2, np.uint8)
+    sb = np.full((N, K // 32), csum - csum // 2, np.uint8)
+    A = upload(fa, ca, sa)
+    A.cols = K
+    B = upload(fb, cb, sb)
+    B.cols = K
+    C = torch.empty(M, N, dtype=torch.float32, device=dev())
+    mx.mx_gemm(A, B, C)
+    torch.cuda.synchronize()
+    Cw, tol = oracle.gemm(oracle.dequantize_f64(fa, ca, sa, M, K), oracle.dequantize_f64(fb, cb, sb, N, K))
+    from tests.gpu_util import check_gemm
+    check_gemm(C.cpu().numpy(), Cw, tol, False, f"fa={fa} fb={fb} c_A+c_B={csum}")
+    assert np.abs(Cw).max() < 2.0**-100  # the products really are tiny
