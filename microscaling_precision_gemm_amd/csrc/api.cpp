@@ -301,6 +301,12 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
     st = check_output(C, cdt, A->rows, B->rows, ldc);
     if (st != MX_OK) return st;
     if (A->rows * B->rows == 0) return MX_OK;
+    if (fp8a && fp8b && mxk::gemm_mxfp8_exact_pipe_fits(A->rows, B->rows, A->cols))
+      // FP8 pairs with E5M2: the exact MXFP8 pipeline (BF16 instruction)
+      return hip_status(mxk::launch_gemm_mxfp8_exact(static_cast<const uint8_t*>(A->codes), A->scales,
+                                                     static_cast<const uint8_t*>(B->codes), B->scales, A->rows,
+                                                     B->rows, A->cols, C, cdt, ldc,
+                                                     reinterpret_cast<hipStream_t>(stream), A->fmt, B->fmt));
     if (mxk::gemm_mx_f6_fits(A->fmt, B->fmt, A->rows, B->rows, A->cols))
       return hip_status(mxk::launch_gemm_mx_f6(A->fmt, static_cast<const uint8_t*>(A->codes), A->scales,
                                                B->fmt, static_cast<const uint8_t*>(B->codes), B->scales,

@@ -410,13 +410,22 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 
 // 8 BF16 values (element 2k in the low half of word k) from the 8 FP8 codes
 // in w0, w1, scaled by E8M0 code c (1 .. 254).
+// BF8: the codes are FP8 E5M2 (v_cvt_scalef32_pk_bf16_bf8), else E4M3.
+template <bool BF8>
 __device__ inline u4 conv8(uint32_t w0, uint32_t w1, uint32_t c) {
   const float X = u2f(c << 23);
   u4 o;
-  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, X, false));
-  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, X, true));
-  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, X, false));
-  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, X, true));
+  if constexpr (BF8) {
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, X, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, X, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, X, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, X, true));
+  } else {
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, X, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, X, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, X, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, X, true));
+  }
   return o;
 }
 
@@ -437,11 +446,14 @@ __device__ inline void read_raw(const uint8_t* __restrict__ L, uint32_t b, uint3
   }
 }
 
-// half H (0: chunk bytes 0..7, 1: 8..15) of block b (scale byte b)
-template <int H>
+// half H (0: chunk bytes 0..7, 1: 8..15) of block b (scale byte b); BA / BB:
+// A (tiles 0..3) / B (tiles 4..7) hold E5M2 codes
+template <int H, bool BA, bool BB>
 __device__ inline void conv_half(const u4 (&raw)[8], const uint32_t (&sc)[8], uint32_t b, u4 (&out)[8]) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) out[t] = conv8(raw[t][2 * H], raw[t][2 * H + 1], (sc[t] >> (8 * b)) & 0xFFu);
+  for (int t = 0; t < 4; ++t) out[t] = conv8<BA>(raw[t][2 * H], raw[t][2 * H + 1], (sc[t] >> (8 * b)) & 0xFFu);
+#pragma unroll
+  for (int t = 4; t < 8; ++t) out[t] = conv8<BB>(raw[t][2 * H], raw[t][2 * H + 1], (sc[t] >> (8 * b)) & 0xFFu);
 }
 
 __device__ inline void mfma_bf16_16(const u4 (&f)[8], v16f (&acc)[4][4]) {
@@ -473,30 +485,30 @@ __device__ inline void load_scales_x(const uint8_t* __restrict__ smem, uint32_t 
 //   H6 b3 lo | convert b3 hi              H7 b3 hi | convert b0' lo, read b1'
 // (primes: stage st+1).  SWITCH: a next stage exists; DMA: refill the buffer
 // just consumed with stage st+2.
-template <bool SWITCH, bool DMA>
+template <bool SWITCH, bool DMA, bool BA, bool BB>
 __device__ inline void exact_step(const PipeCtx& x, uint8_t* __restrict__ smem, uint32_t st, uint32_t wm,
                                   uint32_t wn, uint32_t lr, uint32_t lg, XState& xs, v16f (&acc)[4][4]) {
   uint8_t* cur = smem + (st & 1u) * kStageBytes;
   uint8_t* nxt = smem + ((st + 1u) & 1u) * kStageBytes;
   constexpr int CV = 40;  // VALU per conversion window (32 conversions + scale bytes)
   // H0
-  conv_half<1>(xs.raw[0], xs.sc, 0, xs.hi);
+  conv_half<1, BA, BB>(xs.raw[0], xs.sc, 0, xs.hi);
   mfma_bf16_16(xs.lo, acc);
   spread_x<CV, 0, 0>();
   sched_fence();
   // H1
-  conv_half<0>(xs.raw[1], xs.sc, 1, xs.lo);
+  conv_half<0, BA, BB>(xs.raw[1], xs.sc, 1, xs.lo);
   read_raw(cur, 2, wm, wn, lr, lg, xs.raw[0]);
   mfma_bf16_16(xs.hi, acc);
   spread_x<CV, 8, 0>();
   sched_fence();
   // H2
-  conv_half<1>(xs.raw[1], xs.sc, 1, xs.hi);
+  conv_half<1, BA, BB>(xs.raw[1], xs.sc, 1, xs.hi);
   mfma_bf16_16(xs.lo, acc);
   spread_x<CV, 0, 0>();
   sched_fence();
   // H3
-  conv_half<0>(xs.raw[0], xs.sc, 2, xs.lo);
+  conv_half<0, BA, BB>(xs.raw[0], xs.sc, 2, xs.lo);
   read_raw(cur, 3, wm, wn, lr, lg, xs.raw[1]);
   mfma_bf16_16(xs.hi, acc);
   spread_x<CV, 8, 0>();
@@ -512,12 +524,12 @@ __device__ inline void exact_step(const PipeCtx& x, uint8_t* __restrict__ smem, 
     const uint32_t q = st / PipeCfg<FMT_MXFP8>::kPeriod + 2;
     issue_scales(x, smem, q, q % kScaleBufs, st & 1u);
   }
-  conv_half<1>(xs.raw[0], xs.sc, 2, xs.hi);
+  conv_half<1, BA, BB>(xs.raw[0], xs.sc, 2, xs.hi);
   mfma_bf16_16(xs.lo, acc);
   spread_x<CV, 0, DMA ? 17 : 0>();
   sched_fence();
   // H5
-  conv_half<0>(xs.raw[1], xs.sc, 3, xs.lo);
+  conv_half<0, BA, BB>(xs.raw[1], xs.sc, 3, xs.lo);
   if constexpr (SWITCH) {
     read_raw(nxt, 0, wm, wn, lr, lg, xs.raw[0]);
     load_scales_x(smem, st + 1, wm, wn, lr, xs.scn);
@@ -526,13 +538,13 @@ __device__ inline void exact_step(const PipeCtx& x, uint8_t* __restrict__ smem, 
   spread_x<CV, SWITCH ? 12 : 0, 0>();
   sched_fence();
   // H6
-  conv_half<1>(xs.raw[1], xs.sc, 3, xs.hi);
+  conv_half<1, BA, BB>(xs.raw[1], xs.sc, 3, xs.hi);
   mfma_bf16_16(xs.lo, acc);
   spread_x<CV, 0, 0>();
   sched_fence();
   // H7
   if constexpr (SWITCH) {
-    conv_half<0>(xs.raw[0], xs.scn, 0, xs.lo);
+    conv_half<0, BA, BB>(xs.raw[0], xs.scn, 0, xs.lo);
     read_raw(nxt, 1, wm, wn, lr, lg, xs.raw[1]);
   }
   mfma_bf16_16(xs.hi, acc);
@@ -544,7 +556,7 @@ __device__ inline void exact_step(const PipeCtx& x, uint8_t* __restrict__ smem, 
   }
 }
 
-template <int CDT>
+template <int CDT, bool BA, bool BB>
 __device__ inline void exact_body(const PipeCtx& x, uint8_t* __restrict__ smem, uint32_t steps, uint32_t wm,
                                   uint32_t wn, uint32_t lr, uint32_t lg, uint32_t wid, uint32_t lane,
                                   void* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t m0,
@@ -560,20 +572,20 @@ __device__ inline void exact_body(const PipeCtx& x, uint8_t* __restrict__ smem, 
   load_scales_x(smem, 0, wm, wn, lr, xs.sc);
   read_raw(smem, 0, wm, wn, lr, lg, xs.raw[0]);
   read_raw(smem, 1, wm, wn, lr, lg, xs.raw[1]);
-  conv_half<0>(xs.raw[0], xs.sc, 0, xs.lo);
+  conv_half<0, BA, BB>(xs.raw[0], xs.sc, 0, xs.lo);
   sched_fence();
   uint32_t st = 0;
-  for (; st + 2 < steps; ++st) exact_step<true, true>(x, smem, st, wm, wn, lr, lg, xs, acc);
+  for (; st + 2 < steps; ++st) exact_step<true, true, BA, BB>(x, smem, st, wm, wn, lr, lg, xs, acc);
   if (st + 1 < steps) {
-    exact_step<true, false>(x, smem, st, wm, wn, lr, lg, xs, acc);
+    exact_step<true, false, BA, BB>(x, smem, st, wm, wn, lr, lg, xs, acc);
     ++st;
   }
-  exact_step<false, false>(x, smem, st, wm, wn, lr, lg, xs, acc);
+  exact_step<false, false, BA, BB>(x, smem, st, wm, wn, lr, lg, xs, acc);
   dma_barrier();
   store_tile<CDT>(smem, acc, C, ldc, M, N, m0 + wm * 128, n0 + wn * 128, vec != 0, wid, lane);
 }
 
-template <int CDT>
+template <int CDT, bool BA, bool BB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx8_exact(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, void* __restrict__ C,
@@ -626,15 +638,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     wait_vmcnt<0>();
   }
   dma_barrier();
-  exact_body<CDT>(x, smem, steps, wm, wn, lane & 31u, lane >> 5, wid, lane, C, ldc, M, N, m0, n0, vec);
+  exact_body<CDT, BA, BB>(x, smem, steps, wm, wn, lane & 31u, lane >> 5, wid, lane, C, ldc, M, N, m0, n0, vec);
 }
 
-template <int CDT>
+template <int CDT, bool BA, bool BB>
 hipError_t launch_exact(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                         int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
   const uint32_t tm = (uint32_t)((M + kTile - 1) / kTile), tn = (uint32_t)((N + kTile - 1) / kTile);
   const size_t smem = (size_t)kSmemBytes;
-  auto kern = k_gemm_mx8_exact<CDT>;
+  auto kern = k_gemm_mx8_exact<CDT, BA, BB>;
   static std::atomic<uint64_t> attr_done{0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -803,9 +815,17 @@ bool gemm_mxfp8_exact_pipe_fits(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm_mxfp8_exact_pipe(const uint8_t* a_codes, const uint8_t* a_scales,
                                         const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                         int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
-                                        hipStream_t s) {
-  return cdt == DT_F32 ? launch_exact<DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s)
-                       : launch_exact<DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
+                                        hipStream_t s, bool bf8a, bool bf8b) {
+#define MXK_X(A_, B_)                                                                                \
+  if (bf8a == A_ && bf8b == B_)                                                                      \
+    return cdt == DT_F32 ? launch_exact<DT_F32, A_, B_>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s) \
+                         : launch_exact<DT_BF16, A_, B_>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
+  MXK_X(false, false)
+  MXK_X(true, false)
+  MXK_X(false, true)
+  MXK_X(true, true)
+#undef MXK_X
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,

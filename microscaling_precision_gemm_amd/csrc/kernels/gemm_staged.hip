@@ -53,7 +53,8 @@ struct Unit {
   uint32_t s;  // NVFP4: two E4M3 bytes; MXFP8: one E8M0 byte
 };
 
-template <int SRC>
+// BF8: the MX element type is FP8 E5M2 (MXFP8 units only).
+template <int SRC, bool BF8 = false>
 __device__ inline void convert_store(const Unit<SRC>& u, uint8_t* dst) {
   uint32_t out[16];
   if constexpr (SRC == FMT_NVFP4) {
@@ -80,8 +81,13 @@ __device__ inline void convert_store(const Unit<SRC>& u, uint8_t* dst) {
       const float X = u2f(c << 23);  // 2^(c-127), a normal FP32
 #pragma unroll
       for (int wd = 0; wd < 8; ++wd) {
-        out[2 * wd] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.w[wd], X, false));
-        out[2 * wd + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.w[wd], X, true));
+        if constexpr (BF8) {
+          out[2 * wd] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(u.w[wd], X, false));
+          out[2 * wd + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(u.w[wd], X, true));
+        } else {
+          out[2 * wd] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.w[wd], X, false));
+          out[2 * wd + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.w[wd], X, true));
+        }
       }
     } else {
       // scale code 0 (2^-127 is an FP32 subnormal, which the converter does
@@ -89,8 +95,10 @@ __device__ inline void convert_store(const Unit<SRC>& u, uint8_t* dst) {
       const float X = c == 0u ? u2f(0x00400000u) : __builtin_nanf("");
 #pragma unroll
       for (int wd = 0; wd < 8; ++wd) {
-        const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.w[wd], 1.0f, false);
-        const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.w[wd], 1.0f, true);
+        const v2f lo = BF8 ? __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(u.w[wd], 1.0f, false)
+                           : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.w[wd], 1.0f, false);
+        const v2f hi = BF8 ? __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(u.w[wd], 1.0f, true)
+                           : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.w[wd], 1.0f, true);
         out[2 * wd] = (f2u(lo[0] * X) >> 16) | (f2u(lo[1] * X) & 0xFFFF0000u);
         out[2 * wd + 1] = (f2u(hi[0] * X) >> 16) | (f2u(hi[1] * X) & 0xFFFF0000u);
       }
@@ -111,8 +119,9 @@ __device__ inline uint32_t special_bytes(uint32_t w) {
 // FIXUP (MXFP8, K % 512 == 0): the workgroup first scans the scale rows of
 // its tile and computes the tile only if one holds a code 0 or 255 -- the
 // codes the pipelined exact MXFP8 kernel does not convert; the output of
-// that kernel for such tiles is overwritten.
-template <int SRC, int CDT, int BM, int BN, bool GATHER, bool FIXUP = false>
+// that kernel for such tiles is overwritten.  BA / BB: A / B hold FP8 E5M2
+// (MXFP8 only).
+template <int SRC, int CDT, int BM, int BN, bool GATHER, bool FIXUP = false, bool BA = false, bool BB = false>
 __global__ __launch_bounds__(256) void k_gemm_staged(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const float* __restrict__ a_ts,
     const int32_t* __restrict__ row_index, int64_t a_rows, int64_t R, const uint8_t* __restrict__ B,
@@ -257,7 +266,10 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
   };
   auto store_step = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < kUnits; ++j) convert_store<SRC>(reg[j], &lds[buf][dst_off[j]]);
+    for (int j = 0; j < kUnits; ++j) {
+      if (j < BM / 128) convert_store<SRC, BA>(reg[j], &lds[buf][dst_off[j]]);  // A rows
+      else convert_store<SRC, BB>(reg[j], &lds[buf][dst_off[j]]);
+    }
   };
 
   v16f acc[FM][FN];
@@ -315,13 +327,13 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
     }
 }
 
-template <int SRC, int CDT, int BM, int BN, bool GATHER, bool FIXUP = false>
+template <int SRC, int CDT, int BM, int BN, bool GATHER, bool FIXUP = false, bool BA = false, bool BB = false>
 hipError_t run(const uint8_t* a, const uint8_t* sa, const float* ats, const int32_t* ri, int64_t a_rows, int64_t R,
                const uint8_t* b, const uint8_t* sb, const float* bts, int32_t groups,
                const int64_t* off, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
   const uint32_t tn = (uint32_t)((N + BN - 1) / BN);
   const uint32_t tmb = (uint32_t)((R + BM - 1) / BM + (off ? groups : 0));
-  hipLaunchKernelGGL((k_gemm_staged<SRC, CDT, BM, BN, GATHER, FIXUP>), dim3(tn * tmb), dim3(256), 0, s,
+  hipLaunchKernelGGL((k_gemm_staged<SRC, CDT, BM, BN, GATHER, FIXUP, BA, BB>), dim3(tn * tmb), dim3(256), 0, s,
                      a, sa, ats, ri, a_rows, R, b, sb, bts, groups, off, N, K, C, ldc, tn, tmb);
   return hipGetLastError();
 }
@@ -356,21 +368,42 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, co
 #undef MXK_NV
 }
 
+namespace {
+// the exact pipelined kernel, then the fix-up pass, for FP8 types BA / BB
+template <int CDT, bool BA, bool BB>
+hipError_t exact_pipe_and_fixup(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                                const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc,
+                                hipStream_t s) {
+  const hipError_t e =
+      launch_gemm_mxfp8_exact_pipe(a_codes, a_scales, b_codes, b_scales, M, N, K, C, CDT, ldc, s, BA, BB);
+  if (e != hipSuccess) return e;
+  // tiles whose operands hold scale codes 0 or 255, recomputed here
+  return run<FMT_MXFP8, CDT, 256, 256, false, true, BA, BB>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes,
+                                                             b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
+}
+}  // namespace
+
 hipError_t launch_gemm_mxfp8_exact(const uint8_t* a_codes, const uint8_t* a_scales,
                                    const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                    int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
-                                   hipStream_t s) {
+                                   hipStream_t s, int fa, int fb) {
   if (M == 0 || N == 0) return hipSuccess;
+  const bool ba = fa == FMT_MXFP8_E5M2, bb = fb == FMT_MXFP8_E5M2;
   // large shapes: raw FP8 stages through LDS, converted after the fragment
   // reads (gemm_mx.hip)
   if (gemm_mxfp8_exact_pipe_fits(M, N, K)) {
-    const hipError_t e = launch_gemm_mxfp8_exact_pipe(a_codes, a_scales, b_codes, b_scales, M, N, K, C, cdt, ldc, s);
-    if (e != hipSuccess) return e;
-    // tiles whose operands hold scale codes 0 or 255, recomputed here
-    if (cdt == DT_F32)
-      return run<FMT_MXFP8, DT_F32, 256, 256, false, true>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
-    return run<FMT_MXFP8, DT_BF16, 256, 256, false, true>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
+#define MXK_EX(A_, B_)                                                                                    \
+  if (ba == A_ && bb == B_)                                                                               \
+    return cdt == DT_F32                                                                                  \
+               ? exact_pipe_and_fixup<DT_F32, A_, B_>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s) \
+               : exact_pipe_and_fixup<DT_BF16, A_, B_>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
+    MXK_EX(false, false)
+    MXK_EX(true, false)
+    MXK_EX(false, true)
+    MXK_EX(true, true)
+#undef MXK_EX
   }
+  if (ba || bb) return hipErrorInvalidValue;  // E5M2 pairs take this path only where the pipeline fits
   if (cdt == DT_F32)
     return run_sized<FMT_MXFP8, DT_F32, false>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
   return run_sized<FMT_MXFP8, DT_BF16, false>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);

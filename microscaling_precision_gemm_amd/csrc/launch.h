@@ -96,14 +96,17 @@ hipError_t launch_gemm_mx_tiled(int fmt, const uint8_t* a_codes, const uint8_t* 
                                 hipStream_t s, int fmt_b);
 // exact MXFP8 on the DMA pipeline (BF16 instruction); shapes it takes
 bool gemm_mxfp8_exact_pipe_fits(int64_t M, int64_t N, int64_t K);
+// bf8a / bf8b: A / B hold FP8 E5M2 codes (else E4M3)
 hipError_t launch_gemm_mxfp8_exact_pipe(const uint8_t* a_codes, const uint8_t* a_scales,
                                         const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                         int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
-                                        hipStream_t s);
+                                        hipStream_t s, bool bf8a = false, bool bf8b = false);
+// fa / fb: FMT_MXFP8 (E4M3) or FMT_MXFP8_E5M2; pairs with E5M2 need
+// gemm_mxfp8_exact_pipe_fits
 hipError_t launch_gemm_mxfp8_exact(const uint8_t* a_codes, const uint8_t* a_scales,
                                    const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                    int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
-                                   hipStream_t s);
+                                   hipStream_t s, int fa = FMT_MXFP8, int fb = FMT_MXFP8);
 // a_rows: rows of the A source (row_index entries are clamped to it)
 hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                              const int32_t* row_index, int64_t a_rows, int64_t routed_rows,

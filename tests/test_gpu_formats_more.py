@@ -402,3 +402,38 @@ def test_scaled_instruction_at_the_low_scale_limit(fa, fb, csum):
     from tests.gpu_util import check_gemm
     check_gemm(C.cpu().numpy(), Cw, tol, False, f"fa={fa} fb={fb} c_A+c_B={csum}")
     assert np.abs(Cw).max() < 2.0**-100  # the products really are tiny
+
+
+@pytest.mark.parametrize("fa,fb", [(5, 1), (1, 5), (5, 5)])
+@pytest.mark.parametrize("cdt", ["f32", "bf16"])
+def test_e5m2_pairs_on_the_exact_pipeline(fa, fb, cdt):
+    """FP8 pairs with E5M2 at a size the exact MXFP8 pipeline takes (BF16
+    instruction, 1e-5 bound), with scale codes 0 and 255 in a few blocks of
+    A and B: the fix-up pass recomputes those tiles, NaN reaches exactly the
+    rows and columns the oracle gives, everything else stays in the bound."""
+    M, N, K = 2048, 4096, 512
+    ca, sa = _operand(fa, M, K, 10 * fa + fb, 106, 1.0)
+    cb, sb = _operand(fb, N, K, 10 * fa + fb, 108, 0.05)
+    sa, sb = sa.copy(), sb.copy()
+    sa[5, 3] = 0
+    sa[700, 10] = 255
+    sb[1234, 7] = 0
+    sb[3000, 2] = 255
+    A = upload(fa, ca, sa)
+    A.cols = K
+    B = upload(fb, cb, sb)
+    B.cols = K
+    dt = torch.float32 if cdt == "f32" else torch.bfloat16
+    C = torch.full((M, N), 7.0, dtype=dt, device=dev())
+    mx.mx_gemm(A, B, C)
+    torch.cuda.synchronize()
+    Cw, tol = oracle.gemm(oracle.dequantize_f64(fa, ca, sa, M, K), oracle.dequantize_f64(fb, cb, sb, N, K))
+    got = C.float().cpu().numpy()
+    nan_want = np.isnan(Cw)
+    assert nan_want[700].all() and nan_want[:, 3000].all() and nan_want.sum() == N + M - 1
+    assert np.isnan(got[nan_want]).all(), "NaN scale blocks must give NaN outputs"
+    keep = ~nan_want
+    assert not np.isnan(got[keep]).any()
+    from tests.gpu_util import check_gemm
+    check_gemm(np.where(keep, got, 0.0), np.where(keep, Cw, 0.0), np.where(keep, tol, 1.0), cdt == "bf16",
+               f"fa={fa} fb={fb} {cdt}")
