@@ -91,19 +91,20 @@ __device__ inline void encode_mx(const MxEnc& a, int64_t q, const float v[8], En
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = v[i] * inv;  // exact scaling by a power of two
   }
-  if constexpr (FMT != FMT_MXFP8 && FMT != FMT_MXFP4) {
+  if constexpr (FMT == FMT_MXFP8_E5M2) {  // RNE and SR on the conversion instructions
+    if constexpr (SR) {
+      uint32_t r[8];
+      rand16x8(a.seed, a.counter, (uint64_t)q, r);
+      pack_e5m2_sr(y, r, e.w);
+    } else {
+      pack_e5m2_rne(y, e.w);
+    }
+  } else if constexpr (FMT != FMT_MXFP8 && FMT != FMT_MXFP4) {
     uint32_t r[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     if constexpr (SR) rand16x8(a.seed, a.counter, (uint64_t)q, r);
     uint32_t c[8];
-    if constexpr (FMT == FMT_MXFP8_E5M2 && SR) {  // SR on the conversion instruction
-      uint32_t w8[2];
-      pack_e5m2_sr(y, r, w8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) c[i] = (w8[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) c[i] = mx_elem_encode<FMT>(y[i], SR, r[i]);
-    }
+    for (int i = 0; i < 8; ++i) c[i] = mx_elem_encode<FMT>(y[i], SR, r[i]);
     if constexpr (MxFmt<FMT>::bits == 8) {
       e.w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
       e.w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
