@@ -99,6 +99,8 @@ __device__ inline void encode_mx(const MxEnc& a, int64_t q, const float v[8], En
     } else {
       pack_e5m2_rne(y, e.w);
     }
+  } else if constexpr ((FMT == FMT_MXFP6_E3M2 || FMT == FMT_MXFP6_E2M3) && !SR) {  // RNE on the conversion
+    pack_fp6_rne<FMT == FMT_MXFP6_E3M2>(y, e.w);
   } else if constexpr (FMT != FMT_MXFP8 && FMT != FMT_MXFP4) {
     uint32_t r[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     if constexpr (SR) rand16x8(a.seed, a.counter, (uint64_t)q, r);
