@@ -289,7 +289,7 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
  *          (BF16 for shapes too small for the pipelined kernel), the FP32
  *          result multiplied by S_A * S_B.
  *   FP6 pairs (E2M3 or E3M2 against E2M3, E3M2 or MXFP4, not E3M2 x E3M2),
- *          K % 128 == 0: scaled FP6/FP4 matrix instructions, which form the
+ *          K % 512 == 0: scaled FP6/FP4 matrix instructions, which form the
  *          exact sum of each instruction's 64 products (measured on gfx950;
  *          E3M2 x E3M2 is summed in a narrower window and takes the BF16
  *          path below).

@@ -33,9 +33,10 @@
 // hold 16 consecutive rows, hit 16 distinct bank groups.  A lane's FP6 block
 // (24 bytes) spans two chunks; it reads both whole chunks and keeps its 24
 // bytes (8-byte reads of a 96-byte pitch would conflict two ways).  The
-// step's scale dwords of the 512 rows travel in the same stage (4-byte
-// copies), so the loop's only vector-memory operations are these copies and
-// a counted wait bounds them.  Each step's barrier sits between its two
+// scale bytes of the 512 rows travel per period of 4 steps (16 bytes per row,
+// so a row's scale line is touched once per period instead of once per step) into two buffers behind the code stages (LDS: 160 KB for FP6 x
+// FP6; K % 512 == 0).  The loop's only vector-memory operations are these
+// copies, and a counted wait bounds them.  Each step's barrier sits between its two
 // slices: slice 1 is read while slice 0's instructions run, and the next
 // stage's scales and slice 0 while slice 1's run, with the copy of stage
 // st+3 into the buffer just released.
@@ -81,15 +82,17 @@ __device__ inline uint32_t rot_of(uint32_t r) {
 
 // DMA instructions per wave and stage: the stage holds 256 rows of A then
 // 256 rows of B, i.e. 4 * (chunks_A + chunks_B) instructions of 1 KB.
-// Each stage also holds the step's scale dwords of its 512 rows (A then B):
-// 8 DMAs of 64 lanes x 4 bytes, two per wave.
+// The scales travel per period of 4 steps (512 K elements): 16 bytes of each
+// of the 512 rows (A then B), 8 DMAs of 64 lanes x 16 bytes (two per wave),
+// into two buffers after the three code stages.
 template <int TA, int TB>
 struct Dma {
   static constexpr int kA = 4 * F6Op<TA>::kChunks;
-  static constexpr int kPerWave = (kA + 4 * F6Op<TB>::kChunks) / 4;
-  static constexpr uint32_t kScales = F6Op<TA>::kStage + F6Op<TB>::kStage;  // offset of the scale dwords
-  static constexpr uint32_t kStage = kScales + 512 * 4;
-  static constexpr int kIssues = kPerWave + 2;  // vector-memory instructions per wave and stage
+  static constexpr int kPerWave = (kA + 4 * F6Op<TB>::kChunks) / 4;  // code DMAs per wave and step
+  static constexpr uint32_t kStage = F6Op<TA>::kStage + F6Op<TB>::kStage;
+  static constexpr uint32_t kScaleBase = 3 * kStage;
+  static constexpr uint32_t kScaleBuf = 512 * 16;
+  static constexpr uint32_t kLds = kScaleBase + 2 * kScaleBuf;
 };
 
 // Per-lane copy plan: instruction i of wave w fills stage bytes
@@ -99,7 +102,7 @@ struct Dma {
 template <int TA, int TB>
 struct CopyPlan {
   const uint8_t* src[Dma<TA, TB>::kPerWave];  // step-0 global address of the lane's chunk
-  const uint8_t* ssrc[2];                      // step-0 address of the lane's scale dwords
+  const uint8_t* ssrc[2];                      // period-0 address of the lane's scale bytes
 };
 
 template <int T>
@@ -123,10 +126,19 @@ __device__ inline void issue_dma(const CopyPlan<TA, TB>& p, uint32_t wid, uint32
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.src[i] + (size_t)step * seg), (lds_ptr_t)(stage + 1024u * g),
                                      16, 0, 0);
   }
+}
+
+// Scale bytes of period `per` (steps 4 per .. 4 per + 3) into scale buffer buf:
+// row r's 16 bytes at 16 r.
+template <int TA, int TB>
+__device__ inline void issue_scale_dma(const CopyPlan<TA, TB>& p, uint32_t wid, uint32_t per, uint8_t* smem,
+                                       uint32_t buf) {
+  using D = Dma<TA, TB>;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.ssrc[j] + 4u * step),
-                                     (lds_ptr_t)(stage + D::kScales + 256u * (2u * wid + j)), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(p.ssrc[j] + 16u * per),
+                                     (lds_ptr_t)(smem + D::kScaleBase + buf * D::kScaleBuf + 1024u * (2u * wid + j)),
+                                     16, 0, 0);
 }
 
 // Raw fragment chunks of this lane for one slice q: its K-block is b = 2q +
@@ -185,13 +197,14 @@ struct StepScales {
   uint32_t a[4], b[4];
 };
 template <int TA, int TB>
-__device__ inline void read_scales(const uint8_t* stage, uint32_t wm, uint32_t wn, uint32_t lr, uint32_t lg,
-                                   StepScales& sc) {
-  const uint8_t* S = stage + Dma<TA, TB>::kScales;
+__device__ inline void read_scales(const uint8_t* smem, uint32_t step, uint32_t wm, uint32_t wn, uint32_t lr,
+                                   uint32_t lg, StepScales& sc) {
+  using D = Dma<TA, TB>;
+  const uint8_t* S = smem + D::kScaleBase + ((step >> 2) & 1u) * D::kScaleBuf + 4u * (step & 3u);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sc.a[i] = *reinterpret_cast<const uint32_t*>(S + 4u * (wm * 128 + 32 * i + lr)) >> (8u * lg);
-    sc.b[i] = *reinterpret_cast<const uint32_t*>(S + 4u * (256 + wn * 128 + 32 * i + lr)) >> (8u * lg);
+    sc.a[i] = *reinterpret_cast<const uint32_t*>(S + 16u * (wm * 128 + 32 * i + lr)) >> (8u * lg);
+    sc.b[i] = *reinterpret_cast<const uint32_t*>(S + 16u * (256 + wn * 128 + 32 * i + lr)) >> (8u * lg);
   }
 }
 
@@ -234,7 +247,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    // scale DMA j of this wave: rows 64 (2 wid + j) + lane of the stage (A rows, then B rows)
+    // scale DMA j of this wave: rows 64 (2 wid + j) + lane of the 512 (A rows, then B rows)
     const uint32_t rr = 64u * (2u * wid + j) + lane;
     int64_t g = rr < 256 ? m0 + rr : n0 + (rr - 256);
     const int64_t lim = rr < 256 ? M : N;
@@ -250,15 +263,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // Three stages.  Issue order (vmcnt counts in order): stages 0, 1, 2, then
-  // in step st stage st+3 (into the buffer of stage st, after the step's
-  // barrier).  In step st the wave waits until only stage st+2's issues are
-  // in flight (stage st+1 has landed), joins the barrier, which also means
-  // every wave has read all of stage st, refills that buffer, and reads stage
-  // st+1's scales and first slice while the second slice's instructions run.
-  // Copies past the last step reload it into a buffer nobody reads.
-  constexpr int NI = D::kIssues;
+  // Three code stages.  Issue order (vmcnt counts in order): scales of period
+  // 0, code stages 0, 1, 2; then in step st (after the step's barrier) code
+  // stage st+3 into the buffer of stage st, and in every 4th step the scales
+  // of the next period into the scale buffer of the period before.  In step st
+  // the wave waits until at most kPerWave issues are in flight, so stage st+1
+  // (issued before stage st+2) and every scale copy issued before stage st+2
+  // have landed; the next period's scales are issued 3 steps before their
+  // first read, ahead of two code stages.  The barrier also means that every
+  // wave has read all of stage st and of the period before's scales.  Copies
+  // past the end reload the last step / period into buffers nobody reads.
+  constexpr int NI = D::kPerWave;
+  const uint32_t nper = steps >> 2;
   const bool h = lg != 0;
+  issue_scale_dma<TA, TB>(plan, wid, 0, smem, 0);
   issue_dma<TA, TB>(plan, wid, 0, smem);
   issue_dma<TA, TB>(plan, wid, steps > 1 ? 1 : 0, smem + D::kStage);
   issue_dma<TA, TB>(plan, wid, steps > 2 ? 2 : steps - 1, smem + 2 * D::kStage);
@@ -267,7 +285,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   sched_fence();
   RawSlice<TA, TB> f0, f1;
   StepScales sc, scn;
-  read_scales<TA, TB>(smem, wm, wn, lr, lg, sc);
+  read_scales<TA, TB>(smem, 0, wm, wn, lr, lg, sc);
   read_slice<TA, TB>(smem, 0, wm, wn, lr, lg, f0);
 
   uint32_t cur = 0;  // buffer of step st (st mod 3)
@@ -285,7 +303,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     sched_fence();
     const uint32_t n3 = st + 3 < steps ? st + 3 : steps - 1;
     issue_dma<TA, TB>(plan, wid, n3, smem + cur * D::kStage);
-    read_scales<TA, TB>(next, wm, wn, lr, lg, scn);
+    if ((st & 3u) == 0) {
+      const uint32_t p1 = (st >> 2) + 1;
+      issue_scale_dma<TA, TB>(plan, wid, p1 < nper ? p1 : nper - 1, smem, p1 & 1u);
+    }
+    read_scales<TA, TB>(smem, st + 1, wm, wn, lr, lg, scn);
     read_slice<TA, TB>(next, 0, wm, wn, lr, lg, f0);
     mfma_slice<TA, TB, 1>(f1, sc, h, acc);
     interleave<NI, 1, 2>();
@@ -304,7 +326,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 template <int TA, int TB, int CDT>
 hipError_t launch_f6(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, int64_t M,
                      int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
-  constexpr int kStages = 3 * Dma<TA, TB>::kStage;
+  constexpr int kStages = Dma<TA, TB>::kLds;
   constexpr int kEpi = 4 * 64 * (128 * (CDT == DT_F32 ? 4 : 2) + 16);  // store_tile staging
   constexpr int kLds = kStages > kEpi ? kStages : kEpi;
   static_assert(kLds <= 160 * 1024, "LDS budget");
@@ -338,7 +360,7 @@ bool gemm_mx_f6_fits(int fa, int fb, int64_t M, int64_t N, int64_t K) {
   if (ta < 0 || tb < 0) return false;
   if (ta == kE2M1 && tb == kE2M1) return false;  // MXFP4 x MXFP4 has its own kernels
   if (ta == kE3M2 && tb == kE3M2) return false;  // not exact on the scaled instruction
-  if (K % 128 != 0 || K <= 0) return false;
+  if (K % 512 != 0 || K <= 0) return false;
   // 32-bit tile count; 64-bit addressing elsewhere
   return (uint64_t)((M + 255) / 256) * (uint64_t)((N + 255) / 256) <= 0x7FFFFFFFull;
 }

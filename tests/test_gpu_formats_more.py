@@ -307,7 +307,7 @@ def _operand_blocks(fmt, rows, K, seed, tid, std):
 @pytest.mark.parametrize("fa,fb", F6_PAIRS)
 @pytest.mark.parametrize("shape", [(200, 136, 384), (300, 520, 1024), (33, 257, 128)])
 def test_gemm_fp6_pairs_on_the_scaled_instruction(fa, fb, shape):
-    """K % 128 == 0: the FP6 pairs run on the scaled FP6/FP4 instruction (E3M2 x
+    """K % 512 == 0: the FP6 pairs run on the scaled FP6/FP4 instruction (E3M2 x
     E3M2 on the BF16 kernel), within 1e-5 * sum|a*b| of the oracle's FP64
     product; ragged M and N, several workgroup tiles, one K step."""
     M, N, K = shape
