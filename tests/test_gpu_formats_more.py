@@ -305,11 +305,12 @@ def _operand_blocks(fmt, rows, K, seed, tid, std):
 
 
 @pytest.mark.parametrize("fa,fb", F6_PAIRS)
-@pytest.mark.parametrize("shape", [(200, 136, 384), (300, 520, 1024), (33, 257, 128)])
+@pytest.mark.parametrize("shape", [(200, 136, 384), (300, 520, 1024), (33, 257, 128), (520, 300, 2560)])
 def test_gemm_fp6_pairs_on_the_scaled_instruction(fa, fb, shape):
     """K % 512 == 0: the FP6 pairs run on the scaled FP6/FP4 instruction (E3M2 x
     E3M2 on the BF16 kernel), within 1e-5 * sum|a*b| of the oracle's FP64
-    product; ragged M and N, several workgroup tiles, one K step."""
+    product; ragged M and N, several workgroup tiles, 8 and 20 K steps (2 and
+    5 scale periods).  K = 384 and 128 take the BF16 kernel for every pair."""
     M, N, K = shape
     seed = fa * 10 + fb + K
     ca, sa = _operand_blocks(fa, M, K, seed, 94, 1.0)
@@ -404,14 +405,14 @@ def test_scaled_instruction_at_the_low_scale_limit(fa, fb, csum):
     assert np.abs(Cw).max() < 2.0**-100  # the products really are tiny
 
 
-@pytest.mark.parametrize("fa,fb", [(5, 1), (1, 5), (5, 5)])
+@pytest.mark.parametrize("fa,fb,K", [(5, 1, 512), (1, 5, 512), (5, 5, 512), (5, 1, 2048)])
 @pytest.mark.parametrize("cdt", ["f32", "bf16"])
-def test_e5m2_pairs_on_the_exact_pipeline(fa, fb, cdt):
+def test_e5m2_pairs_on_the_exact_pipeline(fa, fb, K, cdt):
     """FP8 pairs with E5M2 at a size the exact MXFP8 pipeline takes (BF16
     instruction, 1e-5 bound), with scale codes 0 and 255 in a few blocks of
     A and B: the fix-up pass recomputes those tiles, NaN reaches exactly the
     rows and columns the oracle gives, everything else stays in the bound."""
-    M, N, K = 2048, 4096, 512
+    M, N = 2048, 4096
     ca, sa = _operand(fa, M, K, 10 * fa + fb, 106, 1.0)
     cb, sb = _operand(fb, N, K, 10 * fa + fb, 108, 0.05)
     sa, sb = sa.copy(), sb.copy()
