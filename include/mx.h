@@ -222,8 +222,13 @@ mx_status mx_quantize(const void* x, int32_t xdt, int64_t rows, int64_t cols, in
  * jobs[1], ... in order on `stream`.  Consecutive jobs that write MXFP8 or
  * MXFP4 in the tile layout with the same format, input dtype, rounding and
  * MX_FLAG_RHT16 setting are quantized by one kernel launch (up to 4 per
- * launch), which saves the launch gaps and the ramp of small tensors; other
- * jobs are launched one by one.  Every job is checked before anything is
+ * launch), which saves the launch gaps and the ramp of small tensors.
+ * Consecutive NVFP4 jobs with the same input dtype, rounding, flags and sign
+ * mask, and no amax or tensor-scale slot in common (a given amax may be
+ * shared), share each pass (up to 16 per launch): one launch clears their
+ * amax slots, one computes every amax, one encodes -- the expert weights of
+ * a mixture-of-experts layer in three launches instead of 2 per expert.
+ * Other jobs are launched one by one.  Every job is checked before anything is
  * enqueued; the first failing job's status is returned.  No job's input may
  * be written by an earlier job of the same call.  `jobs` is a host array;
  * `out` points to a host descriptor. */

@@ -434,11 +434,12 @@ __device__ inline void encode_nv46(float S, float d6, float d4, const float v[8]
   e.sc = four ? sb[1] : sb[0];
 }
 
+// One wave of the 1-D NVFP4 quantizer (wave index within its tensor; wave 0
+// publishes the tensor scale).
 template <int XDT, bool SR, bool RHT, bool F46>
-__global__ __launch_bounds__(kThreads) void k_quant_nvfp4(QuantArgs a, int64_t Q) {
+__device__ __attribute__((always_inline)) inline void nv1d_wave(const QuantArgs& a, int64_t Q, int64_t wave) {
 #pragma clang fp contract(off)
   const uint32_t lane = threadIdx.x & 63u;
-  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t cpr = a.cols >> 3;
   const bool dense = a.ld_x == a.cols;
   const int64_t q0 = wave * (64 * kU) + lane;
@@ -446,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(QuantArgs a, int64_t Q
   load_slabs<XDT>(a.x, q0, Q, cpr, a.ld_x, dense, raw);
   const float T = *a.amax;
   const float S = (T == 0.0f) ? 1.0f : T / 2688.0f;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.tensor_scale = S;
+  if (wave == 0 && lane == 0) *a.tensor_scale = S;
   const float d = 6.0f * S;
   Enc<FMT_NVFP4> enc[kU];
 #pragma unroll
@@ -460,6 +461,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(QuantArgs a, int64_t Q
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) store_enc<FMT_NVFP4>(a, q0 + 64 * u, Q, lane, 2u, enc[u]);
+}
+
+template <int XDT, bool SR, bool RHT, bool F46>
+__global__ __launch_bounds__(kThreads) void k_quant_nvfp4(QuantArgs a, int64_t Q) {
+  nv1d_wave<XDT, SR, RHT, F46>(a, Q, ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6);
 }
 
 // Empty tensor: only the tensor scale is published.
@@ -486,12 +492,12 @@ constexpr int k2dGroups = 4;  // measured: 2 groups (64-byte code runs) ran at t
 constexpr int k2dCols = 64 * k2dGroups;
 constexpr int k2dLoads = 2 * k2dGroups;
 
+// One wave of the 2-D quantizer (wave index within its tensor).
 template <int XDT, bool SR, bool RHT>
-__global__ __launch_bounds__(kThreads) void k_quant_nvfp4_2d(QuantArgs a, int64_t nwaves,
-                                                             int64_t groups_per_band) {
+__device__ __attribute__((always_inline)) inline void nv2d_wave(const QuantArgs& a, int64_t nwaves,
+                                                                int64_t groups_per_band, int64_t wave) {
 #pragma clang fp contract(off)
   const uint32_t lane = threadIdx.x & 63u;
-  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   if (wave >= nwaves) return;
   const int64_t band = wave / groups_per_band;
   const int64_t G = wave - band * groups_per_band;
@@ -601,6 +607,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4_2d(QuantArgs a, int64_
   }
 }
 
+template <int XDT, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads) void k_quant_nvfp4_2d(QuantArgs a, int64_t nwaves,
+                                                             int64_t groups_per_band) {
+  nv2d_wave<XDT, SR, RHT>(a, nwaves, groups_per_band, ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6);
+}
+
 // ---- per-tensor amax ------------------------------------------------------
 __global__ void k_zero_f32(float* p) { *p = 0.0f; }
 
@@ -609,12 +621,13 @@ __global__ void k_zero_f32(float* p) { *p = 0.0f; }
 // on the same word, and those serialize, so the count is kept at 256.
 constexpr int kAmaxThreads = 1024;
 
+// Max |x| bits over the chunks of waves wave, wave + nwaves, ... of a tensor,
+// reduced over the workgroup into one atomic max on *amax.
 template <int XDT, bool RHT>
-__global__ __launch_bounds__(kAmaxThreads) void k_amax(const void* x, int64_t cols, int64_t ld_x,
-                                                       int64_t Q, uint32_t sign_mask, float* amax) {
+__device__ __attribute__((always_inline)) inline void amax_part(const void* x, int64_t cols, int64_t ld_x,
+                                                                int64_t Q, uint32_t sign_mask, float* amax,
+                                                                int64_t wave, int64_t nwaves) {
   const uint32_t lane = threadIdx.x & 63u;
-  const int64_t wave = ((int64_t)blockIdx.x * kAmaxThreads + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * kAmaxThreads) >> 6;
   const int64_t cpr = cols >> 3;
   const bool dense = ld_x == cols;
   uint32_t m = 0;
@@ -642,6 +655,58 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const void* x, int64_t co
     // non-negative floats order like their bit patterns
     atomicMax(reinterpret_cast<unsigned int*>(amax), t);
   }
+}
+
+template <int XDT, bool RHT>
+__global__ __launch_bounds__(kAmaxThreads) void k_amax(const void* x, int64_t cols, int64_t ld_x,
+                                                       int64_t Q, uint32_t sign_mask, float* amax) {
+  amax_part<XDT, RHT>(x, cols, ld_x, Q, sign_mask, amax, ((int64_t)blockIdx.x * kAmaxThreads + threadIdx.x) >> 6,
+                      ((int64_t)gridDim.x * kAmaxThreads) >> 6);
+}
+
+// ---- several NVFP4 tensors per launch --------------------------------------
+// Jobs with the same input dtype, rounding, transform and variant share one
+// launch per pass: zero the amax slots, the per-tensor amax (each job its own
+// slot), then the encode.  first[j] counts workgroups; a workgroup picks its
+// job from its index (a uniform choice, so the job's arguments come in
+// through scalar loads) and never spans two jobs.
+__global__ void k_zero_amax_batch(NvBatch b) {
+  if (threadIdx.x < (uint32_t)b.n) *b.job[threadIdx.x].amax = 0.0f;
+}
+
+__device__ inline int batch_job(const NvBatch& b, int64_t wg) {
+  int j = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxNvBatch; ++k) j += (k < b.n && wg >= b.first[k]) ? 1 : 0;
+  return j;
+}
+
+template <int XDT, bool RHT>
+__global__ __launch_bounds__(kAmaxThreads) void k_amax_batch(NvBatch b) {
+  const int j = batch_job(b, blockIdx.x);
+  const QuantArgs& a = b.job[j];
+  const int64_t wgs = b.first[j + 1] - b.first[j];
+  amax_part<XDT, RHT>(a.x, a.cols, a.ld_x, a.rows * (a.cols >> 3), a.sign_mask, a.amax,
+                      ((blockIdx.x - b.first[j]) * kAmaxThreads + threadIdx.x) >> 6, (wgs * kAmaxThreads) >> 6);
+}
+
+template <int XDT, bool SR, bool RHT, bool F46>
+__global__ __launch_bounds__(kThreads) void k_quant_nvfp4_batch(NvBatch b) {
+  const int j = batch_job(b, blockIdx.x);
+  const QuantArgs& a = b.job[j];
+  // surplus waves of the job's last workgroup find no chunk (q >= Q) and
+  // store nothing
+  nv1d_wave<XDT, SR, RHT, F46>(a, a.rows * (a.cols >> 3),
+                               ((blockIdx.x - b.first[j]) * kThreads + threadIdx.x) >> 6);
+}
+
+template <int XDT, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads) void k_quant_nvfp4_2d_batch(NvBatch b) {
+  const int j = batch_job(b, blockIdx.x);
+  const QuantArgs& a = b.job[j];
+  const int64_t gpb = (a.cols + k2dCols - 1) / k2dCols;
+  nv2d_wave<XDT, SR, RHT>(a, (a.rows + 15) / 16 * gpb, gpb,
+                          ((blockIdx.x - b.first[j]) * kThreads + threadIdx.x) >> 6);
 }
 
 // ---- decoder ----------------------------------------------------------------
@@ -857,11 +922,94 @@ bool batchable(const QuantArgs& a) {
 bool same_kernel(const QuantArgs& a, const QuantArgs& b) {
   return a.fmt == b.fmt && a.xdt == b.xdt && a.sr == b.sr && a.rht == b.rht;
 }
+// NVFP4 jobs that can share the launches of one NvBatch
+bool nv_batchable(const QuantArgs& a) { return a.fmt == FMT_NVFP4 && a.rows * a.cols > 0; }
+bool nv_same(const QuantArgs& a, const QuantArgs& b) {
+  return a.xdt == b.xdt && a.sr == b.sr && a.rht == b.rht && a.sign_mask == b.sign_mask &&
+         a.four6 == b.four6 && a.block2d == b.block2d && a.amax_given == b.amax_given;
+}
+
+// a[m] may join the group a[0 .. m-1]: no two jobs share an amax or tensor
+// scale slot (sequential calls would keep them apart; a shared amax slot
+// given as input is only read, and may be shared)
+bool nv_disjoint(const QuantArgs* a, int m) {
+  for (int k = 0; k < m; ++k) {
+    if (a[k].tensor_scale == a[m].tensor_scale || a[k].tensor_scale == a[m].amax ||
+        a[k].amax == a[m].tensor_scale)
+      return false;
+    if (!a[m].amax_given && a[k].amax == a[m].amax) return false;
+  }
+  return true;
+}
+
+template <int XDT, bool SR, bool RHT>
+hipError_t nv_encode_batch_t(const NvBatch& b, bool four6, bool block2d, hipStream_t s) {
+  const dim3 g((unsigned)b.first[b.n]), t(kThreads);
+  if (block2d) {
+    hipLaunchKernelGGL((k_quant_nvfp4_2d_batch<XDT, SR, RHT>), g, t, 0, s, b);
+  } else if (four6) {
+    if constexpr (SR) return hipErrorInvalidValue;  // rejected before launch
+    hipLaunchKernelGGL((k_quant_nvfp4_batch<XDT, false, RHT, true>), g, t, 0, s, b);
+  } else {
+    hipLaunchKernelGGL((k_quant_nvfp4_batch<XDT, SR, RHT, false>), g, t, 0, s, b);
+  }
+  return hipGetLastError();
+}
+template <int XDT>
+hipError_t nv_batch_d(NvBatch& b, hipStream_t s) {
+  const QuantArgs& a0 = b.job[0];
+  if (!a0.amax_given) {
+    hipLaunchKernelGGL(k_zero_amax_batch, dim3(1), dim3(64), 0, s, b);
+    // amax workgroups per job: about 512 in all, at most what the job fills
+    const int64_t per = 512 / b.n > 1 ? 512 / b.n : 1;
+    b.first[0] = 0;
+    for (int k = 0; k < b.n; ++k) {
+      const int64_t g = grid_for_amax(b.job[k].rows * (b.job[k].cols >> 3));
+      b.first[k + 1] = b.first[k] + (g < per ? g : per);
+    }
+    if (a0.rht) hipLaunchKernelGGL((k_amax_batch<XDT, true>), dim3((unsigned)b.first[b.n]), dim3(kAmaxThreads), 0, s, b);
+    else hipLaunchKernelGGL((k_amax_batch<XDT, false>), dim3((unsigned)b.first[b.n]), dim3(kAmaxThreads), 0, s, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  b.first[0] = 0;
+  for (int k = 0; k < b.n; ++k) {
+    const QuantArgs& a = b.job[k];
+    int64_t g;
+    if (a.block2d) {
+      const int64_t nwaves = (a.rows + 15) / 16 * ((a.cols + k2dCols - 1) / k2dCols);
+      g = (nwaves + kThreads / 64 - 1) / (kThreads / 64);
+    } else {
+      g = grid_for(a.rows * (a.cols >> 3));
+    }
+    b.first[k + 1] = b.first[k] + g;
+  }
+  if (a0.sr) return a0.rht ? nv_encode_batch_t<XDT, true, true>(b, a0.four6, a0.block2d, s)
+                           : nv_encode_batch_t<XDT, true, false>(b, a0.four6, a0.block2d, s);
+  return a0.rht ? nv_encode_batch_t<XDT, false, true>(b, a0.four6, a0.block2d, s)
+                : nv_encode_batch_t<XDT, false, false>(b, a0.four6, a0.block2d, s);
+}
 }  // namespace
 
 hipError_t launch_quantize_batch(const QuantArgs* a, int n, hipStream_t s) {
+  static_assert(sizeof(NvBatch) <= 3072, "kernel argument size");
   int i = 0;
   while (i < n) {
+    if (nv_batchable(a[i])) {
+      int m = 1;
+      while (m < kMaxNvBatch && i + m < n && nv_batchable(a[i + m]) && nv_same(a[i], a[i + m]) &&
+             nv_disjoint(a + i, m))
+        ++m;
+      if (m > 1) {
+        NvBatch b{};
+        b.n = m;
+        for (int k = 0; k < m; ++k) b.job[k] = a[i + k];
+        const hipError_t e = a[i].xdt == DT_BF16 ? nv_batch_d<DT_BF16>(b, s) : nv_batch_d<DT_F32>(b, s);
+        if (e != hipSuccess) return e;
+        i += m;
+        continue;
+      }
+    }
     int m = 1;
     if (batchable(a[i]))
       while (m < kMaxBatch && i + m < n && batchable(a[i + m]) && same_kernel(a[i], a[i + m])) ++m;

@@ -50,9 +50,18 @@ struct QuantBatch {
   int64_t first[kMaxBatch + 1];  // first wave of each job; first[n] = total
   int n;
 };
+// Up to kMaxNvBatch NVFP4 quantizations per launch (and per pass).
+constexpr int kMaxNvBatch = 16;
+struct NvBatch {
+  QuantArgs job[kMaxNvBatch];
+  int64_t first[kMaxNvBatch + 1];  // first workgroup of each job; first[n] = total
+  int n;
+};
 // Quantize n tensors: one launch per group of up to kMaxBatch consecutive
 // jobs that are tile-layout MX with the same format, input dtype, rounding
-// and transform; any other job is launched on its own.  Same results as n
+// and transform; one launch per pass (amax, encode) for up to kMaxNvBatch
+// consecutive NVFP4 jobs with the same input dtype, rounding, transform and
+// variant; any other job is launched on its own.  Same results as n
 // launch_quantize calls in order.
 hipError_t launch_quantize_batch(const QuantArgs* a, int n, hipStream_t s);
 hipError_t launch_amax(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ld_x, bool rht,

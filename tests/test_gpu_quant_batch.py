@@ -85,3 +85,66 @@ def test_empty_jobs_and_empty_list():
     T = mx.MX_LAYOUT_TILED
     z = torch.empty(0, 1024, dtype=torch.bfloat16, device=dev())
     _check([_job(z, 2, mx.MX_LAYOUT_ROWS), _job(_x(32, 1024, 30), 2, T)])
+
+
+# --- NVFP4 jobs: one launch per pass for up to 16 compatible jobs --------------
+def _nv(rows, cols, seed, rnd=0, flags=0, mask=0, counter=0, amax=None, f32=False):
+    x = _x(rows, cols, seed, f32)
+    a = amax if amax is not None else torch.zeros(1, dtype=torch.float32, device=dev())
+    return _job(x, 3, mx.MX_LAYOUT_ROWS, rnd, seed, counter, flags, mask, amax=a)
+
+
+NV_SHAPES = [(64, 1024), (33, 2048), (128, 512), (17, 4096), (256, 1040), (1, 160)]
+
+
+@pytest.mark.parametrize("variant", ["rne", "sr", "rht_sr", "four6", "2d", "2d_sr", "f32"])
+def test_nvfp4_jobs_share_launches(variant):
+    """Several NVFP4 tensors (ragged rows and columns, per-job seeds and
+    counters) through one batch: bit-identical to one mx_quantize call each,
+    tensor scales included."""
+    rnd = 1 if "sr" in variant else 0
+    flags = {"rht_sr": mx.MX_FLAG_RHT16, "four6": mx.MX_FLAG_FOUR_OVER_SIX, "2d": mx.MX_FLAG_BLOCK_2D,
+             "2d_sr": mx.MX_FLAG_BLOCK_2D}.get(variant, 0)
+    mask = mx.mx_rht_signs(5) if variant == "rht_sr" else 0
+    jobs = [_nv(r, c, 40 + i, rnd, flags, mask, counter=777 * i, f32=variant == "f32")
+            for i, (r, c) in enumerate(NV_SHAPES)]
+    _check(jobs)
+
+
+def test_nvfp4_more_than_one_launch_and_expert_weights():
+    """20 expert-weight slices of one stacked tensor (2-D blocks, each expert
+    its own tensor-scale and amax slot, as a mixture-of-experts layer keeps
+    them): two launches per pass, same results as 20 calls."""
+    E, rows, cols = 20, 96, 1024
+    W_ = _x(E * rows, cols, 60)
+    q = mx.empty(3, E * rows, cols, device=dev(), n_tensor_scales=E)
+    amax = torch.zeros(E, dtype=torch.float32, device=dev())
+    jobs = [dict(x=W_[e * rows:(e + 1) * rows], out=q.view_rows(e * rows, (e + 1) * rows, q.tensor_scale[e:e + 1]),
+                 rnd=0, seed=0, counter=0, flags=mx.MX_FLAG_BLOCK_2D, sign_mask=0, amax=amax[e:e + 1])
+            for e in range(E)]
+    _check(jobs)
+
+
+def test_nvfp4_shared_amax_slot_keeps_call_order():
+    """Jobs that name the same amax slot are not merged into one amax pass:
+    each computes its own max, as consecutive calls do.  A slot given as input
+    (MX_FLAG_AMAX_GIVEN) may be shared."""
+    shared = torch.zeros(1, dtype=torch.float32, device=dev())
+    a, b = _x(64, 1024, 70), _x(64, 1024, 71) * 3.0
+    jobs = [_job(a, 3, mx.MX_LAYOUT_ROWS, amax=shared), _job(b, 3, mx.MX_LAYOUT_ROWS, amax=shared)]
+    mx.mx_quantize_batch(jobs)
+    torch.cuda.synchronize()
+    for j in jobs:
+        s = _single(j)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(j["out"])[0], host(s)[0]) and np.array_equal(host(j["out"])[2], host(s)[2])
+    given = torch.tensor([float(max(a.abs().max(), b.abs().max()))], dtype=torch.float32, device=dev())
+    g = mx.MX_FLAG_AMAX_GIVEN
+    jobs = [_job(a, 3, mx.MX_LAYOUT_ROWS, flags=g, amax=given), _job(b, 3, mx.MX_LAYOUT_ROWS, flags=g, amax=given)]
+    mx.mx_quantize_batch(jobs)
+    for j in jobs:
+        out = mx.empty(3, 64, 1024, device=dev())
+        mx.mx_quantize(j["x"], out, flags=g, amax=given)
+        torch.cuda.synchronize()
+        for u, v in zip(host(j["out"]), host(out)):
+            assert np.array_equal(u, v)
