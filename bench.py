@@ -414,9 +414,9 @@ def detail(torch, mx, W, args):
     Xa, Xb = randn(M2, M2), randn(M2, M2, 0.02)
     Cm = torch.empty(M2, M2, dtype=torch.bfloat16, device="cuda")
     # (FP6 pairs other than E3M2 x E3M2 run on the scaled FP6/FP4 instruction,
-    # k_gemm_mx_f6; FP8 pairs with E5M2 on the exact MXFP8 pipeline; the rest
-    # decode to BF16 in k_gemm_mx_any)
-    for name, fa_, fb_, native in (("mxint8_x_mxint8", mx.MX_MXINT8, mx.MX_MXINT8, False),
+    # k_gemm_mx_f6; FP8 pairs with E5M2 and MXINT8 x MXINT8 on the exact 8-bit
+    # pipeline; the rest decode to BF16 in k_gemm_mx_any)
+    for name, fa_, fb_, native in (("mxint8_x_mxint8", mx.MX_MXINT8, mx.MX_MXINT8, None),
                                    ("e5m2_x_e4m3", mx.MX_MXFP8_E5M2, mx.MX_MXFP8_E4M3, None),
                                    ("fp6_e3m2_x_fp6_e3m2", mx.MX_MXFP6_E3M2, mx.MX_MXFP6_E3M2, False),
                                    ("fp6_e2m3_x_fp6_e2m3", mx.MX_MXFP6_E2M3, mx.MX_MXFP6_E2M3, True),
@@ -429,7 +429,7 @@ def detail(torch, mx, W, args):
         tf = 2 * M2**3 / ms_m / 1e9
         res[f"gemm_4096_{name}"] = {"ms": ms_m, "tflops": tf,
                                     "kernel": "k_gemm_mx_f6 (scaled FP6/FP4 instruction)" if native
-                                    else "k_gemm_mx8_exact (FP8 converted to BF16 after the fragment reads)"
+                                    else "k_gemm_mx8_exact (8-bit codes converted to BF16 after the fragment reads)"
                                     if native is None else "k_gemm_mx_any (exact BF16 decode)",
                                     "frac_peak": tf / PEAK_TFLOPS["fp6" if native else "bf16"],
                                     "peak": "fp6" if native else "bf16"}

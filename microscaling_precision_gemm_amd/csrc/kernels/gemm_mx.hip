@@ -407,15 +407,32 @@ hipError_t launch_pipe(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_x __attribute__((ext_vector_type(2)));
 
 // 8 BF16 values (element 2k in the low half of word k) from the 8 FP8 codes
 // in w0, w1, scaled by E8M0 code c (1 .. 254).
-// BF8: the codes are FP8 E5M2 (v_cvt_scalef32_pk_bf16_bf8), else E4M3.
-template <bool BF8>
+// F: the element type of the codes -- FMT_MXFP8 (E4M3), FMT_MXFP8_E5M2
+// (v_cvt_scalef32_pk_bf16_bf8) or FMT_MXINT8.  INT8 code k (two's
+// complement) means k * 2^-6: with u = k + 128 (the byte with its top bit
+// flipped), u * X' - 128 X' = k X' exactly (X' = 2^(c-133)), a value of at
+// most 8 significant bits, so its top 16 bits are its exact BF16 whenever it
+// is a normal BF16 value (scale codes 7 .. 254).
+template <int F>
 __device__ inline u4 conv8(uint32_t w0, uint32_t w1, uint32_t c) {
   const float X = u2f(c << 23);
   u4 o;
-  if constexpr (BF8) {
+  if constexpr (F == FMT_MXINT8) {
+    const float Xs = X * 0.015625f, off = -128.0f * Xs;  // both exact
+    const uint32_t u[2] = {w0 ^ 0x80808080u, w1 ^ 0x80808080u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t wd = u[k >> 1], sh = 16 * (k & 1);
+      const float lo = __builtin_fmaf((float)((wd >> sh) & 0xFFu), Xs, off);
+      const float hi = __builtin_fmaf((float)((wd >> (sh + 8)) & 0xFFu), Xs, off);
+      // both exact in BF16: the pack's rounding changes nothing
+      o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{lo, hi}, v2bf_x));
+    }
+  } else if constexpr (F == FMT_MXFP8_E5M2) {
     o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, X, false));
     o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, X, true));
     o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, X, false));
@@ -446,9 +463,9 @@ __device__ inline void read_raw(const uint8_t* __restrict__ L, uint32_t b, uint3
   }
 }
 
-// half H (0: chunk bytes 0..7, 1: 8..15) of block b (scale byte b); BA / BB:
-// A (tiles 0..3) / B (tiles 4..7) hold E5M2 codes
-template <int H, bool BA, bool BB>
+// half H (0: chunk bytes 0..7, 1: 8..15) of block b (scale byte b); FA / FB:
+// the element types of A (tiles 0..3) and B (tiles 4..7)
+template <int H, int BA, int BB>
 __device__ inline void conv_half(const u4 (&raw)[8], const uint32_t (&sc)[8], uint32_t b, u4 (&out)[8]) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) out[t] = conv8<BA>(raw[t][2 * H], raw[t][2 * H + 1], (sc[t] >> (8 * b)) & 0xFFu);
@@ -485,12 +502,14 @@ __device__ inline void load_scales_x(const uint8_t* __restrict__ smem, uint32_t 
 //   H6 b3 lo | convert b3 hi              H7 b3 hi | convert b0' lo, read b1'
 // (primes: stage st+1).  SWITCH: a next stage exists; DMA: refill the buffer
 // just consumed with stage st+2.
-template <bool SWITCH, bool DMA, bool BA, bool BB>
+template <bool SWITCH, bool DMA, int BA, int BB>
 __device__ inline void exact_step(const PipeCtx& x, uint8_t* __restrict__ smem, uint32_t st, uint32_t wm,
                                   uint32_t wn, uint32_t lr, uint32_t lg, XState& xs, v16f (&acc)[4][4]) {
   uint8_t* cur = smem + (st & 1u) * kStageBytes;
   uint8_t* nxt = smem + ((st + 1u) & 1u) * kStageBytes;
-  constexpr int CV = 40;  // VALU per conversion window (32 conversions + scale bytes)
+  // VALU per conversion window (FP8: 32 conversions + scale bytes; INT8 about
+  // 11 per 4 elements)
+  constexpr int CV = (BA == FMT_MXINT8 ? 90 : 20) + (BB == FMT_MXINT8 ? 90 : 20);
   // H0
   conv_half<1, BA, BB>(xs.raw[0], xs.sc, 0, xs.hi);
   mfma_bf16_16(xs.lo, acc);
@@ -556,7 +575,7 @@ __device__ inline void exact_step(const PipeCtx& x, uint8_t* __restrict__ smem, 
   }
 }
 
-template <int CDT, bool BA, bool BB>
+template <int CDT, int BA, int BB>
 __device__ inline void exact_body(const PipeCtx& x, uint8_t* __restrict__ smem, uint32_t steps, uint32_t wm,
                                   uint32_t wn, uint32_t lr, uint32_t lg, uint32_t wid, uint32_t lane,
                                   void* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t m0,
@@ -585,7 +604,7 @@ __device__ inline void exact_body(const PipeCtx& x, uint8_t* __restrict__ smem, 
   store_tile<CDT>(smem, acc, C, ldc, M, N, m0 + wm * 128, n0 + wn * 128, vec != 0, wid, lane);
 }
 
-template <int CDT, bool BA, bool BB>
+template <int CDT, int BA, int BB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx8_exact(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, void* __restrict__ C,
@@ -641,7 +660,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   exact_body<CDT, BA, BB>(x, smem, steps, wm, wn, lane & 31u, lane >> 5, wid, lane, C, ldc, M, N, m0, n0, vec);
 }
 
-template <int CDT, bool BA, bool BB>
+template <int CDT, int BA, int BB>
 hipError_t launch_exact(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                         int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
   const uint32_t tm = (uint32_t)((M + kTile - 1) / kTile), tn = (uint32_t)((N + kTile - 1) / kTile);
@@ -815,15 +834,16 @@ bool gemm_mxfp8_exact_pipe_fits(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm_mxfp8_exact_pipe(const uint8_t* a_codes, const uint8_t* a_scales,
                                         const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                         int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
-                                        hipStream_t s, bool bf8a, bool bf8b) {
+                                        hipStream_t s, int fa, int fb) {
 #define MXK_X(A_, B_)                                                                                \
-  if (bf8a == A_ && bf8b == B_)                                                                      \
+  if (fa == A_ && fb == B_)                                                                          \
     return cdt == DT_F32 ? launch_exact<DT_F32, A_, B_>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s) \
                          : launch_exact<DT_BF16, A_, B_>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
-  MXK_X(false, false)
-  MXK_X(true, false)
-  MXK_X(false, true)
-  MXK_X(true, true)
+  MXK_X(FMT_MXFP8, FMT_MXFP8)
+  MXK_X(FMT_MXFP8_E5M2, FMT_MXFP8)
+  MXK_X(FMT_MXFP8, FMT_MXFP8_E5M2)
+  MXK_X(FMT_MXFP8_E5M2, FMT_MXFP8_E5M2)
+  MXK_X(FMT_MXINT8, FMT_MXINT8)
 #undef MXK_X
   return hipErrorInvalidValue;
 }

@@ -53,9 +53,12 @@ struct Unit {
   uint32_t s;  // NVFP4: two E4M3 bytes; MXFP8: one E8M0 byte
 };
 
-// BF8: the MX element type is FP8 E5M2 (MXFP8 units only).
-template <int SRC, bool BF8 = false>
+// F: the element type of MXFP8 units -- FMT_MXFP8 (E4M3), FMT_MXFP8_E5M2 or
+// FMT_MXINT8 (two's complement times 2^-6, decoded in software: the exact
+// FP32 product k * 2^(c-133), truncated to BF16).
+template <int SRC, int F = FMT_MXFP8>
 __device__ inline void convert_store(const Unit<SRC>& u, uint8_t* dst) {
+  constexpr bool BF8 = F == FMT_MXFP8_E5M2;
   uint32_t out[16];
   if constexpr (SRC == FMT_NVFP4) {
 #pragma unroll
@@ -74,6 +77,19 @@ __device__ inline void convert_store(const Unit<SRC>& u, uint8_t* dst) {
           out[blk * 8 + wd * 4 + b] = (f2u(lo) >> 16) | (f2u(hi) & 0xFFFF0000u);
         }
       }
+    }
+  } else if constexpr (F == FMT_MXINT8) {
+    const uint32_t c = u.s & 0xFFu;
+    // 2^(c-127): c = 0 is the FP32 subnormal 2^-127, 0xFF is NaN
+    const float X = c == 0xFFu ? __builtin_nanf("") : (c == 0u ? u2f(0x00400000u) : u2f(c << 23));
+#pragma unroll
+    for (int wd = 0; wd < 8; ++wd) {
+      const float v0 = (float)(int8_t)(u.w[wd] & 0xFFu) * X * 0.015625f;
+      const float v1 = (float)(int8_t)((u.w[wd] >> 8) & 0xFFu) * X * 0.015625f;
+      const float v2 = (float)(int8_t)((u.w[wd] >> 16) & 0xFFu) * X * 0.015625f;
+      const float v3 = (float)(int8_t)(u.w[wd] >> 24) * X * 0.015625f;
+      out[2 * wd] = (f2u(v0) >> 16) | (f2u(v1) & 0xFFFF0000u);
+      out[2 * wd + 1] = (f2u(v2) >> 16) | (f2u(v3) & 0xFFFF0000u);
     }
   } else {
     const uint32_t c = u.s & 0xFFu;
@@ -119,9 +135,10 @@ __device__ inline uint32_t special_bytes(uint32_t w) {
 // FIXUP (MXFP8, K % 512 == 0): the workgroup first scans the scale rows of
 // its tile and computes the tile only if one holds a code 0 or 255 -- the
 // codes the pipelined exact MXFP8 kernel does not convert; the output of
-// that kernel for such tiles is overwritten.  BA / BB: A / B hold FP8 E5M2
-// (MXFP8 only).
-template <int SRC, int CDT, int BM, int BN, bool GATHER, bool FIXUP = false, bool BA = false, bool BB = false>
+// that kernel for such tiles is overwritten.  BA / BB: the element types of A
+// and B for MXFP8 units (FMT_MXFP8, FMT_MXFP8_E5M2 or FMT_MXINT8).
+template <int SRC, int CDT, int BM, int BN, bool GATHER, bool FIXUP = false, int BA = FMT_MXFP8,
+          int BB = FMT_MXFP8>
 __global__ __launch_bounds__(256) void k_gemm_staged(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const float* __restrict__ a_ts,
     const int32_t* __restrict__ row_index, int64_t a_rows, int64_t R, const uint8_t* __restrict__ B,
@@ -327,7 +344,8 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
     }
 }
 
-template <int SRC, int CDT, int BM, int BN, bool GATHER, bool FIXUP = false, bool BA = false, bool BB = false>
+template <int SRC, int CDT, int BM, int BN, bool GATHER, bool FIXUP = false, int BA = FMT_MXFP8,
+          int BB = FMT_MXFP8>
 hipError_t run(const uint8_t* a, const uint8_t* sa, const float* ats, const int32_t* ri, int64_t a_rows, int64_t R,
                const uint8_t* b, const uint8_t* sb, const float* bts, int32_t groups,
                const int64_t* off, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
@@ -369,8 +387,8 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, co
 }
 
 namespace {
-// the exact pipelined kernel, then the fix-up pass, for FP8 types BA / BB
-template <int CDT, bool BA, bool BB>
+// the exact pipelined kernel, then the fix-up pass, for element types BA / BB
+template <int CDT, int BA, int BB>
 hipError_t exact_pipe_and_fixup(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                                 const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc,
                                 hipStream_t s) {
@@ -388,22 +406,24 @@ hipError_t launch_gemm_mxfp8_exact(const uint8_t* a_codes, const uint8_t* a_scal
                                    int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
                                    hipStream_t s, int fa, int fb) {
   if (M == 0 || N == 0) return hipSuccess;
-  const bool ba = fa == FMT_MXFP8_E5M2, bb = fb == FMT_MXFP8_E5M2;
-  // large shapes: raw FP8 stages through LDS, converted after the fragment
+  // large shapes: raw 8-bit stages through LDS, converted after the fragment
   // reads (gemm_mx.hip)
   if (gemm_mxfp8_exact_pipe_fits(M, N, K)) {
 #define MXK_EX(A_, B_)                                                                                    \
-  if (ba == A_ && bb == B_)                                                                               \
+  if (fa == A_ && fb == B_)                                                                               \
     return cdt == DT_F32                                                                                  \
                ? exact_pipe_and_fixup<DT_F32, A_, B_>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s) \
                : exact_pipe_and_fixup<DT_BF16, A_, B_>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
-    MXK_EX(false, false)
-    MXK_EX(true, false)
-    MXK_EX(false, true)
-    MXK_EX(true, true)
+    MXK_EX(FMT_MXFP8, FMT_MXFP8)
+    MXK_EX(FMT_MXFP8_E5M2, FMT_MXFP8)
+    MXK_EX(FMT_MXFP8, FMT_MXFP8_E5M2)
+    MXK_EX(FMT_MXFP8_E5M2, FMT_MXFP8_E5M2)
+    MXK_EX(FMT_MXINT8, FMT_MXINT8)
 #undef MXK_EX
+    return hipErrorInvalidValue;
   }
-  if (ba || bb) return hipErrorInvalidValue;  // E5M2 pairs take this path only where the pipeline fits
+  // E5M2 and INT8 pairs take this path only where the pipeline fits
+  if (fa != FMT_MXFP8 || fb != FMT_MXFP8) return hipErrorInvalidValue;
   if (cdt == DT_F32)
     return run_sized<FMT_MXFP8, DT_F32, false>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
   return run_sized<FMT_MXFP8, DT_BF16, false>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);

@@ -405,13 +405,15 @@ def test_scaled_instruction_at_the_low_scale_limit(fa, fb, csum):
     assert np.abs(Cw).max() < 2.0**-100  # the products really are tiny
 
 
-@pytest.mark.parametrize("fa,fb,K", [(5, 1, 512), (1, 5, 512), (5, 5, 512), (5, 1, 2048)])
+@pytest.mark.parametrize("fa,fb,K", [(5, 1, 512), (1, 5, 512), (5, 5, 512), (5, 1, 2048), (4, 4, 512),
+                                     (4, 4, 2048)])
 @pytest.mark.parametrize("cdt", ["f32", "bf16"])
-def test_e5m2_pairs_on_the_exact_pipeline(fa, fb, K, cdt):
-    """FP8 pairs with E5M2 at a size the exact MXFP8 pipeline takes (BF16
-    instruction, 1e-5 bound), with scale codes 0 and 255 in a few blocks of
-    A and B: the fix-up pass recomputes those tiles, NaN reaches exactly the
-    rows and columns the oracle gives, everything else stays in the bound."""
+def test_8bit_pairs_on_the_exact_pipeline(fa, fb, K, cdt):
+    """FP8 pairs with E5M2, and MXINT8 x MXINT8, at a size the exact 8-bit
+    pipeline takes (BF16 instruction, 1e-5 bound), with scale codes 0 and 255
+    in a few blocks of A and B: the fix-up pass recomputes those tiles, NaN
+    reaches exactly the rows and columns the oracle gives, everything else
+    stays in the bound."""
     M, N = 2048, 4096
     ca, sa = _operand(fa, M, K, 10 * fa + fb, 106, 1.0)
     cb, sb = _operand(fb, N, K, 10 * fa + fb, 108, 0.05)
