@@ -298,9 +298,9 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
  *          exact sum of each instruction's 64 products (measured on gfx950;
  *          E3M2 x E3M2 is summed in a narrower window and takes the BF16
  *          path below).
- *   FP8 pairs with E5M2 (E5M2 x E5M2, E5M2 x E4M3, E4M3 x E5M2), and MXINT8
- *          x MXINT8, where the MXFP8 pipeline fits (K % 512 == 0, M * N >=
- *          2^23): as MXFP8, each element times its scale converted to BF16,
+ *   Other pairs of 8-bit types (E4M3, E5M2, INT8: E5M2 x E4M3, INT8 x INT8,
+ *          INT8 x E4M3, ...) where the MXFP8 pipeline fits (K % 512 == 0,
+ *          M * N >= 2^23): as MXFP8, each element times its scale converted to BF16,
  *          exact for scale codes c in [17, 239] (E5M2) and [7, 254] (INT8);
  *          codes 0 and 255 are recomputed as for MXFP8.
  *   Other MX pairs (mixed formats, INT8, E3M2 x E3M2, FP6 and E5M2 pairs at

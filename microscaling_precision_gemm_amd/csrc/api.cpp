@@ -301,10 +301,10 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
     st = check_output(C, cdt, A->rows, B->rows, ldc);
     if (st != MX_OK) return st;
     if (A->rows * B->rows == 0) return MX_OK;
-    const bool int8s = A->fmt == MX_MXINT8 && B->fmt == MX_MXINT8;
-    if ((int8s || (fp8a && fp8b)) && mxk::gemm_mxfp8_exact_pipe_fits(A->rows, B->rows, A->cols))
-      // FP8 pairs with E5M2, and MXINT8 x MXINT8: the exact 8-bit pipeline
-      // (BF16 instruction)
+    const bool b8a = fp8a || A->fmt == MX_MXINT8, b8b = fp8b || B->fmt == MX_MXINT8;
+    if (b8a && b8b && mxk::gemm_mxfp8_exact_pipe_fits(A->rows, B->rows, A->cols))
+      // pairs of 8-bit MX types (E4M3, E5M2, INT8) other than E4M3 x E4M3:
+      // the exact 8-bit pipeline (BF16 instruction)
       return hip_status(mxk::launch_gemm_mxfp8_exact(static_cast<const uint8_t*>(A->codes), A->scales,
                                                      static_cast<const uint8_t*>(B->codes), B->scales, A->rows,
                                                      B->rows, A->cols, C, cdt, ldc,

@@ -844,6 +844,10 @@ hipError_t launch_gemm_mxfp8_exact_pipe(const uint8_t* a_codes, const uint8_t* a
   MXK_X(FMT_MXFP8, FMT_MXFP8_E5M2)
   MXK_X(FMT_MXFP8_E5M2, FMT_MXFP8_E5M2)
   MXK_X(FMT_MXINT8, FMT_MXINT8)
+  MXK_X(FMT_MXINT8, FMT_MXFP8)
+  MXK_X(FMT_MXFP8, FMT_MXINT8)
+  MXK_X(FMT_MXINT8, FMT_MXFP8_E5M2)
+  MXK_X(FMT_MXFP8_E5M2, FMT_MXINT8)
 #undef MXK_X
   return hipErrorInvalidValue;
 }

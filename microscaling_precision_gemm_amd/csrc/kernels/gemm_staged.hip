@@ -419,10 +419,14 @@ hipError_t launch_gemm_mxfp8_exact(const uint8_t* a_codes, const uint8_t* a_scal
     MXK_EX(FMT_MXFP8, FMT_MXFP8_E5M2)
     MXK_EX(FMT_MXFP8_E5M2, FMT_MXFP8_E5M2)
     MXK_EX(FMT_MXINT8, FMT_MXINT8)
+    MXK_EX(FMT_MXINT8, FMT_MXFP8)
+    MXK_EX(FMT_MXFP8, FMT_MXINT8)
+    MXK_EX(FMT_MXINT8, FMT_MXFP8_E5M2)
+    MXK_EX(FMT_MXFP8_E5M2, FMT_MXINT8)
 #undef MXK_EX
     return hipErrorInvalidValue;
   }
-  // E5M2 and INT8 pairs take this path only where the pipeline fits
+  // pairs other than E4M3 x E4M3 take this path only where the pipeline fits
   if (fa != FMT_MXFP8 || fb != FMT_MXFP8) return hipErrorInvalidValue;
   if (cdt == DT_F32)
     return run_sized<FMT_MXFP8, DT_F32, false>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);

@@ -105,14 +105,14 @@ hipError_t launch_gemm_mx_tiled(int fmt, const uint8_t* a_codes, const uint8_t* 
                                 hipStream_t s, int fmt_b);
 // exact MXFP8 on the DMA pipeline (BF16 instruction); shapes it takes
 bool gemm_mxfp8_exact_pipe_fits(int64_t M, int64_t N, int64_t K);
-// fa / fb: element types FMT_MXFP8 (E4M3) or FMT_MXFP8_E5M2 in any pair, or
-// FMT_MXINT8 for both
+// fa / fb: element types FMT_MXFP8 (E4M3), FMT_MXFP8_E5M2 or FMT_MXINT8, any
+// pair
 hipError_t launch_gemm_mxfp8_exact_pipe(const uint8_t* a_codes, const uint8_t* a_scales,
                                         const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                         int64_t N, int64_t K, void* C, int cdt, int64_t ldc,
                                         hipStream_t s, int fa = FMT_MXFP8, int fb = FMT_MXFP8);
-// fa / fb: FMT_MXFP8 (E4M3) or FMT_MXFP8_E5M2 in any pair, or FMT_MXINT8 for
-// both; pairs other than E4M3 x E4M3 need gemm_mxfp8_exact_pipe_fits
+// fa / fb: FMT_MXFP8 (E4M3), FMT_MXFP8_E5M2 or FMT_MXINT8, any pair; pairs
+// other than E4M3 x E4M3 need gemm_mxfp8_exact_pipe_fits
 hipError_t launch_gemm_mxfp8_exact(const uint8_t* a_codes, const uint8_t* a_scales,
                                    const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                    int64_t N, int64_t K, void* C, int cdt, int64_t ldc,

@@ -406,11 +406,11 @@ def test_scaled_instruction_at_the_low_scale_limit(fa, fb, csum):
 
 
 @pytest.mark.parametrize("fa,fb,K", [(5, 1, 512), (1, 5, 512), (5, 5, 512), (5, 1, 2048), (4, 4, 512),
-                                     (4, 4, 2048)])
+                                     (4, 4, 2048), (4, 1, 512), (1, 4, 512), (4, 5, 512), (5, 4, 512)])
 @pytest.mark.parametrize("cdt", ["f32", "bf16"])
 def test_8bit_pairs_on_the_exact_pipeline(fa, fb, K, cdt):
-    """FP8 pairs with E5M2, and MXINT8 x MXINT8, at a size the exact 8-bit
-    pipeline takes (BF16 instruction, 1e-5 bound), with scale codes 0 and 255
+    """Pairs of 8-bit MX types (E4M3, E5M2, INT8) other than E4M3 x E4M3, at a
+    size the exact 8-bit pipeline takes (BF16 instruction, 1e-5 bound), with scale codes 0 and 255
     in a few blocks of A and B: the fix-up pass recomputes those tiles, NaN
     reaches exactly the rows and columns the oracle gives, everything else
     stays in the bound."""
