@@ -295,12 +295,19 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
   if (A->fmt != B->fmt || !core_fmt(A->fmt)) {
     // mixed formats or the other MX element types: every MX (E8M0) pair, row
     // layout, exact BF16 staging
-    if (A->fmt == MX_NVFP4 || B->fmt == MX_NVFP4 || flags) return MX_ERR_UNSUPPORTED;
+    if (A->fmt == MX_NVFP4 || B->fmt == MX_NVFP4) return MX_ERR_UNSUPPORTED;
+    // MX_GEMM_FP8_NATIVE: FP8 pairs (E4M3 / E5M2) only
+    if (flags && !(fp8a && fp8b)) return MX_ERR_UNSUPPORTED;
     if (A->layout != MX_LAYOUT_ROWS || B->layout != MX_LAYOUT_ROWS) return MX_ERR_UNSUPPORTED;
     if (A->cols != B->cols || A->cols % 32) return MX_ERR_SHAPE;
     st = check_output(C, cdt, A->rows, B->rows, ldc);
     if (st != MX_OK) return st;
     if (A->rows * B->rows == 0) return MX_OK;
+    if (flags)  // row-layout FP8 pairs with E5M2 on the scaled FP8 instruction
+      return hip_status(mxk::launch_gemm_mx(mxk::FMT_MXFP8, static_cast<const uint8_t*>(A->codes), A->scales,
+                                            static_cast<const uint8_t*>(B->codes), B->scales, A->rows, B->rows,
+                                            A->cols, C, cdt, ldc, reinterpret_cast<hipStream_t>(stream), A->fmt,
+                                            B->fmt));
     const bool b8a = fp8a || A->fmt == MX_MXINT8, b8b = fp8b || B->fmt == MX_MXINT8;
     if (b8a && b8b && mxk::gemm_mxfp8_exact_pipe_fits(A->rows, B->rows, A->cols))
       // pairs of 8-bit MX types (E4M3, E5M2, INT8) other than E4M3 x E4M3:

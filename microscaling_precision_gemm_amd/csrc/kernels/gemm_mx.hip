@@ -157,7 +157,12 @@ __device__ inline void shift_scales(const Scales& in, uint32_t lg, Scales& out) 
 // slice q is byte (2q + lg) of the step's scale bytes: dword (2q + lg) / 4,
 // after the shift by lg bytes selected by opsel = 2 * (q % 2) (FP4), or
 // opsel = 2q (FP8, one dword per step).
-template <int FMT, int Q>
+// Matrix-instruction element types (cbsz / blgp) of A and B: FP8 E4M3 0,
+// E5M2 1 (MX_GEMM_FP8_NATIVE pairs), FP4 4.
+template <int FMT>
+constexpr int kType = FMT == FMT_MXFP8 ? 0 : 4;
+
+template <int FMT, int Q, int TA, int TB>
 __device__ inline void mfma_slice(const Slice<FMT>& f, const Scales& sh, v16f (&acc)[4][4]) {
   constexpr int D = FMT == FMT_MXFP8 ? 0 : Q / 2;
   constexpr int OPSEL = FMT == FMT_MXFP8 ? 2 * Q : 2 * (Q % 2);
@@ -166,7 +171,7 @@ __device__ inline void mfma_slice(const Slice<FMT>& f, const Scales& sh, v16f (&
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (FMT == FMT_MXFP8)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f.a[i], f.ahi[i]), widen(f.b[j], f.bhi[j]), acc[i][j], 0, 0, OPSEL, (int)sh.a[D][i], OPSEL, (int)sh.b[D][j]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f.a[i], f.ahi[i]), widen(f.b[j], f.bhi[j]), acc[i][j], TA, TB, OPSEL, (int)sh.a[D][i], OPSEL, (int)sh.b[D][j]);
       else
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen4(f.a[i]), widen4(f.b[j]), acc[i][j], 4, 4, OPSEL, (int)sh.a[D][i], OPSEL, (int)sh.b[D][j]);
     }
@@ -197,7 +202,7 @@ struct PipeState {
 //   W1: MFMAs of slice 1 | DMAs of stage st+2, reads of st+1's scales and
 //       slice 0
 // Spreading the DMAs over matrix work keeps their issue from stalling it.
-template <int FMT, bool SWITCH, bool DMA>
+template <int FMT, bool SWITCH, bool DMA, int TA, int TB>
 __device__ inline void pipe_step(const PipeCtx& x, uint8_t* __restrict__ smem, uint32_t st,
                                  uint32_t wm, uint32_t wn, uint32_t lr, uint32_t lg,
                                  PipeState<FMT>& ps, v16f (&acc)[4][4]) {
@@ -210,11 +215,11 @@ __device__ inline void pipe_step(const PipeCtx& x, uint8_t* __restrict__ smem, u
   if constexpr (FMT == FMT_MXFP4) {
     load_slice<FMT>(cur, 1, wm, wn, lr, lg, ps.s[1]);
     load_slice<FMT>(cur, 2, wm, wn, lr, lg, ps.s[2]);
-    mfma_slice<FMT, 0>(ps.s[0], ps.sh, acc);
+    mfma_slice<FMT, 0, TA, TB>(ps.s[0], ps.sh, acc);
     interleave<8, 0, 2>();
     sched_fence();
     load_slice<FMT>(cur, 3, wm, wn, lr, lg, ps.s[3]);
-    mfma_slice<FMT, 1>(ps.s[1], ps.sh, acc);
+    mfma_slice<FMT, 1, TA, TB>(ps.s[1], ps.sh, acc);
     interleave<8, 0, 1>();
     sched_fence();
     if constexpr (SWITCH) {
@@ -226,23 +231,23 @@ __device__ inline void pipe_step(const PipeCtx& x, uint8_t* __restrict__ smem, u
         const uint32_t q = st / PipeCfg<FMT>::kPeriod + 2;
         issue_scales(x, smem, q, q % kScaleBufs, st & 1u);
       }
-      mfma_slice<FMT, 2>(ps.s[2], ps.sh, acc);
+      mfma_slice<FMT, 2, TA, TB>(ps.s[2], ps.sh, acc);
       interleave<16, 1, 0>();
       sched_fence();
       load_scales<FMT>(smem, st + 1, wm, wn, lr, ps.scn);
       load_slice<FMT>(nxt, 0, wm, wn, lr, lg, ps.s[0]);
-      mfma_slice<FMT, 3>(ps.s[3], ps.sh, acc);
+      mfma_slice<FMT, 3, TA, TB>(ps.s[3], ps.sh, acc);
       interleave<8, 0, 3>();
       sched_fence();
       ps.sc = ps.scn;
     } else {
-      mfma_slice<FMT, 2>(ps.s[2], ps.sh, acc);
-      mfma_slice<FMT, 3>(ps.s[3], ps.sh, acc);
+      mfma_slice<FMT, 2, TA, TB>(ps.s[2], ps.sh, acc);
+      mfma_slice<FMT, 3, TA, TB>(ps.s[3], ps.sh, acc);
       sched_fence();
     }
   } else {
     load_slice<FMT>(cur, 1, wm, wn, lr, lg, ps.s[1]);
-    mfma_slice<FMT, 0>(ps.s[0], ps.sh, acc);
+    mfma_slice<FMT, 0, TA, TB>(ps.s[0], ps.sh, acc);
     interleave<8, 0, 2>();
     sched_fence();
     if constexpr (SWITCH) {
@@ -256,19 +261,19 @@ __device__ inline void pipe_step(const PipeCtx& x, uint8_t* __restrict__ smem, u
       }
       load_scales<FMT>(smem, st + 1, wm, wn, lr, ps.scn);
       load_slice<FMT>(nxt, 0, wm, wn, lr, lg, ps.s[0]);
-      mfma_slice<FMT, 1>(ps.s[1], ps.sh, acc);
+      mfma_slice<FMT, 1, TA, TB>(ps.s[1], ps.sh, acc);
       interleave<12, 2, 2>();
       sched_fence();
       ps.sc = ps.scn;
     } else {
-      mfma_slice<FMT, 1>(ps.s[1], ps.sh, acc);
+      mfma_slice<FMT, 1, TA, TB>(ps.s[1], ps.sh, acc);
       sched_fence();
     }
   }
 }
 
 // One workgroup per CU (256 accumulator registers per lane).
-template <int FMT, int CDT>
+template <int FMT, int CDT, int TA = kType<FMT>, int TB = kType<FMT>>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx_pipe(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, void* __restrict__ C,
@@ -345,24 +350,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   load_scales<FMT>(smem, 0, wm, wn, lr, ps.sc);
   load_slice<FMT>(smem, 0, wm, wn, lr, lg, ps.s[0]);
   uint32_t st = 0;
-  for (; st + 2 < steps; ++st) pipe_step<FMT, true, true>(x, smem, st, wm, wn, lr, lg, ps, acc);
+  for (; st + 2 < steps; ++st) pipe_step<FMT, true, true, TA, TB>(x, smem, st, wm, wn, lr, lg, ps, acc);
   if (st + 1 < steps) {
-    pipe_step<FMT, true, false>(x, smem, st, wm, wn, lr, lg, ps, acc);
+    pipe_step<FMT, true, false, TA, TB>(x, smem, st, wm, wn, lr, lg, ps, acc);
     ++st;
   }
-  pipe_step<FMT, false, false>(x, smem, st, wm, wn, lr, lg, ps, acc);
+  pipe_step<FMT, false, false, TA, TB>(x, smem, st, wm, wn, lr, lg, ps, acc);
 
   // epilogue: LDS is free once every wave is past its last fragment read
   dma_barrier();
   store_tile<CDT>(smem, acc, C, ldc, M, N, m0 + wm * 128, n0 + wn * 128, vec != 0, wid, lane);
 }
 
-template <int FMT, int CDT>
+template <int FMT, int CDT, int TA = kType<FMT>, int TB = kType<FMT>>
 hipError_t launch_pipe(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                        int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
   const uint32_t tm = (uint32_t)((M + kTile - 1) / kTile), tn = (uint32_t)((N + kTile - 1) / kTile);
   const size_t smem = (size_t)kSmemBytes;
-  auto kern = k_gemm_mx_pipe<FMT, CDT>;
+  auto kern = k_gemm_mx_pipe<FMT, CDT, TA, TB>;
   // The dynamic LDS limit is raised once per device (bit d of a mask), so
   // that later launches -- including those recorded into a HIP graph --
   // make no call beyond the launch itself.
@@ -687,7 +692,7 @@ hipError_t launch_exact(const uint8_t* a, const uint8_t* sa, const uint8_t* b, c
 // ---------------------------------------------------------------------------
 constexpr int kPitchS = 80;  // LDS bytes per row: 64 code bytes, 4 scale bytes, pad
 
-template <int FMT, int CDT>
+template <int FMT, int CDT, int TA = kType<FMT>, int TB = kType<FMT>>
 __global__ __launch_bounds__(256) void k_gemm_mx_simple(const uint8_t* __restrict__ A,
                                                         const uint8_t* __restrict__ SA,
                                                         const uint8_t* __restrict__ B,
@@ -786,7 +791,7 @@ __global__ __launch_bounds__(256) void k_gemm_mx_simple(const uint8_t* __restric
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           if constexpr (FMT == FMT_MXFP8)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, (int)sa[i], 0, (int)sb[j]);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], TA, TB, 0, (int)sa[i], 0, (int)sb[j]);
           else if (ins == 0)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, (int)sa[i], 0, (int)sb[j]);
           else
@@ -809,7 +814,7 @@ __global__ __launch_bounds__(256) void k_gemm_mx_simple(const uint8_t* __restric
     }
 }
 
-template <int FMT, int CDT>
+template <int FMT, int CDT, int TA = kType<FMT>, int TB = kType<FMT>>
 hipError_t run(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, int64_t M,
                int64_t N, int64_t K, void* C, int64_t ldc, hipStream_t s) {
   const int64_t rb = FMT == FMT_MXFP8 ? K : K / 2;
@@ -817,9 +822,9 @@ hipError_t run(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint
   // K a multiple of 512: whole steps and whole 16-byte scale periods per row
   const bool pipe = fits32 && K > 0 && (K % 512 == 0) &&
                     M * N >= (int64_t)kTile * kTile * 128;
-  if (pipe) return launch_pipe<FMT, CDT>(a, sa, b, sb, M, N, K, C, ldc, s);
+  if (pipe) return launch_pipe<FMT, CDT, TA, TB>(a, sa, b, sb, M, N, K, C, ldc, s);
   const uint32_t tm = (uint32_t)((M + 127) / 128), tn = (uint32_t)((N + 127) / 128);
-  hipLaunchKernelGGL((k_gemm_mx_simple<FMT, CDT>), dim3(tm * tn), dim3(256), 0, s, a, sa, b, sb,
+  hipLaunchKernelGGL((k_gemm_mx_simple<FMT, CDT, TA, TB>), dim3(tm * tn), dim3(256), 0, s, a, sa, b, sb,
                      M, N, K, C, ldc, tm, tn);
   return hipGetLastError();
 }
@@ -854,8 +859,19 @@ hipError_t launch_gemm_mxfp8_exact_pipe(const uint8_t* a_codes, const uint8_t* a
 
 hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
-                          int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s) {
+                          int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s, int fa, int fb) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (fmt == FMT_MXFP8 && (fa == FMT_MXFP8_E5M2 || fb == FMT_MXFP8_E5M2)) {
+    // FP8 pairs with E5M2 on the scaled FP8 instruction (element types 1 / 0)
+#define MXK_N8(A_, B_)                                                                               \
+  if ((fa == FMT_MXFP8_E5M2) == (A_ == 1) && (fb == FMT_MXFP8_E5M2) == (B_ == 1))                      \
+    return cdt == DT_F32 ? run<FMT_MXFP8, DT_F32, A_, B_>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s) \
+                         : run<FMT_MXFP8, DT_BF16, A_, B_>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
+    MXK_N8(1, 0)
+    MXK_N8(0, 1)
+    MXK_N8(1, 1)
+#undef MXK_N8
+  }
   if (fmt == FMT_MXFP8)
     return cdt == DT_F32 ? run<FMT_MXFP8, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s)
                          : run<FMT_MXFP8, DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);

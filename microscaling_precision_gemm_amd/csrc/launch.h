@@ -77,9 +77,12 @@ hipError_t launch_requant_transpose(const uint8_t* src_codes, const uint8_t* src
                                     int64_t ld_x, int64_t rows, int64_t cols, uint8_t* codes,
                                     uint8_t* scales, bool sr, uint64_t seed, uint64_t counter,
                                     hipStream_t s);
+// fmt FMT_MXFP8 runs on the scaled FP8 instruction; fa / fb (FMT_MXFP8 or
+// FMT_MXFP8_E5M2) then give the element types of A and B.
 hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
-                          int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s);
+                          int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s,
+                          int fa = FMT_MXFP8, int fb = FMT_MXFP8);
 // A and B in the tiled layout (M, N multiples of 32, K of 1024)
 // C = A * B^T for any pair of MX formats (E8M0 scales; row layout), exact
 // BF16 staging (gemm_any.hip).

@@ -165,14 +165,15 @@ def test_s2f6_codec_moe_combine_size_sampled_rows():
 
 
 def test_other_formats_are_rejected_where_not_offered():
-    """A pair with NVFP4, flags on a generic pair, and the tile layout."""
+    """A pair with NVFP4, the FP8 flag on a non-FP8 pair, and the tile layout."""
     a = mx.empty(5, 64, 1024, device=dev())
     nv = mx.empty(3, 64, 1024, device=dev())
     C = torch.empty(64, 64, dtype=torch.float32, device=dev())
     with pytest.raises(mx.MXError):
         mx.mx_gemm(a, nv, C)
+    i8 = mx.empty(4, 64, 1024, device=dev())
     with pytest.raises(mx.MXError):
-        mx.mx_gemm_ex(a, a, C, mx.MX_GEMM_FP8_NATIVE)
+        mx.mx_gemm_ex(i8, i8, C, mx.MX_GEMM_FP8_NATIVE)  # the FP8 instruction takes FP8 only
     tiled_fp6 = mx.empty(6, 64, 1024, device=dev(), layout=mx.MX_LAYOUT_TILED)
     with pytest.raises(mx.MXError):
         mx.mx_quantize(torch.zeros(64, 1024, dtype=torch.bfloat16, device=dev()), tiled_fp6)
@@ -440,3 +441,23 @@ def test_8bit_pairs_on_the_exact_pipeline(fa, fb, K, cdt):
     from tests.gpu_util import check_gemm
     check_gemm(np.where(keep, got, 0.0), np.where(keep, Cw, 0.0), np.where(keep, tol, 1.0), cdt == "bf16",
                f"fa={fa} fb={fb} {cdt}")
+
+
+@pytest.mark.parametrize("fa,fb", [(5, 1), (1, 5), (5, 5)])
+@pytest.mark.parametrize("shape", [(288, 320, 2048), (2048, 4096, 512)])
+def test_e5m2_row_layout_pairs_on_the_fp8_instruction(fa, fb, shape):
+    """Row-layout FP8 pairs with E5M2 and MX_GEMM_FP8_NATIVE (the small-shape
+    kernel and the DMA pipeline): within that flag's bound (1e-3 * sum|a*b|)."""
+    from tests.gpu_util import check_gemm
+    M, N, K = shape
+    ca, sa = _operand(fa, M, K, fa + 3 * fb, 110, 1.0)
+    cb, sb = _operand(fb, N, K, fa + 3 * fb, 111, 0.05)
+    A = upload(fa, ca, sa)
+    A.cols = K
+    B = upload(fb, cb, sb)
+    B.cols = K
+    C = torch.empty(M, N, dtype=torch.float32, device=dev())
+    mx.mx_gemm_ex(A, B, C, mx.MX_GEMM_FP8_NATIVE)
+    torch.cuda.synchronize()
+    Cw, tol = oracle.gemm(oracle.dequantize_f64(fa, ca, sa, M, K), oracle.dequantize_f64(fb, cb, sb, N, K))
+    check_gemm(C.cpu().numpy(), Cw, tol * 100, False, f"fa={fa} fb={fb} {shape}")
