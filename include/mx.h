@@ -338,7 +338,8 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
  * element's row-major position in C.  The FP32 product is never stored: since
  * it is fixed only to within the GEMM's bound, codes and scales are too (a
  * value near a rounding or scale boundary may land on either side).
- * `out` is MXFP8 or MXFP4 with rows = M and cols = N, in the row layout or
+ * `out` is MXFP8 (E4M3, or E5M2 -- the usual gradient format) or MXFP4 with
+ * rows = M and cols = N, in the row layout or
  * the tile layout (then M % 32 == 0 and N % 1024 == 0), so it can be the A
  * operand of the next product.  flags: MX_GEMM_FP8_NATIVE,
  * MX_FLAG_SCALE_CEIL; anything else returns MX_ERR_UNSUPPORTED, as do

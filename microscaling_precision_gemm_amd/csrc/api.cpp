@@ -377,7 +377,8 @@ mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, const mx_tens
   const int64_t M = A->rows, N = B->rows, K = A->cols;
   st = check_tensor(out, M, N);
   if (st != MX_OK) return st;
-  if (out->fmt != MX_MXFP8_E4M3 && out->fmt != MX_MXFP4_E2M1) return MX_ERR_UNSUPPORTED;
+  if (out->fmt != MX_MXFP8_E4M3 && out->fmt != MX_MXFP4_E2M1 && out->fmt != MX_MXFP8_E5M2)
+    return MX_ERR_UNSUPPORTED;
   if (M * N == 0) return MX_OK;
   return hip_status(mxk::launch_gemm_mx_tiled_quant(
       A->fmt, static_cast<const uint8_t*>(A->codes), A->scales,

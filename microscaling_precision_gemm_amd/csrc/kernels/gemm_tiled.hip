@@ -225,10 +225,11 @@ __device__ inline void store_tile_quant(uint8_t* __restrict__ smem, const v16f (
                                         int64_t M, int64_t N, int64_t r0, int64_t c0, uint32_t wid,
                                         uint32_t lane, const MxEnc& enc) {
   constexpr int PITCH = 128 * 4 + 16;  // FP32 rows, as the FP32 epilogue
+  constexpr bool kO8 = MxFmt<OFMT>::bits == 8;  // E4M3 or E5M2 codes (else E2M1)
   uint8_t* W = smem + wid * (64 * PITCH);
   const uint32_t lr = lane & 31u, lg = lane >> 5;
   const uint32_t ch = lane & 15u;  // 8-column chunk of the wave tile's row
-  const int64_t row_bytes = OFMT == FMT_MXFP8 ? N : N >> 1;
+  const int64_t row_bytes = kO8 ? N : N >> 1;
   const int64_t spr = N >> 5;  // scale bytes per row
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -265,7 +266,7 @@ __device__ inline void store_tile_quant(uint8_t* __restrict__ smem, const v16f (
                      s3 = lane_read(e.sc, lane + 12u);
       if (grow < M && gcol < N) {  // N % 32 == 0: a block is all in or all out
         if constexpr (!OTILED) {
-          if constexpr (OFMT == FMT_MXFP8)
+          if constexpr (kO8)
             *reinterpret_cast<uint2*>(codes + grow * row_bytes + gcol) = make_uint2(e.w[0], e.w[1]);
           else
             *reinterpret_cast<uint32_t*>(codes + grow * row_bytes + (gcol >> 1)) = e.w[0];
@@ -282,11 +283,11 @@ __device__ inline void store_tile_quant(uint8_t* __restrict__ smem, const v16f (
           // is byte b % 16 of chunk (b % 128) / 16 of code tile b / 128
           const int64_t T = grow >> 5;
           const uint32_t r = (uint32_t)grow & 31u;
-          const int64_t b = OFMT == FMT_MXFP8 ? gcol : gcol >> 1;
+          const int64_t b = kO8 ? gcol : gcol >> 1;
           const uint32_t c = (uint32_t)(b & 127) >> 4;
           uint8_t* cp = codes + (T * (row_bytes >> 7) + (b >> 7)) * 4096 + (c >> 1) * 1024u +
                         ((c & 1u) * 32u + r) * 16u + (uint32_t)(b & 15);
-          if constexpr (OFMT == FMT_MXFP8)
+          if constexpr (kO8)
             *reinterpret_cast<uint2*>(cp) = make_uint2(e.w[0], e.w[1]);
           else
             *reinterpret_cast<uint32_t*>(cp) = e.w[0];
@@ -398,13 +399,14 @@ hipError_t launch_gemm_mx_tiled_quant(int fmt, const uint8_t* a_codes, const uin
                                       bool ceil, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   const MxEnc enc{ceil, seed, counter};
+#define MXK_Q(F, O) \
+  launch_q_d<F, O>(a_codes, a_scales, b_codes, b_scales, M, N, K, codes, scales, enc, sr, otiled, s)
   if (fmt == FMT_MXFP8)
-    return ofmt == FMT_MXFP8
-               ? launch_q_d<FMT_MXFP8, FMT_MXFP8>(a_codes, a_scales, b_codes, b_scales, M, N, K, codes, scales, enc, sr, otiled, s)
-               : launch_q_d<FMT_MXFP8, FMT_MXFP4>(a_codes, a_scales, b_codes, b_scales, M, N, K, codes, scales, enc, sr, otiled, s);
-  return ofmt == FMT_MXFP8
-             ? launch_q_d<FMT_MXFP4, FMT_MXFP8>(a_codes, a_scales, b_codes, b_scales, M, N, K, codes, scales, enc, sr, otiled, s)
-             : launch_q_d<FMT_MXFP4, FMT_MXFP4>(a_codes, a_scales, b_codes, b_scales, M, N, K, codes, scales, enc, sr, otiled, s);
+    return ofmt == FMT_MXFP8 ? MXK_Q(FMT_MXFP8, FMT_MXFP8)
+           : ofmt == FMT_MXFP8_E5M2 ? MXK_Q(FMT_MXFP8, FMT_MXFP8_E5M2) : MXK_Q(FMT_MXFP8, FMT_MXFP4);
+  return ofmt == FMT_MXFP8 ? MXK_Q(FMT_MXFP4, FMT_MXFP8)
+         : ofmt == FMT_MXFP8_E5M2 ? MXK_Q(FMT_MXFP4, FMT_MXFP8_E5M2) : MXK_Q(FMT_MXFP4, FMT_MXFP4);
+#undef MXK_Q
 }
 
 hipError_t launch_gemm_mx_tiled(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,

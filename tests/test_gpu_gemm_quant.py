@@ -28,7 +28,7 @@ if torch.cuda.is_available():
 
 
 def _elems(fmt, codes, cols):
-    if fmt == oracle.MXFP8:
+    if fmt in (oracle.MXFP8, oracle.MXFP8_E5M2):
         return codes.astype(np.int64)
     out = np.empty((codes.shape[0], cols), np.int64)
     out[:, 0::2] = codes & 0xF
@@ -37,6 +37,9 @@ def _elems(fmt, codes, cols):
 
 
 def _dec(fmt, codes):
+    if fmt == oracle.MXFP8_E5M2:
+        lut = np.array([oracle.elem_decode(fmt, c) for c in range(256)], np.float64)
+        return lut[codes]
     f = oracle.e4m3_decode if fmt == oracle.MXFP8 else oracle.e2m1_decode
     lut = np.array([f(c) for c in range(256 if fmt == oracle.MXFP8 else 16)], np.float64)
     return lut[codes]
@@ -103,13 +106,13 @@ def _run(M, N, K, fmt, ofmt, rnd, otiled, ceil, seed):
     mx.mx_gemm_quantize(A, B, out, rnd, seed, 5 * seed + 1, flags)
     torch.cuda.synchronize()
     codes, scales = out.codes.cpu().numpy(), out.scales.cpu().numpy()
-    rb = N if ofmt == oracle.MXFP8 else N // 2
+    rb = N if ofmt in (oracle.MXFP8, oracle.MXFP8_E5M2) else N // 2
     if otiled:
         codes, scales = untile_codes(codes, M, rb), untile_scales(scales, M, N // 32)
     return qa, qb, codes.reshape(M, rb), scales.reshape(M, N // 32)
 
 
-@pytest.mark.parametrize("ofmt", [1, 2])
+@pytest.mark.parametrize("ofmt", [1, 2, 5])
 @pytest.mark.parametrize("rnd", [0, 1])
 @pytest.mark.parametrize("otiled", [False, True])
 def test_quantized_product_mxfp4(ofmt, rnd, otiled):
