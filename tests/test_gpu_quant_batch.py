@@ -148,3 +148,30 @@ def test_nvfp4_shared_amax_slot_keeps_call_order():
         torch.cuda.synchronize()
         for u, v in zip(host(j["out"]), host(out)):
             assert np.array_equal(u, v)
+
+
+def test_nvfp4_expert_weights_full_size_batch():
+    """The mixture-of-experts weights at full size (32 experts of 2048 x 7168
+    BF16, N(0, 0.02^2)), 2-D blocks, each expert its own amax and tensor scale,
+    in one batch call as the benchmark runs it; experts 0 and 29 checked bit
+    for bit against the oracle, tensor scales of all 32 against the oracle's
+    T / 2688 of each expert."""
+    import oracle
+    E, rows, cols = 32, 2048, 7168
+    bits = W.normal_bf16(E * rows, cols, 0.02, 0, 120)
+    Wt = to_gpu_bf16(bits)
+    q = mx.empty(3, E * rows, cols, device=dev(), n_tensor_scales=E)
+    amax = torch.zeros(E, dtype=torch.float32, device=dev())
+    jobs = [dict(x=Wt[e * rows:(e + 1) * rows], out=q.view_rows(e * rows, (e + 1) * rows, q.tensor_scale[e:e + 1]),
+                 flags=mx.MX_FLAG_BLOCK_2D, amax=amax[e:e + 1]) for e in range(E)]
+    mx.mx_quantize_batch(jobs)
+    torch.cuda.synchronize()
+    codes, scales, ts = host(q)
+    for e in (0, 29):
+        wc, ws, wts = oracle.quantize(bits[e * rows:(e + 1) * rows], 3, variant=oracle.V_2D)
+        assert np.array_equal(scales[e * rows:(e + 1) * rows], ws), f"expert {e}: scales"
+        assert np.array_equal(codes[e * rows:(e + 1) * rows], wc), f"expert {e}: codes"
+        assert np.float32(ts[e]) == np.float32(wts), f"expert {e}: tensor scale"
+    T = np.abs(W.bf16_bits_to_f32(bits).reshape(E, -1)).max(axis=1).astype(np.float32)
+    assert np.array_equal(amax.cpu().numpy(), T)
+    assert np.array_equal(ts.astype(np.float32), (T / np.float32(2688.0)).astype(np.float32))
