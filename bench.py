@@ -293,6 +293,12 @@ def detail(torch, mx, W, args):
         mx.mx_quantize(C, q4c, rnd, 1, 0)
     ms_tr = time_fn(torch, lambda: two_step(mx.MX_RNE), it, wu)
     ms_ts = time_fn(torch, lambda: two_step(mx.MX_SR), it, wu)
+    # the same product written as MXFP8 E5M2 with SR (a gradient's format), tile layout
+    q5c = mx.empty(mx.MX_MXFP8_E5M2, M, N, layout=mx.MX_LAYOUT_TILED)
+    ms_f5 = time_fn(torch, lambda: mx.mx_gemm_quantize(q4at, q4bt, q5c, mx.MX_SR, 1, 0), it, wu)
+    res["mxfp4_gemm_quantize_4096_fused_e5m2_sr"] = {"ms": ms_f5, "tflops": 2 * M * N * K / ms_f5 / 1e9,
+                                                     "kernel": "k_gemm_mx_tiled_q<MXFP4, E5M2, SR, tiled>"}
+    del q5c
     res["mxfp4_gemm_quantize_4096_fused"] = {
         "fused_rne_ms": ms_fr, "fused_rne_tflops": 2 * M * N * K / ms_fr / 1e9, "two_step_rne_ms": ms_tr,
         "fused_sr_ms": ms_fs, "two_step_sr_ms": ms_ts}
@@ -434,6 +440,15 @@ def detail(torch, mx, W, args):
                                     "frac_peak": tf / PEAK_TFLOPS["fp6" if native else "bf16"],
                                     "peak": "fp6" if native else "bf16"}
         del qa_, qb_
+    # E5M2 x E4M3 in the row layout on the scaled FP8 instruction (MX_GEMM_FP8_NATIVE)
+    qa_, qb_ = mx.empty(mx.MX_MXFP8_E5M2, M2, M2), mx.empty(mx.MX_MXFP8_E4M3, M2, M2)
+    mx.mx_quantize(Xa, qa_)
+    mx.mx_quantize(Xb, qb_)
+    ms_m = time_fn(torch, lambda: mx.mx_gemm_ex(qa_, qb_, Cm, mx.MX_GEMM_FP8_NATIVE), it, wu)
+    res["gemm_4096_e5m2_x_e4m3_native_fp8_rows"] = {"ms": ms_m, "tflops": 2 * M2**3 / ms_m / 1e9,
+                                                    "frac_fp8_peak": 2 * M2**3 / ms_m / 1e9 / PEAK_TFLOPS["fp8"],
+                                                    "kernel": "k_gemm_mx_pipe<MXFP8, BF16, E5M2, E4M3>"}
+    del qa_, qb_
     # E5M2 x E4M3 in the tile layout on the scaled FP8 instruction (MX_GEMM_FP8_NATIVE)
     qa_ = mx.empty(mx.MX_MXFP8_E5M2, M2, M2, layout=mx.MX_LAYOUT_TILED)
     qb_ = mx.empty(mx.MX_MXFP8_E4M3, M2, M2, layout=mx.MX_LAYOUT_TILED)
