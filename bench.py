@@ -424,7 +424,7 @@ def detail(torch, mx, W, args):
     # pipeline; the rest decode to BF16 in k_gemm_mx_any)
     for name, fa_, fb_, native in (("mxint8_x_mxint8", mx.MX_MXINT8, mx.MX_MXINT8, None),
                                    ("e5m2_x_e4m3", mx.MX_MXFP8_E5M2, mx.MX_MXFP8_E4M3, None),
-                                   ("fp6_e3m2_x_fp6_e3m2", mx.MX_MXFP6_E3M2, mx.MX_MXFP6_E3M2, False),
+                                   ("fp6_e3m2_x_fp6_e3m2", mx.MX_MXFP6_E3M2, mx.MX_MXFP6_E3M2, "bf16"),
                                    ("fp6_e2m3_x_fp6_e2m3", mx.MX_MXFP6_E2M3, mx.MX_MXFP6_E2M3, True),
                                    ("fp6_e2m3_x_fp4", mx.MX_MXFP6_E2M3, mx.MX_MXFP4_E2M1, True),
                                    ("fp6_e3m2_x_fp4", mx.MX_MXFP6_E3M2, mx.MX_MXFP4_E2M1, True)):
@@ -434,11 +434,14 @@ def detail(torch, mx, W, args):
         ms_m = time_fn(torch, lambda: mx.mx_gemm(qa_, qb_, Cm), it, wu)
         tf = 2 * M2**3 / ms_m / 1e9
         res[f"gemm_4096_{name}"] = {"ms": ms_m, "tflops": tf,
-                                    "kernel": "k_gemm_mx_f6 (scaled FP6/FP4 instruction)" if native
-                                    else "k_gemm_mx8_exact (8-bit codes converted to BF16 after the fragment reads)"
-                                    if native is None else "k_gemm_mx_any (exact BF16 decode)",
-                                    "frac_peak": tf / PEAK_TFLOPS["fp6" if native else "bf16"],
-                                    "peak": "fp6" if native else "bf16"}
+                                    "kernel": {True: "k_gemm_mx_f6 (scaled FP6/FP4 instruction)",
+                                               None: "k_gemm_mx8_exact (8-bit codes converted to BF16 after the "
+                                                     "fragment reads)",
+                                               "bf16": "k_gemm_mx_f6<E3M2, E3M2> (decoded to BF16 in the FP6 kernel) "
+                                                       "+ k_gemm_mx_any fix-up scan",
+                                               False: "k_gemm_mx_any (exact BF16 decode)"}[native],
+                                    "frac_peak": tf / PEAK_TFLOPS["fp6" if native is True else "bf16"],
+                                    "peak": "fp6" if native is True else "bf16"}
         del qa_, qb_
     # E5M2 x E4M3 in the row layout on the scaled FP8 instruction (MX_GEMM_FP8_NATIVE)
     qa_, qb_ = mx.empty(mx.MX_MXFP8_E5M2, M2, M2), mx.empty(mx.MX_MXFP8_E4M3, M2, M2)

@@ -295,16 +295,17 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
  *          result multiplied by S_A * S_B.
  *   FP6 pairs (E2M3 or E3M2 against E2M3, E3M2 or MXFP4, not E3M2 x E3M2),
  *          K % 512 == 0: scaled FP6/FP4 matrix instructions, which form the
- *          exact sum of each instruction's 64 products (measured on gfx950;
- *          E3M2 x E3M2 is summed in a narrower window and takes the BF16
- *          path below).
+ *          exact sum of each instruction's 64 products (measured on gfx950).
+ *          E3M2 x E3M2, which that instruction sums in a narrower window, is
+ *          decoded to exact BF16 in the same kernel (scale codes 5 .. 250;
+ *          tiles with codes 0 or 255 recomputed by the generic kernel).
  *   Other pairs of 8-bit types (E4M3, E5M2, INT8: E5M2 x E4M3, INT8 x INT8,
  *          INT8 x E4M3, ...) where the MXFP8 pipeline fits (K % 512 == 0,
  *          M * N >= 2^23): as MXFP8, each element times its scale converted to BF16,
  *          exact for scale codes c in [17, 239] (E5M2) and [7, 254] (INT8);
  *          codes 0 and 255 are recomputed as for MXFP8.
- *   Other MX pairs (mixed formats, INT8, E3M2 x E3M2, FP6 and E5M2 pairs at
- *          other shapes): every element times its scale decoded to exact
+ *   Other MX pairs (8-bit types mixed with FP6 or FP4, FP6 and 8-bit pairs
+ *          at other shapes): every element times its scale decoded to exact
  *          BF16 (exact while the scaled values are normal BF16 values), BF16
  *          matrix instructions.
  * The scaled matrix instructions (MXFP4, FP6 pairs, MX_GEMM_FP8_NATIVE) flush

@@ -173,18 +173,47 @@ __device__ __attribute__((always_inline)) inline void load_unit(int bits, const 
 
 // Thread t stages, per step, the units t + 256 j: row (t + 256 j) / 2 of the
 // stacked [A tile; B tile] rows, K half t % 2 -- j < U/2 are A rows.
+// nonzero when some byte of w is 0x00 or 0xFF
+__device__ inline uint32_t special_code_bytes(uint32_t w) {
+  const uint32_t z = (w - 0x01010101u) & ~w & 0x80808080u;
+  const uint32_t nw = ~w;
+  return z | ((nw - 0x01010101u) & ~nw & 0x80808080u);
+}
+
+// fixup: the workgroup first scans the scale rows of its tile and computes
+// the tile only if one holds code 0 or 255 (K % 512 == 0: 16-byte scale
+// loads) -- the fix-up pass behind a kernel that does not take those codes.
 template <int CDT, int T>
 __global__ __launch_bounds__(256) void k_gemm_mx_any(int fa, int fb, const uint8_t* __restrict__ A,
                                                      const uint8_t* __restrict__ SA,
                                                      const uint8_t* __restrict__ B,
                                                      const uint8_t* __restrict__ SB, int64_t M, int64_t N,
                                                      int64_t K, void* __restrict__ C, int64_t ldc,
-                                                     uint32_t tiles_n) {
+                                                     uint32_t tiles_n, int fixup) {
   constexpr int U = 2 * T * 2 / 256;  // units per thread and step (2 or 4)
   constexpr int F = T / 64;           // 32 x 32 instruction tiles per wave and dimension
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * T * kPitch];
   const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * T, n0 = (int64_t)(blockIdx.x % tiles_n) * T;
   const uint32_t t = threadIdx.x, lane = t & 63u, wid = t >> 6;
+  if (fixup) {
+    static_assert(T == 128, "one scale row per thread");
+    __shared__ uint32_t found;
+    if (t == 0) found = 0u;
+    __syncthreads();
+    const int64_t r = t < 128 ? m0 + t : n0 + (t - 128);
+    const int64_t kbytes = K / 32;
+    uint32_t sp = 0u;
+    if (r < (t < 128 ? M : N)) {
+      const uint8_t* srow = (t < 128 ? SA : SB) + r * kbytes;
+      for (int64_t q = 0; q < kbytes; q += 16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(srow + q);
+        sp |= special_code_bytes(v.x) | special_code_bytes(v.y) | special_code_bytes(v.z) | special_code_bytes(v.w);
+      }
+    }
+    if (sp) atomicOr(&found, 1u);
+    __syncthreads();
+    if (found == 0u) return;  // uniform
+  }
   const uint32_t wm = wid >> 1, wn = wid & 1u;
   const int ba = code_bits(fa), bb = code_bits(fb);
   const int64_t rba = K * ba / 8, rbb = K * bb / 8, kb = K / 32;
@@ -277,8 +306,9 @@ __global__ __launch_bounds__(256) void k_gemm_mx_any(int fa, int fb, const uint8
 
 hipError_t launch_gemm_mx_any(int fa, const uint8_t* a_codes, const uint8_t* a_scales, int fb,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
-                              int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s) {
+                              int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s, bool fixup) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (fixup && K % 512 != 0) return hipErrorInvalidValue;
   // 128 x 128 tiles, two workgroups per CU: with 256 x 256 tiles the six
   // inlined decoders of four units per thread spill registers
   constexpr int64_t T = 128;
@@ -286,7 +316,7 @@ hipError_t launch_gemm_mx_any(int fa, const uint8_t* a_codes, const uint8_t* a_s
   if ((uint64_t)tm * tn > 0x7FFFFFFFull) return hipErrorInvalidValue;
 #define MXK_ANY(D, TT)                                                                                    \
   hipLaunchKernelGGL((k_gemm_mx_any<D, TT>), dim3(tm * tn), dim3(256), 0, s, fa, fb, a_codes, a_scales, b_codes, \
-                     b_scales, M, N, K, C, ldc, tn)
+                     b_scales, M, N, K, C, ldc, tn, fixup ? 1 : 0)
   if (cdt == DT_F32) MXK_ANY(DT_F32, 128);
   else MXK_ANY(DT_BF16, 128);
 #undef MXK_ANY

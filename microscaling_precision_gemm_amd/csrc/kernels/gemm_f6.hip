@@ -208,8 +208,43 @@ __device__ inline void read_scales(const uint8_t* smem, uint32_t step, uint32_t 
   }
 }
 
+// E3M2 x E3M2 is not summed exactly by the scaled instruction.  Its operands
+// are decoded instead: each lane's 24-byte block times its E8M0 scale becomes
+// 32 BF16 values with one v_cvt_scalef32_pk32_bf16_bf6 (exact while the
+// scaled values are normal BF16 values: scale codes 5 .. 250), which feed
+// four v_mfma_f32_32x32x16_bf16.  Instruction k takes elements 8k .. 8k+7 of
+// every lane's block, the same positions for A and B, so the 64 products of
+// the slice are each summed once (exact products, FP32 accumulation).
+typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+typedef __bf16 v32bf_t __attribute__((ext_vector_type(32)));
+typedef unsigned int v6u_t __attribute__((ext_vector_type(6)));
+struct Bf16Block {
+  v8bf_t k[4];
+};
+
+__device__ inline Bf16Block decode_bf6(const v8i& o, uint32_t code) {
+  const v6u_t w = {(unsigned)o[0], (unsigned)o[1], (unsigned)o[2], (unsigned)o[3], (unsigned)o[4], (unsigned)o[5]};
+  const v32bf_t r = __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(w, u2f(code << 23));
+  return __builtin_bit_cast(Bf16Block, r);
+}
+
 template <int TA, int TB, int Q>
 __device__ inline void mfma_slice(const RawSlice<TA, TB>& s, const StepScales& sc, bool h, v16f (&acc)[4][4]) {
+  if constexpr (TA == kE3M2 && TB == kE3M2) {
+    Bf16Block bd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bd[j] = decode_bf6(operand<TB>(s.b[j], h), (sc.b[j] >> (16 * Q)) & 0xFFu);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const Bf16Block ad = decode_bf6(operand<TA>(s.a[i], h), (sc.a[i] >> (16 * Q)) & 0xFFu);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad.k[k], bd[j].k[k], acc[i][j], 0, 0, 0);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const v8i a = operand<TA>(s.a[i], h);
@@ -359,7 +394,6 @@ bool gemm_mx_f6_fits(int fa, int fb, int64_t M, int64_t N, int64_t K) {
   const int ta = f6_type(fa), tb = f6_type(fb);
   if (ta < 0 || tb < 0) return false;
   if (ta == kE2M1 && tb == kE2M1) return false;  // MXFP4 x MXFP4 has its own kernels
-  if (ta == kE3M2 && tb == kE3M2) return false;  // not exact on the scaled instruction
   if (K % 512 != 0 || K <= 0) return false;
   // 32-bit tile count; 64-bit addressing elsewhere
   return (uint64_t)((M + 255) / 256) * (uint64_t)((N + 255) / 256) <= 0x7FFFFFFFull;
@@ -371,6 +405,15 @@ hipError_t launch_gemm_mx_f6(int fa, const uint8_t* a_codes, const uint8_t* a_sc
   if (!gemm_mx_f6_fits(fa, fb, M, N, K)) return hipErrorInvalidValue;
   if (M == 0 || N == 0) return hipSuccess;
   const int ta = f6_type(fa), tb = f6_type(fb);
+  if (ta == kE3M2 && tb == kE3M2) {
+    // decoded to BF16 (see mfma_slice), then the tiles whose operands hold
+    // scale code 0 or 255 recomputed by the generic kernel's fix-up mode
+    const hipError_t e = cdt == DT_F32
+                             ? launch_f6<kE3M2, kE3M2, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s)
+                             : launch_f6<kE3M2, kE3M2, DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_mx_any(fa, a_codes, a_scales, fb, b_codes, b_scales, M, N, K, C, cdt, ldc, s, true);
+  }
 #define MXK_F6(A_, B_)                                                                                   \
   if (ta == A_ && tb == B_)                                                                              \
     return cdt == DT_F32 ? launch_f6<A_, B_, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s) \

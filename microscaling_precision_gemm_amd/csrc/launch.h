@@ -86,9 +86,11 @@ hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scal
 // A and B in the tiled layout (M, N multiples of 32, K of 1024)
 // C = A * B^T for any pair of MX formats (E8M0 scales; row layout), exact
 // BF16 staging (gemm_any.hip).
+// fixup: only the 128 x 128 tiles whose operand rows hold scale code 0 or
+// 255 are computed (K % 512 == 0), the others are left as they are.
 hipError_t launch_gemm_mx_any(int fa, const uint8_t* a_codes, const uint8_t* a_scales, int fb,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
-                              int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s);
+                              int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s, bool fixup = false);
 // MX pairs with an FP6 operand (E2M3/E3M2 against E2M3/E3M2/E2M1, not E3M2 x
 // E3M2) on the scaled FP6/FP4 instruction (gemm_f6.hip); shapes it takes.
 bool gemm_mx_f6_fits(int fa, int fb, int64_t M, int64_t N, int64_t K);

@@ -461,3 +461,36 @@ def test_e5m2_row_layout_pairs_on_the_fp8_instruction(fa, fb, shape):
     torch.cuda.synchronize()
     Cw, tol = oracle.gemm(oracle.dequantize_f64(fa, ca, sa, M, K), oracle.dequantize_f64(fb, cb, sb, N, K))
     check_gemm(C.cpu().numpy(), Cw, tol * 100, False, f"fa={fa} fb={fb} {shape}")
+
+
+@pytest.mark.parametrize("cdt", ["f32", "bf16"])
+def test_e3m2_pair_decoded_with_special_scale_codes(cdt):
+    """E3M2 x E3M2 (K % 512 == 0) is decoded to BF16 inside the FP6 kernel;
+    tiles whose operands hold scale code 0 or 255 are recomputed by the
+    generic kernel's fix-up pass: NaN exactly where the oracle has it, the
+    rest within the bound."""
+    M, N, K = 300, 520, 1024
+    ca, sa = _operand_blocks(6, M, K, 77, 112, 1.0)
+    cb, sb = _operand_blocks(6, N, K, 77, 114, 0.05)
+    sa, sb = sa.copy(), sb.copy()
+    sa[5, 3] = 0
+    sa[200, 10] = 255
+    sb[130, 7] = 0
+    sb[400, 2] = 255
+    A = upload(6, ca, sa)
+    A.cols = K
+    B = upload(6, cb, sb)
+    B.cols = K
+    C = torch.full((M, N), 7.0, dtype=torch.float32 if cdt == "f32" else torch.bfloat16, device=dev())
+    mx.mx_gemm(A, B, C)
+    torch.cuda.synchronize()
+    Cw, tol = oracle.gemm(oracle.dequantize_f64(6, ca, sa, M, K), oracle.dequantize_f64(6, cb, sb, N, K))
+    got = C.float().cpu().numpy()
+    nan_want = np.isnan(Cw)
+    assert nan_want[200].all() and nan_want[:, 400].all()
+    assert np.isnan(got[nan_want]).all()
+    keep = ~nan_want
+    assert not np.isnan(got[keep]).any()
+    from tests.gpu_util import check_gemm
+    check_gemm(np.where(keep, got, 0.0), np.where(keep, Cw, 0.0), np.where(keep, tol, 1.0), cdt == "bf16",
+               f"e3m2 pair {cdt}")
