@@ -1,6 +1,7 @@
 // gemm_f6.hip -- block-scaled GEMM C = A * B^T for MX pairs with an FP6
 // operand (MXFP6 E2M3 or E3M2 against E2M3, E3M2 or E2M1; row layout) on
-// gfx950's scaled matrix instruction v_mfma_scale_f32_32x32x64_f8f6f4
+// gfx950's scaled matrix instruction v_mfma_scale_f32_32x32x64_f8f6f4 (E3M2 x
+// E3M2 on the BF16 instruction)
 // ("Microscaling (MX) and block-scaled 4-bit formats", section "Hardware and
 // kernels": the block scales are applied inside the matrix instruction;
 // "08 - FP4, MXFP4, NVFP4: The Blackwell Frontier", section "The OCP
@@ -10,7 +11,8 @@
 // adversarial codes): for these pairs the instruction forms the exact sum of
 // its 64 products and rounds it once into the FP32 accumulator, as for FP4 x
 // FP4.  E3M2 x E3M2, whose products span 18 bits, is summed in a narrower
-// window (errors up to ~1e-4 of sum|a*b|) and stays on the BF16 kernel.  Like
+// window (errors up to ~1e-4 of sum|a*b|), so this kernel decodes that pair
+// to BF16 instead (see mfma_slice).  Like
 // every scaled-instruction path, partial sums in FP32's subnormal range are
 // flushed, so exactness needs the products of each block pair to stay above
 // 2^-126 (combined scale codes c_a + c_b >= 135 suffice for every pair).
