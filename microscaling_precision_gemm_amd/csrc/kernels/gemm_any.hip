@@ -196,19 +196,24 @@ __global__ __launch_bounds__(256) void k_gemm_mx_any(int fa, int fb, const uint8
   const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * T, n0 = (int64_t)(blockIdx.x % tiles_n) * T;
   const uint32_t t = threadIdx.x, lane = t & 63u, wid = t >> 6;
   if (fixup) {
-    static_assert(T == 128, "one scale row per thread");
     __shared__ uint32_t found;
     if (t == 0) found = 0u;
     __syncthreads();
-    const int64_t r = t < 128 ? m0 + t : n0 + (t - 128);
+    // The scale rows of the tile's A rows (and of its B rows) are one
+    // contiguous run of rows * K/32 bytes, a multiple of 16: read as
+    // consecutive 16-byte words by consecutive lanes.
     const int64_t kbytes = K / 32;
+    const int64_t na = (M - m0 < T ? M - m0 : T) * kbytes, nb = (N - n0 < T ? N - n0 : T) * kbytes;
+    const uint8_t* pa = SA + m0 * kbytes;
+    const uint8_t* pb = SB + n0 * kbytes;
     uint32_t sp = 0u;
-    if (r < (t < 128 ? M : N)) {
-      const uint8_t* srow = (t < 128 ? SA : SB) + r * kbytes;
-      for (int64_t q = 0; q < kbytes; q += 16) {
-        const uint4 v = *reinterpret_cast<const uint4*>(srow + q);
-        sp |= special_code_bytes(v.x) | special_code_bytes(v.y) | special_code_bytes(v.z) | special_code_bytes(v.w);
-      }
+    for (int64_t q = 16 * (int64_t)t; q < na; q += 16 * 256) {
+      const uint4 v = *reinterpret_cast<const uint4*>(pa + q);
+      sp |= special_code_bytes(v.x) | special_code_bytes(v.y) | special_code_bytes(v.z) | special_code_bytes(v.w);
+    }
+    for (int64_t q = 16 * (int64_t)t; q < nb; q += 16 * 256) {
+      const uint4 v = *reinterpret_cast<const uint4*>(pb + q);
+      sp |= special_code_bytes(v.x) | special_code_bytes(v.y) | special_code_bytes(v.z) | special_code_bytes(v.w);
     }
     if (sp) atomicOr(&found, 1u);
     __syncthreads();
