@@ -187,17 +187,20 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
     __shared__ uint32_t found[4];
     const int64_t kb = K / 32;  // scale bytes per row, a multiple of 16
     uint32_t sp = 0;
-    const int64_t ra = g_lo + t, rb = n0 + t;
-    const u4* pa = ra < g_hi ? reinterpret_cast<const u4*>(SA + ra * kb) : nullptr;
-    const u4* pb = rb < N ? reinterpret_cast<const u4*>(SB + rb * kb) : nullptr;
-    const int64_t n16 = kb / 16;
-    for (int64_t q0 = 0; q0 < n16; q0 += 8) {  // 16 loads in flight per lane
+    // The tile's A scale rows (and its B scale rows) are one contiguous run
+    // of rows * kb bytes: consecutive lanes read consecutive 16-byte words.
+    const int64_t ca = (g_hi - g_lo < BM ? g_hi - g_lo : BM) * kb / 16;
+    const int64_t cb = (N - n0 < BN ? N - n0 : BN) * kb / 16;
+    const u4* pa = reinterpret_cast<const u4*>(SA + g_lo * kb);
+    const u4* pb = reinterpret_cast<const u4*>(SB + n0 * kb);
+    const int64_t cmax = ca > cb ? ca : cb;
+    for (int64_t q0 = t; q0 < cmax; q0 += 256 * 8) {  // 16 loads in flight per lane
       u4 v[16];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t q = q0 + u < n16 ? q0 + u : n16 - 1;
-        v[u] = pa ? pa[q] : u4{1u, 1u, 1u, 1u};
-        v[8 + u] = pb ? pb[q] : u4{1u, 1u, 1u, 1u};
+        const int64_t q = q0 + 256 * u;
+        v[u] = q < ca ? pa[q] : u4{1u, 1u, 1u, 1u};
+        v[8 + u] = q < cb ? pb[q] : u4{1u, 1u, 1u, 1u};
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u)
