@@ -92,6 +92,7 @@ def lib():
         "mxo_codes_bytes": (i64, [ci, i64, i64]),
         "mxo_scales_bytes": (i64, [ci, i64, i64]),
         "mxo_tensor_bytes": (i64, [ci, i64, i64]),
+        "mxo_nv_sq_error_cmp": (ci, [c_f32p, c_u8p, u32, c_u8p, u32, ctypes.c_float]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -257,6 +258,18 @@ def quantize(x: np.ndarray, fmt: int, rnd: int = RNE, seed: int = 0, counter: in
     if rc:
         raise ValueError("oracle rejected the shape")
     return codes, scales, None
+
+
+def nv_sq_error_cmp(v: np.ndarray, codes_a, sb_a: int, codes_b, sb_b: int, S: float) -> int:
+    """Sign of (exact squared error of encoding a) - (that of encoding b) for
+    one 16-element NVFP4 block: v float32[16], codes 16 E2M1 codes each, sb
+    the E4M3 block-scale codes, S the tensor scale."""
+    v = np.ascontiguousarray(v, np.float32)
+    ca = np.ascontiguousarray(codes_a, np.uint8)
+    cb = np.ascontiguousarray(codes_b, np.uint8)
+    assert v.shape == ca.shape == cb.shape == (16,)
+    return int(lib().mxo_nv_sq_error_cmp(_ptr(v, ctypes.c_float), _ptr(ca, ctypes.c_uint8), sb_a,
+                                         _ptr(cb, ctypes.c_uint8), sb_b, S))
 
 
 def dequantize(fmt: int, codes: np.ndarray, scales: np.ndarray, tensor_scale, rows: int,

@@ -630,26 +630,112 @@ static uint32_t nv_encode_block(const float* v, float ab, float T, float S, floa
   return sb;
 }
 
-/* Squared error of a block against its decoded values (for MXO_V_FOUR6).
- * READING (the pages say only that the choice aims at lower quantization
- * error): the error is the sum of squared differences between x and its
- * decoded value fp32(e2m1 * e4m3 * S), evaluated in FP32 in a fixed order --
- * d = x - xhat rounded once, each half of 8 elements accumulated with fused
- * multiply-adds acc = fma(d, d, acc) from element 0 up, then the two halves
- * added -- so that the choice is a reproducible function of the input. */
-static float nv_block_sq_error(const float* v, const uint32_t codes[16], uint32_t sb, float S) {
-  double dsb = mxo_e4m3_decode(sb);
-  float half[2] = {0.0f, 0.0f};
-  for (int h = 0; h < 2; ++h) {
-    for (int i = 0; i < 8; ++i) {
-      int j = 8 * h + i;
-      double p = mxo_e2m1_decode(codes[j]) * dsb; /* exact */
-      float xh = (float)p * S;
-      float d = v[j] - xh;
-      half[h] = fmaf(d, d, half[h]);
-    }
+/* Exact squared error of a block against its decoded values, for the Four
+ * Over Six choice (MXO_V_FOUR6).  The page asks only for the block scale with
+ * the lower quantization error; READING: the error is the sum over the 16
+ * elements of (x - xhat)^2, xhat = fp32(e2m1 * e4m3 * S) the decoded value,
+ * evaluated EXACTLY (no rounding anywhere), and the two candidates are
+ * compared exactly.
+ *
+ * Every finite FP32 value is an integer multiple of 2^-149 below 2^128, so
+ * x - xhat is an integer D times 2^-149 with |D| < 2^278, and (x - xhat)^2 is
+ * the integer D^2 < 2^556 times 2^-298.  The sum of 16 such squares is kept as
+ * an unsigned integer of FX_LIMBS 64-bit limbs (least significant first). */
+#define FX_LIMBS 10
+typedef struct { uint64_t w[FX_LIMBS]; } fx_int;
+
+/* |f| * 2^149 as an integer (f finite). */
+static void fx_from_f32(float f, fx_int* r) {
+  uint32_t b;
+  memcpy(&b, &f, 4);
+  const uint32_t e = (b >> 23) & 0xFFu, m = b & 0x7FFFFFu;
+  /* normal: (m + 2^23) * 2^(e - 150) = (m + 2^23) * 2^(e - 1) * 2^-149;
+   * subnormal: m * 2^-149 */
+  const uint64_t mant = e ? (uint64_t)(m | 0x800000u) : m;
+  const int sh = e ? (int)e - 1 : 0;
+  memset(r, 0, sizeof *r);
+  r->w[sh / 64] = mant << (sh % 64);
+  if (sh % 64 && sh / 64 + 1 < FX_LIMBS) r->w[sh / 64 + 1] = mant >> (64 - sh % 64);
+}
+
+static int fx_cmp(const fx_int* a, const fx_int* b) {
+  for (int i = FX_LIMBS - 1; i >= 0; --i)
+    if (a->w[i] != b->w[i]) return a->w[i] < b->w[i] ? -1 : 1;
+  return 0;
+}
+
+/* r = a - b, for a >= b */
+static void fx_sub(const fx_int* a, const fx_int* b, fx_int* r) {
+  uint64_t borrow = 0;
+  for (int i = 0; i < FX_LIMBS; ++i) {
+    const uint64_t x = a->w[i], y = b->w[i];
+    const uint64_t d = x - y - borrow;
+    borrow = (x < y) || (x - y < borrow);
+    r->w[i] = d;
   }
-  return half[0] + half[1];
+}
+
+/* r = a + b */
+static void fx_add(const fx_int* a, const fx_int* b, fx_int* r) {
+  uint64_t carry = 0;
+  for (int i = 0; i < FX_LIMBS; ++i) {
+    const unsigned __int128 s = (unsigned __int128)a->w[i] + b->w[i] + carry;
+    r->w[i] = (uint64_t)s;
+    carry = (uint64_t)(s >> 64);
+  }
+}
+
+/* acc += a * a (a < 2^320, so only its low FX_LIMBS / 2 limbs are nonzero) */
+static void fx_add_square(const fx_int* a, fx_int* acc) {
+  fx_int p;
+  memset(&p, 0, sizeof p);
+  for (int i = 0; i < FX_LIMBS / 2; ++i) {
+    uint64_t carry = 0;
+    for (int j = 0; j < FX_LIMBS / 2; ++j) {
+      const unsigned __int128 t = (unsigned __int128)a->w[i] * a->w[j] + p.w[i + j] + carry;
+      p.w[i + j] = (uint64_t)t;
+      carry = (uint64_t)(t >> 64);
+    }
+    p.w[i + FX_LIMBS / 2] = carry;
+  }
+  fx_add(acc, &p, acc);
+}
+
+/* The exact error sum of one encoded block (codes, block-scale code sb) as an
+ * integer multiple of 2^-298. */
+static void nv_block_sq_error(const float* v, const uint32_t codes[16], uint32_t sb, float S,
+                              fx_int* err) {
+  const double dsb = mxo_e4m3_decode(sb);
+  memset(err, 0, sizeof *err);
+  for (int j = 0; j < 16; ++j) {
+    const double p = mxo_e2m1_decode(codes[j]) * dsb; /* exact: at most 6 significant bits */
+    const float xh = (float)p * S;                    /* the decoded FP32 value */
+    fx_int a, b, d;
+    fx_from_f32(v[j], &a);
+    fx_from_f32(xh, &b);
+    if (signbit(v[j]) == signbit(xh)) { /* |x - xhat| = ||x| - |xhat|| */
+      if (fx_cmp(&a, &b) >= 0) fx_sub(&a, &b, &d);
+      else fx_sub(&b, &a, &d);
+    } else {
+      fx_add(&a, &b, &d);
+    }
+    fx_add_square(&d, err);
+  }
+}
+
+/* Sign of (error of encoding a) - (error of encoding b) for one block, both
+ * exact (for the tests of this comparison). */
+int mxo_nv_sq_error_cmp(const float v[16], const uint8_t ca[16], uint32_t sba, const uint8_t cb[16],
+                        uint32_t sbb, float S) {
+  uint32_t a[16], b[16];
+  for (int j = 0; j < 16; ++j) {
+    a[j] = ca[j];
+    b[j] = cb[j];
+  }
+  fx_int ea, eb;
+  nv_block_sq_error(v, a, sba, S, &ea);
+  nv_block_sq_error(v, b, sbb, S, &eb);
+  return fx_cmp(&ea, &eb);
 }
 
 /* NVFP4 quantization with the variants:
@@ -658,7 +744,8 @@ static float nv_block_sq_error(const float* v, const uint32_t codes[16], uint32_
  *     quantization error).
  *     READING: every block is encoded twice, with its maximum mapped to 6
  *     (the rule above) and to 4 (q = a_b / (4 S)); the encoding with the
- *     smaller error (nv_block_sq_error) is kept, the 6-encoding on a tie.
+ *     smaller exact squared error (nv_block_sq_error) is kept, the
+ *     6-encoding on a tie.
  *     S is the format's T / 2688 in both, so a 4-candidate whose scale
  *     saturates at 448 simply loses.  Round-to-nearest only.
  *   MXO_V_2D ([MXF] "NVFP4": two-dimensional weight quantisation so forward
@@ -707,7 +794,10 @@ int mxo_quantize_nvfp4(const void* x, int xdt, int64_t ld, int64_t rows, int64_t
           const uint32_t* cw = c6;
           if (four6 && T != 0.0f) {
             uint32_t sb4 = nv_encode_block(v, ab, T, S, 4.0f, rnd, seed, counter, n0, c4);
-            if (nv_block_sq_error(v, c4, sb4, S) < nv_block_sq_error(v, c6, sb, S)) {
+            fx_int e6, e4;
+            nv_block_sq_error(v, c6, sb, S, &e6);
+            nv_block_sq_error(v, c4, sb4, S, &e4);
+            if (fx_cmp(&e4, &e6) < 0) {
               sb = sb4;
               cw = c4;
             }

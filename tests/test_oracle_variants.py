@@ -128,6 +128,121 @@ def test_four_over_six_worked_blocks(orc):
     assert list(_fp4_codes(codes, 48)[0, :16]) == cw
 
 
+# Exact error sums with Python's rational arithmetic, from the pages' E2M1
+# alphabet ("08 - FP4, MXFP4, NVFP4", "Why 4-bit floats at all?") and torch's
+# E4M3 decoder: independent of the oracle's big-integer sums.
+_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _e4m3_value(code):
+    import torch
+    return float(torch.tensor([code], dtype=torch.uint8).view(torch.float8_e4m3fn).float()[0])
+
+
+def _decoded_f32(code, sb, S):
+    p = np.float32((-1.0 if code & 8 else 1.0) * _E2M1[code & 7] * _e4m3_value(sb))  # exact
+    return np.float32(p * np.float32(S))
+
+
+def _exact_err(v, codes, sb, S):
+    from fractions import Fraction as Fr
+    return sum((Fr(float(v[j])) - Fr(float(_decoded_f32(int(codes[j]), sb, S)))) ** 2 for j in range(16))
+
+
+def _f32_round(q):
+    """Correctly rounded (nearest, ties to even) FP32 value of a rational q."""
+    from fractions import Fraction as Fr
+    if q == 0:
+        return np.float32(0.0)
+    sgn, q = (-1 if q < 0 else 1), abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    while Fr(2) ** e > q:
+        e -= 1
+    while Fr(2) ** (e + 1) <= q:
+        e += 1
+    ulp = Fr(2) ** (max(e, -126) - 23)
+    m = q / ulp
+    fl = m.numerator // m.denominator
+    if m - fl > Fr(1, 2) or (m - fl == Fr(1, 2) and fl % 2):
+        fl += 1
+    return np.float32(sgn * float(fl * ulp))
+
+
+def _old_fp32_err(v, codes, sb, S):
+    """The former definition: two FP32 halves of 8 accumulated with fused
+    multiply-adds (one rounding each), then added in FP32."""
+    from fractions import Fraction as Fr
+    half = [np.float32(0.0), np.float32(0.0)]
+    for j in range(16):
+        d = np.float32(v[j] - _decoded_f32(int(codes[j]), sb, S))
+        half[j // 8] = _f32_round(Fr(float(d)) ** 2 + Fr(float(half[j // 8])))
+    return np.float32(half[0] + half[1])
+
+
+def _near_tie_blocks():
+    u, v = 2.0 ** -12, 4095 * 2.0 ** -22
+    D = [24.0] + [21.0] * 6 + [3 + u] + [21.0] * 7 + [2 + u + 2.0 ** -22]
+    E = [24.0, 21.0, 21.0, 3 + v, 0, 0, 0, 0, 21.0, 2 + v - 2.0 ** -22, 0, 0, 0, 0, 0, 0]
+    return np.array([D, E], np.float32)
+
+
+def test_four_over_six_near_ties(orc):
+    """Blocks D and E of the golden file: the exact comparison keeps 4 for D and
+    6 for E, by 2^-21; the former FP32 order decided both the other way."""
+    from fractions import Fraction as Fr
+    rows = {r[0]: (int(r[1], 16), [int(v) for v in r[2:]]) for r in _read_rows("nvfp4_four_over_six.txt")}
+    x = _near_tie_blocks()
+    codes, scales, S = orc.quantize(x, orc.NVFP4, amax=2688.0, variant=orc.V_FOUR6)
+    c0, s0, _ = orc.quantize(x, orc.NVFP4, amax=2688.0)
+    assert S == 1.0
+    c, k0 = _fp4_codes(codes, 16), _fp4_codes(c0, 16)
+    for i, name in enumerate("DE"):
+        sc, cw = rows[name]
+        assert int(scales[i, 0]) == sc and list(c[i]) == cw, name
+    # the two candidates of each block, and their exact errors
+    c4 = [6] * 7 + [1] + [6] * 7 + [1]
+    assert list(k0[0]) == [7] * 7 + [2] + [7] * 7 + [1] and list(c[0]) == c4
+    for i, (want, sign) in enumerate(((0x4C, 1), (0x48, -1))):
+        six = (int(s0[i, 0]), k0[i])
+        four = (0x4C, c4 if i == 0 else [6, 6, 6, 1, 0, 0, 0, 0, 6, 1, 0, 0, 0, 0, 0, 0])
+        d = _exact_err(x[i], six[1], six[0], 1.0) - _exact_err(x[i], four[1], four[0], 1.0)
+        assert d == sign * Fr(1, 2 ** 21)
+        assert orc.nv_sq_error_cmp(x[i], six[1], six[0], four[1], four[0], 1.0) == sign
+        old6, old4 = _old_fp32_err(x[i], six[1], six[0], 1.0), _old_fp32_err(x[i], four[1], four[0], 1.0)
+        assert (old4 < old6) == (sign < 0), "the FP32 order must decide this block the other way"
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_four_over_six_exact_comparison(orc, seed):
+    """The oracle's integer error sums against rational arithmetic, on random
+    FP32 blocks whose values span a wide range of magnitudes (subnormal to
+    2^100) and on near-tie blocks built like D and E with random perturbations."""
+    g = np.random.default_rng(seed)
+    n = 0
+    for t in range(300):
+        if t % 3 == 0:
+            v = (g.standard_normal(16) * np.exp2(g.integers(-140, 100, 16))).astype(np.float32)
+        elif t % 3 == 1:
+            v = (g.standard_normal(16) * 2.0 ** float(g.integers(-130, 120))).astype(np.float32)
+        else:
+            e, f = g.integers(1, 1 << 12, 2) * 2.0 ** -22
+            v = np.array([24.0] + [21.0] * 6 + [3 + e] + [21.0] * 7 + [2 + f], np.float32)
+            v *= np.float32(2.0 ** float(g.integers(-20, 20)))
+        S = np.float32(np.abs(v).max() / 2688.0 * float(g.choice([1.0, 1.5, 4.0])))
+        if S == 0 or not np.isfinite(S):
+            continue
+        ca = g.integers(0, 16, 16).astype(np.uint8)
+        cb = ca.copy()
+        cb[g.integers(0, 16, 3)] = g.integers(0, 16, 3)
+        sa, sbb = int(g.integers(0, 0x7F)), int(g.integers(0, 0x7F))
+        want = _exact_err(v, ca, sa, S) - _exact_err(v, cb, sbb, S)
+        got = orc.nv_sq_error_cmp(v, ca, sa, cb, sbb, float(S))
+        assert got == (want > 0) - (want < 0), (t, v, ca, sa, cb, sbb, S)
+        assert orc.nv_sq_error_cmp(v, ca, sa, ca, sa, float(S)) == 0
+        n += 1
+    assert n > 250
+
+
 def _block_sq_err(x, y):
     d = (x.astype(np.float64) - y.astype(np.float64)) ** 2
     return d.reshape(x.shape[0], -1, 16).sum(axis=2)
