@@ -379,13 +379,19 @@ __device__ inline void encode_nv(const QuantArgs& a, float S, float d, int64_t q
 // lowers the quantization error).  The block is encoded with its maximum
 // mapped to 6 (d6 = 6 S, the format's rule) and to 4 (d4 = 4 S); the one
 // whose decoded values fp32(e2m1 * e4m3 * S) have the smaller squared error
-// is kept, 6 on a tie.  The error is an FP32 sum in a fixed order: each lane
-// of the pair accumulates its 8 elements with fused multiply-adds from
-// element 0, then the pair's two partial sums are added, so the choice is a
-// reproducible function of the input.  Round-to-nearest only.
+// -- the exact sum, with no rounding -- is kept, 6 on a tie.  Round-to-nearest
+// only.
+//
+// Each lane of the pair first sums the squares of its 8 differences in FP32
+// (fused multiply-adds) and the pair adds the halves.  Each sum is then
+// within 11 * 2^-24 of the exact one (relative), plus at most 2^-120 from
+// underflow, so when the two sums differ by more than 2^-18 of their total
+// plus 2^-100, their order is the exact order.  Otherwise (and whenever a sum
+// is not finite) the pair compares the exact errors with integers
+// (nv46_exact_four), which near ties make rare.
 // The 8 codes are decoded by the hardware conversion (scale 1: exact), two
 // per instruction, byte b giving elements 2b (low nibble) and 2b + 1.
-__device__ inline float nv_sq_err(const float v[8], uint32_t w, float dsb, float S) {
+__device__ inline void nv_decode8(uint32_t w, float dsb, float S, float xh[8]) {
 #pragma clang fp contract(off)
   typedef float v2f __attribute__((ext_vector_type(2)));
   v2f q[4];
@@ -393,14 +399,56 @@ __device__ inline float nv_sq_err(const float v[8], uint32_t w, float dsb, float
   q[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
   q[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
   q[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xh[i] = (q[i >> 1][i & 1] * dsb) * S;  // first product exact
+}
+
+__device__ inline float nv_sq_err(const float v[8], uint32_t w, float dsb, float S) {
+#pragma clang fp contract(off)
+  float xh[8];
+  nv_decode8(w, dsb, S, xh);
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float xh = (q[i >> 1][i & 1] * dsb) * S;  // first product exact
-    const float d = v[i] - xh;
+    const float d = v[i] - xh[i];
     acc = __builtin_fmaf(d, d, acc);
   }
   return acc;
+}
+
+// Exact comparison: true when error(4) < error(6).  error(6) - error(4) is the
+// sum over the block of (xh4 - xh6) (2 x - xh6 - xh4), since
+// (x - a)^2 - (x - b)^2 = (b - a)(2 x - a - b); an element with xh6 == xh4
+// adds nothing.  Any other element has a nonzero code under one candidate, so
+// |x| > ab / 36 (a nonzero code needs |x| r > 1/4, and the decoded block
+// scale is at least 2/3 of its target ab / (k S), k <= 6), and its decoded
+// values lie below 3 ab.  With E = floor(log2 ab), every value involved is
+// then a multiple of u = max(2^(E - 29), 2^-149) below 2^32 u, so both
+// factors divided by u are integers below 2^34, formed exactly in FP64; their
+// product is below 2^68 and the block's sum below 2^72: exact in 128 bits.
+__device__ inline bool nv46_exact_four(const float v[8], uint32_t w6, float dsb6, uint32_t w4,
+                                       float dsb4, float S, float ab) {
+  float x6[8], x4[8];
+  nv_decode8(w6, dsb6, S, x6);
+  nv_decode8(w4, dsb4, S, x4);
+  const int eb = (int)((__builtin_bit_cast(uint32_t, ab) >> 23) & 0xFFu);
+  const int eu = eb == 0 ? -149 : (eb - 127 - 29 > -149 ? eb - 127 - 29 : -149);
+  __int128 sum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double a = (double)x4[i] - (double)x6[i];
+    const double b = (2.0 * (double)v[i] - (double)x6[i]) - (double)x4[i];
+    const int64_t ia = (int64_t)__builtin_ldexp(a, -eu);
+    const int64_t ib = (int64_t)__builtin_ldexp(b, -eu);
+    sum += (__int128)ia * (__int128)ib;
+  }
+  // add the other lane's sum (addition commutes: both lanes get the same)
+  const unsigned __int128 us = (unsigned __int128)sum;
+  const uint32_t p0 = dpp_xor1((uint32_t)us), p1 = dpp_xor1((uint32_t)(us >> 32)),
+                 p2 = dpp_xor1((uint32_t)(us >> 64)), p3 = dpp_xor1((uint32_t)(us >> 96));
+  const unsigned __int128 other = ((unsigned __int128)p3 << 96) | ((unsigned __int128)p2 << 64) |
+                                  ((unsigned __int128)p1 << 32) | (unsigned __int128)p0;
+  return (__int128)(us + other) > 0;
 }
 
 __device__ inline void encode_nv46(float S, float d6, float d4, const float v[8],
@@ -411,12 +459,13 @@ __device__ inline void encode_nv46(float S, float d6, float d4, const float v[8]
   m = o > m ? o : m;
   const float ab = u2f(m);
   uint32_t sb[2], w[2];
-  float err[2];
+  float err[2], dsbk[2];
   const float d[2] = {d6, d4};
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     sb[k] = e4m3_rne_mag(ab / d[k]);
     const float dsb = e4m3_mag_value(sb[k]);
+    dsbk[k] = dsb;
     float rcp = 0.0f;
     if (dsb != 0.0f) {
       const float p = dsb * S;
@@ -429,7 +478,11 @@ __device__ inline void encode_nv46(float S, float d6, float d4, const float v[8]
     const float part = nv_sq_err(v, w[k], dsb, S);
     err[k] = part + dpp_xor1f(part);  // addition commutes: both lanes get the same sum
   }
-  const bool four = err[1] < err[0];
+  bool four = err[1] < err[0];
+  // both lanes of the pair hold the same sums, so they take this branch together
+  const float gap = __builtin_fabsf(err[0] - err[1]);
+  if (!(gap > (err[0] + err[1]) * 0x1p-18f + 0x1p-100f))
+    four = nv46_exact_four(v, w[0], dsbk[0], w[1], dsbk[1], S, ab);
   e.w[0] = four ? w[1] : w[0];
   e.sc = four ? sb[1] : sb[0];
 }

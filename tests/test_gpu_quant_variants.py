@@ -128,10 +128,61 @@ def test_four_over_six_worked_blocks_and_given_amax():
     _same(s, ws, "scales")
     _same(c, wc, "codes")
     assert s[0, 0] == 0x58 and s[0, 1] == 0x58 and s[0, 2] == 0x40
+    # the golden file's near-tie blocks D and E (decided by 2^-21)
+    u, v = 2.0**-12, 4095 * 2.0**-22
+    y = np.array([[24.0] + [21.0] * 6 + [3 + u] + [21.0] * 7 + [2 + u + 2.0**-22],
+                  [24.0, 21.0, 21.0, 3 + v, 0, 0, 0, 0, 21.0, 2 + v - 2.0**-22, 0, 0, 0, 0, 0, 0]],
+                 np.float32)
+    out, _ = _quant(to_gpu_f32(y), 3, flags=mx.MX_FLAG_FOUR_OVER_SIX, amax_value=2688.0)
+    c, s, _ = host(out)
+    assert s[0, 0] == 0x4C and s[1, 0] == 0x48
+    wc, ws, _ = oracle.quantize(y, 3, amax=2688.0, variant=oracle.V_FOUR6)
+    _same(s, ws, "near-tie scales")
+    _same(c, wc, "near-tie codes")
     z = torch.zeros(16, 64, dtype=torch.bfloat16, device=dev())
     out, _ = _quant(z, 3, flags=mx.MX_FLAG_FOUR_OVER_SIX)
     c, s, ts = host(out)
     assert float(ts[0]) == 1.0 and not c.any() and not s.any()
+
+
+def _near_tie_tensor(rows, seed):
+    """Blocks whose two candidate errors differ by about 2^-21 of a total near
+    100 (built like the golden file's blocks D and E: 24, 21s, 3 + e and 2 + f
+    with f - e in -2..2 steps of 2^-22), so that the FP32 sums cannot order
+    them and the exact comparison decides; rows scaled by 2^0 .. 2^-6 and
+    negated at random, elements shuffled within their halves."""
+    g = np.random.default_rng(seed)
+    x = np.zeros((rows, 64), np.float32)
+    for r in range(rows):
+        for b in range(4):
+            e = int(g.integers(1, 1 << 12))
+            f = e + int(g.integers(-2, 3))
+            n0, n1 = int(g.integers(0, 7)), int(g.integers(0, 8))
+            h0 = [24.0] + [21.0] * n0 + [3 + e * 2.0**-22]
+            h1 = [21.0] * n1 + [2 + f * 2.0**-22]
+            h0 = np.array(h0 + [0.0] * (8 - len(h0)))
+            h1 = np.array(h1 + [0.0] * (8 - len(h1)))
+            blk = np.concatenate([g.permutation(h0), g.permutation(h1)])
+            if g.random() < 0.3:
+                blk = -blk
+            x[r, 16 * b:16 * b + 16] = blk * 2.0 ** -int(g.integers(0, 7))
+    return x
+
+
+def test_four_over_six_near_ties():
+    """Near-tie blocks, where the exact comparison (not the FP32 sums) decides:
+    bit-exact against the oracle's exact sums, with the tensor scale given
+    (S = 1) and computed."""
+    x = _near_tie_tensor(512, 11)
+    for amax in (2688.0, None):
+        out, _ = _quant(to_gpu_f32(x), 3, flags=mx.MX_FLAG_FOUR_OVER_SIX, amax_value=amax)
+        c, s, ts = host(out)
+        wc, ws, wts = oracle.quantize(x, 3, amax=amax, variant=oracle.V_FOUR6)
+        assert float(ts[0]) == wts
+        _same(s, ws, "scales")
+        _same(c, wc, "codes")
+        if amax is not None:  # both choices occur (6 * 2^-j has mantissa bits 100, 4 * 2^-j 000)
+            assert 0.2 < float(np.mean((ws & 7) == 4)) < 0.8
 
 
 # --- 2-D blocks ----------------------------------------------------------------
