@@ -31,6 +31,18 @@ __device__ inline void tile_of(uint32_t id, uint32_t tm, uint32_t tn, uint32_t* 
   *n = in / gsize;
 }
 
+// Nonzero when some byte of w lies outside [lo, hi], for 1 <= lo <= 128 and
+// 127 <= hi <= 254: a byte below lo borrows into its bit 7 when lo is
+// subtracted from every byte while its own bit 7 is clear (exact as a test of
+// the whole word), and a byte above hi is one whose complement is below
+// 255 - hi.
+__device__ inline uint32_t bytes_outside(uint32_t w, uint32_t lo, uint32_t hi) {
+  const uint32_t below = (w - lo * 0x01010101u) & ~w & 0x80808080u;
+  const uint32_t nw = ~w;
+  const uint32_t above = (nw - (255u - hi) * 0x01010101u) & ~nw & 0x80808080u;
+  return below | above;
+}
+
 // Epilogue through LDS: each wave writes its 128x128 accumulator tile into
 // LDS in 64-row halves and stores it back row-contiguous, 16 bytes per lane.
 template <int CDT>

@@ -25,6 +25,8 @@
 // Workgroup: 256 threads (2 x 2 waves), 128 x 128 C tile, K step 64,
 // double-buffered BF16 tiles in LDS, two workgroups per CU.
 #include "../device/codec.h"
+#include "../device/gemm_common.h"
+#include "../device/lowscale.h"
 #include "../launch.h"
 
 namespace mxk {
@@ -114,10 +116,12 @@ __device__ __attribute__((always_inline)) inline void decode_store_hw(const Unit
   }
 }
 
-// Decode a unit to 32 BF16 values and store them as 64 contiguous bytes.
+// Decode a unit to 32 BF16 values and store them as 64 contiguous bytes;
+// shift: added to the scale code (not to 255, NaN) by the fix-up mode.
 template <int FMT>
-__device__ __attribute__((always_inline)) inline void decode_store(const Unit& u, uint8_t* dst) {
-  const uint32_t c = u.s & 0xFFu;
+__device__ __attribute__((always_inline)) inline void decode_store(const Unit& u, uint8_t* dst, int shift) {
+  const uint32_t c0 = u.s & 0xFFu;
+  const uint32_t c = c0 == 0xFFu ? c0 : (uint32_t)((int)c0 + shift);
   if constexpr (FMT != FMT_MXINT8) {
     if (c >= 17u && c <= 239u) {
       decode_store_hw<FMT>(u, u2f(c << 23), dst);
@@ -137,15 +141,25 @@ __device__ __attribute__((always_inline)) inline void decode_store(const Unit& u
     *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
 }
 
-__device__ __attribute__((always_inline)) inline void decode_store_any(int fmt, const Unit& u, uint8_t* dst) {
+__device__ __attribute__((always_inline)) inline void decode_store_any(int fmt, const Unit& u, uint8_t* dst,
+                                                                     int shift) {
   switch (fmt) {
-    case FMT_MXFP8: decode_store<FMT_MXFP8>(u, dst); break;
-    case FMT_MXFP4: decode_store<FMT_MXFP4>(u, dst); break;
-    case FMT_MXINT8: decode_store<FMT_MXINT8>(u, dst); break;
-    case FMT_MXFP8_E5M2: decode_store<FMT_MXFP8_E5M2>(u, dst); break;
-    case FMT_MXFP6_E3M2: decode_store<FMT_MXFP6_E3M2>(u, dst); break;
-    default: decode_store<FMT_MXFP6_E2M3>(u, dst); break;
+    case FMT_MXFP8: decode_store<FMT_MXFP8>(u, dst, shift); break;
+    case FMT_MXFP4: decode_store<FMT_MXFP4>(u, dst, shift); break;
+    case FMT_MXINT8: decode_store<FMT_MXINT8>(u, dst, shift); break;
+    case FMT_MXFP8_E5M2: decode_store<FMT_MXFP8_E5M2>(u, dst, shift); break;
+    case FMT_MXFP6_E3M2: decode_store<FMT_MXFP6_E3M2>(u, dst, shift); break;
+    default: decode_store<FMT_MXFP6_E2M3>(u, dst, shift); break;
   }
+}
+
+// Element grids (values are multiples of 2^-g) and magnitudes (below 2^top).
+__device__ inline int fmt_grid(int fmt) {
+  return fmt == FMT_MXFP8 ? 9 : fmt == FMT_MXFP8_E5M2 ? 16 : fmt == FMT_MXINT8 ? 6 : fmt == FMT_MXFP6_E3M2 ? 4
+         : fmt == FMT_MXFP6_E2M3 ? 3 : 1;
+}
+__device__ inline int fmt_top(int fmt) {
+  return fmt == FMT_MXFP8 ? 9 : fmt == FMT_MXFP8_E5M2 ? 16 : fmt == FMT_MXINT8 ? 1 : fmt == FMT_MXFP6_E3M2 ? 5 : 3;
 }
 
 // Load the unit of K elements k0 .. k0+31 of a row (codes at `row`, scales
@@ -173,29 +187,24 @@ __device__ __attribute__((always_inline)) inline void load_unit(int bits, const 
 
 // Thread t stages, per step, the units t + 256 j: row (t + 256 j) / 2 of the
 // stacked [A tile; B tile] rows, K half t % 2 -- j < U/2 are A rows.
-// nonzero when some byte of w is 0x00 or 0xFF
-__device__ inline uint32_t special_code_bytes(uint32_t w) {
-  const uint32_t z = (w - 0x01010101u) & ~w & 0x80808080u;
-  const uint32_t nw = ~w;
-  return z | ((nw - 0x01010101u) & ~nw & 0x80808080u);
-}
-
-// fixup: the workgroup first scans the scale rows of its tile and computes
-// the tile only if one holds code 0 or 255 (K % 512 == 0: 16-byte scale
-// loads) -- the fix-up pass behind a kernel that does not take those codes.
+// fix_lo > 0: the workgroup first scans the scale rows of its tile and
+// computes the tile only if one holds a code outside [fix_lo, fix_hi]
+// (K % 512 == 0: 16-byte scale loads) -- the fix-up pass behind a kernel that
+// is exact only for codes in that range.
 template <int CDT, int T>
 __global__ __launch_bounds__(256) void k_gemm_mx_any(int fa, int fb, const uint8_t* __restrict__ A,
                                                      const uint8_t* __restrict__ SA,
                                                      const uint8_t* __restrict__ B,
                                                      const uint8_t* __restrict__ SB, int64_t M, int64_t N,
                                                      int64_t K, void* __restrict__ C, int64_t ldc,
-                                                     uint32_t tiles_n, int fixup) {
+                                                     uint32_t tiles_n, uint32_t fix_lo, uint32_t fix_hi) {
   constexpr int U = 2 * T * 2 / 256;  // units per thread and step (2 or 4)
   constexpr int F = T / 64;           // 32 x 32 instruction tiles per wave and dimension
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * T * kPitch];
   const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * T, n0 = (int64_t)(blockIdx.x % tiles_n) * T;
   const uint32_t t = threadIdx.x, lane = t & 63u, wid = t >> 6;
-  if (fixup) {
+  int shift_a = 0, shift_b = 0;  // the fix-up mode's code shifts
+  if (fix_lo > 0) {
     __shared__ uint32_t found;
     if (t == 0) found = 0u;
     __syncthreads();
@@ -209,15 +218,31 @@ __global__ __launch_bounds__(256) void k_gemm_mx_any(int fa, int fb, const uint8
     uint32_t sp = 0u;
     for (int64_t q = 16 * (int64_t)t; q < na; q += 16 * 256) {
       const uint4 v = *reinterpret_cast<const uint4*>(pa + q);
-      sp |= special_code_bytes(v.x) | special_code_bytes(v.y) | special_code_bytes(v.z) | special_code_bytes(v.w);
+      sp |= bytes_outside(v.x, fix_lo, fix_hi) | bytes_outside(v.y, fix_lo, fix_hi) |
+            bytes_outside(v.z, fix_lo, fix_hi) | bytes_outside(v.w, fix_lo, fix_hi);
     }
     for (int64_t q = 16 * (int64_t)t; q < nb; q += 16 * 256) {
       const uint4 v = *reinterpret_cast<const uint4*>(pb + q);
-      sp |= special_code_bytes(v.x) | special_code_bytes(v.y) | special_code_bytes(v.z) | special_code_bytes(v.w);
+      sp |= bytes_outside(v.x, fix_lo, fix_hi) | bytes_outside(v.y, fix_lo, fix_hi) |
+            bytes_outside(v.z, fix_lo, fix_hi) | bytes_outside(v.w, fix_lo, fix_hi);
     }
     if (sp) atomicOr(&found, 1u);
     __syncthreads();
     if (found == 0u) return;  // uniform
+    // The tile is recomputed.  Its codes are shifted, A's by shift_a and B's
+    // by shift_b, into the range the hardware conversions take exactly (17 ..
+    // 239; INT8's software decode 7 .. 254) when one shift per operand fits
+    // them all there with every product on FP32's 2^-149 grid and no sum
+    // beyond 2^127; the result is scaled back with one rounding.  Else the
+    // codes are decoded as they are.
+    __shared__ uint32_t red[16];
+    int mna, mxa, mnb, mxb;
+    ls_tile_ranges(pa, na / 16, pb, nb / 16, red, &mna, &mxa, &mnb, &mxb);
+    const int la = fa == FMT_MXINT8 ? 7 : 17, ha = fa == FMT_MXINT8 ? 254 : 239;
+    const int lb = fb == FMT_MXINT8 ? 7 : 17, hb = fb == FMT_MXINT8 ? 254 : 239;
+    if (!ls_shift(mna, mxa, mnb, mxb, la, ha, lb, hb, fmt_grid(fa), fmt_grid(fb), fmt_top(fa), fmt_top(fb), K,
+                  &shift_a, &shift_b))
+      shift_a = shift_b = 0;
   }
   const uint32_t wm = wid >> 1, wn = wid & 1u;
   const int ba = code_bits(fa), bb = code_bits(fb);
@@ -253,7 +278,8 @@ __global__ __launch_bounds__(256) void k_gemm_mx_any(int fa, int fb, const uint8
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < U; ++j) decode_store_any(j < U / 2 ? fa : fb, un[j], &lds[buf][dst[j]]);
+    for (int j = 0; j < U; ++j)
+      decode_store_any(j < U / 2 ? fa : fb, un[j], &lds[buf][dst[j]], j < U / 2 ? shift_a : shift_b);
   };
 
   v16f acc[F][F];
@@ -300,8 +326,9 @@ __global__ __launch_bounds__(256) void k_gemm_mx_any(int fa, int fb, const uint8
       for (int v = 0; v < 16; ++v) {
         const int64_t row = m0 + wm * (T / 2) + i * 32 + 8 * (v / 4) + 4 * lg + (v % 4);
         if (row < M && col < N) {
-          if constexpr (CDT == DT_F32) static_cast<float*>(C)[row * ldc + col] = acc[i][j][v];
-          else static_cast<uint16_t*>(C)[row * ldc + col] = f32_to_bf16(acc[i][j][v]);
+          const float val = __builtin_amdgcn_ldexpf(acc[i][j][v], -(shift_a + shift_b));  // exact at shift 0
+          if constexpr (CDT == DT_F32) static_cast<float*>(C)[row * ldc + col] = val;
+          else static_cast<uint16_t*>(C)[row * ldc + col] = f32_to_bf16(val);
         }
       }
     }
@@ -311,9 +338,10 @@ __global__ __launch_bounds__(256) void k_gemm_mx_any(int fa, int fb, const uint8
 
 hipError_t launch_gemm_mx_any(int fa, const uint8_t* a_codes, const uint8_t* a_scales, int fb,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
-                              int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s, bool fixup) {
+                              int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s, uint32_t fix_lo,
+                              uint32_t fix_hi) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (fixup && K % 512 != 0) return hipErrorInvalidValue;
+  if (fix_lo > 0 && (K % 512 != 0 || fix_lo > 128 || fix_hi < 127 || fix_hi > 254)) return hipErrorInvalidValue;
   // 128 x 128 tiles, two workgroups per CU: with 256 x 256 tiles the six
   // inlined decoders of four units per thread spill registers
   constexpr int64_t T = 128;
@@ -321,7 +349,7 @@ hipError_t launch_gemm_mx_any(int fa, const uint8_t* a_codes, const uint8_t* a_s
   if ((uint64_t)tm * tn > 0x7FFFFFFFull) return hipErrorInvalidValue;
 #define MXK_ANY(D, TT)                                                                                    \
   hipLaunchKernelGGL((k_gemm_mx_any<D, TT>), dim3(tm * tn), dim3(256), 0, s, fa, fb, a_codes, a_scales, b_codes, \
-                     b_scales, M, N, K, C, ldc, tn, fixup ? 1 : 0)
+                     b_scales, M, N, K, C, ldc, tn, fix_lo, fix_hi)
   if (cdt == DT_F32) MXK_ANY(DT_F32, 128);
   else MXK_ANY(DT_BF16, 128);
 #undef MXK_ANY

@@ -408,13 +408,14 @@ hipError_t launch_gemm_mx_f6(int fa, const uint8_t* a_codes, const uint8_t* a_sc
   if (M == 0 || N == 0) return hipSuccess;
   const int ta = f6_type(fa), tb = f6_type(fb);
   if (ta == kE3M2 && tb == kE3M2) {
-    // decoded to BF16 (see mfma_slice), then the tiles whose operands hold
-    // scale code 0 or 255 recomputed by the generic kernel's fix-up mode
+    // decoded to BF16 (see mfma_slice), exact for scale codes 5 .. 250; then
+    // the tiles whose operands hold another code recomputed by the generic
+    // kernel's fix-up mode
     const hipError_t e = cdt == DT_F32
                              ? launch_f6<kE3M2, kE3M2, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s)
                              : launch_f6<kE3M2, kE3M2, DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
     if (e != hipSuccess) return e;
-    return launch_gemm_mx_any(fa, a_codes, a_scales, fb, b_codes, b_scales, M, N, K, C, cdt, ldc, s, true);
+    return launch_gemm_mx_any(fa, a_codes, a_scales, fb, b_codes, b_scales, M, N, K, C, cdt, ldc, s, 5u, 250u);
   }
 #define MXK_F6(A_, B_)                                                                                   \
   if (ta == A_ && tb == B_)                                                                              \

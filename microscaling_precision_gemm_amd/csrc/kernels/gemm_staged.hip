@@ -30,6 +30,8 @@
 // with an upper bound of ceil(R/BM) + groups m tiles and surplus workgroups
 // exit.
 #include "../device/codec.h"
+#include "../device/gemm_common.h"
+#include "../device/lowscale.h"
 #include "../launch.h"
 
 namespace mxk {
@@ -56,8 +58,10 @@ struct Unit {
 // F: the element type of MXFP8 units -- FMT_MXFP8 (E4M3), FMT_MXFP8_E5M2 or
 // FMT_MXINT8 (two's complement times 2^-6, decoded in software: the exact
 // FP32 product k * 2^(c-133), truncated to BF16).
+// bias: added to an MXFP8 unit's scale code (not to 255, NaN) -- the fix-up
+// pass's shift of a tile's codes into the exact range (see k_gemm_staged).
 template <int SRC, int F = FMT_MXFP8>
-__device__ inline void convert_store(const Unit<SRC>& u, uint8_t* dst) {
+__device__ inline void convert_store(const Unit<SRC>& u, uint8_t* dst, int bias = 0) {
   constexpr bool BF8 = F == FMT_MXFP8_E5M2;
   uint32_t out[16];
   if constexpr (SRC == FMT_NVFP4) {
@@ -79,20 +83,23 @@ __device__ inline void convert_store(const Unit<SRC>& u, uint8_t* dst) {
       }
     }
   } else if constexpr (F == FMT_MXINT8) {
-    const uint32_t c = u.s & 0xFFu;
+    const uint32_t c0 = u.s & 0xFFu;
+    const uint32_t c = c0 == 0xFFu ? c0 : (uint32_t)((int)c0 + bias);
     // 2^(c-127): c = 0 is the FP32 subnormal 2^-127, 0xFF is NaN
     const float X = c == 0xFFu ? __builtin_nanf("") : (c == 0u ? u2f(0x00400000u) : u2f(c << 23));
 #pragma unroll
     for (int wd = 0; wd < 8; ++wd) {
-      const float v0 = (float)(int8_t)(u.w[wd] & 0xFFu) * X * 0.015625f;
-      const float v1 = (float)(int8_t)((u.w[wd] >> 8) & 0xFFu) * X * 0.015625f;
-      const float v2 = (float)(int8_t)((u.w[wd] >> 16) & 0xFFu) * X * 0.015625f;
-      const float v3 = (float)(int8_t)(u.w[wd] >> 24) * X * 0.015625f;
+      // k 2^-6 first (exact), then the scale: k X alone overflows at code 254
+      const float v0 = (float)(int8_t)(u.w[wd] & 0xFFu) * 0.015625f * X;
+      const float v1 = (float)(int8_t)((u.w[wd] >> 8) & 0xFFu) * 0.015625f * X;
+      const float v2 = (float)(int8_t)((u.w[wd] >> 16) & 0xFFu) * 0.015625f * X;
+      const float v3 = (float)(int8_t)(u.w[wd] >> 24) * 0.015625f * X;
       out[2 * wd] = (f2u(v0) >> 16) | (f2u(v1) & 0xFFFF0000u);
       out[2 * wd + 1] = (f2u(v2) >> 16) | (f2u(v3) & 0xFFFF0000u);
     }
   } else {
-    const uint32_t c = u.s & 0xFFu;
+    const uint32_t c0 = u.s & 0xFFu;
+    const uint32_t c = c0 == 0xFFu ? c0 : (uint32_t)((int)c0 + bias);
     if (c >= 1u && c != 0xFFu) {
       const float X = u2f(c << 23);  // 2^(c-127), a normal FP32
 #pragma unroll
@@ -125,18 +132,27 @@ __device__ inline void convert_store(const Unit<SRC>& u, uint8_t* dst) {
     *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
 }
 
-// nonzero when some byte of w is 0x00 or 0xFF
-__device__ inline uint32_t special_bytes(uint32_t w) {
-  const uint32_t z = (w - 0x01010101u) & ~w & 0x80808080u;
-  const uint32_t nw = ~w;
-  return z | ((nw - 0x01010101u) & ~nw & 0x80808080u);
-}
+// Scale codes for which the pipelined exact 8-bit kernel converts every
+// element exactly to BF16 (the scaled value is a BF16 value): E4M3 3..246,
+// E5M2 17..239, INT8 7..254.
+template <int F>
+constexpr uint32_t kExactLo = F == FMT_MXFP8_E5M2 ? 17u : F == FMT_MXINT8 ? 7u : 3u;
+template <int F>
+constexpr uint32_t kExactHi = F == FMT_MXFP8_E5M2 ? 239u : F == FMT_MXINT8 ? 254u : 246u;
+
+// Every value of element type F is an integer multiple of 2^-kGrid<F>, below
+// 2^kTop<F> in magnitude.
+template <int F>
+constexpr int kGrid = F == FMT_MXFP8_E5M2 ? 16 : F == FMT_MXINT8 ? 6 : 9;
+template <int F>
+constexpr int kTop = F == FMT_MXFP8_E5M2 ? 16 : F == FMT_MXINT8 ? 1 : 9;
 
 // FIXUP (MXFP8, K % 512 == 0): the workgroup first scans the scale rows of
-// its tile and computes the tile only if one holds a code 0 or 255 -- the
-// codes the pipelined exact MXFP8 kernel does not convert; the output of
-// that kernel for such tiles is overwritten.  BA / BB: the element types of A
-// and B for MXFP8 units (FMT_MXFP8, FMT_MXFP8_E5M2 or FMT_MXINT8).
+// its tile and computes the tile only if one holds a code outside the range
+// the pipelined exact 8-bit kernel converts exactly (kExactLo .. kExactHi of
+// the operand's element type; 255, NaN, always); the output of that kernel
+// for such tiles is overwritten.  BA / BB: the element types of A and B for
+// MXFP8 units (FMT_MXFP8, FMT_MXFP8_E5M2 or FMT_MXINT8).
 template <int SRC, int CDT, int BM, int BN, bool GATHER, bool FIXUP = false, int BA = FMT_MXFP8,
           int BB = FMT_MXFP8>
 __global__ __launch_bounds__(256) void k_gemm_staged(
@@ -182,6 +198,7 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
   if (g < 0) return;  // surplus workgroup (uniform across the block)
 
   const uint32_t t = threadIdx.x;
+  int bias_a = 0, bias_b = 0;  // the fix-up pass's code shifts
   if constexpr (FIXUP) {
     static_assert(SRC == FMT_MXFP8 && BM == 256 && BN == 256, "fix-up pass of the exact MXFP8 GEMM");
     __shared__ uint32_t found[4];
@@ -199,18 +216,33 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int64_t q = q0 + 256 * u;
-        v[u] = q < ca ? pa[q] : u4{1u, 1u, 1u, 1u};
-        v[8 + u] = q < cb ? pb[q] : u4{1u, 1u, 1u, 1u};
+        // past the run: code 127 (2^0) in every byte, which is not special
+        v[u] = q < ca ? pa[q] : u4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+        v[8 + u] = q < cb ? pb[q] : u4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
       }
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
+      for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sp |= special_bytes(v[u][e]);
+        for (int e = 0; e < 4; ++e)
+          sp |= bytes_outside(v[u][e], kExactLo<BA>, kExactHi<BA>) |
+                bytes_outside(v[8 + u][e], kExactLo<BB>, kExactHi<BB>);
     }
     const bool wave_found = __builtin_amdgcn_ballot_w64(sp != 0u) != 0;
     if ((t & 63u) == 0) found[t >> 6] = wave_found ? 1u : 0u;
     __syncthreads();
     if ((found[0] | found[1] | found[2] | found[3]) == 0u) return;  // uniform
+    // The tile is recomputed.  Its codes are shifted, A's by bias_a and B's by
+    // bias_b, into the exact range when one shift per operand fits them all
+    // there with every product on FP32's 2^-149 grid and no sum beyond 2^127;
+    // the result is scaled back with one rounding.  Else (codes spanning more
+    // than the range) they are decoded as they are.
+    __shared__ uint32_t red[16];
+    int mna, mxa, mnb, mxb;
+    ls_tile_ranges(reinterpret_cast<const uint8_t*>(pa), ca, reinterpret_cast<const uint8_t*>(pb), cb, red, &mna,
+                   &mxa, &mnb, &mxb);
+    if (!ls_shift(mna, mxa, mnb, mxb, (int)kExactLo<BA>, (int)kExactHi<BA>, (int)kExactLo<BB>, (int)kExactHi<BB>,
+                  kGrid<BA>, kGrid<BB>, kTop<BA>, kTop<BB>, K, &bias_a, &bias_b))
+      bias_a = bias_b = 0;
   }
   const uint32_t lane = t & 63u, wid = t >> 6;
   const uint32_t wm = wid >> 1, wn = wid & 1u;
@@ -287,8 +319,8 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
   auto store_step = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < kUnits; ++j) {
-      if (j < BM / 128) convert_store<SRC, BA>(reg[j], &lds[buf][dst_off[j]]);  // A rows
-      else convert_store<SRC, BB>(reg[j], &lds[buf][dst_off[j]]);
+      if (j < BM / 128) convert_store<SRC, BA>(reg[j], &lds[buf][dst_off[j]], bias_a);  // A rows
+      else convert_store<SRC, BB>(reg[j], &lds[buf][dst_off[j]], bias_b);
     }
   };
 
@@ -330,6 +362,7 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
 
   float sab = 1.0f;
   if constexpr (SRC == FMT_NVFP4) sab = *a_ts * b_ts[g];
+  const int unshift = -(bias_a + bias_b);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -339,7 +372,8 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
       for (int v = 0; v < 16; ++v) {
         const int64_t row = m0 + wm * (BM / 2) + i * 32 + 8 * (v / 4) + 4 * lg + (v % 4);
         if (row < g_hi && col < N) {
-          const float val = SRC == FMT_NVFP4 ? acc[i][j][v] * sab : acc[i][j][v];
+          const float val = SRC == FMT_NVFP4 ? acc[i][j][v] * sab
+                                             : (FIXUP ? __builtin_amdgcn_ldexpf(acc[i][j][v], unshift) : acc[i][j][v]);
           if constexpr (CDT == DT_F32) static_cast<float*>(C)[row * ldc + col] = val;
           else static_cast<uint16_t*>(C)[row * ldc + col] = f32_to_bf16(val);
         }

@@ -28,6 +28,7 @@
 
 #include "../device/codec.h"
 #include "../device/gemm_common.h"
+#include "../device/lowscale.h"
 #include "../device/mxenc.h"
 #include "../device/wave.h"
 #include "../launch.h"
@@ -112,33 +113,51 @@ __device__ inline uint64_t uniform_u64(uint64_t v) {
 
 // Steps S .. kStepsPerGroup-1 of group g: after slice q's instructions, slice
 // q of the next step (clamped to the last step, a harmless reload) is loaded
-// into the same registers.
-template <int FMT, int S, int Q, int TA, int TB>
+// into the same registers.  CHECK: between the group's first instructions and
+// the reload of their fragment registers (free registers there), every scale
+// code of the group is tested against the quick bound of tiled_wave, and
+// lanes that fail set their bit in `low` (wave-uniform, scalar registers).
+template <int FMT, int S, int Q, int TA, int TB, bool CHECK>
 __device__ inline void run_group(const gptr (&base)[8], uint32_t g, uint32_t steps,
                                  uint32_t lane16, TSlice<FMT> (&fr)[TCfg<FMT>::kSlices],
-                                 const u4 (&sc)[8], v16f (&acc)[4][4]) {
+                                 const u4 (&sc)[8], v16f (&acc)[4][4], uint64_t& low) {
   constexpr int SPG = TCfg<FMT>::kStepsPerGroup, KS = TCfg<FMT>::kSlices;
   if constexpr (S < SPG) {
     if constexpr (Q < KS) {
       const uint32_t st = g * SPG + S;
       const uint32_t nst = st + 1 < steps ? st + 1 : st;
       mfma_slice_t<FMT, S, Q, TA, TB>(fr[Q], sc, acc);
+      if constexpr (CHECK && S == 0 && Q == 0) {
+        // bit 7 of every byte stays set while every code is at least 64
+        // (bit 6 or 7 set), or 96 (bit 7, or bits 6 and 5)
+        uint32_t ok = 0x80808080u;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t w = sc[t][d];
+            ok &= ls_threshold(TA, TB) <= 128 ? (w << 1) | w : w | ((w << 1) & (w << 2));
+          }
+        low |= __builtin_amdgcn_ballot_w64((ok & 0x80808080u) != 0x80808080u);
+      }
       load_slice_t<FMT>(base, nst, Q, lane16, fr[Q]);
       sched_fence();
-      run_group<FMT, S, Q + 1, TA, TB>(base, g, steps, lane16, fr, sc, acc);
+      run_group<FMT, S, Q + 1, TA, TB, CHECK>(base, g, steps, lane16, fr, sc, acc, low);
     } else {
-      run_group<FMT, S + 1, 0, TA, TB>(base, g, steps, lane16, fr, sc, acc);
+      run_group<FMT, S + 1, 0, TA, TB, CHECK>(base, g, steps, lane16, fr, sc, acc, low);
     }
   }
 }
 
 // The main loop: the accumulators of this wave's 128x128 part of the C tile
-// at (m0, n0).
-template <int FMT, int TA = kDefaultType<FMT>, int TB = kDefaultType<FMT>>
+// at (m0, n0).  `low` gets the bits of lanes that saw a scale code below the
+// quick bound of tiled_wave.
+template <int FMT, int TA, int TB>
 __device__ inline void tiled_mainloop(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
                                       const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB,
                                       int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
-                                      uint32_t wm, uint32_t wn, uint32_t lane, v16f (&acc)[4][4]) {
+                                      uint32_t wm, uint32_t wn, uint32_t lane, v16f (&acc)[4][4],
+                                      uint64_t& low) {
   using TC = TCfg<FMT>;
   const uint32_t steps = (uint32_t)((FMT == FMT_MXFP8 ? K : K / 2) / 128);  // code tiles per row tile
   const uint32_t groups = (uint32_t)(K / 1024);
@@ -181,13 +200,139 @@ __device__ inline void tiled_mainloop(const uint8_t* __restrict__ A, const uint8
 #pragma unroll
     for (int t = 0; t < 8; ++t) scn[t] = *reinterpret_cast<gptr4>(sb[t] + (uint32_t)(ng * 1024u + lane16));
     sched_fence();
-    run_group<FMT, 0, 0, TA, TB>(cb, g, steps, lane16, fr, sc, acc);
+    run_group<FMT, 0, 0, TA, TB, true>(cb, g, steps, lane16, fr, sc, acc, low);
 #pragma unroll
     for (int t = 0; t < 8; ++t) sc[t] = scn[t];
   }
 
   // the clamped reloads of the last step are still in flight: let them land
   __builtin_amdgcn_s_waitcnt((0 & 15) | (0 << 14) | (7 << 4) | (15 << 8));  // vmcnt(0)
+}
+
+// Smallest and largest scale codes over the row tiles this wave reads (A:
+// its 4 row tiles of the tile at m0, B: its 4 at n0; clamped at M and N as in
+// the main loop), read again from memory: only waves whose quick test fails
+// come here.  A scale row tile (32 rows) is K / 1024 tiles of 1 KB,
+// contiguous.
+__device__ inline void wave_scale_range(const uint8_t* __restrict__ SA, const uint8_t* __restrict__ SB, int64_t M,
+                                        int64_t N, int64_t K, int64_t m0, int64_t n0, uint32_t wm, uint32_t wn,
+                                        uint32_t lane, uint32_t* min_a, uint32_t* max_a, uint32_t* min_b,
+                                        uint32_t* max_b) {
+  uint32_t r[4] = {0x00FF00FFu, 0u, 0x00FF00FFu, 0u};  // min A, max A, min B, max B
+  for (int t = 0; t < 8; ++t) {
+    int64_t rt = t < 4 ? m0 / 32 + wm * 4 + t : n0 / 32 + wn * 4 + (t - 4);
+    const int64_t last = (t < 4 ? M : N) / 32 - 1;
+    rt = rt < last ? rt : last;
+    const uint8_t* p = (t < 4 ? SA : SB) + rt * K;
+    const int o = t < 4 ? 0 : 2;
+    for (int64_t q = 16 * (int64_t)lane; q < K; q += 16 * 64) {
+      const u4 v = *reinterpret_cast<const u4*>(p + q);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        r[o] = ls_min_bytes(r[o], v[d]);
+        r[o + 1] = ls_max_bytes(r[o + 1], v[d]);
+      }
+    }
+  }
+  uint32_t f[4] = {ls_fold_min(r[0]), ls_fold_max(r[1]), ls_fold_min(r[2]), ls_fold_max(r[3])};
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = lane_read(f[i], lane ^ (uint32_t)off);
+      f[i] = (i & 1) ? (o > f[i] ? o : f[i]) : (o < f[i] ? o : f[i]);
+    }
+  *min_a = (uint32_t)__builtin_amdgcn_readfirstlane(f[0]);
+  *max_a = (uint32_t)__builtin_amdgcn_readfirstlane(f[1]);
+  *min_b = (uint32_t)__builtin_amdgcn_readfirstlane(f[2]);
+  *max_b = (uint32_t)__builtin_amdgcn_readfirstlane(f[3]);
+}
+
+// The wave's 128x128 accumulators computed again with every A scale code
+// raised by bias_a and every B code by bias_b (no code reaches 255), then
+// scaled back by 2^-(bias_a + bias_b) with one rounding each.  A plain loop,
+// one 32x32 instruction tile at a time (it reloads fragments, and only waves
+// that need it run it), so that it adds few registers to the kernel.
+template <int FMT, int TA, int TB>
+__device__ inline void tiled_recompute_raised(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
+                                              const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB,
+                                              int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
+                                              uint32_t wm, uint32_t wn, uint32_t lane, uint32_t bias_a,
+                                              uint32_t bias_b, v16f (&acc)[4][4]) {
+  using TC = TCfg<FMT>;
+  const int64_t steps = (FMT == FMT_MXFP8 ? K : K / 2) / 128;
+  const uint32_t lane16 = lane * 16u;
+  const int sh = -(int)(bias_a + bias_b);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // unrolled: acc stays in registers
+      int64_t ra = m0 / 32 + wm * 4 + i, rb = n0 / 32 + wn * 4 + j;
+      ra = ra < M / 32 - 1 ? ra : M / 32 - 1;
+      rb = rb < N / 32 - 1 ? rb : N / 32 - 1;
+      const uint8_t* ca = A + ra * steps * 4096 + lane16;
+      const uint8_t* cb = B + rb * steps * 4096 + lane16;
+      const uint8_t* sa = SA + ra * K + lane16;  // K / 1024 scale tiles of 1 KB per row tile
+      const uint8_t* sb = SB + rb * K + lane16;
+      v16f c;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) c[v] = 0.0f;
+      for (int64_t st = 0; st < steps; ++st) {
+        const int64_t g = st / TC::kStepsPerGroup;
+        const uint32_t S = (uint32_t)(st % TC::kStepsPerGroup);
+        const u4 wa = *reinterpret_cast<const u4*>(sa + g * 1024);
+        const u4 wb = *reinterpret_cast<const u4*>(sb + g * 1024);
+#pragma unroll
+        for (int q = 0; q < TC::kSlices; ++q) {
+          // the scale byte of slice q of step S (see mfma_slice_t), raised
+          const uint32_t byte = (FMT == FMT_MXFP8 ? 2 * S : 4 * S) + (uint32_t)q;
+          const uint32_t xa = ((wa[byte >> 2] >> (8 * (byte & 3))) & 0xFFu) + bias_a;
+          const uint32_t xb = ((wb[byte >> 2] >> (8 * (byte & 3))) & 0xFFu) + bias_b;
+          const uint8_t* pa = ca + st * 4096 + q * TC::kParts * 1024;
+          const uint8_t* pb = cb + st * 4096 + q * TC::kParts * 1024;
+          if constexpr (FMT == FMT_MXFP8)
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                widen(*reinterpret_cast<const u4*>(pa), *reinterpret_cast<const u4*>(pa + 1024)),
+                widen(*reinterpret_cast<const u4*>(pb), *reinterpret_cast<const u4*>(pb + 1024)), c, TA, TB, 0,
+                (int)xa, 0, (int)xb);
+          else
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen4(*reinterpret_cast<const u4*>(pa)),
+                                                                 widen4(*reinterpret_cast<const u4*>(pb)), c, TA,
+                                                                 TB, 0, (int)xa, 0, (int)xb);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_amdgcn_ldexpf(c[v], sh);
+    }
+}
+
+// One wave's part of a tile with the exactness check of lowscale.h: the
+// main loop, then -- when the smallest scale codes of the wave's A rows and B
+// rows could pair below the threshold of the element types -- the
+// accumulators again with raised codes, scaled back, then the epilogue
+// `epi(acc)`.  The loop tests every code against a quick bound in two
+// instructions per scale dword: at least 64 (96 for pairs whose threshold
+// exceeds 128) on both sides settles it, as the sum of the two smallest codes
+// then reaches the threshold.  A wave that saw a smaller code (all-zero blocks
+// have code 0) reads its exact code ranges.  Waves decide alone: the loop,
+// the check and the epilogue are wave-local.
+template <int FMT, int TA, int TB, class Epi>
+__device__ inline void tiled_wave(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
+                                  const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB, int64_t M,
+                                  int64_t N, int64_t K, int64_t m0, int64_t n0, uint32_t wm, uint32_t wn,
+                                  uint32_t lane, Epi epi) {
+  constexpr int kThr = ls_threshold(TA, TB);
+  static_assert(kThr <= 192, "threshold above 192");
+  v16f acc[4][4];
+  uint64_t low = 0;
+  tiled_mainloop<FMT, TA, TB>(A, SA, B, SB, M, N, K, m0, n0, wm, wn, lane, acc, low);
+  if (low != 0) {  // wave-uniform, rare
+    uint32_t a, b, max_a, max_b, ba, bb;
+    wave_scale_range(SA, SB, M, N, K, m0, n0, wm, wn, lane, &a, &max_a, &b, &max_b);
+    if ((int)(a + b) < kThr && ls_bias(TA, TB, K, a, max_a, b, max_b, &ba, &bb))
+      tiled_recompute_raised<FMT, TA, TB>(A, SA, B, SB, M, N, K, m0, n0, wm, wn, lane, ba, bb, acc);
+  }
+  epi(acc);
 }
 
 template <int FMT, int CDT, int TA = kDefaultType<FMT>, int TB = kDefaultType<FMT>>
@@ -202,9 +347,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t wm = wid >> 1, wn = wid & 1u;
-  v16f acc[4][4];
-  tiled_mainloop<FMT, TA, TB>(A, SA, B, SB, M, N, K, m0, n0, wm, wn, lane, acc);
-  store_tile<CDT>(smem, acc, C, ldc, M, N, m0 + wm * 128, n0 + wn * 128, vec != 0, wid, lane);
+  tiled_wave<FMT, TA, TB>(A, SA, B, SB, M, N, K, m0, n0, wm, wn, lane, [=](const v16f(&acc)[4][4]) {
+    store_tile<CDT>(smem, acc, C, ldc, M, N, m0 + wm * 128, n0 + wn * 128, vec != 0, wid, lane);
+  });
 }
 
 // ---- GEMM with its output quantized (fused quantize-and-GEMM) --------------
@@ -319,10 +464,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t wm = wid >> 1, wn = wid & 1u;
-  v16f acc[4][4];
-  tiled_mainloop<FMT>(A, SA, B, SB, M, N, K, m0, n0, wm, wn, lane, acc);
-  store_tile_quant<OFMT, SR, OTILED>(smem, acc, codes, scales, M, N, m0 + wm * 128, n0 + wn * 128, wid,
-                                     lane, enc);
+  tiled_wave<FMT, kDefaultType<FMT>, kDefaultType<FMT>>(
+      A, SA, B, SB, M, N, K, m0, n0, wm, wn, lane, [=](const v16f(&acc)[4][4]) {
+        store_tile_quant<OFMT, SR, OTILED>(smem, acc, codes, scales, M, N, m0 + wm * 128, n0 + wn * 128, wid,
+                                           lane, enc);
+      });
 }
 
 // Raise a kernel's dynamic LDS limit once per device, so later launches (also

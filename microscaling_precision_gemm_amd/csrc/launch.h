@@ -70,6 +70,10 @@ hipError_t launch_dequantize(int fmt, const uint8_t* codes, const uint8_t* scale
                              const float* tensor_scale, int64_t rows, int64_t cols, void* y,
                              int ydt, int64_t ld_y, bool rht, uint32_t sign_mask, bool tiled,
                              hipStream_t s);
+// Round-trip error statistics of y (FP32) against x (stats.hip): stats[0..3]
+// = sum (y-x)^2, sum x^2, sum (y-x), max |y-x| (device doubles, overwritten).
+hipError_t launch_error_stats(const void* x, int xdt, int64_t ld_x, const float* y, int64_t ld_y, int64_t rows,
+                              int64_t cols, double* stats, hipStream_t s);
 hipError_t launch_hadamard16(const void* x, int xdt, void* y, int ydt, int64_t rows, int64_t cols,
                              uint32_t sign_mask, bool inverse, hipStream_t s);
 hipError_t launch_requant_transpose(const uint8_t* src_codes, const uint8_t* src_scales,
@@ -86,11 +90,13 @@ hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scal
 // A and B in the tiled layout (M, N multiples of 32, K of 1024)
 // C = A * B^T for any pair of MX formats (E8M0 scales; row layout), exact
 // BF16 staging (gemm_any.hip).
-// fixup: only the 128 x 128 tiles whose operand rows hold scale code 0 or
-// 255 are computed (K % 512 == 0), the others are left as they are.
+// fix_lo > 0: fix-up mode -- only the 128 x 128 tiles whose operand rows hold
+// a scale code outside [fix_lo, fix_hi] are computed (K % 512 == 0), the
+// others are left as they are.
 hipError_t launch_gemm_mx_any(int fa, const uint8_t* a_codes, const uint8_t* a_scales, int fb,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
-                              int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s, bool fixup = false);
+                              int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s, uint32_t fix_lo = 0,
+                              uint32_t fix_hi = 254);
 // MX pairs with an FP6 operand (E2M3/E3M2 against E2M3/E3M2/E2M1, not E3M2 x
 // E3M2) on the scaled FP6/FP4 instruction (gemm_f6.hip); shapes it takes.
 bool gemm_mx_f6_fits(int fa, int fb, int64_t M, int64_t N, int64_t K);

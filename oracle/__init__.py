@@ -354,6 +354,36 @@ def bf16_interval(C: np.ndarray, tol: np.ndarray):
     return lo, hi
 
 
+def roundtrip_stats(x: np.ndarray, y: np.ndarray):
+    """Round-trip error statistics of a decoded tensor y against its source x
+    ("Microscaling (MX) and block-scaled 4-bit formats", section "NVFP4" and
+    glossary "stochastic rounding": what the Hadamard transform and stochastic
+    rounding buy).  x: bf16 bits (uint16) or float32; y: float32 or float64,
+    same shape.  Returns (sum (y-x)^2, sum x^2, sum (y-x), max |y-x|), every
+    term formed and summed in FP64."""
+    xv = bf16_bits_to_f64(x) if x.dtype == np.uint16 else np.asarray(x, np.float64)
+    d = np.asarray(y, np.float64) - xv
+    return float(np.sum(d * d)), float(np.sum(xv * xv)), float(np.sum(d)), float(np.max(np.abs(d)))
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f32_interval(C: np.ndarray, tol: np.ndarray):
+    """FP32-output acceptance interval [fp32_rne(C - tol), fp32_rne(C + tol)]
+    as float64 arrays: the FP32 values that are the rounding of some value
+    within the bound.  Where C +- tol are FP32 values this is the bound
+    itself; it differs only where the bound is narrower than FP32's spacing
+    (results in or below FP32's subnormal range)."""
+    C = np.asarray(C, np.float64)
+    tol = np.asarray(tol, np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        lo = (C - tol).astype(np.float32).astype(np.float64)
+        hi = (C + tol).astype(np.float32).astype(np.float64)
+    return lo, hi
+
+
 def _round_bf16_f64(v: np.ndarray) -> np.ndarray:
     """Round FP64 values to the nearest bf16 (ties to even), returned as FP64.
 

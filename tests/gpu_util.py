@@ -63,18 +63,25 @@ def upload(fmt, codes: np.ndarray, scales: np.ndarray, ts=None) -> mx.MXTensor:
 
 
 def check_gemm(C: np.ndarray, Chat: np.ndarray, tol: np.ndarray, bf16_out: bool, what=""):
-    """FP32 output: |C - Chat| <= tol.  BF16 output: C in
-    [bf16_rne(Chat - tol), bf16_rne(Chat + tol)]."""
+    """C must be the output format's rounding of a value within the bound:
+    FP32 output: C in [fp32_rne(Chat - tol), fp32_rne(Chat + tol)] (the plain
+    |C - Chat| <= tol wherever Chat +- tol are FP32 values); BF16 output: C in
+    [bf16_rne(Chat - tol), bf16_rne(Chat + tol)].  Where the oracle's value is
+    NaN (a NaN scale code), C must be NaN, and nowhere else."""
     C = C.astype(np.float64)
+    Chat = np.asarray(Chat, np.float64)
+    nan_want = np.isnan(Chat)
     if bf16_out:
-        lo, hi = oracle.bf16_interval(Chat, tol)
-        bad = ~((C >= lo) & (C <= hi))
+        lo, hi = oracle.bf16_interval(np.where(nan_want, 0.0, Chat), np.where(nan_want, 0.0, tol))
     else:
-        bad = ~(np.abs(C - Chat) <= tol)
+        lo, hi = oracle.f32_interval(np.where(nan_want, 0.0, Chat), np.where(nan_want, 0.0, tol))
+    inside = (C >= lo) & (C <= hi)
+    bad = np.where(nan_want, ~np.isnan(C), ~inside)
     if bad.any():
         idx = np.argwhere(bad)[:5]
         msg = "; ".join(f"{tuple(i)}: got {C[tuple(i)]!r} want {Chat[tuple(i)]!r} tol {tol[tuple(i)]!r}"
                         for i in idx)
-        ratio = np.max(np.abs(C - Chat) / np.maximum(tol / 1e-5, 1e-300))
+        ok = ~nan_want & ~np.isnan(C)
+        ratio = np.max(np.abs(C - Chat)[ok] / np.maximum(tol[ok] / 1e-5, 1e-300)) if ok.any() else float("nan")
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance "
                              f"(max |err|/sum|ab| = {ratio:.3g}); {msg}")

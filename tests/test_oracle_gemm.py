@@ -89,3 +89,18 @@ def test_bf16_interval_rounding(orc):
     x = np.random.default_rng(22).standard_normal(10000).astype(np.float32)
     ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(orc._round_bf16_f64(x.astype(np.float64)), ref)
+
+
+def test_f32_interval(orc):
+    """The FP32 acceptance interval is the plain bound where C +- tol are FP32
+    values, and the FP32 rounding of C when the bound is narrower than FP32's
+    spacing (subnormal results, results below 2^-149)."""
+    C = np.array([1.0, -3.5, 2.0**-140, 2.0**-140 + 2.0**-170, 2.0**-200, -(2.0**-151) * 3])
+    tol = np.array([2.0**-10, 2.0**-8, 2.0**-157, 2.0**-187, 2.0**-217, 2.0**-170])
+    lo, hi = orc.f32_interval(C, tol)
+    assert lo[0] == 1.0 - 2.0**-10 and hi[0] == 1.0 + 2.0**-10
+    assert lo[1] == -3.5 - 2.0**-8 and hi[1] == -3.5 + 2.0**-8
+    assert lo[2] == hi[2] == 2.0**-140
+    assert lo[3] == hi[3] == 2.0**-140
+    assert lo[4] == hi[4] == 0.0
+    assert lo[5] == hi[5] == -(2.0**-149)  # three quarters of a spacing rounds to one spacing
