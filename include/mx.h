@@ -259,6 +259,22 @@ mx_status mx_amax(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_
 mx_status mx_dequantize(const mx_tensor* in, void* y, int32_t ydt, int64_t ld_y, uint32_t flags,
                         uint16_t rht_sign_mask, mx_stream stream);
 
+/* Round-trip error statistics of a decoded tensor y against its source x
+ * (measurement support for the decode row; [MXF] "NVFP4": random Hadamard
+ * transforms bound block outliers and stochastic rounding keeps gradients
+ * unbiased; glossary "stochastic rounding": the expected value is
+ * preserved).  x: [rows, cols] BF16 or FP32 (xdt), row pitch ld_x; y:
+ * [rows, cols] FP32, row pitch ld_y (e.g. mx_dequantize's output).  Writes
+ * four FP64 values to stats (device, 16-byte aligned): sum (y - x)^2,
+ * sum x^2, sum (y - x), max |y - x|, each term formed in FP64; relative RMSE
+ * = sqrt(stats[0] / stats[1]), mean error (bias) = stats[2] / (rows * cols).
+ * The sums are accumulated with atomics, so their last bits may differ from
+ * call to call.  cols % 8 == 0; 16-byte aligned rows.  The stats buffer is
+ * cleared by a kernel on the stream first (no memset).  Errors:
+ * MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT, MX_ERR_HIP. */
+mx_status mx_error_stats(const void* x, int32_t xdt, int64_t ld_x, const float* y, int64_t ld_y, int64_t rows,
+                         int64_t cols, double* stats, mx_stream stream);
+
 /* Backward-pass requantization ([INK] "A precision choice for each stage":
  * dequantize saved values, transpose at higher precision, stochastically
  * re-quantize to MXFP8).  Source [rows, cols]: either an NVFP4 tensor `src`

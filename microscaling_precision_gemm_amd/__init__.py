@@ -32,7 +32,7 @@ FORMATS = {"mxfp8": MX_MXFP8_E4M3, "mxfp4": MX_MXFP4_E2M1, "nvfp4": MX_NVFP4, "m
 EXPORTED = [
     "mx_codes_bytes", "mx_scales_bytes", "mx_rht_signs", "mx_quantize", "mx_amax",
     "mx_dequantize", "mx_requant_transpose", "mx_hadamard16", "mx_gemm", "mx_gemm_ex",
-    "mx_gemm_grouped", "mx_gemm_quantize", "mx_quantize_batch",
+    "mx_gemm_grouped", "mx_gemm_quantize", "mx_quantize_batch", "mx_error_stats",
     "mx_status_string",
 ]
 
@@ -78,6 +78,7 @@ def load():
         "mx_rht_signs": (u16, [u64]),
         "mx_quantize": (i32, [vp, i32, i64, i64, i64, TP, i32, _Rng, u32, u16, vp, vp]),
         "mx_amax": (i32, [vp, i32, i64, i64, i64, u32, u16, vp, vp]),
+        "mx_error_stats": (i32, [vp, i32, i64, vp, i64, i64, i64, vp, vp]),
         "mx_dequantize": (i32, [TP, vp, i32, i64, u32, u16, vp]),
         "mx_requant_transpose": (i32, [TP, vp, i64, i64, i64, TP, i32, _Rng, vp]),
         "mx_hadamard16": (i32, [vp, i32, vp, i32, i64, i64, u16, i32, vp]),
@@ -230,6 +231,17 @@ def mx_dequantize(t: MXTensor, y, flags: int = 0, sign_mask: int = 0, stream=Non
     _check(L.mx_dequantize(ctypes.byref(d), _ptr(y), _dt(y), y.stride(0), flags, sign_mask,
                            _stream(stream)))
     return y
+
+
+def mx_error_stats(x, y, stats, stream=None):
+    """Round-trip error statistics of the FP32 tensor y against x (bf16 or
+    fp32, same shape) into `stats` (4 float64 on the device): sum (y-x)^2,
+    sum x^2, sum (y-x), max |y-x|."""
+    L = load()
+    rows, cols = x.shape
+    _check(L.mx_error_stats(_ptr(x), _dt(x), x.stride(0), _ptr(y), y.stride(0), rows, cols, _ptr(stats),
+                            _stream(stream)))
+    return stats
 
 
 def mx_requant_transpose(out: MXTensor, src: MXTensor | None = None, x_bf16=None,

@@ -25,6 +25,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "gemm_nvpipe.hip"),
     os.path.join(CSRC, "kernels", "gemm_any.hip"),
     os.path.join(CSRC, "kernels", "gemm_f6.hip"),
+    os.path.join(CSRC, "kernels", "stats.hip"),
 ]
 
 # -ffp-contract=off: the quantizers' FP32 scale arithmetic must round once per

@@ -269,6 +269,19 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
+mx_status mx_error_stats(const void* x, int32_t xdt, int64_t ld_x, const float* y, int64_t ld_y, int64_t rows,
+                         int64_t cols, double* stats, mx_stream stream) {
+  if (!stats) return MX_ERR_NULL;
+  if (!aligned16(stats)) return MX_ERR_ALIGN;
+  mx_status st = check_matrix(x, xdt, rows, cols, ld_x);
+  if (st != MX_OK) return st;
+  st = check_matrix(y, MX_F32, rows, cols, ld_y);
+  if (st != MX_OK) return st;
+  if (cols % 8) return MX_ERR_SHAPE;
+  return hip_status(mxk::launch_error_stats(x, xdt, ld_x, y, ld_y, rows, cols, stats,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,
                      uint32_t flags, mx_stream stream) {
   if (!A || !B) return MX_ERR_NULL;

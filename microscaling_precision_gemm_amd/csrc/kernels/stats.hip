@@ -1,0 +1,117 @@
+// stats.hip -- round-trip error statistics of a decoded tensor against its
+// source ("Microscaling (MX) and block-scaled 4-bit formats", section "NVFP4":
+// random Hadamard transforms bound block outliers, stochastic rounding keeps
+// gradients unbiased; glossary "stochastic rounding": the expected value is
+// preserved).  For x (BF16 or FP32) and its decoded y (FP32), both
+// [rows, cols], the kernel accumulates in FP64
+//   s[0] = sum (y - x)^2,  s[1] = sum x^2,  s[2] = sum (y - x),
+//   s[3] = max |y - x|
+// from which relative RMSE sqrt(s0 / s1), the mean error (bias) s2 / n and the
+// largest error follow.  Memory-bound: one read of x and y.
+//
+// A lane takes 8 consecutive elements of a row per chunk (grid-stride over
+// chunks); partial sums go through a wave reduction and LDS to one FP64
+// atomic add (and one 64-bit atomic max: non-negative doubles order as their
+// bit patterns) per workgroup.  The differences are formed in FP64 from the
+// FP32 values.
+#include "../device/codec.h"
+#include "../launch.h"
+
+namespace mxk {
+
+namespace {
+
+constexpr int kStatThreads = 256;
+
+__global__ void k_stats_clear(double* s) {
+  if (threadIdx.x < 4) s[threadIdx.x] = 0.0;
+}
+
+template <int XDT>
+__global__ __launch_bounds__(kStatThreads) void k_error_stats(const void* __restrict__ x, int64_t ld_x,
+                                                              const float* __restrict__ y, int64_t ld_y,
+                                                              int64_t cols, int64_t Q, double* __restrict__ s) {
+  const int64_t cpr = cols >> 3;
+  double e2 = 0.0, x2 = 0.0, e1 = 0.0, mx = 0.0;
+  for (int64_t q = (int64_t)blockIdx.x * kStatThreads + threadIdx.x; q < Q;
+       q += (int64_t)gridDim.x * kStatThreads) {
+    const int64_t r = q / cpr, c = (q - r * cpr) * 8;
+    float xv[8], yv[8];
+    if constexpr (XDT == DT_BF16) {
+      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + r * ld_x + c);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xv[2 * i] = u2f(ww[i] << 16);
+        xv[2 * i + 1] = u2f(ww[i] & 0xFFFF0000u);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + r * ld_x + c);
+      const float4 a = p[0], b = p[1];
+      xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+      xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+    }
+    const float4* py = reinterpret_cast<const float4*>(y + r * ld_y + c);
+    const float4 a = py[0], b = py[1];
+    yv[0] = a.x; yv[1] = a.y; yv[2] = a.z; yv[3] = a.w;
+    yv[4] = b.x; yv[5] = b.y; yv[6] = b.z; yv[7] = b.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double xd = xv[i], d = (double)yv[i] - xd;
+      e2 += d * d;
+      x2 += xd * xd;
+      e1 += d;
+      const double ad = __builtin_fabs(d);
+      mx = ad > mx ? ad : mx;
+    }
+  }
+  // wave, then workgroup
+  for (int off = 32; off >= 1; off >>= 1) {
+    e2 += __shfl_xor(e2, off);
+    x2 += __shfl_xor(x2, off);
+    e1 += __shfl_xor(e1, off);
+    const double o = __shfl_xor(mx, off);
+    mx = o > mx ? o : mx;
+  }
+  __shared__ double red[kStatThreads / 64][4];
+  const uint32_t wid = threadIdx.x >> 6;
+  if ((threadIdx.x & 63u) == 0) {
+    red[wid][0] = e2;
+    red[wid][1] = x2;
+    red[wid][2] = e1;
+    red[wid][3] = mx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kStatThreads / 64; ++w) {
+      e2 += red[w][0];
+      x2 += red[w][1];
+      e1 += red[w][2];
+      mx = red[w][3] > mx ? red[w][3] : mx;
+    }
+    atomicAdd(&s[0], e2);
+    atomicAdd(&s[1], x2);
+    atomicAdd(&s[2], e1);
+    atomicMax(reinterpret_cast<unsigned long long*>(&s[3]), (unsigned long long)__double_as_longlong(mx));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_error_stats(const void* x, int xdt, int64_t ld_x, const float* y, int64_t ld_y, int64_t rows,
+                              int64_t cols, double* stats, hipStream_t s) {
+  // cleared by a kernel, not a memset: the call stays capturable in a graph
+  hipLaunchKernelGGL(k_stats_clear, dim3(1), dim3(64), 0, s, stats);
+  const int64_t Q = rows * (cols / 8);
+  if (Q > 0) {
+    const int64_t want = (Q + kStatThreads - 1) / kStatThreads;
+    const int g = (int)(want < 2048 ? want : 2048);
+    if (xdt == DT_BF16)
+      hipLaunchKernelGGL(k_error_stats<DT_BF16>, dim3(g), dim3(kStatThreads), 0, s, x, ld_x, y, ld_y, cols, Q, stats);
+    else
+      hipLaunchKernelGGL(k_error_stats<DT_F32>, dim3(g), dim3(kStatThreads), 0, s, x, ld_x, y, ld_y, cols, Q, stats);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mxk

@@ -159,6 +159,11 @@ def test_other_entry_point_checks(mx):
     assert L.mx_amax(FAKE, 0, 4, 64, 64, 4, 0, FAKE, None) == 5
     assert L.mx_dequantize(ctypes.byref(a8), FAKE, 0, 32, 0, 0, None) == 2
     assert L.mx_dequantize(None, FAKE, 0, 64, 0, 0, None) == 1
+    # error stats: missing output, cols % 8, pitch, unaligned output
+    assert L.mx_error_stats(FAKE, 0, 64, FAKE, 64, 4, 64, None, None) == 1
+    assert L.mx_error_stats(FAKE, 0, 64, FAKE, 64, 4, 60, FAKE, None) == 2
+    assert L.mx_error_stats(FAKE, 0, 32, FAKE, 64, 4, 64, FAKE, None) == 2
+    assert L.mx_error_stats(FAKE, 0, 64, FAKE, 64, 4, 64, ctypes.c_void_p(FAKE + 8), None) == 3
 
 
 def test_binding_fails_loudly_without_library(mx, monkeypatch):

@@ -293,3 +293,40 @@ def test_requant_transpose_bf16_source(orc):
     codes, scales = orc.requant_transpose(64, 32, orc.SR, seed=1, counter=3, bf16=dY)
     want = orc.quantize(np.ascontiguousarray(dY.T), orc.MXFP8, orc.SR, seed=1, counter=3)
     assert np.array_equal(codes, want[0]) and np.array_equal(scales, want[1])
+
+
+# --- round-trip error statistics ---------------------------------------------
+def test_roundtrip_stats_closed_forms(orc):
+    """Closed forms: y = x gives zeros; y = x + c gives n c^2, n c, |c|;
+    sum x^2 is the plain sum of squares."""
+    g = np.random.default_rng(3)
+    x = g.standard_normal((16, 64)).astype(np.float32)
+    s = orc.roundtrip_stats(x, x.copy())
+    assert s[0] == 0.0 and s[2] == 0.0 and s[3] == 0.0
+    assert abs(s[1] - float(np.sum(x.astype(np.float64) ** 2))) <= 1e-12 * s[1]
+    c = 0.125
+    s = orc.roundtrip_stats(x, x.astype(np.float64) + c)
+    assert abs(s[0] - x.size * c * c) <= 1e-9 and abs(s[2] - x.size * c) <= 1e-9 and s[3] == c
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)  # bf16 inputs by truncation
+    s = orc.roundtrip_stats(bits, orc.bf16_bits_to_f64(bits))
+    assert s[0] == 0.0 and s[3] == 0.0
+
+
+def test_roundtrip_stats_of_sr_are_unbiased(orc):
+    """The page's claim for stochastic rounding: over many seeds, the mean
+    decoded error of an NVFP4 round trip goes to zero (within 5 standard
+    errors plus the rule's bias bound), while round-to-nearest keeps one
+    fixed error.  The tensor is a single row of one repeated block."""
+    base = np.array([0.3, -1.7, 2.2, 5.1, -0.45, 0.9, 3.3, -2.6, 1.1, -0.2, 4.4, 0.05, -3.9, 2.7, -1.05, 0.6],
+                     np.float32)
+    x = np.tile(base, (1, 64))
+    means = []
+    for seed in range(200):
+        c, sc, S = orc.quantize(x, orc.NVFP4, orc.SR, seed=seed, amax=6.0 * 448.0 * 0.01)
+        y = orc.dequantize(orc.NVFP4, c, sc, S, 1, x.shape[1])
+        means.append(orc.roundtrip_stats(x, y)[2] / x.size)
+    m, se = float(np.mean(means)), float(np.std(means)) / np.sqrt(len(means))
+    assert abs(m) <= 5 * se + 2.0**-16 * 2.0
+    c, sc, S = orc.quantize(x, orc.NVFP4, amax=6.0 * 448.0 * 0.01)
+    y = orc.dequantize(orc.NVFP4, c, sc, S, 1, x.shape[1])
+    assert abs(orc.roundtrip_stats(x, y)[2] / x.size) > 10 * se
