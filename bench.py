@@ -175,7 +175,28 @@ def headline(torch, mx, W, args):
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
 
-    # kernel timing: every launch between its own pair of events
+    # kernel timing: back-to-back launches of one kernel between two events
+    # (per launch: the interval / count, launch gaps included, so a little
+    # above the kernel's own duration); and every launch between its own pair
+    # of events (which stalls the queue between launches and lets the clock
+    # drop on some boxes: reported beside it, not used)
+    nb = max(args.steps, 20)
+
+    def batch_ms(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(nb):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / nb
+
+    gemm_ms = batch_ms(lambda i=0: mx.mx_gemm(qa, qb, C))
+    quant_ms = batch_ms(lambda i=0: batches[i % nrot].run()) / 2  # per operand: one launch quantizes both
     tq, tg = Timer(torch), Timer(torch)
     for i in range(args.steps):
         s = tq.start()
@@ -186,8 +207,6 @@ def headline(torch, mx, W, args):
         tg.stop(s)
     torch.cuda.synchronize()
     flops = 2.0 * M * N * K
-    gemm_ms = tg.mean_ms()
-    quant_ms = tq.mean_ms() / 2  # per operand: one launch quantizes both
     # algorithmic bytes of one MXFP4 quantize of a 4096x4096 BF16 operand:
     # read 2 B/elem, write 0.5 B codes + 1/32 B scales
     qbytes = M * K * (2 + 0.5 + 1 / 32)
@@ -196,6 +215,8 @@ def headline(torch, mx, W, args):
         "ms_per_step": ms_step,
         "value": flops / (ms_step * 1e-3) / 1e12,
         "gemm_ms": gemm_ms,
+        "gemm_ms_bracketed": tg.mean_ms(),
+        "quant_ms_bracketed": tq.mean_ms() / 2,
         "gemm_tflops": gemm_tflops,
         "quant_ms": quant_ms,
         "quant_gbs": qbytes / (quant_ms * 1e-3) / 1e9,
@@ -215,27 +236,74 @@ def cpu_baseline(W, oracle, A_bits, B_bits, rows: int, min_seconds: float = 10.0
     in the step's unit (TFLOP/s of 2*M*N*K-equivalent work) over the sampled
     fraction of the output."""
     oracle.lib()
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = oracle.get_threads()
     M, K = A_bits.shape
     N = B_bits.shape[0]
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        qa = oracle.quantize(np.ascontiguousarray(A_bits[:rows]), oracle.MXFP4)
-        qb = oracle.quantize(B_bits, oracle.MXFP4)
-        Ad = oracle.dequantize_f64(oracle.MXFP4, qa[0], qa[1], rows, K)
-        Bd = oracle.dequantize_f64(oracle.MXFP4, qb[0], qb[1], N, K)
-        oracle.gemm(Ad, Bd)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    sample_flops = 2.0 * rows * N * K * reps
-    return {"value": sample_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": dt,
+
+    def run(r, nb, secs):
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            qa = oracle.quantize(np.ascontiguousarray(A_bits[:r]), oracle.MXFP4)
+            qb = oracle.quantize(np.ascontiguousarray(B_bits[:nb]), oracle.MXFP4)
+            Ad = oracle.dequantize_f64(oracle.MXFP4, qa[0], qa[1], r, K)
+            Bd = oracle.dequantize_f64(oracle.MXFP4, qb[0], qb[1], nb, K)
+            oracle.gemm(Ad, Bd)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= secs:
+                return reps, dt
+
+    reps, dt = run(rows, N, min_seconds)
+    # the same on one thread, on a sixteenth of the output (rows / 16 x N / ... )
+    oracle.set_threads(1)
+    r1 = max(rows // 16, 1)
+    reps1, dt1 = run(r1, N, min_seconds / 2)
+    oracle.set_threads(threads)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": 2.0 * rows * N * K * reps / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": dt, "cpu_model": cpu, "cpus_visible": os.cpu_count(),
+            "one_thread_value": 2.0 * r1 * N * K * reps1 / dt1 / 1e12, "one_thread_seconds": dt1,
             "sample": f"{reps} repetitions of: MXFP4 quantize of {rows} rows of A and all {N} rows "
                       f"of B, then {rows} of the {M} output rows of the FP64 GEMM (K={K}); "
-                      f"throughput = {reps}*2*{rows}*{N}*{K} / time"}
+                      f"throughput = {reps}*2*{rows}*{N}*{K} / time; one thread: {reps1} repetitions "
+                      f"with {r1} rows of A"}
+
+
+def device_facts(torch):
+    """The box's own figures: compute units and clock from the device
+    properties (peaks derived from them: dense FP4/FP6 16384, FP8 8192, BF16
+    4096 flop per clock and CU), and a device-to-device copy of 1 GiB as the
+    practical HBM ceiling (read + write bytes / time)."""
+    p = torch.cuda.get_device_properties(0)
+    cus = int(p.multi_processor_count)
+    clk = None
+    try:
+        from ctypes import CDLL, byref, c_int
+        hip = CDLL("libamdhip64.so")
+        v = c_int(0)
+        if hip.hipDeviceGetAttribute(byref(v), 5, 0) == 0:  # hipDeviceAttributeClockRate (kHz)
+            clk = v.value / 1e6
+    except OSError:
+        pass
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = time_fn(torch, lambda: dst.copy_(src), 10, 3)
+    del src, dst
+    out = {"compute_units": cus, "max_clock_ghz": clk, "copy_gbs_1gib": 2 * (1 << 30) / ms / 1e6,
+           "copy_frac_of_8tbs": 2 * (1 << 30) / ms / 1e6 / PEAK_HBM_GBS}
+    if clk:
+        out["peak_tflops_from_clock"] = {k: cus * f * clk * 1e9 / 1e12 for k, f in
+                                         (("fp4", 16384), ("fp8", 8192), ("bf16", 4096))}
+    return out
 
 
 def detail(torch, mx, W, args):
@@ -272,6 +340,16 @@ def detail(torch, mx, W, args):
     ms = time_fn(torch, lambda: mx.mx_quantize(a, qa), it, wu)
     by = M * K * (2 + 1 + 1 / 32)
     res["mxfp8_quantize_4096x4096"] = {"ms": ms, "gbs": by / ms / 1e6, "frac_hbm": by / ms / 1e6 / PEAK_HBM_GBS}
+    # NVFP4 4096^3 (E4M3 block scales applied explicitly, FP16 instruction)
+    qna, qnb = mx.empty(3, M, K), mx.empty(3, N, K)
+    mx.mx_quantize(a, qna, amax=torch.zeros(1, device="cuda"))
+    mx.mx_quantize(b, qnb, amax=torch.zeros(1, device="cuda"))
+    ms = time_fn(torch, lambda: mx.mx_gemm(qna, qnb, C), it, wu)
+    res["nvfp4_gemm_4096"] = {"ms": ms, "tflops": 2 * M * N * K / ms / 1e9,
+                              "kernel": "k_gemm_nv_pipe (E2M1 x E4M3 to exact FP16, FP16 instruction)",
+                              "frac_fp4_peak": 2 * M * N * K / ms / 1e9 / PEAK_TFLOPS["fp4"],
+                              "frac_bf16_peak": 2 * M * N * K / ms / 1e9 / PEAK_TFLOPS["bf16"]}
+    del qna, qnb
     # MXFP4 4096^3 on row-major operands (LDS-pipelined kernel), for comparison
     q4a, q4b = mx.empty(2, M, K), mx.empty(2, N, K)
     mx.mx_quantize(a, q4a)
@@ -471,7 +549,25 @@ def detail(torch, mx, W, args):
     by2 = 8192 * 7168 * (2 * 2 + 0.5 + 1 / 16)
     res["rht_nvfp4_sr_8192x7168"] = {"ms": ms_h, "gbs_2pass": by2 / ms_h / 1e6,
                                      "frac_hbm": by2 / ms_h / 1e6 / PEAK_HBM_GBS}
-    del G, qg
+    # round-trip error statistics of the same tensor: quantize, decode (inverse
+    # transform where the forward one was used), compare -- all on the device
+    Y = torch.empty(8192, 7168, dtype=torch.float32, device="cuda")
+    st = torch.empty(4, dtype=torch.float64, device="cuda")
+    rt = {}
+    n = 8192 * 7168
+    for rnd_name, rnd in (("rne", mx.MX_RNE), ("sr", mx.MX_SR)):
+        for rht in (False, True):
+            fl_ = mx.MX_FLAG_RHT16 if rht else 0
+            mx.mx_quantize(G, qg, rnd, 0, 0, fl_, mask, ga)
+            ms_dq = time_fn(torch, lambda: mx.mx_dequantize(qg, Y, fl_, mask), it, wu)
+            ms_st = time_fn(torch, lambda: mx.mx_error_stats(G, Y, st), it, wu)
+            v = st.cpu().numpy()
+            rt[f"{rnd_name}_{'rht' if rht else 'plain'}"] = {
+                "rel_rmse": float(np.sqrt(v[0] / v[1])), "mean_err": float(v[2] / n),
+                "max_abs_err": float(v[3]), "dequant_ms": ms_dq, "stats_ms": ms_st}
+    rt["source"] = "Student-t(3) 8192x7168 BF16 (torch sampler), NVFP4 E2M1/E4M3/16 + FP32 tensor scale"
+    res["nvfp4_roundtrip_stats_8192x7168"] = rt
+    del G, qg, Y
     return res
 
 
@@ -495,6 +591,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    dev = device_facts(torch)
     h = headline(torch, mx, W, args)
     roof = {"bound": "mfma", "achieved": h["gemm_tflops"], "peak": PEAK_TFLOPS["fp4"],
             "unit": "TFLOP/s", "frac": h["gemm_tflops"] / PEAK_TFLOPS["fp4"], "traffic": gemm_traffic(),
@@ -520,6 +617,7 @@ def main():
                    "M": 4096, "N": 4096, "K": 4096, "input_rotation": 16, "launch": h["launch"],
                    "layout": "mx tile layout"},
         "roofline": roof,
+        "device": dev,
         "quantize": {"ms_per_operand": h["quant_ms"], "achieved_gbs": h["quant_gbs"],
                      "peak_gbs": PEAK_HBM_GBS, "frac": h["quant_gbs"] / PEAK_HBM_GBS,
                      "bytes_per_operand": h["qbytes"],

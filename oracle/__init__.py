@@ -93,6 +93,8 @@ def lib():
         "mxo_scales_bytes": (i64, [ci, i64, i64]),
         "mxo_tensor_bytes": (i64, [ci, i64, i64]),
         "mxo_nv_sq_error_cmp": (ci, [c_f32p, c_u8p, u32, c_u8p, u32, ctypes.c_float]),
+        "mxo_set_threads": (None, [ci]),
+        "mxo_get_threads": (ci, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -258,6 +260,15 @@ def quantize(x: np.ndarray, fmt: int, rnd: int = RNE, seed: int = 0, counter: in
     if rc:
         raise ValueError("oracle rejected the shape")
     return codes, scales, None
+
+
+def set_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP loops."""
+    lib().mxo_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().mxo_get_threads())
 
 
 def nv_sq_error_cmp(v: np.ndarray, codes_a, sb_a: int, codes_b, sb_b: int, S: float) -> int:

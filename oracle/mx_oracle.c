@@ -35,6 +35,7 @@
  * per operation, no fused multiply-add.)
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -168,6 +169,10 @@ static void ensure_tables(void) {
   build_alphabet(&g_int8, mxo_int8_decode, 256, 0, 1);
   g_ready = 1;
 }
+
+/* Thread count of the oracle's OpenMP loops (for timing it on one core). */
+void mxo_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int mxo_get_threads(void) { return omp_get_max_threads(); }
 
 int mxo_init(void) {
   ensure_tables();
