@@ -36,6 +36,17 @@ __device__ inline void pack_e4m3_rne(const float y[8], uint32_t w[2]) {
   }
 }
 
+// The same for inputs the caller has already clamped to +-448.
+__device__ inline void pack_e4m3_rne_clamped(const float y[8], uint32_t w[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    v2s p = {0, 0};
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, y[4 * h], y[4 * h + 1], 1.0f, false);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, y[4 * h + 2], y[4 * h + 3], 1.0f, true);
+    w[h] = __builtin_bit_cast(uint32_t, p);
+  }
+}
+
 // E5M2: clamped to +-57344 first, as E4M3 to +-448 (checked on the device over
 // every FP32 input up to +Inf and its negative, element and byte placement
 // included: 0 mismatches against the software encoder of codec.h).
@@ -110,6 +121,20 @@ __device__ inline uint32_t sr_seed(uint32_t r16) { return (~r16 & 0xFFFFu) << 16
 // 8 E4M3 codes by SR (r: the 8 random 16-bit values), 4 per word
 __device__ inline void pack_e4m3_sr(const float y[8], const uint32_t r[8], uint32_t w[2]) {
   MXK_SR8(__builtin_amdgcn_cvt_scalef32_sr_fp8_f32, 448.0f)
+}
+// the same for inputs the caller has already clamped to +-448
+__device__ inline void pack_e4m3_sr_clamped(const float y[8], const uint32_t r[8], uint32_t w[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float* c = y + 4 * h;
+    const uint32_t* rr = r + 4 * h;
+    int a = 0;
+    a = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(a, c[0], sr_seed(rr[0]), 1.0f, 0);
+    a = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(a, c[1], sr_seed(rr[1]), 1.0f, 1);
+    a = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(a, c[2], sr_seed(rr[2]), 1.0f, 2);
+    a = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(a, c[3], sr_seed(rr[3]), 1.0f, 3);
+    w[h] = (uint32_t)a;
+  }
 }
 // 8 E5M2 codes by SR
 __device__ inline void pack_e5m2_sr(const float y[8], const uint32_t r[8], uint32_t w[2]) {

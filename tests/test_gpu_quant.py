@@ -195,6 +195,69 @@ def test_requant_transpose_bit_exact(shape, rnd, src):
     assert np.array_equal(c, wc), f"codes differ at {np.argwhere(c != wc)[:5]}"
 
 
+@pytest.mark.parametrize("ts", [2.0 ** -120, 2.0 ** -116, 2.0 ** -100, 0.0, 1e38, float("inf"), float("nan")])
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_requant_transpose_tensor_scale_edges(ts, rnd):
+    """NVFP4 source whose tensor scale makes p * S subnormal, zero, overflow
+    or NaN, with all-zero blocks in the first 64 rows."""
+    rows, cols = 256, 192
+    bits = W.normal_bf16(rows, cols, 1.0, 7, 47)
+    nv = oracle.quantize(bits, 3, 0)
+    codes = nv[0].copy()
+    codes[:64] = 0
+    tsv = np.float32(ts)
+    out = mx.empty(1, cols, rows, device=dev())
+    mx.mx_requant_transpose(out, src=upload(3, codes, nv[1], tsv), rnd=rnd, seed=5, counter=3)
+    wc, ws = oracle.requant_transpose(rows, cols, rnd, seed=5, counter=3, nvfp4=(codes, nv[1], tsv))
+    torch.cuda.synchronize()
+    c, s, _ = host(out)
+    assert np.array_equal(s, ws), f"scales differ at {np.argwhere(s != ws)[:5]}"
+    assert np.array_equal(c, wc), f"codes differ at {np.argwhere(c != wc)[:5]}"
+
+
+@pytest.mark.parametrize("shape", [(256, 320), (224, 336)])
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_requant_transpose_every_e4m3_scale_code(shape, rnd):
+    """NVFP4 source with random FP4 codes and block scales drawn from every
+    finite E4M3 code 0..126 (subnormal scales included): the decode of each
+    scale code against the oracle's."""
+    rows, cols = shape
+    rng = np.random.default_rng(rows + cols)
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 127, size=(rows, cols // 16), dtype=np.uint8)
+    scales.flat[:127] = np.arange(127, dtype=np.uint8)
+    ts = np.float32(0.37)
+    out = mx.empty(1, cols, rows, device=dev())
+    mx.mx_requant_transpose(out, src=upload(3, codes, scales, ts), rnd=rnd, seed=2, counter=11)
+    wc, ws = oracle.requant_transpose(rows, cols, rnd, seed=2, counter=11, nvfp4=(codes, scales, ts))
+    torch.cuda.synchronize()
+    c, s, _ = host(out)
+    assert np.array_equal(s, ws), f"scales differ at {np.argwhere(s != ws)[:5]}"
+    assert np.array_equal(c, wc), f"codes differ at {np.argwhere(c != wc)[:5]}"
+
+
+def test_requant_transpose_nvfp4_several_tiles_per_workgroup():
+    """4096 x 4096 NVFP4 source: 2048 tiles of 128 x 64, several per
+    workgroup of the persistent grid; bit-exact against the oracle and
+    identical over repeated launches (no LDS race between a workgroup's
+    tiles or between its producer and consumer waves)."""
+    rows, cols = 4096, 4096
+    bits = W.normal_bf16(rows, cols, 1.0, 3, 48, outlier_entries=0.001, outlier_mult=20)
+    nv = oracle.quantize(bits, 3, 0)
+    t = upload(3, nv[0], nv[1], nv[2])
+    ref = mx.empty(1, cols, rows, device=dev())
+    mx.mx_requant_transpose(ref, src=t, rnd=1, seed=9, counter=77)
+    wc, ws = oracle.requant_transpose(rows, cols, 1, seed=9, counter=77, nvfp4=nv)
+    torch.cuda.synchronize()
+    c, s, _ = host(ref)
+    assert np.array_equal(s, ws), f"scales differ at {np.argwhere(s != ws)[:5]}"
+    assert np.array_equal(c, wc), f"codes differ at {np.argwhere(c != wc)[:5]}"
+    for _ in range(10):
+        o = mx.empty(1, cols, rows, device=dev())
+        mx.mx_requant_transpose(o, src=t, rnd=1, seed=9, counter=77)
+        assert torch.equal(o.codes, ref.codes) and torch.equal(o.scales, ref.scales)
+
+
 def test_requant_transpose_repeatable():
     """No LDS race: 20 repeated launches give identical bytes."""
     bits = W.normal_bf16(512, 1024, 1.0, 1, 46)
