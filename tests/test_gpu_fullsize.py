@@ -1,8 +1,9 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times: quantizer codes and scales bit-exact over the whole tensors;
-GEMM outputs checked on seeded samples of entries that the FP64 oracle
-computes one by one (|C - C_oracle| <= 1e-5 * sum|ab|, BF16 outputs inside
-the rounded interval)."""
+GEMM outputs checked against the FP64 oracle over the whole output where the
+oracle's full product takes seconds (256^3, 4096^3), else on seeded samples
+of entries it computes one by one (|C - C_oracle| <= 1e-5 * sum|ab|, outputs
+inside the interval of their format's rounding)."""
 import numpy as np
 import pytest
 import torch
@@ -15,6 +16,7 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     import microscaling_precision_gemm_amd as mx
     from tests.gpu_util import check_gemm, dev, host, to_gpu_bf16, upload
+    from tests.tiles import untile_codes, untile_scales
 
 
 def _sample(M, N, n, seed):
@@ -43,6 +45,66 @@ def test_cfg2_quantize_bit_exact_full(cfg2_data, fmt):
         c, s, _ = host(out)
         wc, ws, _ = oracle.quantize(x, fmt)
         assert np.array_equal(s, ws) and np.array_equal(c, wc)
+
+
+def test_cfg1_quantize_gemm_end_to_end():
+    """MXFP8 end to end at 256^3: A, B N(0,1) with 0.1% entries x100
+    quantized on the GPU (E4M3, RNE; codes and scales bit-exact), then the
+    block-scaled GEMM to FP32, every output entry against the oracle."""
+    A, B = W.cfg1(0)
+    M = N = K = 256
+    qa = mx.empty(1, M, K, device=dev())
+    qb = mx.empty(1, N, K, device=dev())
+    mx.mx_quantize(to_gpu_bf16(A), qa)
+    mx.mx_quantize(to_gpu_bf16(B), qb)
+    C = torch.empty(M, N, dtype=torch.float32, device=dev())
+    mx.mx_gemm(qa, qb, C)
+    torch.cuda.synchronize()
+    oa, ob = oracle.quantize(A, 1), oracle.quantize(B, 1)
+    for q, o in ((qa, oa), (qb, ob)):
+        c, sc, _ = host(q)
+        assert np.array_equal(sc, o[1]) and np.array_equal(c, o[0])
+    Chat, tol = oracle.gemm(oracle.dequantize_f64(1, oa[0], oa[1], M, K),
+                            oracle.dequantize_f64(1, ob[0], ob[1], N, K))
+    check_gemm(C.cpu().numpy(), Chat, tol, False, "cfg1 256^3")
+
+
+def test_cfg2_batch_quantize_and_tiled_gemm_full_output(cfg2_data):
+    """The benchmark's step at full size: both cfg2 operands quantized to
+    MXFP4 in the tile layout by one mx_quantize_batch call (codes and scales
+    bit-exact against the oracle), then the tiled GEMM, BF16 out, every one
+    of the 4096^2 outputs against the FP64 oracle."""
+    A, B = cfg2_data
+    M = N = K = 4096
+    T = mx.MX_LAYOUT_TILED
+    qa = mx.empty(2, M, K, device=dev(), layout=T)
+    qb = mx.empty(2, N, K, device=dev(), layout=T)
+    mx.mx_quantize_batch([dict(x=to_gpu_bf16(A), out=qa), dict(x=to_gpu_bf16(B), out=qb)])
+    C = torch.empty(M, N, dtype=torch.bfloat16, device=dev())
+    mx.mx_gemm(qa, qb, C)
+    torch.cuda.synchronize()
+    oa, ob = oracle.quantize(A, 2), oracle.quantize(B, 2)
+    for q, o, R in ((qa, oa, M), (qb, ob, N)):
+        c, sc, _ = host(q)
+        assert np.array_equal(untile_scales(sc, R, K // 32), o[1])
+        assert np.array_equal(untile_codes(c, R, K // 2), o[0])
+    Chat, tol = oracle.gemm(oracle.dequantize_f64(2, oa[0], oa[1], M, K),
+                            oracle.dequantize_f64(2, ob[0], ob[1], N, K))
+    check_gemm(C.float().cpu().numpy(), Chat, tol, True, "tiled MXFP4 4096^3")
+
+
+def test_cfg2_exact_mxfp8_gemm_full_output(cfg2_data):
+    """MXFP8 (E4M3) 4096^3 on the exact path, BF16 out, every output entry
+    against the FP64 oracle."""
+    A, B = cfg2_data
+    M = N = K = 4096
+    qa, qb = oracle.quantize(A, 1), oracle.quantize(B, 1)
+    C = torch.empty(M, N, dtype=torch.bfloat16, device=dev())
+    mx.mx_gemm(upload(1, *qa), upload(1, *qb), C)
+    torch.cuda.synchronize()
+    Chat, tol = oracle.gemm(oracle.dequantize_f64(1, qa[0], qa[1], M, K),
+                            oracle.dequantize_f64(1, qb[0], qb[1], N, K))
+    check_gemm(C.float().cpu().numpy(), Chat, tol, True, "exact MXFP8 4096^3")
 
 
 @pytest.mark.parametrize("fmt,flags,scale", [(2, 0, 1.0), (1, 0, 1.0), (1, 1, 100.0)])
@@ -123,7 +185,12 @@ def test_cfg5_rht_nvfp4_sr_full_bit_exact():
 
 
 def test_cfg4_requant_full_bit_exact():
-    X, dY = W.cfg4(0, tokens=16384, hidden=4096, out=1024)  # dY columns reduced for host memory
+    """Backward requant at full size, stochastic rounding: X (16384 x 4096,
+    NVFP4) and dY (16384 x 14336, BF16) re-quantized transposed on the GPU in
+    one launch each; every code and scale against the oracle.  dY's output
+    is checked in bands of 2048 output rows (source columns), each band's
+    oracle run starting its random counter where the band starts."""
+    X, dY = W.cfg4(0, tokens=16384, hidden=4096, out=14336)
     nv = oracle.quantize(X, 3)
     out = mx.empty(1, 4096, 16384, device=dev())
     mx.mx_requant_transpose(out, src=upload(3, *nv), rnd=mx.MX_SR, seed=0, counter=0)
@@ -131,10 +198,18 @@ def test_cfg4_requant_full_bit_exact():
     c, s, _ = host(out)
     wc, ws = oracle.requant_transpose(16384, 4096, oracle.SR, 0, 0, nvfp4=nv)
     assert np.array_equal(s, ws) and np.array_equal(c, wc)
-    out2 = mx.empty(1, 1024, 16384, device=dev())
-    ctr = 16384 * 4096 // 8
+    del c, s, wc, ws, out
+    rows, cols = dY.shape
+    ctr = rows * 4096 // 8
+    out2 = mx.empty(1, cols, rows, device=dev())
     mx.mx_requant_transpose(out2, x_bf16=to_gpu_bf16(dY), rnd=mx.MX_SR, seed=0, counter=ctr)
     torch.cuda.synchronize()
     c2, s2, _ = host(out2)
-    wc2, ws2 = oracle.requant_transpose(16384, 1024, oracle.SR, 0, ctr, bf16=dY)
-    assert np.array_equal(s2, ws2) and np.array_equal(c2, wc2)
+    band = 2048
+    for c0 in range(0, cols, band):
+        # output element n = oc * rows + orow draws counter + n / 8; a band
+        # starting at output row c0 starts its oracle counter c0 * rows / 8 on
+        wc2, ws2 = oracle.requant_transpose(rows, band, oracle.SR, 0, ctr + c0 * rows // 8,
+                                            bf16=np.ascontiguousarray(dY[:, c0:c0 + band]))
+        assert np.array_equal(s2[c0:c0 + band], ws2), f"scales, band {c0}"
+        assert np.array_equal(c2[c0:c0 + band], wc2), f"codes, band {c0}"
