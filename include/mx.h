@@ -304,8 +304,11 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
  * FP32-accumulated sum of the exact products of the decoded operands:
  *   MXFP4  scaled FP4 matrix instructions (E8M0 scales inside the instruction);
  *   MXFP8  E4M3 * 2^(c-127) converted to exact BF16 (exact for scale codes c
- *          in [3, 246]; codes 0 and 255 give 2^-127 and NaN), BF16 matrix
- *          instructions;
+ *          in [3, 246]), BF16 matrix instructions; a fix-up pass recomputes
+ *          every tile holding a code outside that range with each operand's
+ *          codes shifted into it by one power of two per tile (exact unless
+ *          a tile's codes span more than the range on one side); code 255
+ *          gives NaN in its rows / columns;
  *   NVFP4  e2m1 * e4m3 converted to exact FP16, FP16 matrix instructions
  *          (BF16 for shapes too small for the pipelined kernel), the FP32
  *          result multiplied by S_A * S_B.
@@ -314,21 +317,28 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
  *          exact sum of each instruction's 64 products (measured on gfx950).
  *          E3M2 x E3M2, which that instruction sums in a narrower window, is
  *          decoded to exact BF16 in the same kernel (scale codes 5 .. 250;
- *          tiles with codes 0 or 255 recomputed by the generic kernel).
+ *          tiles with other codes recomputed by the generic kernel with
+ *          shifted codes, as for MXFP8).
  *   Other pairs of 8-bit types (E4M3, E5M2, INT8: E5M2 x E4M3, INT8 x INT8,
  *          INT8 x E4M3, ...) where the MXFP8 pipeline fits (K % 512 == 0,
  *          M * N >= 2^23): as MXFP8, each element times its scale converted to BF16,
  *          exact for scale codes c in [17, 239] (E5M2) and [7, 254] (INT8);
- *          codes 0 and 255 are recomputed as for MXFP8.
+ *          tiles with other codes are recomputed as for MXFP8.
  *   Other MX pairs (8-bit types mixed with FP6 or FP4, FP6 and 8-bit pairs
  *          at other shapes): every element times its scale decoded to exact
  *          BF16 (exact while the scaled values are normal BF16 values), BF16
  *          matrix instructions.
- * The scaled matrix instructions (MXFP4, FP6 pairs, MX_GEMM_FP8_NATIVE) flush
- * partial sums and results that fall into FP32's subnormal range (measured),
- * so those paths meet their bound while every pair of blocks has scale codes
- * with c_A + c_B >= 135 (MXFP4 and FP6 pairs; native E4M3 146, E5M2 160):
- * then every nonzero partial sum is at least 2^-126.
+ * The scaled matrix instructions (MXFP4, FP6 pairs, MX_GEMM_FP8_NATIVE) form
+ * the exact sum of their scaled products and round it once into FP32,
+ * subnormals included (measured), so the bound holds while every product is
+ * a multiple of 2^-149: an element of type X is a multiple of 2^-g(X) (E2M1
+ * 1, E2M3 3, E3M2 4, E4M3 9, E5M2 16), which gives c_A + c_B >= 105 + g(A) +
+ * g(B) (MXFP4 pairs 107).  The tile-layout paths (MXFP4 and native FP8 on
+ * MX_LAYOUT_TILED operands, mx_gemm_quantize) detect tiles whose scale codes
+ * could pair below that and compute them again with raised codes, so they
+ * meet the bound for every finite code; the row-layout MXFP4 and the FP6-pair
+ * paths meet it only above the threshold.  Scale code 255 (NaN) gives NaN in
+ * exactly the output rows / columns whose blocks carry it.
  * Requirements: A->fmt == B->fmt, or both MX formats (E8M0 scales) in the
  * row layout; A->cols == B->cols == K; K % 32 == 0. */
 mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,
