@@ -231,14 +231,24 @@ __host__ __device__ inline uint16_t f32_to_bf16(float f) {
 struct u32x4 {
   uint32_t x, y, z, w;
 };
+// a ^ b ^ c: one v_bitop3_b32 on the device (truth table 0x96), which the
+// compiler does not always form from two xors by itself
+__host__ __device__ inline uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+#if __HIP_DEVICE_COMPILE__
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+#else
+  return a ^ b ^ c;
+#endif
+}
+
 __host__ __device__ inline u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+    uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;

@@ -9,11 +9,12 @@
 // from which relative RMSE sqrt(s0 / s1), the mean error (bias) s2 / n and the
 // largest error follow.  Memory-bound: one read of x and y.
 //
-// A lane takes 8 consecutive elements of a row per chunk (grid-stride over
-// chunks); partial sums go through a wave reduction and LDS to one FP64
-// atomic add (and one 64-bit atomic max: non-negative doubles order as their
-// bit patterns) per workgroup.  The differences are formed in FP64 from the
-// FP32 values.
+// A workgroup takes whole rows (grid-stride over rows, one workgroup per CU)
+// and its lanes take 8 consecutive elements of the row per chunk, two chunks
+// in flight; partial
+// sums go through a wave reduction and LDS to one FP64 atomic add (and one
+// 64-bit atomic max: non-negative doubles order as their bit patterns) per
+// workgroup.  The differences are formed in FP64 from the FP32 values.
 #include "../device/codec.h"
 #include "../launch.h"
 
@@ -21,48 +22,66 @@ namespace mxk {
 
 namespace {
 
-constexpr int kStatThreads = 256;
+constexpr int kStatThreads = 512;
 
 __global__ void k_stats_clear(double* s) {
   if (threadIdx.x < 4) s[threadIdx.x] = 0.0;
 }
 
 template <int XDT>
+__device__ inline void load8(const void* __restrict__ x, int64_t off, float (&xv)[8]) {
+  if constexpr (XDT == DT_BF16) {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xv[2 * i] = u2f(ww[i] << 16);
+      xv[2 * i + 1] = u2f(ww[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
+    const float4 a = p[0], b = p[1];
+    xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+    xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+  }
+}
+
+__device__ inline void accumulate8(const float (&xv)[8], const float (&yv)[8], double& e2, double& x2, double& e1,
+                                   double& mx) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double xd = xv[i], d = (double)yv[i] - xd;
+    e2 += d * d;
+    x2 += xd * xd;
+    e1 += d;
+    const double ad = __builtin_fabs(d);
+    mx = ad > mx ? ad : mx;
+  }
+}
+
+template <int XDT>
 __global__ __launch_bounds__(kStatThreads) void k_error_stats(const void* __restrict__ x, int64_t ld_x,
                                                               const float* __restrict__ y, int64_t ld_y,
-                                                              int64_t cols, int64_t Q, double* __restrict__ s) {
-  const int64_t cpr = cols >> 3;
+                                                              int64_t rows, int64_t cols, double* __restrict__ s) {
+  const int64_t cpr = cols >> 3;  // 8-element chunks per row
   double e2 = 0.0, x2 = 0.0, e1 = 0.0, mx = 0.0;
-  for (int64_t q = (int64_t)blockIdx.x * kStatThreads + threadIdx.x; q < Q;
-       q += (int64_t)gridDim.x * kStatThreads) {
-    const int64_t r = q / cpr, c = (q - r * cpr) * 8;
-    float xv[8], yv[8];
-    if constexpr (XDT == DT_BF16) {
-      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + r * ld_x + c);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xv[2 * i] = u2f(ww[i] << 16);
-        xv[2 * i + 1] = u2f(ww[i] & 0xFFFF0000u);
-      }
-    } else {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + r * ld_x + c);
-      const float4 a = p[0], b = p[1];
-      xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
-      xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const int64_t ox = r * ld_x, oy = r * ld_y;
+    int64_t c = threadIdx.x;
+    for (; c + kStatThreads < cpr; c += 2 * kStatThreads) {  // two chunks in flight
+      float xa[8], xb[8], ya[8], yb[8];
+      load8<XDT>(x, ox + 8 * c, xa);
+      load8<XDT>(x, ox + 8 * (c + kStatThreads), xb);
+      load8<DT_F32>(y, oy + 8 * c, ya);
+      load8<DT_F32>(y, oy + 8 * (c + kStatThreads), yb);
+      accumulate8(xa, ya, e2, x2, e1, mx);
+      accumulate8(xb, yb, e2, x2, e1, mx);
     }
-    const float4* py = reinterpret_cast<const float4*>(y + r * ld_y + c);
-    const float4 a = py[0], b = py[1];
-    yv[0] = a.x; yv[1] = a.y; yv[2] = a.z; yv[3] = a.w;
-    yv[4] = b.x; yv[5] = b.y; yv[6] = b.z; yv[7] = b.w;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const double xd = xv[i], d = (double)yv[i] - xd;
-      e2 += d * d;
-      x2 += xd * xd;
-      e1 += d;
-      const double ad = __builtin_fabs(d);
-      mx = ad > mx ? ad : mx;
+    if (c < cpr) {
+      float xa[8], ya[8];
+      load8<XDT>(x, ox + 8 * c, xa);
+      load8<DT_F32>(y, oy + 8 * c, ya);
+      accumulate8(xa, ya, e2, x2, e1, mx);
     }
   }
   // wave, then workgroup
@@ -102,14 +121,18 @@ hipError_t launch_error_stats(const void* x, int xdt, int64_t ld_x, const float*
                               int64_t cols, double* stats, hipStream_t s) {
   // cleared by a kernel, not a memset: the call stays capturable in a graph
   hipLaunchKernelGGL(k_stats_clear, dim3(1), dim3(64), 0, s, stats);
-  const int64_t Q = rows * (cols / 8);
-  if (Q > 0) {
-    const int64_t want = (Q + kStatThreads - 1) / kStatThreads;
-    const int g = (int)(want < 2048 ? want : 2048);
+  if (rows > 0 && cols > 0) {
+    // one 512-lane workgroup per CU: the four results live in one cache
+    // line, so the per-workgroup atomics serialize there (2048 workgroups of
+    // 256 lanes: 125 us at 8192 x 7168; 256 of 256: 82 us; 256 of 512: 65 us,
+    // the device-copy rate)
+    const int g = (int)(rows < 256 ? rows : 256);
     if (xdt == DT_BF16)
-      hipLaunchKernelGGL(k_error_stats<DT_BF16>, dim3(g), dim3(kStatThreads), 0, s, x, ld_x, y, ld_y, cols, Q, stats);
+      hipLaunchKernelGGL(k_error_stats<DT_BF16>, dim3(g), dim3(kStatThreads), 0, s, x, ld_x, y, ld_y, rows, cols,
+                         stats);
     else
-      hipLaunchKernelGGL(k_error_stats<DT_F32>, dim3(g), dim3(kStatThreads), 0, s, x, ld_x, y, ld_y, cols, Q, stats);
+      hipLaunchKernelGGL(k_error_stats<DT_F32>, dim3(g), dim3(kStatThreads), 0, s, x, ld_x, y, ld_y, rows, cols,
+                         stats);
   }
   return hipGetLastError();
 }
