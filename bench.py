@@ -381,6 +381,29 @@ def detail(torch, mx, W, args):
         "fused_rne_ms": ms_fr, "fused_rne_tflops": 2 * M * N * K / ms_fr / 1e9, "two_step_rne_ms": ms_tr,
         "fused_sr_ms": ms_fs, "two_step_sr_ms": ms_ts}
     del q4at, q4bt, q4c
+    # fused quantize-and-GEMM, prologue half: A arrives in BF16 and is quantized inside the
+    # GEMM (Q(A) also written out), against mx_quantize followed by mx_gemm
+    qa_out = mx.empty(1, M, K)
+    ms_q8 = time_fn(torch, lambda: mx.mx_gemm_quantize_a(a, mx.MX_MXFP8_E4M3, qb, C, a_out=qa_out), it, wu)
+
+    def two_step_a8():
+        mx.mx_quantize(a, qa)
+        mx.mx_gemm(qa, qb, C)
+    ms_t8 = time_fn(torch, two_step_a8, it, wu)
+    q4o = mx.empty(2, M, K)
+    ms_q4 = time_fn(torch, lambda: mx.mx_gemm_quantize_a(a, mx.MX_MXFP4_E2M1, q4b, C, a_out=q4o), it, wu)
+
+    def two_step_a4():
+        mx.mx_quantize(a, q4a)
+        mx.mx_gemm(q4a, q4b, C)
+    ms_t4 = time_fn(torch, two_step_a4, it, wu)
+    res["gemm_4096_quantize_a_in_prologue"] = {
+        "mxfp8_fused_ms": ms_q8, "mxfp8_fused_tflops": 2 * M * N * K / ms_q8 / 1e9,
+        "mxfp8_two_step_ms": ms_t8, "mxfp4_fused_ms": ms_q4, "mxfp4_fused_tflops": 2 * M * N * K / ms_q4 / 1e9,
+        "mxfp4_two_step_rows_layout_ms": ms_t4,
+        "kernel": "k_gemm_qa (A quantized per 32-element block in registers, decoded to exact BF16 in LDS, "
+                  "BF16 instruction); two-step: mx_quantize then the exact MXFP8 / row-layout MXFP4 GEMM"}
+    del qa_out, q4o
     # MXFP4 tile-layout quantize of the activation operand, floor and ceil scale rules
     q4t = mx.empty(2, M, K, layout=mx.MX_LAYOUT_TILED)
     by4 = M * K * (2 + 0.5 + 1 / 32)

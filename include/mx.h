@@ -377,6 +377,29 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
 mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, const mx_tensor* out,
                            int32_t rnd, mx_rng rng, uint32_t flags, mx_stream stream);
 
+/* Block-scaled GEMM whose A operand is quantized inside the GEMM's prologue
+ * ([MXF] "Open points": fused quantize-and-GEMM kernels, since computing block
+ * scales is memory traffic of its own).  A: BF16 [M, K] (device, row pitch
+ * lda elements, 16-byte aligned rows).  Every 32-element block of A's rows is
+ * quantized in the kernel exactly as mx_quantize quantizes A into a_fmt
+ * (MX_MXFP8_E4M3 or MX_MXFP4_E2M1, E8M0 floor rule, rounding rnd, SR draws
+ * indexed by the element's row-major position in A with the given rng), and
+ * C = Q(A) * B^T [M, N] (cdt, row pitch ldc) is the FP32-accumulated sum of
+ * the exact products of the decoded operands.  B: MXFP8 E4M3 or MXFP4, row
+ * layout, cols == K.  a_out (optional, NULL to skip): receives Q(A) (fmt
+ * a_fmt, row layout, [M, K]), e.g. for the backward pass; each block is
+ * written once.  Exact for MXFP4 at every scale code, for E4M3 at codes 3 ..
+ * 246 (blocks with max |x| >= 2^-116; smaller blocks lose bits in BF16).
+ * Runs on the BF16 matrix instruction after decoding in LDS; at 4096^3 it is
+ * slower than mx_quantize followed by mx_gemm, because each of the N/256
+ * column tiles quantizes its A panel again (measured; the fused product pays
+ * only where A must not be written before the GEMM).  Requirements: K % 32
+ * == 0.  Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT,
+ * MX_ERR_UNSUPPORTED, MX_ERR_HIP. */
+mx_status mx_gemm_quantize_a(const void* A, int64_t lda, int64_t M, int32_t a_fmt, int32_t rnd, mx_rng rng,
+                             const mx_tensor* B, void* C, int32_t cdt, int64_t ldc, const mx_tensor* a_out,
+                             mx_stream stream);
+
 /* Grouped NVFP4 GEMM for a mixture-of-experts forward pass ([MXF] "NVFP4";
  * [INK] "A precision choice for each stage": NVFP4 forward in the expert
  * layers).  B stacks num_groups expert matrices [N, K] as one NVFP4 tensor of

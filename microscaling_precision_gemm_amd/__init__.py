@@ -32,7 +32,7 @@ FORMATS = {"mxfp8": MX_MXFP8_E4M3, "mxfp4": MX_MXFP4_E2M1, "nvfp4": MX_NVFP4, "m
 EXPORTED = [
     "mx_codes_bytes", "mx_scales_bytes", "mx_rht_signs", "mx_quantize", "mx_amax",
     "mx_dequantize", "mx_requant_transpose", "mx_hadamard16", "mx_gemm", "mx_gemm_ex",
-    "mx_gemm_grouped", "mx_gemm_quantize", "mx_quantize_batch", "mx_error_stats",
+    "mx_gemm_grouped", "mx_gemm_quantize", "mx_gemm_quantize_a", "mx_quantize_batch", "mx_error_stats",
     "mx_status_string",
 ]
 
@@ -86,6 +86,7 @@ def load():
         "mx_gemm_ex": (i32, [TP, TP, vp, i32, i64, u32, vp]),
         "mx_gemm_grouped": (i32, [TP, vp, i64, TP, i32, vp, vp, i32, i64, vp]),
         "mx_gemm_quantize": (i32, [TP, TP, TP, i32, _Rng, u32, vp]),
+        "mx_gemm_quantize_a": (i32, [vp, i64, i64, i32, i32, _Rng, TP, vp, i32, i64, TP, vp]),
         "mx_quantize_batch": (i32, [ctypes.POINTER(_Job), i32, vp]),
         "mx_status_string": (ctypes.c_char_p, [i32]),
     }
@@ -301,6 +302,19 @@ def mx_gemm_quantize(A: MXTensor, B: MXTensor, out: MXTensor, rnd: int = MX_RNE,
     _check(L.mx_gemm_quantize(ctypes.byref(da), ctypes.byref(db), ctypes.byref(do), rnd,
                               _Rng(seed, counter), flags, _stream(stream)))
     return out
+
+
+def mx_gemm_quantize_a(A, a_fmt: int, B: MXTensor, C, rnd: int = MX_RNE, seed: int = 0, counter: int = 0,
+                       a_out: "MXTensor | None" = None, stream=None):
+    """C = Q(A) * B^T with A a BF16 [M, K] matrix quantized to a_fmt (MXFP8
+    E4M3 or MXFP4) inside the GEMM; Q(A) also lands in a_out when given."""
+    L = load()
+    db = B.desc()
+    dq = a_out.desc() if a_out is not None else None
+    _check(L.mx_gemm_quantize_a(_ptr(A), A.stride(0), A.shape[0], a_fmt, rnd, _Rng(seed, counter),
+                                ctypes.byref(db), _ptr(C), _dt(C), C.stride(0),
+                                ctypes.byref(dq) if dq is not None else None, _stream(stream)))
+    return C
 
 
 def mx_gemm_grouped(A: MXTensor, row_index, routed_rows: int, B: MXTensor, num_groups: int,

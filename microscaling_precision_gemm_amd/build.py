@@ -26,6 +26,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "gemm_any.hip"),
     os.path.join(CSRC, "kernels", "gemm_f6.hip"),
     os.path.join(CSRC, "kernels", "stats.hip"),
+    os.path.join(CSRC, "kernels", "gemm_qa.hip"),
 ]
 
 # -ffp-contract=off: the quantizers' FP32 scale arithmetic must round once per

@@ -400,6 +400,34 @@ mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, const mx_tens
       rng.seed, rng.counter, (flags & MX_FLAG_SCALE_CEIL) != 0, reinterpret_cast<hipStream_t>(stream)));
 }
 
+mx_status mx_gemm_quantize_a(const void* A, int64_t lda, int64_t M, int32_t a_fmt, int32_t rnd, mx_rng rng,
+                             const mx_tensor* B, void* C, int32_t cdt, int64_t ldc, const mx_tensor* a_out,
+                             mx_stream stream) {
+  if (!B) return MX_ERR_NULL;
+  if (rnd != MX_RNE && rnd != MX_SR) return MX_ERR_FORMAT;
+  if (a_fmt != MX_MXFP8_E4M3 && a_fmt != MX_MXFP4_E2M1) return MX_ERR_UNSUPPORTED;
+  mx_status st = check_tensor(B, B->rows, B->cols);
+  if (st != MX_OK) return st;
+  if ((B->fmt != MX_MXFP8_E4M3 && B->fmt != MX_MXFP4_E2M1) || B->layout != MX_LAYOUT_ROWS)
+    return MX_ERR_UNSUPPORTED;
+  const int64_t N = B->rows, K = B->cols;
+  if (M < 0 || K % 32) return MX_ERR_SHAPE;
+  st = check_matrix(A, MX_BF16, M, K, lda);
+  if (st != MX_OK) return st;
+  st = check_output(C, cdt, M, N, ldc);
+  if (st != MX_OK) return st;
+  if (a_out) {
+    st = check_tensor(a_out, M, K);
+    if (st != MX_OK) return st;
+    if (a_out->fmt != a_fmt || a_out->layout != MX_LAYOUT_ROWS) return MX_ERR_UNSUPPORTED;
+  }
+  if (M * N == 0) return MX_OK;
+  return hip_status(mxk::launch_gemm_quantize_a(
+      a_fmt, static_cast<const uint16_t*>(A), lda, static_cast<const uint8_t*>(B->codes), B->scales, B->fmt, M, N,
+      K, C, cdt, ldc, a_out ? static_cast<uint8_t*>(a_out->codes) : nullptr, a_out ? a_out->scales : nullptr,
+      rnd == MX_SR, rng.seed, rng.counter, reinterpret_cast<hipStream_t>(stream)));
+}
+
 mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,
                   mx_stream stream) {
   return mx_gemm_ex(A, B, C, cdt, ldc, 0u, stream);

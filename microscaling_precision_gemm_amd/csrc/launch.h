@@ -105,6 +105,13 @@ hipError_t launch_gemm_mx_f6(int fa, const uint8_t* a_codes, const uint8_t* a_sc
                              int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s);
 // C = A * B^T of tile-layout MX operands, written quantized along its rows
 // (MX format ofmt, row or tile layout) by the GEMM's epilogue.
+// C = Q(A) * B^T with A (BF16, row pitch lda) quantized to afmt (FMT_MXFP8 or
+// FMT_MXFP4) inside the GEMM; B in bfmt (FMT_MXFP8 or FMT_MXFP4), row layout;
+// a_codes / a_scales (both or neither): Q(A) written out, row layout.
+hipError_t launch_gemm_quantize_a(int afmt, const uint16_t* a, int64_t lda, const uint8_t* b_codes,
+                                  const uint8_t* b_scales, int bfmt, int64_t M, int64_t N, int64_t K, void* C,
+                                  int cdt, int64_t ldc, uint8_t* a_codes, uint8_t* a_scales, bool sr,
+                                  uint64_t seed, uint64_t counter, hipStream_t s);
 hipError_t launch_gemm_mx_tiled_quant(int fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                                       const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                       int64_t N, int64_t K, int ofmt, bool otiled, uint8_t* codes,

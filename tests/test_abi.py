@@ -164,6 +164,21 @@ def test_other_entry_point_checks(mx):
     assert L.mx_error_stats(FAKE, 0, 64, FAKE, 64, 4, 60, FAKE, None) == 2
     assert L.mx_error_stats(FAKE, 0, 32, FAKE, 64, 4, 64, FAKE, None) == 2
     assert L.mx_error_stats(FAKE, 0, 64, FAKE, 64, 4, 64, ctypes.c_void_p(FAKE + 8), None) == 3
+    # GEMM quantizing A in its prologue: missing B, A format, rounding mode, B
+    # format, missing / unaligned A, A pitch, missing C, Q(A) format and shape
+    f = L.mx_gemm_quantize_a
+    assert f(FAKE, 64, 32, 1, 0, rng, None, FAKE, 1, 64, None, None) == 1
+    assert f(FAKE, 64, 32, 3, 0, rng, ctypes.byref(a8), FAKE, 1, 64, None, None) == 5
+    assert f(FAKE, 64, 32, 1, 2, rng, ctypes.byref(a8), FAKE, 1, 64, None, None) == 4
+    assert f(FAKE, 64, 32, 1, 0, rng, ctypes.byref(nv), FAKE, 1, 64, None, None) == 5
+    assert f(None, 64, 32, 1, 0, rng, ctypes.byref(a8), FAKE, 1, 64, None, None) == 1
+    assert f(ctypes.c_void_p(FAKE + 8), 64, 32, 1, 0, rng, ctypes.byref(a8), FAKE, 1, 64, None, None) == 3
+    assert f(FAKE, 48, 32, 1, 0, rng, ctypes.byref(a8), FAKE, 1, 64, None, None) == 2
+    assert f(FAKE, 64, 32, 1, 0, rng, ctypes.byref(a8), None, 1, 64, None, None) == 1
+    q4 = _t(mx, 2, 32, 64)
+    assert f(FAKE, 64, 32, 1, 0, rng, ctypes.byref(a8), FAKE, 1, 64, ctypes.byref(q4), None) == 5
+    q8 = _t(mx, 1, 48, 64)
+    assert f(FAKE, 64, 32, 1, 0, rng, ctypes.byref(a8), FAKE, 1, 64, ctypes.byref(q8), None) == 2
 
 
 def test_binding_fails_loudly_without_library(mx, monkeypatch):
