@@ -234,3 +234,39 @@ def test_grouped_nvfp4_pipelined(gather, cdt):
         Bd = oracle.dequantize_f64(3, qw[e][0], qw[e][1], N, K)
         Chat, tol = oracle.gemm(Ad[rows], Bd, float(np.float64(qx[2]) * np.float64(qw[e][2])))
         check_gemm(Cg[lo:hi], Chat, tol, cdt == "bf16", f"pipelined expert {e} gather={gather}")
+
+
+@pytest.mark.parametrize("gather", [False, True])
+def test_grouped_nvfp4_pipelined_short_last_tiles(gather):
+    """Pipelined grouped NVFP4 whose groups end 10, 40, 150, 230 and 18 rows
+    into their last row tile (rows past a group's end are clamped copies that
+    are computed but never stored), with and without the row gather."""
+    K, N = 512, 4096
+    offsets = np.array([0, 266, 306, 968, 1198, 1216], np.int64)
+    E = offsets.size - 1
+    R = int(offsets[-1])
+    tokens = 900
+    X = W.normal_bf16(tokens, K, 1.0, 7, 57)
+    rng = np.random.default_rng(7)
+    row_index = rng.integers(0, tokens, R).astype(np.int32)
+    qw = [oracle.quantize(W.normal_bf16(N, K, 0.05, 7, 90 + e), 3, 0) for e in range(E)]
+    if gather:
+        qx = oracle.quantize(X, 3, 0)
+        ri = torch.from_numpy(row_index).to(dev())
+    else:
+        qx = oracle.quantize(np.ascontiguousarray(X[row_index]), 3, 0)
+        ri = None
+    A = upload(3, *qx)
+    B = upload(3, np.concatenate([q[0] for q in qw]), np.concatenate([q[1] for q in qw]),
+               np.array([q[2] for q in qw], np.float32))
+    C = torch.full((R, N), float("nan"), dtype=torch.float32, device=dev())
+    mx.mx_gemm_grouped(A, ri, R, B, E, torch.from_numpy(offsets).to(dev()), C)
+    torch.cuda.synchronize()
+    Cg = C.cpu().numpy()
+    Ad = oracle.dequantize_f64(3, qx[0], qx[1], qx[0].shape[0], K)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        rows = row_index[lo:hi] if gather else np.arange(lo, hi)
+        Bd = oracle.dequantize_f64(3, qw[e][0], qw[e][1], N, K)
+        Chat, tol = oracle.gemm(Ad[rows], Bd, float(np.float64(qx[2]) * np.float64(qw[e][2])))
+        check_gemm(Cg[lo:hi], Chat, tol, False, f"short-tile expert {e} gather={gather}")
