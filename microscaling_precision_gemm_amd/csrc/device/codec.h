@@ -259,12 +259,18 @@ __host__ __device__ inline u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   return {c0, c1, c2, c3};
 }
 
+// The Philox block of output elements 8q .. 8q+7 of a stream: element
+// 8q + 2k draws the low 16 bits of word k, element 8q + 2k + 1 the high 16.
+__host__ __device__ inline u32x4 rand_words(uint64_t seed, uint64_t counter, uint64_t q) {
+  const uint64_t c = counter + q;
+  return philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), 0u, 0u, (uint32_t)seed,
+                       (uint32_t)(seed >> 32));
+}
+
 // Eight 16-bit random values for output elements 8q .. 8q+7 of a stream.
 __host__ __device__ inline void rand16x8(uint64_t seed, uint64_t counter, uint64_t q,
                                          uint32_t out[8]) {
-  uint64_t c = counter + q;
-  u32x4 w = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), 0u, 0u, (uint32_t)seed,
-                          (uint32_t)(seed >> 32));
+  const u32x4 w = rand_words(seed, counter, q);
   out[0] = w.x & 0xFFFFu; out[1] = w.x >> 16;
   out[2] = w.y & 0xFFFFu; out[3] = w.y >> 16;
   out[4] = w.z & 0xFFFFu; out[5] = w.z >> 16;

@@ -94,14 +94,16 @@ __device__ inline void pack_fp6_rne(const float y[8], uint32_t w[2]) {
 // exactly when r16 < floor((|y| - lo) * 2^16 / (hi - lo)).  gfx950's scaled
 // SR conversions take a 32-bit seed and round |y| up exactly when the seed's
 // top 16 bits are at least 2^16 - floor((|y| - lo) * 2^16 / (hi - lo)),
-// ignoring the lower seed bits and the lower fraction bits (measured on the
-// device), so the seed (~r16 & 0xFFFF) << 16 takes the rule's decision.
+// ignoring the lower fraction bits (measured on the device), so the seed
+// (~r16 & 0xFFFF) << 16, lower bits zero, takes the rule's decision.
 // Inputs are clamped to the largest finite value first (the rule saturates;
 // the instruction would round past it).  Checked on the device against the
 // software encoders of codec.h for E4M3, E5M2 and E2M1 over every FP32 input
 // up to +Inf and its negative.  The FP4 pair instruction draws its first
-// element from seed bits 16..31 but its second from bits 15..30, so FP4 is
-// converted one element per instruction.
+// element from seed bits 16..31 but its second from bits 15..30, so each
+// element of a pair takes a conversion of its own; for the second the seed
+// is (~r16 & 0xFFFF) << 15 with every other bit zero (set bits below bit 15
+// change some decisions: measured).
 typedef float v2f_cvt __attribute__((ext_vector_type(2)));
 
 __device__ inline uint32_t sr_seed(uint32_t r16) { return (~r16 & 0xFFFFu) << 16; }
@@ -141,6 +143,36 @@ __device__ inline void pack_e5m2_sr(const float y[8], const uint32_t r[8], uint3
   MXK_SR8(__builtin_amdgcn_cvt_scalef32_sr_bf8_f32, 57344.0f)
 }
 #undef MXK_SR8
+
+// 8 E2M1 codes by SR from the four words of one Philox block (w0..w3:
+// element 2k draws the low half of word k, element 2k + 1 its high half, as
+// in pack_e2m1_sr), element i in nibble i.  Each pair (y[2k], y[2k+1]) is
+// converted twice: seeded for element 2k (bits 16..31; its low nibble is
+// kept) and for element 2k + 1 (bits 15..30; its high nibble is kept), every
+// other seed bit zero.  Only
+// byte 0 of each result is used: the compiler does not carry the old
+// destination through this instruction, so its byte select cannot merge
+// results.  A bit-field insert per pair and two byte permutes assemble the
+// word.
+__device__ inline uint32_t pack_e2m1_sr_words(const float y[8], uint32_t w0, uint32_t w1,
+                                              uint32_t w2, uint32_t w3) {
+  float c[8];  // clamped to +-6 (the inputs are not NaN: one median instruction)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_fmed3f(y[i], -6.0f, 6.0f);
+  const uint32_t n[4] = {~w0, ~w1, ~w2, ~w3};
+  uint32_t x[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const v2f_cvt p = {c[2 * k], c[2 * k + 1]};
+    const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, n[k] << 16, 1.0f, 0);
+    const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, (n[k] >> 1) & 0x7FFF8000u, 1.0f, 0);
+    x[k] = (lo & 0x0Fu) | (hi & 0xFFFFFFF0u);  // byte 0: both codes of the pair
+  }
+  // byte 0 of x0 and x1 into bytes 0 and 1 (selector 0x0C: a zero byte)
+  const uint32_t p01 = __builtin_amdgcn_perm(x[1], x[0], 0x0C0C0400u);
+  const uint32_t p23 = __builtin_amdgcn_perm(x[3], x[2], 0x0C0C0400u);
+  return p01 | (p23 << 16);
+}
 
 // 8 E2M1 codes by SR, element i in nibble i
 __device__ inline uint32_t pack_e2m1_sr(const float y[8], const uint32_t r[8]) {

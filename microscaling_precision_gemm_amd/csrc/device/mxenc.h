@@ -120,11 +120,13 @@ __device__ inline void encode_mx(const MxEnc& a, int64_t q, const float v[8], En
     } else {
       e.w[0] = pack_e2m1_rne(y);
     }
-  } else {  // SR on the conversion instructions (cvt.h)
+  } else if constexpr (FMT == FMT_MXFP8) {  // SR on the conversion instructions (cvt.h)
     uint32_t r[8];
     rand16x8(a.seed, a.counter, (uint64_t)q, r);
-    if constexpr (FMT == FMT_MXFP8) pack_e4m3_sr(y, r, e.w);
-    else e.w[0] = pack_e2m1_sr(y, r);
+    pack_e4m3_sr(y, r, e.w);
+  } else {
+    const u32x4 w = rand_words(a.seed, a.counter, (uint64_t)q);
+    e.w[0] = pack_e2m1_sr_words(y, w.x, w.y, w.z, w.w);
   }
   if (sc == 0xFFu) {  // NaN / Inf in the block
 #pragma unroll

@@ -108,11 +108,13 @@ __device__ inline void encode_block(const uint32_t (&x)[16], uint64_t seed, uint
   for (int i = 0; i < 32; ++i) y[i] = v[i] * inv;  // exact scaling by a power of two
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    if constexpr (SR) {
+    if constexpr (SR && F == FMT_MXFP8) {
       uint32_t r[8];
       rand16x8(seed, counter, q0 + (uint64_t)c, r);
-      if constexpr (F == FMT_MXFP8) pack_e4m3_sr(y + 8 * c, r, w + 2 * c);
-      else w[c] = pack_e2m1_sr(y + 8 * c, r);
+      pack_e4m3_sr(y + 8 * c, r, w + 2 * c);
+    } else if constexpr (SR) {
+      const u32x4 rw = rand_words(seed, counter, q0 + (uint64_t)c);
+      w[c] = pack_e2m1_sr_words(y + 8 * c, rw.x, rw.y, rw.z, rw.w);
     } else {
       if constexpr (F == FMT_MXFP8) pack_e4m3_rne(y + 8 * c, w + 2 * c);
       else w[c] = pack_e2m1_rne(y + 8 * c);

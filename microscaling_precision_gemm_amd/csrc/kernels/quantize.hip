@@ -115,15 +115,43 @@ __device__ inline void store8(void* base, int64_t off, const float v[8]) {
   }
 }
 
-// Forward 16-point transform of a group split over a lane pair: this lane
-// holds elements 8*half .. 8*half+7.  y = (1/4) H16 D x, stages 1, 2, 4 in
-// the lane, stage 8 across the pair (the lower lane keeps a + b, the upper
-// lane a - b, with a the lower lane's value).
-__device__ inline void rht_forward(float v[8], uint32_t mask, uint32_t half) {
-  uint32_t m = (mask >> (8 * half)) & 0xFFu;
+// The random signs D of the forward transform as XOR masks on the raw bits
+// of a chunk (bit i of the lane's byte of the mask negates element i): one
+// XOR per word instead of a select per element.  The masks depend only on
+// the lane's half, so a wave computes them once.
+template <int XDT>
+struct SignBits {
+  u4 w[XDT == DT_BF16 ? 1 : 2];
+};
+
+template <int XDT>
+__device__ inline SignBits<XDT> rht_sign_bits(uint32_t mask, uint32_t half) {
+  const uint32_t m = (mask >> (8 * half)) & 0xFFu;
+  SignBits<XDT> s;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if ((m >> i) & 1u) v[i] = -v[i];
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (XDT == DT_BF16) {  // word i: elements 2i (bits 0..15) and 2i + 1
+      s.w[0][i] = (((m >> (2 * i)) & 1u) << 15) | (((m >> (2 * i + 1)) & 1u) << 31);
+    } else {
+      s.w[0][i] = ((m >> i) & 1u) << 31;
+      s.w[1][i] = ((m >> (4 + i)) & 1u) << 31;
+    }
+  }
+  return s;
+}
+
+template <int XDT>
+__device__ inline void apply_signs(Raw<XDT>& r, const SignBits<XDT>& s) {
+#pragma unroll
+  for (int h = 0; h < (XDT == DT_BF16 ? 1 : 2); ++h) r.w[h] ^= s.w[h];
+}
+
+// Forward 16-point transform of a group split over a lane pair, for values
+// whose signs D are already applied (apply_signs): this lane holds elements
+// 8*half .. 8*half+7.  y = (1/4) H16 D x, stages 1, 2, 4 in the lane, stage 8
+// across the pair (the lower lane keeps a + b, the upper lane a - b, with a
+// the lower lane's value).
+__device__ inline void rht_forward_signed(float v[8], uint32_t half) {
   hadamard8_stages(v);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -202,13 +230,17 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx(QuantArgs a, int64_t Q) {
   const int64_t q0 = wave * (64 * kU) + lane;
   Raw<XDT> raw[kU];
   load_slabs<XDT>(a.x, q0, Q, cpr, a.ld_x, dense, raw);
+  // q0 is even: the lane's half of its Hadamard group is lane & 1 in every slab
+  SignBits<XDT> sg;
+  if constexpr (RHT) sg = rht_sign_bits<XDT>(a.sign_mask, lane & 1u);
   Enc<FMT> enc[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int64_t q = q0 + 64 * u;
     float v[8];
+    if constexpr (RHT) apply_signs<XDT>(raw[u], sg);
     widen<XDT>(raw[u], v);
-    if constexpr (RHT) rht_forward(v, a.sign_mask, (uint32_t)(q & 1));
+    if constexpr (RHT) rht_forward_signed(v, lane & 1u);
     encode_mx<FMT, SR>(a, q, v, enc[u]);
   }
 #pragma unroll
@@ -254,12 +286,15 @@ __device__ __attribute__((always_inline)) inline void quant_tiled_wave(const Qua
     for (int t = 0; t < NT; ++t) load_raw<XDT>(a.x, xoff + 64 * t, raw[t]);
   }
   const int64_t q0 = (row * a.cols + col0) >> 3;
+  SignBits<XDT> sg;
+  if constexpr (RHT) sg = rht_sign_bits<XDT>(a.sign_mask, k & 1u);
   Enc<FMT> enc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     float v[8];
+    if constexpr (RHT) apply_signs<XDT>(raw[t], sg);
     widen<XDT>(raw[t], v);
-    if constexpr (RHT) rht_forward(v, a.sign_mask, k & 1u);
+    if constexpr (RHT) rht_forward_signed(v, k & 1u);
     encode_mx<FMT, SR>(a, q0 + 8 * t, v, enc[t]);
   }
   // Codes: instruction index T = t0 + t in the group.  FP4: code byte
@@ -345,31 +380,86 @@ hipError_t quant_mx_tiled_d(const QuantArgs& a, hipStream_t s) {
 }
 
 // ---- NVFP4 (E4M3 per 16 + FP32 per tensor) quantizer ----------------------
+// Per 16-block: q = fl(a_b / d) (d = 6 S, or 4 S for the second Four Over Six
+// candidate), sb = E4M3 RNE of q, rcp = 1 / fl(dec(sb) S).  Both FP32
+// divisions are replaced by exact equivalents:
+//  * rcp comes from a per-workgroup table of the reciprocals for the 127
+//    finite E4M3 magnitudes, filled with the same FP32 operations (code 0, and
+//    a product that overflows to +Inf, give 0);
+//  * q is the product a_b fl(1/d) corrected once by its residual
+//    a_b - q0 d, which a fused multiply-add forms exactly (Markstein's
+//    correction step: the rounded result is the correctly rounded quotient
+//    when fl(1/d) is the rounded reciprocal and no step under- or
+//    overflows).  For 2^-80 <= d <= 2^80 the residual of every quotient that
+//    can round to a nonzero E4M3 code (q >= 2^-11) is exact, smaller quotients
+//    (code 0 either way) stay below 2^-10, and a product past the FP32 range
+//    keeps its +Inf.  Other divisors take the division.
+struct NvDiv {
+  float d, rd;
+  bool exact;
+};
+
+__device__ inline NvDiv nv_div(float d) {
+#pragma clang fp contract(off)
+  NvDiv k;
+  k.d = d;
+  k.rd = 1.0f / d;
+  k.exact = d >= 0x1p-80f && d <= 0x1p80f;
+  return k;
+}
+
+__device__ inline float nv_quot(float m, const NvDiv& k) {
+#pragma clang fp contract(off)
+  if (!k.exact) return m / k.d;
+  const float q0 = m * k.rd;
+  const float r = __builtin_fmaf(-q0, k.d, m);
+  const float q1 = __builtin_fmaf(r, k.rd, q0);
+  return q1 == q1 ? q1 : q0;  // NaN: the product overflowed (or m is not finite)
+}
+
+// The reciprocal table of one tensor scale S, filled by the first 128
+// threads of the workgroup (all of its threads call this).
+constexpr int kNvRcp = 128;
+
+__device__ inline void nv_fill_recips(float* tab, float S) {
+#pragma clang fp contract(off)
+  const uint32_t c = threadIdx.x;
+  if (c < (uint32_t)kNvRcp) {
+    float r = 0.0f;
+    if (c < 0x7Fu) {
+      const float dsb = e4m3_mag_value(c);
+      if (dsb != 0.0f) {
+        const float p = dsb * S;
+        r = 1.0f / p;
+      }
+    }
+    tab[c] = r;
+  }
+  __syncthreads();
+}
+
+// Codes of finite quotients are at most 0x7E; the mask keeps the read in the
+// table for any input.
+__device__ inline float nv_recip(const float* tab, uint32_t sb) { return tab[sb & 0x7Fu]; }
+
 template <bool SR>
-__device__ inline void encode_nv(const QuantArgs& a, float S, float d, int64_t q, const float v[8],
-                                 Enc<FMT_NVFP4>& e) {
+__device__ inline void encode_nv(const QuantArgs& a, const float* rtab, const NvDiv& dk, int64_t q,
+                                 const float v[8], Enc<FMT_NVFP4>& e) {
 #pragma clang fp contract(off)
   uint32_t m = max_abs_bits(v);
   uint32_t o = dpp_xor1(m);
   m = o > m ? o : m;
-  const float qb = u2f(m) / d;
-  const uint32_t sb = e4m3_rne_mag(qb);
-  const float dsb = e4m3_mag_value(sb);
-  float rcp = 0.0f;
-  if (dsb != 0.0f) {
-    const float p = dsb * S;
-    rcp = 1.0f / p;
-  }
+  const uint32_t sb = e4m3_rne_mag(nv_quot(u2f(m), dk));
   // rcp = 0 (a zero block scale) gives y = +-0 and so the codes +-0
+  const float rcp = nv_recip(rtab, sb);
   float y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = v[i] * rcp;
   if constexpr (!SR) {
     e.w[0] = pack_e2m1_rne(y);
   } else {
-    uint32_t r[8];
-    rand16x8(a.seed, a.counter, (uint64_t)q, r);
-    e.w[0] = pack_e2m1_sr(y, r);  // SR on the conversion instruction
+    const u32x4 w = rand_words(a.seed, a.counter, (uint64_t)q);
+    e.w[0] = pack_e2m1_sr_words(y, w.x, w.y, w.z, w.w);  // SR on the conversion instruction
   }
   e.sc = sb;
 }
@@ -451,8 +541,8 @@ __device__ inline bool nv46_exact_four(const float v[8], uint32_t w6, float dsb6
   return (__int128)(us + other) > 0;
 }
 
-__device__ inline void encode_nv46(float S, float d6, float d4, const float v[8],
-                                   Enc<FMT_NVFP4>& e) {
+__device__ inline void encode_nv46(float S, const float* rtab, const NvDiv& d6, const NvDiv& d4,
+                                   const float v[8], Enc<FMT_NVFP4>& e) {
 #pragma clang fp contract(off)
   uint32_t m = max_abs_bits(v);
   uint32_t o = dpp_xor1(m);
@@ -460,17 +550,12 @@ __device__ inline void encode_nv46(float S, float d6, float d4, const float v[8]
   const float ab = u2f(m);
   uint32_t sb[2], w[2];
   float err[2], dsbk[2];
-  const float d[2] = {d6, d4};
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    sb[k] = e4m3_rne_mag(ab / d[k]);
+    sb[k] = e4m3_rne_mag(nv_quot(ab, k == 0 ? d6 : d4));
     const float dsb = e4m3_mag_value(sb[k]);
     dsbk[k] = dsb;
-    float rcp = 0.0f;
-    if (dsb != 0.0f) {
-      const float p = dsb * S;
-      rcp = 1.0f / p;
-    }
+    const float rcp = nv_recip(rtab, sb[k]);
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = v[i] * rcp;
@@ -501,16 +586,24 @@ __device__ __attribute__((always_inline)) inline void nv1d_wave(const QuantArgs&
   const float T = *a.amax;
   const float S = (T == 0.0f) ? 1.0f : T / 2688.0f;
   if (wave == 0 && lane == 0) *a.tensor_scale = S;
-  const float d = 6.0f * S;
+  __shared__ float rtab[kNvRcp];
+  nv_fill_recips(rtab, S);
+  const NvDiv d6 = nv_div(6.0f * S);
+  NvDiv d4 = d6;
+  if constexpr (F46) d4 = nv_div(4.0f * S);
+  // q0 is even, so the lane's half of its Hadamard group is lane & 1 in every slab
+  SignBits<XDT> sg;
+  if constexpr (RHT) sg = rht_sign_bits<XDT>(a.sign_mask, lane & 1u);
   Enc<FMT_NVFP4> enc[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int64_t q = q0 + 64 * u;
     float v[8];
+    if constexpr (RHT) apply_signs<XDT>(raw[u], sg);
     widen<XDT>(raw[u], v);
-    if constexpr (RHT) rht_forward(v, a.sign_mask, (uint32_t)(q & 1));
-    if constexpr (F46) encode_nv46(S, d, 4.0f * S, v, enc[u]);
-    else encode_nv<SR>(a, S, d, q, v, enc[u]);
+    if constexpr (RHT) rht_forward_signed(v, lane & 1u);
+    if constexpr (F46) encode_nv46(S, rtab, d6, d4, v, enc[u]);
+    else encode_nv<SR>(a, rtab, d6, q, v, enc[u]);
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) store_enc<FMT_NVFP4>(a, q0 + 64 * u, Q, lane, 2u, enc[u]);
@@ -551,6 +644,10 @@ __device__ __attribute__((always_inline)) inline void nv2d_wave(const QuantArgs&
                                                                 int64_t groups_per_band, int64_t wave) {
 #pragma clang fp contract(off)
   const uint32_t lane = threadIdx.x & 63u;
+  const float T = *a.amax;
+  const float S = (T == 0.0f) ? 1.0f : T / 2688.0f;
+  __shared__ float rtab[kNvRcp];
+  nv_fill_recips(rtab, S);  // before any wave of the workgroup leaves
   if (wave >= nwaves) return;
   const int64_t band = wave / groups_per_band;
   const int64_t G = wave - band * groups_per_band;
@@ -569,18 +666,19 @@ __device__ __attribute__((always_inline)) inline void nv2d_wave(const QuantArgs&
     const int64_t c = col[u] < cols ? col[u] : cols - 8;
     load_raw<XDT>(a.x, r * a.ld_x + c, raw[u]);
   }
-  const float T = *a.amax;
-  const float S = (T == 0.0f) ? 1.0f : T / 2688.0f;
   if (wave == 0 && lane == 0) *a.tensor_scale = S;
-  const float d = 6.0f * S;
+  const NvDiv d6 = nv_div(6.0f * S);
   float v[k2dLoads][8];
   uint32_t m[k2dGroups];
 #pragma unroll
   for (int c = 0; c < k2dGroups; ++c) m[c] = 0u;
+  SignBits<XDT> sg;
+  if constexpr (RHT) sg = rht_sign_bits<XDT>(a.sign_mask, k & 1u);
 #pragma unroll
   for (int u = 0; u < k2dLoads; ++u) {
+    if constexpr (RHT) apply_signs<XDT>(raw[u], sg);
     widen<XDT>(raw[u], v[u]);
-    if constexpr (RHT) rht_forward(v[u], a.sign_mask, k & 1u);
+    if constexpr (RHT) rht_forward_signed(v[u], k & 1u);
     const uint32_t b = ok[u] ? max_abs_bits(v[u]) : 0u;
     m[u >> 1] = b > m[u >> 1] ? b : m[u >> 1];
   }
@@ -604,22 +702,16 @@ __device__ __attribute__((always_inline)) inline void nv2d_wave(const QuantArgs&
   uint32_t w[k2dLoads], sw[k2dLoads];
 #pragma unroll
   for (int u = 0; u < k2dLoads; ++u) {
-    const uint32_t sb = e4m3_rne_mag(u2f(m[u >> 1]) / d);
-    const float dsb = e4m3_mag_value(sb);
-    float rcp = 0.0f;
-    if (dsb != 0.0f) {
-      const float p = dsb * S;
-      rcp = 1.0f / p;
-    }
+    const uint32_t sb = e4m3_rne_mag(nv_quot(u2f(m[u >> 1]), d6));
+    const float rcp = nv_recip(rtab, sb);
     float y[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = v[u][j] * rcp;
     if constexpr (!SR) {
       w[u] = pack_e2m1_rne(y);
     } else {
-      uint32_t r[8];
-      rand16x8(a.seed, a.counter, (uint64_t)((row[u] * cols + col[u]) >> 3), r);
-      w[u] = pack_e2m1_sr(y, r);  // SR on the conversion instruction
+      const u32x4 rw = rand_words(a.seed, a.counter, (uint64_t)((row[u] * cols + col[u]) >> 3));
+      w[u] = pack_e2m1_sr_words(y, rw.x, rw.y, rw.z, rw.w);  // SR on the conversion instruction
     }
     // lane 8 i + 2 p holds block p of its row's 64-column group: gather the
     // group's 4 scale bytes into lane 8 i
@@ -684,14 +776,18 @@ __device__ __attribute__((always_inline)) inline void amax_part(const void* x, i
   const int64_t cpr = cols >> 3;
   const bool dense = ld_x == cols;
   uint32_t m = 0;
+  // every q0 - lane is a multiple of 64: the lane's half of its group is lane & 1
+  SignBits<XDT> sg;
+  if constexpr (RHT) sg = rht_sign_bits<XDT>(sign_mask, lane & 1u);
   for (int64_t q0 = wave * (64 * kU) + lane; q0 - lane < Q; q0 += nwaves * (64 * kU)) {
     Raw<XDT> raw[kU];
     load_slabs<XDT>(x, q0, Q, cpr, ld_x, dense, raw);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       float v[8];
+      if constexpr (RHT) apply_signs<XDT>(raw[u], sg);
       widen<XDT>(raw[u], v);
-      if constexpr (RHT) rht_forward(v, sign_mask, (uint32_t)((q0 + 64 * u) & 1));
+      if constexpr (RHT) rht_forward_signed(v, lane & 1u);
       // Chunks past the end reload chunk Q - 1 and are left out: after the
       // Hadamard transform a pair of them is not a group of the input.
       const uint32_t b = q0 + 64 * u < Q ? max_abs_bits(v) : 0u;
@@ -855,13 +951,16 @@ __global__ __launch_bounds__(kThreads) void k_hadamard(const void* x, void* y, i
   const int64_t q0 = wave * (64 * kU) + lane;
   Raw<XDT> raw[kU];
   load_slabs<XDT>(x, q0, Q, cols >> 3, cols, true, raw);
+  SignBits<XDT> sg;  // q0 is even: the lane's half is lane & 1
+  if constexpr (!INV) sg = rht_sign_bits<XDT>(sign_mask, lane & 1u);
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int64_t q = q0 + 64 * u;
     float v[8];
+    if constexpr (!INV) apply_signs<XDT>(raw[u], sg);
     widen<XDT>(raw[u], v);
-    if constexpr (INV) rht_inverse(v, sign_mask, (uint32_t)(q & 1));
-    else rht_forward(v, sign_mask, (uint32_t)(q & 1));
+    if constexpr (INV) rht_inverse(v, sign_mask, lane & 1u);
+    else rht_forward_signed(v, lane & 1u);
     if (q < Q) store8<YDT>(y, q * 8, v);
   }
 }
