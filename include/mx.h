@@ -180,9 +180,10 @@ uint16_t mx_rht_signs(uint64_t seed);
  *
  * NVFP4 ([MXF] "NVFP4"; [FP4] format table): T = max|x| over the tensor,
  * S = T / 2688 (S = 1 when T = 0); per 16-block sb = E4M3 round-to-nearest of
- * max|x| / (6 S); elements x * (1 / (dec(sb) * S)) rounded to E2M1 (rnd);
- * blocks whose sb decodes to 0 store +-0.  All steps are FP32, one rounding
- * each, in that order.  `amax` (device, one float) is required: with
+ * max|x| / (6 S); elements x * (1 / (dec(sb) * S)) rounded to E2M1 (rnd),
+ * saturating at +-6; blocks whose sb decodes to 0, and zero elements (also
+ * where a tiny S makes the reciprocal +Inf), store +-0.  All steps are FP32,
+ * one rounding each, in that order.  `amax` (device, one float) is required: with
  * MX_FLAG_AMAX_GIVEN it is read, otherwise T is computed into it first (two
  * passes over x).  Inputs must be finite.
  *

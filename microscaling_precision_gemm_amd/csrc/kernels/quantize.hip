@@ -442,9 +442,23 @@ __device__ inline void nv_fill_recips(float* tab, float S) {
 // table for any input.
 __device__ inline float nv_recip(const float* tab, uint32_t sb) { return tab[sb & 0x7Fu]; }
 
+// For S < 2^-100 a reciprocal 1 / fl(dec(sb) S) can overflow to +Inf, and a
+// zero element's product 0 * Inf is NaN: zero elements keep their +-0, the
+// code every finite reciprocal gives them.  Infinite products need nothing:
+// the conversions saturate +-Inf to +-6.  (`tiny` is kernel-wide, so this is
+// a scalar branch.)
+constexpr float kNvTinyS = 0x1p-100f;
+
+__device__ inline void nv_keep_zeros(bool tiny, const float v[8], float y[8]) {
+  if (tiny) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = v[i] == 0.0f ? v[i] : y[i];
+  }
+}
+
 template <bool SR>
-__device__ inline void encode_nv(const QuantArgs& a, const float* rtab, const NvDiv& dk, int64_t q,
-                                 const float v[8], Enc<FMT_NVFP4>& e) {
+__device__ inline void encode_nv(const QuantArgs& a, const float* rtab, const NvDiv& dk, bool tiny,
+                                 int64_t q, const float v[8], Enc<FMT_NVFP4>& e) {
 #pragma clang fp contract(off)
   uint32_t m = max_abs_bits(v);
   uint32_t o = dpp_xor1(m);
@@ -455,6 +469,7 @@ __device__ inline void encode_nv(const QuantArgs& a, const float* rtab, const Nv
   float y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = v[i] * rcp;
+  nv_keep_zeros(tiny, v, y);
   if constexpr (!SR) {
     e.w[0] = pack_e2m1_rne(y);
   } else {
@@ -542,7 +557,7 @@ __device__ inline bool nv46_exact_four(const float v[8], uint32_t w6, float dsb6
 }
 
 __device__ inline void encode_nv46(float S, const float* rtab, const NvDiv& d6, const NvDiv& d4,
-                                   const float v[8], Enc<FMT_NVFP4>& e) {
+                                   bool tiny, const float v[8], Enc<FMT_NVFP4>& e) {
 #pragma clang fp contract(off)
   uint32_t m = max_abs_bits(v);
   uint32_t o = dpp_xor1(m);
@@ -559,6 +574,7 @@ __device__ inline void encode_nv46(float S, const float* rtab, const NvDiv& d6, 
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = v[i] * rcp;
+    nv_keep_zeros(tiny, v, y);
     w[k] = pack_e2m1_rne(y);
     const float part = nv_sq_err(v, w[k], dsb, S);
     err[k] = part + dpp_xor1f(part);  // addition commutes: both lanes get the same sum
@@ -591,6 +607,7 @@ __device__ __attribute__((always_inline)) inline void nv1d_wave(const QuantArgs&
   const NvDiv d6 = nv_div(6.0f * S);
   NvDiv d4 = d6;
   if constexpr (F46) d4 = nv_div(4.0f * S);
+  const bool tiny = S < kNvTinyS;
   // q0 is even, so the lane's half of its Hadamard group is lane & 1 in every slab
   SignBits<XDT> sg;
   if constexpr (RHT) sg = rht_sign_bits<XDT>(a.sign_mask, lane & 1u);
@@ -602,8 +619,8 @@ __device__ __attribute__((always_inline)) inline void nv1d_wave(const QuantArgs&
     if constexpr (RHT) apply_signs<XDT>(raw[u], sg);
     widen<XDT>(raw[u], v);
     if constexpr (RHT) rht_forward_signed(v, lane & 1u);
-    if constexpr (F46) encode_nv46(S, rtab, d6, d4, v, enc[u]);
-    else encode_nv<SR>(a, rtab, d6, q, v, enc[u]);
+    if constexpr (F46) encode_nv46(S, rtab, d6, d4, tiny, v, enc[u]);
+    else encode_nv<SR>(a, rtab, d6, tiny, q, v, enc[u]);
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) store_enc<FMT_NVFP4>(a, q0 + 64 * u, Q, lane, 2u, enc[u]);
@@ -668,6 +685,7 @@ __device__ __attribute__((always_inline)) inline void nv2d_wave(const QuantArgs&
   }
   if (wave == 0 && lane == 0) *a.tensor_scale = S;
   const NvDiv d6 = nv_div(6.0f * S);
+  const bool tiny = S < kNvTinyS;
   float v[k2dLoads][8];
   uint32_t m[k2dGroups];
 #pragma unroll
@@ -707,6 +725,7 @@ __device__ __attribute__((always_inline)) inline void nv2d_wave(const QuantArgs&
     float y[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = v[u][j] * rcp;
+    nv_keep_zeros(tiny, v[u], y);
     if constexpr (!SR) {
       w[u] = pack_e2m1_rne(y);
     } else {

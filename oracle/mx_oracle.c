@@ -580,7 +580,9 @@ int mxo_quantize_mx(const void* x, int xdt, int64_t ld, int64_t rows, int64_t co
 /*   S  = T / 2688            (2688 = 6 * 448: largest E2M1 x largest E4M3)  */
 /*   per 16-block: q = a_b / (6*S);  sb = E4M3 RNE of q (saturating)         */
 /*   sb decodes to 0: element codes +-0                                      */
-/*   else r = 1 / (dec(sb) * S);  y_i = x_i * r;  E2M1 (RNE or SR) of y_i.   */
+/*   else r = 1 / (dec(sb) * S);  y_i = x_i * r;  E2M1 (RNE or SR) of y_i,   */
+/*   saturating (y_i = +-Inf gives +-6); x_i = +-0 gives +-0 even when r is  */
+/*   +Inf (0 * Inf has no value).                                            */
 /* Stored: codes, block-scale codes, and S (a decode multiplier: x is        */
 /* recovered as e2m1 * e4m3 * S).                                            */
 /* ------------------------------------------------------------------------ */
@@ -624,7 +626,9 @@ static uint32_t nv_encode_block(const float* v, float ab, float T, float S, floa
     }
   }
   for (int i = 0; i < 16; ++i) {
-    if (rcp == 0.0f) {
+    /* READING: a zero element is +-0 also when r overflows to +Inf (S below
+     * about 2^-119): 0 * Inf has no value, and every finite r gives +-0. */
+    if (rcp == 0.0f || v[i] == 0.0f) {
       codes[i] = signbit(v[i]) ? 0x8u : 0x0u;
     } else {
       float y = v[i] * rcp;

@@ -92,6 +92,42 @@ def test_nvfp4_amax_given_and_zero_tensor():
     assert float(ts[0]) == 1.0 == wts and np.array_equal(c, wc) and np.array_equal(s, ws)
 
 
+@pytest.mark.parametrize("t_exp", [-137, -126, -81, -80, -72, -70, 0, 88, 89, 90, 127])
+def test_nvfp4_given_amax_across_the_divisor_range(t_exp):
+    """A given tensor amax T = 1.75 * 2^t_exp puts the block-scale divisor
+    d = 6 fl(T / 2688) on both sides of the range where the quotient is
+    formed as a corrected product (2^-80 <= d <= 2^80) and at the FP32
+    extremes, with subnormal T, reciprocals that overflow to +Inf and blocks
+    whose maximum lies far below T, at T and (below the FP32 limit) above it.
+    Codes, block scales and the tensor scale match the oracle bit for bit for
+    the 1-D, 2-D and Four Over Six encoders."""
+    T = np.float32(1.75) * np.float32(2.0) ** np.float32(t_exp)
+    assert np.isfinite(T) and T > 0
+    rows, cols = 48, 256
+    rng = np.random.default_rng(t_exp + 200)
+    u = rng.uniform(-1.0, 1.0, size=(rows, cols))
+    shrink = 2.0 ** rng.integers(0, 40, size=(rows, cols // 16))  # per block: 2^0 .. 2^-39 of T
+    u = u / np.repeat(shrink, 16, axis=1)
+    if t_exp < 100:
+        u[::5, 3] = 1.5  # blocks above the given amax: their scale saturates
+    x = (u * np.float64(T)).astype(np.float32)
+    assert np.all(np.isfinite(x))
+    xd = to_gpu_f32(x)
+    for flags, rnd in ((0, 0), (0, 1), (mx.MX_FLAG_BLOCK_2D, 0), (mx.MX_FLAG_BLOCK_2D, 1),
+                       (mx.MX_FLAG_FOUR_OVER_SIX, 0)):
+        out = mx.empty(3, rows, cols, device=dev())
+        amax = torch.full((1,), float(T), dtype=torch.float32, device=dev())
+        mx.mx_quantize(xd, out, rnd, 5, 9, flags | mx.MX_FLAG_AMAX_GIVEN, 0, amax)
+        torch.cuda.synchronize()
+        c, s, ts = host(out)
+        variant = oracle.V_2D if flags == mx.MX_FLAG_BLOCK_2D else (
+            oracle.V_FOUR6 if flags == mx.MX_FLAG_FOUR_OVER_SIX else 0)
+        wc, ws, wts = oracle.quantize(x, 3, rnd, seed=5, counter=9, amax=float(T), variant=variant)
+        assert float(ts[0]) == wts, (t_exp, flags, rnd)
+        assert np.array_equal(s, ws), (t_exp, flags, rnd, np.argwhere(s != ws)[:5])
+        assert np.array_equal(c, wc), (t_exp, flags, rnd, np.argwhere(c != wc)[:5])
+
+
 def test_mx_special_values():
     """All-zero blocks, signed zeros, NaN/Inf blocks, FP32 subnormals, values
     at the saturation limits and exact ties."""

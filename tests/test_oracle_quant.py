@@ -190,6 +190,30 @@ def test_nvfp4_zero_tensor_and_amax_override(orc):
     assert S1 == float(np.float32(2.0) / np.float32(2688.0))
 
 
+def test_nvfp4_tiny_tensor_scale_overflowing_reciprocal(orc):
+    """T = 1.75 * 2^-126 gives S ~ 2^-136.6, so a block whose scale decodes
+    to the smallest E4M3 value has 1 / (e4m3 * S) = +Inf in FP32.  Its nonzero
+    elements become +-Inf and saturate to +-6 (codes 7 / 0xF), and its zero
+    elements keep +-0 (codes 0 / 8) under both roundings."""
+    T = np.float32(1.75) * np.float32(2.0) ** -126
+    S = np.float32(T) / np.float32(2688.0)
+    assert np.isinf(np.float32(1.0) / (np.float32(2.0 ** -9) * S))
+    x = np.zeros((1, 32), np.float32)
+    # block 0: maximum near 2^-9 * 6 S, so its scale code is 1 (2^-9)
+    m = np.float32(6.0 * 2.0 ** -9) * S
+    x[0, 0:4] = [m, -m, np.float32(0.0), np.float32(-0.0)]
+    x[0, 4] = np.float32(m * 0.25)
+    x[0, 16] = T  # block 1 holds the amax
+    for rnd in (orc.RNE, orc.SR):
+        codes, scales, S_out = orc.quantize(x, orc.NVFP4, rnd, seed=1, amax=float(T))
+        assert S_out == float(S)
+        assert scales[0, 0] == 1
+        nib = [(int(codes[0, c // 2]) >> (4 * (c & 1))) & 0xF for c in range(16)]
+        assert nib[0] == 0x7 and nib[1] == 0xF and nib[4] == 0x7  # +-Inf saturates
+        assert nib[2] == 0x0 and nib[3] == 0x8  # signed zeros
+        assert all(n in (0x0, 0x8) for n in nib[5:])  # the other zeros
+
+
 def test_nvfp4_dequant_single_rounding(orc):
     g = np.random.default_rng(13)
     x = g.standard_normal((4, 32)).astype(np.float32)
