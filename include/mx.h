@@ -305,11 +305,12 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
  * FP32-accumulated sum of the exact products of the decoded operands:
  *   MXFP4  scaled FP4 matrix instructions (E8M0 scales inside the instruction);
  *   MXFP8  E4M3 * 2^(c-127) converted to exact BF16 (exact for scale codes c
- *          in [3, 246]), BF16 matrix instructions; a fix-up pass recomputes
- *          every tile holding a code outside that range with each operand's
- *          codes shifted into it by one power of two per tile (exact unless
- *          a tile's codes span more than the range on one side); code 255
- *          gives NaN in its rows / columns;
+ *          in [3, 246]), BF16 matrix instructions, whose products must be
+ *          normal FP32 values (c_A + c_B >= 146); a fix-up pass recomputes
+ *          every tile holding a code outside [73, 246] with each operand's
+ *          codes shifted by one power of two per tile so that both hold
+ *          (exact unless a tile's codes span more than the range on one
+ *          side); code 255 gives NaN in its rows / columns;
  *   NVFP4  e2m1 * e4m3 converted to exact FP16, FP16 matrix instructions
  *          (BF16 for shapes too small for the pipelined kernel), the FP32
  *          result multiplied by S_A * S_B.
@@ -317,18 +318,22 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
  *          K % 512 == 0: scaled FP6/FP4 matrix instructions, which form the
  *          exact sum of each instruction's 64 products (measured on gfx950).
  *          E3M2 x E3M2, which that instruction sums in a narrower window, is
- *          decoded to exact BF16 in the same kernel (scale codes 5 .. 250;
- *          tiles with other codes recomputed by the generic kernel with
- *          shifted codes, as for MXFP8).
+ *          decoded to exact BF16 in the same kernel (scale codes 68 .. 250,
+ *          where the decode is exact and the products are normal FP32
+ *          values; tiles with other codes recomputed by the generic kernel
+ *          with shifted codes, as for MXFP8).
  *   Other pairs of 8-bit types (E4M3, E5M2, INT8: E5M2 x E4M3, INT8 x INT8,
  *          INT8 x E4M3, ...) where the MXFP8 pipeline fits (K % 512 == 0,
  *          M * N >= 2^23): as MXFP8, each element times its scale converted to BF16,
- *          exact for scale codes c in [17, 239] (E5M2) and [7, 254] (INT8);
- *          tiles with other codes are recomputed as for MXFP8.
+ *          exact for scale codes c in [17, 239] (E5M2) and [7, 254] (INT8)
+ *          with normal FP32 products (c_A + c_B >= 128 + g_A + g_B, g
+ *          below); tiles holding a code below half of that bound or outside
+ *          the range are recomputed as for MXFP8.
  *   Other MX pairs (8-bit types mixed with FP6 or FP4, FP6 and 8-bit pairs
  *          at other shapes): every element times its scale decoded to exact
- *          BF16 (exact while the scaled values are normal BF16 values), BF16
- *          matrix instructions.
+ *          BF16, BF16 matrix instructions; a tile holding a code below half
+ *          of 128 + g_A + g_B, or outside the decode's exact range, is
+ *          computed with shifted codes as in the MXFP8 fix-up.
  * The scaled matrix instructions (MXFP4, FP6 pairs, MX_GEMM_FP8_NATIVE) form
  * the exact sum of their scaled products and round it once into FP32,
  * subnormals included (measured), so the bound holds while every product is
@@ -336,10 +341,12 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
  * 1, E2M3 3, E3M2 4, E4M3 9, E5M2 16), which gives c_A + c_B >= 105 + g(A) +
  * g(B) (MXFP4 pairs 107).  The tile-layout paths (MXFP4 and native FP8 on
  * MX_LAYOUT_TILED operands, mx_gemm_quantize) detect tiles whose scale codes
- * could pair below that and compute them again with raised codes, so they
- * meet the bound for every finite code; the row-layout MXFP4 and the FP6-pair
- * paths meet it only above the threshold.  Scale code 255 (NaN) gives NaN in
- * exactly the output rows / columns whose blocks carry it.
+ * could pair below that and compute them again with raised codes; the
+ * row-layout MXFP4 and FP6-pair kernels are followed by a fix-up pass that
+ * recomputes every tile holding a code below half of that bound (rounded
+ * up) with shifted codes.  So every path meets the bound for every finite
+ * code whose tile one shift per operand fits into range.  Scale code 255
+ * (NaN) gives NaN in exactly the output rows / columns whose blocks carry it.
  * Requirements: A->fmt == B->fmt, or both MX formats (E8M0 scales) in the
  * row layout; A->cols == B->cols == K; K % 32 == 0. */
 mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,

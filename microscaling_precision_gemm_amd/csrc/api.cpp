@@ -334,10 +334,22 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
                                                B->fmt, static_cast<const uint8_t*>(B->codes), B->scales,
                                                A->rows, B->rows, A->cols, C, cdt, ldc,
                                                reinterpret_cast<hipStream_t>(stream)));
-    return hip_status(mxk::launch_gemm_mx_any(A->fmt, static_cast<const uint8_t*>(A->codes), A->scales,
-                                              B->fmt, static_cast<const uint8_t*>(B->codes), B->scales,
-                                              A->rows, B->rows, A->cols, C, cdt, ldc,
-                                              reinterpret_cast<hipStream_t>(stream)));
+    {
+      // the generic kernel decodes to BF16: a tile is computed as it is when
+      // every code lies in the conversions' exact range and every pair of
+      // codes puts the products at normal FP32 values (c_A + c_B >= 128 +
+      // g_A + g_B, elements multiples of 2^-g), else with shifted codes
+      auto grid = [](int32_t f) {
+        return f == MX_MXFP8_E4M3 ? 9u : f == MX_MXFP8_E5M2 ? 16u : f == MX_MXINT8 ? 6u
+               : f == MX_MXFP6_E3M2 ? 4u : f == MX_MXFP6_E2M3 ? 3u : 1u;
+      };
+      const uint32_t lo = (128u + grid(A->fmt) + grid(B->fmt) + 1u) / 2u;
+      const uint32_t hi = (A->fmt == MX_MXINT8 && B->fmt == MX_MXINT8) ? 254u : 239u;
+      return hip_status(mxk::launch_gemm_mx_any(A->fmt, static_cast<const uint8_t*>(A->codes), A->scales,
+                                                B->fmt, static_cast<const uint8_t*>(B->codes), B->scales,
+                                                A->rows, B->rows, A->cols, C, cdt, ldc,
+                                                reinterpret_cast<hipStream_t>(stream), lo, hi, true));
+    }
   }
   if ((flags & MX_GEMM_FP8_NATIVE) && A->fmt != MX_MXFP8_E4M3) return MX_ERR_UNSUPPORTED;
   if (A->cols != B->cols || A->cols % 32) return MX_ERR_SHAPE;

@@ -121,16 +121,17 @@ __device__ inline bool ls_shift(int min_a, int max_a, int min_b, int max_b, int 
   return true;
 }
 
-// Smallest and largest codes (255 left out) of two runs of 16-byte scale
-// words, over a whole workgroup of 256 threads (red: 16 words of LDS); the
-// result is uniform.
+// Smallest and largest codes (255 left out) of two runs of scale bytes (na,
+// nb bytes from 16-byte aligned pa, pb: whole 16-byte words, then the last
+// bytes one by one), over a whole workgroup of 256 threads (red: 16 words of
+// LDS); the result is uniform.
 __device__ inline void ls_tile_ranges(const uint8_t* pa, int64_t na, const uint8_t* pb, int64_t nb,
                                       uint32_t* red, int* min_a, int* max_a, int* min_b, int* max_b) {
   uint32_t r[4] = {255u, 0u, 255u, 0u};  // min A, max A, min B, max B
   for (int op = 0; op < 2; ++op) {
     const uint8_t* p = op ? pb : pa;
     const int64_t n = op ? nb : na;
-    for (int64_t q = threadIdx.x; q < n; q += 256) {
+    for (int64_t q = threadIdx.x; q < (n >> 4); q += 256) {
       const uint4 v = reinterpret_cast<const uint4*>(p)[q];
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
       for (int e = 0; e < 16; ++e) {
@@ -139,6 +140,12 @@ __device__ inline void ls_tile_ranges(const uint8_t* pa, int64_t na, const uint8
         r[2 * op] = c < r[2 * op] ? c : r[2 * op];
         r[2 * op + 1] = c > r[2 * op + 1] ? c : r[2 * op + 1];
       }
+    }
+    for (int64_t q = (n & ~(int64_t)15) + threadIdx.x; q < n; q += 256) {
+      const uint32_t c = p[q];
+      if (c == 0xFFu) continue;
+      r[2 * op] = c < r[2 * op] ? c : r[2 * op];
+      r[2 * op + 1] = c > r[2 * op + 1] ? c : r[2 * op + 1];
     }
   }
   const uint32_t lane = threadIdx.x & 63u, wid = threadIdx.x >> 6;

@@ -187,151 +187,178 @@ __device__ __attribute__((always_inline)) inline void load_unit(int bits, const 
 
 // Thread t stages, per step, the units t + 256 j: row (t + 256 j) / 2 of the
 // stacked [A tile; B tile] rows, K half t % 2 -- j < U/2 are A rows.
-// fix_lo > 0: the workgroup first scans the scale rows of its tile and
-// computes the tile only if one holds a code outside [fix_lo, fix_hi]
-// (K % 512 == 0: 16-byte scale loads) -- the fix-up pass behind a kernel that
-// is exact only for codes in that range.
+// fix_lo > 0: the workgroup first scans the scale rows of its tile (fix-up
+// mode: of its 2 x 2 tiles) for a code outside [fix_lo, fix_hi]; if there is
+// one it computes them with shifted codes (below), else it computes them as
+// they are when `every`, or leaves them -- the fix-up pass behind a kernel
+// that is exact only for codes in that range.
 template <int CDT, int T>
 __global__ __launch_bounds__(256) void k_gemm_mx_any(int fa, int fb, const uint8_t* __restrict__ A,
                                                      const uint8_t* __restrict__ SA,
                                                      const uint8_t* __restrict__ B,
                                                      const uint8_t* __restrict__ SB, int64_t M, int64_t N,
                                                      int64_t K, void* __restrict__ C, int64_t ldc,
-                                                     uint32_t tiles_n, uint32_t fix_lo, uint32_t fix_hi) {
+                                                     uint32_t tiles_n, uint32_t fix_lo, uint32_t fix_hi,
+                                                     bool every) {
   constexpr int U = 2 * T * 2 / 256;  // units per thread and step (2 or 4)
   constexpr int F = T / 64;           // 32 x 32 instruction tiles per wave and dimension
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * T * kPitch];
-  const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * T, n0 = (int64_t)(blockIdx.x % tiles_n) * T;
+  // Fix-up mode (fix_lo > 0, not every): one workgroup per region of 2 x 2
+  // tiles, whose scale rows it scans once; otherwise one per tile.
+  const int span = (fix_lo > 0 && !every) ? 2 : 1;
+  const int64_t r0 = (int64_t)(blockIdx.x / tiles_n) * T * span, c0 = (int64_t)(blockIdx.x % tiles_n) * T * span;
   const uint32_t t = threadIdx.x, lane = t & 63u, wid = t >> 6;
   int shift_a = 0, shift_b = 0;  // the fix-up mode's code shifts
   if (fix_lo > 0) {
     __shared__ uint32_t found;
     if (t == 0) found = 0u;
     __syncthreads();
-    // The scale rows of the tile's A rows (and of its B rows) are one
-    // contiguous run of rows * K/32 bytes, a multiple of 16: read as
-    // consecutive 16-byte words by consecutive lanes.
-    const int64_t kbytes = K / 32;
-    const int64_t na = (M - m0 < T ? M - m0 : T) * kbytes, nb = (N - n0 < T ? N - n0 : T) * kbytes;
-    const uint8_t* pa = SA + m0 * kbytes;
-    const uint8_t* pb = SB + n0 * kbytes;
+    // The scale rows of the region's A rows (and of its B rows) are one
+    // contiguous run of rows * K/32 bytes, 16-byte aligned (the scale arrays
+    // are, and 128 rows of K/32 bytes are a multiple of 16): read as
+    // consecutive 16-byte words by consecutive lanes, then the last bytes
+    // one by one.
+    const int64_t kbytes = K / 32, R = (int64_t)span * T;
+    const int64_t na = (M - r0 < R ? M - r0 : R) * kbytes, nb = (N - c0 < R ? N - c0 : R) * kbytes;
+    const uint8_t* pa = SA + r0 * kbytes;
+    const uint8_t* pb = SB + c0 * kbytes;
     uint32_t sp = 0u;
-    for (int64_t q = 16 * (int64_t)t; q < na; q += 16 * 256) {
-      const uint4 v = *reinterpret_cast<const uint4*>(pa + q);
-      sp |= bytes_outside(v.x, fix_lo, fix_hi) | bytes_outside(v.y, fix_lo, fix_hi) |
-            bytes_outside(v.z, fix_lo, fix_hi) | bytes_outside(v.w, fix_lo, fix_hi);
-    }
-    for (int64_t q = 16 * (int64_t)t; q < nb; q += 16 * 256) {
-      const uint4 v = *reinterpret_cast<const uint4*>(pb + q);
-      sp |= bytes_outside(v.x, fix_lo, fix_hi) | bytes_outside(v.y, fix_lo, fix_hi) |
-            bytes_outside(v.z, fix_lo, fix_hi) | bytes_outside(v.w, fix_lo, fix_hi);
+    const uint32_t pad = fix_lo * 0x01010101u;  // a word of codes inside the range
+    for (int op = 0; op < 2; ++op) {
+      const uint8_t* p = op ? pb : pa;
+      const int64_t n = op ? nb : na;
+      // 8 loads in flight per lane
+      for (int64_t q0 = 16 * (int64_t)t; q0 + 16 <= n; q0 += 16 * 256 * 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t q = q0 + 16 * 256 * u;
+          v[u] = q + 16 <= n ? *reinterpret_cast<const uint4*>(p + q) : make_uint4(pad, pad, pad, pad);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          sp |= bytes_outside(v[u].x, fix_lo, fix_hi) | bytes_outside(v[u].y, fix_lo, fix_hi) |
+                bytes_outside(v[u].z, fix_lo, fix_hi) | bytes_outside(v[u].w, fix_lo, fix_hi);
+      }
+      // a lone byte, padded with codes inside the range in the other bytes
+      for (int64_t q = (n & ~(int64_t)15) + t; q < n; q += 256)
+        sp |= bytes_outside((pad & 0xFFFFFF00u) | p[q], fix_lo, fix_hi);
     }
     if (sp) atomicOr(&found, 1u);
     __syncthreads();
-    if (found == 0u) return;  // uniform
-    // The tile is recomputed.  Its codes are shifted, A's by shift_a and B's
-    // by shift_b, into the range the hardware conversions take exactly (17 ..
-    // 239; INT8's software decode 7 .. 254) when one shift per operand fits
-    // them all there with every product on FP32's 2^-149 grid and no sum
-    // beyond 2^127; the result is scaled back with one rounding.  Else the
-    // codes are decoded as they are.
-    __shared__ uint32_t red[16];
-    int mna, mxa, mnb, mxb;
-    ls_tile_ranges(pa, na / 16, pb, nb / 16, red, &mna, &mxa, &mnb, &mxb);
-    const int la = fa == FMT_MXINT8 ? 7 : 17, ha = fa == FMT_MXINT8 ? 254 : 239;
-    const int lb = fb == FMT_MXINT8 ? 7 : 17, hb = fb == FMT_MXINT8 ? 254 : 239;
-    if (!ls_shift(mna, mxa, mnb, mxb, la, ha, lb, hb, fmt_grid(fa), fmt_grid(fb), fmt_top(fa), fmt_top(fb), K,
-                  &shift_a, &shift_b))
-      shift_a = shift_b = 0;
-  }
-  const uint32_t wm = wid >> 1, wn = wid & 1u;
-  const int ba = code_bits(fa), bb = code_bits(fb);
-  const int64_t rba = K * ba / 8, rbb = K * bb / 8, kb = K / 32;
-  const uint32_t h = t & 1u;
-  const uint8_t* crow[U];
-  const uint8_t* srow[U];
-  bool ok[U];
-  uint32_t dst[U];
-#pragma unroll
-  for (int j = 0; j < U; ++j) {
-    const uint32_t r = (t + 256u * j) >> 1;  // stacked row: A rows 0 .. T-1, then B rows
-    dst[j] = r * kPitch + h * 64;
-    if (j < U / 2) {
-      const int64_t ra = m0 + r;
-      ok[j] = ra < M;
-      crow[j] = A + (ok[j] ? ra : 0) * rba;
-      srow[j] = SA + (ok[j] ? ra : 0) * kb;
+    if (found == 0u) {  // uniform
+      if (!every) return;
     } else {
-      const int64_t rb = n0 + (r - T);
-      ok[j] = rb < N;
-      crow[j] = B + (ok[j] ? rb : 0) * rbb;
-      srow[j] = SB + (ok[j] ? rb : 0) * kb;
+      // The tile is computed with its codes shifted, A's by shift_a and B's
+      // by shift_b, into the range the hardware conversions take exactly (17
+      // .. 239; INT8's software decode 7 .. 254) when one shift per operand
+      // fits them all there with every product a normal FP32 value and no
+      // sum beyond 2^127; the result is scaled back with one rounding.  Else
+      // the codes are decoded as they are.
+      __shared__ uint32_t red[16];
+      int mna, mxa, mnb, mxb;
+      ls_tile_ranges(pa, na, pb, nb, red, &mna, &mxa, &mnb, &mxb);
+      const int la = fa == FMT_MXINT8 ? 7 : 17, ha = fa == FMT_MXINT8 ? 254 : 239;
+      const int lb = fb == FMT_MXINT8 ? 7 : 17, hb = fb == FMT_MXINT8 ? 254 : 239;
+      if (!ls_shift(mna, mxa, mnb, mxb, la, ha, lb, hb, fmt_grid(fa), fmt_grid(fb), fmt_top(fa), fmt_top(fb), K,
+                    &shift_a, &shift_b))
+        shift_a = shift_b = 0;
     }
   }
-  const int64_t steps = (K + kStepK - 1) / kStepK;
-
-  Unit un[U];
-  auto load = [&](int64_t st) {
-    const int64_t k0 = st * kStepK + h * 32;  // K % 32 == 0: a unit is all in or out
+  // the region's tiles (one outside the fix-up mode); the barrier that ends
+  // a tile's last step also ends every LDS read before the next tile's stores
+  for (int sub = 0; sub < span * span; ++sub) {
+    const int64_t m0 = r0 + (int64_t)(sub / span) * T, n0 = c0 + (int64_t)(sub % span) * T;
+    if (m0 >= M || n0 >= N) continue;  // uniform
+    const uint32_t wm = wid >> 1, wn = wid & 1u;
+    const int ba = code_bits(fa), bb = code_bits(fb);
+    const int64_t rba = K * ba / 8, rbb = K * bb / 8, kb = K / 32;
+    const uint32_t h = t & 1u;
+    const uint8_t* crow[U];
+    const uint8_t* srow[U];
+    bool ok[U];
+    uint32_t dst[U];
 #pragma unroll
-    for (int j = 0; j < U; ++j) load_unit(j < U / 2 ? ba : bb, crow[j], srow[j], k0, ok[j] && k0 < K, un[j]);
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < U; ++j)
-      decode_store_any(j < U / 2 ? fa : fb, un[j], &lds[buf][dst[j]], j < U / 2 ? shift_a : shift_b);
-  };
-
-  v16f acc[F][F];
-#pragma unroll
-  for (int i = 0; i < F; ++i)
-#pragma unroll
-    for (int j = 0; j < F; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  load(0);
-  store(0);
-  __syncthreads();
-  const uint32_t lr = lane & 31u, lg = lane >> 5;
-  for (int64_t st = 0; st < steps; ++st) {
-    const int buf = (int)(st & 1);
-    if (st + 1 < steps) load(st + 1);
-    const uint8_t* L = lds[buf];
-#pragma unroll
-    for (int kk = 0; kk < kStepK / 16; ++kk) {
-      const uint32_t off = (kk * 16 + lg * 8) * 2;
-      v8bf af[F], bfr[F];
-#pragma unroll
-      for (int i = 0; i < F; ++i)
-        af[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(L + (wm * (T / 2) + i * 32 + lr) * kPitch + off));
-#pragma unroll
-      for (int j = 0; j < F; ++j)
-        bfr[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(L + (T + wn * (T / 2) + j * 32 + lr) * kPitch + off));
-#pragma unroll
-      for (int i = 0; i < F; ++i)
-#pragma unroll
-        for (int j = 0; j < F; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (st + 1 < steps) store(buf ^ 1);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int i = 0; i < F; ++i)
-#pragma unroll
-    for (int j = 0; j < F; ++j) {
-      const int64_t col = n0 + wn * (T / 2) + j * 32 + lr;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm * (T / 2) + i * 32 + 8 * (v / 4) + 4 * lg + (v % 4);
-        if (row < M && col < N) {
-          const float val = __builtin_amdgcn_ldexpf(acc[i][j][v], -(shift_a + shift_b));  // exact at shift 0
-          if constexpr (CDT == DT_F32) static_cast<float*>(C)[row * ldc + col] = val;
-          else static_cast<uint16_t*>(C)[row * ldc + col] = f32_to_bf16(val);
-        }
+    for (int j = 0; j < U; ++j) {
+      const uint32_t r = (t + 256u * j) >> 1;  // stacked row: A rows 0 .. T-1, then B rows
+      dst[j] = r * kPitch + h * 64;
+      if (j < U / 2) {
+        const int64_t ra = m0 + r;
+        ok[j] = ra < M;
+        crow[j] = A + (ok[j] ? ra : 0) * rba;
+        srow[j] = SA + (ok[j] ? ra : 0) * kb;
+      } else {
+        const int64_t rb = n0 + (r - T);
+        ok[j] = rb < N;
+        crow[j] = B + (ok[j] ? rb : 0) * rbb;
+        srow[j] = SB + (ok[j] ? rb : 0) * kb;
       }
     }
+    const int64_t steps = (K + kStepK - 1) / kStepK;
+
+    Unit un[U];
+    auto load = [&](int64_t st) {
+      const int64_t k0 = st * kStepK + h * 32;  // K % 32 == 0: a unit is all in or out
+#pragma unroll
+      for (int j = 0; j < U; ++j) load_unit(j < U / 2 ? ba : bb, crow[j], srow[j], k0, ok[j] && k0 < K, un[j]);
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+        decode_store_any(j < U / 2 ? fa : fb, un[j], &lds[buf][dst[j]], j < U / 2 ? shift_a : shift_b);
+    };
+
+    v16f acc[F][F];
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+      for (int j = 0; j < F; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    load(0);
+    store(0);
+    __syncthreads();
+    const uint32_t lr = lane & 31u, lg = lane >> 5;
+    for (int64_t st = 0; st < steps; ++st) {
+      const int buf = (int)(st & 1);
+      if (st + 1 < steps) load(st + 1);
+      const uint8_t* L = lds[buf];
+#pragma unroll
+      for (int kk = 0; kk < kStepK / 16; ++kk) {
+        const uint32_t off = (kk * 16 + lg * 8) * 2;
+        v8bf af[F], bfr[F];
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+          af[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(L + (wm * (T / 2) + i * 32 + lr) * kPitch + off));
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+          bfr[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(L + (T + wn * (T / 2) + j * 32 + lr) * kPitch + off));
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+#pragma unroll
+          for (int j = 0; j < F; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+      if (st + 1 < steps) store(buf ^ 1);
+      __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+      for (int j = 0; j < F; ++j) {
+        const int64_t col = n0 + wn * (T / 2) + j * 32 + lr;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = m0 + wm * (T / 2) + i * 32 + 8 * (v / 4) + 4 * lg + (v % 4);
+          if (row < M && col < N) {
+            const float val = __builtin_amdgcn_ldexpf(acc[i][j][v], -(shift_a + shift_b));  // exact at shift 0
+            if constexpr (CDT == DT_F32) static_cast<float*>(C)[row * ldc + col] = val;
+            else static_cast<uint16_t*>(C)[row * ldc + col] = f32_to_bf16(val);
+          }
+        }
+      }
+  }
 }
 
 }  // namespace
@@ -339,17 +366,18 @@ __global__ __launch_bounds__(256) void k_gemm_mx_any(int fa, int fb, const uint8
 hipError_t launch_gemm_mx_any(int fa, const uint8_t* a_codes, const uint8_t* a_scales, int fb,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
                               int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s, uint32_t fix_lo,
-                              uint32_t fix_hi) {
+                              uint32_t fix_hi, bool every) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (fix_lo > 0 && (K % 512 != 0 || fix_lo > 128 || fix_hi < 127 || fix_hi > 254)) return hipErrorInvalidValue;
+  if (fix_lo > 0 && (fix_lo > 128 || fix_hi < 127 || fix_hi > 254)) return hipErrorInvalidValue;
   // 128 x 128 tiles, two workgroups per CU: with 256 x 256 tiles the six
   // inlined decoders of four units per thread spill registers
   constexpr int64_t T = 128;
-  const uint32_t tm = (uint32_t)((M + T - 1) / T), tn = (uint32_t)((N + T - 1) / T);
+  const int64_t R = (fix_lo > 0 && !every) ? 2 * T : T;  // the kernel's span
+  const uint32_t tm = (uint32_t)((M + R - 1) / R), tn = (uint32_t)((N + R - 1) / R);
   if ((uint64_t)tm * tn > 0x7FFFFFFFull) return hipErrorInvalidValue;
 #define MXK_ANY(D, TT)                                                                                    \
   hipLaunchKernelGGL((k_gemm_mx_any<D, TT>), dim3(tm * tn), dim3(256), 0, s, fa, fb, a_codes, a_scales, b_codes, \
-                     b_scales, M, N, K, C, ldc, tn, fix_lo, fix_hi)
+                     b_scales, M, N, K, C, ldc, tn, fix_lo, fix_hi, every)
   if (cdt == DT_F32) MXK_ANY(DT_F32, 128);
   else MXK_ANY(DT_BF16, 128);
 #undef MXK_ANY

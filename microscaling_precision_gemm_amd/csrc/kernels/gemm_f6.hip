@@ -408,19 +408,21 @@ hipError_t launch_gemm_mx_f6(int fa, const uint8_t* a_codes, const uint8_t* a_sc
   if (M == 0 || N == 0) return hipSuccess;
   const int ta = f6_type(fa), tb = f6_type(fb);
   if (ta == kE3M2 && tb == kE3M2) {
-    // decoded to BF16 (see mfma_slice), exact for scale codes 5 .. 250; then
-    // the tiles whose operands hold another code recomputed by the generic
-    // kernel's fix-up mode
+    // decoded to BF16 (see mfma_slice), exact for scale codes 5 .. 250 whose
+    // products are normal FP32 values (c_A + c_B >= 128 + 4 + 4: codes of at
+    // least 68); the tiles whose operands hold another code are recomputed
+    // by the generic kernel's fix-up mode
     const hipError_t e = cdt == DT_F32
                              ? launch_f6<kE3M2, kE3M2, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s)
                              : launch_f6<kE3M2, kE3M2, DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
     if (e != hipSuccess) return e;
-    return launch_gemm_mx_any(fa, a_codes, a_scales, fb, b_codes, b_scales, M, N, K, C, cdt, ldc, s, 5u, 250u);
+    return launch_gemm_mx_any(fa, a_codes, a_scales, fb, b_codes, b_scales, M, N, K, C, cdt, ldc, s, 68u, 250u);
   }
+  hipError_t e = hipErrorInvalidValue;
 #define MXK_F6(A_, B_)                                                                                   \
   if (ta == A_ && tb == B_)                                                                              \
-    return cdt == DT_F32 ? launch_f6<A_, B_, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s) \
-                         : launch_f6<A_, B_, DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
+    e = cdt == DT_F32 ? launch_f6<A_, B_, DT_F32>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s) \
+                      : launch_f6<A_, B_, DT_BF16>(a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, s);
   MXK_F6(kE2M3, kE2M3)
   MXK_F6(kE2M3, kE3M2)
   MXK_F6(kE3M2, kE2M3)
@@ -429,7 +431,16 @@ hipError_t launch_gemm_mx_f6(int fa, const uint8_t* a_codes, const uint8_t* a_sc
   MXK_F6(kE3M2, kE2M1)
   MXK_F6(kE2M1, kE3M2)
 #undef MXK_F6
-  return hipErrorInvalidValue;
+  if (e != hipSuccess) return e;
+  // The scaled instruction rounds the exact sum of its products once into
+  // FP32, so it is exact while every product is a multiple of 2^-149:
+  // c_A + c_B >= 105 + g(A) + g(B), with elements multiples of 2^-g (E2M3 3,
+  // E3M2 4, E2M1 1).  Tiles whose operands hold a code below half of that
+  // (or 255) are recomputed by the generic kernel's fix-up mode.
+  auto grid = [](int t) { return t == kE2M3 ? 3u : (t == kE3M2 ? 4u : 1u); };
+  const uint32_t thr = 105u + grid(ta) + grid(tb);
+  return launch_gemm_mx_any(fa, a_codes, a_scales, fb, b_codes, b_scales, M, N, K, C, cdt, ldc, s,
+                            (thr + 1u) / 2u, 254u);
 }
 
 }  // namespace mxk

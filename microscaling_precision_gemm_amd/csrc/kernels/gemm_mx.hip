@@ -822,11 +822,21 @@ hipError_t run(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint
   // K a multiple of 512: whole steps and whole 16-byte scale periods per row
   const bool pipe = fits32 && K > 0 && (K % 512 == 0) &&
                     M * N >= (int64_t)kTile * kTile * 128;
-  if (pipe) return launch_pipe<FMT, CDT, TA, TB>(a, sa, b, sb, M, N, K, C, ldc, s);
-  const uint32_t tm = (uint32_t)((M + 127) / 128), tn = (uint32_t)((N + 127) / 128);
-  hipLaunchKernelGGL((k_gemm_mx_simple<FMT, CDT, TA, TB>), dim3(tm * tn), dim3(256), 0, s, a, sa, b, sb,
-                     M, N, K, C, ldc, tm, tn);
-  return hipGetLastError();
+  hipError_t e;
+  if (pipe) {
+    e = launch_pipe<FMT, CDT, TA, TB>(a, sa, b, sb, M, N, K, C, ldc, s);
+  } else {
+    const uint32_t tm = (uint32_t)((M + 127) / 128), tn = (uint32_t)((N + 127) / 128);
+    hipLaunchKernelGGL((k_gemm_mx_simple<FMT, CDT, TA, TB>), dim3(tm * tn), dim3(256), 0, s, a, sa, b, sb,
+                       M, N, K, C, ldc, tm, tn);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess || FMT != FMT_MXFP4) return e;
+  // MXFP4 x MXFP4: the scaled instruction is exact while every product is a
+  // multiple of 2^-149, i.e. c_A + c_B >= 107 (E2M1 elements are multiples
+  // of 2^-1).  Tiles whose operands hold a code below 54 (or 255) are
+  // recomputed by the generic kernel's fix-up mode.
+  return launch_gemm_mx_any(FMT_MXFP4, a, sa, FMT_MXFP4, b, sb, M, N, K, C, CDT, ldc, s, 54u, 254u);
 }
 
 }  // namespace

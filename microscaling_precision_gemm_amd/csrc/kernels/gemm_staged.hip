@@ -147,9 +147,19 @@ constexpr int kGrid = F == FMT_MXFP8_E5M2 ? 16 : F == FMT_MXINT8 ? 6 : 9;
 template <int F>
 constexpr int kTop = F == FMT_MXFP8_E5M2 ? 16 : F == FMT_MXINT8 ? 1 : 9;
 
+// Lowest scale code of an F operand (against a G operand) whose tiles the
+// pipelined kernel computes exactly: inside the conversion range, and at
+// least half of 128 + g_F + g_G (rounded up), so that every nonzero product
+// of two such codes is a normal FP32 value (the BF16 instruction is not
+// relied on for subnormal products).
+template <int F, int G>
+constexpr uint32_t kScanLo = kExactLo<F> > (128u + kGrid<F> + kGrid<G> + 1u) / 2u
+                                 ? kExactLo<F>
+                                 : (128u + kGrid<F> + kGrid<G> + 1u) / 2u;
+
 // FIXUP (MXFP8, K % 512 == 0): the workgroup first scans the scale rows of
 // its tile and computes the tile only if one holds a code outside the range
-// the pipelined exact 8-bit kernel converts exactly (kExactLo .. kExactHi of
+// the pipelined exact 8-bit kernel computes exactly (kScanLo .. kExactHi of
 // the operand's element type; 255, NaN, always); the output of that kernel
 // for such tiles is overwritten.  BA / BB: the element types of A and B for
 // MXFP8 units (FMT_MXFP8, FMT_MXFP8_E5M2 or FMT_MXINT8).
@@ -224,8 +234,8 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
       for (int u = 0; u < 8; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          sp |= bytes_outside(v[u][e], kExactLo<BA>, kExactHi<BA>) |
-                bytes_outside(v[8 + u][e], kExactLo<BB>, kExactHi<BB>);
+          sp |= bytes_outside(v[u][e], kScanLo<BA, BB>, kExactHi<BA>) |
+                bytes_outside(v[8 + u][e], kScanLo<BB, BA>, kExactHi<BB>);
     }
     const bool wave_found = __builtin_amdgcn_ballot_w64(sp != 0u) != 0;
     if ((t & 63u) == 0) found[t >> 6] = wave_found ? 1u : 0u;
@@ -238,8 +248,8 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
     // than the range) they are decoded as they are.
     __shared__ uint32_t red[16];
     int mna, mxa, mnb, mxb;
-    ls_tile_ranges(reinterpret_cast<const uint8_t*>(pa), ca, reinterpret_cast<const uint8_t*>(pb), cb, red, &mna,
-                   &mxa, &mnb, &mxb);
+    ls_tile_ranges(reinterpret_cast<const uint8_t*>(pa), 16 * ca, reinterpret_cast<const uint8_t*>(pb), 16 * cb,
+                   red, &mna, &mxa, &mnb, &mxb);
     if (!ls_shift(mna, mxa, mnb, mxb, (int)kExactLo<BA>, (int)kExactHi<BA>, (int)kExactLo<BB>, (int)kExactHi<BB>,
                   kGrid<BA>, kGrid<BB>, kTop<BA>, kTop<BB>, K, &bias_a, &bias_b))
       bias_a = bias_b = 0;
@@ -465,9 +475,15 @@ hipError_t launch_gemm_mxfp8_exact(const uint8_t* a_codes, const uint8_t* a_scal
   }
   // pairs other than E4M3 x E4M3 take this path only where the pipeline fits
   if (fa != FMT_MXFP8 || fb != FMT_MXFP8) return hipErrorInvalidValue;
-  if (cdt == DT_F32)
-    return run_sized<FMT_MXFP8, DT_F32, false>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
-  return run_sized<FMT_MXFP8, DT_BF16, false>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
+  const hipError_t e =
+      cdt == DT_F32
+          ? run_sized<FMT_MXFP8, DT_F32, false>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s)
+          : run_sized<FMT_MXFP8, DT_BF16, false>(a_codes, a_scales, nullptr, nullptr, M, M, b_codes, b_scales, nullptr, 1, nullptr, N, K, C, ldc, s);
+  if (e != hipSuccess) return e;
+  // tiles with a code below kScanLo (products that could be subnormal FP32
+  // values) or above the generic kernel's exact range, recomputed there
+  return launch_gemm_mx_any(FMT_MXFP8, a_codes, a_scales, FMT_MXFP8, b_codes, b_scales, M, N, K, C, cdt, ldc, s,
+                            kScanLo<FMT_MXFP8, FMT_MXFP8>, 239u);
 }
 
 }  // namespace mxk

@@ -90,13 +90,15 @@ hipError_t launch_gemm_mx(int fmt, const uint8_t* a_codes, const uint8_t* a_scal
 // A and B in the tiled layout (M, N multiples of 32, K of 1024)
 // C = A * B^T for any pair of MX formats (E8M0 scales; row layout), exact
 // BF16 staging (gemm_any.hip).
-// fix_lo > 0: fix-up mode -- only the 128 x 128 tiles whose operand rows hold
-// a scale code outside [fix_lo, fix_hi] are computed (K % 512 == 0), the
-// others are left as they are.
+// fix_lo > 0: the 128 x 128 tiles whose operand rows hold a scale code
+// outside [fix_lo, fix_hi] are computed with the codes shifted into the exact
+// range where one shift per operand allows; the others are computed as they
+// are when `every`, else left as they are (the fix-up pass behind another
+// kernel).
 hipError_t launch_gemm_mx_any(int fa, const uint8_t* a_codes, const uint8_t* a_scales, int fb,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
                               int64_t K, void* C, int cdt, int64_t ldc, hipStream_t s, uint32_t fix_lo = 0,
-                              uint32_t fix_hi = 254);
+                              uint32_t fix_hi = 254, bool every = false);
 // MX pairs with an FP6 operand (E2M3/E3M2 against E2M3/E3M2/E2M1, not E3M2 x
 // E3M2) on the scaled FP6/FP4 instruction (gemm_f6.hip); shapes it takes.
 bool gemm_mx_f6_fits(int fa, int fb, int64_t M, int64_t N, int64_t K);

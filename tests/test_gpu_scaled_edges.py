@@ -212,3 +212,49 @@ def test_exact_8bit_pipeline_clean_operands_k4096(fa, fb):
         sb = g.integers(112, 126, (N, K // 32)).astype(np.uint8)
         got, Cw, tol = _run(fa, fb, ca, sa, cb, sb, M, N, K, False, "f32")
         check_gemm(got, Cw, tol, False, f"fa={fa} fb={fb} K={K}")
+
+
+# Row-layout paths: the scaled instruction (MXFP4 on the pipelined and the
+# simple kernel, FP6 pairs) and the kernels that decode to BF16 (E3M2 x E3M2,
+# the exact 8-bit pipeline, the generic kernel for other pairs).
+ROW_CASES = [
+    (2, 2, 512, 512, 2048),     # MXFP4, simple kernel
+    (2, 2, 320, 288, 1056),     # MXFP4, simple kernel, K/32 not a multiple of 16
+    (2, 2, 2048, 4096, 1024),   # MXFP4, pipelined kernel
+    (7, 7, 512, 512, 2048),     # FP6 pairs on the scaled instruction
+    (7, 2, 512, 512, 2048),
+    (6, 2, 512, 512, 2048),
+    (2, 7, 512, 512, 1024),
+    (6, 6, 512, 512, 2048),     # E3M2 x E3M2, decoded to BF16
+    (1, 1, 320, 288, 1024),     # MXFP8, small-shape kernel
+    (1, 1, 2048, 4096, 1024),   # exact 8-bit pipeline
+    (5, 1, 2048, 4096, 1024),
+    (4, 4, 2048, 4096, 1024),
+    (1, 2, 320, 288, 1024),     # generic kernel (8-bit x FP4)
+]
+
+
+@pytest.mark.parametrize("fa,fb,M,N,K", ROW_CASES)
+@pytest.mark.parametrize("pattern", ["rows", "tile"])
+def test_row_layout_products_below_fp32_spacing(fa, fb, M, N, K, pattern):
+    """Row layout, every exact path: scale codes inside each kernel's
+    conversion range whose pairs put products below FP32's subnormal spacing
+    (c_A + c_B < 105 + g_A + g_B), as whole rows among ordinary rows or as a
+    whole 256 x 256 output tile.  FP32 out, checked in full as the FP32
+    rounding of a value within the bound."""
+    g = np.random.default_rng(fa * 1000 + fb * 100 + K // 32 + (5 if pattern == "tile" else 0))
+    ca, cb = _codes(g, fa, M, K), _codes(g, fb, N, K)
+    thr = _grid_threshold(fa, fb) if fa in (1, 5, 7, 6, 2) and fb in (1, 5, 7, 6, 2) else 117
+    sa = g.integers(115, 135, (M, K // 32)).astype(np.uint8)
+    sb = g.integers(115, 135, (N, K // 32)).astype(np.uint8)
+    lo = 20 if fa not in (1, 4, 5, 6) else 25  # inside every kernel's conversion range
+    if pattern == "rows":
+        for r in (0, 5, M - 1):
+            sa[r] = g.integers(lo, lo + 15, K // 32)
+        for r in (1, 5, N - 2):
+            sb[r] = g.integers(thr - lo - 30, thr - lo - 15, K // 32)
+    else:
+        sa[:256] = g.integers(thr // 2 - 30, thr // 2 - 15, (min(M, 256), K // 32))
+        sb[:256] = g.integers(thr // 2 - 30, thr // 2 - 15, (min(N, 256), K // 32))
+    got, Cw, tol = _run(fa, fb, ca, sa, cb, sb, M, N, K, False, "f32")
+    check_gemm(got, Cw, tol, False, f"row layout low codes fa={fa} fb={fb} {M}x{N}x{K} {pattern}")
