@@ -396,9 +396,14 @@ mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, const mx_tens
  * the exact products of the decoded operands.  B: MXFP8 E4M3 or MXFP4, row
  * layout, cols == K.  a_out (optional, NULL to skip): receives Q(A) (fmt
  * a_fmt, row layout, [M, K]), e.g. for the backward pass; each block is
- * written once.  Exact for MXFP4 at every scale code, for E4M3 at codes 3 ..
- * 246 (blocks with max |x| >= 2^-116; smaller blocks lose bits in BF16).
- * Runs on the BF16 matrix instruction after decoding in LDS; at 4096^3 it is
+ * written once.  Runs on the BF16 matrix instruction after decoding in LDS,
+ * which is within the bound while every decoded value is a normal BF16 value
+ * (E4M3 codes 3 .. 246; E2M1 2 .. 252) and every product a normal FP32 value
+ * (c_A + c_B >= 128 + g_A + g_B, g: E4M3 9, E2M1 1).  With a_out, a fix-up
+ * pass recomputes the tiles where a code falls below half of that bound
+ * (rounded up) or above 239 from Q(A) and B with shifted codes, as mx_gemm
+ * does; without it, codes outside those limits are the caller's to avoid
+ * (Q(A)'s codes fall below half of it only for blocks with max |x| < 2^-46).  At 4096^3 it is
  * slower than mx_quantize followed by mx_gemm, because each of the N/256
  * column tiles quantizes its A panel again (measured; the fused product pays
  * only where A must not be written before the GEMM).  Requirements: K % 32

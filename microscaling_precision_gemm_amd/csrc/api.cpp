@@ -434,10 +434,19 @@ mx_status mx_gemm_quantize_a(const void* A, int64_t lda, int64_t M, int32_t a_fm
     if (a_out->fmt != a_fmt || a_out->layout != MX_LAYOUT_ROWS) return MX_ERR_UNSUPPORTED;
   }
   if (M * N == 0) return MX_OK;
-  return hip_status(mxk::launch_gemm_quantize_a(
+  const hipError_t e = mxk::launch_gemm_quantize_a(
       a_fmt, static_cast<const uint16_t*>(A), lda, static_cast<const uint8_t*>(B->codes), B->scales, B->fmt, M, N,
       K, C, cdt, ldc, a_out ? static_cast<uint8_t*>(a_out->codes) : nullptr, a_out ? a_out->scales : nullptr,
-      rnd == MX_SR, rng.seed, rng.counter, reinterpret_cast<hipStream_t>(stream)));
+      rnd == MX_SR, rng.seed, rng.counter, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess || !a_out) return hip_status(e);
+  // With Q(A) written out, the tiles whose codes could pair below normal
+  // FP32 products (c_A + c_B < 128 + g_A + g_B; E4M3 9, E2M1 1) or lie
+  // outside the decode's exact range are recomputed from Q(A) and B.
+  const uint32_t ga = a_fmt == MX_MXFP8_E4M3 ? 9u : 1u, gb = B->fmt == MX_MXFP8_E4M3 ? 9u : 1u;
+  return hip_status(mxk::launch_gemm_mx_any(a_fmt, static_cast<const uint8_t*>(a_out->codes), a_out->scales,
+                                            B->fmt, static_cast<const uint8_t*>(B->codes), B->scales, M, N, K, C,
+                                            cdt, ldc, reinterpret_cast<hipStream_t>(stream),
+                                            (128u + ga + gb + 1u) / 2u, 239u, false));
 }
 
 mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,

@@ -17,12 +17,14 @@ if torch.cuda.is_available():
     from tests.gpu_util import check_gemm, dev, host, to_gpu_bf16, upload
 
 
-def _run(M, N, K, a_fmt, b_fmt, rnd, cdt, seed=0, pad=0, nan_rows=(), emit=True):
+def _run(M, N, K, a_fmt, b_fmt, rnd, cdt, seed=0, pad=0, nan_rows=(), emit=True, low_b_rows=()):
     A = W.normal_bf16(M, K, 1.0, M + N, 60, outlier_entries=0.002, outlier_mult=40.0)
     for r in nan_rows:
         A[r, 37] = 0x7FC0  # a NaN: its block gets scale 0xFF and zero codes
     Bb = W.normal_bf16(N, K, 0.05, M + N, 61)
     qb = oracle.quantize(Bb, b_fmt)
+    for r in low_b_rows:  # scale codes whose products with Q(A)'s are subnormal FP32 values
+        qb[1][r] = (20 if b_fmt == 1 else 2) + (np.arange(K // 32) % 7)
     B = upload(b_fmt, qb[0], qb[1])
     tdt = torch.float32 if cdt == 1 else torch.bfloat16
     C = torch.empty(M, N + 3, dtype=tdt, device=dev())[:, :N]
@@ -65,3 +67,12 @@ def test_prologue_quantized_gemm_nan_blocks_and_no_output_copy():
     assert torch.equal(torch.isnan(C1), torch.isnan(C2))
     c1, c2 = C1.nan_to_num(0.0), C2.nan_to_num(0.0)
     assert torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", [(1, 1), (2, 2), (2, 1)])
+def test_prologue_quantized_gemm_low_b_codes_with_q_a_written(a_fmt, b_fmt):
+    """Rows of B at scale codes 20 .. 26 (E4M3) or 2 .. 8 (E2M1), whose
+    products with Q(A)'s blocks (codes near 120) are subnormal FP32 values:
+    with Q(A) written out, the fix-up pass recomputes those tiles and every
+    output is within the bound (FP32 out, checked in full)."""
+    _run(384, 320, 1024, a_fmt, b_fmt, 0, cdt=1, seed=2, low_b_rows=(0, 77, 300))
