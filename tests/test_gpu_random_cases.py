@@ -1,0 +1,97 @@
+"""Seeded random cases against the oracle, a net under the targeted tests:
+
+* quantizers: every format, both roundings, BF16 or FP32 input, row pitches
+  wider than the row, Hadamard on or off, the ceil rule (MX), Four Over Six
+  and 2-D blocks (NVFP4); Student-t values over ten decades with planted
+  zeros.  Codes, scales and the NVFP4 tensor scale bit for bit;
+* GEMMs: random shapes (ragged in M, N and K) for every class of operand
+  pair, FP32 out, every entry checked within the bound."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import microscaling_precision_gemm_amd as mx
+    from tests.gpu_util import check_gemm, dev, host, to_gpu_bf16, to_gpu_f32, upload
+
+
+def _quant_case(g):
+    fmt = int(g.choice([1, 2, 3, 4, 5, 6, 7, 3, 3, 2]))
+    blk = 16 if fmt == 3 else 32
+    rows, cols = int(g.integers(1, 200)), blk * int(g.integers(1, 40))
+    bf16 = g.random() < 0.6
+    pad = int(g.choice([0, 0, 8, 24]))
+    rnd = int(g.integers(0, 2))
+    rht = bool(g.random() < 0.4)
+    variant, flags = 0, 0
+    if fmt == 3:
+        r = g.random()
+        if r < 0.2 and rnd == 0:
+            variant, flags = oracle.V_FOUR6, mx.MX_FLAG_FOUR_OVER_SIX
+        elif r < 0.45:
+            variant, flags = oracle.V_2D, mx.MX_FLAG_BLOCK_2D
+    elif g.random() < 0.2:
+        variant, flags = oracle.V_CEIL, mx.MX_FLAG_SCALE_CEIL
+    if rht:
+        flags |= mx.MX_FLAG_RHT16
+    x = (g.standard_t(3, (rows, cols)) * 10.0 ** g.uniform(-6, 4)).astype(np.float32)
+    if g.random() < 0.2:
+        x[g.integers(0, rows, 3), g.integers(0, cols, 3)] = 0.0
+    if bf16:
+        xin = (x.view(np.uint32) >> 16).astype(np.uint16)  # BF16 by truncation
+        xd = to_gpu_bf16(xin, pad)
+    else:
+        xin, xd = x, to_gpu_f32(x, pad)
+    seed, counter, mask = int(g.integers(0, 2**40)), int(g.integers(0, 2**40)), int(g.integers(0, 65536))
+    out = mx.empty(fmt, rows, cols, device=dev())
+    amax = torch.zeros(1, dtype=torch.float32, device=dev())
+    mx.mx_quantize(xd, out, rnd, seed, counter, flags, mask, amax if fmt == 3 else None)
+    torch.cuda.synchronize()
+    c, s, ts = host(out)
+    wc, ws, wts = oracle.quantize(xin, fmt, rnd, seed=seed, counter=counter, rht=rht, sign_mask=mask,
+                                  variant=variant)
+    ok = np.array_equal(c, wc) and np.array_equal(s, ws) and (fmt != 3 or float(ts[0]) == wts)
+    return ok, dict(fmt=fmt, rows=rows, cols=cols, bf16=bf16, pad=pad, rnd=rnd, flags=flags)
+
+
+@pytest.mark.parametrize("seed", [101, 202])
+def test_random_quantize_cases(seed):
+    g = np.random.default_rng(seed)
+    bad = [case for ok, case in (_quant_case(g) for _ in range(300)) if not ok]
+    assert not bad, f"{len(bad)} of 300 cases differ from the oracle, e.g. {bad[:3]}"
+
+
+PAIRS = [(1, 1), (2, 2), (3, 3), (5, 1), (4, 4), (7, 7), (6, 6), (7, 2), (1, 2), (6, 4)]
+
+
+@pytest.mark.parametrize("seed", [303, 404])
+def test_random_gemm_cases(seed):
+    g = np.random.default_rng(seed)
+    bad = []
+    for _ in range(50):
+        fa, fb = PAIRS[int(g.integers(0, len(PAIRS)))]
+        M, N = int(g.integers(1, 300)), int(g.integers(1, 300))
+        K = 32 * int(g.integers(1, 40))
+        if (fa in (6, 7) or fb in (6, 7)) and g.random() < 0.5:
+            K = 512 * int(g.integers(1, 3))
+        A = W.normal_bf16(M, K, float(10.0 ** g.uniform(-3, 2)), int(g.integers(0, 1000)), 1)
+        B = W.normal_bf16(N, K, float(10.0 ** g.uniform(-3, 2)), int(g.integers(0, 1000)), 2)
+        qa, qb = oracle.quantize(A, fa), oracle.quantize(B, fb)
+        ta, tb = upload(fa, qa[0], qa[1], qa[2]), upload(fb, qb[0], qb[1], qb[2])
+        ta.cols = tb.cols = K
+        C = torch.empty(M, N, dtype=torch.float32, device=dev())
+        mx.mx_gemm(ta, tb, C)
+        torch.cuda.synchronize()
+        Ahat = oracle.dequantize_f64(fa, qa[0], qa[1], M, K) * (qa[2] if fa == 3 else 1.0)
+        Bhat = oracle.dequantize_f64(fb, qb[0], qb[1], N, K) * (qb[2] if fb == 3 else 1.0)
+        Cw, tol = oracle.gemm(Ahat, Bhat)
+        try:
+            check_gemm(C.cpu().numpy(), Cw, tol, False, f"{fa} x {fb} {M}x{N}x{K}")
+        except AssertionError as e:
+            bad.append(str(e)[:200])
+    assert not bad, f"{len(bad)} of 50 products outside the bound: {bad[:2]}"
