@@ -125,20 +125,22 @@ def test_cfg2_gemm_4096_sampled(cfg2_data, fmt, flags, scale):
     check_gemm(got, Chat, tol * scale, True, f"fmt {fmt} flags {flags}")
 
 
-def test_cfg4_wgrad_shape_sampled():
-    """MXFP8 wgrad shape M=4096 N=14336 K=16384 with FP32 output (exact path)
-    on seeded N(0,1) operands quantized by the oracle."""
+@pytest.mark.parametrize("flags,scale", [(0, 1.0), (1, 100.0)])
+def test_cfg4_wgrad_shape_sampled(flags, scale):
+    """MXFP8 wgrad shape M=4096 N=14336 K=16384 with FP32 output on seeded
+    N(0,1) operands quantized by the oracle: the exact path, and (flags=1)
+    the native FP8 instruction with its 1e-3 bound."""
     M, N, K = 4096, 14336, 16384
     a = W.normal_bf16(M, K, 1.0, 1, 80)
     b = W.normal_bf16(N, K, 1.0, 1, 81)
     qa, qb = oracle.quantize(a, 1), oracle.quantize(b, 1)
     C = torch.empty(M, N, dtype=torch.float32, device=dev())
-    mx.mx_gemm(upload(1, *qa), upload(1, *qb), C)
+    mx.mx_gemm_ex(upload(1, *qa), upload(1, *qb), C, flags)
     torch.cuda.synchronize()
     ri, cj = _sample(M, N, 2048, 8)
     Chat, tol = oracle.gemm_sampled(oracle.dequantize_f64(1, qa[0], qa[1], M, K),
                                     oracle.dequantize_f64(1, qb[0], qb[1], N, K), ri, cj)
-    check_gemm(C.cpu().numpy()[ri, cj], Chat, tol, False, "wgrad")
+    check_gemm(C.cpu().numpy()[ri, cj], Chat, tol * scale, False, f"wgrad flags {flags}")
 
 
 def test_cfg3_grouped_full_sampled():
