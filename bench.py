@@ -58,7 +58,12 @@ def parse():
 # passes, stored with the hash of the kernel source they were taken on: a
 # changed kernel reports null until the counters are taken again.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mxfp4_4096_traffic.txt")
-GEMM_SOURCE = os.path.join(ROOT, "microscaling_precision_gemm_amd", "csrc", "kernels", "gemm_tiled.hip")
+# the headline GEMM's source and every header it includes: the traffic figure
+# is used only while their combined hash matches the one it was measured on
+_CSRC = os.path.join(ROOT, "microscaling_precision_gemm_amd", "csrc")
+GEMM_SOURCES = [os.path.join(_CSRC, *p.split("/")) for p in (
+    "kernels/gemm_tiled.hip", "device/codec.h", "device/cvt.h", "device/gemm_common.h", "device/lowscale.h",
+    "device/mxenc.h", "device/wave.h", "launch.h")]
 
 
 def gemm_traffic():
@@ -71,8 +76,11 @@ def gemm_traffic():
             if ":" in ln and not ln.startswith("#"):
                 k, v = ln.split(":", 1)
                 kv[k.strip()] = v.strip()
-    with open(GEMM_SOURCE, "rb") as f:
-        h = hashlib.sha256(f.read()).hexdigest()
+    sha = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(p, "rb") as f:
+            sha.update(f.read())
+    h = sha.hexdigest()
     if kv.get("kernel_source_sha256") != h or "hbm_bytes_per_launch" not in kv:
         return None
     return float(kv["hbm_bytes_per_launch"])

@@ -6,6 +6,7 @@
 
 #include "../launch.h"
 #include "codec.h"
+#include "wave.h"
 
 namespace mxk {
 
@@ -82,7 +83,7 @@ __device__ inline void store_tile(uint8_t* __restrict__ smem, const v16f (&acc)[
       const int64_t gcol = c0 + cb / EB;
       if (grow < M) {
         if (vec && gcol + 16 / EB <= N) {
-          *reinterpret_cast<u4*>(static_cast<uint8_t*>(C) + (grow * ldc + gcol) * EB) = val;
+          store_nt(static_cast<uint8_t*>(C) + (grow * ldc + gcol) * EB, val[0], val[1], val[2], val[3]);
         } else {
           for (int e = 0; e < 16 / EB; ++e)
             if (gcol + e < N) {

@@ -31,4 +31,22 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// Streaming stores (the nt bit) for outputs that no kernel of this library
+// reads back at once: GEMM results, decoded tensors, transposed
+// re-quantizations larger than the L2s.  Their lines leave the XCD's L2 early
+// instead of waiting for the write-back at the end of the kernel.  Quantizer
+// outputs, which the GEMM reads next, keep ordinary stores (streamed, the
+// quantize + GEMM step measured slower), and so does the FP32 decode, whose
+// store instructions each cover every other 16 bytes (streamed, 1.7 times
+// slower).  p must be aligned to the store size.
+typedef uint32_t st_u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t st_u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline void store_nt(void* p, uint32_t a) { __builtin_nontemporal_store(a, static_cast<uint32_t*>(p)); }
+__device__ inline void store_nt(void* p, uint32_t a, uint32_t b) {
+  __builtin_nontemporal_store(st_u32x2{a, b}, static_cast<st_u32x2*>(p));
+}
+__device__ inline void store_nt(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  __builtin_nontemporal_store(st_u32x4{a, b, c, d}, static_cast<st_u32x4*>(p));
+}
+
 }  // namespace mxk

@@ -107,7 +107,7 @@ __device__ inline void store8(void* base, int64_t off, const float v[8]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = make_uint4(w[0], w[1], w[2], w[3]);
+    store_nt(static_cast<uint16_t*>(base) + off, w[0], w[1], w[2], w[3]);
   } else {
     float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + off);
     p[0] = make_float4(v[0], v[1], v[2], v[3]);

@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void k_requant_bf(const uint16_t* __restrict__
     }
     if (sc == 0xFFu) p[0] = p[1] = 0u;  // NaN / Inf in the block
     if ((int)c < cols_here && (int)(8 * j) < rows_here) {
-      *reinterpret_cast<uint2*>(codes + n) = make_uint2(p[0], p[1]);
+      store_nt(codes + n, p[0], p[1]);
       if ((t & 3u) == 0) scales[oc * (rows >> 5) + (orow >> 5)] = (uint8_t)sc;
     }
   }
@@ -424,9 +424,8 @@ __global__ __launch_bounds__(2 * kNvProducers) void k_requant_nv(const uint8_t* 
         for (int i = 0; i < 8; ++i) wq[i] = 0u;
       }
       if ((int64_t)c < cols - c0 && (int64_t)(32 * b) < rows - r0) {
-        uint4* dst = reinterpret_cast<uint4*>(codes + n);
-        dst[0] = make_uint4(wq[0], wq[1], wq[2], wq[3]);
-        dst[1] = make_uint4(wq[4], wq[5], wq[6], wq[7]);
+        store_nt(codes + n, wq[0], wq[1], wq[2], wq[3]);
+        store_nt(codes + n + 16, wq[4], wq[5], wq[6], wq[7]);
         scales[oc * (rows >> 5) + (orow >> 5)] = (uint8_t)sc;
       }
     }
