@@ -27,12 +27,14 @@
 // feeds 16 instructions.  A and B use the same assignment of K positions to
 // (instruction, lane group, element), so every block's products are summed.
 //
-// Per step: 16 windows of 16 instructions.  Window u converts unit u+1 and
-// reads the code dwords of unit u+2 (two windows ahead); the scale codes of
-// the next slice are read in its window 4q+1 and looked up in 4q+2.  The
-// barrier of the step follows window 13, the last read of the current stage;
-// the next stage's reads and the refill DMAs of the stage just consumed come
-// after it.  Each workgroup owns a 256x256 output tile of one group.
+// Per step: 16 windows of 16 instructions.  Window u converts unit u+1; the
+// code dwords of the next slice arrive two units at a time (8-byte reads),
+// units 0-1 in window 4q+1 and units 2-3 in window 4q+3, each into the
+// registers of two units already converted; the scale codes of the next
+// slice are read in its window 4q+1 and looked up in 4q+2.  The barrier of
+// the step follows window 13; the next stage's reads (windows 14 and 15) and
+// the refill DMAs of the stage just consumed come after it.  Each workgroup
+// owns a 256x256 output tile of one group.
 #include <atomic>
 
 #include "../device/codec.h"
@@ -83,7 +85,7 @@ __device__ inline u4 nv_conv(uint32_t w, TabE tab) {
 }
 
 struct NvState {
-  uint32_t raw[2][8];  // [unit parity][A 0..3, B 4..7]: the lane's code dword
+  uint32_t raw[8][4];  // [A 0..3, B 4..7][unit of the slice]: the lane's code dwords
   u4 cv[2][8];         // [unit parity]: FP16 fragments
   uint32_t code[8];    // the two scale codes (blocks 2c, 2c+1) of a slice
   TabE tab[2][8][2];     // [slice parity][fragment][block of the chunk]
@@ -93,12 +95,17 @@ __device__ inline uint32_t frag_row(int t, uint32_t wm, uint32_t wn, uint32_t lr
   return t < 4 ? wm * 128 + t * 32 + lr : kTile + wn * 128 + (t - 4) * 32 + lr;
 }
 
-// code dword m of chunk 2q + g of each fragment row
-__device__ inline void read_unit(const uint8_t* __restrict__ L, uint32_t q, uint32_t m, uint32_t wm,
-                                 uint32_t wn, uint32_t lr, uint32_t lg, uint32_t (&raw)[8]) {
+// code dwords 2h, 2h+1 of chunk 2q + g of each fragment row, one 8-byte read
+// each (a 4-byte read per dword met 4-way bank conflicts: 32 rows of one
+// 16-byte column fall on 16 distinct 4-byte banks; 8-byte reads halve that)
+__device__ inline void read_half(const uint8_t* __restrict__ L, uint32_t q, int h, uint32_t wm, uint32_t wn,
+                                 uint32_t lr, uint32_t lg, uint32_t (&raw)[8][4]) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
-    raw[t] = *reinterpret_cast<const uint32_t*>(L + chunk_off(frag_row(t, wm, wn, lr), 2 * q + lg) + 4 * m);
+  for (int t = 0; t < 8; ++t) {
+    const uint2 v = *reinterpret_cast<const uint2*>(L + chunk_off(frag_row(t, wm, wn, lr), 2 * q + lg) + 8 * h);
+    raw[t][2 * h] = v.x;
+    raw[t][2 * h + 1] = v.y;
+  }
 }
 
 // scale codes of blocks 2c, 2c+1 (c = 2q + g) of step `step` for each fragment row
@@ -118,9 +125,9 @@ __device__ inline void lookup(const uint8_t* __restrict__ smem, const uint32_t (
       tab[t][h] = *reinterpret_cast<const TabE*>(smem + kTabBase + ((code[t] >> (8 * h)) & 0xFFu) * 8);
 }
 
-__device__ inline void conv_unit(const uint32_t (&raw)[8], const TabE (&tab)[8][2], int h, u4 (&cv)[8]) {
+__device__ inline void conv_unit(const uint32_t (&raw)[8][4], int m, const TabE (&tab)[8][2], u4 (&cv)[8]) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) cv[t] = nv_conv(raw[t], tab[t][h]);
+  for (int t = 0; t < 8; ++t) cv[t] = nv_conv(raw[t][m], tab[t][m / 2]);
 }
 
 __device__ inline void mfma_f16_16(const u4 (&f)[8], v16f (&acc)[4][4]) {
@@ -145,12 +152,15 @@ __device__ inline void nv_window(const PipeCtx& x, uint8_t* __restrict__ smem, u
   if constexpr (U == 15 && SWITCH) {
     lookup(smem, s.code, s.tab[0]);
   }
-  if constexpr (kConvNext) conv_unit(s.raw[(U + 1) % 2], s.tab[((U + 1) / 4) % 2], ((U + 1) % 4) / 2, s.cv[(U + 1) % 2]);
-  // code dwords two units ahead
-  if constexpr (U + 2 <= 15) {
-    read_unit(cur, (U + 2) / 4, (U + 2) % 4, wm, wn, lr, lg, s.raw[U % 2]);
-  } else if constexpr (SWITCH) {
-    read_unit(nxt, 0, U + 2 - 16, wm, wn, lr, lg, s.raw[U % 2]);
+  if constexpr (kConvNext) conv_unit(s.raw, (U + 1) % 4, s.tab[((U + 1) / 4) % 2], s.cv[(U + 1) % 2]);
+  // code dwords of the next slice, two at a time into the registers of the
+  // two units already converted: dwords 0-1 in window 4q+1, 2-3 in 4q+3
+  // (the next step's first slice after the barrier, in windows 14 and 15)
+  constexpr bool kHalf0 = (U % 4 == 1 && U < 12) || (U == 14 && SWITCH);
+  constexpr bool kHalf1 = (U % 4 == 3 && U < 12) || (U == 15 && SWITCH);
+  if constexpr (kHalf0 || kHalf1) {
+    if constexpr (U < 12) read_half(cur, U / 4 + 1, kHalf1 ? 1 : 0, wm, wn, lr, lg, s.raw);
+    else read_half(nxt, 0, kHalf1 ? 1 : 0, wm, wn, lr, lg, s.raw);
   }
   // scale codes and table entries of the next slice
   if constexpr (U % 4 == 1 && U < 12) {
@@ -170,7 +180,7 @@ __device__ inline void nv_window(const PipeCtx& x, uint8_t* __restrict__ smem, u
     issue_scales(x, smem, st + 2, (st + 2) % kScaleBufs, 1);
   }
   mfma_f16_16(s.cv[U % 2], acc);
-  constexpr int kRaw = (U + 2 <= 15 || SWITCH) ? 8 : 0;
+  constexpr int kRaw = (kHalf0 || kHalf1) ? 8 : 0;
   constexpr int kCodes = ((U % 4 == 1 && U < 12) || (U == 14 && SWITCH)) ? 8 : 0;
   constexpr int kLook = ((U % 4 == 2 && U < 12) || (U == 15 && SWITCH)) ? 16 : 0;
   spread_front<kConvNext ? kConvValu : 0, kRaw + kCodes + kLook, DMA ? (U == 14 ? 16 : (U == 15 ? 2 : 0)) : 0>();
@@ -306,9 +316,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   NvState s;
   read_codes(smem, 0, 0, wm, wn, lr, lg, s.code);
   lookup(smem, s.code, s.tab[0]);
-  read_unit(smem, 0, 0, wm, wn, lr, lg, s.raw[0]);
-  read_unit(smem, 0, 1, wm, wn, lr, lg, s.raw[1]);
-  conv_unit(s.raw[0], s.tab[0], 0, s.cv[0]);
+  read_half(smem, 0, 0, wm, wn, lr, lg, s.raw);
+  read_half(smem, 0, 1, wm, wn, lr, lg, s.raw);
+  conv_unit(s.raw, 0, s.tab[0], s.cv[0]);
   sched_fence();
   uint32_t st = 0;
   for (; st + 2 < steps; ++st) nv_windows<0, true, true>(x, smem, st, wm, wn, lr, lg, s, acc);
