@@ -348,7 +348,8 @@ mx_status mx_hadamard16(const void* x, int32_t xdt, void* y, int32_t ydt, int64_
  * code whose tile one shift per operand fits into range.  Scale code 255
  * (NaN) gives NaN in exactly the output rows / columns whose blocks carry it.
  * Requirements: A->fmt == B->fmt, or both MX formats (E8M0 scales) in the
- * row layout; A->cols == B->cols == K; K % 32 == 0. */
+ * row layout; A->cols == B->cols == K; K % 32 == 0.  M == 0 or N == 0
+ * enqueues nothing; K == 0 (an empty sum) writes C = 0. */
 mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cdt, int64_t ldc,
                   mx_stream stream);
 
@@ -379,9 +380,9 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
  * operand of the next product.  flags: MX_GEMM_FP8_NATIVE,
  * MX_FLAG_SCALE_CEIL; anything else returns MX_ERR_UNSUPPORTED, as do
  * row-layout operands and an NVFP4 output (its tensor scale needs the whole
- * product first).  Cost (4096^3 MXFP4, measured): 42 us fused against 48 us
- * for mx_gemm into a BF16 buffer followed by mx_quantize with MX_RNE, 48
- * against 52 us with MX_SR. */
+ * product first).  K == 0 returns MX_ERR_SHAPE.  Cost (4096^3 MXFP4,
+ * measured): 42 us fused against 48 us for mx_gemm into a BF16 buffer
+ * followed by mx_quantize with MX_RNE, 48 against 52 us with MX_SR. */
 mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, const mx_tensor* out,
                            int32_t rnd, mx_rng rng, uint32_t flags, mx_stream stream);
 
@@ -407,7 +408,7 @@ mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, const mx_tens
  * slower than mx_quantize followed by mx_gemm, because each of the N/256
  * column tiles quantizes its A panel again (measured; the fused product pays
  * only where A must not be written before the GEMM).  Requirements: K % 32
- * == 0.  Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT,
+ * == 0, K > 0.  Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT,
  * MX_ERR_UNSUPPORTED, MX_ERR_HIP. */
 mx_status mx_gemm_quantize_a(const void* A, int64_t lda, int64_t M, int32_t a_fmt, int32_t rnd, mx_rng rng,
                              const mx_tensor* B, void* C, int32_t cdt, int64_t ldc, const mx_tensor* a_out,
@@ -424,7 +425,9 @@ mx_status mx_gemm_quantize_a(const void* A, int64_t lda, int64_t M, int32_t a_fm
  * clamped into it); otherwise A has R rows.
  * C is [R, N] (pitch ldc).  C[r, :] = A[src(r)] * B_e^T * S_A * S_B[e].
  * Requirements: A and B NVFP4, K % 32 == 0, num_groups >= 1, `routed_rows`
- * (host) = R, B->rows % num_groups == 0. */
+ * (host) = R, B->rows % num_groups == 0, and with row_index and R > 0, A
+ * has at least one row (else MX_ERR_SHAPE).  R == 0 enqueues nothing;
+ * K == 0 writes C = 0. */
 mx_status mx_gemm_grouped(const mx_tensor* A, const int32_t* row_index, int64_t routed_rows,
                           const mx_tensor* B, int32_t num_groups, const int64_t* group_offsets,
                           void* C, int32_t cdt, int64_t ldc, mx_stream stream);

@@ -29,6 +29,12 @@ int64_t block_of(int32_t f) { return f == MX_NVFP4 ? 16 : 32; }
 
 mx_status hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 
+// The product over an empty K: C = 0.
+mx_status zero_product(void* C, int32_t cdt, int64_t ldc, int64_t M, int64_t N, mx_stream stream) {
+  return hip_status(mxk::launch_zero_matrix(C, cdt == MX_F32 ? mxk::DT_F32 : mxk::DT_BF16, ldc, M, N,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 // Checks the descriptor of a quantized tensor of logical shape [rows, cols].
 // The tiled layout is MX-only with rows % 32 == 0 and cols % 1024 == 0.
 mx_status check_tensor(const mx_tensor* t, int64_t rows, int64_t cols) {
@@ -300,6 +306,7 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
     st = check_output(C, cdt, A->rows, B->rows, ldc);
     if (st != MX_OK) return st;
     if (A->rows * B->rows == 0) return MX_OK;
+    if (A->cols == 0) return zero_product(C, cdt, ldc, A->rows, B->rows, stream);
     return hip_status(mxk::launch_gemm_mx_tiled(A->fmt, static_cast<const uint8_t*>(A->codes), A->scales,
                                                 static_cast<const uint8_t*>(B->codes), B->scales, A->rows,
                                                 B->rows, A->cols, C, cdt, ldc,
@@ -316,6 +323,7 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
     st = check_output(C, cdt, A->rows, B->rows, ldc);
     if (st != MX_OK) return st;
     if (A->rows * B->rows == 0) return MX_OK;
+    if (A->cols == 0) return zero_product(C, cdt, ldc, A->rows, B->rows, stream);
     if (flags)  // row-layout FP8 pairs with E5M2 on the scaled FP8 instruction
       return hip_status(mxk::launch_gemm_mx(mxk::FMT_MXFP8, static_cast<const uint8_t*>(A->codes), A->scales,
                                             static_cast<const uint8_t*>(B->codes), B->scales, A->rows, B->rows,
@@ -361,6 +369,7 @@ mx_status mx_gemm_ex(const mx_tensor* A, const mx_tensor* B, void* C, int32_t cd
   st = check_output(C, cdt, M, N, ldc);
   if (st != MX_OK) return st;
   if (M * N == 0) return MX_OK;
+  if (K == 0) return zero_product(C, cdt, ldc, M, N, stream);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const uint8_t* ac = static_cast<const uint8_t*>(A->codes);
   const uint8_t* bc = static_cast<const uint8_t*>(B->codes);
@@ -404,6 +413,7 @@ mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, const mx_tens
   if (st != MX_OK) return st;
   if (out->fmt != MX_MXFP8_E4M3 && out->fmt != MX_MXFP4_E2M1 && out->fmt != MX_MXFP8_E5M2)
     return MX_ERR_UNSUPPORTED;
+  if (K == 0) return MX_ERR_SHAPE;
   if (M * N == 0) return MX_OK;
   return hip_status(mxk::launch_gemm_mx_tiled_quant(
       A->fmt, static_cast<const uint8_t*>(A->codes), A->scales,
@@ -423,7 +433,7 @@ mx_status mx_gemm_quantize_a(const void* A, int64_t lda, int64_t M, int32_t a_fm
   if ((B->fmt != MX_MXFP8_E4M3 && B->fmt != MX_MXFP4_E2M1) || B->layout != MX_LAYOUT_ROWS)
     return MX_ERR_UNSUPPORTED;
   const int64_t N = B->rows, K = B->cols;
-  if (M < 0 || K % 32) return MX_ERR_SHAPE;
+  if (M < 0 || K % 32 || K == 0) return MX_ERR_SHAPE;
   st = check_matrix(A, MX_BF16, M, K, lda);
   if (st != MX_OK) return st;
   st = check_output(C, cdt, M, N, ldc);
@@ -468,11 +478,13 @@ mx_status mx_gemm_grouped(const mx_tensor* A, const int32_t* row_index, int64_t 
   if (B->rows % num_groups) return MX_ERR_SHAPE;
   if (routed_rows < 0) return MX_ERR_SHAPE;
   if (!row_index && routed_rows != A->rows) return MX_ERR_SHAPE;
+  if (row_index && routed_rows > 0 && A->rows == 0) return MX_ERR_SHAPE;  // no row to gather
   if (!group_offsets) return MX_ERR_NULL;
   const int64_t N = B->rows / num_groups, K = A->cols;
   st = check_output(C, cdt, routed_rows, N, ldc);
   if (st != MX_OK) return st;
   if (routed_rows * N == 0) return MX_OK;
+  if (K == 0) return zero_product(C, cdt, ldc, routed_rows, N, stream);
   return hip_status(mxk::launch_gemm_nvfp4(
       static_cast<const uint8_t*>(A->codes), A->scales, A->tensor_scale, row_index, A->rows, routed_rows,
       static_cast<const uint8_t*>(B->codes), B->scales, B->tensor_scale, num_groups,

@@ -115,7 +115,26 @@ __global__ __launch_bounds__(kStatThreads) void k_error_stats(const void* __rest
   }
 }
 
+// C[r, c] = 0 for r < rows, c < cols (row pitch ldc elements, BF16 or FP32):
+// the product over an empty K.  Grid-stride over the rows, lanes along a row.
+template <typename T>
+__global__ __launch_bounds__(256) void k_zero_matrix(T* __restrict__ c, int64_t ldc, int64_t rows, int64_t cols) {
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
+    for (int64_t j = threadIdx.x; j < cols; j += 256) c[r * ldc + j] = T(0);
+}
+
 }  // namespace
+
+hipError_t launch_zero_matrix(void* c, int cdt, int64_t ldc, int64_t rows, int64_t cols, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  const int g = (int)(rows < 4096 ? rows : 4096);
+  if (cdt == DT_F32)
+    hipLaunchKernelGGL(k_zero_matrix<float>, dim3(g), dim3(256), 0, s, static_cast<float*>(c), ldc, rows, cols);
+  else
+    hipLaunchKernelGGL(k_zero_matrix<uint16_t>, dim3(g), dim3(256), 0, s, static_cast<uint16_t*>(c), ldc, rows,
+                       cols);
+  return hipGetLastError();
+}
 
 hipError_t launch_error_stats(const void* x, int xdt, int64_t ld_x, const float* y, int64_t ld_y, int64_t rows,
                               int64_t cols, double* stats, hipStream_t s) {

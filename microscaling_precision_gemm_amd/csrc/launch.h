@@ -74,6 +74,10 @@ hipError_t launch_dequantize(int fmt, const uint8_t* codes, const uint8_t* scale
 // = sum (y-x)^2, sum x^2, sum (y-x), max |y-x| (device doubles, overwritten).
 hipError_t launch_error_stats(const void* x, int xdt, int64_t ld_x, const float* y, int64_t ld_y, int64_t rows,
                               int64_t cols, double* stats, hipStream_t s);
+// C = 0 over rows x cols (BF16 or FP32, row pitch ldc elements; stats.hip):
+// a GEMM's result when K is 0.  A kernel, not a memset, so that the call
+// stays capturable in a graph.
+hipError_t launch_zero_matrix(void* c, int cdt, int64_t ldc, int64_t rows, int64_t cols, hipStream_t s);
 hipError_t launch_hadamard16(const void* x, int xdt, void* y, int ydt, int64_t rows, int64_t cols,
                              uint32_t sign_mask, bool inverse, hipStream_t s);
 hipError_t launch_requant_transpose(const uint8_t* src_codes, const uint8_t* src_scales,

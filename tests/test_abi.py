@@ -142,6 +142,15 @@ def test_other_entry_point_checks(mx):
     assert L.mx_gemm_grouped(ctypes.byref(nv), None, 64, ctypes.byref(nv), 3, FAKE, FAKE, 0, 64, None) == 2
     assert L.mx_gemm_grouped(ctypes.byref(nv), None, 64, ctypes.byref(nv), 2, None, FAKE, 0, 32, None) == 1
     assert L.mx_gemm_grouped(ctypes.byref(nv), None, 60, ctypes.byref(nv), 2, FAKE, FAKE, 0, 32, None) == 2
+    # grouped with a row gather but no A row to gather from
+    nv0 = _t(mx, 3, 0, 64)
+    assert L.mx_gemm_grouped(ctypes.byref(nv0), FAKE, 64, ctypes.byref(nv), 2, FAKE, FAKE, 0, 32, None) == 2
+    # the products whose output is quantized need K > 0
+    t0 = mx._Tensor(2, 1, 32, 0, None, None, None)
+    q_out = _t(mx, 2, 32, 32)
+    assert L.mx_gemm_quantize(ctypes.byref(t0), ctypes.byref(t0), ctypes.byref(q_out), 0, rng, 0, None) == 2
+    b0 = _t(mx, 1, 64, 0, codes=None, scales=None)
+    assert L.mx_gemm_quantize_a(FAKE, 64, 32, 1, 0, rng, ctypes.byref(b0), FAKE, 1, 64, None, None) == 2
     # requant: both or neither source, wrong out format, rows % 32
     out = _t(mx, 1, 64, 64)
     assert L.mx_requant_transpose(ctypes.byref(nv), FAKE, 64, 64, 64, ctypes.byref(out), 1, rng, None) == 1

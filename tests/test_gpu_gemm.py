@@ -270,3 +270,41 @@ def test_grouped_nvfp4_pipelined_short_last_tiles(gather):
         Bd = oracle.dequantize_f64(3, qw[e][0], qw[e][1], N, K)
         Chat, tol = oracle.gemm(Ad[rows], Bd, float(np.float64(qx[2]) * np.float64(qw[e][2])))
         check_gemm(Cg[lo:hi], Chat, tol, False, f"short-tile expert {e} gather={gather}")
+
+
+# K = 0: every GEMM path writes the empty sum, C = 0, into exactly [M, N]
+EMPTY_K_CASES = [  # (A format, B format, layout, flags)
+    (2, 2, 0, 0), (2, 2, 1, 0), (1, 1, 0, 0), (1, 1, 0, 1), (1, 1, 1, 1), (3, 3, 0, 0),
+    (5, 1, 0, 0), (5, 5, 1, 1), (4, 4, 0, 0), (7, 7, 0, 0), (6, 6, 0, 0), (7, 2, 0, 0)]
+
+
+@pytest.mark.parametrize("fa,fb,layout,flags", EMPTY_K_CASES)
+@pytest.mark.parametrize("cdt", [torch.float32, torch.bfloat16])
+def test_empty_k_product_is_zero(fa, fb, layout, flags, cdt):
+    M, N = 64, 96
+    A = mx.empty(fa, M, 0, device=dev(), layout=layout)
+    B = mx.empty(fb, N, 0, device=dev(), layout=layout)
+    C = torch.full((M, N + 8), float("nan"), dtype=cdt, device=dev())
+    mx.mx_gemm_ex(A, B, C[:, :N], flags)
+    torch.cuda.synchronize()
+    assert bool(torch.all(C[:, :N] == 0))
+    assert bool(torch.all(torch.isnan(C[:, N:])))  # the pitch padding is not written
+
+
+def test_empty_k_grouped_and_empty_rows():
+    E, N = 4, 32
+    A = mx.empty(3, 40, 0, device=dev())
+    B = mx.empty(3, E * N, 0, device=dev(), n_tensor_scales=E)
+    off = torch.tensor([0, 10, 10, 25, 40], dtype=torch.int64, device=dev())
+    C = torch.full((40, N), float("nan"), dtype=torch.float32, device=dev())
+    mx.mx_gemm_grouped(A, None, 40, B, E, off, C)
+    torch.cuda.synchronize()
+    assert bool(torch.all(C == 0))
+    # no routed rows, or M = 0 on a plain GEMM: nothing is written
+    C.fill_(float("nan"))
+    mx.mx_gemm_grouped(mx.empty(3, 0, 64, device=dev()), None, 0, mx.empty(3, E * N, 64, device=dev(),
+                       n_tensor_scales=E), E, torch.zeros(E + 1, dtype=torch.int64, device=dev()), C[:0])
+    a0 = mx.empty(2, 0, 64, device=dev())
+    mx.mx_gemm(a0, mx.empty(2, N, 64, device=dev()), C[:0])
+    torch.cuda.synchronize()
+    assert bool(torch.all(torch.isnan(C)))
