@@ -420,7 +420,9 @@ mx_status mx_gemm_quantize_a(const void* A, int64_t lda, int64_t M, int32_t a_fm
  * rows = num_groups * N whose tensor_scale points to num_groups floats.
  * group_offsets (device, int64 [num_groups + 1], non-decreasing, first 0, last
  * = number of routed rows R) assigns output rows [off[e], off[e+1]) to expert
- * e.  A row source: if row_index is non-NULL (device int32 [R]), routed row r
+ * e.  Being on the device, the offsets are not checked; each range is clamped
+ * into [0, R] there, so offsets that break this contract give wrong rows but
+ * never a write outside C.  A row source: if row_index is non-NULL (device int32 [R]), routed row r
  * reads A row row_index[r] (A is [tokens, K]; entries outside [0, tokens) are
  * clamped into it); otherwise A has R rows.
  * C is [R, N] (pitch ldc).  C[r, :] = A[src(r)] * B_e^T * S_A * S_B[e].

@@ -194,7 +194,11 @@ __global__ __launch_bounds__(256) void k_gemm_staged(
   } else {
     int64_t acc = 0;
     for (int32_t e = 0; e < groups; ++e) {
-      const int64_t lo = offsets[e], hi = offsets[e + 1];
+      // clamped into [0, R]: offsets that break their contract (decreasing,
+      // past R) cannot move a write outside C
+      int64_t lo = offsets[e], hi = offsets[e + 1];
+      lo = lo < 0 ? 0 : (lo > R ? R : lo);
+      hi = hi < lo ? lo : (hi > R ? R : hi);
       const int64_t nt = (hi - lo + BM - 1) / BM;
       if (tile < acc + nt) {
         g = e;

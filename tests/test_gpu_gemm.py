@@ -308,3 +308,41 @@ def test_empty_k_grouped_and_empty_rows():
     mx.mx_gemm(a0, mx.empty(2, N, 64, device=dev()), C[:0])
     torch.cuda.synchronize()
     assert bool(torch.all(torch.isnan(C)))
+
+
+@pytest.mark.parametrize("R,N,K,offsets", [
+    (40, 32, 64, [0, 30, 20, 100]),                  # small shapes (staged kernel)
+    (4096, 1024, 256, [0, 1000, 900, 5000, 6000]),   # the pipelined kernel
+])
+def test_grouped_offsets_outside_their_contract_stay_inside_c(R, N, K, offsets):
+    """Group offsets that decrease or run past R (a broken caller) are
+    clamped into [0, R] on the device: rows past C are never written."""
+    E = len(offsets) - 1
+    g = torch.Generator(device=dev()).manual_seed(3)
+    x = torch.randn(R, K, device=dev(), generator=g).to(torch.bfloat16)
+    w = torch.randn(E * N, K, device=dev(), generator=g).to(torch.bfloat16)
+    A = mx.empty(3, R, K, device=dev())
+    mx.mx_quantize(x, A, amax=torch.zeros(1, device=dev()))
+    B = mx.empty(3, E * N, K, device=dev(), n_tensor_scales=E)
+    for e in range(E):
+        sub = mx.MXTensor(3, N, K, B.codes[e * N:(e + 1) * N], B.scales[e * N:(e + 1) * N],
+                          B.tensor_scale[e:e + 1])
+        mx.mx_quantize(w[e * N:(e + 1) * N], sub, amax=torch.zeros(1, device=dev()))
+    big = torch.full((R + 64, N), float("nan"), dtype=torch.float32, device=dev())
+    off = torch.tensor(offsets, dtype=torch.int64, device=dev())
+    mx.mx_gemm_grouped(A, None, R, B, E, off, big[:R])
+    torch.cuda.synchronize()
+    assert bool(torch.all(torch.isnan(big[R:])))
+    # rows that only the first group covers after the clamp match the same
+    # call with offsets that keep the contract (same kernel, same tiles)
+    ranges = []
+    for e in range(E):
+        lo = min(max(offsets[e], 0), R)
+        ranges.append((lo, min(max(offsets[e + 1], lo), R)))
+    cut = min([ranges[0][1]] + [lo for lo, hi in ranges[1:] if hi > lo])
+    assert cut > 0
+    good = torch.tensor([0, offsets[1]] + [R] * (E - 1), dtype=torch.int64, device=dev())
+    ref = torch.empty(R, N, dtype=torch.float32, device=dev())
+    mx.mx_gemm_grouped(A, None, R, B, E, good, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(big[:cut], ref[:cut])
