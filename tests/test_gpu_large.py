@@ -1,0 +1,93 @@
+"""Tensors past 32-bit offsets: a 66048 x 65536 BF16 tensor (8.7 GB, 4.3e9
+elements) through the row-layout quantizers, the decode and both requant
+kernels, so that input, code and output offsets all pass 2^32.  Rows and
+columns are sampled at both ends and compared with the oracle bit for bit
+(blocks are row-local, NVFP4 given the tensor's amax, requant bands given
+the random counter where the band starts)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import microscaling_precision_gemm_amd as mx
+    from tests.gpu_util import dev
+
+ROWS, COLS = 66048, 65536        # rows % 128 == 0: also a requant source
+SAMPLE_ROWS = [0, 1, 32767, 65535, 65536, ROWS - 1]
+BAND = 64                         # source columns per requant band
+
+
+@pytest.fixture(scope="module")
+def big():
+    g = torch.Generator(device=dev()).manual_seed(11)
+    x = torch.randn((ROWS, COLS), dtype=torch.bfloat16, device=dev(), generator=g)
+    yield x
+    del x
+    torch.cuda.empty_cache()
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _host(t):
+    return t.cpu().numpy()
+
+
+def test_mxfp8_quantize_and_decode_past_32bit_offsets(big):
+    q = mx.empty(mx.MX_MXFP8_E4M3, ROWS, COLS, device=dev())
+    mx.mx_quantize(big, q)
+    y = torch.empty_like(big)
+    mx.mx_dequantize(q, y)
+    torch.cuda.synchronize()
+    rows = torch.tensor(SAMPLE_ROWS, device=dev())
+    xs = _bits(big[rows])
+    wc, ws, _ = oracle.quantize(xs, 1)
+    assert np.array_equal(_host(q.codes[rows]), wc)
+    assert np.array_equal(_host(q.scales[rows]), ws)
+    ref = oracle.dequantize(1, wc, ws, None, len(SAMPLE_ROWS), COLS)
+    assert np.array_equal(_bits(y[rows]), _bits(torch.from_numpy(ref).to(torch.bfloat16)))
+    del q, y
+    torch.cuda.empty_cache()
+
+
+def test_nvfp4_amax_and_quantize_past_32bit_offsets(big):
+    q = mx.empty(mx.MX_NVFP4, ROWS, COLS, device=dev())
+    amax = torch.zeros(1, dtype=torch.float32, device=dev())
+    mx.mx_quantize(big, q, amax=amax)
+    torch.cuda.synchronize()
+    T = float(amax.item())
+    assert T == float(big.abs().max().float().item())
+    rows = torch.tensor(SAMPLE_ROWS, device=dev())
+    wc, ws, wts = oracle.quantize(_bits(big[rows]), 3, amax=T)
+    assert float(q.tensor_scale.item()) == wts
+    assert np.array_equal(_host(q.codes[rows]), wc)
+    assert np.array_equal(_host(q.scales[rows]), ws)
+    # requant of this NVFP4 source (SR): the last band of source columns
+    out = mx.empty(mx.MX_MXFP8_E4M3, COLS, ROWS, device=dev())
+    mx.mx_requant_transpose(out, src=q, rnd=mx.MX_SR, seed=5, counter=9)
+    torch.cuda.synchronize()
+    c0 = COLS - BAND
+    band = (_host(q.codes[:, c0 // 2:]), _host(q.scales[:, c0 // 16:]), wts)
+    oc, os_ = oracle.requant_transpose(ROWS, BAND, oracle.SR, 5, 9 + c0 * ROWS // 8, nvfp4=band)
+    assert np.array_equal(_host(out.codes[c0:]), oc)
+    assert np.array_equal(_host(out.scales[c0:]), os_)
+    del q, out
+    torch.cuda.empty_cache()
+
+
+def test_bf16_requant_past_32bit_offsets(big):
+    out = mx.empty(mx.MX_MXFP8_E4M3, COLS, ROWS, device=dev())
+    mx.mx_requant_transpose(out, x_bf16=big, rnd=mx.MX_SR, seed=7, counter=3)
+    torch.cuda.synchronize()
+    for c0 in (0, COLS - BAND):
+        xs = _bits(big[:, c0:c0 + BAND])
+        oc, os_ = oracle.requant_transpose(ROWS, BAND, oracle.SR, 7, 3 + c0 * ROWS // 8, bf16=xs)
+        assert np.array_equal(_host(out.codes[c0:c0 + BAND]), oc)
+        assert np.array_equal(_host(out.scales[c0:c0 + BAND]), os_)
+    del out
+    torch.cuda.empty_cache()
