@@ -1,9 +1,10 @@
 """Tensors past 32-bit offsets: a 66048 x 65536 BF16 tensor (8.7 GB, 4.3e9
 elements) through the row-layout quantizers, the decode and both requant
-kernels, so that input, code and output offsets all pass 2^32.  Rows and
-columns are sampled at both ends and compared with the oracle bit for bit
-(blocks are row-local, NVFP4 given the tensor's amax, requant bands given
-the random counter where the band starts)."""
+kernels, so that input, code and output offsets all pass 2^32; and an MXFP4
+GEMM whose A operand holds 4.3 GB of codes, in both layouts.  Rows and
+columns are sampled at both ends and compared with the oracle: codes bit for
+bit (blocks are row-local, NVFP4 given the tensor's amax, requant bands
+given the random counter where the band starts), products within the bound."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import microscaling_precision_gemm_amd as mx
-    from tests.gpu_util import dev
+    from tests.gpu_util import check_gemm, dev
 
 ROWS, COLS = 66048, 65536        # rows % 128 == 0: also a requant source
 SAMPLE_ROWS = [0, 1, 32767, 65535, 65536, ROWS - 1]
@@ -90,4 +91,34 @@ def test_bf16_requant_past_32bit_offsets(big):
         assert np.array_equal(_host(out.codes[c0:c0 + BAND]), oc)
         assert np.array_equal(_host(out.scales[c0:c0 + BAND]), os_)
     del out
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_mxfp4_gemm_operand_past_32bit_offsets(layout):
+    """M = 66048, N = 512, K = 131072: A's codes span 4.3 GB.  Row layout:
+    past the pipelined kernel's 32-bit offsets, so the general kernel and
+    the fix-up scan run; tile layout: the register-direct kernel."""
+    M, N, K = 66048, 512, 131072
+    g = torch.Generator(device=dev()).manual_seed(12)
+    a = torch.randn((M, K), dtype=torch.bfloat16, device=dev(), generator=g)
+    b = torch.randn((N, K), dtype=torch.bfloat16, device=dev(), generator=g)
+    qa = mx.empty(mx.MX_MXFP4_E2M1, M, K, device=dev(), layout=layout)
+    qb = mx.empty(mx.MX_MXFP4_E2M1, N, K, device=dev(), layout=layout)
+    mx.mx_quantize(a, qa)
+    mx.mx_quantize(b, qb)
+    C = torch.empty(M, N, dtype=torch.float32, device=dev())
+    mx.mx_gemm(qa, qb, C)
+    torch.cuda.synchronize()
+    rows, cols = [0, 32767, 65535, M - 1], [0, 1, 255, N - 1]
+    ca, sa, _ = oracle.quantize(_bits(a[torch.tensor(rows, device=dev())]), 2)
+    cb, sb, _ = oracle.quantize(_bits(b[torch.tensor(cols, device=dev())]), 2)
+    Ad = oracle.dequantize_f64(2, ca, sa, len(rows), K)
+    Bd = oracle.dequantize_f64(2, cb, sb, len(cols), K)
+    ri = np.repeat(np.arange(len(rows)), len(cols))
+    cj = np.tile(np.arange(len(cols)), len(rows))
+    Chat, tol = oracle.gemm_sampled(Ad, Bd, ri, cj)
+    got = C[torch.tensor(rows, device=dev())][:, torch.tensor(cols, device=dev())].cpu().numpy().reshape(-1)
+    check_gemm(got, Chat, tol, False, f"layout {layout}")
+    del a, b, qa, qb, C
     torch.cuda.empty_cache()
