@@ -1,7 +1,8 @@
 """Tensors past 32-bit offsets: a 66048 x 65536 BF16 tensor (8.7 GB, 4.3e9
 elements) through the row-layout quantizers, the decode and both requant
-kernels, so that input, code and output offsets all pass 2^32; and an MXFP4
-GEMM whose A operand holds 4.3 GB of codes, in both layouts.  Rows and
+kernels, so that input, code and output offsets all pass 2^32; and GEMMs
+whose A operand holds 4.3 GB of codes (MXFP4 in both layouts, exact MXFP8,
+grouped NVFP4 with a row gather).  Rows and
 columns are sampled at both ends and compared with the oracle: codes bit for
 bit (blocks are row-local, NVFP4 given the tensor's amax, requant bands
 given the random counter where the band starts), products within the bound."""
@@ -121,4 +122,75 @@ def test_mxfp4_gemm_operand_past_32bit_offsets(layout):
     got = C[torch.tensor(rows, device=dev())][:, torch.tensor(cols, device=dev())].cpu().numpy().reshape(-1)
     check_gemm(got, Chat, tol, False, f"layout {layout}")
     del a, b, qa, qb, C
+    torch.cuda.empty_cache()
+
+
+def test_exact_mxfp8_gemm_operand_past_32bit_offsets(big):
+    """The 8.7 GB tensor as an MXFP8 A operand (4.3 GB of codes), N = 256:
+    past the exact pipeline's 32-bit offsets, so the staged kernel and its
+    fix-up pass run."""
+    M, K, N = ROWS, COLS, 256
+    qa = mx.empty(mx.MX_MXFP8_E4M3, M, K, device=dev())
+    mx.mx_quantize(big, qa)
+    g = torch.Generator(device=dev()).manual_seed(13)
+    b = torch.randn((N, K), dtype=torch.bfloat16, device=dev(), generator=g)
+    qb = mx.empty(mx.MX_MXFP8_E4M3, N, K, device=dev())
+    mx.mx_quantize(b, qb)
+    C = torch.empty(M, N, dtype=torch.float32, device=dev())
+    mx.mx_gemm(qa, qb, C)
+    torch.cuda.synchronize()
+    rows, cols = SAMPLE_ROWS, [0, 1, 128, N - 1]
+    ca, sa, _ = oracle.quantize(_bits(big[torch.tensor(rows, device=dev())]), 1)
+    cb, sb, _ = oracle.quantize(_bits(b[torch.tensor(cols, device=dev())]), 1)
+    Ad = oracle.dequantize_f64(1, ca, sa, len(rows), K)
+    Bd = oracle.dequantize_f64(1, cb, sb, len(cols), K)
+    ri = np.repeat(np.arange(len(rows)), len(cols))
+    cj = np.tile(np.arange(len(cols)), len(rows))
+    Chat, tol = oracle.gemm_sampled(Ad, Bd, ri, cj)
+    got = C[torch.tensor(rows, device=dev())][:, torch.tensor(cols, device=dev())].cpu().numpy().reshape(-1)
+    check_gemm(got, Chat, tol, False, "exact MXFP8")
+    del qa, qb, b, C
+    torch.cuda.empty_cache()
+
+
+def test_grouped_nvfp4_gather_past_32bit_offsets():
+    """Grouped NVFP4 GEMM whose gathered A (66048 x 131072) holds 4.3 GB of
+    codes; routed rows gather from both ends of A, two experts."""
+    T, K, N, E = 66048, 131072, 256, 2
+    g = torch.Generator(device=dev()).manual_seed(14)
+    x = torch.randn((T, K), dtype=torch.bfloat16, device=dev(), generator=g)
+    qx = mx.empty(mx.MX_NVFP4, T, K, device=dev())
+    ax = torch.zeros(1, dtype=torch.float32, device=dev())
+    mx.mx_quantize(x, qx, amax=ax)
+    w = torch.randn((E * N, K), dtype=torch.bfloat16, device=dev(), generator=g)
+    qw = mx.empty(mx.MX_NVFP4, E * N, K, device=dev(), n_tensor_scales=E)
+    aw = torch.zeros(E, dtype=torch.float32, device=dev())
+    for e in range(E):
+        sub = mx.MXTensor(3, N, K, qw.codes[e * N:(e + 1) * N], qw.scales[e * N:(e + 1) * N],
+                          qw.tensor_scale[e:e + 1])
+        mx.mx_quantize(w[e * N:(e + 1) * N], sub, amax=aw[e:e + 1])
+    R = 512
+    src = np.concatenate([np.arange(T - 256, T), np.arange(256)]).astype(np.int32)  # far end first
+    ri = torch.from_numpy(src).to(dev())
+    off = torch.tensor([0, 256, R], dtype=torch.int64, device=dev())
+    C = torch.empty(R, N, dtype=torch.float32, device=dev())
+    mx.mx_gemm_grouped(qx, ri, R, qw, E, off, C)
+    torch.cuda.synchronize()
+    TA = float(ax.item())
+    routed = [0, 255, 256, 511]
+    cols = [0, 77, N - 1]
+    xr = _bits(x[torch.from_numpy(src[routed].astype(np.int64)).to(dev())])
+    cx, sx, ts_x = oracle.quantize(xr, 3, amax=TA)
+    Ad = oracle.dequantize_f64(3, cx, sx, len(routed), K)
+    for e in range(E):
+        wr = _bits(w[torch.tensor([e * N + c for c in cols], device=dev())])
+        cw, sw, ts_w = oracle.quantize(wr, 3, amax=float(aw[e].item()))
+        Bd = oracle.dequantize_f64(3, cw, sw, len(cols), K)
+        mine = [i for i, r in enumerate(routed) if (r >= 256) == (e == 1)]
+        ri_ = np.repeat(np.array(mine), len(cols))
+        cj_ = np.tile(np.arange(len(cols)), len(mine))
+        Chat, tol = oracle.gemm_sampled(Ad, Bd, ri_, cj_, float(np.float64(ts_x) * np.float64(ts_w)))
+        got = C[torch.tensor([routed[i] for i in mine], device=dev())][:, torch.tensor(cols, device=dev())]
+        check_gemm(got.cpu().numpy().reshape(-1), Chat, tol, False, f"expert {e}")
+    del x, qx, w, qw, C
     torch.cuda.empty_cache()
