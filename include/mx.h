@@ -39,12 +39,14 @@
  *   - Pointers are device pointers (HIP), except the mx_tensor descriptor
  *     itself and the arguments documented as host values.
  *   - Ownership: the caller allocates and frees every buffer.  The library
- *     never allocates, frees or synchronizes.
+ *     never allocates, frees or synchronizes; its one device array (1 KiB per
+ *     device, the amax slots of mx_quantize_batch_noalloc) is static.
  *   - Execution: every call enqueues work on `stream` (NULL = the default
  *     stream) and returns before the work has run.  Buffers must stay alive
  *     until the stream reaches the work.  Calls are thread-safe; the only
  *     state the library keeps is a per-device flag recording that a kernel's
- *     dynamic LDS limit has been raised (set on first use, idempotent).
+ *     dynamic LDS limit has been raised (set on first use, idempotent) and,
+ *     per device, the address of that static array (looked up on first use).
  *   - Errors: arguments are checked on the host before anything is enqueued
  *     (no HIP call happens on a failed check).  A failed check returns
  *     MX_ERR_NULL / MX_ERR_SHAPE / MX_ERR_ALIGN / MX_ERR_FORMAT /
@@ -201,10 +203,10 @@ uint16_t mx_rht_signs(uint64_t seed);
  *     each stage": a choice between block scales that lowers the
  *     quantization error): each block is encoded with sb from
  *     max|x| / (6 S) and from max|x| / (4 S); the encoding whose decoded
- *     values have the smaller squared error is kept, the first on a tie.  The
- *     error is an FP32 sum: d = x - fp32(e2m1 * e4m3 * S), each half of 8
- *     elements accumulated as acc = fma(d, d, acc) from its first element,
- *     then the two halves added.
+ *     values have the smaller squared error is kept, the first (6) on a tie.
+ *     The error is the exact sum over the 16 elements of
+ *     (x - fp32(e2m1 * e4m3 * S))^2, with no rounding, so the choice does
+ *     not depend on an order of summation.
  *   MX_FLAG_BLOCK_2D (NVFP4; [MXF] "NVFP4": two-dimensional weight
  *     quantisation): one block scale per tile of 16 rows x 16 columns (the
  *     last band of rows may be shorter), from the tile's max|x|, stored in
@@ -433,6 +435,26 @@ mx_status mx_gemm_quantize_a(const void* A, int64_t lda, int64_t M, int32_t a_fm
 mx_status mx_gemm_grouped(const mx_tensor* A, const int32_t* row_index, int64_t routed_rows,
                           const mx_tensor* B, int32_t num_groups, const int64_t* group_offsets,
                           void* C, int32_t cdt, int64_t ldc, mx_stream stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * result as mx_quantize_batch(jobs, count, stream), with the amax slot of
+ * every NVFP4 job taken from a library-owned device array instead of
+ * jobs[i].amax.  Job i uses slot i of that array; the array holds
+ * MX_NOALLOC_MAX_JOBS FP32 values (1 KiB) per device, lives until the process
+ * ends, and is obtained once per device on the first call made with that
+ * device current.  The call allocates nothing and frees nothing.
+ * Requirements, on top of mx_quantize_batch's: count <= MX_NOALLOC_MAX_JOBS
+ * (else MX_ERR_SHAPE); every jobs[i].amax is NULL and no job sets
+ * MX_FLAG_AMAX_GIVEN (else MX_ERR_UNSUPPORTED); `stream` belongs to the
+ * current device (else MX_ERR_UNSUPPORTED).  A failure of the symbol lookup
+ * returns MX_ERR_HIP.  Every slot a job uses is written by a kernel before it
+ * is read, so nothing left by an earlier call leaks into a result.  All calls
+ * on one device share the array: calls whose work can overlap on that device
+ * (other streams, other threads) race and must be serialized by the
+ * caller. */
+#define MX_NOALLOC_MAX_JOBS 256
+mx_status mx_quantize_batch_noalloc(const mx_quantize_job* jobs, int32_t count, mx_stream stream);
 
 /* Human-readable name of a status code (static string). */
 const char* mx_status_string(int32_t status);

@@ -23,6 +23,7 @@ MX_FLAG_RHT16, MX_FLAG_AMAX_GIVEN = 1, 2
 MX_FLAG_SCALE_CEIL, MX_FLAG_FOUR_OVER_SIX, MX_FLAG_BLOCK_2D = 4, 8, 16
 MX_GEMM_FP8_NATIVE = 1
 MX_LAYOUT_ROWS, MX_LAYOUT_TILED = 0, 1
+MX_NOALLOC_MAX_JOBS = 256
 
 FORMATS = {"mxfp8": MX_MXFP8_E4M3, "mxfp4": MX_MXFP4_E2M1, "nvfp4": MX_NVFP4, "mxint8": MX_MXINT8,
            "s2f6": MX_MXINT8, "mxfp8_e5m2": MX_MXFP8_E5M2, "mxfp6_e3m2": MX_MXFP6_E3M2,
@@ -33,7 +34,7 @@ EXPORTED = [
     "mx_codes_bytes", "mx_scales_bytes", "mx_rht_signs", "mx_quantize", "mx_amax",
     "mx_dequantize", "mx_requant_transpose", "mx_hadamard16", "mx_gemm", "mx_gemm_ex",
     "mx_gemm_grouped", "mx_gemm_quantize", "mx_gemm_quantize_a", "mx_quantize_batch", "mx_error_stats",
-    "mx_status_string",
+    "mx_quantize_batch_noalloc", "mx_status_string",
 ]
 
 
@@ -88,6 +89,7 @@ def load():
         "mx_gemm_quantize": (i32, [TP, TP, TP, i32, _Rng, u32, vp]),
         "mx_gemm_quantize_a": (i32, [vp, i64, i64, i32, i32, _Rng, TP, vp, i32, i64, TP, vp]),
         "mx_quantize_batch": (i32, [ctypes.POINTER(_Job), i32, vp]),
+        "mx_quantize_batch_noalloc": (i32, [ctypes.POINTER(_Job), i32, vp]),
         "mx_status_string": (ctypes.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -194,7 +196,7 @@ class QuantizeBatch:
     """A prepared mx_quantize_batch call: the job array is built once (the
     tensors must stay alive), and each run() is one call of the C function."""
 
-    def __init__(self, jobs):
+    def __init__(self, jobs, noalloc: bool = False):
         self._descs = [j["out"].desc() for j in jobs]
         self._keep = [j["x"] for j in jobs] + [j["out"] for j in jobs]
         self._arr = (_Job * max(len(jobs), 1))()
@@ -205,7 +207,8 @@ class QuantizeBatch:
                                 _Rng(j.get("seed", 0), j.get("counter", 0)), j.get("flags", 0),
                                 j.get("sign_mask", 0), _ptr(j.get("amax")))
         self._n = len(jobs)
-        self._fn = load().mx_quantize_batch
+        L = load()
+        self._fn = L.mx_quantize_batch_noalloc if noalloc else L.mx_quantize_batch
 
     def run(self, stream=None):
         _check(self._fn(self._arr, self._n, _stream(stream)))
@@ -216,6 +219,14 @@ def mx_quantize_batch(jobs, stream=None):
     mx_quantize (x, out, and optionally rnd, seed, counter, flags, sign_mask,
     amax).  Compatible tile-layout jobs share kernel launches."""
     QuantizeBatch(jobs).run(stream)
+    return [j["out"] for j in jobs]
+
+
+def mx_quantize_batch_noalloc(jobs, stream=None):
+    """mx_quantize_batch without an amax buffer from the caller: NVFP4 jobs
+    take their amax slots from the library's own device array (no job may
+    carry "amax" or MX_FLAG_AMAX_GIVEN; at most MX_NOALLOC_MAX_JOBS jobs)."""
+    QuantizeBatch(jobs, noalloc=True).run(stream)
     return [j["out"] for j in jobs]
 
 

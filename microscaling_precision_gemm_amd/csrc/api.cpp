@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "device/codec.h"
 #include "launch.h"
 
@@ -175,17 +177,21 @@ mx_status mx_quantize(const void* x, int32_t xdt, int64_t rows, int64_t cols, in
   return hip_status(mxk::launch_quantize(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
-mx_status mx_quantize_batch(const mx_quantize_job* jobs, int32_t count, mx_stream stream) {
+namespace {
+// mx_quantize_batch's work.  With slots != NULL, job i's amax slot is
+// slots + i instead of jobs[i].amax.
+mx_status quantize_batch(const mx_quantize_job* jobs, int32_t count, float* slots, mx_stream stream) {
   if (count < 0) return MX_ERR_SHAPE;
   if (count == 0) return MX_OK;
   if (!jobs) return MX_ERR_NULL;
+  auto slot = [&](int32_t i) { return slots ? slots + i : jobs[i].amax; };
   // every job is checked before anything is enqueued
   for (int32_t i = 0; i < count; ++i) {
     const mx_quantize_job& j = jobs[i];
     mxk::QuantArgs a;
     bool empty = false;
     const mx_status st = make_quant_args(j.x, j.xdt, j.rows, j.cols, j.ld_x, j.out, j.rnd, j.rng, j.flags,
-                                         j.rht_sign_mask, j.amax, &a, &empty);
+                                         j.rht_sign_mask, slot(i), &a, &empty);
     if (st != MX_OK) return st;
   }
   constexpr int kChunk = 64;  // then built and launched kChunk at a time
@@ -197,7 +203,7 @@ mx_status mx_quantize_batch(const mx_quantize_job* jobs, int32_t count, mx_strea
       const mx_quantize_job& j = jobs[i];
       bool empty = false;
       const mx_status st = make_quant_args(j.x, j.xdt, j.rows, j.cols, j.ld_x, j.out, j.rnd, j.rng, j.flags,
-                                           j.rht_sign_mask, j.amax, &args[n], &empty);
+                                           j.rht_sign_mask, slot(i), &args[n], &empty);
       if (st != MX_OK) return st;
       if (!empty) ++n;
     }
@@ -205,6 +211,55 @@ mx_status mx_quantize_batch(const mx_quantize_job* jobs, int32_t count, mx_strea
     if (st != MX_OK) return st;
   }
   return MX_OK;
+}
+}  // namespace
+
+mx_status mx_quantize_batch(const mx_quantize_job* jobs, int32_t count, mx_stream stream) {
+  return quantize_batch(jobs, count, nullptr, stream);
+}
+
+// The amax slots of mx_quantize_batch_noalloc: one FP32 per job, one copy per
+// device.  Host code never uses this name as an address (on the host it is
+// only a stand-in for the symbol); the device address comes from
+// hipGetSymbolAddress, once per device, and is kept in g_scratch.
+static __device__ __align__(256) float scratch[MX_NOALLOC_MAX_JOBS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices];  // device address of `scratch` on each device
+
+// The scratch address on the current device (looked up on first use).
+mx_status scratch_of_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MX_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MX_ERR_HIP;
+    g_scratch[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch[dev];
+  return MX_OK;
+}
+}  // namespace
+
+mx_status mx_quantize_batch_noalloc(const mx_quantize_job* jobs, int32_t count, mx_stream stream) {
+  if (count < 0 || count > MX_NOALLOC_MAX_JOBS) return MX_ERR_SHAPE;
+  if (count == 0) return MX_OK;
+  if (!jobs) return MX_ERR_NULL;
+  for (int32_t i = 0; i < count; ++i)
+    if (jobs[i].amax || (jobs[i].flags & MX_FLAG_AMAX_GIVEN)) return MX_ERR_UNSUPPORTED;
+  if (stream) {
+    int cur = -1, sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+      return MX_ERR_HIP;
+    if (cur != sdev) return MX_ERR_UNSUPPORTED;
+  }
+  float* slots = nullptr;
+  const mx_status st = scratch_of_current_device(&slots);
+  if (st != MX_OK) return st;
+  return quantize_batch(jobs, count, slots, stream);
 }
 
 mx_status mx_amax(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ld_x,

@@ -106,6 +106,24 @@ def test_quantize_batch_checks(mx):
     assert L.mx_quantize_batch(jobs, 2, None) == 5
 
 
+def test_quantize_batch_noalloc_checks(mx):
+    """The no-allocation batch rejects, before any HIP call, more jobs than
+    its slot array holds, a caller's amax buffer and MX_FLAG_AMAX_GIVEN."""
+    L = mx.load()
+    f = L.mx_quantize_batch_noalloc
+    assert f(None, 0, None) == 0
+    assert f(None, 2, None) == 1
+    assert f(None, -1, None) == 2
+    assert f(None, mx.MX_NOALLOC_MAX_JOBS + 1, None) == 2
+    nv = mx._Tensor(3, 0, 4, 64, FAKE, FAKE, FAKE)
+    jobs = (mx._Job * 2)()
+    jobs[0] = mx._Job(FAKE, 0, 4, 64, 64, ctypes.pointer(nv), 0, mx._Rng(0, 0), 0, 0, None)
+    jobs[1] = mx._Job(FAKE, 0, 4, 64, 64, ctypes.pointer(nv), 0, mx._Rng(0, 0), 0, 0, FAKE)
+    assert f(jobs, 2, None) == 5  # a job brings its own amax slot
+    jobs[1] = mx._Job(FAKE, 0, 4, 64, 64, ctypes.pointer(nv), 0, mx._Rng(0, 0), 2, 0, None)
+    assert f(jobs, 2, None) == 5  # MX_FLAG_AMAX_GIVEN: there is no caller amax to read
+
+
 def test_gemm_format_pair_checks(mx):
     """Mixed formats and the other MX element types: row layout, no flags, no
     NVFP4 in the pair."""
