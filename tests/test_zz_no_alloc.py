@@ -2,7 +2,9 @@
 slots, bit for bit, on two calls in a row: the second has fewer jobs and
 smaller tensors whose amax lies far below what the first call left in the
 library's slot array, so a slot that was read before being rewritten would
-change the tensor scales."""
+change the tensor scales.  Then the call recorded into a HIP graph (the use
+it exists for): every replay, with an eager no-allocation call on other
+inputs between replays, reproduces the eager result bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -93,3 +95,50 @@ def test_noalloc_batch_rejects_what_it_cannot_hold():
     j[0]["amax"] = torch.zeros(1, dtype=torch.float32, device=dev())
     with pytest.raises(mx.MXError):
         mx.mx_quantize_batch_noalloc(j)
+
+
+def _graph_jobs(seed, scale):
+    specs = [(mx.MX_RNE, 0), (mx.MX_SR, mx.MX_FLAG_RHT16), (mx.MX_RNE, mx.MX_FLAG_BLOCK_2D),
+             (mx.MX_RNE, mx.MX_FLAG_FOUR_OVER_SIX), (mx.MX_SR, 0), (mx.MX_RNE, 0)]
+    jobs = []
+    for i, (rnd, flags) in enumerate(specs):
+        x = to_gpu_bf16(W.normal_bf16(64, 512, scale * (i + 1), seed, 400 + i, outlier_entries=0.002,
+                                      outlier_mult=30.0))
+        mask = mx.mx_rht_signs(seed + i) if flags & mx.MX_FLAG_RHT16 else 0
+        jobs.append(dict(x=x, out=mx.empty(mx.MX_NVFP4, 64, 512, dev()), rnd=rnd, seed=seed + i, counter=3 * i,
+                         flags=flags, sign_mask=mask))
+    x = to_gpu_bf16(W.normal_bf16(64, 1024, scale, seed, 420))
+    jobs.append(dict(x=x, out=mx.empty(mx.MX_MXFP4_E2M1, 64, 1024, dev(), layout=mx.MX_LAYOUT_TILED)))
+    return jobs
+
+
+def _snap(jobs):
+    return [tuple(np.copy(a) for a in host(j["out"]) if a is not None) for j in jobs]
+
+
+def test_noalloc_batch_in_a_graph():
+    jobs = _graph_jobs(1, 2.0)
+    other = _graph_jobs(2, 0.001)
+    qb = mx.QuantizeBatch(jobs, noalloc=True)
+    qo = mx.QuantizeBatch(other, noalloc=True)
+    qb.run()
+    torch.cuda.synchronize()
+    want = _snap(jobs)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        qb.run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for j in jobs:
+            j["out"].codes.fill_(0x5A)
+            j["out"].scales.fill_(0x5A)
+            if j["out"].tensor_scale is not None:
+                j["out"].tensor_scale.fill_(-1.0)
+        qo.run()  # other amax values into the shared slots
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _snap(jobs)
+        for k, (g, w) in enumerate(zip(got, want)):
+            for a, b in zip(g, w):
+                assert np.array_equal(a, b), f"replay {rep}, job {k}"
