@@ -5,7 +5,10 @@
   and 2-D blocks (NVFP4); Student-t values over ten decades with planted
   zeros.  Codes, scales and the NVFP4 tensor scale bit for bit;
 * GEMMs: random shapes (ragged in M, N and K) for every class of operand
-  pair, FP32 out, every entry checked within the bound."""
+  pair, FP32 out, every entry checked within the bound; row-layout shapes
+  past one 256 x 256 tile (the pipelined kernels); MXFP4 in the tile layout
+  quantized on the GPU (codes and scales checked against the oracle), BF16 or
+  FP32 out."""
 import numpy as np
 import pytest
 import torch
@@ -18,6 +21,7 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     import microscaling_precision_gemm_amd as mx
     from tests.gpu_util import check_gemm, dev, host, to_gpu_bf16, to_gpu_f32, upload
+    from tests.tiles import untile_codes, untile_scales
 
 
 def _quant_case(g):
@@ -95,3 +99,65 @@ def test_random_gemm_cases(seed):
         except AssertionError as e:
             bad.append(str(e)[:200])
     assert not bad, f"{len(bad)} of 50 products outside the bound: {bad[:2]}"
+
+
+def _gemm_pair_case(g, fa, fb, M, N, K):
+    A = W.normal_bf16(M, K, float(10.0 ** g.uniform(-3, 2)), int(g.integers(0, 1000)), 1)
+    B = W.normal_bf16(N, K, float(10.0 ** g.uniform(-3, 2)), int(g.integers(0, 1000)), 2)
+    qa, qb = oracle.quantize(A, fa), oracle.quantize(B, fb)
+    ta, tb = upload(fa, qa[0], qa[1], qa[2]), upload(fb, qb[0], qb[1], qb[2])
+    ta.cols = tb.cols = K
+    C = torch.empty(M, N, dtype=torch.float32, device=dev())
+    mx.mx_gemm(ta, tb, C)
+    torch.cuda.synchronize()
+    Ahat = oracle.dequantize_f64(fa, qa[0], qa[1], M, K) * (qa[2] if fa == 3 else 1.0)
+    Bhat = oracle.dequantize_f64(fb, qb[0], qb[1], N, K) * (qb[2] if fb == 3 else 1.0)
+    Cw, tol = oracle.gemm(Ahat, Bhat)
+    check_gemm(C.cpu().numpy(), Cw, tol, False, f"{fa} x {fb} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("seed", [505, 606])
+def test_random_gemm_cases_past_one_tile(seed):
+    g = np.random.default_rng(seed)
+    pairs = PAIRS + [(5, 5), (1, 5)]
+    bad = []
+    for _ in range(16):
+        fa, fb = pairs[int(g.integers(0, len(pairs)))]
+        M, N = int(g.integers(257, 1100)), int(g.integers(257, 1100))
+        K = 512 * int(g.integers(1, 5)) if g.random() < 0.7 else 32 * int(g.integers(1, 80))
+        try:
+            _gemm_pair_case(g, fa, fb, M, N, K)
+        except AssertionError as e:
+            bad.append(str(e)[:200])
+    assert not bad, f"{len(bad)} of 16 products outside the bound: {bad[:2]}"
+
+
+@pytest.mark.parametrize("seed", [707, 808])
+def test_random_tiled_mxfp4_cases(seed):
+    g = np.random.default_rng(seed)
+    bad = []
+    for _ in range(16):
+        M, N = 32 * int(g.integers(1, 40)), 32 * int(g.integers(1, 40))
+        K = 1024 * int(g.integers(1, 5))
+        A = W.normal_bf16(M, K, float(10.0 ** g.uniform(-3, 2)), int(g.integers(0, 1000)), 1,
+                          outlier_entries=0.002, outlier_mult=50.0)
+        B = W.normal_bf16(N, K, float(10.0 ** g.uniform(-3, 2)), int(g.integers(0, 1000)), 2)
+        qa = mx.empty(2, M, K, device=dev(), layout=mx.MX_LAYOUT_TILED)
+        qb = mx.empty(2, N, K, device=dev(), layout=mx.MX_LAYOUT_TILED)
+        mx.mx_quantize(to_gpu_bf16(A), qa)
+        mx.mx_quantize(to_gpu_bf16(B), qb)
+        cdt = torch.bfloat16 if g.random() < 0.5 else torch.float32
+        C = torch.empty(M, N, dtype=cdt, device=dev())
+        mx.mx_gemm(qa, qb, C)
+        torch.cuda.synchronize()
+        oa, ob = oracle.quantize(A, 2), oracle.quantize(B, 2)
+        for q, o, R in ((qa, oa, M), (qb, ob, N)):
+            c, sc, _ = host(q)
+            if not (np.array_equal(untile_codes(c, R, K // 2), o[0]) and np.array_equal(untile_scales(sc, R, K // 32), o[1])):
+                bad.append(f"tiled quantize {R}x{K}")
+        Cw, tol = oracle.gemm(oracle.dequantize_f64(2, oa[0], oa[1], M, K), oracle.dequantize_f64(2, ob[0], ob[1], N, K))
+        try:
+            check_gemm(C.float().cpu().numpy(), Cw, tol, cdt == torch.bfloat16, f"tiled MXFP4 {M}x{N}x{K}")
+        except AssertionError as e:
+            bad.append(str(e)[:200])
+    assert not bad, f"{len(bad)} of 16 tiled cases failed: {bad[:2]}"
