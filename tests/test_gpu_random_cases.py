@@ -161,3 +161,34 @@ def test_random_tiled_mxfp4_cases(seed):
         except AssertionError as e:
             bad.append(str(e)[:200])
     assert not bad, f"{len(bad)} of 16 tiled cases failed: {bad[:2]}"
+
+
+@pytest.mark.parametrize("seed", [909])
+def test_random_requant_cases(seed):
+    """Requant-transpose on random shapes (rows % 32 == 0, cols % 16 == 0,
+    ragged against the 128 x 64 tiles), both sources and both roundings,
+    bit for bit."""
+    g = np.random.default_rng(seed)
+    bad = []
+    for _ in range(24):
+        rows, cols = 32 * int(g.integers(1, 30)), 16 * int(g.integers(1, 60))
+        rnd = int(g.integers(0, 2))
+        sd, ctr = int(g.integers(0, 1 << 40)), int(g.integers(0, 1 << 40))
+        bits = W.normal_bf16(rows, cols, float(10.0 ** g.uniform(-3, 3)), int(g.integers(0, 1000)), 45,
+                             outlier_entries=0.005, outlier_mult=30.0)
+        out = mx.empty(1, cols, rows, device=dev())
+        if g.random() < 0.5:
+            nv = oracle.quantize(bits, 3, 0)
+            mx.mx_requant_transpose(out, src=upload(3, nv[0], nv[1], nv[2]), rnd=rnd, seed=sd, counter=ctr)
+            wc, ws = oracle.requant_transpose(rows, cols, rnd, seed=sd, counter=ctr, nvfp4=nv)
+            what = "nvfp4"
+        else:
+            mx.mx_requant_transpose(out, x_bf16=to_gpu_bf16(bits, pad_cols=int(g.choice([0, 8, 24]))), rnd=rnd,
+                                    seed=sd, counter=ctr)
+            wc, ws = oracle.requant_transpose(rows, cols, rnd, seed=sd, counter=ctr, bf16=bits)
+            what = "bf16"
+        torch.cuda.synchronize()
+        c, s, _ = host(out)
+        if not (np.array_equal(s, ws) and np.array_equal(c, wc)):
+            bad.append(f"{what} {rows}x{cols} rnd {rnd}")
+    assert not bad, f"{len(bad)} of 24 requant cases differ from the oracle: {bad[:3]}"
