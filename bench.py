@@ -622,8 +622,8 @@ def detail(torch, mx, W, args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the path is measured on one MI355X "
-              "(see DESIGN.md for how it would shard); --gpus must be 1", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the path is built and measured on one MI355X "
+              "(sharding across GPUs is not built); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
