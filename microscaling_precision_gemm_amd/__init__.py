@@ -69,6 +69,14 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise MXError(f"{LIB_PATH} is not built; run microscaling_precision_gemm_amd.build.build()")
+    # torch ships its own HIP runtime under the same soname.  Loaded first, it
+    # is the one libmx.so binds to; loaded after libmx.so (which would pull in
+    # the system copy), the process would hold two runtimes, and launches on
+    # torch's streams would fail.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, u32, u64, u16 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                    ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint16)

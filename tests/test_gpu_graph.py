@@ -66,3 +66,27 @@ def test_graph_replays_match_eager():
         got = _snap(qa, qb, C, qg, xt)
         for i, (x, y) in enumerate(zip(got, want)):
             assert np.array_equal(x, y), f"replay {rep}: output {i} differs from eager"
+
+
+def test_library_loaded_before_torch():
+    """load() called before torch is imported still binds libmx.so to the HIP
+    runtime torch uses (one runtime in the process): a quantization on
+    torch's stream then runs and matches the oracle (in a fresh process)."""
+    import os
+    import subprocess
+    import sys
+    code = (
+        "import microscaling_precision_gemm_amd as mx\n"
+        "mx.load()\n"
+        "import numpy as np, torch, oracle, workloads as W\n"
+        "b = W.normal_bf16(64, 256, 1.0, 0, 5)\n"
+        "x = torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)\n"
+        "q = mx.empty(2, 64, 256, 'cuda')\n"
+        "mx.mx_quantize(x, q)\n"
+        "torch.cuda.synchronize()\n"
+        "o = oracle.quantize(b, 2)\n"
+        "assert np.array_equal(q.codes.cpu().numpy(), o[0]) and np.array_equal(q.scales.cpu().numpy(), o[1])\n"
+        "print('ok')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
