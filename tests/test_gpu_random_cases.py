@@ -24,12 +24,16 @@ if torch.cuda.is_available():
     from tests.tiles import untile_codes, untile_scales
 
 
-def _quant_case(g):
-    fmt = int(g.choice([1, 2, 3, 4, 5, 6, 7, 3, 3, 2]))
+def _quant_case(g, max_rows=200, max_blocks=40, tiled_share=0.0):
+    tiled = tiled_share > 0 and g.random() < tiled_share  # no extra draw for the small cases
+    fmt = int(g.choice([1, 2, 5])) if tiled else int(g.choice([1, 2, 3, 4, 5, 6, 7, 3, 3, 2]))
     blk = 16 if fmt == 3 else 32
-    rows, cols = int(g.integers(1, 200)), blk * int(g.integers(1, 40))
+    if tiled:  # the tile layout: rows % 32 == 0, cols % 1024 == 0
+        rows, cols = 32 * int(g.integers(1, max_rows // 32 + 2)), 1024 * int(g.integers(1, 5))
+    else:
+        rows, cols = int(g.integers(1, max_rows)), blk * int(g.integers(1, max_blocks))
     bf16 = g.random() < 0.6
-    pad = int(g.choice([0, 0, 8, 24]))
+    pad = 0 if tiled else int(g.choice([0, 0, 8, 24]))
     rnd = int(g.integers(0, 2))
     rht = bool(g.random() < 0.4)
     variant, flags = 0, 0
@@ -52,11 +56,13 @@ def _quant_case(g):
     else:
         xin, xd = x, to_gpu_f32(x, pad)
     seed, counter, mask = int(g.integers(0, 2**40)), int(g.integers(0, 2**40)), int(g.integers(0, 65536))
-    out = mx.empty(fmt, rows, cols, device=dev())
+    out = mx.empty(fmt, rows, cols, device=dev(), layout=mx.MX_LAYOUT_TILED if tiled else mx.MX_LAYOUT_ROWS)
     amax = torch.zeros(1, dtype=torch.float32, device=dev())
     mx.mx_quantize(xd, out, rnd, seed, counter, flags, mask, amax if fmt == 3 else None)
     torch.cuda.synchronize()
     c, s, ts = host(out)
+    if tiled:
+        c, s = untile_codes(c, rows, cols if fmt != 2 else cols // 2), untile_scales(s, rows, cols // 32)
     wc, ws, wts = oracle.quantize(xin, fmt, rnd, seed=seed, counter=counter, rht=rht, sign_mask=mask,
                                   variant=variant)
     ok = np.array_equal(c, wc) and np.array_equal(s, ws) and (fmt != 3 or float(ts[0]) == wts)
@@ -68,6 +74,15 @@ def test_random_quantize_cases(seed):
     g = np.random.default_rng(seed)
     bad = [case for ok, case in (_quant_case(g) for _ in range(300)) if not ok]
     assert not bad, f"{len(bad)} of 300 cases differ from the oracle, e.g. {bad[:3]}"
+
+
+@pytest.mark.parametrize("seed", [111])
+def test_random_quantize_cases_large(seed):
+    """Larger shapes (grids of many workgroups, the grid-stride amax pass),
+    row and tile layouts."""
+    g = np.random.default_rng(seed)
+    bad = [case for ok, case in (_quant_case(g, 1500, 300, 0.3) for _ in range(24)) if not ok]
+    assert not bad, f"{len(bad)} of 24 cases differ from the oracle, e.g. {bad[:3]}"
 
 
 PAIRS = [(1, 1), (2, 2), (3, 3), (5, 1), (4, 4), (7, 7), (6, 6), (7, 2), (1, 2), (6, 4)]
